@@ -1,0 +1,146 @@
+"""Python front end of the plain float64 C oracle (``kda_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this module; the library and its Python
+binding never do.  It shares no code with the HIP path.
+
+Every input is converted exactly to float64 before the call (bf16 and fp32
+values are exactly representable), so the oracle sees the very values the
+GPU receives.  See ``kda_oracle.c`` for the recurrence and its citations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+EPS = 1e-6  # L2-norm epsilon: x / sqrt(sum x^2 + EPS) (not given by the pages)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER(ctypes.c_double)
+        I = ctypes.c_int
+        D = ctypes.c_double
+        lib.kda_oracle_prefill.argtypes = [P, P, P, P, P, P, P, P,
+                                           ctypes.POINTER(ctypes.c_int64), I, I, I, I, D, D, D,
+                                           I, I, ctypes.POINTER(ctypes.c_int32), I, P, P, I]
+        lib.kda_oracle_prefill.restype = I
+        lib.kda_oracle_decode.argtypes = [P, P, P, P, P, P, P, D, D, D, I, I, I, I, I, I, P, P, I]
+        lib.kda_oracle_decode.restype = I
+        lib.kda_oracle_max_threads.restype = I
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().kda_oracle_max_threads())
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    if x is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_seqlens=None,
+            scale=None, lower_bound=-5.0, use_qk_l2norm=True, ejk=False, units=None,
+            threads=0, eps=EPS):
+    """Token-by-token float64 recurrence over every (sequence, head).
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv]; g: [B, T, H, dk] raw gate (KDA) or
+    [B, T, H] log-decay / None (EJK); beta: [B, T, H] logits (KDA) or
+    activated (EJK); a_log [H]; dt_bias [dk, H]; initial_state [N, H, dk, dv].
+    With cu_seqlens ([N+1]) the batch must be 1 and sequences are packed.
+    ``units`` restricts the work to a list of (seq * H + head) items; outputs
+    of the other items are left as zeros.
+    Returns (o [B, T, H, dv], final_state [N, H, dk, dv]) in float64.
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("cu_seqlens requires batch 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n = cu.shape[0] - 1
+    g = _f64(g)
+    beta = _f64(beta)
+    a_log = _f64(np.zeros(H) if a_log is None else np.reshape(a_log, (H,)))
+    dt_bias = _f64(dt_bias)
+    s0 = _f64(initial_state)
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    fs = np.zeros((n, H, dk, dv), dtype=np.float64)
+    if units is None:
+        uptr, nu = ctypes.POINTER(ctypes.c_int32)(), 0
+        uarr = None
+    else:
+        uarr = np.ascontiguousarray(np.asarray(units, dtype=np.int32))
+        uptr, nu = uarr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(uarr.size)
+    sc = -1.0 if scale is None else float(scale)
+    rc = lib.kda_oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(a_log),
+                                _ptr(dt_bias), _ptr(s0),
+                                cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, H, dk, dv,
+                                sc, float(lower_bound), float(eps), int(bool(use_qk_l2norm)),
+                                int(bool(ejk)), uptr, nu, _ptr(o), _ptr(fs), int(threads))
+    if rc != 0:
+        raise ValueError("oracle prefill rejected its arguments")
+    return o, fs
+
+
+def decode(q, k, g, v, beta, a_log, dt_bias, S, scale=None, lower_bound=-5.0,
+           use_qk_l2norm=True, ejk=False, threads=0, eps=EPS):
+    """One step for each of B requests, kda_tkg layouts.
+
+    q, k, g: [B, dk, H] (EJK: g is [B, 1, H] log-decay or None); v: [B, H, dv];
+    beta: [B, 1, H]; a_log: [1, H]; dt_bias: [dk, H]; S: [B, H, dk, dv].
+    Returns (out [B, H, dv], S_new) without touching the caller's S.
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, dk, H = q.shape
+    dv = v.shape[-1]
+    g = _f64(g)
+    beta = _f64(beta)
+    a_log = _f64(np.zeros(H) if a_log is None else np.reshape(a_log, (H,)))
+    dt_bias = _f64(dt_bias)
+    S_new = np.array(S, dtype=np.float64, copy=True, order="C")
+    out = np.zeros((B, H, dv), dtype=np.float64)
+    sc = -1.0 if scale is None else float(scale)
+    rc = lib.kda_oracle_decode(_ptr(q), _ptr(k), _ptr(g), _ptr(v), _ptr(beta), _ptr(a_log),
+                               _ptr(dt_bias), sc, float(lower_bound), float(eps), B, H, dk, dv,
+                               int(bool(use_qk_l2norm)), int(bool(ejk)), _ptr(out), _ptr(S_new),
+                               int(threads))
+    if rc != 0:
+        raise ValueError("oracle decode rejected its arguments")
+    return out, S_new
