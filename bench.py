@@ -1,0 +1,231 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+Headline (``value``): single-token decode steps/s for B=64 requests, H=32,
+dk=dv=128, fp32 (the kda_tkg-shaped workload): one step is one
+kda_decode_step call - prologue, state decay, delta update and output for all
+64 x 32 (request, head) items.  Inputs are resident in HBM before timing; the
+state rotates over 5 buffers (640 MiB) so that the 256 MB Infinity Cache
+cannot hold it between steps.
+
+The same JSON line also carries:
+  roofline      the decode kernel against MI355X's 8 TB/s HBM (algorithmic
+                bytes per launch / mean launch time from HIP events)
+  cpu_baseline  the float64 CPU oracle timed on the host on a bounded sample
+  prefill       chunked prefill tokens/s for B=4, T=4096, H=16, dk=dv=128
+                (bf16 inputs) with its own roofline fractions (--no-prefill
+                skips it)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + decode steps/s; % MFMA peak / % HBM BW peak"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFS = 2500.0
+
+# decode, B=64 H=32 dk=dv=128: state read + write, q/k/g [B,dk,H], v/out [B,H,dv],
+# beta [B,1,H], a_log [1,H], dt_bias [dk,H] - all fp32
+def decode_bytes(B, H, dk, dv):
+    return 4 * (2 * B * H * dk * dv + 3 * B * dk * H + 2 * B * H * dv + B * H + H + dk * H)
+
+
+def decode_flops(B, H, dk, dv):
+    # decay (1), S^T k (2), S^T q (2), rank-1 update (2) per state element
+    return 7 * B * H * dk * dv
+
+
+def prefill_bytes(ntok, H, dk, dv, n_states, init_state):
+    per_tok = H * (2 * dk * 2 + dv * 2 + dk * 4 + 4 + dv * 2)  # q,k,v bf16; g fp32; beta; o bf16
+    states = n_states * H * dk * dv * 4 * (2 if init_state else 1)
+    return ntok * per_tok + states + H * 4 + dk * H * 4
+
+
+def prefill_flops(ntok, H, dk, dv, C=64):
+    # triangle-aware: intra-chunk Gram and output terms + the three state products
+    return ntok * H * (C * (3 * dk + 2 * dv) + 6 * dk * dv)
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_90_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_traffic(name, src_hash, bytes_per_launch):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_pmc.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("src_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def bench_decode(steps, warmup, nbuf=5):
+    import torch
+    import gated_delta_rule_90_amd as kda
+    from gated_delta_rule_90_amd import workloads
+    inp = workloads.decode_b64_h32_d128()
+    f = torch.float32
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", f)
+    q, k, v, g, beta = d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta)
+    a_log, dtb = d(inp.a_log), d(inp.dt_bias)
+    S0 = d(inp.S)
+    states = [S0.clone() for _ in range(nbuf)]
+    out = torch.empty_like(v)
+    B, dk, H = inp.q.shape
+    dv = inp.v.shape[-1]
+
+    def step(i):
+        kda.decode_step(q, k, v, g, beta, a_log, dtb, states[i % nbuf], scale=inp.scale,
+                        lower_bound=inp.lower_bound, out=out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = decode_bytes(B, H, dk, dv)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    sh = _src_hash("kda_decode.hip")
+    traffic = _counter_traffic("decode_b64_h32_d128", sh, nbytes)
+    return inp, {
+        "ms": ms, "wall_s": wall, "steps_per_s": 1e3 / ms, "bytes": nbytes,
+        "flops": decode_flops(B, H, dk, dv),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel<128,128,false>",
+                     "bytes_per_launch": nbytes, "src_hash": sh},
+    }
+
+
+def cpu_decode_baseline(inp, budget_s=10.0):
+    from oracle import kda_oracle
+    kda_oracle.build(force=False)
+    threads = kda_oracle.max_threads()
+    t0 = time.perf_counter()
+    kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
+                      scale=inp.scale, lower_bound=inp.lower_bound)
+    one = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(one, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
+                          scale=inp.scale, lower_bound=inp.lower_bound)
+    el = time.perf_counter() - t0
+    return {"value": round(reps / el, 3), "unit": "decode steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} full decode steps (B=64, H=32, dk=dv=128, float64) in {el:.1f} s"}
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    import gated_delta_rule_90_amd as kda
+    from gated_delta_rule_90_amd import workloads
+    inp = workloads.prefill_b4_t4096_h16_d128()
+    bf, f = torch.bfloat16, torch.float32
+    d = lambda x, t: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(t)
+    sets = []
+    for rep in range(2):  # two input sets (2 x 408 MB) so the Infinity Cache cannot hold one
+        sets.append([d(inp.q, bf), d(inp.k, bf), d(inp.v, bf), d(inp.g, f), d(inp.beta, f)])
+    a_log, dtb = d(inp.a_log, f), d(inp.dt_bias, f)
+    B, T, H, dk = inp.q.shape
+    dv = inp.v.shape[-1]
+    o = torch.empty((B, T, H, dv), dtype=bf, device="cuda")
+    fs = torch.empty((B, H, dk, dv), dtype=f, device="cuda")
+
+    def step(i):
+        q, k, v, g, beta = sets[i % 2]
+        kda.prefill(q, k, v, g, beta, a_log, dtb, scale=inp.scale, lower_bound=inp.lower_bound,
+                    out=o, final_state=fs)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ntok = B * T
+    nbytes = prefill_bytes(ntok, H, dk, dv, B, False)
+    fl = prefill_flops(ntok, H, dk, dv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = fl / (ms * 1e-3) / 1e12
+    floor_ms = max(nbytes / (HBM_PEAK_GBS * 1e9), fl / (BF16_MFMA_PEAK_TFS * 1e12)) * 1e3
+    return {"workload": "kda_chunked_prefill_b4_t4096_h16_d128_bf16",
+            "tokens_per_s": round(ntok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+            "alg_bytes": nbytes, "alg_flops_tri": fl,
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
+            "roofline_frac": round(floor_ms / ms, 4), "achieved_GBs": round(gbs, 1),
+            "achieved_TFs": round(tfs, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the KDA kernels use no collectives and the pass does not shard", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    inp, dec = bench_decode(args.steps, args.warmup)
+    line = {
+        "metric": METRIC,
+        "value": round(dec["steps_per_s"], 2),
+        "unit": "decode steps/s (B=64 requests x H=32 heads, dk=dv=128)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "kda_decode_b64_h32_d128_fp32", "B": 64, "H": 32, "dk": 128,
+                   "dv": 128, "state_buffers": 5, "seed": 1002},
+        "request_tokens_per_s": round(64 * dec["steps_per_s"], 1),
+        "roofline": dec["roofline"],
+    }
+    if not args.no_prefill:
+        line["prefill"] = bench_prefill(max(5, args.steps // 10), max(2, args.warmup // 10))
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_decode_baseline(inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+// kda_api.cpp - the C ABI of libkda.so: argument validation, routing to the
+// kernels, status codes and the thread-local error message.  Every
+// host-detectable error is reported before any HIP call is made.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status_t fail(kda_status_t st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kda_status_t ok()
+{
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+kda_status_t hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(KDA_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr uint32_t kKnownFlags = KDA_QK_L2NORM | KDA_CHUNKED | KDA_EJK;
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk,
+                                   int32_t dv, uint32_t flags)
+{
+    (void)flags;
+    if (B < 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    const bool packed = num_seqs > 0 && B == 1;
+    const int N = packed ? num_seqs : B;
+    return kda::chunked_workspace_bytes(N, T, H, dk, dv, packed);
+}
+
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                         const float* g, const float* beta, const float* a_log,
+                         const float* dt_bias, const float* initial_state,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                         int32_t H, int32_t dk, int32_t dv, float scale, float lower_bound,
+                         int32_t chunk_size, uint32_t flags, void* o, kda_dtype_t out_dtype,
+                         float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream)
+{
+    if (flags & ~kKnownFlags) return fail(KDA_EINVAL, "kda_prefill: unknown flag bits 0x%x", flags & ~kKnownFlags);
+    const bool ejk = (flags & KDA_EJK) != 0;
+    const bool chunked = (flags & KDA_CHUNKED) != 0;
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_EINVAL, "kda_prefill: bad sizes B=%d T=%d H=%d dk=%d dv=%d", B, T, H, dk, dv);
+    if (in_dtype != KDA_F32 && in_dtype != KDA_BF16) return fail(KDA_EINVAL, "kda_prefill: unknown in_dtype %d", (int)in_dtype);
+    if (out_dtype != KDA_F32 && out_dtype != KDA_BF16) return fail(KDA_EINVAL, "kda_prefill: unknown out_dtype %d", (int)out_dtype);
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_EINVAL, "kda_prefill: cu_seqlens requires B == 1 (got %d)", B);
+        if (num_seqs < 0) return fail(KDA_EINVAL, "kda_prefill: num_seqs must be >= 0 with cu_seqlens");
+    } else if (num_seqs != 0 && num_seqs != B) {
+        return fail(KDA_EINVAL, "kda_prefill: num_seqs (%d) must be 0 or B (%d) without cu_seqlens", num_seqs, B);
+    }
+    const int N = cu_seqlens ? num_seqs : B;
+    const bool has_tokens = (cu_seqlens ? (T > 0 && N > 0) : (B > 0 && T > 0));
+    if (has_tokens) {
+        if (!q || !k || !v || !beta || !o) return fail(KDA_EINVAL, "kda_prefill: q, k, v, beta and o are required");
+        if (!ejk && (!g || !a_log)) return fail(KDA_EINVAL, "kda_prefill: KDA mode needs g and a_log");
+    }
+    if (!ejk && !(std::isfinite(lower_bound) && lower_bound <= 0.f))
+        return fail(KDA_EINVAL, "kda_prefill: lower_bound must be finite and <= 0 (got %g)", (double)lower_bound);
+    if (!dim_ok(dk) || !dim_ok(dv))
+        return fail(KDA_EUNSUPPORTED, "kda_prefill: dk and dv must be in {16, 32, 64, 128} (got %d, %d)", dk, dv);
+    if (in_dtype == KDA_F32 && out_dtype == KDA_BF16)
+        return fail(KDA_EUNSUPPORTED, "kda_prefill: bf16 output needs bf16 input");
+    if (chunked && chunk_size != 64)
+        return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path implements chunk_size 64 (got %d)", chunk_size);
+    if (chunked && !ejk && lower_bound < -5.0f)
+        return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path needs lower_bound >= -5 (got %g)", (double)lower_bound);
+    if (N == 0) return ok();
+    if (!has_tokens && !final_state) return ok();
+
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.g = g; a.beta = beta; a.a_log = a_log; a.dt_bias = dt_bias;
+    a.init = initial_state;
+    a.cu = cu_seqlens;
+    a.N = N;
+    a.T = T;
+    a.H = H; a.dk = dk; a.dv = dv;
+    a.scale = (scale > 0.f) ? scale : 1.0f / std::sqrt((float)dk);  // NaN also selects the default
+    a.lower_bound = lower_bound;
+    a.l2norm = (flags & KDA_QK_L2NORM) != 0;
+    a.ejk = ejk;
+    a.o = o;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.final_state = final_state;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (has_tokens && chunked && kda::chunked_supported(a)) {
+        const size_t need = kda::chunked_workspace_bytes(N, T, H, dk, dv, cu_seqlens != nullptr);
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        return hip_status(kda::launch_chunked(a, st), "kda_prefill (chunked)");
+    }
+    // token-by-token path; with T == 0 it only carries initial_state to final_state
+    return hip_status(kda::launch_recurrent(a, st), "kda_prefill (recurrent)");
+}
+
+kda_status_t kda_decode_step(const float* q, const float* k, const float* g, const float* v,
+                             const float* beta, const float* a_log, const float* dt_bias,
+                             float scale, float lower_bound, int32_t B, int32_t H, int32_t dk,
+                             int32_t dv, uint32_t flags, float* out, float* S, void* stream)
+{
+    if (flags & ~(KDA_QK_L2NORM | KDA_EJK))
+        return fail(KDA_EINVAL, "kda_decode_step: unsupported flag bits 0x%x", flags & ~(KDA_QK_L2NORM | KDA_EJK));
+    const bool ejk = (flags & KDA_EJK) != 0;
+    if (B < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_EINVAL, "kda_decode_step: bad sizes B=%d H=%d dk=%d dv=%d", B, H, dk, dv);
+    if (B > 0) {
+        if (!q || !k || !v || !beta || !out || !S) return fail(KDA_EINVAL, "kda_decode_step: q, k, v, beta, out and S are required");
+        if (!ejk && (!g || !a_log)) return fail(KDA_EINVAL, "kda_decode_step: KDA mode needs g and a_log");
+    }
+    if (!ejk && !(std::isfinite(lower_bound) && lower_bound <= 0.f))
+        return fail(KDA_EINVAL, "kda_decode_step: lower_bound must be finite and <= 0 (got %g)", (double)lower_bound);
+    if (!dim_ok(dk) || !dim_ok(dv))
+        return fail(KDA_EUNSUPPORTED, "kda_decode_step: dk and dv must be in {16, 32, 64, 128} (got %d, %d)", dk, dv);
+    if ((long long)B * H > 0x7fffffffLL) return fail(KDA_EUNSUPPORTED, "kda_decode_step: B * H too large");
+    if (B == 0) return ok();
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.g = g; a.v = v; a.beta = beta; a.a_log = a_log; a.dt_bias = dt_bias;
+    a.scale = (scale > 0.f) ? scale : 1.0f / std::sqrt((float)dk);
+    a.lower_bound = lower_bound;
+    a.B = B; a.H = H; a.dk = dk; a.dv = dv;
+    a.l2norm = (flags & KDA_QK_L2NORM) != 0;
+    a.ejk = ejk;
+    a.out = out;
+    a.S = S;
+    return hip_status(kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream)), "kda_decode_step");
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// kda_internal.h - argument blocks passed from the C ABI layer to the kernel
+// launchers.  Arguments are already validated when these are filled.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    bool in_bf16;
+    const float* g;        // KDA: [Ntok, H, dk]; EJK: [Ntok, H] or null
+    const float* beta;     // [Ntok, H]
+    const float* a_log;    // [H]
+    const float* dt_bias;  // [dk, H] or null
+    const float* init;     // [N, H, dk, dv] or null
+    const int32_t* cu;     // [N + 1] or null (dense: sequence n = batch row n)
+    int N;                 // number of sequences (dense: B)
+    int T;                 // dense: tokens per sequence; packed: total tokens
+    int H, dk, dv;
+    float scale;
+    float lower_bound;
+    bool l2norm;
+    bool ejk;
+    void* o;               // [Ntok, H, dv]
+    bool out_bf16;
+    float* final_state;    // [N, H, dk, dv] or null
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+struct DecodeArgs {
+    const float* q;
+    const float* k;
+    const float* g;
+    const float* v;
+    const float* beta;
+    const float* a_log;
+    const float* dt_bias;
+    float scale;
+    float lower_bound;
+    int B, H, dk, dv;
+    bool l2norm;
+    bool ejk;
+    float* out;
+    float* S;
+};
+
+// Each launcher returns the hipError_t of its launch (hipGetLastError).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_recurrent(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_chunked(const PrefillArgs& a, hipStream_t stream);
+bool chunked_supported(const PrefillArgs& a);
+size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed);
+
+}  // namespace kda

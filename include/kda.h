@@ -1,0 +1,140 @@
+/*
+ * kda.h - C ABI of libkda.so, a gfx950 (MI355X) implementation of the Kimi
+ * Delta Attention (KDA) gated delta-rule recurrence.
+ *
+ * What is computed.  For every (sequence n, head h) the library carries a
+ * float32 state S in R^{dk x dv} (ejkernel "kernel_delta_attention":
+ * "Memory matrix: [num_heads, head_dim, value_dim] per batch"; AWS Neuron
+ * "KDA TKG Kernel API Reference", parameter S: [B, num_head, dk, dv]).
+ * Per token, from raw inputs (kda_tkg parameters q, k, g, beta, a_log,
+ * dt_bias, scale, lower_bound):
+ *     qh    = scale * q / sqrt(sum q^2 + 1e-6)       (scale folded into the query)
+ *     kh    = k / sqrt(sum k^2 + 1e-6)
+ *     gamma = lower_bound * sigmoid(exp(a_log[h]) * (g + dt_bias[:, h]))   per key channel
+ *     beta  = sigmoid(beta_logit)
+ *     S <- Diag(exp(gamma)) S;  S <- S + beta * kh (v - S^T kh)^T;  o = S^T qh
+ * With KDA_QK_L2NORM clear, qh = scale * q and kh = k.
+ * With KDA_EJK set, the ejkernel ordering of "The core recurrence" is used
+ * instead: g is a per-head scalar log-decay d (NULL means 0), beta is used as
+ * given, and S <- exp(d) S + beta * kh (v - S^T kh)^T with the residual taken
+ * against the undecayed state; o = S^T qh.
+ *
+ * Conventions shared by every entry point.
+ *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major buffer
+ *    owned by the caller.  The library never allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  KDA_OK means the
+ *    work was enqueued on that stream; results are valid once it completes.
+ *  - Host-checkable argument errors return a non-OK status before any HIP
+ *    call is made and enqueue nothing.  Device-side values are not
+ *    inspected: NaN/Inf propagate, and out-of-range cu_seqlens entries are
+ *    clamped to [0, T] (a decreasing pair is an empty sequence) so they can
+ *    never address memory outside the buffers.
+ *  - kda_last_error() returns a thread-local message for the last non-OK
+ *    status of the calling thread.  The library holds no other mutable state
+ *    and is re-entrant; calls on one stream execute in order.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_EINVAL = 1,        /* malformed arguments (null pointer, bad shape, bad flag) */
+    KDA_EUNSUPPORTED = 2,  /* well-formed but outside what the kernels implement      */
+    KDA_EHIP = 3           /* a HIP launch failed; message from hipGetErrorString      */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* flags */
+#define KDA_QK_L2NORM (1u << 0) /* ejkernel use_qk_l2norm (its default is on)          */
+#define KDA_CHUNKED   (1u << 1) /* ejkernel use_chunked: chunk-parallel algorithm;     */
+                                /* clear = token-by-token recurrent scan               */
+#define KDA_EJK       (1u << 2) /* ejkernel ordering with a scalar per-head decay      */
+
+/*
+ * kda_prefill - run the recurrence over whole sequences (ejkernel
+ * "kernel_delta_attention" run(): query, key, value, beta, decay,
+ * initial_state, softmax_scale, chunk_size, use_qk_l2norm, use_chunked,
+ * return_state; varlen packing as in ejkernel "recurrent" run(): cu_seqlens).
+ *
+ * Shapes (dense batch): q, k [B, T, H, dk]; v [B, T, H, dv]; o [B, T, H, dv];
+ * states [B, H, dk, dv].  With cu_seqlens ([num_seqs + 1] int32, device,
+ * cu[0] = 0, non-decreasing, cu[num_seqs] = T) the batch must be B = 1 and
+ * sequence n covers tokens [cu[n], cu[n+1]); states are [num_seqs, H, dk, dv]
+ * and every sequence restarts from its own initial state.
+ *
+ *   q, k, v        in_dtype (KDA_BF16 or KDA_F32)
+ *   g              KDA: raw gate [B, T, H, dk] float32 (required);
+ *                  EJK: log-decay [B, T, H] float32, NULL = 0 (no decay)
+ *   beta           KDA: logits [B, T, H]; EJK: activated [B, T, H]; float32
+ *   a_log          [H] float32 (KDA; ignored for EJK; required for KDA)
+ *   dt_bias        [dk, H] float32 (KDA; NULL = 0)
+ *   initial_state  [N, H, dk, dv] float32, NULL = zeros
+ *   scale          query scale; <= 0 or NaN selects 1/sqrt(dk)
+ *   lower_bound    KDA gate bound, finite and <= 0; the chunked path needs
+ *                  lower_bound >= -5 (the kda_tkg documented range [-5, 0])
+ *   chunk_size     64 (the ejkernel default) when KDA_CHUNKED is set
+ *   o              out_dtype; KDA_BF16 output needs bf16 input
+ *   final_state    [N, H, dk, dv] float32 or NULL (return_state = False);
+ *                  may alias initial_state exactly (in-place carry)
+ *   workspace      device scratch of kda_prefill_workspace_bytes() bytes,
+ *                  may be NULL when that size is 0
+ *
+ * Dimensions: dk, dv in {16, 32, 64, 128} (kda_tkg: dk <= 128).  B = 0 or
+ * T = 0 is a no-op, except that final_state then receives initial_state (or
+ * zeros).  Routing: KDA_CHUNKED with bf16 inputs, dk in {64, 128} and dv a
+ * multiple of 32 runs the MFMA chunked kernel; every other combination runs
+ * the exact token-by-token kernel, which computes the same function.
+ */
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                         const float* g, const float* beta, const float* a_log,
+                         const float* dt_bias, const float* initial_state,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                         int32_t H, int32_t dk, int32_t dv, float scale, float lower_bound,
+                         int32_t chunk_size, uint32_t flags, void* o, kda_dtype_t out_dtype,
+                         float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Device workspace kda_prefill needs for these arguments (0 = none). */
+size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                                   int32_t dk, int32_t dv, uint32_t flags);
+
+/*
+ * kda_decode_step - advance the recurrence by exactly one token for each of
+ * B requests (AWS Neuron "KDA TKG Kernel API Reference", kda_tkg: same
+ * tensors, layouts and in-place state; scale and lower_bound are host floats
+ * here instead of [1, 1] device tensors).  All float32:
+ *   q, k, g   [B, dk, H] raw (EJK: g is the log-decay [B, 1, H], NULL = 0)
+ *   v         [B, H, dv]
+ *   beta      [B, 1, H] logits (EJK: activated)
+ *   a_log     [1, H] (ignored for EJK);  dt_bias [dk, H] (NULL = 0)
+ *   out       [B, H, dv], caller-allocated, written
+ *   S         [B, H, dk, dv] IN/OUT: read, then overwritten with the new state
+ * flags: KDA_QK_L2NORM and KDA_EJK (KDA_CHUNKED is meaningless here and is
+ * rejected).  dk, dv in {16, 32, 64, 128}; B = 0 is a no-op.
+ */
+kda_status_t kda_decode_step(const float* q, const float* k, const float* g, const float* v,
+                             const float* beta, const float* a_log, const float* dt_bias,
+                             float scale, float lower_bound, int32_t B, int32_t H, int32_t dk,
+                             int32_t dv, uint32_t flags, float* out, float* S, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */
