@@ -1,0 +1,148 @@
+"""MFMA chunked prefill (bf16 q/k/v, fp32 gates and state) against the oracle.
+
+Bar: relative L2 <= 2e-2 for o and the final state (bf16-input path).
+Packed varlen runs must equal per-sequence runs bitwise, and a split at a
+chunk boundary with state passthrough must equal the unsplit run bitwise."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_90_amd import workloads
+from tests._common import prefill_gpu, prefill_oracle, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _check(inp, units=None, **kw):
+    o, s = prefill_gpu(inp, **kw)
+    ro, rs = prefill_oracle(inp, units=units, use_qk_l2norm=kw.get("use_qk_l2norm", True))
+    if units is not None:
+        H = inp.q.shape[2]
+        sel_o = [(u // H, u % H) for u in units]
+        if inp.cu_seqlens is None:
+            o_s = np.stack([o[n, :, h] for n, h in sel_o])
+            ro_s = np.stack([ro[n, :, h] for n, h in sel_o])
+        else:
+            cu = inp.cu_seqlens
+            o_s = np.concatenate([o[0, cu[n]:cu[n + 1], h].ravel() for n, h in sel_o])
+            ro_s = np.concatenate([ro[0, cu[n]:cu[n + 1], h].ravel() for n, h in sel_o])
+        s_s = np.stack([s[n, h] for n, h in sel_o])
+        rs_s = np.stack([rs[n, h] for n, h in sel_o])
+    else:
+        o_s, ro_s, s_s, rs_s = o, ro, s, rs
+    eo, es = rel_l2(o_s, ro_s), rel_l2(s_s, rs_s)
+    say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+    assert eo <= TOL and es <= TOL, (eo, es)
+    return o, s
+
+
+@pytest.mark.parametrize("T", [64, 200, 1, 130])
+def test_chunked_ragged_small(T):
+    inp = workloads.prefill_inputs(2, T, 3, 128, 128, seed=100 + T, init_state=True)
+    say("chunked B=2 T=%d H=3" % T)
+    _check(inp)
+
+
+@pytest.mark.parametrize("dv", [32, 64])
+def test_chunked_dv_tiles(dv):
+    inp = workloads.prefill_inputs(1, 150, 2, 128, dv, seed=200 + dv, init_state=True)
+    say("chunked dv=%d" % dv)
+    _check(inp)
+
+
+def test_chunked_fp32_output_and_no_l2norm():
+    import torch
+    inp = workloads.prefill_inputs(2, 96, 2, 128, 64, seed=300, scale=0.05)
+    say("chunked fp32 out, l2norm on")
+    _check(inp, out_dtype=torch.float32)
+    inp2 = workloads.prefill_inputs(1, 80, 2, 128, 32, seed=301, scale=0.02)
+    inp2.q *= 0.1
+    inp2.k *= 0.1
+    inp2.q = workloads.round_to_bf16(inp2.q)
+    inp2.k = workloads.round_to_bf16(inp2.k)
+    say("chunked no l2norm")
+    _check(inp2, use_qk_l2norm=False)
+
+
+def test_chunked_strongest_decay():
+    """lower_bound = -5 with saturated gates: in-chunk log-decay near -320."""
+    inp = workloads.prefill_inputs(1, 256, 2, 128, 64, seed=400, init_state=True)
+    inp.g = (inp.g + 20.0).astype(np.float32)
+    say("chunked saturated gates")
+    _check(inp)
+    inp.g = (inp.g - 40.0).astype(np.float32)   # sigma ~ 0: almost no decay
+    say("chunked almost no decay")
+    _check(inp)
+
+
+def test_chunked_determinism():
+    inp = workloads.prefill_inputs(2, 300, 4, 128, 128, seed=500, init_state=True)
+    say("chunked determinism")
+    o1, s1 = prefill_gpu(inp)
+    o2, s2 = prefill_gpu(inp)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_chunked_varlen_bitwise_and_zero_length():
+    lens = [130, 0, 64, 1, 257, 63]
+    inp = workloads.prefill_inputs(1, 0, 3, 128, 64, seed=600, lengths=lens, init_state=True)
+    say("chunked varlen", lens)
+    o, s = _check(inp)
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if a == b:
+            np.testing.assert_array_equal(s[n], inp.initial_state[n])
+            continue
+        sub = workloads.PrefillInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b], inp.g[:, a:b],
+                                      inp.beta[:, a:b], inp.a_log, inp.dt_bias,
+                                      inp.initial_state[n:n + 1], None, inp.dtype, inp.scale,
+                                      inp.lower_bound)
+        on, sn = prefill_gpu(sub)
+        np.testing.assert_array_equal(o[:, a:b], on)
+        np.testing.assert_array_equal(s[n], sn[0])
+
+
+def test_chunked_split_at_chunk_boundary_is_bitwise():
+    inp = workloads.prefill_inputs(2, 384, 2, 128, 128, seed=700, init_state=True)
+    say("chunked split at 192")
+    o, s = prefill_gpu(inp)
+    cut = 192
+
+    def part(a, b, s0):
+        return workloads.PrefillInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b],
+                                       inp.g[:, a:b], inp.beta[:, a:b], inp.a_log, inp.dt_bias,
+                                       s0, None, inp.dtype, inp.scale, inp.lower_bound)
+
+    o1, s1 = prefill_gpu(part(0, cut, inp.initial_state))
+    o2, s2 = prefill_gpu(part(cut, 384, s1))
+    np.testing.assert_array_equal(np.concatenate([o1, o2], axis=1), o)
+    np.testing.assert_array_equal(s2, s)
+
+
+def test_chunked_matches_recurrent_kernel():
+    import torch
+    inp = workloads.prefill_inputs(1, 333, 2, 128, 128, seed=800, init_state=True)
+    say("chunked vs recurrent")
+    oc, sc = prefill_gpu(inp, out_dtype=torch.float32)
+    orc, src = prefill_gpu(inp, use_chunked=False, out_dtype=torch.float32)
+    assert rel_l2(oc, orc) <= TOL and rel_l2(sc, src) <= TOL
+
+
+def test_chunked_full_size_b4_t4096_h16_sampled():
+    """Launch shape of the benchmark; the oracle checks three (batch, head) items."""
+    inp = workloads.prefill_b4_t4096_h16_d128()
+    say("chunked full size B=4 T=4096 H=16")
+    _check(inp, units=[0, 37, 63])
+
+
+def test_chunked_varlen_8seq_sampled():
+    inp = workloads.prefill_varlen_8seq_h32_d128()
+    say("chunked varlen 8 seqs", inp.meta["lengths"])
+    H = 32
+    # the longest sequence's first and last head, and one head of the shortest
+    lens = inp.meta["lengths"]
+    nl, ns = int(np.argmax(lens)), int(np.argmin(lens))
+    _check(inp, units=[nl * H, nl * H + H - 1, ns * H + 5])
