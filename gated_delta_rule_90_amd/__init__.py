@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
                               i32, i32, i32, f32, f32, i32, u32, vp, ctypes.c_int, fp, vp,
                               ctypes.c_size_t, vp]
     L.kda_prefill.restype = ctypes.c_int
-    L.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, u32]
+    L.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, u32]
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_decode_step.argtypes = [fp, fp, fp, fp, fp, fp, fp, f32, f32, i32, i32, i32, i32, u32,
                                   fp, fp, vp]
@@ -95,8 +95,8 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def prefill_workspace_bytes(num_seqs, B, T, H, dk, dv, flags) -> int:
-    return int(lib().kda_prefill_workspace_bytes(num_seqs, B, T, H, dk, dv, flags))
+def prefill_workspace_bytes(num_seqs, B, T, H, dk, dv, flags, in_dtype=BF16) -> int:
+    return int(lib().kda_prefill_workspace_bytes(num_seqs, B, T, H, dk, dv, in_dtype, flags))
 
 
 def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_seqlens=None, *,
@@ -155,7 +155,8 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
     flags = (QK_L2NORM if use_qk_l2norm else 0) | (CHUNKED if use_chunked else 0) | \
         (EJK if ejk else 0)
     nseq = N if cu_seqlens is not None else 0
-    wsb = prefill_workspace_bytes(nseq, B, T, H, dk, dv, flags) if use_chunked else 0
+    idt = BF16 if q.dtype == torch.bfloat16 else F32
+    wsb = prefill_workspace_bytes(nseq, B, T, H, dk, dv, flags, idt)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb > 0 else None
     sc = -1.0 if scale is None else float(scale)
     _check(lib().kda_prefill(

@@ -49,12 +49,19 @@ int kda_abi_version(void) { return KDA_ABI_VERSION; }
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk,
-                                   int32_t dv, uint32_t flags)
+                                   int32_t dv, kda_dtype_t in_dtype, uint32_t flags)
 {
-    (void)flags;
     if (B < 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    if (!(flags & KDA_CHUNKED) || (flags & KDA_EJK) || in_dtype != KDA_BF16) return 0;
     const bool packed = num_seqs > 0 && B == 1;
     const int N = packed ? num_seqs : B;
+    kda::PrefillArgs probe{};
+    probe.in_bf16 = true;
+    probe.dk = dk;
+    probe.dv = dv;
+    probe.g = reinterpret_cast<const float*>(1);
+    probe.a_log = reinterpret_cast<const float*>(1);
+    if (!kda::chunked_supported(probe)) return 0;
     return kda::chunked_workspace_bytes(N, T, H, dk, dv, packed);
 }
 
@@ -94,8 +101,8 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
         return fail(KDA_EUNSUPPORTED, "kda_prefill: bf16 output needs bf16 input");
     if (chunked && chunk_size != 64)
         return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path implements chunk_size 64 (got %d)", chunk_size);
-    if (chunked && !ejk && lower_bound < -5.0f)
-        return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path needs lower_bound >= -5 (got %g)", (double)lower_bound);
+    if (H > 65535 || N > 65535)
+        return fail(KDA_EUNSUPPORTED, "kda_prefill: H and the number of sequences must be <= 65535 (got %d, %d)", H, N);
     if (N == 0) return ok();
     if (!has_tokens && !final_state) return ok();
 
@@ -120,6 +127,8 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (has_tokens && chunked && kda::chunked_supported(a)) {
+        if (lower_bound < -5.0f)
+            return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path needs lower_bound >= -5 (got %g)", (double)lower_bound);
         const size_t need = kda::chunked_workspace_bytes(N, T, H, dk, dv, cu_seqlens != nullptr);
         if (need > 0 && (!workspace || workspace_bytes < need))
             return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);

@@ -84,7 +84,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
             sh_red[wave][2] = r2;
         }
     }
-    __syncthreads();
+    lds_barrier();
     float sqq = 0.f, skk = 0.f, sqk = 0.f;
 #pragma unroll
     for (int w = 0; w < NWAVES; ++w) {
@@ -107,7 +107,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
         sh_k[t] = ki * nk;
         if (!EJK) sh_alpha[t] = expf(lower_bound * sigmoid_f(expf(a_log[h]) * zi));
     }
-    __syncthreads();
+    lds_barrier();
 
     // 3. one sweep: decay (KDA) and the two column reductions
     float4 u = make_float4(0.f, 0.f, 0.f, 0.f), p = u;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
             sh_uv[wave][cg][0] = u;
             sh_uv[wave][cg][1] = p;
         }
-        __syncthreads();
+        lds_barrier();
         u = sh_uv[0][cg][0];
         p = sh_uv[0][cg][1];
 #pragma unroll

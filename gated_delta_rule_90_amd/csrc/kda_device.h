@@ -40,6 +40,17 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// Workgroup barrier that orders LDS traffic only: it waits for this wave's
+// LDS operations and then for every wave of the workgroup.  Unlike
+// __syncthreads() it does not drain the vector memory counter, so global loads
+// issued ahead (prefetch) and global stores stay in flight across it.  Only
+// valid where no wave reads global memory written by another wave of the
+// same workgroup before the kernel ends.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float4 fma4(float a, float4 b, float4 c)
 {
     return make_float4(fmaf(a, b.x, c.x), fmaf(a, b.y, c.y), fmaf(a, b.z, c.z), fmaf(a, b.w, c.w));

@@ -80,8 +80,9 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *   dt_bias        [dk, H] float32 (KDA; NULL = 0)
  *   initial_state  [N, H, dk, dv] float32, NULL = zeros
  *   scale          query scale; <= 0 or NaN selects 1/sqrt(dk)
- *   lower_bound    KDA gate bound, finite and <= 0; the chunked path needs
- *                  lower_bound >= -5 (the kda_tkg documented range [-5, 0])
+ *   lower_bound    KDA gate bound, finite and <= 0; when the call takes the
+ *                  MFMA chunked kernel it must be >= -5 (the kda_tkg documented
+ *                  range [-5, 0]), else KDA_EUNSUPPORTED
  *   chunk_size     64 (the ejkernel default) when KDA_CHUNKED is set
  *   o              out_dtype; KDA_BF16 output needs bf16 input
  *   final_state    [N, H, dk, dv] float32 or NULL (return_state = False);
@@ -89,7 +90,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *   workspace      device scratch of kda_prefill_workspace_bytes() bytes,
  *                  may be NULL when that size is 0
  *
- * Dimensions: dk, dv in {16, 32, 64, 128} (kda_tkg: dk <= 128).  B = 0 or
+ * Dimensions: dk, dv in {16, 32, 64, 128} (kda_tkg: dk <= 128); H and the
+ * number of sequences at most 65535.  B = 0 or
  * T = 0 is a no-op, except that final_state then receives initial_state (or
  * zeros).  Routing: KDA_CHUNKED with bf16 inputs, dk in {64, 128} and dv a
  * multiple of 32 runs the MFMA chunked kernel; every other combination runs
@@ -104,9 +106,15 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
                          float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Device workspace kda_prefill needs for these arguments (0 = none). */
+/* Device workspace (bytes) kda_prefill needs for these arguments; 0 = none.
+ * Only the chunked MFMA path uses it: per (chunk, head) it holds the
+ * state-independent operands of that chunk (64.5 KiB), plus the chunk
+ * offsets of packed sequences (num_seqs > 0 with B == 1 means packed).  The
+ * caller allocates it (the library never allocates); it must not be shared
+ * by calls that may run concurrently. */
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H,
-                                   int32_t dk, int32_t dv, uint32_t flags);
+                                   int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                                   uint32_t flags);
 
 /*
  * kda_decode_step - advance the recurrence by exactly one token for each of

@@ -135,8 +135,13 @@ def test_decode_empty_batch_is_a_no_op():
 
 def test_workspace_query_is_host_only():
     n = kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.QK_L2NORM | kda.CHUNKED)
-    assert n >= 0
+    assert n == 4 * 64 * 16 * 66048            # one 64.5 KiB record per (chunk, head)
+    packed = kda.prefill_workspace_bytes(8, 1, 32768, 32, 128, 128, kda.CHUNKED)
+    assert packed == 256 + (512 + 8) * 32 * 66048
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 100, 128, kda.CHUNKED) == 0
+    assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.QK_L2NORM) == 0
+    assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED, kda.F32) == 0
+    assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED | kda.EJK) == 0
 
 
 def test_error_message_is_thread_local():
