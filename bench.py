@@ -65,19 +65,24 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def _counter_traffic(name, src_hash, bytes_per_launch):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"{name}_pmc.json")
+def _counter_traffic(name, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary
+    (profiles/<name>_pmc.txt, "key: value" lines), if it was taken on the
+    current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}_pmc.txt")
     if not os.path.exists(p):
         return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_hash") != src_hash:
+        return None
     try:
-        d = json.load(open(p))
-    except ValueError:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
         return None
-    if d.get("src_hash") != src_hash:
-        return None
-    return d.get("hbm_bytes_per_launch")
 
 
 def bench_decode(steps, warmup, nbuf=5):
@@ -114,7 +119,7 @@ def bench_decode(steps, warmup, nbuf=5):
     nbytes = decode_bytes(B, H, dk, dv)
     achieved = nbytes / (ms * 1e-3) / 1e9
     sh = _src_hash("kda_decode.hip")
-    traffic = _counter_traffic("decode_b64_h32_d128", sh, nbytes)
+    traffic = _counter_traffic("decode_b64_h32_d128", sh)
     return inp, {
         "ms": ms, "wall_s": wall, "steps_per_s": 1e3 / ms, "bytes": nbytes,
         "flops": decode_flops(B, H, dk, dv),
@@ -189,6 +194,18 @@ def bench_prefill(steps, warmup):
             "achieved_TFs": round(tfs, 2)}
 
 
+def copy_calibration(mib=256):
+    """One device-to-device copy of a known size (read and write `mib` MiB each),
+    so that profiler byte counters can be scaled against a known amount."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +214,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calib", action="store_true",
+                    help="run a 256 MiB device copy first (profiler counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -206,6 +225,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calib:
+        copy_calibration()
     inp, dec = bench_decode(args.steps, args.warmup)
     line = {
         "metric": METRIC,

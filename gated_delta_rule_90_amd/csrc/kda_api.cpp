@@ -156,7 +156,7 @@ kda_status_t kda_decode_step(const float* q, const float* k, const float* g, con
         return fail(KDA_EINVAL, "kda_decode_step: lower_bound must be finite and <= 0 (got %g)", (double)lower_bound);
     if (!dim_ok(dk) || !dim_ok(dv))
         return fail(KDA_EUNSUPPORTED, "kda_decode_step: dk and dv must be in {16, 32, 64, 128} (got %d, %d)", dk, dv);
-    if ((long long)B * H > 0x7fffffffLL) return fail(KDA_EUNSUPPORTED, "kda_decode_step: B * H too large");
+    if ((long long)((B + 7) / 8) * 8 * H > 0x7fffffffLL) return fail(KDA_EUNSUPPORTED, "kda_decode_step: B * H too large");
     if (B == 0) return ok();
     kda::DecodeArgs a{};
     a.q = q; a.k = k; a.g = g; a.v = v; a.beta = beta; a.a_log = a_log; a.dt_bias = dt_bias;

@@ -49,8 +49,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;        // chunk length
 constexpr int DK = 128;      // key dimension handled by the MFMA path
-constexpr int DVT = 32;      // state columns per scan workgroup
-constexpr int NJB = DVT / 16;
+constexpr int DV_MULT = 32;  // the MFMA path needs dv to be a multiple of this
 constexpr int NTHREADS = 256;
 
 // ---- workspace record of one (chunk, head), bf16 operands in k-slices of 32:
@@ -452,12 +451,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         *reinterpret_cast<float4*>(AB + r * SA + 16 * J + 4 * g4) = make_float4(a4[0], a4[1], a4[2], a4[3]);
         st4bf(gP + ksl(C, r, 16 * J + 4 * g4), p4[0], p4[1], p4[2], p4[3]);
     }
-    // upper blocks of P that the 32-wide k-steps read: (0,1) and (2,3)
-    if (wave == 0 || wave == 2) {
-        const int r = 16 * wave + (lane >> 2);
-        const int s = 16 * wave + 16 + 4 * (lane & 3);
-        st4bf(gP + ksl(C, r, s), 0.f, 0.f, 0.f, 0.f);
-    }
     lds_barrier();
 
     // ---------------- phase 3: T = (I + A)^-1, T' = T diag(beta)
@@ -563,24 +556,38 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 st4bf(gW + ksl(C, 16 * I + l16, 16 * ib + 4 * g4), acc[0], acc[1], acc[2], acc[3]);
             }
         }
-        // T' [64][64] -> k-sliced: thread writes 16 elements (two 16-byte pieces)
+        // T' [64][64] -> k-sliced, thread = (row, 16-column block); blocks above the
+        // diagonal are written as zeros (the scan always runs both k-slices)
         const int r = tid >> 2;
         const int s0 = 16 * (tid & 3);
+        const bool upper = (tid & 3) > (r >> 4);
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {
-            const uint4 val = *reinterpret_cast<const uint4*>(TP + r * SW + s0 + 8 * h8);
+            uint4 val = *reinterpret_cast<const uint4*>(TP + r * SW + s0 + 8 * h8);
+            if (upper) val = make_uint4(0u, 0u, 0u, 0u);
             *reinterpret_cast<uint4*>(gTP + ksl(C, r, s0 + 8 * h8)) = val;
+            if (upper) *reinterpret_cast<uint4*>(gP + ksl(C, r, s0 + 8 * h8)) = val;
         }
     }
 }
 
 // ------------------------------------------------------------------------
-// chunk_scan: one workgroup per (sequence, head, 32-column dv tile)
-constexpr int S_ST = 0;                              // S0^T bf16 [DVT][SR]
-constexpr int S_UT = S_ST + DVT * SR * 2;            // U^T  bf16 [DVT][SW]
-constexpr int S_VT = S_UT + DVT * SW * 2;            // V^T  bf16 [DVT][SW]
-constexpr int SCAN_LDS = S_VT + DVT * SW * 2;
+// chunk_scan: one workgroup (4 waves) per (sequence, head, tile of 16*NJB state
+// columns).  Wave w owns rows [16w, 16w+16) of U and O and state rows
+// [32w, 32w+32); every wave covers all NJB 16-column blocks of the tile, so
+// each operand fragment is loaded once per workgroup and reused NJB times.
+template <int NJB>
+struct ScanShape {
+    static constexpr int DVT = 16 * NJB;
+    static constexpr int ST_OFF = 0;                                // S0^T bf16 [DVT][SR]
+    static constexpr int UT_OFF = ST_OFF + DVT * SR * 2;            // U^T  bf16 [DVT][SW]
+    static constexpr int VT_OFF = UT_OFF + DVT * SW * 2;            // V^T  bf16 [DVT][SW]
+    static constexpr int LDS = VT_OFF + DVT * SW * 2;
+    static constexpr int VSEG = C * DVT / 8 / NTHREADS;             // 16-byte V pieces per thread
+    static_assert(VSEG >= 1, "V tile split");
+};
 
+template <int NJB>
 struct Frags {
     bf16x8_t tp[2];      // T' rows of this wave's 16-row block, k-slices 0..1
     bf16x8_t w[4];       // W  rows, k-slices 0..3
@@ -588,11 +595,12 @@ struct Frags {
     bf16x8_t p[2];       // P  rows, k-slices 0..1
     bf16x8_t kc[2][2];   // Kc^T rows [32w + 16ib, +16), k-slices 0..1
     float4 ec[2];        // e^{b_C} for the 4 state rows of each ib
-    uint4 v;             // 8 values of the V tile (one row segment per thread)
+    uint4 v[ScanShape<NJB>::VSEG];   // V tile pieces
 };
 
-__device__ __forceinline__ void load_frags(Frags& f, const unsigned char* rec, const bf16_t* v, int c0, int len,
-                                           int H, int h, int DV, int j0, int wave, int lane, int tid)
+template <int NJB>
+__device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* rec, const bf16_t* v, int c0,
+                                           int len, int H, int h, int DV, int j0, int wave, int lane, int tid)
 {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int fo = l16 * 32 + 8 * g4;   // lane offset inside a 16x32 fragment
@@ -618,23 +626,30 @@ __device__ __forceinline__ void load_frags(Frags& f, const unsigned char* rec, c
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
         f.ec[ib] = *reinterpret_cast<const float4*>(EC + 32 * wave + 16 * ib + 4 * g4);
-    // V tile row s, 8 columns; rows past the sequence read row 0 and are zeroed on use
-    const int s = tid / (DVT / 8);
-    const int jj = (tid % (DVT / 8)) * 8;
-    const int ss = (s < len) ? s : 0;
-    f.v = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * H + h) * DV + j0 + jj);
+    // V tile: row s, 8 columns per piece; rows past the sequence read row 0 and are zeroed on use
+    constexpr int DVT = ScanShape<NJB>::DVT;
+#pragma unroll
+    for (int it = 0; it < ScanShape<NJB>::VSEG; ++it) {
+        const int seg = tid + it * NTHREADS;
+        const int s = seg / (DVT / 8);
+        const int jj = (seg % (DVT / 8)) * 8;
+        const int ss = (s < len) ? s : 0;
+        f.v[it] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * H + h) * DV + j0 + jj);
+    }
 }
 
-template <typename Tout>
+template <int NJB, typename Tout>
 __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ init, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ off, int N, int T, int H, int DV, const unsigned char* __restrict__ ws,
     Tout* __restrict__ o, float* __restrict__ final_state)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SCAN_LDS];
-    uint16_t* STB = reinterpret_cast<uint16_t*>(smem + S_ST);
-    uint16_t* UT = reinterpret_cast<uint16_t*>(smem + S_UT);
-    uint16_t* VT = reinterpret_cast<uint16_t*>(smem + S_VT);
+    using Sh = ScanShape<NJB>;
+    constexpr int DVT = Sh::DVT;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::LDS];
+    uint16_t* STB = reinterpret_cast<uint16_t*>(smem + Sh::ST_OFF);
+    uint16_t* UT = reinterpret_cast<uint16_t*>(smem + Sh::UT_OFF);
+    uint16_t* VT = reinterpret_cast<uint16_t*>(smem + Sh::VT_OFF);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -642,7 +657,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
 
-    // XCD-aware placement: the dv tiles of one (sequence, head) share an XCD and its L2
+    // XCD-aware placement: the column tiles of one (sequence, head) share an XCD and its L2
     const int ntiles = DV / DVT;
     const int units = N * H;
     const int xcd = blockIdx.x & 7;
@@ -659,7 +674,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
     const int nch = (t_end - t_begin + C - 1) / C;
     const int slot0 = off ? off[n] : n * ((T + C - 1) / C);
 
-    // state: wave w owns rows i in [32w, 32w+32) as 2 x NJB accumulator tiles
+    // state: wave w owns rows i in [32w, 32w+32) x all DVT columns
     f32x4_t S[2][NJB];
     const size_t soff = (size_t)unit * DK * DV;
 #pragma unroll
@@ -679,10 +694,10 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
             st4bf(STB + (16 * jb + l16) * SR + 32 * wave + 16 * ib + 4 * g4, S[ib][jb][0], S[ib][jb][1],
                   S[ib][jb][2], S[ib][jb][3]);
 
-    Frags cur, nxt;
+    Frags<NJB> cur, nxt;
     if (nch > 0)
-        load_frags(cur, ws + ((size_t)slot0 * H + h) * REC_BYTES, v, t_begin, min(C, t_end - t_begin), H, h, DV,
-                   j0, wave, lane, tid);
+        load_frags<NJB>(cur, ws + ((size_t)slot0 * H + h) * REC_BYTES, v, t_begin, min(C, t_end - t_begin), H, h,
+                        DV, j0, wave, lane, tid);
     for (int c = 0; c < nch; ++c) {
         const int c0 = t_begin + c * C;
         const int len = min(C, t_end - c0);
@@ -692,15 +707,18 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         if (c + 1 < nch) {
             const int c1 = c0 + C;
-            load_frags(nxt, ws + ((size_t)(slot0 + c + 1) * H + h) * REC_BYTES, v, c1, min(C, t_end - c1), H, h, DV,
-                       j0, wave, lane, tid);
+            load_frags<NJB>(nxt, ws + ((size_t)(slot0 + c + 1) * H + h) * REC_BYTES, v, c1, min(C, t_end - c1), H,
+                            h, DV, j0, wave, lane, tid);
         }
         // V tile, transposed: VT[j][s]
-        {
-            const int s = tid / (DVT / 8);
-            const int jj = (tid % (DVT / 8)) * 8;
+#pragma unroll
+        for (int it = 0; it < Sh::VSEG; ++it) {
+            const int seg = tid + it * NTHREADS;
+            const int s = seg / (DVT / 8);
+            const int jj = (seg % (DVT / 8)) * 8;
             const bool in = s < len;
-            const uint32_t w4[4] = {in ? cur.v.x : 0u, in ? cur.v.y : 0u, in ? cur.v.z : 0u, in ? cur.v.w : 0u};
+            const uint32_t w4[4] = {in ? cur.v[it].x : 0u, in ? cur.v[it].y : 0u, in ? cur.v[it].z : 0u,
+                                    in ? cur.v[it].w : 0u};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 VT[(jj + 2 * e) * SW + s] = (uint16_t)(w4[e] & 0xffff);
@@ -709,39 +727,44 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
         }
         lds_barrier();
 
-        // U = T' V - W S0 (rows of this wave's block), stored as U^T[j][s]
-        const int I = wave;
+        // U = T' V - W S0 and the S0 part of O^T = S0^T Qg^T, per 16-column block
+        f32x4_t O[NJB];
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            f32x4_t u = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            bf16x8_t sb[4], vt[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks == 1 && I < 2) continue;
-                u = mfma32(cur.tp[ks], ld8(VT, SW, 16 * jb + l16, 32 * ks + 8 * g4), u);
+            for (int ks = 0; ks < 4; ++ks) sb[ks] = ld8(STB, SR, 16 * jb + l16, 32 * ks + 8 * g4);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) vt[ks] = ld8(VT, SW, 16 * jb + l16, 32 * ks + 8 * g4);
+            f32x4_t u = f32x4_t{0.f, 0.f, 0.f, 0.f}, wsum = u, oa = u;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                wsum = mfma32(cur.w[ks], sb[ks], wsum);
+                oa = mfma32(sb[ks], cur.qg[ks], oa);
+                if (ks < 2) u = mfma32(cur.tp[ks], vt[ks], u);
             }
-            f32x4_t wsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                wsum = mfma32(cur.w[ks], ld8(STB, SR, 16 * jb + l16, 32 * ks + 8 * g4), wsum);
-            u = u - wsum;
-            st4bf(UT + (16 * jb + l16) * SW + 16 * I + 4 * g4, u[0], u[1], u[2], u[3]);
+            O[jb] = oa;
+            u = u - wsum;   // u[e] = U[s = 16w + 4*g4 + e][j = 16jb + l16]
+            st4bf(UT + (16 * jb + l16) * SW + 16 * wave + 4 * g4, u[0], u[1], u[2], u[3]);
         }
         lds_barrier();
 
-        // O^T = S0^T Qg^T + U^T P^T  (rows of this wave's block)
+        // O^T += U^T P^T;  S = Diag(e^{b_C}) S0 + Kc^T U
+        const int r = 16 * wave + l16;
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            bf16x8_t ut[2];
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mfma32(ld8(STB, SR, 16 * jb + l16, 32 * ks + 8 * g4), cur.qg[ks], acc);
+            for (int ks = 0; ks < 2; ++ks) ut[ks] = ld8(UT, SW, 16 * jb + l16, 32 * ks + 8 * g4);
+            f32x4_t acc = O[jb];
+            f32x4_t d0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, d1 = d0;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if (ks == 1 && I < 2) continue;
-                acc = mfma32(ld8(UT, SW, 16 * jb + l16, 32 * ks + 8 * g4), cur.p[ks], acc);
+                acc = mfma32(ut[ks], cur.p[ks], acc);
+                d0 = mfma32(cur.kc[0][ks], ut[ks], d0);
+                d1 = mfma32(cur.kc[1][ks], ut[ks], d1);
             }
-            // acc[e] = O[r = 16I + l16][j = 16jb + 4*g4 + e]
-            const int r = 16 * I + l16;
+            // acc[e] = O[r = 16w + l16][j = 16jb + 4*g4 + e]
             if (r < len) {
                 Tout* op = o + ((size_t)(c0 + r) * H + h) * DV + j0 + 16 * jb + 4 * g4;
                 if constexpr (sizeof(Tout) == 2) {
@@ -750,30 +773,18 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
                     *reinterpret_cast<float4*>(op) = make_float4(acc[0], acc[1], acc[2], acc[3]);
                 }
             }
-        }
-        // S = Diag(e^{b_C}) S0 + Kc^T U
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const float4 ec = cur.ec[ib];
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb) {
-                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    acc = mfma32(cur.kc[ib][ks], ld8(UT, SW, 16 * jb + l16, 32 * ks + 8 * g4), acc);
-                S[ib][jb][0] = fmaf(ec.x, S[ib][jb][0], acc[0]);
-                S[ib][jb][1] = fmaf(ec.y, S[ib][jb][1], acc[1]);
-                S[ib][jb][2] = fmaf(ec.z, S[ib][jb][2], acc[2]);
-                S[ib][jb][3] = fmaf(ec.w, S[ib][jb][3], acc[3]);
+            for (int e = 0; e < 4; ++e) {
+                S[0][jb][e] = fmaf(cur.ec[0][e], S[0][jb][e], d0[e]);
+                S[1][jb][e] = fmaf(cur.ec[1][e], S[1][jb][e], d1[e]);
             }
-        }
-        lds_barrier();
+            // S0^T is only read before the previous barrier, so the new state's bf16
+            // copy can go in now; the next chunk's first barrier publishes it.
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
+            for (int ib = 0; ib < 2; ++ib)
                 st4bf(STB + (16 * jb + l16) * SR + 32 * wave + 16 * ib + 4 * g4, S[ib][jb][0], S[ib][jb][1],
                       S[ib][jb][2], S[ib][jb][3]);
+        }
         if (c + 1 < nch) cur = nxt;
     }
 
@@ -800,6 +811,18 @@ size_t max_slots(int N, int T, bool packed)
     return (size_t)N * (size_t)((T + C - 1) / C);
 }
 
+// 16-column blocks per scan workgroup: wide tiles load each chunk's operands
+// fewer times, narrow tiles put more workgroups on the chip.
+int scan_tile_blocks(int N, int H, int dv)
+{
+    const int units = N * H;
+    int njb = 2;
+    if (units >= 192) njb = 8;
+    else if (units >= 48) njb = 4;
+    while (njb > 2 && dv % (16 * njb) != 0) njb >>= 1;
+    return njb;
+}
+
 template <typename Tout>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 {
@@ -823,12 +846,22 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int ntiles = a.dv / DVT;
     const int units = a.N * a.H;
     const unsigned groups = (unsigned)((units + 7) / 8);
-    hipLaunchKernelGGL((chunk_scan_kernel<Tout>), dim3(groups * 8u * (unsigned)ntiles), dim3(NTHREADS), 0, stream,
-                       static_cast<const bf16_t*>(a.v), a.init, a.cu, off, a.N, a.T, a.H, a.dv, recs,
-                       static_cast<Tout*>(a.o), a.final_state);
+    const int njb = scan_tile_blocks(a.N, a.H, a.dv);
+    const unsigned ntiles = (unsigned)(a.dv / (16 * njb));
+    const dim3 grid(groups * 8u * ntiles);
+    const bf16_t* vv = static_cast<const bf16_t*>(a.v);
+    Tout* oo = static_cast<Tout*>(a.o);
+    if (njb == 8)
+        hipLaunchKernelGGL((chunk_scan_kernel<8, Tout>), grid, dim3(NTHREADS), 0, stream, vv, a.init, a.cu, off, a.N,
+                           a.T, a.H, a.dv, recs, oo, a.final_state);
+    else if (njb == 4)
+        hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(NTHREADS), 0, stream, vv, a.init, a.cu, off, a.N,
+                           a.T, a.H, a.dv, recs, oo, a.final_state);
+    else
+        hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(NTHREADS), 0, stream, vv, a.init, a.cu, off, a.N,
+                           a.T, a.H, a.dv, recs, oo, a.final_state);
     return hipGetLastError();
 }
 
@@ -836,12 +869,12 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 
 bool chunked_supported(const PrefillArgs& a)
 {
-    return a.in_bf16 && !a.ejk && a.dk == DK && a.dv % DVT == 0 && a.g != nullptr && a.a_log != nullptr;
+    return a.in_bf16 && !a.ejk && a.dk == DK && a.dv % DV_MULT == 0 && a.g != nullptr && a.a_log != nullptr;
 }
 
 size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
 {
-    if (dk != DK || dv % DVT != 0 || N <= 0 || T <= 0) return 0;
+    if (dk != DK || dv % DV_MULT != 0 || N <= 0 || T <= 0) return 0;
     return (packed ? offsets_bytes(N) : 0) + max_slots(N, T, packed) * (size_t)H * REC_BYTES;
 }
 

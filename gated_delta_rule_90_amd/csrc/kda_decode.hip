@@ -40,7 +40,7 @@ template <int DK, int DV, bool EJK>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ a_log,
-    const float* __restrict__ dt_bias, float scale, float lower_bound, int H, int l2norm,
+    const float* __restrict__ dt_bias, float scale, float lower_bound, int B, int H, int l2norm,
     float* __restrict__ out, float* __restrict__ S)
 {
     using Sh = DecodeShape<DK, DV>;
@@ -52,9 +52,15 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     __shared__ float sh_red[NWAVES][3];
     __shared__ float4 sh_uv[NWAVES > 1 ? NWAVES : 1][NCG][2];
 
-    const int item = blockIdx.x;  // b * H + h
-    const int b = item / H;
-    const int h = item - b * H;
+    // XCD-aware placement: workgroups are dealt round-robin over the 8 XCDs, and
+    // all heads of one request read the same strided q/k/g cache lines, so every
+    // head of request b runs on XCD b % 8 and those lines are fetched into one L2.
+    const int xcd = blockIdx.x & 7;
+    const int idx = blockIdx.x >> 3;
+    const int b = 8 * (idx / H) + xcd;
+    const int h = idx % H;
+    if (b >= B) return;
+    const int item = b * H + h;
     const int t = threadIdx.x;
     const int cg = t % NCG;
     const int rg = t / NCG;
@@ -172,15 +178,15 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(a.B * a.H));
+    const dim3 grid((unsigned)(((a.B + 7) / 8) * 8 * a.H));
     const dim3 block(DecodeShape<DK, DV>::THREADS);
     if (a.ejk)
         hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, 0, stream, a.q, a.k, a.g, a.v,
-                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.H, (int)a.l2norm,
+                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.B, a.H, (int)a.l2norm,
                            a.out, a.S);
     else
         hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, 0, stream, a.q, a.k, a.g, a.v,
-                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.H, (int)a.l2norm,
+                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.B, a.H, (int)a.l2norm,
                            a.out, a.S);
     return hipGetLastError();
 }
