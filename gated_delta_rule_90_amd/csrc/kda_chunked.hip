@@ -37,6 +37,8 @@
 // Rows of a partial last chunk are padded with exact neutral values
 // (q = k = v = 0, gamma = 0, beta = 0) and never stored, so a packed varlen
 // batch gives bitwise the same result as each sequence alone.
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -91,11 +93,13 @@ static_assert(C * SA * 4 <= TILE_R, "A fits in a tile slot");
 static_assert(2 * C * ST * 2 <= TILE_R, "Tcol + Trow fit in a tile slot");
 static_assert(C * SW * 2 + 32 * SY * 2 <= TILE_R, "T' + scratch");
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
-    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
-    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
-    return lo | (hi << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 __device__ __forceinline__ float lo_bf(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -206,7 +210,43 @@ __global__ __launch_bounds__(64) void chunk_offsets_kernel(const int32_t* __rest
 }
 
 // ------------------------------------------------------------------------
-// chunk_prep: one workgroup per (chunk slot, head)
+// chunk_prep: one workgroup per (chunk slot, head), two per CU by LDS.  (A
+// persistent variant that prefetches the next item into registers exceeds the
+// 256-register budget of two waves per SIMD and was slower.)
+struct PrepItem {
+    int slot, h, c0, len;
+};
+
+struct PrepRaw {
+    uint32_t q[16], k[16];   // bf16 pairs of channels (2*lane, 2*lane+1), rows 16*wave + m
+    float g0[16], g1[16];
+    float beta;              // lanes < 16: beta logit of row 16*wave + lane
+};
+
+// Rows past the sequence read the chunk's first row; they are zeroed on use.
+__device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const bf16_t* q, const bf16_t* k,
+                                          const float* g, const float* beta, int H, int lane, int blk)
+{
+    const int ch = 2 * lane;
+    const size_t base0 = ((size_t)it.c0 * H + it.h) * DK + ch;
+    const bf16_t* qb = q + base0;
+    const bf16_t* kb = k + base0;
+    const float* gb = g + base0;
+    const int rstride = H * DK;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int rr = 16 * blk + m;
+        const int off = ((rr < it.len) ? rr : 0) * rstride;
+        r.q[m] = *reinterpret_cast<const uint32_t*>(qb + off);
+        r.k[m] = *reinterpret_cast<const uint32_t*>(kb + off);
+        const float2 gg = *reinterpret_cast<const float2*>(gb + off);
+        r.g0[m] = gg.x;
+        r.g1[m] = gg.y;
+    }
+    const int rb = 16 * blk + (lane & 15);
+    r.beta = beta[(size_t)(it.c0 + ((rb < it.len) ? rb : 0)) * H + it.h];
+}
+
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const float* __restrict__ a_log, const float* __restrict__ dt_bias,
@@ -230,73 +270,70 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
-    const int slot = blockIdx.x;
-    const int h = blockIdx.y;
+    const int ch = 2 * lane;          // this lane's key channels in the prologue
+    const int blk = wave;             // this wave's 16-row block in the prologue
+    const float lb2 = lower_bound * kLog2e;             // gamma in log2 units
 
     // which sequence and chunk this slot is
-    int n, c;
-    if (off) {
-        if (slot >= off[N]) return;
-        int lo = 0, hi = N - 1;          // largest n with off[n] <= slot
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (off[mid] <= slot) lo = mid; else hi = mid - 1;
+    PrepItem it;
+    it.slot = blockIdx.x;
+    it.h = blockIdx.y;
+    {
+        int n, c;
+        if (off) {
+            if (it.slot >= off[N]) return;
+            int lo = 0, hi = N - 1;          // largest n with off[n] <= slot
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= it.slot) lo = mid; else hi = mid - 1;
+            }
+            n = lo;
+            c = it.slot - off[n];
+        } else {
+            const int ncs = (T + C - 1) / C;
+            n = it.slot / ncs;
+            c = it.slot - n * ncs;
         }
-        n = lo;
-        c = slot - off[n];
-    } else {
-        const int ncs = (T + C - 1) / C;
-        n = slot / ncs;
-        c = slot - n * ncs;
+        int t_begin, t_end;
+        seq_bounds(cu, n, T, t_begin, t_end);
+        it.c0 = t_begin + c * C;
+        it.len = min(C, t_end - it.c0);
     }
-    int t_begin, t_end;
-    seq_bounds(cu, n, T, t_begin, t_end);
-    const int c0 = t_begin + c * C;
-    const int len = min(C, t_end - c0);
-    unsigned char* rec = ws + ((size_t)slot * H + h) * REC_BYTES;
+    PrepRaw cur;
+    prep_load(cur, it, q, k, g, beta, H, lane, blk);
+
+    const int h = it.h;
+    const int c0 = it.c0;
+    const int len = it.len;
+    unsigned char* rec = ws + ((size_t)it.slot * H + h) * REC_BYTES;
     uint16_t* gW = reinterpret_cast<uint16_t*>(rec + REC_W);
     uint16_t* gQG = reinterpret_cast<uint16_t*>(rec + REC_QG);
     uint16_t* gKCT = reinterpret_cast<uint16_t*>(rec + REC_KCT);
     uint16_t* gTP = reinterpret_cast<uint16_t*>(rec + REC_TP);
     uint16_t* gP = reinterpret_cast<uint16_t*>(rec + REC_P);
     float* gEC = reinterpret_cast<float*>(rec + REC_EC);
-
-    // this lane owns key channels 2*lane, 2*lane+1 in the prologue; wave = 16-row block
-    const int ch = 2 * lane;
-    const int blk = wave;
     const float ea = expf(a_log[h]) * kLog2e;          // exp(a_log) folded with log2(e)
     const float dtb0 = dt_bias ? dt_bias[(size_t)ch * H + h] : 0.f;
     const float dtb1 = dt_bias ? dt_bias[(size_t)(ch + 1) * H + h] : 0.f;
-    const float lb2 = lower_bound * kLog2e;             // gamma in log2 units
+    (void)c0;
 
-    // ---------------- phase 1a: loads, partial norms, gate, in-block cumsum
+    // ---------------- phase 1a: partial norms, gate, in-block cumsum (inputs already loaded)
     uint32_t qraw[16], kraw[16];
     float cb0[16], cb1[16];
     {
-        float sq[16], sk[16], g0v[16], g1v[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            // rows past the sequence read the chunk's first row and are zeroed below
-            const int r = 16 * blk + m;
-            const int rr = (r < len) ? r : 0;
-            const size_t base = ((size_t)(c0 + rr) * H + h) * DK + ch;
-            qraw[m] = *reinterpret_cast<const uint32_t*>(q + base);
-            kraw[m] = *reinterpret_cast<const uint32_t*>(k + base);
-            const float2 gg = *reinterpret_cast<const float2*>(g + base);
-            g0v[m] = gg.x;
-            g1v[m] = gg.y;
-        }
+        float sq[16], sk[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const bool valid = 16 * blk + m < len;
-            if (!valid) { qraw[m] = 0u; kraw[m] = 0u; }
+            qraw[m] = valid ? cur.q[m] : 0u;
+            kraw[m] = valid ? cur.k[m] : 0u;
             const float q0 = lo_bf(qraw[m]), q1 = hi_bf(qraw[m]);
             const float k0 = lo_bf(kraw[m]), k1 = hi_bf(kraw[m]);
             sq[m] = q0 * q0 + q1 * q1;
             sk[m] = k0 * k0 + k1 * k1;
             // gamma' = lb * log2(e) * sigmoid(exp(a_log) * (g + dt_bias))
-            const float e0 = __builtin_amdgcn_exp2f(-ea * (g0v[m] + dtb0));
-            const float e1 = __builtin_amdgcn_exp2f(-ea * (g1v[m] + dtb1));
+            const float e0 = __builtin_amdgcn_exp2f(-ea * (cur.g0[m] + dtb0));
+            const float e1 = __builtin_amdgcn_exp2f(-ea * (cur.g1[m] + dtb1));
             const float gm0 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e0) : 0.f;
             const float gm1 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e1) : 0.f;
             cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm0;
@@ -313,7 +350,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         VEC[V_BT + blk * DK + ch + 1] = cb1[15];
         if (lane < 16) {
             const int r = 16 * blk + lane;
-            VEC[V_BETA + r] = (r < len) ? sigmoid_f(beta[(size_t)(c0 + r) * H + h]) : 0.f;
+            VEC[V_BETA + r] = (r < len) ? sigmoid_f(cur.beta) : 0.f;
         }
     }
     lds_barrier();
@@ -422,8 +459,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 const float4 q1 = *reinterpret_cast<const float4*>(cv + 4);
                 const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
                 const float cc[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                const uint4 rw = __builtin_bit_cast(uint4, raw);
+                const uint32_t wv[4] = {rw.x, rw.y, rw.z, rw.w};
+                uint4 outw;
+                uint32_t* ow = reinterpret_cast<uint32_t*>(&outw);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (__bf16)(((float)raw[e] * cc[e]) * mm[e]);
+                for (int e = 0; e < 4; ++e)
+                    ow[e] = pack2((lo_bf(wv[e]) * cc[2 * e]) * mm[2 * e], (hi_bf(wv[e]) * cc[2 * e + 1]) * mm[2 * e + 1]);
+                x = __builtin_bit_cast(bf16x8_t, outw);
             }
             accA[pp] = mfma32(x, ld8(KL, SR, 16 * I + l16, kc), accA[pp]);
             accP[pp] = mfma32(x, ld8(QL, SR, 16 * I + l16, kc), accP[pp]);
@@ -455,19 +498,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
 
     // ---------------- phase 3: T = (I + A)^-1, T' = T diag(beta)
     // level 1: diagonal 16x16 inverses by forward substitution (fp32), lane j = column
-    {
-        const int I = wave;
-        if (I == 0 || I == 2) {
-            const int r = 16 * I + (lane >> 2);
-            const int s = 16 * I + 16 + 4 * (lane & 3);
-            st4bf(TP + r * SW + s, 0.f, 0.f, 0.f, 0.f);
-            if (I == 0)
-                st4bf(TCOL + (16 + (lane >> 2)) * ST + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
-            else
-                st4bf(TROW + (32 + (lane >> 2)) * ST + 48 + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
-        }
-        if (lane < 16) {
-            const int j = lane;
+    // (wave 0 solves all four blocks, lane = 16 * block + column; waves 1 and 2
+    // zero the upper blocks the later stages read)
+    if (wave == 1 || wave == 2) {
+        const int I = 2 * (wave - 1);
+        const int r = 16 * I + (lane >> 2);
+        const int s = 16 * I + 16 + 4 * (lane & 3);
+        st4bf(TP + r * SW + s, 0.f, 0.f, 0.f, 0.f);
+        if (I == 0)
+            st4bf(TCOL + (16 + (lane >> 2)) * ST + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
+        else
+            st4bf(TROW + (32 + (lane >> 2)) * ST + 48 + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
+    }
+    if (wave == 0) {
+        const int I = lane >> 4;
+        {
+            const int j = l16;
             float t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
@@ -572,19 +618,24 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
 }
 
 // ------------------------------------------------------------------------
-// chunk_scan: one workgroup (4 waves) per (sequence, head, tile of 16*NJB state
-// columns).  Wave w owns rows [16w, 16w+16) of U and O and state rows
-// [32w, 32w+32); every wave covers all NJB 16-column blocks of the tile, so
-// each operand fragment is loaded once per workgroup and reused NJB times.
+// chunk_scan: one workgroup of 4 waves per (sequence, head, tile of 16*NJB state
+// columns).  Wave w owns row block I = w (rows [16I, 16I+16) of U and O, state
+// rows [32I, 32I+32)) for every 16-column block of the tile, so each operand
+// fragment is loaded once per workgroup and reused NJB times.  (Eight waves,
+// two per row block, measured slower: each fragment is then fetched twice.)
+constexpr int SCAN_WAVES = 4;
+constexpr int SCAN_THREADS = 64 * SCAN_WAVES;
+
 template <int NJB>
 struct ScanShape {
     static constexpr int DVT = 16 * NJB;
+    static constexpr int NJW = NJB * 4 / SCAN_WAVES;                // column blocks per wave
     static constexpr int ST_OFF = 0;                                // S0^T bf16 [DVT][SR]
     static constexpr int UT_OFF = ST_OFF + DVT * SR * 2;            // U^T  bf16 [DVT][SW]
     static constexpr int VT_OFF = UT_OFF + DVT * SW * 2;            // V^T  bf16 [DVT][SW]
     static constexpr int LDS = VT_OFF + DVT * SW * 2;
-    static constexpr int VSEG = C * DVT / 8 / NTHREADS;             // 16-byte V pieces per thread
-    static_assert(VSEG >= 1, "V tile split");
+    static constexpr int VSEG = (C * DVT / 8 + SCAN_THREADS - 1) / SCAN_THREADS;   // 16-byte V pieces per thread
+    static_assert(NJW >= 1 && NJW * SCAN_WAVES == 4 * NJB, "column blocks split over the waves");
 };
 
 template <int NJB>
@@ -593,14 +644,14 @@ struct Frags {
     bf16x8_t w[4];       // W  rows, k-slices 0..3
     bf16x8_t qg[4];      // Qg rows, k-slices 0..3
     bf16x8_t p[2];       // P  rows, k-slices 0..1
-    bf16x8_t kc[2][2];   // Kc^T rows [32w + 16ib, +16), k-slices 0..1
+    bf16x8_t kc[2][2];   // Kc^T rows [32I + 16ib, +16), k-slices 0..1
     float4 ec[2];        // e^{b_C} for the 4 state rows of each ib
     uint4 v[ScanShape<NJB>::VSEG];   // V tile pieces
 };
 
 template <int NJB>
 __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* rec, const bf16_t* v, int c0,
-                                           int len, int H, int h, int DV, int j0, int wave, int lane, int tid)
+                                           int len, int H, int h, int DV, int j0, int I, int lane, int tid)
 {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int fo = l16 * 32 + 8 * g4;   // lane offset inside a 16x32 fragment
@@ -612,26 +663,26 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
     const float* EC = reinterpret_cast<const float*>(rec + REC_EC);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        f.tp[ks] = *reinterpret_cast<const bf16x8_t*>(TP + (ks * C + 16 * wave) * 32 + fo);
-        f.p[ks] = *reinterpret_cast<const bf16x8_t*>(P + (ks * C + 16 * wave) * 32 + fo);
+        f.tp[ks] = *reinterpret_cast<const bf16x8_t*>(TP + (ks * C + 16 * I) * 32 + fo);
+        f.p[ks] = *reinterpret_cast<const bf16x8_t*>(P + (ks * C + 16 * I) * 32 + fo);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
-            f.kc[ib][ks] = *reinterpret_cast<const bf16x8_t*>(KCT + (ks * DK + 32 * wave + 16 * ib) * 32 + fo);
+            f.kc[ib][ks] = *reinterpret_cast<const bf16x8_t*>(KCT + (ks * DK + 32 * I + 16 * ib) * 32 + fo);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        f.w[ks] = *reinterpret_cast<const bf16x8_t*>(W + (ks * C + 16 * wave) * 32 + fo);
-        f.qg[ks] = *reinterpret_cast<const bf16x8_t*>(QG + (ks * C + 16 * wave) * 32 + fo);
+        f.w[ks] = *reinterpret_cast<const bf16x8_t*>(W + (ks * C + 16 * I) * 32 + fo);
+        f.qg[ks] = *reinterpret_cast<const bf16x8_t*>(QG + (ks * C + 16 * I) * 32 + fo);
     }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
-        f.ec[ib] = *reinterpret_cast<const float4*>(EC + 32 * wave + 16 * ib + 4 * g4);
+        f.ec[ib] = *reinterpret_cast<const float4*>(EC + 32 * I + 16 * ib + 4 * g4);
     // V tile: row s, 8 columns per piece; rows past the sequence read row 0 and are zeroed on use
     constexpr int DVT = ScanShape<NJB>::DVT;
 #pragma unroll
     for (int it = 0; it < ScanShape<NJB>::VSEG; ++it) {
-        const int seg = tid + it * NTHREADS;
-        const int s = seg / (DVT / 8);
+        const int seg = tid + it * SCAN_THREADS;
+        const int s = min(seg / (DVT / 8), C - 1);
         const int jj = (seg % (DVT / 8)) * 8;
         const int ss = (s < len) ? s : 0;
         f.v[it] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * H + h) * DV + j0 + jj);
@@ -639,13 +690,14 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
 }
 
 template <int NJB, typename Tout>
-__global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
+__global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ init, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ off, int N, int T, int H, int DV, const unsigned char* __restrict__ ws,
     Tout* __restrict__ o, float* __restrict__ final_state)
 {
     using Sh = ScanShape<NJB>;
     constexpr int DVT = Sh::DVT;
+    constexpr int NJW = Sh::NJW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::LDS];
     uint16_t* STB = reinterpret_cast<uint16_t*>(smem + Sh::ST_OFF);
     uint16_t* UT = reinterpret_cast<uint16_t*>(smem + Sh::UT_OFF);
@@ -654,6 +706,8 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int I = wave & 3;              // row block
+    const int jb0 = (wave >> 2) * NJW;   // first of this wave's column blocks
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
 
@@ -674,30 +728,30 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
     const int nch = (t_end - t_begin + C - 1) / C;
     const int slot0 = off ? off[n] : n * ((T + C - 1) / C);
 
-    // state: wave w owns rows i in [32w, 32w+32) x all DVT columns
-    f32x4_t S[2][NJB];
+    // state: rows [32I, 32I+32) x this wave's NJW column blocks
+    f32x4_t S[2][NJW];
     const size_t soff = (size_t)unit * DK * DV;
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
+        for (int jw = 0; jw < NJW; ++jw)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 32 * wave + 16 * ib + 4 * g4 + e;
-                const int j = j0 + 16 * jb + l16;
-                S[ib][jb][e] = init ? init[soff + (size_t)i * DV + j] : 0.f;
+                const int i = 32 * I + 16 * ib + 4 * g4 + e;
+                const int j = j0 + 16 * (jb0 + jw) + l16;
+                S[ib][jw][e] = init ? init[soff + (size_t)i * DV + j] : 0.f;
             }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
-            st4bf(STB + (16 * jb + l16) * SR + 32 * wave + 16 * ib + 4 * g4, S[ib][jb][0], S[ib][jb][1],
-                  S[ib][jb][2], S[ib][jb][3]);
+        for (int jw = 0; jw < NJW; ++jw)
+            st4bf(STB + (16 * (jb0 + jw) + l16) * SR + 32 * I + 16 * ib + 4 * g4, S[ib][jw][0], S[ib][jw][1],
+                  S[ib][jw][2], S[ib][jw][3]);
 
     Frags<NJB> cur, nxt;
     if (nch > 0)
         load_frags<NJB>(cur, ws + ((size_t)slot0 * H + h) * REC_BYTES, v, t_begin, min(C, t_end - t_begin), H, h,
-                        DV, j0, wave, lane, tid);
+                        DV, j0, I, lane, tid);
     for (int c = 0; c < nch; ++c) {
         const int c0 = t_begin + c * C;
         const int len = min(C, t_end - c0);
@@ -707,83 +761,88 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         if (c + 1 < nch) {
             const int c1 = c0 + C;
-            load_frags<NJB>(nxt, ws + ((size_t)(slot0 + c + 1) * H + h) * REC_BYTES, v, c1, min(C, t_end - c1), H,
-                            h, DV, j0, wave, lane, tid);
+            load_frags<NJB>(nxt, ws + ((size_t)(slot0 + c + 1) * H + h) * REC_BYTES, v, c1, min(C, t_end - c1),
+                            H, h, DV, j0, I, lane, tid);
         }
         // V tile, transposed: VT[j][s]
 #pragma unroll
         for (int it = 0; it < Sh::VSEG; ++it) {
-            const int seg = tid + it * NTHREADS;
-            const int s = seg / (DVT / 8);
-            const int jj = (seg % (DVT / 8)) * 8;
-            const bool in = s < len;
-            const uint32_t w4[4] = {in ? cur.v[it].x : 0u, in ? cur.v[it].y : 0u, in ? cur.v[it].z : 0u,
-                                    in ? cur.v[it].w : 0u};
+            const int seg = tid + it * SCAN_THREADS;
+            if (seg < C * DVT / 8) {
+                const int s = seg / (DVT / 8);
+                const int jj = (seg % (DVT / 8)) * 8;
+                const bool in = s < len;
+                const uint32_t w4[4] = {in ? cur.v[it].x : 0u, in ? cur.v[it].y : 0u, in ? cur.v[it].z : 0u,
+                                        in ? cur.v[it].w : 0u};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                VT[(jj + 2 * e) * SW + s] = (uint16_t)(w4[e] & 0xffff);
-                VT[(jj + 2 * e + 1) * SW + s] = (uint16_t)(w4[e] >> 16);
+                for (int e = 0; e < 4; ++e) {
+                    VT[(jj + 2 * e) * SW + s] = (uint16_t)(w4[e] & 0xffff);
+                    VT[(jj + 2 * e + 1) * SW + s] = (uint16_t)(w4[e] >> 16);
+                }
             }
         }
         lds_barrier();
 
         // U = T' V - W S0 and the S0 part of O^T = S0^T Qg^T, per 16-column block
-        f32x4_t O[NJB];
+        f32x4_t O[NJW];
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
+        for (int jw = 0; jw < NJW; ++jw) {
+            const int jb = jb0 + jw;
             bf16x8_t sb[4], vt[2];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) sb[ks] = ld8(STB, SR, 16 * jb + l16, 32 * ks + 8 * g4);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) vt[ks] = ld8(VT, SW, 16 * jb + l16, 32 * ks + 8 * g4);
-            f32x4_t u = f32x4_t{0.f, 0.f, 0.f, 0.f}, wsum = u, oa = u;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                wsum = mfma32(cur.w[ks], sb[ks], wsum);
-                oa = mfma32(sb[ks], cur.qg[ks], oa);
-                if (ks < 2) u = mfma32(cur.tp[ks], vt[ks], u);
-            }
-            O[jb] = oa;
-            u = u - wsum;   // u[e] = U[s = 16w + 4*g4 + e][j = 16jb + l16]
-            st4bf(UT + (16 * jb + l16) * SW + 16 * wave + 4 * g4, u[0], u[1], u[2], u[3]);
+            const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // two partial sums per product halve the dependent MFMA chains
+            f32x4_t w0 = mfma32(cur.w[0], sb[0], z), w1 = mfma32(cur.w[1], sb[1], z);
+            f32x4_t o0 = mfma32(sb[0], cur.qg[0], z), o1 = mfma32(sb[1], cur.qg[1], z);
+            f32x4_t u0 = mfma32(cur.tp[0], vt[0], z), u1 = mfma32(cur.tp[1], vt[1], z);
+            w0 = mfma32(cur.w[2], sb[2], w0);
+            w1 = mfma32(cur.w[3], sb[3], w1);
+            o0 = mfma32(sb[2], cur.qg[2], o0);
+            o1 = mfma32(sb[3], cur.qg[3], o1);
+            O[jw] = o0 + o1;
+            const f32x4_t u = (u0 + u1) - (w0 + w1);   // U[s = 16I + 4*g4 + e][j = 16jb + l16]
+            st4bf(UT + (16 * jb + l16) * SW + 16 * I + 4 * g4, u[0], u[1], u[2], u[3]);
         }
         lds_barrier();
 
         // O^T += U^T P^T;  S = Diag(e^{b_C}) S0 + Kc^T U
-        const int r = 16 * wave + l16;
+        const int r = 16 * I + l16;
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
+        for (int jw = 0; jw < NJW; ++jw) {
+            const int jb = jb0 + jw;
             bf16x8_t ut[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) ut[ks] = ld8(UT, SW, 16 * jb + l16, 32 * ks + 8 * g4);
-            f32x4_t acc = O[jb];
-            f32x4_t d0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, d1 = d0;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                acc = mfma32(ut[ks], cur.p[ks], acc);
-                d0 = mfma32(cur.kc[0][ks], ut[ks], d0);
-                d1 = mfma32(cur.kc[1][ks], ut[ks], d1);
-            }
-            // acc[e] = O[r = 16w + l16][j = 16jb + 4*g4 + e]
+            const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            f32x4_t a0 = mfma32(ut[0], cur.p[0], O[jw]);
+            f32x4_t d0 = mfma32(cur.kc[0][0], ut[0], z);
+            f32x4_t d1 = mfma32(cur.kc[1][0], ut[0], z);
+            a0 = mfma32(ut[1], cur.p[1], a0);
+            d0 = mfma32(cur.kc[0][1], ut[1], d0);
+            d1 = mfma32(cur.kc[1][1], ut[1], d1);
+            // a0[e] = O[r = 16I + l16][j = 16jb + 4*g4 + e]
             if (r < len) {
                 Tout* op = o + ((size_t)(c0 + r) * H + h) * DV + j0 + 16 * jb + 4 * g4;
                 if constexpr (sizeof(Tout) == 2) {
-                    *reinterpret_cast<uint2*>(op) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+                    *reinterpret_cast<uint2*>(op) = make_uint2(pack2(a0[0], a0[1]), pack2(a0[2], a0[3]));
                 } else {
-                    *reinterpret_cast<float4*>(op) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    *reinterpret_cast<float4*>(op) = make_float4(a0[0], a0[1], a0[2], a0[3]);
                 }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                S[0][jb][e] = fmaf(cur.ec[0][e], S[0][jb][e], d0[e]);
-                S[1][jb][e] = fmaf(cur.ec[1][e], S[1][jb][e], d1[e]);
+                S[0][jw][e] = fmaf(cur.ec[0][e], S[0][jw][e], d0[e]);
+                S[1][jw][e] = fmaf(cur.ec[1][e], S[1][jw][e], d1[e]);
             }
             // S0^T is only read before the previous barrier, so the new state's bf16
             // copy can go in now; the next chunk's first barrier publishes it.
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
-                st4bf(STB + (16 * jb + l16) * SR + 32 * wave + 16 * ib + 4 * g4, S[ib][jb][0], S[ib][jb][1],
-                      S[ib][jb][2], S[ib][jb][3]);
+                st4bf(STB + (16 * jb + l16) * SR + 32 * I + 16 * ib + 4 * g4, S[ib][jw][0], S[ib][jw][1],
+                      S[ib][jw][2], S[ib][jw][3]);
         }
         if (c + 1 < nch) cur = nxt;
     }
@@ -792,12 +851,12 @@ __global__ __launch_bounds__(NTHREADS) void chunk_scan_kernel(
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
+            for (int jw = 0; jw < NJW; ++jw)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int i = 32 * wave + 16 * ib + 4 * g4 + e;
-                    const int j = j0 + 16 * jb + l16;
-                    final_state[soff + (size_t)i * DV + j] = S[ib][jb][e];
+                    const int i = 32 * I + 16 * ib + 4 * g4 + e;
+                    const int j = j0 + 16 * (jb0 + jw) + l16;
+                    final_state[soff + (size_t)i * DV + j] = S[ib][jw][e];
                 }
     }
 }
@@ -811,14 +870,13 @@ size_t max_slots(int N, int T, bool packed)
     return (size_t)N * (size_t)((T + C - 1) / C);
 }
 
-// 16-column blocks per scan workgroup: wide tiles load each chunk's operands
-// fewer times, narrow tiles put more workgroups on the chip.
+// 16-column blocks per scan workgroup: narrow tiles put more independent
+// chains on the chip (the scan is latency-bound per chain), wide tiles load
+// each chunk's operands fewer times once there are more chains than CUs.
 int scan_tile_blocks(int N, int H, int dv)
 {
     const int units = N * H;
-    int njb = 2;
-    if (units >= 192) njb = 8;
-    else if (units >= 48) njb = 4;
+    int njb = (units > 128) ? 4 : 2;
     while (njb > 2 && dv % (16 * njb) != 0) njb >>= 1;
     return njb;
 }
@@ -853,14 +911,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     const dim3 grid(groups * 8u * ntiles);
     const bf16_t* vv = static_cast<const bf16_t*>(a.v);
     Tout* oo = static_cast<Tout*>(a.o);
-    if (njb == 8)
-        hipLaunchKernelGGL((chunk_scan_kernel<8, Tout>), grid, dim3(NTHREADS), 0, stream, vv, a.init, a.cu, off, a.N,
-                           a.T, a.H, a.dv, recs, oo, a.final_state);
-    else if (njb == 4)
-        hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(NTHREADS), 0, stream, vv, a.init, a.cu, off, a.N,
+    if (njb == 4)
+        hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
                            a.T, a.H, a.dv, recs, oo, a.final_state);
     else
-        hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(NTHREADS), 0, stream, vv, a.init, a.cu, off, a.N,
+        hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
                            a.T, a.H, a.dv, recs, oo, a.final_state);
     return hipGetLastError();
 }
