@@ -52,11 +52,12 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
                                    int32_t dv, kda_dtype_t in_dtype, uint32_t flags)
 {
     if (B < 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv)) return 0;
-    if (!(flags & KDA_CHUNKED) || (flags & KDA_EJK) || in_dtype != KDA_BF16) return 0;
+    if (!(flags & KDA_CHUNKED) || in_dtype != KDA_BF16) return 0;
     const bool packed = num_seqs > 0 && B == 1;
     const int N = packed ? num_seqs : B;
     kda::PrefillArgs probe{};
     probe.in_bf16 = true;
+    probe.ejk = (flags & KDA_EJK) != 0;
     probe.dk = dk;
     probe.dv = dv;
     probe.g = reinterpret_cast<const float*>(1);
@@ -127,7 +128,7 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (has_tokens && chunked && kda::chunked_supported(a)) {
-        if (lower_bound < -5.0f)
+        if (!ejk && lower_bound < -5.0f)
             return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path needs lower_bound >= -5 (got %g)", (double)lower_bound);
         const size_t need = kda::chunked_workspace_bytes(N, T, H, dk, dv, cu_seqlens != nullptr);
         if (need > 0 && (!workspace || workspace_bytes < need))

@@ -34,6 +34,14 @@
 // so every factor stays inside fp32/bf16 range and every underflow is of a
 // value that is itself below 1e-38.  Masks are applied by select.
 //
+// EJK mode (scalar per-head decay d_t, beta used as given, residual against
+// the undecayed state): the residual of row r sees the state decayed up to
+// row r-1 only, so A_rs carries e^{b_{r-1} - b_s} and Kg_r = e^{b_{r-1}} kh_r
+// (b_{-1} = 0); P, Qg, Kc and the carry are as above with the scalar b.  One
+// decay for all channels means A and P are the plain Gram products of the
+// normalised rows, scaled element by element: with d <= 0 every factor is at
+// most 1, so no factorisation is needed.
+//
 // Rows of a partial last chunk are padded with exact neutral values
 // (q = k = v = 0, gamma = 0, beta = 0) and never stored, so a packed varlen
 // batch gives bitwise the same result as each sequence alone.
@@ -82,6 +90,7 @@ constexpr int P_KGT = P_KRD + TILE_R;               // Kg^T [DK][SW]
 constexpr int P_VEC = P_KGT + DK * SW * 2;          // fp32 vectors
 constexpr int V_BETA = 0, V_NQ = 64, V_NK = 128, V_BT = 192, V_M = V_BT + 4 * DK, V_C = V_M + 6 * DK;
 constexpr int VEC_FLOATS = V_C + 4 * DK;
+constexpr int V_B = V_M, V_BX = V_M + C;   // EJK: row cumsums b_r, b_{r-1} (in the pair-vector space)
 constexpr int PREP_LDS = P_VEC + VEC_FLOATS * 4;
 constexpr int P_TP = P_QL;
 constexpr int P_Y = P_QL + C * SW * 2;
@@ -224,6 +233,8 @@ struct PrepRaw {
 };
 
 // Rows past the sequence read the chunk's first row; they are zeroed on use.
+// EJK: g is [tokens][H] (one decay per token and head; NULL = no decay).
+template <bool EJK>
 __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const bf16_t* q, const bf16_t* k,
                                           const float* g, const float* beta, int H, int lane, int blk)
 {
@@ -231,7 +242,7 @@ __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const 
     const size_t base0 = ((size_t)it.c0 * H + it.h) * DK + ch;
     const bf16_t* qb = q + base0;
     const bf16_t* kb = k + base0;
-    const float* gb = g + base0;
+    const float* gb = EJK ? nullptr : g + base0;
     const int rstride = H * DK;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
@@ -239,14 +250,20 @@ __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const 
         const int off = ((rr < it.len) ? rr : 0) * rstride;
         r.q[m] = *reinterpret_cast<const uint32_t*>(qb + off);
         r.k[m] = *reinterpret_cast<const uint32_t*>(kb + off);
-        const float2 gg = *reinterpret_cast<const float2*>(gb + off);
-        r.g0[m] = gg.x;
-        r.g1[m] = gg.y;
+        if constexpr (EJK) {
+            r.g0[m] = g ? g[(size_t)(it.c0 + ((rr < it.len) ? rr : 0)) * H + it.h] : 0.f;
+            r.g1[m] = 0.f;
+        } else {
+            const float2 gg = *reinterpret_cast<const float2*>(gb + off);
+            r.g0[m] = gg.x;
+            r.g1[m] = gg.y;
+        }
     }
     const int rb = 16 * blk + (lane & 15);
     r.beta = beta[(size_t)(it.c0 + ((rb < it.len) ? rb : 0)) * H + it.h];
 }
 
+template <bool EJK>
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const float* __restrict__ a_log, const float* __restrict__ dt_bias,
@@ -300,7 +317,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         it.len = min(C, t_end - it.c0);
     }
     PrepRaw cur;
-    prep_load(cur, it, q, k, g, beta, H, lane, blk);
+    prep_load<EJK>(cur, it, q, k, g, beta, H, lane, blk);
 
     const int h = it.h;
     const int c0 = it.c0;
@@ -312,9 +329,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     uint16_t* gTP = reinterpret_cast<uint16_t*>(rec + REC_TP);
     uint16_t* gP = reinterpret_cast<uint16_t*>(rec + REC_P);
     float* gEC = reinterpret_cast<float*>(rec + REC_EC);
-    const float ea = expf(a_log[h]) * kLog2e;          // exp(a_log) folded with log2(e)
-    const float dtb0 = dt_bias ? dt_bias[(size_t)ch * H + h] : 0.f;
-    const float dtb1 = dt_bias ? dt_bias[(size_t)(ch + 1) * H + h] : 0.f;
+    const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) folded with log2(e)
+    const float dtb0 = (!EJK && dt_bias) ? dt_bias[(size_t)ch * H + h] : 0.f;
+    const float dtb1 = (!EJK && dt_bias) ? dt_bias[(size_t)(ch + 1) * H + h] : 0.f;
     (void)c0;
 
     // ---------------- phase 1a: partial norms, gate, in-block cumsum (inputs already loaded)
@@ -331,13 +348,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
             const float k0 = lo_bf(kraw[m]), k1 = hi_bf(kraw[m]);
             sq[m] = q0 * q0 + q1 * q1;
             sk[m] = k0 * k0 + k1 * k1;
-            // gamma' = lb * log2(e) * sigmoid(exp(a_log) * (g + dt_bias))
-            const float e0 = __builtin_amdgcn_exp2f(-ea * (cur.g0[m] + dtb0));
-            const float e1 = __builtin_amdgcn_exp2f(-ea * (cur.g1[m] + dtb1));
-            const float gm0 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e0) : 0.f;
-            const float gm1 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e1) : 0.f;
-            cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm0;
-            cb1[m] = (m == 0 ? 0.f : cb1[m - 1]) + gm1;
+            if constexpr (EJK) {
+                // the token's log-decay in log2 units, shared by all channels
+                const float gm = valid ? cur.g0[m] * kLog2e : 0.f;
+                cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm;
+                cb1[m] = cb0[m];
+            } else {
+                // gamma' = lb * log2(e) * sigmoid(exp(a_log) * (g + dt_bias))
+                const float e0 = __builtin_amdgcn_exp2f(-ea * (cur.g0[m] + dtb0));
+                const float e1 = __builtin_amdgcn_exp2f(-ea * (cur.g1[m] + dtb1));
+                const float gm0 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e0) : 0.f;
+                const float gm1 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e1) : 0.f;
+                cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm0;
+                cb1[m] = (m == 0 ? 0.f : cb1[m - 1]) + gm1;
+            }
         }
         const float rq = rowsum16(sq, lane);
         const float rk = rowsum16(sk, lane);
@@ -350,13 +374,63 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         VEC[V_BT + blk * DK + ch + 1] = cb1[15];
         if (lane < 16) {
             const int r = 16 * blk + lane;
-            VEC[V_BETA + r] = (r < len) ? sigmoid_f(cur.beta) : 0.f;
+            VEC[V_BETA + r] = (r < len) ? (EJK ? cur.beta : sigmoid_f(cur.beta)) : 0.f;
         }
     }
     lds_barrier();
 
     // ---------------- phase 1b: decay factors; QL, KL, KRd and Kg^T in LDS; Qg, Kc^T out
-    {
+    if constexpr (EJK) {
+        // scalar decay: QL, KL hold the normalised rows; the row cumsums b_r and
+        // b_{r-1} go to V_B / V_BX for the element-wise scaling of A and P
+        float P0 = 0.f, tot = 0.f;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const float t = VEC[V_BT + J * DK];
+            if (J < blk) P0 += t;
+            tot += t;
+        }
+        if (blk == 0) {
+            const float ec = __builtin_amdgcn_exp2f(tot);
+            *reinterpret_cast<float2*>(gEC + ch) = make_float2(ec, ec);
+        }
+        float kg0[16], kg1[16], kc0[16], kc1[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int r = 16 * blk + m;
+            const float b = P0 + cb0[m];
+            const float bx = P0 + (m == 0 ? 0.f : cb0[m - 1]);
+            if (lane == 0) {
+                VEC[V_B + r] = b;
+                VEC[V_BX + r] = bx;
+            }
+            const float nq = VEC[V_NQ + r], nk = VEC[V_NK + r];
+            const float qh0 = lo_bf(qraw[m]) * nq, qh1 = hi_bf(qraw[m]) * nq;
+            const float kh0 = lo_bf(kraw[m]) * nk, kh1 = hi_bf(kraw[m]) * nk;
+            const float eb = __builtin_amdgcn_exp2f(b);
+            const float ebx = __builtin_amdgcn_exp2f(bx);
+            const float ecb = __builtin_amdgcn_exp2f(tot - b);
+            const int at = r * SR + ch;
+            *reinterpret_cast<uint32_t*>(QL + at) = pack2(qh0, qh1);
+            *reinterpret_cast<uint32_t*>(KL + at) = pack2(kh0, kh1);
+            *reinterpret_cast<uint32_t*>(gQG + ksl(C, r, ch)) = pack2(eb * qh0, eb * qh1);
+            kg0[m] = ebx * kh0;
+            kg1[m] = ebx * kh1;
+            kc0[m] = ecb * kh0;
+            kc1[m] = ecb * kh1;
+        }
+        uint16_t* g0p = KGT + ch * SW + 16 * blk;
+        uint16_t* g1p = KGT + (ch + 1) * SW + 16 * blk;
+        uint16_t* c0p = gKCT + ksl(DK, ch, 16 * blk);
+        uint16_t* c1p = gKCT + ksl(DK, ch + 1, 16 * blk);
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            *reinterpret_cast<uint4*>(g0p + 8 * h8) = pack8(kg0 + 8 * h8);
+            *reinterpret_cast<uint4*>(g1p + 8 * h8) = pack8(kg1 + 8 * h8);
+            *reinterpret_cast<uint4*>(c0p + 8 * h8) = pack8(kc0 + 8 * h8);
+            *reinterpret_cast<uint4*>(c1p + 8 * h8) = pack8(kc1 + 8 * h8);
+        }
+    } else {
         float P0 = 0.f, P1 = 0.f, tot0 = 0.f, tot1 = 0.f;
         float pre0[4], pre1[4];   // b at the end of block J
 #pragma unroll
@@ -446,9 +520,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks) {
             const int kc = 32 * ks + 8 * g4;
-            const bf16x8_t raw = ld8(KRD, SR, 16 * J + l16, kc);
+            const bf16x8_t raw = ld8(EJK ? KL : KRD, SR, 16 * J + l16, kc);
             bf16x8_t x = raw;
-            if (I != J) {
+            if (!EJK && I != J) {
                 // e^{b_fI - b_eJ} * (e^{b_eJ - b_fJ} * (e^{b_fJ - b_s} kh_s)): the inner product is
                 // <= 1 first, so the outer factor can only underflow what is below 1e-38 anyway
                 const float* mv = VEC + V_M + pair_slot(I, J) * DK + kc;
@@ -488,8 +562,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
             const int sl = 4 * g4 + e;
             const bool below = (I > J) || (sl < l16);
             const bool belowEq = (I > J) || (sl <= l16);
-            a4[e] = below ? br * accA[pp][e] : 0.f;
-            p4[e] = belowEq ? accP[pp][e] : 0.f;
+            if constexpr (EJK) {
+                // e^{b_{r-1} - b_s} and e^{b_r - b_s}: at most 1 where kept
+                const int s = 16 * J + sl;
+                const float fa = __builtin_amdgcn_exp2f(VEC[V_BX + r] - VEC[V_B + s]);
+                const float fp = __builtin_amdgcn_exp2f(VEC[V_B + r] - VEC[V_B + s]);
+                a4[e] = below ? br * (accA[pp][e] * fa) : 0.f;
+                p4[e] = belowEq ? accP[pp][e] * fp : 0.f;
+            } else {
+                a4[e] = below ? br * accA[pp][e] : 0.f;
+                p4[e] = belowEq ? accP[pp][e] : 0.f;
+            }
         }
         *reinterpret_cast<float4*>(AB + r * SA + 16 * J + 4 * g4) = make_float4(a4[0], a4[1], a4[2], a4[3]);
         st4bf(gP + ksl(C, r, 16 * J + 4 * g4), p4[0], p4[1], p4[2], p4[3]);
@@ -897,10 +980,17 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     }
     const size_t slots = max_slots(a.N, a.T, packed);
     if (slots > 0) {
-        hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, (unsigned)a.H), dim3(NTHREADS), 0, stream,
-                           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.g, a.beta,
-                           a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.scale, a.lower_bound,
-                           (int)a.l2norm, recs);
+        const dim3 pgrid((unsigned)slots, (unsigned)a.H);
+        const bf16_t* qq = static_cast<const bf16_t*>(a.q);
+        const bf16_t* kk = static_cast<const bf16_t*>(a.k);
+        if (a.ejk)
+            hipLaunchKernelGGL(chunk_prep_kernel<true>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.scale, a.lower_bound,
+                               (int)a.l2norm, recs);
+        else
+            hipLaunchKernelGGL(chunk_prep_kernel<false>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.scale, a.lower_bound,
+                               (int)a.l2norm, recs);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -924,7 +1014,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 
 bool chunked_supported(const PrefillArgs& a)
 {
-    return a.in_bf16 && !a.ejk && a.dk == DK && a.dv % DV_MULT == 0 && a.g != nullptr && a.a_log != nullptr;
+    return a.in_bf16 && a.dk == DK && a.dv % DV_MULT == 0 && (a.ejk || (a.g != nullptr && a.a_log != nullptr));
 }
 
 size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)

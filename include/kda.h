@@ -93,9 +93,13 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * Dimensions: dk, dv in {16, 32, 64, 128} (kda_tkg: dk <= 128); H and the
  * number of sequences at most 65535.  B = 0 or
  * T = 0 is a no-op, except that final_state then receives initial_state (or
- * zeros).  Routing: KDA_CHUNKED with bf16 inputs, dk in {64, 128} and dv a
- * multiple of 32 runs the MFMA chunked kernel; every other combination runs
- * the exact token-by-token kernel, which computes the same function.
+ * zeros).  Routing: KDA_CHUNKED with bf16 inputs, dk = 128 and dv a
+ * multiple of 32 runs the MFMA chunked kernel (KDA and EJK modes); every
+ * other combination runs the exact token-by-token kernel, which computes the
+ * same function.  EJK decays are expected to be <= 0 (the ejkernel page
+ * says so); the chunked kernel scales by e^{sum of decays} within a chunk,
+ * so a positive decay large enough to overflow float32 there gives inf/NaN
+ * where the token-by-token kernel would only overflow later.
  */
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
                          const float* g, const float* beta, const float* a_log,

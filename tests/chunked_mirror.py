@@ -16,6 +16,15 @@ is exactly
 The mirror evaluates A and P the way the kernel does, on 16-row sub-blocks
 with reference rows chosen so that no factor overflows, and inverts I + A by
 16x16 diagonal inverses merged 16 -> 32 -> 64.
+
+EJK variant (scalar per-head decay d_t, beta as given, residual against the
+undecayed state): with b_r = sum_{s<=r} d_s, the residual of row r sees the
+state decayed only up to row r-1, so
+    A_rs = beta_r e^{b_{r-1} - b_s} kh_r . kh_s           (s < r, b_{-1} = 0)
+    Kg_r = e^{b_{r-1}} kh_r
+and P, Qg, Kc and the carry are as above with the scalar b.  With d <= 0
+every factor is at most 1, so the kernel scales the plain Gram products
+instead of factorising.
 """
 from __future__ import annotations
 
@@ -94,11 +103,34 @@ def chunk_step(S0, qh, kh, v, gam, bt):
     return O, S
 
 
-def prefill(q, k, v, g, beta, a_log, dt_bias, initial_state=None, cu_seqlens=None,
-            scale=None, lower_bound=-5.0, use_qk_l2norm=True):
-    """Same arguments and returns as the oracle's prefill (KDA mode)."""
+def chunk_step_ejk(S0, qh, kh, v, d, bt):
+    """EJK chunk: d [C] scalar log-decays, bt [C] betas as given (padding rows
+    d = 0, beta = 0)."""
+    b = np.cumsum(d)
+    bx = np.concatenate([[0.0], b[:-1]])               # b_{r-1}
+    r_idx = np.arange(C)
+    lower = r_idx[:, None] > r_idx[None, :]
+    A = np.where(lower, np.exp(np.where(lower, bx[:, None] - b[None, :], 0.0)), 0.0)
+    A = A * (kh @ kh.T) * bt[:, None]
+    lower_eq = r_idx[:, None] >= r_idx[None, :]
+    P = np.where(lower_eq, np.exp(np.where(lower_eq, b[:, None] - b[None, :], 0.0)), 0.0)
+    P = P * (qh @ kh.T)
+    T = _blocked_unit_lower_inverse(A)
+    Tb = T * bt[None, :]
+    W = Tb @ (np.exp(bx)[:, None] * kh)
+    U = Tb @ v - W @ S0
+    O = (np.exp(b)[:, None] * qh) @ S0 + P @ U
+    S = np.exp(b[-1]) * S0 + (np.exp(b[-1] - b)[:, None] * kh).T @ U
+    return O, S
+
+
+def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_seqlens=None,
+            scale=None, lower_bound=-5.0, use_qk_l2norm=True, ejk=False):
+    """Same arguments and returns as the oracle's prefill (EJK: g [B, T, H]
+    log-decays or None, beta used as given)."""
     q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
-    g, beta = np.asarray(g, np.float64), np.asarray(beta, np.float64)
+    g = None if g is None else np.asarray(g, np.float64)
+    beta = np.asarray(beta, np.float64)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if scale is None:
@@ -117,11 +149,18 @@ def prefill(q, k, v, g, beta, a_log, dt_bias, initial_state=None, cu_seqlens=Non
             for c0 in range(t0, t1, C):
                 c1 = min(c0 + C, t1)
                 m = c1 - c0
-                qh, kh, gam, bt = _prologue(q[b, c0:c1, h], k[b, c0:c1, h], g[b, c0:c1, h],
-                                            beta[b, c0:c1, h], a_log[h], dt_bias[:, h], scale,
-                                            lower_bound, use_qk_l2norm)
                 pad = lambda x: np.concatenate([x, np.zeros((C - m,) + x.shape[1:])])
-                O, S = chunk_step(S, pad(qh), pad(kh), pad(v[b, c0:c1, h]), pad(gam), pad(bt))
+                if ejk:
+                    qh, kh, _, _ = _prologue(q[b, c0:c1, h], k[b, c0:c1, h], 0.0, 0.0, 0.0, 0.0,
+                                             scale, 0.0, use_qk_l2norm)
+                    d = np.zeros(m) if g is None else g[b, c0:c1, h]
+                    O, S = chunk_step_ejk(S, pad(qh), pad(kh), pad(v[b, c0:c1, h]), pad(d),
+                                          pad(beta[b, c0:c1, h]))
+                else:
+                    qh, kh, gam, bt = _prologue(q[b, c0:c1, h], k[b, c0:c1, h], g[b, c0:c1, h],
+                                                beta[b, c0:c1, h], a_log[h], dt_bias[:, h], scale,
+                                                lower_bound, use_qk_l2norm)
+                    O, S = chunk_step(S, pad(qh), pad(kh), pad(v[b, c0:c1, h]), pad(gam), pad(bt))
                 o[b, c0:c1, h] = O[:m]
             fs[n, h] = S
     return o, fs

@@ -141,7 +141,7 @@ def test_workspace_query_is_host_only():
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 100, 128, kda.CHUNKED) == 0
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.QK_L2NORM) == 0
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED, kda.F32) == 0
-    assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED | kda.EJK) == 0
+    assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED | kda.EJK) == n
 
 
 def test_error_message_is_thread_local():

@@ -146,3 +146,40 @@ def test_chunked_varlen_8seq_sampled():
     lens = inp.meta["lengths"]
     nl, ns = int(np.argmax(lens)), int(np.argmin(lens))
     _check(inp, units=[nl * H, nl * H + H - 1, ns * H + 5])
+
+
+@pytest.mark.parametrize("T", [64, 1, 200])
+def test_chunked_ejk_ragged(T):
+    """EJK ordering on the MFMA path: scalar per-head decay, beta as given,
+    residual against the undecayed state."""
+    inp = workloads.prefill_inputs(2, T, 3, 128, 128, seed=900 + T, ejk=True, init_state=True)
+    say("chunked EJK B=2 T=%d H=3" % T)
+    _check(inp)
+
+
+def test_chunked_ejk_strong_and_no_decay():
+    inp = workloads.prefill_inputs(1, 256, 2, 128, 64, seed=950, ejk=True, init_state=True)
+    inp.g = (-20.0 * np.abs(inp.g) / np.maximum(np.abs(inp.g).max(), 1e-30) - 3.0).astype(np.float32)
+    say("chunked EJK strong decay (cumulative past e^-190 in a chunk)")
+    _check(inp)
+    inp.g = None
+    say("chunked EJK without decay")
+    _check(inp)
+
+
+def test_chunked_ejk_matches_recurrent_kernel():
+    import torch
+    inp = workloads.prefill_inputs(1, 333, 2, 128, 128, seed=960, ejk=True, init_state=True)
+    say("chunked EJK vs recurrent")
+    oc, sc = prefill_gpu(inp, out_dtype=torch.float32)
+    orc, src = prefill_gpu(inp, use_chunked=False, out_dtype=torch.float32)
+    assert rel_l2(oc, orc) <= TOL and rel_l2(sc, src) <= TOL
+
+
+def test_chunked_ejk_varlen_8seq_sampled():
+    inp = workloads.prefill_varlen_8seq_h32_d128(ejk=True)
+    say("chunked EJK varlen 8 seqs", inp.meta["lengths"])
+    H = 32
+    lens = inp.meta["lengths"]
+    nl, ns = int(np.argmax(lens)), int(np.argmin(lens))
+    _check(inp, units=[nl * H + 3, ns * H, ns * H + H - 1])

@@ -64,3 +64,29 @@ def test_mirror_varlen_and_no_l2norm():
         ro, rs = kda_oracle.prefill(q, k, v, g, beta, a_log, dtb, s0, cu_seqlens=cu,
                                     use_qk_l2norm=l2, scale=0.3)
         assert _rel(o, ro) < 1e-11 and _rel(s, rs) < 1e-11
+
+
+@pytest.mark.parametrize("decay", ["mild", "strong", "none"])
+def test_mirror_ejk_matches_oracle(decay):
+    """EJK: scalar per-head decay, beta as given, residual against the
+    undecayed state.  'strong' takes the cumulative decay in a chunk past
+    e^-1000 (every scaled factor underflows cleanly to zero)."""
+    rng = np.random.default_rng(11)
+    lens = [130, 64, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    N = int(cu[-1])
+    H, dk, dv = 2, 16, 8
+    q, k = rng.standard_normal((1, N, H, dk)), rng.standard_normal((1, N, H, dk))
+    v = rng.standard_normal((1, N, H, dv))
+    beta = rng.uniform(0.0, 1.0, (1, N, H))
+    if decay == "none":
+        d = None
+    elif decay == "mild":
+        d = -0.05 * np.abs(rng.standard_normal((1, N, H)))
+    else:
+        d = -20.0 * np.abs(rng.standard_normal((1, N, H)))
+    s0 = rng.standard_normal((len(lens), H, dk, dv))
+    o, s = chunked_mirror.prefill(q, k, v, d, beta, initial_state=s0, cu_seqlens=cu, ejk=True)
+    ro, rs = kda_oracle.prefill(q, k, v, d, beta, None, None, s0, cu_seqlens=cu, ejk=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+    assert _rel(o, ro) < 1e-11 and _rel(s, rs) < 1e-11
