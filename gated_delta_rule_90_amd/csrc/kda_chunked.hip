@@ -831,27 +831,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
             st4bf(STB + (16 * (jb0 + jw) + l16) * SR + 32 * I + 16 * ib + 4 * g4, S[ib][jw][0], S[ib][jw][1],
                   S[ib][jw][2], S[ib][jw][3]);
 
-    Frags<NJB> cur, nxt;
-    if (nch > 0)
-        load_frags<NJB>(cur, ws + ((size_t)slot0 * H + h) * REC_BYTES, v, t_begin, min(C, t_end - t_begin), H, h,
-                        DV, j0, I, lane, tid);
-    for (int c = 0; c < nch; ++c) {
+    // One chunk: U = T' V - W S0, O = Qg S0 + P U, S = Diag(e^{b_C}) S0 + Kc^T U.
+    auto step = [&](const Frags<NJB>& cur, int c) {
         const int c0 = t_begin + c * C;
         const int len = min(C, t_end - c0);
-        // Everything loaded for this chunk has arrived (it was issued a chunk ago).
-        // Waiting here, before the next prefetch is issued, keeps the compiler
-        // from draining that prefetch at the first use of this chunk's operands.
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        if (c + 1 < nch) {
-            const int c1 = c0 + C;
-            load_frags<NJB>(nxt, ws + ((size_t)(slot0 + c + 1) * H + h) * REC_BYTES, v, c1, min(C, t_end - c1),
-                            H, h, DV, j0, I, lane, tid);
-        }
         // V tile, transposed: VT[j][s]
 #pragma unroll
         for (int it = 0; it < Sh::VSEG; ++it) {
             const int seg = tid + it * SCAN_THREADS;
-            if (seg < C * DVT / 8) {
+            if ((C * DVT / 8) % SCAN_THREADS == 0 || seg < C * DVT / 8) {
                 const int s = seg / (DVT / 8);
                 const int jj = (seg % (DVT / 8)) * 8;
                 const bool in = s < len;
@@ -917,8 +905,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                S[0][jw][e] = fmaf(cur.ec[0][e], S[0][jw][e], d0[e]);
-                S[1][jw][e] = fmaf(cur.ec[1][e], S[1][jw][e], d1[e]);
+                S[0][jw][e] = (c < nch) ? fmaf(cur.ec[0][e], S[0][jw][e], d0[e]) : S[0][jw][e];
+                S[1][jw][e] = (c < nch) ? fmaf(cur.ec[1][e], S[1][jw][e], d1[e]) : S[1][jw][e];
             }
             // S0^T is only read before the previous barrier, so the new state's bf16
             // copy can go in now; the next chunk's first barrier publishes it.
@@ -927,7 +915,30 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
                 st4bf(STB + (16 * jb + l16) * SR + 32 * I + 16 * ib + 4 * g4, S[ib][jw][0], S[ib][jw][1],
                       S[ib][jw][2], S[ib][jw][3]);
         }
-        if (c + 1 < nch) cur = nxt;
+    };
+    // Operands are prefetched one chunk ahead into two register sets used in
+    // turn (the loop is unrolled by two, so no set is ever copied).  Every
+    // prefetch is issued, past the end as a reload of the last chunk, so the
+    // outstanding-load count is the same on every path and the wait before a
+    // chunk's first use only covers that chunk's own loads.  (Prefetching
+    // deeper does not help: a CU's outstanding misses are the limit.)
+    auto prefetch = [&](Frags<NJB>& f, int c) {
+        const int cc = min(c, nch - 1);
+        const int c0 = t_begin + cc * C;
+        load_frags<NJB>(f, ws + ((size_t)(slot0 + cc) * H + h) * REC_BYTES, v, c0, min(C, t_end - c0), H, h, DV,
+                        j0, I, lane, tid);
+    };
+    if (nch > 0) {
+        Frags<NJB> fa, fb;
+        prefetch(fa, 0);
+        // the chunk count is padded to even; a step past the end stores nothing
+        // and leaves the state as it is
+        for (int c = 0; c < nch; c += 2) {
+            prefetch(fb, c + 1);
+            step(fa, c);
+            prefetch(fa, c + 2);
+            step(fb, c + 1);
+        }
     }
 
     if (final_state) {
@@ -953,15 +964,16 @@ size_t max_slots(int N, int T, bool packed)
     return (size_t)N * (size_t)((T + C - 1) / C);
 }
 
-// 16-column blocks per scan workgroup: narrow tiles put more independent
-// chains on the chip (the scan is latency-bound per chain), wide tiles load
-// each chunk's operands fewer times once there are more chains than CUs.
+// 16-column blocks per scan workgroup.  Every workgroup loads a whole
+// record per chunk, and a CU's outstanding misses bound how fast it can, so
+// the widest tile that still gives at least one workgroup per CU wins: narrow
+// tiles put more chains on the chip, wide tiles load each record fewer times.
 int scan_tile_blocks(int N, int H, int dv)
 {
-    const int units = N * H;
-    int njb = (units > 128) ? 4 : 2;
-    while (njb > 2 && dv % (16 * njb) != 0) njb >>= 1;
-    return njb;
+    const long units = (long)N * H;
+    for (int njb = 4; njb > 1; njb >>= 1)
+        if (dv % (16 * njb) == 0 && units * (dv / (16 * njb)) >= 256) return njb;
+    return 1;
 }
 
 template <typename Tout>
@@ -1004,8 +1016,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     if (njb == 4)
         hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
                            a.T, a.H, a.dv, recs, oo, a.final_state);
-    else
+    else if (njb == 2)
         hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
+                           a.T, a.H, a.dv, recs, oo, a.final_state);
+    else
+        hipLaunchKernelGGL((chunk_scan_kernel<1, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
                            a.T, a.H, a.dv, recs, oo, a.final_state);
     return hipGetLastError();
 }
