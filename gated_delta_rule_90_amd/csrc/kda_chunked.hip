@@ -219,12 +219,46 @@ __global__ __launch_bounds__(64) void chunk_offsets_kernel(const int32_t* __rest
 }
 
 // ------------------------------------------------------------------------
-// chunk_prep: one workgroup per (chunk slot, head), two per CU by LDS.  (A
-// persistent variant that prefetches the next item into registers exceeds the
-// 256-register budget of two waves per SIMD and was slower.)
+// chunk_prep: a persistent grid of two workgroups per CU (by LDS) walks the
+// (chunk slot, head) items; each workgroup loads its next item's inputs as
+// soon as the current item's prologue has consumed its own, so the loads
+// overlap the rest of the item's work.
 struct PrepItem {
     int slot, h, c0, len;
+    bool valid;
 };
+
+// Item = slot * H + head.  Slots past the packed chunk count (and items past
+// the end) are not valid.
+__device__ __forceinline__ PrepItem prep_item(int item, int nitems, int H, const int32_t* cu, const int32_t* off,
+                                              int N, int T)
+{
+    PrepItem it{0, 0, 0, 0, false};
+    if (item >= nitems) return it;
+    it.slot = item / H;
+    it.h = item - it.slot * H;
+    int n, c;
+    if (off) {
+        if (it.slot >= off[N]) return it;
+        int lo = 0, hi = N - 1;          // largest n with off[n] <= slot
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= it.slot) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+        c = it.slot - off[n];
+    } else {
+        const int ncs = (T + C - 1) / C;
+        n = it.slot / ncs;
+        c = it.slot - n * ncs;
+    }
+    int t_begin, t_end;
+    seq_bounds(cu, n, T, t_begin, t_end);
+    it.c0 = t_begin + c * C;
+    it.len = min(C, t_end - it.c0);
+    it.valid = true;
+    return it;
+}
 
 struct PrepRaw {
     uint32_t q[16], k[16];   // bf16 pairs of channels (2*lane, 2*lane+1), rows 16*wave + m
@@ -267,7 +301,7 @@ template <bool EJK>
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const float* __restrict__ a_log, const float* __restrict__ dt_bias,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ off, int N, int T, int H,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ off, int N, int T, int H, int nslots,
     float scale, float lower_bound, int l2norm, unsigned char* __restrict__ ws)
 {
     __shared__ __attribute__((aligned(16))) unsigned char smem[PREP_LDS];
@@ -282,421 +316,413 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     uint16_t* TROW = reinterpret_cast<uint16_t*>(smem + P_TROW);
     float* AB = reinterpret_cast<float*>(smem + P_A);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l16 = lane & 15;
-    const int g4 = lane >> 4;
-    const int ch = 2 * lane;          // this lane's key channels in the prologue
-    const int blk = wave;             // this wave's 16-row block in the prologue
     const float lb2 = lower_bound * kLog2e;             // gamma in log2 units
 
-    // which sequence and chunk this slot is
-    PrepItem it;
-    it.slot = blockIdx.x;
-    it.h = blockIdx.y;
-    {
-        int n, c;
-        if (off) {
-            if (it.slot >= off[N]) return;
-            int lo = 0, hi = N - 1;          // largest n with off[n] <= slot
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= it.slot) lo = mid; else hi = mid - 1;
-            }
-            n = lo;
-            c = it.slot - off[n];
-        } else {
-            const int ncs = (T + C - 1) / C;
-            n = it.slot / ncs;
-            c = it.slot - n * ncs;
-        }
-        int t_begin, t_end;
-        seq_bounds(cu, n, T, t_begin, t_end);
-        it.c0 = t_begin + c * C;
-        it.len = min(C, t_end - it.c0);
-    }
+    const int nitems = nslots * H;
+    int item = blockIdx.x;
+    PrepItem it = prep_item(item, nitems, H, cu, off, N, T);
     PrepRaw cur;
-    prep_load<EJK>(cur, it, q, k, g, beta, H, lane, blk);
+    if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, threadIdx.x & 63, threadIdx.x >> 6);
+    for (; item < nitems; item += gridDim.x) {
+        // Thread indices are re-read opaquely in every iteration, so that the
+        // per-lane address arithmetic derived from them is recomputed where it
+        // is used instead of being hoisted out of the loop into registers.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int l16 = lane & 15;
+        const int g4 = lane >> 4;
+        const int ch = 2 * lane;          // this lane's key channels in the prologue
+        const int blk = wave;             // this wave's 16-row block in the prologue
+        const PrepItem me = it;
+        if (!me.valid) {   // a slot past the packed chunk count: only move on
+            it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
+            if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, lane, blk);
+            continue;
+        }
+        const int h = me.h;
+        const int len = me.len;
+        unsigned char* rec = ws + ((size_t)me.slot * H + h) * REC_BYTES;
+        uint16_t* gW = reinterpret_cast<uint16_t*>(rec + REC_W);
+        uint16_t* gQG = reinterpret_cast<uint16_t*>(rec + REC_QG);
+        uint16_t* gKCT = reinterpret_cast<uint16_t*>(rec + REC_KCT);
+        uint16_t* gTP = reinterpret_cast<uint16_t*>(rec + REC_TP);
+        uint16_t* gP = reinterpret_cast<uint16_t*>(rec + REC_P);
+        float* gEC = reinterpret_cast<float*>(rec + REC_EC);
+        const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) folded with log2(e)
+        const float dtb0 = (!EJK && dt_bias) ? dt_bias[(size_t)ch * H + h] : 0.f;
+        const float dtb1 = (!EJK && dt_bias) ? dt_bias[(size_t)(ch + 1) * H + h] : 0.f;
 
-    const int h = it.h;
-    const int c0 = it.c0;
-    const int len = it.len;
-    unsigned char* rec = ws + ((size_t)it.slot * H + h) * REC_BYTES;
-    uint16_t* gW = reinterpret_cast<uint16_t*>(rec + REC_W);
-    uint16_t* gQG = reinterpret_cast<uint16_t*>(rec + REC_QG);
-    uint16_t* gKCT = reinterpret_cast<uint16_t*>(rec + REC_KCT);
-    uint16_t* gTP = reinterpret_cast<uint16_t*>(rec + REC_TP);
-    uint16_t* gP = reinterpret_cast<uint16_t*>(rec + REC_P);
-    float* gEC = reinterpret_cast<float*>(rec + REC_EC);
-    const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) folded with log2(e)
-    const float dtb0 = (!EJK && dt_bias) ? dt_bias[(size_t)ch * H + h] : 0.f;
-    const float dtb1 = (!EJK && dt_bias) ? dt_bias[(size_t)(ch + 1) * H + h] : 0.f;
-    (void)c0;
-
-    // ---------------- phase 1a: partial norms, gate, in-block cumsum (inputs already loaded)
-    uint32_t qraw[16], kraw[16];
-    float cb0[16], cb1[16];
-    {
-        float sq[16], sk[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const bool valid = 16 * blk + m < len;
-            qraw[m] = valid ? cur.q[m] : 0u;
-            kraw[m] = valid ? cur.k[m] : 0u;
-            const float q0 = lo_bf(qraw[m]), q1 = hi_bf(qraw[m]);
-            const float k0 = lo_bf(kraw[m]), k1 = hi_bf(kraw[m]);
-            sq[m] = q0 * q0 + q1 * q1;
-            sk[m] = k0 * k0 + k1 * k1;
-            if constexpr (EJK) {
-                // the token's log-decay in log2 units, shared by all channels
-                const float gm = valid ? cur.g0[m] * kLog2e : 0.f;
-                cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm;
-                cb1[m] = cb0[m];
-            } else {
-                // gamma' = lb * log2(e) * sigmoid(exp(a_log) * (g + dt_bias))
-                const float e0 = __builtin_amdgcn_exp2f(-ea * (cur.g0[m] + dtb0));
-                const float e1 = __builtin_amdgcn_exp2f(-ea * (cur.g1[m] + dtb1));
-                const float gm0 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e0) : 0.f;
-                const float gm1 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e1) : 0.f;
-                cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm0;
-                cb1[m] = (m == 0 ? 0.f : cb1[m - 1]) + gm1;
-            }
-        }
-        const float rq = rowsum16(sq, lane);
-        const float rk = rowsum16(sk, lane);
-        if ((lane & 3) == 0) {
-            const int r = 16 * blk + (lane >> 2);
-            VEC[V_NQ + r] = l2norm ? scale / sqrtf(rq + kNormEps) : scale;
-            VEC[V_NK + r] = l2norm ? 1.0f / sqrtf(rk + kNormEps) : 1.0f;
-        }
-        VEC[V_BT + blk * DK + ch] = cb0[15];
-        VEC[V_BT + blk * DK + ch + 1] = cb1[15];
-        if (lane < 16) {
-            const int r = 16 * blk + lane;
-            VEC[V_BETA + r] = (r < len) ? (EJK ? cur.beta : sigmoid_f(cur.beta)) : 0.f;
-        }
-    }
-    lds_barrier();
-
-    // ---------------- phase 1b: decay factors; QL, KL, KRd and Kg^T in LDS; Qg, Kc^T out
-    if constexpr (EJK) {
-        // scalar decay: QL, KL hold the normalised rows; the row cumsums b_r and
-        // b_{r-1} go to V_B / V_BX for the element-wise scaling of A and P
-        float P0 = 0.f, tot = 0.f;
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const float t = VEC[V_BT + J * DK];
-            if (J < blk) P0 += t;
-            tot += t;
-        }
-        if (blk == 0) {
-            const float ec = __builtin_amdgcn_exp2f(tot);
-            *reinterpret_cast<float2*>(gEC + ch) = make_float2(ec, ec);
-        }
-        float kg0[16], kg1[16], kc0[16], kc1[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int r = 16 * blk + m;
-            const float b = P0 + cb0[m];
-            const float bx = P0 + (m == 0 ? 0.f : cb0[m - 1]);
-            if (lane == 0) {
-                VEC[V_B + r] = b;
-                VEC[V_BX + r] = bx;
-            }
-            const float nq = VEC[V_NQ + r], nk = VEC[V_NK + r];
-            const float qh0 = lo_bf(qraw[m]) * nq, qh1 = hi_bf(qraw[m]) * nq;
-            const float kh0 = lo_bf(kraw[m]) * nk, kh1 = hi_bf(kraw[m]) * nk;
-            const float eb = __builtin_amdgcn_exp2f(b);
-            const float ebx = __builtin_amdgcn_exp2f(bx);
-            const float ecb = __builtin_amdgcn_exp2f(tot - b);
-            const int at = r * SR + ch;
-            *reinterpret_cast<uint32_t*>(QL + at) = pack2(qh0, qh1);
-            *reinterpret_cast<uint32_t*>(KL + at) = pack2(kh0, kh1);
-            *reinterpret_cast<uint32_t*>(gQG + ksl(C, r, ch)) = pack2(eb * qh0, eb * qh1);
-            kg0[m] = ebx * kh0;
-            kg1[m] = ebx * kh1;
-            kc0[m] = ecb * kh0;
-            kc1[m] = ecb * kh1;
-        }
-        uint16_t* g0p = KGT + ch * SW + 16 * blk;
-        uint16_t* g1p = KGT + (ch + 1) * SW + 16 * blk;
-        uint16_t* c0p = gKCT + ksl(DK, ch, 16 * blk);
-        uint16_t* c1p = gKCT + ksl(DK, ch + 1, 16 * blk);
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) {
-            *reinterpret_cast<uint4*>(g0p + 8 * h8) = pack8(kg0 + 8 * h8);
-            *reinterpret_cast<uint4*>(g1p + 8 * h8) = pack8(kg1 + 8 * h8);
-            *reinterpret_cast<uint4*>(c0p + 8 * h8) = pack8(kc0 + 8 * h8);
-            *reinterpret_cast<uint4*>(c1p + 8 * h8) = pack8(kc1 + 8 * h8);
-        }
-    } else {
-        float P0 = 0.f, P1 = 0.f, tot0 = 0.f, tot1 = 0.f;
-        float pre0[4], pre1[4];   // b at the end of block J
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const float t0 = VEC[V_BT + J * DK + ch], t1 = VEC[V_BT + J * DK + ch + 1];
-            if (J < blk) { P0 += t0; P1 += t1; }
-            tot0 += t0;
-            tot1 += t1;
-            pre0[J] = tot0;
-            pre1[J] = tot1;
-        }
-        const float bf0 = P0 + cb0[0], bf1 = P1 + cb1[0];          // b at the first row of the block
-        const float E0 = __builtin_amdgcn_exp2f(bf0), E1 = __builtin_amdgcn_exp2f(bf1);
-        const float c_0 = __builtin_amdgcn_exp2f(cb0[15] - cb0[0]);  // e^{b_e - b_f} of this block
-        const float c_1 = __builtin_amdgcn_exp2f(cb1[15] - cb1[0]);
-        const float N0 = __builtin_amdgcn_exp2f(tot0 - pre0[blk]);    // e^{b_C - b_e}
-        const float N1 = __builtin_amdgcn_exp2f(tot1 - pre1[blk]);
-        // pair vectors e^{b_fI - b_eJ} for rows of this block against earlier blocks J
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-            if (J < blk) {
-                const int ps = pair_slot(blk, J);
-                VEC[V_M + ps * DK + ch] = __builtin_amdgcn_exp2f(bf0 - pre0[J]);
-                VEC[V_M + ps * DK + ch + 1] = __builtin_amdgcn_exp2f(bf1 - pre1[J]);
-            }
-        }
-        if (blk == 0) {
-            *reinterpret_cast<float2*>(gEC + ch) = make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
-        }
-        float kg0[16], kg1[16], kc0[16], kc1[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int r = 16 * blk + m;
-            const float nq = VEC[V_NQ + r], nk = VEC[V_NK + r];
-            const float qh0 = lo_bf(qraw[m]) * nq, qh1 = hi_bf(qraw[m]) * nq;
-            const float kh0 = lo_bf(kraw[m]) * nk, kh1 = hi_bf(kraw[m]) * nk;
-            const float L0 = __builtin_amdgcn_exp2f(cb0[m] - cb0[0]);
-            const float L1 = __builtin_amdgcn_exp2f(cb1[m] - cb1[0]);
-            const float iL0 = __builtin_amdgcn_rcpf(L0), iL1 = __builtin_amdgcn_rcpf(L1);
-            const float ql0 = L0 * qh0, ql1 = L1 * qh1;
-            const float kl0 = L0 * kh0, kl1 = L1 * kh1;
-            const float kd0 = iL0 * kh0, kd1 = iL1 * kh1;
-            const int at = r * SR + ch;
-            *reinterpret_cast<uint32_t*>(QL + at) = pack2(ql0, ql1);
-            *reinterpret_cast<uint32_t*>(KL + at) = pack2(kl0, kl1);
-            *reinterpret_cast<uint32_t*>(KRD + at) = pack2(kd0, kd1);
-            *reinterpret_cast<uint32_t*>(gQG + ksl(C, r, ch)) = pack2(E0 * ql0, E1 * ql1);
-            kg0[m] = E0 * kl0;
-            kg1[m] = E1 * kl1;
-            kc0[m] = N0 * c_0 * kd0;   // e^{b_C - b_e} e^{b_e - b_f} e^{b_f - b_s} kh_s
-            kc1[m] = N1 * c_1 * kd1;
-        }
-        // 16 consecutive tokens of one channel = 32 contiguous bytes
-        uint16_t* g0p = KGT + ch * SW + 16 * blk;
-        uint16_t* g1p = KGT + (ch + 1) * SW + 16 * blk;
-        uint16_t* c0p = gKCT + ksl(DK, ch, 16 * blk);
-        uint16_t* c1p = gKCT + ksl(DK, ch + 1, 16 * blk);
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) {
-            *reinterpret_cast<uint4*>(g0p + 8 * h8) = pack8(kg0 + 8 * h8);
-            *reinterpret_cast<uint4*>(g1p + 8 * h8) = pack8(kg1 + 8 * h8);
-            *reinterpret_cast<uint4*>(c0p + 8 * h8) = pack8(kc0 + 8 * h8);
-            *reinterpret_cast<uint4*>(c1p + 8 * h8) = pack8(kc1 + 8 * h8);
-        }
-        // this block's e^{b_e - b_f}, which turns KRd into e^{b_e - b_s} kh_s for later blocks
-        VEC[V_C + blk * DK + ch] = c_0;
-        VEC[V_C + blk * DK + ch + 1] = c_1;
-    }
-    lds_barrier();
-
-    // ---------------- phase 2: A and P on 16x16 block pairs (I >= J)
-    f32x4_t accA[3], accP[3];
-    int pI[3], pJ[3];
-#pragma unroll
-    for (int pp = 0; pp < 3; ++pp) {
-        const int pidx = wave + 4 * pp;
-        accA[pp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        accP[pp] = accA[pp];
-        int I = 0, J = 0;
-        if (pidx < 4) { I = pidx; J = pidx; }
-        else if (pidx < 7) { I = pidx - 3; J = I - 1; }
-        else if (pidx < 9) { I = pidx - 5; J = I - 2; }
-        else { I = 3; J = 0; }
-        pI[pp] = I;
-        pJ[pp] = J;
-        if (pidx >= 10) continue;
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-            const int kc = 32 * ks + 8 * g4;
-            const bf16x8_t raw = ld8(EJK ? KL : KRD, SR, 16 * J + l16, kc);
-            bf16x8_t x = raw;
-            if (!EJK && I != J) {
-                // e^{b_fI - b_eJ} * (e^{b_eJ - b_fJ} * (e^{b_fJ - b_s} kh_s)): the inner product is
-                // <= 1 first, so the outer factor can only underflow what is below 1e-38 anyway
-                const float* mv = VEC + V_M + pair_slot(I, J) * DK + kc;
-                const float* cv = VEC + V_C + J * DK + kc;
-                const float4 m0 = *reinterpret_cast<const float4*>(mv);
-                const float4 m1 = *reinterpret_cast<const float4*>(mv + 4);
-                const float4 q0 = *reinterpret_cast<const float4*>(cv);
-                const float4 q1 = *reinterpret_cast<const float4*>(cv + 4);
-                const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-                const float cc[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                const uint4 rw = __builtin_bit_cast(uint4, raw);
-                const uint32_t wv[4] = {rw.x, rw.y, rw.z, rw.w};
-                uint4 outw;
-                uint32_t* ow = reinterpret_cast<uint32_t*>(&outw);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ow[e] = pack2((lo_bf(wv[e]) * cc[2 * e]) * mm[2 * e], (hi_bf(wv[e]) * cc[2 * e + 1]) * mm[2 * e + 1]);
-                x = __builtin_bit_cast(bf16x8_t, outw);
-            }
-            accA[pp] = mfma32(x, ld8(KL, SR, 16 * I + l16, kc), accA[pp]);
-            accP[pp] = mfma32(x, ld8(QL, SR, 16 * I + l16, kc), accP[pp]);
-        }
-    }
-    lds_barrier();
-    // A (fp32, beta-scaled, strict lower) to LDS; P (bf16, lower incl. diagonal) out.
-    // accumulator element e is (s = 16J + 4*g4 + e, r = 16I + l16)
-#pragma unroll
-    for (int pp = 0; pp < 3; ++pp) {
-        const int pidx = wave + 4 * pp;
-        if (pidx >= 10) continue;
-        const int I = pI[pp], J = pJ[pp];
-        const int r = 16 * I + l16;
-        const float br = VEC[V_BETA + r];
-        float a4[4], p4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int sl = 4 * g4 + e;
-            const bool below = (I > J) || (sl < l16);
-            const bool belowEq = (I > J) || (sl <= l16);
-            if constexpr (EJK) {
-                // e^{b_{r-1} - b_s} and e^{b_r - b_s}: at most 1 where kept
-                const int s = 16 * J + sl;
-                const float fa = __builtin_amdgcn_exp2f(VEC[V_BX + r] - VEC[V_B + s]);
-                const float fp = __builtin_amdgcn_exp2f(VEC[V_B + r] - VEC[V_B + s]);
-                a4[e] = below ? br * (accA[pp][e] * fa) : 0.f;
-                p4[e] = belowEq ? accP[pp][e] * fp : 0.f;
-            } else {
-                a4[e] = below ? br * accA[pp][e] : 0.f;
-                p4[e] = belowEq ? accP[pp][e] : 0.f;
-            }
-        }
-        *reinterpret_cast<float4*>(AB + r * SA + 16 * J + 4 * g4) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-        st4bf(gP + ksl(C, r, 16 * J + 4 * g4), p4[0], p4[1], p4[2], p4[3]);
-    }
-    lds_barrier();
-
-    // ---------------- phase 3: T = (I + A)^-1, T' = T diag(beta)
-    // level 1: diagonal 16x16 inverses by forward substitution (fp32), lane j = column
-    // (wave 0 solves all four blocks, lane = 16 * block + column; waves 1 and 2
-    // zero the upper blocks the later stages read)
-    if (wave == 1 || wave == 2) {
-        const int I = 2 * (wave - 1);
-        const int r = 16 * I + (lane >> 2);
-        const int s = 16 * I + 16 + 4 * (lane & 3);
-        st4bf(TP + r * SW + s, 0.f, 0.f, 0.f, 0.f);
-        if (I == 0)
-            st4bf(TCOL + (16 + (lane >> 2)) * ST + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
-        else
-            st4bf(TROW + (32 + (lane >> 2)) * ST + 48 + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
-    }
-    if (wave == 0) {
-        const int I = lane >> 4;
+        // ---------------- phase 1a: partial norms, gate, in-block cumsum (inputs already loaded)
+        uint32_t qraw[16], kraw[16];
+        float cb0[16], cb1[16];
         {
-            const int j = l16;
-            float t[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
-            const float* arow = AB + (16 * I) * SA + 16 * I;
-#pragma unroll
-            for (int r = 1; r < 16; ++r) {
-                float acc = 0.f;
-#pragma unroll
-                for (int s = 0; s < r; ++s) acc = fmaf(arow[r * SA + s], t[s], acc);
-                if (r > j) t[r] = -acc;
-            }
-            const float bj = VEC[V_BETA + 16 * I + j];
-            uint16_t* tc = TCOL + (16 * I + j) * ST + 16 * I;
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) st4bf(tc + r, t[r], t[r + 1], t[r + 2], t[r + 3]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                st1bf(TROW + (16 * I + r) * ST + 16 * I + j, t[r]);
-                st1bf(TP + (16 * I + r) * SW + 16 * I + j, t[r] * bj);
-            }
-        }
-    }
-    lds_barrier();
-    // level 2: T10 = -T11 (A10 T00) on wave 0, T32 = -T33 (A32 T22) on wave 1
-    if (wave < 2) {
-        const int Ib = 2 * wave + 1, Jb = 2 * wave;
-        uint16_t* ys = YS + wave * 16 * SY;
-        const float4 af = *reinterpret_cast<const float4*>(AB + (16 * Ib + l16) * SA + 16 * Jb + 4 * g4);
-        const f32x4_t y = mfma16(f32_to_s16x4(af), ld4(TCOL, ST, 16 * Jb + l16, 16 * Jb + 4 * g4),
-                                 f32x4_t{0.f, 0.f, 0.f, 0.f});
-        st4bf(ys + l16 * SY + 4 * g4, y[0], y[1], y[2], y[3]);   // column-major Y
-        const f32x4_t tt = mfma16(ld4(TROW, ST, 16 * Ib + l16, 16 * Ib + 4 * g4), ld4(ys, SY, l16, 4 * g4),
-                                  f32x4_t{0.f, 0.f, 0.f, 0.f});
-        const float bj = VEC[V_BETA + 16 * Jb + l16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * Ib + 4 * g4 + e;
-            st1bf(TP + r * SW + 16 * Jb + l16, -tt[e] * bj);
-            if (wave == 1) st1bf(TROW + r * ST + 16 * Jb + l16, -tt[e]);
-        }
-        if (wave == 0)
-            st4bf(TCOL + (16 * Jb + l16) * ST + 16 * Ib + 4 * g4, -tt[0], -tt[1], -tt[2], -tt[3]);
-    }
-    lds_barrier();
-    // level 3: T[32:64, 0:32] = -T_B (A[32:64, 0:32] T_A), one 16x16 tile per wave
-    {
-        const int ti = wave >> 1, tj = wave & 1;
-        f32x4_t y = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float4 af = *reinterpret_cast<const float4*>(AB + (32 + 16 * ti + l16) * SA + 16 * kk + 4 * g4);
-            y = mfma16(f32_to_s16x4(af), ld4(TCOL, ST, 16 * tj + l16, 16 * kk + 4 * g4), y);
-        }
-        st4bf(YS + (16 * tj + l16) * SY + 16 * ti + 4 * g4, y[0], y[1], y[2], y[3]);
-    }
-    lds_barrier();
-    {
-        const int ti = wave >> 1, tj = wave & 1;
-        f32x4_t tt = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            tt = mfma16(ld4(TROW, ST, 32 + 16 * ti + l16, 32 + 16 * kk + 4 * g4),
-                        ld4(YS, SY, 16 * tj + l16, 16 * kk + 4 * g4), tt);
-        const float bj = VEC[V_BETA + 16 * tj + l16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            st1bf(TP + (32 + 16 * ti + 4 * g4 + e) * SW + 16 * tj + l16, -tt[e] * bj);
-    }
-    lds_barrier();
-
-    // ---------------- phase 4: W = T' Kg (as W^T = Kg^T T'^T); T' out
-    {
-#pragma unroll
-        for (int ibl = 0; ibl < 2; ++ibl) {
-            const int ib = 2 * wave + ibl;
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks == 1 && I < 2) continue;
-                    acc = mfma32(ld8(KGT, SW, 16 * ib + l16, 32 * ks + 8 * g4),
-                                 ld8(TP, SW, 16 * I + l16, 32 * ks + 8 * g4), acc);
+            float sq[16], sk[16];
+    #pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const bool valid = 16 * blk + m < len;
+                qraw[m] = valid ? cur.q[m] : 0u;
+                kraw[m] = valid ? cur.k[m] : 0u;
+                const float q0 = lo_bf(qraw[m]), q1 = hi_bf(qraw[m]);
+                const float k0 = lo_bf(kraw[m]), k1 = hi_bf(kraw[m]);
+                sq[m] = q0 * q0 + q1 * q1;
+                sk[m] = k0 * k0 + k1 * k1;
+                if constexpr (EJK) {
+                    // the token's log-decay in log2 units, shared by all channels
+                    const float gm = valid ? cur.g0[m] * kLog2e : 0.f;
+                    cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm;
+                    cb1[m] = cb0[m];
+                } else {
+                    // gamma' = lb * log2(e) * sigmoid(exp(a_log) * (g + dt_bias))
+                    const float e0 = __builtin_amdgcn_exp2f(-ea * (cur.g0[m] + dtb0));
+                    const float e1 = __builtin_amdgcn_exp2f(-ea * (cur.g1[m] + dtb1));
+                    const float gm0 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e0) : 0.f;
+                    const float gm1 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e1) : 0.f;
+                    cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm0;
+                    cb1[m] = (m == 0 ? 0.f : cb1[m - 1]) + gm1;
                 }
-                // acc[e] = W[r = 16I + l16][i = 16ib + 4*g4 + e]
-                st4bf(gW + ksl(C, 16 * I + l16, 16 * ib + 4 * g4), acc[0], acc[1], acc[2], acc[3]);
+            }
+            const float rq = rowsum16(sq, lane);
+            const float rk = rowsum16(sk, lane);
+            if ((lane & 3) == 0) {
+                const int r = 16 * blk + (lane >> 2);
+                VEC[V_NQ + r] = l2norm ? scale / sqrtf(rq + kNormEps) : scale;
+                VEC[V_NK + r] = l2norm ? 1.0f / sqrtf(rk + kNormEps) : 1.0f;
+            }
+            VEC[V_BT + blk * DK + ch] = cb0[15];
+            VEC[V_BT + blk * DK + ch + 1] = cb1[15];
+            if (lane < 16) {
+                const int r = 16 * blk + lane;
+                VEC[V_BETA + r] = (r < len) ? (EJK ? cur.beta : sigmoid_f(cur.beta)) : 0.f;
             }
         }
-        // T' [64][64] -> k-sliced, thread = (row, 16-column block); blocks above the
-        // diagonal are written as zeros (the scan always runs both k-slices)
-        const int r = tid >> 2;
-        const int s0 = 16 * (tid & 3);
-        const bool upper = (tid & 3) > (r >> 4);
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) {
-            uint4 val = *reinterpret_cast<const uint4*>(TP + r * SW + s0 + 8 * h8);
-            if (upper) val = make_uint4(0u, 0u, 0u, 0u);
-            *reinterpret_cast<uint4*>(gTP + ksl(C, r, s0 + 8 * h8)) = val;
-            if (upper) *reinterpret_cast<uint4*>(gP + ksl(C, r, s0 + 8 * h8)) = val;
+        // the inputs are in qraw, kraw, cb0, cb1 and VEC now: fetch the next item's
+        it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
+        if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, lane, blk);
+        lds_barrier();
+
+        // ---------------- phase 1b: decay factors; QL, KL, KRd and Kg^T in LDS; Qg, Kc^T out
+        if constexpr (EJK) {
+            // scalar decay: QL, KL hold the normalised rows; the row cumsums b_r and
+            // b_{r-1} go to V_B / V_BX for the element-wise scaling of A and P
+            float P0 = 0.f, tot = 0.f;
+    #pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const float t = VEC[V_BT + J * DK];
+                if (J < blk) P0 += t;
+                tot += t;
+            }
+            if (blk == 0) {
+                const float ec = __builtin_amdgcn_exp2f(tot);
+                *reinterpret_cast<float2*>(gEC + ch) = make_float2(ec, ec);
+            }
+            float kg0[16], kg1[16], kc0[16], kc1[16];
+    #pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int r = 16 * blk + m;
+                const float b = P0 + cb0[m];
+                const float bx = P0 + (m == 0 ? 0.f : cb0[m - 1]);
+                if (lane == 0) {
+                    VEC[V_B + r] = b;
+                    VEC[V_BX + r] = bx;
+                }
+                const float nq = VEC[V_NQ + r], nk = VEC[V_NK + r];
+                const float qh0 = lo_bf(qraw[m]) * nq, qh1 = hi_bf(qraw[m]) * nq;
+                const float kh0 = lo_bf(kraw[m]) * nk, kh1 = hi_bf(kraw[m]) * nk;
+                const float eb = __builtin_amdgcn_exp2f(b);
+                const float ebx = __builtin_amdgcn_exp2f(bx);
+                const float ecb = __builtin_amdgcn_exp2f(tot - b);
+                const int at = r * SR + ch;
+                *reinterpret_cast<uint32_t*>(QL + at) = pack2(qh0, qh1);
+                *reinterpret_cast<uint32_t*>(KL + at) = pack2(kh0, kh1);
+                *reinterpret_cast<uint32_t*>(gQG + ksl(C, r, ch)) = pack2(eb * qh0, eb * qh1);
+                kg0[m] = ebx * kh0;
+                kg1[m] = ebx * kh1;
+                kc0[m] = ecb * kh0;
+                kc1[m] = ecb * kh1;
+            }
+            uint16_t* g0p = KGT + ch * SW + 16 * blk;
+            uint16_t* g1p = KGT + (ch + 1) * SW + 16 * blk;
+            uint16_t* c0p = gKCT + ksl(DK, ch, 16 * blk);
+            uint16_t* c1p = gKCT + ksl(DK, ch + 1, 16 * blk);
+    #pragma unroll
+            for (int h8 = 0; h8 < 2; ++h8) {
+                *reinterpret_cast<uint4*>(g0p + 8 * h8) = pack8(kg0 + 8 * h8);
+                *reinterpret_cast<uint4*>(g1p + 8 * h8) = pack8(kg1 + 8 * h8);
+                *reinterpret_cast<uint4*>(c0p + 8 * h8) = pack8(kc0 + 8 * h8);
+                *reinterpret_cast<uint4*>(c1p + 8 * h8) = pack8(kc1 + 8 * h8);
+            }
+        } else {
+            float P0 = 0.f, P1 = 0.f, tot0 = 0.f, tot1 = 0.f;
+            float pre0[4], pre1[4];   // b at the end of block J
+    #pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const float t0 = VEC[V_BT + J * DK + ch], t1 = VEC[V_BT + J * DK + ch + 1];
+                if (J < blk) { P0 += t0; P1 += t1; }
+                tot0 += t0;
+                tot1 += t1;
+                pre0[J] = tot0;
+                pre1[J] = tot1;
+            }
+            const float bf0 = P0 + cb0[0], bf1 = P1 + cb1[0];          // b at the first row of the block
+            const float E0 = __builtin_amdgcn_exp2f(bf0), E1 = __builtin_amdgcn_exp2f(bf1);
+            const float c_0 = __builtin_amdgcn_exp2f(cb0[15] - cb0[0]);  // e^{b_e - b_f} of this block
+            const float c_1 = __builtin_amdgcn_exp2f(cb1[15] - cb1[0]);
+            const float N0 = __builtin_amdgcn_exp2f(tot0 - pre0[blk]);    // e^{b_C - b_e}
+            const float N1 = __builtin_amdgcn_exp2f(tot1 - pre1[blk]);
+            // pair vectors e^{b_fI - b_eJ} for rows of this block against earlier blocks J
+    #pragma unroll
+            for (int J = 0; J < 3; ++J) {
+                if (J < blk) {
+                    const int ps = pair_slot(blk, J);
+                    VEC[V_M + ps * DK + ch] = __builtin_amdgcn_exp2f(bf0 - pre0[J]);
+                    VEC[V_M + ps * DK + ch + 1] = __builtin_amdgcn_exp2f(bf1 - pre1[J]);
+                }
+            }
+            if (blk == 0) {
+                *reinterpret_cast<float2*>(gEC + ch) = make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
+            }
+            float kg0[16], kg1[16], kc0[16], kc1[16];
+    #pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int r = 16 * blk + m;
+                const float nq = VEC[V_NQ + r], nk = VEC[V_NK + r];
+                const float qh0 = lo_bf(qraw[m]) * nq, qh1 = hi_bf(qraw[m]) * nq;
+                const float kh0 = lo_bf(kraw[m]) * nk, kh1 = hi_bf(kraw[m]) * nk;
+                const float L0 = __builtin_amdgcn_exp2f(cb0[m] - cb0[0]);
+                const float L1 = __builtin_amdgcn_exp2f(cb1[m] - cb1[0]);
+                const float iL0 = __builtin_amdgcn_rcpf(L0), iL1 = __builtin_amdgcn_rcpf(L1);
+                const float ql0 = L0 * qh0, ql1 = L1 * qh1;
+                const float kl0 = L0 * kh0, kl1 = L1 * kh1;
+                const float kd0 = iL0 * kh0, kd1 = iL1 * kh1;
+                const int at = r * SR + ch;
+                *reinterpret_cast<uint32_t*>(QL + at) = pack2(ql0, ql1);
+                *reinterpret_cast<uint32_t*>(KL + at) = pack2(kl0, kl1);
+                *reinterpret_cast<uint32_t*>(KRD + at) = pack2(kd0, kd1);
+                *reinterpret_cast<uint32_t*>(gQG + ksl(C, r, ch)) = pack2(E0 * ql0, E1 * ql1);
+                kg0[m] = E0 * kl0;
+                kg1[m] = E1 * kl1;
+                kc0[m] = N0 * c_0 * kd0;   // e^{b_C - b_e} e^{b_e - b_f} e^{b_f - b_s} kh_s
+                kc1[m] = N1 * c_1 * kd1;
+            }
+            // 16 consecutive tokens of one channel = 32 contiguous bytes
+            uint16_t* g0p = KGT + ch * SW + 16 * blk;
+            uint16_t* g1p = KGT + (ch + 1) * SW + 16 * blk;
+            uint16_t* c0p = gKCT + ksl(DK, ch, 16 * blk);
+            uint16_t* c1p = gKCT + ksl(DK, ch + 1, 16 * blk);
+    #pragma unroll
+            for (int h8 = 0; h8 < 2; ++h8) {
+                *reinterpret_cast<uint4*>(g0p + 8 * h8) = pack8(kg0 + 8 * h8);
+                *reinterpret_cast<uint4*>(g1p + 8 * h8) = pack8(kg1 + 8 * h8);
+                *reinterpret_cast<uint4*>(c0p + 8 * h8) = pack8(kc0 + 8 * h8);
+                *reinterpret_cast<uint4*>(c1p + 8 * h8) = pack8(kc1 + 8 * h8);
+            }
+            // this block's e^{b_e - b_f}, which turns KRd into e^{b_e - b_s} kh_s for later blocks
+            VEC[V_C + blk * DK + ch] = c_0;
+            VEC[V_C + blk * DK + ch + 1] = c_1;
         }
+        lds_barrier();
+
+        // ---------------- phase 2: A and P on 16x16 block pairs (I >= J)
+        f32x4_t accA[3], accP[3];
+        int pI[3], pJ[3];
+    #pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+            const int pidx = wave + 4 * pp;
+            accA[pp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accP[pp] = accA[pp];
+            int I = 0, J = 0;
+            if (pidx < 4) { I = pidx; J = pidx; }
+            else if (pidx < 7) { I = pidx - 3; J = I - 1; }
+            else if (pidx < 9) { I = pidx - 5; J = I - 2; }
+            else { I = 3; J = 0; }
+            pI[pp] = I;
+            pJ[pp] = J;
+            if (pidx >= 10) continue;
+    #pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const int kc = 32 * ks + 8 * g4;
+                const bf16x8_t raw = ld8(EJK ? KL : KRD, SR, 16 * J + l16, kc);
+                bf16x8_t x = raw;
+                if (!EJK && I != J) {
+                    // e^{b_fI - b_eJ} * (e^{b_eJ - b_fJ} * (e^{b_fJ - b_s} kh_s)): the inner product is
+                    // <= 1 first, so the outer factor can only underflow what is below 1e-38 anyway
+                    const float* mv = VEC + V_M + pair_slot(I, J) * DK + kc;
+                    const float* cv = VEC + V_C + J * DK + kc;
+                    const float4 m0 = *reinterpret_cast<const float4*>(mv);
+                    const float4 m1 = *reinterpret_cast<const float4*>(mv + 4);
+                    const float4 q0 = *reinterpret_cast<const float4*>(cv);
+                    const float4 q1 = *reinterpret_cast<const float4*>(cv + 4);
+                    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+                    const float cc[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                    const uint4 rw = __builtin_bit_cast(uint4, raw);
+                    const uint32_t wv[4] = {rw.x, rw.y, rw.z, rw.w};
+                    uint4 outw;
+                    uint32_t* ow = reinterpret_cast<uint32_t*>(&outw);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ow[e] = pack2((lo_bf(wv[e]) * cc[2 * e]) * mm[2 * e], (hi_bf(wv[e]) * cc[2 * e + 1]) * mm[2 * e + 1]);
+                    x = __builtin_bit_cast(bf16x8_t, outw);
+                }
+                accA[pp] = mfma32(x, ld8(KL, SR, 16 * I + l16, kc), accA[pp]);
+                accP[pp] = mfma32(x, ld8(QL, SR, 16 * I + l16, kc), accP[pp]);
+            }
+        }
+        lds_barrier();
+        // A (fp32, beta-scaled, strict lower) to LDS; P (bf16, lower incl. diagonal) out.
+        // accumulator element e is (s = 16J + 4*g4 + e, r = 16I + l16)
+    #pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+            const int pidx = wave + 4 * pp;
+            if (pidx >= 10) continue;
+            const int I = pI[pp], J = pJ[pp];
+            const int r = 16 * I + l16;
+            const float br = VEC[V_BETA + r];
+            float a4[4], p4[4];
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sl = 4 * g4 + e;
+                const bool below = (I > J) || (sl < l16);
+                const bool belowEq = (I > J) || (sl <= l16);
+                if constexpr (EJK) {
+                    // e^{b_{r-1} - b_s} and e^{b_r - b_s}: at most 1 where kept
+                    const int s = 16 * J + sl;
+                    const float fa = __builtin_amdgcn_exp2f(VEC[V_BX + r] - VEC[V_B + s]);
+                    const float fp = __builtin_amdgcn_exp2f(VEC[V_B + r] - VEC[V_B + s]);
+                    a4[e] = below ? br * (accA[pp][e] * fa) : 0.f;
+                    p4[e] = belowEq ? accP[pp][e] * fp : 0.f;
+                } else {
+                    a4[e] = below ? br * accA[pp][e] : 0.f;
+                    p4[e] = belowEq ? accP[pp][e] : 0.f;
+                }
+            }
+            *reinterpret_cast<float4*>(AB + r * SA + 16 * J + 4 * g4) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+            st4bf(gP + ksl(C, r, 16 * J + 4 * g4), p4[0], p4[1], p4[2], p4[3]);
+        }
+        lds_barrier();
+
+        // ---------------- phase 3: T = (I + A)^-1, T' = T diag(beta)
+        // level 1: diagonal 16x16 inverses by forward substitution (fp32), lane j = column
+        // (wave 0 solves all four blocks, lane = 16 * block + column; waves 1 and 2
+        // zero the upper blocks the later stages read)
+        if (wave == 1 || wave == 2) {
+            const int I = 2 * (wave - 1);
+            const int r = 16 * I + (lane >> 2);
+            const int s = 16 * I + 16 + 4 * (lane & 3);
+            st4bf(TP + r * SW + s, 0.f, 0.f, 0.f, 0.f);
+            if (I == 0)
+                st4bf(TCOL + (16 + (lane >> 2)) * ST + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
+            else
+                st4bf(TROW + (32 + (lane >> 2)) * ST + 48 + 4 * (lane & 3), 0.f, 0.f, 0.f, 0.f);
+        }
+        if (wave == 0) {
+            const int I = lane >> 4;
+            {
+                const int j = l16;
+                float t[16];
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
+                const float* arow = AB + (16 * I) * SA + 16 * I;
+    #pragma unroll
+                for (int r = 1; r < 16; ++r) {
+                    float acc = 0.f;
+    #pragma unroll
+                    for (int s = 0; s < r; ++s) acc = fmaf(arow[r * SA + s], t[s], acc);
+                    if (r > j) t[r] = -acc;
+                }
+                const float bj = VEC[V_BETA + 16 * I + j];
+                uint16_t* tc = TCOL + (16 * I + j) * ST + 16 * I;
+    #pragma unroll
+                for (int r = 0; r < 16; r += 4) st4bf(tc + r, t[r], t[r + 1], t[r + 2], t[r + 3]);
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    st1bf(TROW + (16 * I + r) * ST + 16 * I + j, t[r]);
+                    st1bf(TP + (16 * I + r) * SW + 16 * I + j, t[r] * bj);
+                }
+            }
+        }
+        lds_barrier();
+        // level 2: T10 = -T11 (A10 T00) on wave 0, T32 = -T33 (A32 T22) on wave 1
+        if (wave < 2) {
+            const int Ib = 2 * wave + 1, Jb = 2 * wave;
+            uint16_t* ys = YS + wave * 16 * SY;
+            const float4 af = *reinterpret_cast<const float4*>(AB + (16 * Ib + l16) * SA + 16 * Jb + 4 * g4);
+            const f32x4_t y = mfma16(f32_to_s16x4(af), ld4(TCOL, ST, 16 * Jb + l16, 16 * Jb + 4 * g4),
+                                     f32x4_t{0.f, 0.f, 0.f, 0.f});
+            st4bf(ys + l16 * SY + 4 * g4, y[0], y[1], y[2], y[3]);   // column-major Y
+            const f32x4_t tt = mfma16(ld4(TROW, ST, 16 * Ib + l16, 16 * Ib + 4 * g4), ld4(ys, SY, l16, 4 * g4),
+                                      f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const float bj = VEC[V_BETA + 16 * Jb + l16];
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * Ib + 4 * g4 + e;
+                st1bf(TP + r * SW + 16 * Jb + l16, -tt[e] * bj);
+                if (wave == 1) st1bf(TROW + r * ST + 16 * Jb + l16, -tt[e]);
+            }
+            if (wave == 0)
+                st4bf(TCOL + (16 * Jb + l16) * ST + 16 * Ib + 4 * g4, -tt[0], -tt[1], -tt[2], -tt[3]);
+        }
+        lds_barrier();
+        // level 3: T[32:64, 0:32] = -T_B (A[32:64, 0:32] T_A), one 16x16 tile per wave
+        {
+            const int ti = wave >> 1, tj = wave & 1;
+            f32x4_t y = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float4 af = *reinterpret_cast<const float4*>(AB + (32 + 16 * ti + l16) * SA + 16 * kk + 4 * g4);
+                y = mfma16(f32_to_s16x4(af), ld4(TCOL, ST, 16 * tj + l16, 16 * kk + 4 * g4), y);
+            }
+            st4bf(YS + (16 * tj + l16) * SY + 16 * ti + 4 * g4, y[0], y[1], y[2], y[3]);
+        }
+        lds_barrier();
+        {
+            const int ti = wave >> 1, tj = wave & 1;
+            f32x4_t tt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                tt = mfma16(ld4(TROW, ST, 32 + 16 * ti + l16, 32 + 16 * kk + 4 * g4),
+                            ld4(YS, SY, 16 * tj + l16, 16 * kk + 4 * g4), tt);
+            const float bj = VEC[V_BETA + 16 * tj + l16];
+    #pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st1bf(TP + (32 + 16 * ti + 4 * g4 + e) * SW + 16 * tj + l16, -tt[e] * bj);
+        }
+        lds_barrier();
+
+        // ---------------- phase 4: W = T' Kg (as W^T = Kg^T T'^T); T' out
+        {
+    #pragma unroll
+            for (int ibl = 0; ibl < 2; ++ibl) {
+                const int ib = 2 * wave + ibl;
+    #pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if (ks == 1 && I < 2) continue;
+                        acc = mfma32(ld8(KGT, SW, 16 * ib + l16, 32 * ks + 8 * g4),
+                                     ld8(TP, SW, 16 * I + l16, 32 * ks + 8 * g4), acc);
+                    }
+                    // acc[e] = W[r = 16I + l16][i = 16ib + 4*g4 + e]
+                    st4bf(gW + ksl(C, 16 * I + l16, 16 * ib + 4 * g4), acc[0], acc[1], acc[2], acc[3]);
+                }
+            }
+            // T' [64][64] -> k-sliced, thread = (row, 16-column block); blocks above the
+            // diagonal are written as zeros (the scan always runs both k-slices)
+            const int r = tid >> 2;
+            const int s0 = 16 * (tid & 3);
+            const bool upper = (tid & 3) > (r >> 4);
+    #pragma unroll
+            for (int h8 = 0; h8 < 2; ++h8) {
+                uint4 val = *reinterpret_cast<const uint4*>(TP + r * SW + s0 + 8 * h8);
+                if (upper) val = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4*>(gTP + ksl(C, r, s0 + 8 * h8)) = val;
+                if (upper) *reinterpret_cast<uint4*>(gP + ksl(C, r, s0 + 8 * h8)) = val;
+            }
+        }
+        // phase 4 of this item reads KGT and TP, which the next item overwrites
+        lds_barrier();
     }
 }
 
@@ -992,16 +1018,18 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     }
     const size_t slots = max_slots(a.N, a.T, packed);
     if (slots > 0) {
-        const dim3 pgrid((unsigned)slots, (unsigned)a.H);
+        // persistent: two workgroups per CU (the LDS limit), at most one per item
+        const size_t items = slots * (size_t)a.H;
+        const dim3 pgrid((unsigned)std::min<size_t>(items, 2 * 256));
         const bf16_t* qq = static_cast<const bf16_t*>(a.q);
         const bf16_t* kk = static_cast<const bf16_t*>(a.k);
         if (a.ejk)
             hipLaunchKernelGGL(chunk_prep_kernel<true>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
-                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.scale, a.lower_bound,
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, (int)slots, a.scale, a.lower_bound,
                                (int)a.l2norm, recs);
         else
             hipLaunchKernelGGL(chunk_prep_kernel<false>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
-                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.scale, a.lower_bound,
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, (int)slots, a.scale, a.lower_bound,
                                (int)a.l2norm, recs);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
