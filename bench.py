@@ -14,8 +14,14 @@ The same JSON line also carries:
   prefill       chunked prefill tokens/s for B=4, T=4096, H=16, dk=dv=128
                 (bf16 inputs) with its own roofline fractions (--no-prefill
                 skips it)
+  configs       the other workloads, each timed the same way: the fp32
+                token-by-token kernel at B=1, T=64, H=2, d=16 (latency bound),
+                one 65536-token sequence with 32 heads (also split at 32768
+                with the state passed through, checked bitwise against the
+                unsplit call), and 8 packed sequences of 512..8192 tokens with
+                32 heads, in KDA and EJK mode (--no-configs skips them)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-configs] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -46,10 +52,13 @@ def decode_flops(B, H, dk, dv):
     return 7 * B * H * dk * dv
 
 
-def prefill_bytes(ntok, H, dk, dv, n_states, init_state):
-    per_tok = H * (2 * dk * 2 + dv * 2 + dk * 4 + 4 + dv * 2)  # q,k,v bf16; g fp32; beta; o bf16
+def prefill_bytes(ntok, H, dk, dv, n_states, init_state, ejk=False, io_bytes=2):
+    # q, k, v in; g (KDA: [dk] per token-head, EJK: one decay) and beta fp32; o out;
+    # final states written, initial states read when given; a_log, dt_bias (KDA)
+    gate = 4 if ejk else dk * 4
+    per_tok = H * ((2 * dk + dv) * io_bytes + gate + 4 + dv * io_bytes)
     states = n_states * H * dk * dv * 4 * (2 if init_state else 1)
-    return ntok * per_tok + states + H * 4 + dk * H * 4
+    return ntok * per_tok + states + (0 if ejk else H * 4 + dk * H * 4)
 
 
 def prefill_flops(ntok, H, dk, dv, C=64):
@@ -149,49 +158,108 @@ def cpu_decode_baseline(inp, budget_s=10.0):
             "sample": f"{reps} full decode steps (B=64, H=32, dk=dv=128, float64) in {el:.1f} s"}
 
 
-def bench_prefill(steps, warmup):
+def _prefill_run(inp, steps, warmup, nsets=1, split=None):
+    """Time kda.prefill on one workload (inputs resident in HBM, nsets input
+    copies used in turn so the Infinity Cache cannot hold them)."""
     import torch
     import gated_delta_rule_90_amd as kda
-    from gated_delta_rule_90_amd import workloads
-    inp = workloads.prefill_b4_t4096_h16_d128()
-    bf, f = torch.bfloat16, torch.float32
-    d = lambda x, t: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(t)
-    sets = []
-    for rep in range(2):  # two input sets (2 x 408 MB) so the Infinity Cache cannot hold one
-        sets.append([d(inp.q, bf), d(inp.k, bf), d(inp.v, bf), d(inp.g, f), d(inp.beta, f)])
-    a_log, dtb = d(inp.a_log, f), d(inp.dt_bias, f)
+    io = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    f = torch.float32
+    d = lambda x, t: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(t)
+    sets = [[d(inp.q, io), d(inp.k, io), d(inp.v, io), d(inp.g, f), d(inp.beta, f)]
+            for _ in range(nsets)]
+    a_log = None if inp.ejk else d(inp.a_log, f)
+    dtb = None if inp.ejk else d(inp.dt_bias, f)
+    s0 = d(inp.initial_state, f)
+    cu = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to("cuda")
     B, T, H, dk = inp.q.shape
     dv = inp.v.shape[-1]
-    o = torch.empty((B, T, H, dv), dtype=bf, device="cuda")
-    fs = torch.empty((B, H, dk, dv), dtype=f, device="cuda")
+    nst = B if cu is None else cu.numel() - 1
+    o = torch.empty((B, T, H, dv), dtype=io, device="cuda")
+    fs = torch.empty((nst, H, dk, dv), dtype=f, device="cuda")
 
-    def step(i):
-        q, k, v, g, beta = sets[i % 2]
-        kda.prefill(q, k, v, g, beta, a_log, dtb, scale=inp.scale, lower_bound=inp.lower_bound,
-                    out=o, final_state=fs)
+    def call(i, q=None, k=None, v=None, g=None, beta=None, init=s0, out=o, fin=fs, use_chunked=True):
+        qq, kk, vv, gg, bb = sets[i % nsets]
+        return kda.prefill(qq if q is None else q, kk if k is None else k, vv if v is None else v,
+                           gg if g is None else g, bb if beta is None else beta, a_log, dtb, init,
+                           cu, scale=inp.scale, lower_bound=inp.lower_bound, ejk=inp.ejk,
+                           use_chunked=use_chunked, out=out, final_state=fin)
 
+    chunked = inp.dtype == "bf16"
     for i in range(warmup):
-        step(i)
+        call(i, use_chunked=chunked)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
-        step(i)
+        call(i, use_chunked=chunked)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    ntok = B * T
-    nbytes = prefill_bytes(ntok, H, dk, dv, B, False)
-    fl = prefill_flops(ntok, H, dk, dv)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    tfs = fl / (ms * 1e-3) / 1e12
-    floor_ms = max(nbytes / (HBM_PEAK_GBS * 1e9), fl / (BF16_MFMA_PEAK_TFS * 1e12)) * 1e3
-    return {"workload": "kda_chunked_prefill_b4_t4096_h16_d128_bf16",
-            "tokens_per_s": round(ntok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
-            "alg_bytes": nbytes, "alg_flops_tri": fl,
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
-            "roofline_frac": round(floor_ms / ms, 4), "achieved_GBs": round(gbs, 1),
-            "achieved_TFs": round(tfs, 2)}
+    ntok = B * T if cu is None else int(inp.cu_seqlens[-1])
+    io_bytes = 2 if inp.dtype == "bf16" else 4
+    nbytes = prefill_bytes(ntok, H, dk, dv, nst, s0 is not None, inp.ejk, io_bytes)
+    res = {"tokens_per_s": round(ntok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+           "alg_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "path": "chunked MFMA" if chunked else "token-by-token"}
+    if chunked:
+        fl = prefill_flops(ntok, H, dk, dv)
+        tfs = fl / (ms * 1e-3) / 1e12
+        floor_ms = max(nbytes / (HBM_PEAK_GBS * 1e9), fl / (BF16_MFMA_PEAK_TFS * 1e12)) * 1e3
+        res.update({"alg_flops_tri": fl, "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
+                    "roofline_frac": round(floor_ms / ms, 4),
+                    "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "achieved_TFs": round(tfs, 2)})
+    if split is not None:
+        # the same call in two halves with the state passed through: bitwise equal?
+        call(0, use_chunked=chunked)
+        torch.cuda.synchronize()
+        o_ref, fs_ref = o.clone(), fs.clone()
+        qq, kk, vv, gg, bb = sets[0]
+        o1 = torch.empty_like(o[:, :split])
+        o2 = torch.empty_like(o[:, split:])
+        mid = torch.empty_like(fs)
+        fin = torch.empty_like(fs)
+        part = lambda x, a, b: None if x is None else x[:, a:b].contiguous()
+        call(0, part(qq, 0, split), part(kk, 0, split), part(vv, 0, split), part(gg, 0, split),
+             part(bb, 0, split), s0, o1, mid, use_chunked=chunked)
+        call(0, part(qq, split, T), part(kk, split, T), part(vv, split, T), part(gg, split, T),
+             part(bb, split, T), mid, o2, fin, use_chunked=chunked)
+        torch.cuda.synchronize()
+        res["split_at"] = split
+        res["split_bitwise_equal"] = bool(torch.equal(torch.cat([o1, o2], 1), o_ref) and
+                                          torch.equal(fin, fs_ref))
+    del sets
+    return res
+
+
+def bench_prefill(steps, warmup):
+    from gated_delta_rule_90_amd import workloads
+    inp = workloads.prefill_b4_t4096_h16_d128()
+    res = _prefill_run(inp, steps, warmup, nsets=2)   # 2 x 408 MB: more than the Infinity Cache
+    res.pop("path")
+    return dict({"workload": "kda_chunked_prefill_b4_t4096_h16_d128_bf16"}, **res)
+
+
+def bench_configs(steps, warmup):
+    """The other workloads: each is generated on the host (seeded), uploaded,
+    then timed; inputs are freed before the next one."""
+    import gc
+    from gated_delta_rule_90_amd import workloads
+    out = {}
+    inp = workloads.recurrent_fp32_small()
+    out["recurrent_fp32_b1_t64_h2_d16"] = dict(_prefill_run(inp, 10 * steps, warmup), note="64 dependent token steps per call: latency bound")
+    for name, make, kw in (
+            ("prefill_long_t65536_h32_d128", workloads.prefill_long_t65536_h32_d128, {"split": 32768}),
+            ("prefill_varlen_8seq_h32_d128", workloads.prefill_varlen_8seq_h32_d128, {}),
+            ("prefill_varlen_8seq_h32_d128_ejk", lambda: workloads.prefill_varlen_8seq_h32_d128(ejk=True), {})):
+        inp = make()
+        res = _prefill_run(inp, steps, warmup, **kw)
+        if inp.cu_seqlens is not None:
+            res["lengths"] = inp.meta["lengths"]
+        out[name] = res
+        del inp
+        gc.collect()
+    return out
 
 
 def copy_calibration(mib=256):
@@ -212,6 +280,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calib", action="store_true",
@@ -243,6 +312,8 @@ def main():
     }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(max(5, args.steps // 10), max(2, args.warmup // 10))
+    if not args.no_configs:
+        line["configs"] = bench_configs(max(3, args.steps // 40), max(1, args.warmup // 10))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_decode_baseline(inp, args.cpu_budget)
     print(json.dumps(line), flush=True)

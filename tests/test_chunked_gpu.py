@@ -183,3 +183,35 @@ def test_chunked_ejk_varlen_8seq_sampled():
     lens = inp.meta["lengths"]
     nl, ns = int(np.argmax(lens)), int(np.argmin(lens))
     _check(inp, units=[nl * H + 3, ns * H, ns * H + H - 1])
+
+
+def test_chunked_long_context_t65536_h32_split_and_sampled():
+    """One 65536-token sequence, 32 heads, nonzero initial state: the call split
+    at 32768 with the state passed through equals the unsplit call bitwise, and
+    two heads (first and last) match the oracle."""
+    inp = workloads.prefill_long_t65536_h32_d128()
+    say("chunked long context T=65536 H=32")
+    o, s = prefill_gpu(inp)
+    cut = 32768
+
+    def part(a, b, s0):
+        return workloads.PrefillInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b],
+                                       inp.g[:, a:b], inp.beta[:, a:b], inp.a_log, inp.dt_bias,
+                                       s0, None, inp.dtype, inp.scale, inp.lower_bound)
+
+    say("  split at 32768")
+    o1, s1 = prefill_gpu(part(0, cut, inp.initial_state))
+    o2, s2 = prefill_gpu(part(cut, 65536, s1))
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), o)
+    assert np.array_equal(s2, s)
+    del o1, o2
+    heads = [0, 31]
+    sub = workloads.PrefillInputs(inp.q[:, :, heads], inp.k[:, :, heads], inp.v[:, :, heads],
+                                  inp.g[:, :, heads], inp.beta[:, :, heads], inp.a_log[heads],
+                                  inp.dt_bias[:, heads], inp.initial_state[:, heads], None,
+                                  inp.dtype, inp.scale, inp.lower_bound)
+    say("  oracle on heads", heads)
+    ro, rs = prefill_oracle(sub)
+    eo, es = rel_l2(o[:, :, heads], ro), rel_l2(s[:, heads], rs)
+    say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL and es <= TOL, (eo, es)
