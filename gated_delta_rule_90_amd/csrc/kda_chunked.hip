@@ -46,6 +46,7 @@
 // (q = k = v = 0, gamma = 0, beta = 0) and never stored, so a packed varlen
 // batch gives bitwise the same result as each sequence alone.
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -758,7 +759,10 @@ struct Frags {
     uint4 v[ScanShape<NJB>::VSEG];   // V tile pieces
 };
 
-template <int NJB>
+// The loads of one chunk in three parts, issued at the starts of the three
+// phases of the previous chunk so that their drain overlaps its compute:
+// part 0 = V tile, T', P, e^{b_C}; part 1 = W, Qg; part 2 = Kc^T.
+template <int NJB, int PART>
 __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* rec, const bf16_t* v, int c0,
                                            int len, int H, int h, int DV, int j0, int I, int lane, int tid)
 {
@@ -770,31 +774,37 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
     const uint16_t* TP = reinterpret_cast<const uint16_t*>(rec + REC_TP);
     const uint16_t* P = reinterpret_cast<const uint16_t*>(rec + REC_P);
     const float* EC = reinterpret_cast<const float*>(rec + REC_EC);
+    if constexpr (PART == 0) {
+        // V tile: row s, 8 columns per piece; rows past the sequence read row 0 and are zeroed on use
+        constexpr int DVT = ScanShape<NJB>::DVT;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        f.tp[ks] = *reinterpret_cast<const bf16x8_t*>(TP + (ks * C + 16 * I) * 32 + fo);
-        f.p[ks] = *reinterpret_cast<const bf16x8_t*>(P + (ks * C + 16 * I) * 32 + fo);
+        for (int it = 0; it < ScanShape<NJB>::VSEG; ++it) {
+            const int seg = tid + it * SCAN_THREADS;
+            const int s = min(seg / (DVT / 8), C - 1);
+            const int jj = (seg % (DVT / 8)) * 8;
+            const int ss = (s < len) ? s : 0;
+            f.v[it] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * H + h) * DV + j0 + jj);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f.tp[ks] = *reinterpret_cast<const bf16x8_t*>(TP + (ks * C + 16 * I) * 32 + fo);
+            f.p[ks] = *reinterpret_cast<const bf16x8_t*>(P + (ks * C + 16 * I) * 32 + fo);
+        }
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
-            f.kc[ib][ks] = *reinterpret_cast<const bf16x8_t*>(KCT + (ks * DK + 32 * I + 16 * ib) * 32 + fo);
-    }
+            f.ec[ib] = *reinterpret_cast<const float4*>(EC + 32 * I + 16 * ib + 4 * g4);
+    } else if constexpr (PART == 1) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        f.w[ks] = *reinterpret_cast<const bf16x8_t*>(W + (ks * C + 16 * I) * 32 + fo);
-        f.qg[ks] = *reinterpret_cast<const bf16x8_t*>(QG + (ks * C + 16 * I) * 32 + fo);
-    }
+        for (int ks = 0; ks < 4; ++ks) {
+            f.w[ks] = *reinterpret_cast<const bf16x8_t*>(W + (ks * C + 16 * I) * 32 + fo);
+            f.qg[ks] = *reinterpret_cast<const bf16x8_t*>(QG + (ks * C + 16 * I) * 32 + fo);
+        }
+    } else {
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-        f.ec[ib] = *reinterpret_cast<const float4*>(EC + 32 * I + 16 * ib + 4 * g4);
-    // V tile: row s, 8 columns per piece; rows past the sequence read row 0 and are zeroed on use
-    constexpr int DVT = ScanShape<NJB>::DVT;
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int it = 0; it < ScanShape<NJB>::VSEG; ++it) {
-        const int seg = tid + it * SCAN_THREADS;
-        const int s = min(seg / (DVT / 8), C - 1);
-        const int jj = (seg % (DVT / 8)) * 8;
-        const int ss = (s < len) ? s : 0;
-        f.v[it] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * H + h) * DV + j0 + jj);
+            for (int ib = 0; ib < 2; ++ib)
+                f.kc[ib][ks] = *reinterpret_cast<const bf16x8_t*>(KCT + (ks * DK + 32 * I + 16 * ib) * 32 + fo);
     }
 }
 
@@ -858,9 +868,27 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
                   S[ib][jw][2], S[ib][jw][3]);
 
     // One chunk: U = T' V - W S0, O = Qg S0 + P U, S = Diag(e^{b_C}) S0 + Kc^T U.
-    auto step = [&](const Frags<NJB>& cur, int c) {
+    // Operands are prefetched one chunk ahead into two register sets used in
+    // turn (the loop is unrolled by two, so no set is ever copied), in three
+    // parts issued at the starts of the current chunk's three phases: a CU's
+    // outstanding misses bound how fast a chunk's 64.5 KiB arrive, and spread
+    // out, that drain overlaps the compute instead of stalling issue before it.
+    // Every prefetch is issued (past the end it reloads the last chunk), so the
+    // outstanding-load count is the same on every path and the wait before a
+    // chunk's first use only covers that chunk's own loads.
+    auto prefetch = [&](auto part, Frags<NJB>& f, int c) {
+        const int cc = min(c, nch - 1);
+        const int c0 = t_begin + cc * C;
+        load_frags<NJB, decltype(part)::value>(f, ws + ((size_t)(slot0 + cc) * H + h) * REC_BYTES, v, c0,
+                                               min(C, t_end - c0), H, h, DV, j0, I, lane, tid);
+    };
+    using Part0 = std::integral_constant<int, 0>;
+    using Part1 = std::integral_constant<int, 1>;
+    using Part2 = std::integral_constant<int, 2>;
+    auto step = [&](const Frags<NJB>& cur, Frags<NJB>& nxt, int c) {
         const int c0 = t_begin + c * C;
         const int len = min(C, t_end - c0);
+        prefetch(Part0{}, nxt, c + 1);
         // V tile, transposed: VT[j][s]
 #pragma unroll
         for (int it = 0; it < Sh::VSEG; ++it) {
@@ -880,6 +908,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
         }
         lds_barrier();
 
+        prefetch(Part1{}, nxt, c + 1);
         // U = T' V - W S0 and the S0 part of O^T = S0^T Qg^T, per 16-column block
         f32x4_t O[NJW];
 #pragma unroll
@@ -905,6 +934,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
         }
         lds_barrier();
 
+        prefetch(Part2{}, nxt, c + 1);
         // O^T += U^T P^T;  S = Diag(e^{b_C}) S0 + Kc^T U
         const int r = 16 * I + l16;
 #pragma unroll
@@ -942,28 +972,20 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
                       S[ib][jw][2], S[ib][jw][3]);
         }
     };
-    // Operands are prefetched one chunk ahead into two register sets used in
-    // turn (the loop is unrolled by two, so no set is ever copied).  Every
-    // prefetch is issued, past the end as a reload of the last chunk, so the
-    // outstanding-load count is the same on every path and the wait before a
-    // chunk's first use only covers that chunk's own loads.  (Prefetching
-    // deeper does not help: a CU's outstanding misses are the limit.)
-    auto prefetch = [&](Frags<NJB>& f, int c) {
-        const int cc = min(c, nch - 1);
-        const int c0 = t_begin + cc * C;
-        load_frags<NJB>(f, ws + ((size_t)(slot0 + cc) * H + h) * REC_BYTES, v, c0, min(C, t_end - c0), H, h, DV,
-                        j0, I, lane, tid);
-    };
     if (nch > 0) {
         Frags<NJB> fa, fb;
-        prefetch(fa, 0);
+        // in the loop's issue order, so that its waits count the same way on entry
+        prefetch(Part0{}, fa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        prefetch(Part1{}, fa, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        prefetch(Part2{}, fa, 0);
+        __builtin_amdgcn_sched_barrier(0);
         // the chunk count is padded to even; a step past the end stores nothing
         // and leaves the state as it is
         for (int c = 0; c < nch; c += 2) {
-            prefetch(fb, c + 1);
-            step(fa, c);
-            prefetch(fa, c + 2);
-            step(fb, c + 1);
+            step(fa, fb, c);
+            step(fb, fa, c + 1);
         }
     }
 
