@@ -331,7 +331,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63;
-        const int wave = tid >> 6;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar address math
         const int l16 = lane & 15;
         const int g4 = lane >> 4;
         const int ch = 2 * lane;          // this lane's key channels in the prologue
