@@ -25,6 +25,21 @@
 namespace kda {
 namespace {
 
+// The state is streamed: read once and written once per step, and by the next
+// step of the same layer it has long left the caches, so its loads and stores
+// are non-temporal (no cache allocation).  Measured at B=64, H=32,
+// dk=dv=128: 54.2 -> 47.9 us per step.
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float* p)
+{
+    const f32x4v_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_stream(float* p, float4 v)
+{
+    __builtin_nontemporal_store(f32x4v_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v_t*>(p));
+}
+
 template <int DK, int DV>
 struct DecodeShape {
     static constexpr int NCG = DV / 4;                                 // float4 column groups
@@ -72,7 +87,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     float4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        s[m] = *reinterpret_cast<const float4*>(Sp + (size_t)(rg * RPT + m) * DV + cg * 4);
+        s[m] = load_stream(Sp + (size_t)(rg * RPT + m) * DV + cg * 4);
 
     // 2. prologue: thread i < DK owns key channel i
     float qi = 0.f, ki = 0.f, zi = 0.f;
@@ -171,7 +186,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
             sn.x *= alpha_s; sn.y *= alpha_s; sn.z *= alpha_s; sn.w *= alpha_s;
         }
         sn = fma4(kr, d, sn);
-        *reinterpret_cast<float4*>(Sp + (size_t)r * DV + cg * 4) = sn;
+        store_stream(Sp + (size_t)r * DV + cg * 4, sn);
     }
 }
 
