@@ -60,7 +60,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;        // chunk length
 constexpr int DK = 128;      // key dimension handled by the MFMA path
-constexpr int DV_MULT = 32;  // the MFMA path needs dv to be a multiple of this
+constexpr int DV_MULT = 16;  // the MFMA path needs dv to be a multiple of this (one 16-column tile)
 constexpr int NTHREADS = 256;
 
 // ---- workspace record of one (chunk, head), bf16 operands in k-slices of 32:

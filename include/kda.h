@@ -93,8 +93,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * Dimensions: dk, dv in {16, 32, 64, 128} (kda_tkg: dk <= 128); H and the
  * number of sequences at most 65535.  B = 0 or
  * T = 0 is a no-op, except that final_state then receives initial_state (or
- * zeros).  Routing: KDA_CHUNKED with bf16 inputs, dk = 128 and dv a
- * multiple of 32 runs the MFMA chunked kernel (KDA and EJK modes); every
+ * zeros).  Routing: KDA_CHUNKED with bf16 inputs and dk = 128 (any of the
+ * dv above) runs the MFMA chunked kernel (KDA and EJK modes); every
  * other combination runs the exact token-by-token kernel, which computes the
  * same function.  EJK decays are expected to be <= 0 (the ejkernel page
  * says so); the chunked kernel scales by e^{sum of decays} within a chunk,

@@ -139,6 +139,8 @@ def test_workspace_query_is_host_only():
     packed = kda.prefill_workspace_bytes(8, 1, 32768, 32, 128, 128, kda.CHUNKED)
     assert packed == 256 + (512 + 8) * 32 * 66048
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 100, 128, kda.CHUNKED) == 0
+    assert kda.prefill_workspace_bytes(0, 1, 64, 2, 128, 16, kda.CHUNKED) == 2 * 66048   # 16-column tiles
+    assert kda.prefill_workspace_bytes(0, 1, 64, 2, 64, 128, kda.CHUNKED) == 0           # dk 64: token by token
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.QK_L2NORM) == 0
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED, kda.F32) == 0
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED | kda.EJK) == n

@@ -44,7 +44,7 @@ def test_chunked_ragged_small(T):
     _check(inp)
 
 
-@pytest.mark.parametrize("dv", [32, 64])
+@pytest.mark.parametrize("dv", [16, 32, 64])
 def test_chunked_dv_tiles(dv):
     inp = workloads.prefill_inputs(1, 150, 2, 128, dv, seed=200 + dv, init_state=True)
     say("chunked dv=%d" % dv)
