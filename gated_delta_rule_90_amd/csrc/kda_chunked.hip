@@ -399,8 +399,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
             }
         }
         // the inputs are in qraw, kraw, cb0, cb1 and VEC now: fetch the next item's
+        // (unconditionally: past the end this reloads the current item, which keeps
+        // the loaded registers out of a branch and saves copying them around the loop)
         it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
-        if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, lane, blk);
+        prep_load<EJK>(cur, it.valid ? it : me, q, k, g, beta, H, lane, blk);
         lds_barrier();
 
         // ---------------- phase 1b: decay factors; QL, KL, KRd and Kg^T in LDS; Qg, Kc^T out
