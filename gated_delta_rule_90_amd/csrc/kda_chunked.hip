@@ -626,13 +626,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 float t[16];
     #pragma unroll
                 for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.f : 0.f;
-                const float* arow = AB + (16 * I) * SA + 16 * I;
+                // column-oriented: once t[s] is final it updates every later row, so the
+                // dependent chain is 15 steps long instead of 120 (t[s] = 0 for s < j)
+                const float* ablk = AB + (16 * I) * SA + 16 * I;
     #pragma unroll
-                for (int r = 1; r < 16; ++r) {
-                    float acc = 0.f;
+                for (int s = 0; s < 15; ++s) {
+                    const float ts = t[s];
     #pragma unroll
-                    for (int s = 0; s < r; ++s) acc = fmaf(arow[r * SA + s], t[s], acc);
-                    if (r > j) t[r] = -acc;
+                    for (int r = s + 1; r < 16; ++r) t[r] = fmaf(-ablk[r * SA + s], ts, t[r]);
                 }
                 const float bj = VEC[V_BETA + 16 * I + j];
                 uint16_t* tc = TCOL + (16 * I + j) * ST + 16 * I;
