@@ -11,6 +11,7 @@ The same JSON line also carries:
   roofline      the decode kernel against MI355X's 8 TB/s HBM (algorithmic
                 bytes per launch / mean launch time from HIP events)
   cpu_baseline  the float64 CPU oracle timed on the host on a bounded sample
+                (decode here; the prefill entry carries its own)
   prefill       chunked prefill tokens/s for B=4, T=4096, H=16, dk=dv=128
                 (bf16 inputs) with its own roofline fractions (--no-prefill
                 skips it)
@@ -156,6 +157,34 @@ def cpu_decode_baseline(inp, budget_s=10.0):
     return {"value": round(reps / el, 3), "unit": "decode steps/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{reps} full decode steps (B=64, H=32, dk=dv=128, float64) in {el:.1f} s"}
+
+
+def cpu_prefill_baseline(budget_s=5.0):
+    """The float64 oracle on a bounded sample of the B4 T4096 H16 workload: all
+    four sequences of the first few heads (enough (sequence, head) units for every
+    core), repeated for about budget_s; reported as tokens/s over all 16 heads."""
+    from gated_delta_rule_90_amd import workloads
+    from oracle import kda_oracle
+    kda_oracle.build(force=False)
+    threads = kda_oracle.max_threads()
+    inp = workloads.prefill_b4_t4096_h16_d128()
+    B, T, H, _ = inp.q.shape
+    nh = min(H, max(1, -(-threads // B)))
+    hs = slice(0, nh)
+    args = (inp.q[:, :, hs], inp.k[:, :, hs], inp.v[:, :, hs], inp.g[:, :, hs], inp.beta[:, :, hs],
+            inp.a_log[hs], inp.dt_bias[:, hs])
+    t0 = time.perf_counter()
+    kda_oracle.prefill(*args, scale=inp.scale, lower_bound=inp.lower_bound)
+    one = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(one, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        kda_oracle.prefill(*args, scale=inp.scale, lower_bound=inp.lower_bound)
+    el = time.perf_counter() - t0
+    token_heads = reps * B * T * nh
+    return {"value": round(token_heads / H / el, 1), "unit": "prefill tokens/s (all 16 heads)",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x (4 sequences x 4096 tokens x {nh} heads), float64, in {el:.1f} s"}
 
 
 def _prefill_run(inp, steps, warmup, nsets=1, split=None):
@@ -316,6 +345,8 @@ def main():
         line["configs"] = bench_configs(max(3, args.steps // 40), max(1, args.warmup // 10))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_decode_baseline(inp, args.cpu_budget)
+        if "prefill" in line:
+            line["prefill"]["cpu_baseline"] = cpu_prefill_baseline(args.cpu_budget / 2)
     print(json.dumps(line), flush=True)
 
 
