@@ -269,7 +269,8 @@ struct PrepRaw {
 
 // Rows past the sequence read the chunk's first row; they are zeroed on use.
 // EJK: g is [tokens][H] (one decay per token and head; NULL = no decay).
-template <bool EJK>
+// PART 0 loads q, k and beta, PART 1 the gates (half of the bytes), PART 2 both.
+template <bool EJK, int PART = 2>
 __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const bf16_t* q, const bf16_t* k,
                                           const float* g, const float* beta, int H, int lane, int blk)
 {
@@ -283,19 +284,25 @@ __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const 
     for (int m = 0; m < 16; ++m) {
         const int rr = 16 * blk + m;
         const int off = ((rr < it.len) ? rr : 0) * rstride;
-        r.q[m] = *reinterpret_cast<const uint32_t*>(qb + off);
-        r.k[m] = *reinterpret_cast<const uint32_t*>(kb + off);
-        if constexpr (EJK) {
-            r.g0[m] = g ? g[(size_t)(it.c0 + ((rr < it.len) ? rr : 0)) * H + it.h] : 0.f;
-            r.g1[m] = 0.f;
-        } else {
-            const float2 gg = *reinterpret_cast<const float2*>(gb + off);
-            r.g0[m] = gg.x;
-            r.g1[m] = gg.y;
+        if constexpr (PART != 1) {
+            r.q[m] = *reinterpret_cast<const uint32_t*>(qb + off);
+            r.k[m] = *reinterpret_cast<const uint32_t*>(kb + off);
+        }
+        if constexpr (PART != 0) {
+            if constexpr (EJK) {
+                r.g0[m] = g ? g[(size_t)(it.c0 + ((rr < it.len) ? rr : 0)) * H + it.h] : 0.f;
+                r.g1[m] = 0.f;
+            } else {
+                const float2 gg = *reinterpret_cast<const float2*>(gb + off);
+                r.g0[m] = gg.x;
+                r.g1[m] = gg.y;
+            }
         }
     }
-    const int rb = 16 * blk + (lane & 15);
-    r.beta = beta[(size_t)(it.c0 + ((rb < it.len) ? rb : 0)) * H + it.h];
+    if constexpr (PART != 1) {
+        const int rb = 16 * blk + (lane & 15);
+        r.beta = beta[(size_t)(it.c0 + ((rb < it.len) ? rb : 0)) * H + it.h];
+    }
 }
 
 template <bool EJK>
@@ -398,11 +405,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 VEC[V_BETA + r] = (r < len) ? (EJK ? cur.beta : sigmoid_f(cur.beta)) : 0.f;
             }
         }
-        // the inputs are in qraw, kraw, cb0, cb1 and VEC now: fetch the next item's
-        // (unconditionally: past the end this reloads the current item, which keeps
-        // the loaded registers out of a branch and saves copying them around the loop)
+        // the inputs are in qraw, kraw, cb0, cb1 and VEC now: fetch the next item's,
+        // q, k and beta here and the gates after phase 1b, so that a CU's limited
+        // outstanding requests drain under this item's compute instead of stalling
+        // issue in one place (unconditionally: past the end this reloads the current
+        // item, which keeps the loaded registers out of a branch)
         it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
-        prep_load<EJK>(cur, it.valid ? it : me, q, k, g, beta, H, lane, blk);
+        const PrepItem nx = it.valid ? it : me;
+        prep_load<EJK, 0>(cur, nx, q, k, g, beta, H, lane, blk);
         lds_barrier();
 
         // ---------------- phase 1b: decay factors; QL, KL, KRd and Kg^T in LDS; Qg, Kc^T out
@@ -526,6 +536,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
             VEC[V_C + blk * DK + ch + 1] = c_1;
         }
         lds_barrier();
+
+        prep_load<EJK, 1>(cur, nx, q, k, g, beta, H, lane, blk);
 
         // ---------------- phase 2: A and P on 16x16 block pairs (I >= J)
         f32x4_t accA[3], accP[3];
