@@ -10,8 +10,9 @@
 // (request, head) item.  Its 256 threads hold the whole [dk, dv] slice in
 // registers as float4 columns: thread (rg, cg) keeps rows rg*RPT .. +RPT-1 of
 // columns 4cg .. 4cg+3, so every load and store instruction of a wave covers
-// full 512-byte rows.  The state loads are issued first; the prologue
-// (L2 norms, gate, beta) runs while they are in flight.  The pass computes
+// full 512-byte rows.  The prologue's loads are issued just before the state
+// loads, so the prologue (L2 norms, gate, beta) runs while the state is in
+// flight.  The pass computes
 //     S' = Diag(exp gamma) S,  u = S'^T kh,  p = S'^T qh
 // in one sweep, reduces u and p over the rows (lane xor within a wave, then
 // LDS across waves), and writes
@@ -83,20 +84,29 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     const int wave = t / kWave;
     float* Sp = S + (size_t)item * DK * DV;
 
-    // 1. state loads first: RPT float4 per thread
-    float4 s[RPT];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s[m] = load_stream(Sp + (size_t)(rg * RPT + m) * DV + cg * 4);
-
-    // 2. prologue: thread i < DK owns key channel i
-    float qi = 0.f, ki = 0.f, zi = 0.f;
+    // 1. the prologue's few loads first (thread i < DK owns key channel i), then the
+    // state: loads complete in issue order, so the prologue below waits only for
+    // its own values and runs while the state streams in
+    float qi = 0.f, ki = 0.f, gi = 0.f, di = 0.f;
     if (t < DK) {
         const size_t off = ((size_t)b * DK + t) * H + h;
         qi = q[off];
         ki = k[off];
-        if (!EJK) zi = g[off] + (dt_bias ? dt_bias[(size_t)t * H + h] : 0.f);
+        if (!EJK) {
+            gi = g[off];
+            di = dt_bias ? dt_bias[(size_t)t * H + h] : 0.f;
+        }
     }
+    float4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = load_stream(Sp + (size_t)(rg * RPT + m) * DV + cg * 4);
+    // nothing of the prologue may be scheduled above the state loads: its first
+    // use of a loaded value would hold back the rest of the stream
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. prologue: norms, gate, beta
+    const float zi = gi + di;
     {
         const float r0 = wave_sum(qi * qi), r1 = wave_sum(ki * ki), r2 = wave_sum(qi * ki);
         if (lane == 0) {
