@@ -204,19 +204,49 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int T, int&
 }
 
 // ------------------------------------------------------------------------
-// chunk offsets of packed sequences: off[n] = sum_{m<n} ceil(len_m / 64)
-__global__ __launch_bounds__(64) void chunk_offsets_kernel(const int32_t* __restrict__ cu, int N, int T,
-                                                           int32_t* __restrict__ off)
+// Plan of a packed batch: chunk offsets off[n] = sum_{m<n} ceil(len_m / 64),
+// and order[] = the sequences by decreasing chunk count (ties by index).  The
+// scan hands out its workgroups in that order, longest chains first, so the
+// longest sequences do not start last (list scheduling by decreasing length).
+// Above PLAN_SORT_MAX sequences the order is the identity.
+constexpr int PLAN_THREADS = 256;
+constexpr int PLAN_SORT_MAX = 2048;
+
+__global__ __launch_bounds__(PLAN_THREADS) void chunk_plan_kernel(const int32_t* __restrict__ cu, int N, int T,
+                                                                  int32_t* __restrict__ off,
+                                                                  int32_t* __restrict__ order)
 {
-    if (threadIdx.x != 0) return;
-    int acc = 0;
-    for (int n = 0; n < N; ++n) {
+    __shared__ int nchunks[PLAN_SORT_MAX];
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        int acc = 0;
+        for (int n = 0; n < N; ++n) {
+            int t0, t1;
+            seq_bounds(cu, n, T, t0, t1);
+            off[n] = acc;
+            acc += (t1 - t0 + C - 1) / C;
+        }
+        off[N] = acc;
+    }
+    if (N > PLAN_SORT_MAX) {
+        for (int n = tid; n < N; n += PLAN_THREADS) order[n] = n;
+        return;
+    }
+    for (int n = tid; n < N; n += PLAN_THREADS) {
         int t0, t1;
         seq_bounds(cu, n, T, t0, t1);
-        off[n] = acc;
-        acc += (t1 - t0 + C - 1) / C;
+        nchunks[n] = (t1 - t0 + C - 1) / C;
     }
-    off[N] = acc;
+    __syncthreads();
+    for (int n = tid; n < N; n += PLAN_THREADS) {
+        const int ln = nchunks[n];
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = nchunks[m];
+            rank += (lm > ln || (lm == ln && m < n)) ? 1 : 0;
+        }
+        order[rank] = n;
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -826,8 +856,8 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
 template <int NJB, typename Tout>
 __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ init, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ off, int N, int T, int H, int DV, const unsigned char* __restrict__ ws,
-    Tout* __restrict__ o, float* __restrict__ final_state)
+    const int32_t* __restrict__ off, const int32_t* __restrict__ order, int N, int T, int H, int DV,
+    const unsigned char* __restrict__ ws, Tout* __restrict__ o, float* __restrict__ final_state)
 {
     using Sh = ScanShape<NJB>;
     constexpr int DVT = Sh::DVT;
@@ -851,10 +881,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const int xcd = blockIdx.x & 7;
     const int w8 = blockIdx.x >> 3;
     const int tile = w8 % ntiles;
-    const int unit = (w8 / ntiles) * 8 + xcd;
-    if (unit >= units) return;
-    const int n = unit / H;
-    const int h = unit - n * H;
+    const int urank = (w8 / ntiles) * 8 + xcd;
+    if (urank >= units) return;
+    const int nrank = urank / H;
+    const int h = urank - nrank * H;
+    const int n = order ? order[nrank] : nrank;   // packed batches: longest sequences first
+    const int unit = n * H + h;
     const int j0 = tile * DVT;
 
     int t_begin, t_end;
@@ -1019,7 +1051,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
 }
 
 // workspace: [chunk offsets (N + 1 ints, padded)][records: slots x H x REC_BYTES]
-size_t offsets_bytes(int N) { return ((size_t)(N + 1) * 4 + OFFSETS_BYTES_ALIGN - 1) / OFFSETS_BYTES_ALIGN * OFFSETS_BYTES_ALIGN; }
+// packed plan: off[N + 1] then order[N], int32
+size_t offsets_bytes(int N) { return ((size_t)(2 * N + 1) * 4 + OFFSETS_BYTES_ALIGN - 1) / OFFSETS_BYTES_ALIGN * OFFSETS_BYTES_ALIGN; }
 
 size_t max_slots(int N, int T, bool packed)
 {
@@ -1045,11 +1078,13 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     const bool packed = a.cu != nullptr;
     unsigned char* wsb = static_cast<unsigned char*>(a.workspace);
     int32_t* off = nullptr;
+    int32_t* order = nullptr;
     unsigned char* recs = wsb;
     if (packed) {
         off = reinterpret_cast<int32_t*>(wsb);
         recs = wsb + offsets_bytes(a.N);
-        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, stream, a.cu, a.N, a.T, off);
+        order = off + a.N + 1;
+        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.cu, a.N, a.T, off, order);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1079,14 +1114,14 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     const bf16_t* vv = static_cast<const bf16_t*>(a.v);
     Tout* oo = static_cast<Tout*>(a.o);
     if (njb == 4)
-        hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
-                           a.T, a.H, a.dv, recs, oo, a.final_state);
+        hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
+                           order, a.N, a.T, a.H, a.dv, recs, oo, a.final_state);
     else if (njb == 2)
-        hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
-                           a.T, a.H, a.dv, recs, oo, a.final_state);
+        hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
+                           order, a.N, a.T, a.H, a.dv, recs, oo, a.final_state);
     else
-        hipLaunchKernelGGL((chunk_scan_kernel<1, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off, a.N,
-                           a.T, a.H, a.dv, recs, oo, a.final_state);
+        hipLaunchKernelGGL((chunk_scan_kernel<1, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
+                           order, a.N, a.T, a.H, a.dv, recs, oo, a.final_state);
     return hipGetLastError();
 }
 
