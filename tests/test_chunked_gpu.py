@@ -215,3 +215,20 @@ def test_chunked_long_context_t65536_h32_split_and_sampled():
     eo, es = rel_l2(o[:, :, heads], ro), rel_l2(s[:, heads], rs)
     say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
     assert eo <= TOL and es <= TOL, (eo, es)
+
+
+@pytest.mark.parametrize("nseq", [300, 2100])
+def test_chunked_varlen_many_sequences(nseq):
+    """Many packed sequences with repeated and zero lengths: the longest-first
+    scan order (sorted up to 2048 sequences, identity beyond) must not change
+    any result."""
+    rng = np.random.default_rng(nseq)
+    lens = rng.integers(0, 131, nseq)
+    lens[::7] = 64                      # ties
+    lens[3::11] = 0                     # empty sequences
+    inp = workloads.prefill_inputs(1, 0, 2, 128, 32, seed=1200 + nseq, lengths=list(lens),
+                                   init_state=True)
+    say("chunked varlen", nseq, "sequences, total", int(lens.sum()))
+    o, s = _check(inp)
+    empty = np.flatnonzero(lens == 0)
+    np.testing.assert_array_equal(s[empty], inp.initial_state[empty])
