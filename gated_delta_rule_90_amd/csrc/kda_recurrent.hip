@@ -12,11 +12,22 @@
 // (EJK: u from the undecayed column, s <- e^d s + kh beta (v_c - u)).
 // Packed sequences come from cu_seqlens (ejkernel "recurrent" run()); bounds
 // read from device memory are clamped to [0, T].
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
+
+// The per-token gate sits on the kernel's dependent chain: hardware exp2 and
+// reciprocal (about 1 ulp each) instead of the correctly rounded library
+// sequences, well inside the fp32 path's 1e-5 relative bound.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float fast_sigmoid(float x)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
 
 template <int DK, typename Tin, typename Tout, bool EJK>
 __global__ __launch_bounds__(kWave) void recurrent_kernel(
@@ -59,19 +70,53 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         dtb[p] = (!EJK && dt_bias && i < DK) ? dt_bias[(size_t)i * H + h] : 0.f;
     }
 
-    for (int t = t0; t < t1; ++t) {
+    // Inputs of token t + PD are loaded while token t is computed (a ring of PD
+    // register sets, the loop unrolled by PD so that no set is copied), which
+    // hides the global-memory latency that otherwise every token would pay.
+    // Loads past the end reload the last token (in bounds, unused); steps past
+    // the end leave the state and the output untouched.
+    // The ring holds the loaded values as they arrive; everything computed from
+    // them happens at use, so no instruction waits on a load right after issue.
+    constexpr int PD = (DK >= 128) ? 1 : 4;   // dk = 128: the column already takes 128 registers
+    struct Raw {
+        Tin q[PER_LANE], k[PER_LANE];
+        float z[PER_LANE];
+        float bt, vc;
+    };
+    const int cc = active ? c : 0;
+    auto load = [&](Raw& r, int t) {
+        t = min(t, t1 - 1);
         const size_t th = (size_t)t * H + h;
-        float qv[PER_LANE], kv[PER_LANE], zv[PER_LANE];
-        float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
             const int i = lane + p * kWave;
-            qv[p] = kv[p] = zv[p] = 0.f;
-            if (i < DK) {
-                qv[p] = to_f32(q[th * DK + i]);
-                kv[p] = to_f32(k[th * DK + i]);
-                if (!EJK) zv[p] = g[th * DK + i] + dtb[p];
-            }
+            const int ic = (i < DK) ? i : 0;   // lanes past dk read channel 0 and are zeroed on use
+            r.q[p] = q[th * DK + ic];
+            r.k[p] = k[th * DK + ic];
+            if (!EJK) r.z[p] = g[th * DK + ic];
+        }
+        r.bt = beta[th];
+        if (EJK) r.z[0] = g ? g[th] : 0.f;   // EJK: the token's scalar log-decay
+        r.vc = to_f32(v[th * DV + cc]);
+    };
+    Raw ring[PD];
+    if (t0 < t1) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) load(ring[j], t0 + j);
+    }
+    // one token from ring slot J (a compile-time index, so the ring stays in registers)
+    auto token = [&](auto J, const int tb) {
+        constexpr int j = decltype(J)::value;
+        const int t = tb + j;
+        const bool live = t < t1;
+        const Raw& r = ring[j];
+        float qv[PER_LANE], kv[PER_LANE];
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int p = 0; p < PER_LANE; ++p) {
+            const bool in = lane + p * kWave < DK;
+            qv[p] = in ? to_f32(r.q[p]) : 0.f;
+            kv[p] = in ? to_f32(r.k[p]) : 0.f;
             sq += qv[p] * qv[p];
             sk += kv[p] * kv[p];
         }
@@ -85,34 +130,55 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
             if (i < DK) {
                 sh_q[i] = qv[p] * nq;
                 sh_k[i] = kv[p] * nk;
-                if (!EJK) sh_alpha[i] = expf(lower_bound * sigmoid_f(ea * zv[p]));
+                if (!EJK) sh_alpha[i] = fast_exp(lower_bound * fast_sigmoid(ea * (r.z[p] + dtb[p])));
             }
         }
         float bt, alpha_s = 1.0f;
         if (!EJK) {
-            bt = sigmoid_f(beta[th]);
+            bt = fast_sigmoid(r.bt);
         } else {
-            bt = beta[th];
-            alpha_s = g ? expf(g[th]) : 1.0f;
+            bt = r.bt;
+            alpha_s = fast_exp(r.z[0]);
         }
-        const float vc = active ? to_f32(v[th * DV + c]) : 0.f;
-        __syncthreads();
+        lds_barrier();
 
-        float u = 0.f;
+        if (live) {
+            // four partial sums per dot product: the per-token dependent chain is
+            // what bounds this kernel, not its arithmetic
+            constexpr int NP = (DK >= 4) ? 4 : 1;
+            float up[NP];
 #pragma unroll
-        for (int i = 0; i < DK; ++i) {
-            if (!EJK) s[i] *= sh_alpha[i];
-            u = fmaf(s[i], sh_k[i], u);
-        }
-        const float d = bt * (vc - u);
-        float oc = 0.f;
+            for (int e = 0; e < NP; ++e) up[e] = 0.f;
 #pragma unroll
-        for (int i = 0; i < DK; ++i) {
-            s[i] = fmaf(sh_k[i], d, EJK ? alpha_s * s[i] : s[i]);
-            oc = fmaf(s[i], sh_q[i], oc);
+            for (int i = 0; i < DK; ++i) {
+                if (!EJK) s[i] *= sh_alpha[i];
+                up[i % NP] = fmaf(s[i], sh_k[i], up[i % NP]);
+            }
+            float u = up[0];
+#pragma unroll
+            for (int e = 1; e < NP; ++e) u += up[e];
+            const float d = bt * (r.vc - u);
+            float op[NP];
+#pragma unroll
+            for (int e = 0; e < NP; ++e) op[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < DK; ++i) {
+                s[i] = fmaf(sh_k[i], d, EJK ? alpha_s * s[i] : s[i]);
+                op[i % NP] = fmaf(s[i], sh_q[i], op[i % NP]);
+            }
+            float oc = op[0];
+#pragma unroll
+            for (int e = 1; e < NP; ++e) oc += op[e];
+            if (active) o[((size_t)t * H + h) * DV + c] = from_f32<Tout>(oc);
         }
-        if (active) o[th * DV + c] = from_f32<Tout>(oc);
-        __syncthreads();
+        lds_barrier();   // the next token rewrites the prologue vectors
+        load(ring[j], t + PD);
+    };
+    for (int tb = t0; tb < t1; tb += PD) {
+        token(std::integral_constant<int, 0>{}, tb);
+        if constexpr (PD > 1) token(std::integral_constant<int, (PD > 1 ? 1 : 0)>{}, tb);
+        if constexpr (PD > 2) token(std::integral_constant<int, (PD > 2 ? 2 : 0)>{}, tb);
+        if constexpr (PD > 3) token(std::integral_constant<int, (PD > 3 ? 3 : 0)>{}, tb);
     }
 
     if (final_state && active) {
