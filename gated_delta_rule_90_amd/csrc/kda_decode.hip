@@ -153,12 +153,11 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
         p = fma4(sh_q[r], s[m], p);
     }
     // reduce over row groups: lanes of one wave that share cg, then waves
-#pragma unroll
-    for (int off = NCG; off < kWave; off <<= 1) {
-        u.x += __shfl_xor(u.x, off, kWave); u.y += __shfl_xor(u.y, off, kWave);
-        u.z += __shfl_xor(u.z, off, kWave); u.w += __shfl_xor(u.w, off, kWave);
-        p.x += __shfl_xor(p.x, off, kWave); p.y += __shfl_xor(p.y, off, kWave);
-        p.z += __shfl_xor(p.z, off, kWave); p.w += __shfl_xor(p.w, off, kWave);
+    if constexpr (NCG < kWave) {
+        u.x = xor_sum_from<NCG>(u.x); u.y = xor_sum_from<NCG>(u.y);
+        u.z = xor_sum_from<NCG>(u.z); u.w = xor_sum_from<NCG>(u.w);
+        p.x = xor_sum_from<NCG>(p.x); p.y = xor_sum_from<NCG>(p.y);
+        p.z = xor_sum_from<NCG>(p.z); p.w = xor_sum_from<NCG>(p.w);
     }
     if (NWAVES > 1) {
         if (lane < NCG) {

@@ -32,12 +32,70 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x)
 // Numerically safe logistic: 1 / (1 + e^-x); exp overflow gives 0, underflow 1.
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-template <int W = kWave>
+// Cross-lane sums on VALU data paths instead of LDS permutes (ds_bpermute, one
+// LDS round trip per step): DPP within quads and 16-lane rows, ds_swizzle for
+// the xor-4/8 partners, and gfx950's v_permlane16/32_swap between rows and
+// halves.  A swap of a value with a copy of itself leaves, in every lane, the
+// value of the lane's own row (half) in one register and that of the partner
+// row (half) in the other, so their sum is x + partner(x).  The swaps are
+// written as inline assembly: the compiler's builtins for them return the
+// first result twice.  The s_nop before covers the VALU-write-to-permlane-read
+// hazard, the one after the permlane-write-to-VALU-read side.
+__device__ __forceinline__ float swap_add16(float x)
+{
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return a + b;
+}
+__device__ __forceinline__ float swap_add32(float x)
+{
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return a + b;
+}
+
+template <int OFF>
+__device__ __forceinline__ float xor_add(float x)
+{
+    static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "power of two < 64");
+    const int xi = __builtin_bit_cast(int, x);
+    if constexpr (OFF == 1) {
+        return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    } else if constexpr (OFF == 2) {
+        return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    } else if constexpr (OFF == 4 || OFF == 8) {
+        return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(xi, 0x1F | (OFF << 10)));   // lane ^ OFF
+    } else if constexpr (OFF == 16) {
+        return swap_add16(x);
+    } else {
+        return swap_add32(x);
+    }
+}
+
+// x summed over the lanes that agree with this one outside bits [log2 FROM, 6):
+// lanes l and l ^ OFF for every OFF = FROM, 2 FROM, ..., 32.  The whole wave must be active.
+template <int FROM>
+__device__ __forceinline__ float xor_sum_from(float x)
+{
+    if constexpr (FROM <= 1) x = xor_add<1>(x);
+    if constexpr (FROM <= 2) x = xor_add<2>(x);
+    if constexpr (FROM <= 4) x = xor_add<4>(x);
+    if constexpr (FROM <= 8) x = xor_add<8>(x);
+    if constexpr (FROM <= 16) x = xor_add<16>(x);
+    if constexpr (FROM <= 32) x = xor_add<32>(x);
+    return x;
+}
+
+// Sum over the 64 lanes of a wave, in every lane.  The whole wave must be active.
 __device__ __forceinline__ float wave_sum(float x)
 {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
-    return x;
+    const int xi0 = __builtin_bit_cast(int, x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi0, 0xB1, 0xF, 0xF, false));                 // quads
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));  // row_half_mirror: 8
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));  // row_mirror: 16
+    x = xor_add<16>(x);
+    return xor_add<32>(x);
 }
 
 // Workgroup barrier that orders LDS traffic only: it waits for this wave's
