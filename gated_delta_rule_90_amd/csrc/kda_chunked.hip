@@ -152,40 +152,39 @@ __device__ __forceinline__ uint4 pack8(const float* x)
 }
 
 // Sum 16 per-row partials over the 64 lanes of a wave.  On return lane l
-// holds the total of row (l >> 2).
+// holds the total of row (l >> 2).  Each step halves the entries a lane
+// carries and sums over a lane partner: the two halves and the row pairs by
+// permlane swaps (the swap itself routes entry k to one side and entry
+// k + width to the other), then partners whose lane bits 3 and 2 differ by DPP
+// mirrors within a row and a half row (lane i <-> 15 - i, 7 - i), and last the
+// quad.
 __device__ __forceinline__ float rowsum16(float (&a)[16], int lane)
 {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const bool hi = lane & 32;
-        const float send = hi ? a[k] : a[k + 8];
-        const float keep = hi ? a[k + 8] : a[k];
-        a[k] = keep + __shfl_xor(send, 32, kWave);
+        swap_halves32(a[k], a[k + 8]);
+        a[k] += a[k + 8];
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const bool hi = lane & 16;
-        const float send = hi ? a[k] : a[k + 4];
-        const float keep = hi ? a[k + 4] : a[k];
-        a[k] = keep + __shfl_xor(send, 16, kWave);
+        swap_rows16(a[k], a[k + 4]);
+        a[k] += a[k + 4];
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const bool hi = lane & 8;
         const float send = hi ? a[k] : a[k + 2];
         const float keep = hi ? a[k + 2] : a[k];
-        a[k] = keep + __shfl_xor(send, 8, kWave);
+        a[k] = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0x140, 0xF, 0xF, false));
     }
+    float s;
     {
         const bool hi = lane & 4;
         const float send = hi ? a[0] : a[1];
         const float keep = hi ? a[1] : a[0];
-        a[0] = keep + __shfl_xor(send, 4, kWave);
+        s = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0x141, 0xF, 0xF, false));
     }
-    float s = a[0];
-    s += __shfl_xor(s, 2, kWave);
-    s += __shfl_xor(s, 1, kWave);
-    return s;
+    return xor_add<1>(xor_add<2>(s));
 }
 
 // index of the off-diagonal pair (I, J), I > J, in the pair-vector table

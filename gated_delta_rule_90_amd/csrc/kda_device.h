@@ -35,23 +35,36 @@ __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf
 // Cross-lane sums on VALU data paths instead of LDS permutes (ds_bpermute, one
 // LDS round trip per step): DPP within quads and 16-lane rows, ds_swizzle for
 // the xor-4/8 partners, and gfx950's v_permlane16/32_swap between rows and
-// halves.  A swap of a value with a copy of itself leaves, in every lane, the
-// value of the lane's own row (half) in one register and that of the partner
-// row (half) in the other, so their sum is x + partner(x).  The swaps are
-// written as inline assembly: the compiler's builtins for them return the
-// first result twice.  The s_nop before covers the VALU-write-to-permlane-read
-// hazard, the one after the permlane-write-to-VALU-read side.
+// halves.
+//
+// swap_rows16(x, y): rows are the four 16-lane groups; afterwards
+//     x = (x.row0, y.row0, x.row2, y.row2),  y = (x.row1, y.row1, x.row3, y.row3).
+// swap_halves32(x, y): afterwards x = (x.lo, y.lo), y = (x.hi, y.hi).
+// So x + y holds, in the lanes of the first row (half) of each pair, the sum of
+// x over the pair and, in the second, the sum of y: a transposing reduction
+// step.  For y = x, x + y = x + partner(x) in every lane.
+// The swaps are inline assembly: the compiler's builtins for them return the
+// first result twice.  The s_nop covers the hazard of a VALU write read by the
+// permlane two instructions later.
+__device__ __forceinline__ void swap_rows16(float& x, float& y)
+{
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void swap_halves32(float& x, float& y)
+{
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
 __device__ __forceinline__ float swap_add16(float x)
 {
-    float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    return a + b;
+    float y = x;
+    swap_rows16(x, y);
+    return x + y;
 }
 __device__ __forceinline__ float swap_add32(float x)
 {
-    float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    return a + b;
+    float y = x;
+    swap_halves32(x, y);
+    return x + y;
 }
 
 template <int OFF>
