@@ -128,7 +128,7 @@ def bench_decode(steps, warmup, nbuf=5):
     ms = e0.elapsed_time(e1) / steps
     nbytes = decode_bytes(B, H, dk, dv)
     achieved = nbytes / (ms * 1e-3) / 1e9
-    sh = _src_hash("kda_decode.hip")
+    sh = _src_hash("kda_decode.hip", "kda_device.h")
     traffic = _counter_traffic("decode_b64_h32_d128", sh)
     return inp, {
         "ms": ms, "wall_s": wall, "steps_per_s": 1e3 / ms, "bytes": nbytes,
