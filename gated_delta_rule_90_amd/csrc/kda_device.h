@@ -111,6 +111,18 @@ __device__ __forceinline__ float wave_sum(float x)
     return xor_add<32>(x);
 }
 
+// A zero held in a vector register that the compiler cannot see through.
+// Added to a uniform index it turns the load into a per-lane (vector) load.
+// That matters for prefetches: scalar loads share the lgkm counter with LDS
+// operations, so the next LDS barrier would wait for a scalar prefetch to
+// arrive from memory.
+__device__ __forceinline__ int vector_zero()
+{
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
 // Workgroup barrier that orders LDS traffic only: it waits for this wave's
 // LDS operations and then for every wave of the workgroup.  Unlike
 // __syncthreads() it does not drain the vector memory counter, so global loads

@@ -84,6 +84,7 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         float bt, vc;
     };
     const int cc = active ? c : 0;
+    const int vz = vector_zero();   // beta and the EJK decay: vector loads, see vector_zero()
     auto load = [&](Raw& r, int t) {
         t = min(t, t1 - 1);
         const size_t th = (size_t)t * H + h;
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
             r.k[p] = k[th * DK + ic];
             if (!EJK) r.z[p] = g[th * DK + ic];
         }
-        r.bt = beta[th];
-        if (EJK) r.z[0] = g ? g[th] : 0.f;   // EJK: the token's scalar log-decay
+        r.bt = beta[th + vz];
+        if (EJK) r.z[0] = g ? g[th + vz] : 0.f;   // EJK: the token's scalar log-decay
         r.vc = to_f32(v[th * DV + cc]);
     };
     Raw ring[PD];
@@ -104,6 +105,11 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
 #pragma unroll
         for (int j = 0; j < PD; ++j) load(ring[j], t0 + j);
     }
+    // the initial state has to be in registers before the loop: taking it here
+    // (after the ring loads are issued) keeps the loop's waits precise instead
+    // of a full drain of the prefetch at every token
+#pragma unroll
+    for (int i = 0; i < DK; ++i) asm volatile("" ::"v"(s[i]));
     // one token from ring slot J (a compile-time index, so the ring stays in registers)
     auto token = [&](auto J, const int tb) {
         constexpr int j = decltype(J)::value;
