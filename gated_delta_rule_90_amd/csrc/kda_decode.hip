@@ -88,6 +88,12 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     // state: loads complete in issue order, so the prologue below waits only for
     // its own values and runs while the state streams in
     float qi = 0.f, ki = 0.f, gi = 0.f, di = 0.f;
+    // the item's scalars go out with them as vector loads (see vector_zero()):
+    // as scalar loads they would be issued late and waited for at an LDS barrier
+    const int vz = vector_zero();
+    const float braw = beta[item + vz];
+    const float araw = EJK ? 0.f : a_log[h + vz];
+    const float draw = (EJK && g) ? g[item + vz] : 0.f;
     if (t < DK) {
         const size_t off = ((size_t)b * DK + t) * H + h;
         qi = q[off];
@@ -128,15 +134,15 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     const float kq = sqk * nq * nk;  // kh . qh
     float bt, alpha_s = 1.0f;
     if (!EJK) {
-        bt = sigmoid_f(beta[item]);
+        bt = sigmoid_f(braw);
     } else {
-        bt = beta[item];
-        alpha_s = g ? expf(g[item]) : 1.0f;
+        bt = braw;
+        alpha_s = g ? expf(draw) : 1.0f;
     }
     if (t < DK) {
         sh_q[t] = qi * nq;
         sh_k[t] = ki * nk;
-        if (!EJK) sh_alpha[t] = expf(lower_bound * sigmoid_f(expf(a_log[h]) * zi));
+        if (!EJK) sh_alpha[t] = expf(lower_bound * sigmoid_f(expf(araw) * zi));
     }
     lds_barrier();
 
