@@ -17,7 +17,11 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_recurrent.hip", "kda_chunked.hip"]
+# (source, object name, extra flags): the recurrent kernel is built once per key
+# dimension so that its instantiations compile in parallel
+SOURCES = [("kda_api.cpp", "kda_api", []), ("kda_decode.hip", "kda_decode", []),
+           ("kda_chunked.hip", "kda_chunked", [])] + \
+    [("kda_recurrent.hip", f"kda_recurrent_dk{dk}", [f"-DKDA_RECURRENT_DK={dk}"]) for dk in (16, 32, 64, 128)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -30,9 +34,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry) -> str:
+    src, name, extra = entry
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

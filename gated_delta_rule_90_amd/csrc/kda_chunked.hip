@@ -175,14 +175,14 @@ __device__ __forceinline__ float rowsum16(float (&a)[16], int lane)
         const bool hi = lane & 8;
         const float send = hi ? a[k] : a[k + 2];
         const float keep = hi ? a[k + 2] : a[k];
-        a[k] = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0x140, 0xF, 0xF, false));
+        a[k] = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0x140, 0xF, 0xF, true));
     }
     float s;
     {
         const bool hi = lane & 4;
         const float send = hi ? a[0] : a[1];
         const float keep = hi ? a[1] : a[0];
-        s = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0x141, 0xF, 0xF, false));
+        s = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0x141, 0xF, 0xF, true));
     }
     return xor_add<1>(xor_add<2>(s));
 }

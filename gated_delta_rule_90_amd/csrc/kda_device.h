@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace kda {
@@ -73,9 +75,9 @@ __device__ __forceinline__ float xor_add(float x)
     static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "power of two < 64");
     const int xi = __builtin_bit_cast(int, x);
     if constexpr (OFF == 1) {
-        return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+        return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
     } else if constexpr (OFF == 2) {
-        return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+        return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
     } else if constexpr (OFF == 4 || OFF == 8) {
         return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(xi, 0x1F | (OFF << 10)));   // lane ^ OFF
     } else if constexpr (OFF == 16) {
@@ -99,17 +101,30 @@ __device__ __forceinline__ float xor_sum_from(float x)
     return x;
 }
 
-// Sum over the 64 lanes of a wave, in every lane.  The whole wave must be active.
-__device__ __forceinline__ float wave_sum(float x)
+// Sum over each aligned group of N lanes (N = 16, 32 or 64), in every lane of
+// the group: quads and rows by DPP (the row mirrors pair lanes whose partial
+// sums are already equal within their quad and half row), then rows and halves
+// by permlane swaps.  The whole wave must be active.  The DPP moves request
+// bound_ctrl, which lets the compiler fold each into its add; every source
+// lane of these patterns exists, so it does not change the result.
+template <int N>
+__device__ __forceinline__ float group_sum(float x)
 {
-    const int xi0 = __builtin_bit_cast(int, x);
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi0, 0xB1, 0xF, 0xF, false));                 // quads
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));  // row_half_mirror: 8
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));  // row_mirror: 16
-    x = xor_add<16>(x);
-    return xor_add<32>(x);
+    static_assert(N == 16 || N == 32 || N == 64, "group of 16, 32 or 64 lanes");
+    auto dpp_add = [](float v, auto ctrl) {
+        return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    x = dpp_add(x, std::integral_constant<int, 0xB1>{});    // quad_perm 1,0,3,2
+    x = dpp_add(x, std::integral_constant<int, 0x4E>{});    // quad_perm 2,3,0,1
+    x = dpp_add(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    x = dpp_add(x, std::integral_constant<int, 0x140>{});   // row_mirror
+    if constexpr (N >= 32) x = swap_add16(x);
+    if constexpr (N >= 64) x = swap_add32(x);
+    return x;
 }
+
+// Sum over the 64 lanes of a wave, in every lane.  The whole wave must be active.
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
 // A zero held in a vector register that the compiler cannot see through.
 // Added to a uniform index it turns the load into a per-lane (vector) load.

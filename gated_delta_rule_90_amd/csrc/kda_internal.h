@@ -52,7 +52,20 @@ struct DecodeArgs {
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_recurrent(const PrefillArgs& a, hipStream_t stream);
+// the recurrent kernel, one object per key dimension
+hipError_t launch_recurrent_dk16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_recurrent_dk32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_recurrent_dk64(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_recurrent_dk128(const PrefillArgs& a, hipStream_t stream);
+inline hipError_t launch_recurrent(const PrefillArgs& a, hipStream_t stream)
+{
+    switch (a.dk) {
+    case 16: return launch_recurrent_dk16(a, stream);
+    case 32: return launch_recurrent_dk32(a, stream);
+    case 64: return launch_recurrent_dk64(a, stream);
+    default: return launch_recurrent_dk128(a, stream);
+    }
+}
 hipError_t launch_chunked(const PrefillArgs& a, hipStream_t stream);
 bool chunked_supported(const PrefillArgs& a);
 size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed);

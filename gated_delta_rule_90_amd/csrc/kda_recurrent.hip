@@ -1,18 +1,23 @@
 // kda_recurrent.hip - token-by-token KDA prefill (ejkernel use_chunked=False:
 // "Recurrent: Pure sequential scan for memory efficiency").
 //
-// Grid (dv / 64 column tiles, H, N sequences); one wave per block.  Lane j
-// owns state column c = 64 * tile + j as dk float32 registers, so the
-// contractions over dk (S^T k, S^T q) stay inside the lane and the only
-// cross-lane work per token is the L2 norm of q and k.  Per token: load
-// q, k, g into LDS-shared prologue vectors (lanes own channels j and j + 64),
-// reduce the squared norms over the wave, activate the gate and beta, then
+// Grid (column tiles, H, N sequences); one wave per block.  Each state column
+// is held in registers by LPC adjacent lanes (LPC = 4 for dv = 16, 2 for
+// dv = 32, else 1), dk / LPC rows each, so the contractions over dk (S^T k,
+// S^T q) stay in registers up to a sum over those lanes, and the only other
+// cross-lane work per token is the L2 norm of q and k.  Per token: q, k, g
+// become LDS-shared prologue vectors (lanes own channels j and j + 64), the
+// squared norms are reduced over the wave, the gate and beta activated, then
 // every lane advances its column:
 //     s <- exp(gamma) * s;  u = s . kh;  s <- s + kh * beta (v_c - u);  o_c = s . qh
 // (EJK: u from the undecayed column, s <- e^d s + kh beta (v_c - u)).
+// It is evaluated as u = (alpha kh) . s_old and p = (alpha qh) . s_old side by
+// side, d = beta (v_c - u), o_c = p + d (kh . qh) and s <- alpha s_old + kh d,
+// which is the same column update with a shorter dependent chain per token.
 // Packed sequences come from cu_seqlens (ejkernel "recurrent" run()); bounds
 // read from device memory are clamped to [0, T].
 #include <type_traits>
+#include <utility>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -20,16 +25,42 @@
 namespace kda {
 namespace {
 
-// The per-token gate sits on the kernel's dependent chain: hardware exp2 and
-// reciprocal (about 1 ulp each) instead of the correctly rounded library
-// sequences, well inside the fp32 path's 1e-5 relative bound.
+// The per-token gate and norms sit on the kernel's dependent chain: hardware
+// exp2, reciprocal and reciprocal square root (about 1 ulp each) instead of the
+// correctly rounded library sequences, well inside the fp32 path's 1e-5
+// relative bound.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float fast_sigmoid(float x)
 {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
-template <int DK, typename Tin, typename Tout, bool EJK>
+// Element i of a row of n elements, stored through a buffer resource that
+// covers just that row: the buffer unit drops stores with i >= n, so lanes
+// past the row need no branch around the store.  The row pointer must be
+// uniform across the wave.
+template <typename T>
+__device__ __forceinline__ void row_store(T* row, int n, int i, T val)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, n * (int)sizeof(T), 0x00020000);
+    if constexpr (sizeof(T) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, i * 4, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, val), rs, i * 2, 0, 0);
+}
+
+// f(integral_constant<int, J>) for J = 0 .. N-1, unrolled at compile time.
+template <typename F, int... J>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, J...>)
+{
+    (f(std::integral_constant<int, J>{}), ...);
+}
+
+// LPC lanes share one state column (LPC = 1, 2 or 4): each holds DK / LPC of
+// its rows, and the column's dot products finish with a sum over the LPC lanes
+// (adjacent lanes, DPP within a quad).  Narrow value heads use LPC > 1, so
+// that more of the wave's lanes carry rows.
+template <int DK, int LPC, typename Tin, typename Tout, bool EJK>
 __global__ __launch_bounds__(kWave) void recurrent_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ a_log,
@@ -38,12 +69,21 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     int l2norm, Tout* __restrict__ o, float* __restrict__ final_state)
 {
     constexpr int PER_LANE = (DK + kWave - 1) / kWave;  // prologue channels per lane
-    __shared__ float sh_alpha[DK];
-    __shared__ float sh_k[DK];
-    __shared__ float sh_q[DK];
+    // prologue vectors, two sets: token t uses set (t - t0) & 1.  They are padded
+    // to whole waves, so every lane writes its slot without a branch (lanes past
+    // dk write values that are never read).
+    constexpr int DKP = PER_LANE * kWave;
+    __shared__ float sh_alpha[2][DKP];   // per-channel decay (KDA)
+    __shared__ float sh_k[2][DKP];       // kh
+    __shared__ float sh_ak[2][DKP];      // alpha * kh (EJK: kh)
+    __shared__ float sh_aq[2][DKP];      // alpha * qh (EJK: qh)
 
+    constexpr int RPL = DK / LPC;        // state rows per lane
+    constexpr int CPW = kWave / LPC;     // state columns per workgroup
+    static_assert(RPL * LPC == DK && RPL >= 4, "rows per lane");
     const int lane = threadIdx.x;
-    const int c = blockIdx.x * kWave + lane;
+    const int part = lane % LPC;         // rows part * RPL .. part * RPL + RPL - 1
+    const int c = blockIdx.x * CPW + lane / LPC;
     const int h = blockIdx.y;
     const int n = blockIdx.z;
     const bool active = c < DV;
@@ -57,10 +97,10 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         t1 = t0 + T;
     }
 
-    float s[DK];
+    float s[RPL];
     const size_t soff = ((size_t)n * H + h) * DK * DV;
 #pragma unroll
-    for (int i = 0; i < DK; ++i) s[i] = (init && active) ? init[soff + (size_t)i * DV + c] : 0.f;
+    for (int m = 0; m < RPL; ++m) s[m] = (init && active) ? init[soff + (size_t)(part * RPL + m) * DV + c] : 0.f;
 
     const float ea = (EJK || !a_log) ? 0.f : expf(a_log[h]);
     float dtb[PER_LANE];
@@ -77,7 +117,11 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     // the end leave the state and the output untouched.
     // The ring holds the loaded values as they arrive; everything computed from
     // them happens at use, so no instruction waits on a load right after issue.
-    constexpr int PD = (DK >= 128) ? 1 : 4;   // dk = 128: the column already takes 128 registers
+    // Prefetch distance in tokens: with one token taking a few hundred cycles, a
+    // global load needs a dozen or more tokens of lead to arrive in time.  A slot
+    // costs five registers up to dk = 64; at dk = 128 the column already takes
+    // 128 registers.  PD is even, so ring slot j's prologue set is j & 1.
+    constexpr int PD = (DK >= 128) ? 2 : (DK >= 64 ? 8 : 16);
     struct Raw {
         Tin q[PER_LANE], k[PER_LANE];
         float z[PER_LANE];
@@ -85,7 +129,7 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     };
     const int cc = active ? c : 0;
     const int vz = vector_zero();   // beta and the EJK decay: vector loads, see vector_zero()
-    auto load = [&](Raw& r, int t) {
+    auto load = [&](Raw& r, int t) __attribute__((always_inline)) {
         t = min(t, t1 - 1);
         const size_t th = (size_t)t * H + h;
 #pragma unroll
@@ -109,15 +153,24 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     // (after the ring loads are issued) keeps the loop's waits precise instead
     // of a full drain of the prefetch at every token
 #pragma unroll
-    for (int i = 0; i < DK; ++i) asm volatile("" ::"v"(s[i]));
-    // one token from ring slot J (a compile-time index, so the ring stays in registers)
-    auto token = [&](auto J, const int tb) {
-        constexpr int j = decltype(J)::value;
-        const int t = tb + j;
-        const bool live = t < t1;
+    for (int m = 0; m < RPL; ++m) asm volatile("" ::"v"(s[m]));
+    // The prologue of a token (norms, gate, beta) does not depend on the state,
+    // so it runs one token ahead: step j advances the column with token t's
+    // prologue set while it computes token t + 1's into the other set, and the
+    // compiler interleaves the two independent chains.  The workgroup is one
+    // wave and the LDS operations of a wave are performed in issue order, so
+    // the sets need no barrier between the lanes that write them and the lanes
+    // that read them.
+    const float fl2 = l2norm ? 1.0f : 0.0f;
+    struct Pro {
+        float bt, kq, as;   // beta, kh . qh, EJK decay factor e^d (1 for KDA)
+    };
+    // prologue of the token in ring slot J, written to set P
+    auto prologue = [&](auto J, auto P) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value, pb = decltype(P)::value;
         const Raw& r = ring[j];
         float qv[PER_LANE], kv[PER_LANE];
-        float sq = 0.f, sk = 0.f;
+        float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
             const bool in = lane + p * kWave < DK;
@@ -125,112 +178,159 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
             kv[p] = in ? to_f32(r.k[p]) : 0.f;
             sq += qv[p] * qv[p];
             sk += kv[p] * kv[p];
+            sqk += qv[p] * kv[p];
         }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
-        const float nq = l2norm ? scale / sqrtf(sq + kNormEps) : scale;
-        const float nk = l2norm ? 1.0f / sqrtf(sk + kNormEps) : 1.0f;
+        // only lanes below dk hold channels: a row or a half of the wave
+        // suffices for dk <= 16 or 32, and lane 0's group holds them all
+        constexpr int NSUM = (DK <= 16) ? 16 : (DK <= 32 ? 32 : 64);
+        sq = group_sum<NSUM>(sq);
+        sk = group_sum<NSUM>(sk);
+        sqk = group_sum<NSUM>(sqk);
+        // l2norm blended arithmetically: a branch here would split the block
+        // that the compiler interleaves with the column update
+        const float nq = scale * fmaf(fl2, __builtin_amdgcn_rsqf(sq + kNormEps) - 1.0f, 1.0f);
+        const float nk = fmaf(fl2, __builtin_amdgcn_rsqf(sk + kNormEps) - 1.0f, 1.0f);
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
             const int i = lane + p * kWave;
-            if (i < DK) {
-                sh_q[i] = qv[p] * nq;
-                sh_k[i] = kv[p] * nk;
-                if (!EJK) sh_alpha[i] = fast_exp(lower_bound * fast_sigmoid(ea * (r.z[p] + dtb[p])));
+            const float qh = qv[p] * nq, kh = kv[p] * nk;
+            sh_k[pb][i] = kh;
+            if (!EJK) {
+                const float a = fast_exp(lower_bound * fast_sigmoid(ea * (r.z[p] + dtb[p])));
+                sh_alpha[pb][i] = a;
+                sh_ak[pb][i] = a * kh;
+                sh_aq[pb][i] = a * qh;
+            } else {
+                sh_ak[pb][i] = kh;
+                sh_aq[pb][i] = qh;
             }
         }
-        float bt, alpha_s = 1.0f;
+        Pro pr;
+        pr.kq = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sqk * nq * nk)));
         if (!EJK) {
-            bt = fast_sigmoid(r.bt);
+            pr.bt = fast_sigmoid(r.bt);
+            pr.as = 1.0f;
         } else {
-            bt = r.bt;
-            alpha_s = fast_exp(r.z[0]);
+            pr.bt = r.bt;
+            pr.as = fast_exp(r.z[0]);
         }
-        lds_barrier();
-
-        if (live) {
-            // four partial sums per dot product: the per-token dependent chain is
-            // what bounds this kernel, not its arithmetic
-            constexpr int NP = (DK >= 4) ? 4 : 1;
-            float up[NP];
-#pragma unroll
-            for (int e = 0; e < NP; ++e) up[e] = 0.f;
-#pragma unroll
-            for (int i = 0; i < DK; ++i) {
-                if (!EJK) s[i] *= sh_alpha[i];
-                up[i % NP] = fmaf(s[i], sh_k[i], up[i % NP]);
-            }
-            float u = up[0];
-#pragma unroll
-            for (int e = 1; e < NP; ++e) u += up[e];
-            const float d = bt * (r.vc - u);
-            float op[NP];
-#pragma unroll
-            for (int e = 0; e < NP; ++e) op[e] = 0.f;
-#pragma unroll
-            for (int i = 0; i < DK; ++i) {
-                s[i] = fmaf(sh_k[i], d, EJK ? alpha_s * s[i] : s[i]);
-                op[i % NP] = fmaf(s[i], sh_q[i], op[i % NP]);
-            }
-            float oc = op[0];
-#pragma unroll
-            for (int e = 1; e < NP; ++e) oc += op[e];
-            if (active) o[((size_t)t * H + h) * DV + c] = from_f32<Tout>(oc);
-        }
-        lds_barrier();   // the next token rewrites the prologue vectors
-        load(ring[j], t + PD);
+        return pr;
     };
-    for (int tb = t0; tb < t1; tb += PD) {
-        token(std::integral_constant<int, 0>{}, tb);
-        if constexpr (PD > 1) token(std::integral_constant<int, (PD > 1 ? 1 : 0)>{}, tb);
-        if constexpr (PD > 2) token(std::integral_constant<int, (PD > 2 ? 2 : 0)>{}, tb);
-        if constexpr (PD > 3) token(std::integral_constant<int, (PD > 3 ? 3 : 0)>{}, tb);
+    // column update for token t from ring slot J with prologue set P:
+    // u = (alpha kh) . s_old and p = (alpha qh) . s_old side by side, in four
+    // partial sums each; the output needs no pass over the new column,
+    // S_new^T qh = p + d (kh . qh).  (EJK: u, p from the undecayed column,
+    // output e^d p + d (kh . qh).)
+    auto column = [&](auto J, auto P, const Pro& pr, const int t) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value, pb = decltype(P)::value;
+        constexpr int NP = (RPL >= 4) ? 4 : 1;
+        const float* ak = &sh_ak[pb][part * RPL];
+        const float* aq = &sh_aq[pb][part * RPL];
+        float up[NP], pp[NP];
+#pragma unroll
+        for (int e = 0; e < NP; ++e) up[e] = pp[e] = 0.f;
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            up[m % NP] = fmaf(s[m], ak[m], up[m % NP]);
+            pp[m % NP] = fmaf(s[m], aq[m], pp[m % NP]);
+        }
+        float u = up[0], pq = pp[0];
+#pragma unroll
+        for (int e = 1; e < NP; ++e) {
+            u += up[e];
+            pq += pp[e];
+        }
+        if constexpr (LPC >= 2) {
+            u = xor_add<1>(u);
+            pq = xor_add<1>(pq);
+        }
+        if constexpr (LPC >= 4) {
+            u = xor_add<2>(u);
+            pq = xor_add<2>(pq);
+        }
+        const float d = pr.bt * (ring[j].vc - u);
+        // one lane per column stores; the others pass an index past the row
+        row_store(o + ((size_t)t * H + h) * DV, DV, part == 0 ? c : DV, from_f32<Tout>(fmaf(d, pr.kq, pr.as * pq)));
+        const float* kk = &sh_k[pb][part * RPL];
+        const float* al = &sh_alpha[pb][part * RPL];
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) s[m] = fmaf(kk[m], d, (EJK ? pr.as : al[m]) * s[m]);
+    };
+    if (t0 < t1) {
+        Pro pr = prologue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        // step j of a block of PD tokens starting at tb; CHECKED: tokens may be past the end
+        auto step = [&](auto J, const int tb, auto CHECKED) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+            const int t = tb + j;
+            if (!decltype(CHECKED)::value || t < t1) column(J, std::integral_constant<int, (j & 1)>{}, pr, t);
+            load(ring[j], t + PD);
+            pr = prologue(std::integral_constant<int, (j + 1) % PD>{}, std::integral_constant<int, ((j + 1) & 1)>{});
+        };
+        int tb = t0;
+        for (; tb + PD <= t1; tb += PD)
+            unroll_seq([&](auto J) __attribute__((always_inline)) { step(J, tb, std::false_type{}); },
+                       std::make_integer_sequence<int, PD>{});
+        if (tb < t1)
+            unroll_seq([&](auto J) __attribute__((always_inline)) { step(J, tb, std::true_type{}); },
+                       std::make_integer_sequence<int, PD>{});
     }
 
     if (final_state && active) {
 #pragma unroll
-        for (int i = 0; i < DK; ++i) final_state[soff + (size_t)i * DV + c] = s[i];
+        for (int m = 0; m < RPL; ++m) final_state[soff + (size_t)(part * RPL + m) * DV + c] = s[m];
     }
 }
 
-template <int DK, typename Tin, typename Tout>
+template <int DK, int LPC, typename Tin, typename Tout>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((a.dv + kWave - 1) / kWave), (unsigned)a.H, (unsigned)a.N);
+    constexpr int CPW = kWave / LPC;
+    const dim3 grid((unsigned)((a.dv + CPW - 1) / CPW), (unsigned)a.H, (unsigned)a.N);
     const dim3 block(kWave);
     const Tin* q = static_cast<const Tin*>(a.q);
     const Tin* k = static_cast<const Tin*>(a.k);
     const Tin* v = static_cast<const Tin*>(a.v);
     Tout* o = static_cast<Tout*>(a.o);
     if (a.ejk)
-        hipLaunchKernelGGL((recurrent_kernel<DK, Tin, Tout, true>), grid, block, 0, stream, q, k, v,
+        hipLaunchKernelGGL((recurrent_kernel<DK, LPC, Tin, Tout, true>), grid, block, 0, stream, q, k, v,
                            a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.dv, a.scale,
                            a.lower_bound, (int)a.l2norm, o, a.final_state);
     else
-        hipLaunchKernelGGL((recurrent_kernel<DK, Tin, Tout, false>), grid, block, 0, stream, q, k, v,
+        hipLaunchKernelGGL((recurrent_kernel<DK, LPC, Tin, Tout, false>), grid, block, 0, stream, q, k, v,
                            a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.dv, a.scale,
                            a.lower_bound, (int)a.l2norm, o, a.final_state);
     return hipGetLastError();
 }
 
+// value heads of up to 16 (32) columns: four (two) lanes per column
+template <int DK, typename Tin, typename Tout>
+hipError_t launch_lpc(const PrefillArgs& a, hipStream_t stream)
+{
+    if (a.dv <= 16) return launch_typed<DK, 4, Tin, Tout>(a, stream);
+    if (a.dv <= 32) return launch_typed<DK, 2, Tin, Tout>(a, stream);
+    return launch_typed<DK, 1, Tin, Tout>(a, stream);
+}
+
 template <int DK>
 hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream)
 {
-    if (!a.in_bf16) return launch_typed<DK, float, float>(a, stream);
-    if (a.out_bf16) return launch_typed<DK, bf16_t, bf16_t>(a, stream);
-    return launch_typed<DK, bf16_t, float>(a, stream);
+    if (!a.in_bf16) return launch_lpc<DK, float, float>(a, stream);
+    if (a.out_bf16) return launch_lpc<DK, bf16_t, bf16_t>(a, stream);
+    return launch_lpc<DK, bf16_t, float>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_recurrent(const PrefillArgs& a, hipStream_t stream)
+// One object per key dimension (KDA_RECURRENT_DK set by the build), so the
+// instantiations compile in parallel; the dispatch over dk is in kda_api.cpp.
+#ifndef KDA_RECURRENT_DK
+#error "build kda_recurrent.hip with -DKDA_RECURRENT_DK=16, 32, 64 or 128"
+#endif
+#define KDA_CAT2(a, b) a##b
+#define KDA_CAT(a, b) KDA_CAT2(a, b)
+hipError_t KDA_CAT(launch_recurrent_dk, KDA_RECURRENT_DK)(const PrefillArgs& a, hipStream_t stream)
 {
-    switch (a.dk) {
-    case 16: return launch_dk<16>(a, stream);
-    case 32: return launch_dk<32>(a, stream);
-    case 64: return launch_dk<64>(a, stream);
-    default: return launch_dk<128>(a, stream);
-    }
+    return launch_dk<KDA_RECURRENT_DK>(a, stream);
 }
 
 }  // namespace kda
