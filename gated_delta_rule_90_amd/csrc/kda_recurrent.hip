@@ -2,10 +2,10 @@
 // "Recurrent: Pure sequential scan for memory efficiency").
 //
 // Grid (column tiles, H, N sequences); one wave per block.  Each state column
-// is held in registers by LPC adjacent lanes (LPC = 4 for dv = 16, 2 for
-// dv = 32, else 1), dk / LPC rows each, so the contractions over dk (S^T k,
-// S^T q) stay in registers up to a sum over those lanes, and the only other
-// cross-lane work per token is the L2 norm of q and k.  Per token: q, k, g
+// is held in registers by LPC adjacent lanes (8, or 4 at dk = 16), dk / LPC
+// rows each, so the contractions over dk (S^T k, S^T q) stay in registers up
+// to a sum over those lanes, and the only other cross-lane work per token is
+// the L2 norm of q and k.  Per token: q, k, g
 // become LDS-shared prologue vectors (lanes own channels j and j + 64), the
 // squared norms are reduced over the wave, the gate and beta activated, then
 // every lane advances its column:
@@ -56,10 +56,23 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, J..
     (f(std::integral_constant<int, J>{}), ...);
 }
 
-// LPC lanes share one state column (LPC = 1, 2 or 4): each holds DK / LPC of
-// its rows, and the column's dot products finish with a sum over the LPC lanes
-// (adjacent lanes, DPP within a quad).  Narrow value heads use LPC > 1, so
-// that more of the wave's lanes carry rows.
+// Sum over each aligned group of N adjacent lanes (N = 1, 2, 4 or 8), in every
+// lane of the group: DPP within quads, then the half-row mirror pairs the two
+// quads of an 8-lane group (their lanes already agree within each quad).
+template <int N>
+__device__ __forceinline__ float lanes_sum(float x)
+{
+    if constexpr (N >= 2) x = xor_add<1>(x);
+    if constexpr (N >= 4) x = xor_add<2>(x);
+    if constexpr (N >= 8)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+    return x;
+}
+
+// LPC adjacent lanes share one state column: each holds DK / LPC of its rows,
+// and the column's dot products finish with lanes_sum<LPC>.  Fewer rows per
+// lane shorten the per-token chain and the registers; the tiles of columns
+// run in parallel workgroups, each repeating the (cheap) prologue.
 template <int DK, int LPC, typename Tin, typename Tout, bool EJK>
 __global__ __launch_bounds__(kWave) void recurrent_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
@@ -119,9 +132,9 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     // them happens at use, so no instruction waits on a load right after issue.
     // Prefetch distance in tokens: with one token taking a few hundred cycles, a
     // global load needs a dozen or more tokens of lead to arrive in time.  A slot
-    // costs five registers up to dk = 64; at dk = 128 the column already takes
-    // 128 registers.  PD is even, so ring slot j's prologue set is j & 1.
-    constexpr int PD = (DK >= 128) ? 2 : (DK >= 64 ? 8 : 16);
+    // costs five registers up to dk = 64 and eight at dk = 128.  PD is even, so
+    // ring slot j's prologue set is j & 1.
+    constexpr int PD = (DK >= 64) ? 8 : 16;
     struct Raw {
         Tin q[PER_LANE], k[PER_LANE];
         float z[PER_LANE];
@@ -240,14 +253,8 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
             u += up[e];
             pq += pp[e];
         }
-        if constexpr (LPC >= 2) {
-            u = xor_add<1>(u);
-            pq = xor_add<1>(pq);
-        }
-        if constexpr (LPC >= 4) {
-            u = xor_add<2>(u);
-            pq = xor_add<2>(pq);
-        }
+        u = lanes_sum<LPC>(u);
+        pq = lanes_sum<LPC>(pq);
         const float d = pr.bt * (ring[j].vc - u);
         // one lane per column stores; the others pass an index past the row
         row_store(o + ((size_t)t * H + h) * DV, DV, part == 0 ? c : DV, from_f32<Tout>(fmaf(d, pr.kq, pr.as * pq)));
@@ -302,13 +309,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// value heads of up to 16 (32) columns: four (two) lanes per column
+// eight lanes per column (four at dk = 16: at least four rows per lane)
 template <int DK, typename Tin, typename Tout>
 hipError_t launch_lpc(const PrefillArgs& a, hipStream_t stream)
 {
-    if (a.dv <= 16) return launch_typed<DK, 4, Tin, Tout>(a, stream);
-    if (a.dv <= 32) return launch_typed<DK, 2, Tin, Tout>(a, stream);
-    return launch_typed<DK, 1, Tin, Tout>(a, stream);
+    return launch_typed<DK, (DK >= 32 ? 8 : 4), Tin, Tout>(a, stream);
 }
 
 template <int DK>
