@@ -754,16 +754,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 }
             }
             // T' [64][64] -> k-sliced, thread = (row, 16-column block); blocks above the
-            // diagonal are written as zeros (the scan always runs both k-slices)
+            // diagonal are written as zeros, except k-slice 1 of rows 0..31, which the
+            // scan never reads (it loads zeros for it from past the record's end)
             const int r = tid >> 2;
             const int s0 = 16 * (tid & 3);
             const bool upper = (tid & 3) > (r >> 4);
+            if (!(r < 32 && s0 >= 32)) {
     #pragma unroll
-            for (int h8 = 0; h8 < 2; ++h8) {
-                uint4 val = *reinterpret_cast<const uint4*>(TP + r * SW + s0 + 8 * h8);
-                if (upper) val = make_uint4(0u, 0u, 0u, 0u);
-                *reinterpret_cast<uint4*>(gTP + ksl(C, r, s0 + 8 * h8)) = val;
-                if (upper) *reinterpret_cast<uint4*>(gP + ksl(C, r, s0 + 8 * h8)) = val;
+                for (int h8 = 0; h8 < 2; ++h8) {
+                    uint4 val = *reinterpret_cast<const uint4*>(TP + r * SW + s0 + 8 * h8);
+                    if (upper) val = make_uint4(0u, 0u, 0u, 0u);
+                    *reinterpret_cast<uint4*>(gTP + ksl(C, r, s0 + 8 * h8)) = val;
+                    if (upper) *reinterpret_cast<uint4*>(gP + ksl(C, r, s0 + 8 * h8)) = val;
+                }
             }
         }
         // phase 4 of this item reads KGT and TP, which the next item overwrites
@@ -815,8 +818,6 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
     const uint16_t* W = reinterpret_cast<const uint16_t*>(rec + REC_W);
     const uint16_t* QG = reinterpret_cast<const uint16_t*>(rec + REC_QG);
     const uint16_t* KCT = reinterpret_cast<const uint16_t*>(rec + REC_KCT);
-    const uint16_t* TP = reinterpret_cast<const uint16_t*>(rec + REC_TP);
-    const uint16_t* P = reinterpret_cast<const uint16_t*>(rec + REC_P);
     const float* EC = reinterpret_cast<const float*>(rec + REC_EC);
     if constexpr (PART == 0) {
         // V tile: row s, 8 columns per piece; rows past the sequence read row 0 and are zeroed on use
@@ -829,10 +830,20 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
             const int ss = (s < len) ? s : 0;
             f.v[it] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * H + h) * DV + j0 + jj);
         }
+        // T' and P are lower triangular: k-slice 1 (columns 32..63) of the first
+        // two row blocks is zero and is not stored.  Those two fragments are
+        // loaded from past the end of a buffer resource over the record, which
+        // returns zeros without a memory request, so every wave issues the same
+        // loads and only rows 32..63 fetch them.
+        const __amdgpu_buffer_rsrc_t rr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rec), 0, REC_BYTES, 0x00020000);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            f.tp[ks] = *reinterpret_cast<const bf16x8_t*>(TP + (ks * C + 16 * I) * 32 + fo);
-            f.p[ks] = *reinterpret_cast<const bf16x8_t*>(P + (ks * C + 16 * I) * 32 + fo);
+            const bool stored = ks == 0 || I >= 2;
+            const int tpo = stored ? REC_TP + 2 * ((ks * C + 16 * I) * 32 + fo) : REC_BYTES;
+            const int po = stored ? REC_P + 2 * ((ks * C + 16 * I) * 32 + fo) : REC_BYTES;
+            f.tp[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rr, tpo, 0, 0));
+            f.p[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rr, po, 0, 0));
         }
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
