@@ -115,39 +115,51 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
 #pragma unroll
     for (int m = 0; m < RPL; ++m) s[m] = (init && active) ? init[soff + (size_t)(part * RPL + m) * DV + c] : 0.f;
 
+    // Tokens are taken in packs of TPP = 64 / dk (dk <= 32; else 1): the
+    // prologue of a whole pack runs at once, lane l on token l / dk and channel
+    // l % dk (at dk >= 64 one token, lanes on channels l and l + 64), so no
+    // lane idles in it.  The prologue vectors of token tk of a pack are
+    // entries tk * dk .. tk * dk + dk - 1 of a set.
+    constexpr int TPP = (DK <= 32) ? kWave / DK : 1;
+    const int ltok = (TPP > 1) ? lane / DK : 0;   // this lane's token in a pack
+    const int lch = (TPP > 1) ? lane % DK : lane; // this lane's (first) channel
+
     const float ea = (EJK || !a_log) ? 0.f : expf(a_log[h]);
     float dtb[PER_LANE];
 #pragma unroll
     for (int p = 0; p < PER_LANE; ++p) {
-        const int i = lane + p * kWave;
+        const int i = lch + p * kWave;
         dtb[p] = (!EJK && dt_bias && i < DK) ? dt_bias[(size_t)i * H + h] : 0.f;
     }
 
-    // Inputs of token t + PD are loaded while token t is computed (a ring of PD
-    // register sets, the loop unrolled by PD so that no set is copied), which
-    // hides the global-memory latency that otherwise every token would pay.
-    // Loads past the end reload the last token (in bounds, unused); steps past
-    // the end leave the state and the output untouched.
-    // The ring holds the loaded values as they arrive; everything computed from
-    // them happens at use, so no instruction waits on a load right after issue.
-    // Prefetch distance in tokens: with one token taking a few hundred cycles, a
-    // global load needs a dozen or more tokens of lead to arrive in time.  A slot
-    // costs five registers up to dk = 64 and eight at dk = 128.  PD is even, so
-    // ring slot j's prologue set is j & 1.
+    // Inputs of the pack PD tokens ahead are loaded while the current one is
+    // computed (a ring of register sets, the loop unrolled over it so that no
+    // set is copied), which hides the global-memory latency that otherwise
+    // every token would pay.  Loads past the end reload the last token (in
+    // bounds, unused); steps past the end leave the state and the output
+    // untouched.  The ring holds the loaded values as they arrive; everything
+    // computed from them happens at use, so no instruction waits on a load
+    // right after issue.
+    // Prefetch distance: with one token taking a few hundred cycles, a global
+    // load needs a dozen or more tokens of lead to arrive in time.  PD / TPP
+    // ring slots, an even number, so slot j's prologue set is j & 1.
     constexpr int PD = (DK >= 64) ? 8 : 16;
+    constexpr int NSLOT = PD / TPP;
+    static_assert(NSLOT % 2 == 0, "even ring");
     struct Raw {
         Tin q[PER_LANE], k[PER_LANE];
         float z[PER_LANE];
-        float bt, vc;
+        float bt;         // this lane's token's beta
+        float vc[TPP];    // v of this lane's column for each token of the pack
     };
     const int cc = active ? c : 0;
     const int vz = vector_zero();   // beta and the EJK decay: vector loads, see vector_zero()
-    auto load = [&](Raw& r, int t) __attribute__((always_inline)) {
-        t = min(t, t1 - 1);
-        const size_t th = (size_t)t * H + h;
+    auto load = [&](Raw& r, const int tp) __attribute__((always_inline)) {
+        const int tl = min(tp + ltok, t1 - 1);
+        const size_t th = (size_t)tl * H + h;
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
-            const int i = lane + p * kWave;
+            const int i = lch + p * kWave;
             const int ic = (i < DK) ? i : 0;   // lanes past dk read channel 0 and are zeroed on use
             r.q[p] = q[th * DK + ic];
             r.k[p] = k[th * DK + ic];
@@ -155,30 +167,35 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         }
         r.bt = beta[th + vz];
         if (EJK) r.z[0] = g ? g[th + vz] : 0.f;   // EJK: the token's scalar log-decay
-        r.vc = to_f32(v[th * DV + cc]);
+#pragma unroll
+        for (int tk = 0; tk < TPP; ++tk)
+            r.vc[tk] = to_f32(v[((size_t)min(tp + tk, t1 - 1) * H + h) * DV + cc]);
     };
-    Raw ring[PD];
+    Raw ring[NSLOT];
     if (t0 < t1) {
 #pragma unroll
-        for (int j = 0; j < PD; ++j) load(ring[j], t0 + j);
+        for (int j = 0; j < NSLOT; ++j) load(ring[j], t0 + j * TPP);
     }
     // the initial state has to be in registers before the loop: taking it here
     // (after the ring loads are issued) keeps the loop's waits precise instead
     // of a full drain of the prefetch at every token
 #pragma unroll
     for (int m = 0; m < RPL; ++m) asm volatile("" ::"v"(s[m]));
-    // The prologue of a token (norms, gate, beta) does not depend on the state,
-    // so it runs one token ahead: step j advances the column with token t's
-    // prologue set while it computes token t + 1's into the other set, and the
-    // compiler interleaves the two independent chains.  The workgroup is one
-    // wave and the LDS operations of a wave are performed in issue order, so
-    // the sets need no barrier between the lanes that write them and the lanes
-    // that read them.
+    // The prologue of a pack (norms, gate, beta) does not depend on the state,
+    // so it runs one pack ahead: step j advances the column over pack j's
+    // tokens with its prologue set while it computes the next pack's into the
+    // other set, and the compiler interleaves the independent chains.  The
+    // workgroup is one wave and the LDS operations of a wave are performed in
+    // issue order, so the sets need no barrier between the lanes that write
+    // them and the lanes that read them.
     const float fl2 = l2norm ? 1.0f : 0.0f;
     struct Pro {
         float bt, kq, as;   // beta, kh . qh, EJK decay factor e^d (1 for KDA)
     };
-    // prologue of the token in ring slot J, written to set P
+    struct ProPack {
+        Pro tok[TPP];
+    };
+    // prologue of the pack in ring slot J, written to set P
     auto prologue = [&](auto J, auto P) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value, pb = decltype(P)::value;
         const Raw& r = ring[j];
@@ -186,15 +203,14 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
-            const bool in = lane + p * kWave < DK;
+            const bool in = lch + p * kWave < DK;
             qv[p] = in ? to_f32(r.q[p]) : 0.f;
             kv[p] = in ? to_f32(r.k[p]) : 0.f;
             sq += qv[p] * qv[p];
             sk += kv[p] * kv[p];
             sqk += qv[p] * kv[p];
         }
-        // only lanes below dk hold channels: a row or a half of the wave
-        // suffices for dk <= 16 or 32, and lane 0's group holds them all
+        // one token's channels: a row (dk = 16), a half (32) or the wave
         constexpr int NSUM = (DK <= 16) ? 16 : (DK <= 32 ? 32 : 64);
         sq = group_sum<NSUM>(sq);
         sk = group_sum<NSUM>(sk);
@@ -205,7 +221,7 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         const float nk = fmaf(fl2, __builtin_amdgcn_rsqf(sk + kNormEps) - 1.0f, 1.0f);
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
-            const int i = lane + p * kWave;
+            const int i = lane + p * kWave;   // = token * dk + channel
             const float qh = qv[p] * nq, kh = kv[p] * nk;
             sh_k[pb][i] = kh;
             if (!EJK) {
@@ -218,27 +234,31 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
                 sh_aq[pb][i] = qh;
             }
         }
-        Pro pr;
-        pr.kq = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sqk * nq * nk)));
-        if (!EJK) {
-            pr.bt = fast_sigmoid(r.bt);
-            pr.as = 1.0f;
-        } else {
-            pr.bt = r.bt;
-            pr.as = fast_exp(r.z[0]);
+        // the token scalars, from the first lane of each token's group
+        const float kql = sqk * nq * nk;
+        const float btl = EJK ? r.bt : fast_sigmoid(r.bt);
+        const float asl = EJK ? fast_exp(r.z[0]) : 1.0f;
+        ProPack pk;
+#pragma unroll
+        for (int tk = 0; tk < TPP; ++tk) {
+            pk.tok[tk].kq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kql), tk * DK));
+            pk.tok[tk].bt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btl), tk * DK));
+            pk.tok[tk].as = EJK ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, asl), tk * DK))
+                                : 1.0f;
         }
-        return pr;
+        return pk;
     };
-    // column update for token t from ring slot J with prologue set P:
+    // column update for token TK of the pack in ring slot J, prologue set P:
     // u = (alpha kh) . s_old and p = (alpha qh) . s_old side by side, in four
     // partial sums each; the output needs no pass over the new column,
     // S_new^T qh = p + d (kh . qh).  (EJK: u, p from the undecayed column,
     // output e^d p + d (kh . qh).)
-    auto column = [&](auto J, auto P, const Pro& pr, const int t) __attribute__((always_inline)) {
-        constexpr int j = decltype(J)::value, pb = decltype(P)::value;
+    auto column = [&](auto J, auto P, auto TK, const Pro& pr, const int t) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value, pb = decltype(P)::value, tk = decltype(TK)::value;
         constexpr int NP = (RPL >= 4) ? 4 : 1;
-        const float* ak = &sh_ak[pb][part * RPL];
-        const float* aq = &sh_aq[pb][part * RPL];
+        const int base = tk * DK + part * RPL;
+        const float* ak = &sh_ak[pb][base];
+        const float* aq = &sh_aq[pb][base];
         float up[NP], pp[NP];
 #pragma unroll
         for (int e = 0; e < NP; ++e) up[e] = pp[e] = 0.f;
@@ -255,31 +275,37 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         }
         u = lanes_sum<LPC>(u);
         pq = lanes_sum<LPC>(pq);
-        const float d = pr.bt * (ring[j].vc - u);
+        const float d = pr.bt * (ring[j].vc[tk] - u);
         // one lane per column stores; the others pass an index past the row
         row_store(o + ((size_t)t * H + h) * DV, DV, part == 0 ? c : DV, from_f32<Tout>(fmaf(d, pr.kq, pr.as * pq)));
-        const float* kk = &sh_k[pb][part * RPL];
-        const float* al = &sh_alpha[pb][part * RPL];
+        const float* kk = &sh_k[pb][base];
+        const float* al = &sh_alpha[pb][base];
 #pragma unroll
         for (int m = 0; m < RPL; ++m) s[m] = fmaf(kk[m], d, (EJK ? pr.as : al[m]) * s[m]);
     };
     if (t0 < t1) {
-        Pro pr = prologue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        ProPack pk = prologue(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
         // step j of a block of PD tokens starting at tb; CHECKED: tokens may be past the end
         auto step = [&](auto J, const int tb, auto CHECKED) __attribute__((always_inline)) {
             constexpr int j = decltype(J)::value;
-            const int t = tb + j;
-            if (!decltype(CHECKED)::value || t < t1) column(J, std::integral_constant<int, (j & 1)>{}, pr, t);
-            load(ring[j], t + PD);
-            pr = prologue(std::integral_constant<int, (j + 1) % PD>{}, std::integral_constant<int, ((j + 1) & 1)>{});
+            const int tp = tb + j * TPP;
+            unroll_seq(
+                [&](auto TK) __attribute__((always_inline)) {
+                    const int t = tp + decltype(TK)::value;
+                    if (!decltype(CHECKED)::value || t < t1)
+                        column(J, std::integral_constant<int, (j & 1)>{}, TK, pk.tok[decltype(TK)::value], t);
+                },
+                std::make_integer_sequence<int, TPP>{});
+            load(ring[j], tp + PD);
+            pk = prologue(std::integral_constant<int, (j + 1) % NSLOT>{}, std::integral_constant<int, ((j + 1) & 1)>{});
         };
         int tb = t0;
         for (; tb + PD <= t1; tb += PD)
             unroll_seq([&](auto J) __attribute__((always_inline)) { step(J, tb, std::false_type{}); },
-                       std::make_integer_sequence<int, PD>{});
+                       std::make_integer_sequence<int, NSLOT>{});
         if (tb < t1)
             unroll_seq([&](auto J) __attribute__((always_inline)) { step(J, tb, std::true_type{}); },
-                       std::make_integer_sequence<int, PD>{});
+                       std::make_integer_sequence<int, NSLOT>{});
     }
 
     if (final_state && active) {

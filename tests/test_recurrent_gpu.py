@@ -53,11 +53,14 @@ def test_recurrent_no_l2norm_lower_bound_beyond_chunk_range():
     assert rel_l2(o, ro) <= TOL and rel_l2(s, rs) <= TOL
 
 
-def test_recurrent_varlen_bitwise_equal_to_separate_runs():
-    lens = [17, 0, 64, 1, 40]
-    inp = workloads.prefill_inputs(1, 0, 3, 64, 32, seed=5, dtype="f32", lengths=lens,
+@pytest.mark.parametrize("dk,dv", [(64, 32), (16, 16), (32, 64)])
+def test_recurrent_varlen_bitwise_equal_to_separate_runs(dk, dv):
+    """Sequences start at arbitrary offsets; dk 16 and 32 take tokens in packs
+    of 4 and 2 (the pack boundaries then fall at every possible phase)."""
+    lens = [17, 0, 64, 1, 40, 3, 22]
+    inp = workloads.prefill_inputs(1, 0, 3, dk, dv, seed=5 + dk, dtype="f32", lengths=lens,
                                    init_state=True)
-    say("recurrent varlen", lens)
+    say("recurrent varlen", dk, dv, lens)
     o, s = prefill_gpu(inp, use_chunked=False)
     ro, rs = prefill_oracle(inp)
     assert rel_l2(o, ro) <= TOL and rel_l2(s, rs) <= TOL
