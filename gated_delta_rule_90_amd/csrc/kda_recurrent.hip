@@ -5,10 +5,11 @@
 // is held in registers by LPC adjacent lanes (8, or 4 at dk = 16), dk / LPC
 // rows each, so the contractions over dk (S^T k, S^T q) stay in registers up
 // to a sum over those lanes, and the only other cross-lane work per token is
-// the L2 norm of q and k.  Per token: q, k, g
-// become LDS-shared prologue vectors (lanes own channels j and j + 64), the
-// squared norms are reduced over the wave, the gate and beta activated, then
-// every lane advances its column:
+// the L2 norm of q and k.  Per token: q, k, g become LDS-shared prologue
+// vectors (at dk <= 32 for several tokens at once, one token per group of dk
+// lanes; else lanes own channels j and j + 64), the squared norms are reduced
+// over each token's lanes, the gate and beta activated, then every lane
+// advances its column:
 //     s <- exp(gamma) * s;  u = s . kh;  s <- s + kh * beta (v_c - u);  o_c = s . qh
 // (EJK: u from the undecayed column, s <- e^d s + kh beta (v_c - u)).
 // It is evaluated as u = (alpha kh) . s_old and p = (alpha qh) . s_old side by
