@@ -2,10 +2,10 @@
 // "Recurrent: Pure sequential scan for memory efficiency").
 //
 // Grid (column tiles, H, N sequences); one wave per block.  Each state column
-// is held in registers by LPC adjacent lanes (8, or 4 at dk = 16), dk / LPC
-// rows each, so the contractions over dk (S^T k, S^T q) stay in registers up
-// to a sum over those lanes, and the only other cross-lane work per token is
-// the L2 norm of q and k.  Per token: q, k, g become LDS-shared prologue
+// is held in registers by LPC adjacent lanes (16 at dk = 128, 8 at dk = 32
+// and 64, 4 at dk = 16), dk / LPC rows each, so the contractions over dk
+// (S^T k, S^T q) stay in registers up to a sum over those lanes, and the only
+// other cross-lane work per token is the L2 norm of q and k.  Per token: q, k, g become LDS-shared prologue
 // vectors (at dk <= 32 for several tokens at once, one token per group of dk
 // lanes; else lanes own channels j and j + 64), the squared norms are reduced
 // over each token's lanes, the gate and beta activated, then every lane
@@ -57,9 +57,9 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, J..
     (f(std::integral_constant<int, J>{}), ...);
 }
 
-// Sum over each aligned group of N adjacent lanes (N = 1, 2, 4 or 8), in every
-// lane of the group: DPP within quads, then the half-row mirror pairs the two
-// quads of an 8-lane group (their lanes already agree within each quad).
+// Sum over each aligned group of N adjacent lanes (N = 1, 2, 4, 8 or 16), in
+// every lane of the group: DPP within quads, then the half-row and row mirrors
+// pair quads and half rows whose lanes already agree.
 template <int N>
 __device__ __forceinline__ float lanes_sum(float x)
 {
@@ -67,6 +67,8 @@ __device__ __forceinline__ float lanes_sum(float x)
     if constexpr (N >= 4) x = xor_add<2>(x);
     if constexpr (N >= 8)
         x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+    if constexpr (N >= 16)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
     return x;
 }
 
@@ -336,11 +338,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// eight lanes per column (four at dk = 16: at least four rows per lane)
+// lanes per column: dk / 4 up to 16 (four or eight rows per lane)
 template <int DK, typename Tin, typename Tout>
 hipError_t launch_lpc(const PrefillArgs& a, hipStream_t stream)
 {
-    return launch_typed<DK, (DK >= 32 ? 8 : 4), Tin, Tout>(a, stream);
+    return launch_typed<DK, (DK >= 128 ? 16 : DK >= 32 ? 8 : 4), Tin, Tout>(a, stream);
 }
 
 template <int DK>
