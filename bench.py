@@ -187,7 +187,7 @@ def cpu_prefill_baseline(budget_s=5.0):
             "sample": f"{reps} x (4 sequences x 4096 tokens x {nh} heads), float64, in {el:.1f} s"}
 
 
-def _prefill_run(inp, steps, warmup, nsets=1, split=None):
+def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False):
     """Time kda.prefill on one workload (inputs resident in HBM, nsets input
     copies used in turn so the Infinity Cache cannot hold them)."""
     import torch
@@ -238,6 +238,42 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None):
         res.update({"alg_flops_tri": fl, "mfma_frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
                     "roofline_frac": round(floor_ms / ms, 4),
                     "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "achieved_TFs": round(tfs, 2)})
+    if graph:
+        # a call this small is bound by the host's per-call overhead; captured
+        # in a HIP graph (GRAPH_CALLS calls per replay) it shows the device time.
+        # Each replay's output must equal the eager call's bitwise.
+        GRAPH_CALLS = 20
+        call(0, use_chunked=chunked)
+        torch.cuda.synchronize()
+        o_ref, fs_ref = o.clone(), fs.clone()
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(0, use_chunked=chunked)   # warm the side stream before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for _ in range(GRAPH_CALLS):
+                call(0, use_chunked=chunked)
+        same = True
+        for _ in range(3):
+            o.zero_()
+            fs.zero_()
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            same = same and bool(torch.equal(o, o_ref) and torch.equal(fs, fs_ref))
+        reps = max(1, steps // GRAPH_CALLS)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            gr.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        res["graph_ms_per_call"] = round(g0.elapsed_time(g1) / (reps * GRAPH_CALLS), 4)
+        res["graph_replay_bitwise_equal"] = same
+        del gr
     if split is not None:
         # the same call in two halves with the state passed through: bitwise equal?
         call(0, use_chunked=chunked)
@@ -276,7 +312,10 @@ def bench_configs(steps, warmup):
     from gated_delta_rule_90_amd import workloads
     out = {}
     inp = workloads.recurrent_fp32_small()
-    out["recurrent_fp32_b1_t64_h2_d16"] = dict(_prefill_run(inp, 10 * steps, warmup), note="64 dependent token steps per call: latency bound")
+    out["recurrent_fp32_b1_t64_h2_d16"] = dict(_prefill_run(inp, 10 * steps, warmup, graph=True),
+                                               note="64 dependent token steps per call: latency bound; "
+                                                    "ms_per_call includes the host's per-call overhead, "
+                                                    "graph_ms_per_call is the device time")
     for name, make, kw in (
             ("prefill_long_t65536_h32_d128", workloads.prefill_long_t65536_h32_d128, {"split": 32768}),
             ("prefill_varlen_8seq_h32_d128", workloads.prefill_varlen_8seq_h32_d128, {}),
