@@ -95,8 +95,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * T = 0 is a no-op, except that final_state then receives initial_state (or
  * zeros).  Routing: KDA_CHUNKED with bf16 inputs and dk = 128 (any of the
  * dv above) runs the MFMA chunked kernel (KDA and EJK modes); every
- * other combination runs the exact token-by-token kernel, which computes the
- * same function.  EJK decays are expected to be <= 0 (the ejkernel page
+ * other combination runs the float32 token-by-token kernel, which computes
+ * the same function step by step.  EJK decays are expected to be <= 0 (the ejkernel page
  * says so); the chunked kernel scales by e^{sum of decays} within a chunk,
  * so a positive decay large enough to overflow float32 there gives inf/NaN
  * where the token-by-token kernel would only overflow later.
