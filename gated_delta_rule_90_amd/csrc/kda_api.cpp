@@ -130,6 +130,10 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
     if (has_tokens && chunked && kda::chunked_supported(a)) {
         if (!ejk && lower_bound < -5.0f)
             return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path needs lower_bound >= -5 (got %g)", (double)lower_bound);
+        // its kernels move q, k, v, o and the KDA gates 16 bytes per lane
+        auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+        if (!a16(q) || !a16(k) || !a16(v) || !a16(o) || (!ejk && !a16(g)))
+            return fail(KDA_EINVAL, "kda_prefill: the chunked path needs q, k, v, o and g 16-byte aligned");
         const size_t need = kda::chunked_workspace_bytes(N, T, H, dk, dv, cu_seqlens != nullptr);
         if (need > 0 && (!workspace || workspace_bytes < need))
             return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);

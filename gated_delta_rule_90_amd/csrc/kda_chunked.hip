@@ -57,6 +57,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;        // chunk length
 constexpr int DK = 128;      // key dimension handled by the MFMA path
@@ -98,6 +99,12 @@ constexpr int P_Y = P_QL + C * SW * 2;
 constexpr int P_TCOL = P_KL;
 constexpr int P_TROW = P_KL + C * ST * 2;
 constexpr int P_A = P_KRD;
+// staging of an item's inputs at the start of phase 1a (before any of the above
+// is written): per wave [16 rows][128] bf16 q, then k, then fp32 gates
+constexpr int P_STG_Q = 0;
+constexpr int P_STG_K = P_STG_Q + 4 * 16 * DK * 2;
+constexpr int P_STG_G = P_STG_K + 4 * 16 * DK * 2;
+static_assert(P_STG_G + 4 * 16 * DK * 4 <= P_VEC, "staging below the vectors");
 static_assert(PREP_LDS <= 80 * 1024, "two prep workgroups per CU");
 static_assert(C * SA * 4 <= TILE_R, "A fits in a tile slot");
 static_assert(2 * C * ST * 2 <= TILE_R, "Tcol + Trow fit in a tile slot");
@@ -290,10 +297,13 @@ __device__ __forceinline__ PrepItem prep_item(int item, int nitems, int H, const
     return it;
 }
 
+// An item's inputs as loaded, 16 bytes per lane: wide loads keep more bytes in
+// flight per outstanding request than one row of two channels per lane would.
 struct PrepRaw {
-    uint32_t q[16], k[16];   // bf16 pairs of channels (2*lane, 2*lane+1), rows 16*wave + m
-    float g0[16], g1[16];
-    float beta;              // lanes < 16: beta logit of row 16*wave + lane
+    u32x4_t q[4], k[4];   // rows 16*blk + 4i + (lane >> 4), channels 8*(lane & 15) .. +7 (bf16)
+    u32x4_t g[8];         // KDA gates: rows 16*blk + 2i + (lane >> 5), channels 4*(lane & 31) .. +3
+    float ge[16];         // EJK: the decay of row 16*blk + m (the same in every lane)
+    float beta;           // lanes < 16: beta logit of row 16*blk + lane
 };
 
 // Rows past the sequence read the chunk's first row; they are zeroed on use.
@@ -303,34 +313,34 @@ template <bool EJK, int PART = 2>
 __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const bf16_t* q, const bf16_t* k,
                                           const float* g, const float* beta, int H, int lane, int blk)
 {
-    const int ch = 2 * lane;
-    const size_t base0 = ((size_t)it.c0 * H + it.h) * DK + ch;
-    const bf16_t* qb = q + base0;
-    const bf16_t* kb = k + base0;
-    const float* gb = EJK ? nullptr : g + base0;
-    const int rstride = H * DK;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int rr = 16 * blk + m;
-        const int off = ((rr < it.len) ? rr : 0) * rstride;
-        if constexpr (PART != 1) {
-            r.q[m] = *reinterpret_cast<const uint32_t*>(qb + off);
-            r.k[m] = *reinterpret_cast<const uint32_t*>(kb + off);
-        }
-        if constexpr (PART != 0) {
-            if constexpr (EJK) {
-                r.g0[m] = g ? g[(size_t)(it.c0 + ((rr < it.len) ? rr : 0)) * H + it.h] : 0.f;
-                r.g1[m] = 0.f;
-            } else {
-                const float2 gg = *reinterpret_cast<const float2*>(gb + off);
-                r.g0[m] = gg.x;
-                r.g1[m] = gg.y;
-            }
-        }
-    }
+    const size_t base = ((size_t)it.c0 * H + it.h) * DK;   // channel 0 of the item's first row
+    const size_t rstride = (size_t)H * DK;
     if constexpr (PART != 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * blk + 4 * i + (lane >> 4);
+            const size_t off = base + (size_t)((row < it.len) ? row : 0) * rstride + 8 * (lane & 15);
+            r.q[i] = *reinterpret_cast<const u32x4_t*>(q + off);
+            r.k[i] = *reinterpret_cast<const u32x4_t*>(k + off);
+        }
         const int rb = 16 * blk + (lane & 15);
         r.beta = beta[(size_t)(it.c0 + ((rb < it.len) ? rb : 0)) * H + it.h];
+    }
+    if constexpr (PART != 0) {
+        if constexpr (EJK) {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int rr = 16 * blk + m;
+                r.ge[m] = g ? g[(size_t)(it.c0 + ((rr < it.len) ? rr : 0)) * H + it.h] : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 16 * blk + 2 * i + (lane >> 5);
+                const size_t off = base + (size_t)((row < it.len) ? row : 0) * rstride + 4 * (lane & 31);
+                r.g[i] = *reinterpret_cast<const u32x4_t*>(g + off);
+            }
+        }
     }
 }
 
@@ -392,6 +402,34 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         const float dtb1 = (!EJK && dt_bias) ? dt_bias[(size_t)(ch + 1) * H + h] : 0.f;
 
         // ---------------- phase 1a: partial norms, gate, in-block cumsum (inputs already loaded)
+        // The inputs arrive 16 bytes per lane.  This wave's rows go through its
+        // own LDS staging region to the prologue's layout, two channels of every
+        // row per lane; a wave's LDS operations are performed in order, so no
+        // barrier is needed between its writes and its reads.
+        uint32_t qin[16], kin[16];
+        float2 gin[16];
+        {
+            uint16_t* stq = reinterpret_cast<uint16_t*>(smem + P_STG_Q) + blk * 16 * DK;
+            uint16_t* stk = reinterpret_cast<uint16_t*>(smem + P_STG_K) + blk * 16 * DK;
+            float* stg = reinterpret_cast<float*>(smem + P_STG_G) + blk * 16 * DK;
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = 4 * i + (lane >> 4);
+                *reinterpret_cast<u32x4_t*>(stq + rl * DK + 8 * (lane & 15)) = cur.q[i];
+                *reinterpret_cast<u32x4_t*>(stk + rl * DK + 8 * (lane & 15)) = cur.k[i];
+            }
+            if constexpr (!EJK) {
+    #pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<u32x4_t*>(stg + (2 * i + (lane >> 5)) * DK + 4 * (lane & 31)) = cur.g[i];
+            }
+    #pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                qin[m] = *reinterpret_cast<const uint32_t*>(stq + m * DK + ch);
+                kin[m] = *reinterpret_cast<const uint32_t*>(stk + m * DK + ch);
+                gin[m] = EJK ? make_float2(cur.ge[m], 0.f) : *reinterpret_cast<const float2*>(stg + m * DK + ch);
+            }
+        }
         uint32_t qraw[16], kraw[16];
         float cb0[16], cb1[16];
         {
@@ -399,21 +437,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 const bool valid = 16 * blk + m < len;
-                qraw[m] = valid ? cur.q[m] : 0u;
-                kraw[m] = valid ? cur.k[m] : 0u;
+                qraw[m] = valid ? qin[m] : 0u;
+                kraw[m] = valid ? kin[m] : 0u;
                 const float q0 = lo_bf(qraw[m]), q1 = hi_bf(qraw[m]);
                 const float k0 = lo_bf(kraw[m]), k1 = hi_bf(kraw[m]);
                 sq[m] = q0 * q0 + q1 * q1;
                 sk[m] = k0 * k0 + k1 * k1;
                 if constexpr (EJK) {
                     // the token's log-decay in log2 units, shared by all channels
-                    const float gm = valid ? cur.g0[m] * kLog2e : 0.f;
+                    const float gm = valid ? gin[m].x * kLog2e : 0.f;
                     cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm;
                     cb1[m] = cb0[m];
                 } else {
                     // gamma' = lb * log2(e) * sigmoid(exp(a_log) * (g + dt_bias))
-                    const float e0 = __builtin_amdgcn_exp2f(-ea * (cur.g0[m] + dtb0));
-                    const float e1 = __builtin_amdgcn_exp2f(-ea * (cur.g1[m] + dtb1));
+                    const float e0 = __builtin_amdgcn_exp2f(-ea * (gin[m].x + dtb0));
+                    const float e1 = __builtin_amdgcn_exp2f(-ea * (gin[m].y + dtb1));
                     const float gm0 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e0) : 0.f;
                     const float gm1 = valid ? lb2 * __builtin_amdgcn_rcpf(1.f + e1) : 0.f;
                     cb0[m] = (m == 0 ? 0.f : cb0[m - 1]) + gm0;

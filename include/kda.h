@@ -94,7 +94,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * number of sequences at most 65535.  B = 0 or
  * T = 0 is a no-op, except that final_state then receives initial_state (or
  * zeros).  Routing: KDA_CHUNKED with bf16 inputs and dk = 128 (any of the
- * dv above) runs the MFMA chunked kernel (KDA and EJK modes); every
+ * dv above) runs the MFMA chunked kernel (KDA and EJK modes), which needs
+ * q, k, v, o and (KDA) g 16-byte aligned (KDA_EINVAL otherwise); every
  * other combination runs the float32 token-by-token kernel, which computes
  * the same function step by step.  EJK decays are expected to be <= 0 (the ejkernel page
  * says so); the chunked kernel scales by e^{sum of decays} within a chunk,

@@ -87,6 +87,10 @@ PREFILL_ERRORS = [
     (dict(in_dtype=kda.F32, out_dtype=kda.BF16), kda.KDA_EUNSUPPORTED, "bf16 output"),
     (dict(chunk_size=32), kda.KDA_EUNSUPPORTED, "chunk_size"),
     (dict(lower_bound=-6.0), kda.KDA_EUNSUPPORTED, "lower_bound >= -5"),
+    (dict(q=P + 8), kda.KDA_EINVAL, "16-byte aligned"),
+    (dict(v=P + 2), kda.KDA_EINVAL, "16-byte aligned"),
+    (dict(o=P + 4), kda.KDA_EINVAL, "16-byte aligned"),
+    (dict(g=P + 4), kda.KDA_EINVAL, "16-byte aligned"),
 ]
 
 
