@@ -64,8 +64,8 @@ class PrefillInputs:
 @dataclass
 class DecodeInputs:
     q: np.ndarray            # [B, dk, H]
-    k: np.ndarray            # [B, dk, H]
-    v: np.ndarray            # [B, H, dv]
+    k: np.ndarray            # [B, dk, Hkv]
+    v: np.ndarray            # [B, Hkv, dv]
     g: np.ndarray | None     # KDA: [B, dk, H]; EJK: [B, 1, H]
     beta: np.ndarray         # [B, 1, H]
     a_log: np.ndarray        # [1, H]
@@ -84,9 +84,10 @@ def varlen_lengths(rng, n=8, lo=512, hi=8192, total_lo=30720, total_hi=34816):
 
 
 def prefill_inputs(B, T, H, dk, dv, seed, dtype="bf16", ejk=False, init_state=False,
-                   lengths=None, zero_params=False, lower_bound=-5.0, scale=None):
+                   lengths=None, zero_params=False, lower_bound=-5.0, scale=None, hkv=None):
     """Inputs of one prefill call.  With ``lengths`` (a list, or "varlen" for the
-    8-sequence recipe) the batch is packed: B must be 1 and T is the sum."""
+    8-sequence recipe) the batch is packed: B must be 1 and T is the sum.  With
+    ``hkv`` the key and value carry hkv heads (grouped heads)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     cu = None
     if lengths is not None:
@@ -97,9 +98,10 @@ def prefill_inputs(B, T, H, dk, dv, seed, dtype="bf16", ejk=False, init_state=Fa
         cu[1:] = np.cumsum(lengths)
         B, T = 1, int(cu[-1])
     n_state = (lengths.size if lengths is not None else B)
+    hkv = H if hkv is None else hkv
     q = _normal(rng, (B, T, H, dk))
-    k = _normal(rng, (B, T, H, dk))
-    v = _normal(rng, (B, T, H, dv))
+    k = _normal(rng, (B, T, hkv, dk))
+    v = _normal(rng, (B, T, hkv, dv))
     if not ejk:
         g = _normal(rng, (B, T, H, dk))
         beta = _normal(rng, (B, T, H))
@@ -126,11 +128,12 @@ def prefill_inputs(B, T, H, dk, dv, seed, dtype="bf16", ejk=False, init_state=Fa
                                [int(x) for x in lengths]})
 
 
-def decode_inputs(B, H, dk, dv, seed, ejk=False, lower_bound=-5.0, scale=None):
+def decode_inputs(B, H, dk, dv, seed, ejk=False, lower_bound=-5.0, scale=None, hkv=None):
     rng = np.random.Generator(np.random.PCG64(seed))
+    hkv = H if hkv is None else hkv
     q = _normal(rng, (B, dk, H))
-    k = _normal(rng, (B, dk, H))
-    v = _normal(rng, (B, H, dv))
+    k = _normal(rng, (B, dk, hkv))
+    v = _normal(rng, (B, hkv, dv))
     if not ejk:
         g = _normal(rng, (B, dk, H))
         beta = _normal(rng, (B, 1, H))
@@ -165,6 +168,16 @@ def prefill_b4_t4096_h16_d128():
 def prefill_long_t65536_h32_d128():
     """Long-context prefill: B=1, T=65536, H=32, dk=dv=128, nonzero initial state."""
     return prefill_inputs(1, 65536, 32, 128, 128, seed=1004, init_state=True)
+
+
+def prefill_grouped_b4_t4096_h16_hkv4_d128():
+    """Grouped key/value heads: the chunked-prefill shape with 4 key/value heads."""
+    return prefill_inputs(4, 4096, 16, 128, 128, seed=1006, hkv=4)
+
+
+def decode_grouped_b64_h32_hkv8_d128():
+    """Grouped key/value heads: the decode shape with 8 key/value heads."""
+    return decode_inputs(64, 32, 128, 128, seed=1007, hkv=8)
 
 
 def prefill_varlen_8seq_h32_d128(ejk=False):

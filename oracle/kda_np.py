@@ -52,10 +52,13 @@ def step(S, qh, kh, v, gamma_or_d, beta, ejk):
 
 def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_seqlens=None,
             scale=None, lower_bound=-5.0, use_qk_l2norm=True, ejk=False, eps=EPS):
+    """q [B, T, H, dk]; k [B, T, Hkv, dk], v [B, T, Hkv, dv]: query head h
+    uses key/value head h // (H // Hkv) (ejkernel "recurrent", num_kv_heads)."""
     q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
     B, T, H, dk = q.shape
+    grp = H // np.shape(k)[2]
+    k = np.repeat(np.asarray(k, np.float64), grp, axis=2)
+    v = np.repeat(np.asarray(v, np.float64), grp, axis=2)
     dv = v.shape[-1]
     if scale is None or not (scale > 0):
         scale = 1.0 / np.sqrt(dk)
@@ -89,10 +92,13 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
 
 def decode(q, k, g, v, beta, a_log, dt_bias, S, scale=None, lower_bound=-5.0,
            use_qk_l2norm=True, ejk=False, eps=EPS):
-    """kda_tkg layouts: q, k, g [B, dk, H]; v [B, H, dv]; beta [B, 1, H]."""
+    """kda_tkg layouts: q, g [B, dk, H]; k [B, dk, Hkv]; v [B, Hkv, dv];
+    beta [B, 1, H]."""
     q = np.swapaxes(np.asarray(q, np.float64), 1, 2)   # [B, H, dk]
-    k = np.swapaxes(np.asarray(k, np.float64), 1, 2)
     B, H, dk = q.shape
+    grp = H // np.shape(k)[2]
+    k = np.repeat(np.swapaxes(np.asarray(k, np.float64), 1, 2), grp, axis=1)
+    v = np.repeat(np.asarray(v, np.float64), grp, axis=1)
     if scale is None or not (scale > 0):
         scale = 1.0 / np.sqrt(dk)
     a_log = np.reshape(np.asarray(a_log, np.float64), (H,))

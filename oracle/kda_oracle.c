@@ -39,11 +39,16 @@
  *   [cu[n], cu[n+1]); each sequence starts from its own initial state (or
  *   zeros) and returns its own final state.
  *
- * Layouts (row-major): q, k [Ntok, H, dk]; v [Ntok, H, dv]; g [Ntok, H, dk]
- * (KDA) or [Ntok, H] (EJK, may be NULL = no decay); beta [Ntok, H];
- * a_log [H]; dt_bias [dk, H]; states [N, H, dk, dv]; o [Ntok, H, dv].
- * Decode uses the kda_tkg layouts: q, k, g [B, dk, H]; v [B, H, dv];
- * beta [B, H]; out [B, H, dv]; S [B, H, dk, dv] advanced in place.
+ *   Grouped heads (ejkernel "recurrent" page, run(): query has num_heads,
+ *   key and value num_kv_heads; gates, state and output num_heads): head h
+ *   takes the key and value of head h / (H / Hkv).
+ *
+ * Layouts (row-major): q [Ntok, H, dk]; k [Ntok, Hkv, dk]; v [Ntok, Hkv, dv];
+ * g [Ntok, H, dk] (KDA) or [Ntok, H] (EJK, may be NULL = no decay);
+ * beta [Ntok, H]; a_log [H]; dt_bias [dk, H]; states [N, H, dk, dv];
+ * o [Ntok, H, dv].  Decode uses the kda_tkg layouts: q, g [B, dk, H];
+ * k [B, dk, Hkv]; v [B, Hkv, dv]; beta [B, H]; out [B, H, dv];
+ * S [B, H, dk, dv] advanced in place.
  */
 #include <math.h>
 #include <stdint.h>
@@ -113,11 +118,11 @@ static double oracle_resolve_scale(double scale, int dk)
 int kda_oracle_prefill(const double* q, const double* k, const double* v, const double* g,
                        const double* beta, const double* a_log, const double* dt_bias,
                        const double* initial_state, const int64_t* cu_seqlens, int n_seqs,
-                       int H, int dk, int dv, double scale, double lower_bound, double eps,
+                       int H, int Hkv, int dk, int dv, double scale, double lower_bound, double eps,
                        int use_l2norm, int ejk, const int32_t* units, int n_units,
                        double* o, double* final_state, int n_threads)
 {
-    if (n_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return 1;
+    if (n_seqs < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return 1;
     scale = oracle_resolve_scale(scale, dk);
     const int total = units ? n_units : n_seqs * H;
 #ifdef _OPENMP
@@ -130,6 +135,7 @@ int kda_oracle_prefill(const double* q, const double* k, const double* v, const 
     for (int w = 0; w < total; ++w) {
         const int unit = units ? units[w] : w;
         const int n = unit / H, h = unit % H;
+        const int hk = h / (H / Hkv);   /* key/value head of head h */
         if (n < 0 || n >= n_seqs) { bad |= 1; continue; }
         double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
         double* qh = (double*)malloc(sizeof(double) * (size_t)dk);
@@ -142,8 +148,9 @@ int kda_oracle_prefill(const double* q, const double* k, const double* v, const 
         else memset(S, 0, sizeof(double) * sz);
         for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
             const size_t th = (size_t)t * H + h;
+            const size_t tkv = (size_t)t * Hkv + hk;
             oracle_normalise(q + th * dk, 1, dk, use_l2norm, eps, scale, qh);
-            oracle_normalise(k + th * dk, 1, dk, use_l2norm, eps, 1.0, kh);
+            oracle_normalise(k + tkv * dk, 1, dk, use_l2norm, eps, 1.0, kh);
             double b, d = 0.0;
             if (!ejk) {
                 oracle_gate(g + th * dk, 1, dt_bias, H, h, a_log[h], lower_bound, dk, gam);
@@ -152,7 +159,7 @@ int kda_oracle_prefill(const double* q, const double* k, const double* v, const 
                 d = g ? g[th] : 0.0;
                 b = beta[th];
             }
-            oracle_step(S, dk, dv, qh, kh, v + th * dv, 1, gam, d, b, ejk, o + th * dv, 1, u);
+            oracle_step(S, dk, dv, qh, kh, v + tkv * dv, 1, gam, d, b, ejk, o + th * dv, 1, u);
         }
         if (final_state) memcpy(final_state + soff, S, sizeof(double) * sz);
         free(S); free(qh); free(kh); free(gam); free(u);
@@ -162,10 +169,10 @@ int kda_oracle_prefill(const double* q, const double* k, const double* v, const 
 
 int kda_oracle_decode(const double* q, const double* k, const double* g, const double* v,
                       const double* beta, const double* a_log, const double* dt_bias,
-                      double scale, double lower_bound, double eps, int B, int H, int dk, int dv,
-                      int use_l2norm, int ejk, double* out, double* S, int n_threads)
+                      double scale, double lower_bound, double eps, int B, int H, int Hkv, int dk,
+                      int dv, int use_l2norm, int ejk, double* out, double* S, int n_threads)
 {
-    if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return 1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || dk <= 0 || dv <= 0) return 1;
     scale = oracle_resolve_scale(scale, dk);
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);
@@ -175,15 +182,17 @@ int kda_oracle_decode(const double* q, const double* k, const double* g, const d
 #pragma omp parallel for schedule(static)
     for (int w = 0; w < B * H; ++w) {
         const int b = w / H, h = w % H;
+        const int hk = h / (H / Hkv);   /* key/value head of head h */
         double* qv = (double*)malloc(sizeof(double) * (size_t)dk);
         double* kv = (double*)malloc(sizeof(double) * (size_t)dk);
         double* gam = (double*)malloc(sizeof(double) * (size_t)dk);
         double* u = (double*)malloc(sizeof(double) * (size_t)dv);
-        /* q, k, g are [B, dk, H]: element i of item (b, h) sits at (b*dk + i)*H + h */
+        /* q, g are [B, dk, H]: element i of item (b, h) sits at (b*dk + i)*H + h;
+           k is [B, dk, Hkv] and v [B, Hkv, dv] */
         const double* qb = q + (size_t)b * dk * H + h;
-        const double* kb = k + (size_t)b * dk * H + h;
+        const double* kb = k + (size_t)b * dk * Hkv + hk;
         oracle_normalise(qb, H, dk, use_l2norm, eps, scale, qv);
-        oracle_normalise(kb, H, dk, use_l2norm, eps, 1.0, kv);
+        oracle_normalise(kb, Hkv, dk, use_l2norm, eps, 1.0, kv);
         double bt, d = 0.0;
         if (!ejk) {
             oracle_gate(g + (size_t)b * dk * H + h, H, dt_bias, H, h, a_log[h], lower_bound, dk, gam);
@@ -192,7 +201,7 @@ int kda_oracle_decode(const double* q, const double* k, const double* g, const d
             d = g ? g[(size_t)b * H + h] : 0.0;
             bt = beta[(size_t)b * H + h];
         }
-        oracle_step(S + (size_t)w * dk * dv, dk, dv, qv, kv, v + (size_t)w * dv, 1, gam, d, bt, ejk,
+        oracle_step(S + (size_t)w * dk * dv, dk, dv, qv, kv, v + ((size_t)b * Hkv + hk) * dv, 1, gam, d, bt, ejk,
                     out + (size_t)w * dv, 1, u);
         free(qv); free(kv); free(gam); free(u);
     }

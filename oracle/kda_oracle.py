@@ -44,10 +44,10 @@ def _load():
         I = ctypes.c_int
         D = ctypes.c_double
         lib.kda_oracle_prefill.argtypes = [P, P, P, P, P, P, P, P,
-                                           ctypes.POINTER(ctypes.c_int64), I, I, I, I, D, D, D,
+                                           ctypes.POINTER(ctypes.c_int64), I, I, I, I, I, D, D, D,
                                            I, I, ctypes.POINTER(ctypes.c_int32), I, P, P, I]
         lib.kda_oracle_prefill.restype = I
-        lib.kda_oracle_decode.argtypes = [P, P, P, P, P, P, P, D, D, D, I, I, I, I, I, I, P, P, I]
+        lib.kda_oracle_decode.argtypes = [P, P, P, P, P, P, P, D, D, D, I, I, I, I, I, I, I, P, P, I]
         lib.kda_oracle_decode.restype = I
         lib.kda_oracle_max_threads.restype = I
         _lib = lib
@@ -75,7 +75,8 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
             threads=0, eps=EPS):
     """Token-by-token float64 recurrence over every (sequence, head).
 
-    q, k: [B, T, H, dk]; v: [B, T, H, dv]; g: [B, T, H, dk] raw gate (KDA) or
+    q: [B, T, H, dk]; k: [B, T, Hkv, dk]; v: [B, T, Hkv, dv] (Hkv divides H;
+    head h uses key/value head h // (H // Hkv)); g: [B, T, H, dk] raw gate (KDA) or
     [B, T, H] log-decay / None (EJK); beta: [B, T, H] logits (KDA) or
     activated (EJK); a_log [H]; dt_bias [dk, H]; initial_state [N, H, dk, dv].
     With cu_seqlens ([N+1]) the batch must be 1 and sequences are packed.
@@ -86,6 +87,7 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, dk = q.shape
+    Hkv = k.shape[2]
     dv = v.shape[-1]
     if cu_seqlens is None:
         cu = np.arange(B + 1, dtype=np.int64) * T
@@ -110,7 +112,7 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
     sc = -1.0 if scale is None else float(scale)
     rc = lib.kda_oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(a_log),
                                 _ptr(dt_bias), _ptr(s0),
-                                cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, H, dk, dv,
+                                cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, H, Hkv, dk, dv,
                                 sc, float(lower_bound), float(eps), int(bool(use_qk_l2norm)),
                                 int(bool(ejk)), uptr, nu, _ptr(o), _ptr(fs), int(threads))
     if rc != 0:
@@ -122,13 +124,15 @@ def decode(q, k, g, v, beta, a_log, dt_bias, S, scale=None, lower_bound=-5.0,
            use_qk_l2norm=True, ejk=False, threads=0, eps=EPS):
     """One step for each of B requests, kda_tkg layouts.
 
-    q, k, g: [B, dk, H] (EJK: g is [B, 1, H] log-decay or None); v: [B, H, dv];
+    q, g: [B, dk, H] (EJK: g is [B, 1, H] log-decay or None); k: [B, dk, Hkv];
+    v: [B, Hkv, dv];
     beta: [B, 1, H]; a_log: [1, H]; dt_bias: [dk, H]; S: [B, H, dk, dv].
     Returns (out [B, H, dv], S_new) without touching the caller's S.
     """
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, dk, H = q.shape
+    Hkv = k.shape[2]
     dv = v.shape[-1]
     g = _f64(g)
     beta = _f64(beta)
@@ -138,7 +142,7 @@ def decode(q, k, g, v, beta, a_log, dt_bias, S, scale=None, lower_bound=-5.0,
     out = np.zeros((B, H, dv), dtype=np.float64)
     sc = -1.0 if scale is None else float(scale)
     rc = lib.kda_oracle_decode(_ptr(q), _ptr(k), _ptr(g), _ptr(v), _ptr(beta), _ptr(a_log),
-                               _ptr(dt_bias), sc, float(lower_bound), float(eps), B, H, dk, dv,
+                               _ptr(dt_bias), sc, float(lower_bound), float(eps), B, H, Hkv, dk, dv,
                                int(bool(use_qk_l2norm)), int(bool(ejk)), _ptr(out), _ptr(S_new),
                                int(threads))
     if rc != 0:

@@ -404,3 +404,44 @@ def test_zero_vector_normalises_to_zero():
     o, s = kda_oracle.prefill(q, k, v, np.zeros((1, 1, 1, 4)), np.zeros((1, 1, 1)),
                               a_log=np.zeros(1))
     assert np.all(s == 0) and np.all(o == 0)
+
+
+# --------------------------------------------------------- grouped heads ---
+# ejkernel "recurrent" run(): query, gates and state carry num_heads, key and
+# value num_kv_heads.  Reading taken: consecutive heads share a key/value head
+# (head h reads head h // (H // Hkv)).  A grouped run must equal the ungrouped
+# run on keys and values repeated that way, exactly: the grouping is indexing.
+@pytest.mark.parametrize("impl", IMPLS, ids=["c", "numpy"])
+@pytest.mark.parametrize("ejk", [False, True])
+def test_grouped_heads_equal_repeated_kv(impl, ejk):
+    args, kw = _rand_case(80 + ejk, B=2, T=9, H=6, dk=5, dv=4, ejk=ejk)
+    q, k, v, g, beta = args
+    grp = 3                                   # Hkv = 2
+    kg, vg = k[:, :, ::grp].copy(), v[:, :, ::grp].copy()
+    o_g, s_g = impl.prefill(q, kg, vg, g, beta, **kw)
+    o_r, s_r = kda_oracle.prefill(q, np.repeat(kg, grp, axis=2), np.repeat(vg, grp, axis=2), g, beta, **kw)
+    np.testing.assert_allclose(o_g, o_r, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(s_g, s_r, rtol=1e-14, atol=1e-15)
+    # and it is not the interleaved grouping (head h reading h % Hkv)
+    o_i, _ = kda_oracle.prefill(q, np.tile(kg, (1, 1, grp, 1)), np.tile(vg, (1, 1, grp, 1)), g, beta, **kw)
+    assert _rel(o_g, o_i) > 1e-3
+
+
+@pytest.mark.parametrize("impl", IMPLS, ids=["c", "numpy"])
+@pytest.mark.parametrize("ejk", [False, True])
+def test_grouped_decode_equals_repeated_kv(impl, ejk):
+    rng = np.random.default_rng(90 + ejk)
+    B, H, Hkv, dk, dv = 3, 4, 2, 5, 3
+    q, g = rng.standard_normal((B, dk, H)), rng.standard_normal((B, dk, H))
+    k, v = rng.standard_normal((B, dk, Hkv)), rng.standard_normal((B, Hkv, dv))
+    beta = rng.standard_normal((B, 1, H))
+    if ejk:
+        g = -0.1 * np.abs(rng.standard_normal((B, 1, H)))
+        beta = 1.0 / (1.0 + np.exp(-beta))
+    a_log, dtb = rng.uniform(-1, 1, (1, H)), 0.1 * rng.standard_normal((dk, H))
+    S = rng.standard_normal((B, H, dk, dv))
+    o_g, s_g = impl.decode(q, k, g, v, beta, a_log, dtb, S, ejk=ejk)
+    o_r, s_r = kda_oracle.decode(q, np.repeat(k, 2, axis=2), g, np.repeat(v, 2, axis=1), beta, a_log, dtb, S,
+                                 ejk=ejk)
+    np.testing.assert_allclose(o_g, o_r, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(s_g, s_r, rtol=1e-14, atol=1e-15)
