@@ -42,10 +42,12 @@ METRIC = "KDA prefill tokens/s + decode steps/s; % MFMA peak / % HBM BW peak"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFS = 2500.0
 
-# decode, B=64 H=32 dk=dv=128: state read + write, q/k/g [B,dk,H], v/out [B,H,dv],
-# beta [B,1,H], a_log [1,H], dt_bias [dk,H] - all fp32
-def decode_bytes(B, H, dk, dv):
-    return 4 * (2 * B * H * dk * dv + 3 * B * dk * H + 2 * B * H * dv + B * H + H + dk * H)
+# decode, B=64 H=32 dk=dv=128: state read + write, q/g [B,dk,H], k [B,dk,Hkv],
+# v [B,Hkv,dv], out [B,H,dv], beta [B,1,H], a_log [1,H], dt_bias [dk,H] - all fp32
+def decode_bytes(B, H, dk, dv, hkv=None):
+    hkv = H if hkv is None else hkv
+    return 4 * (2 * B * H * dk * dv + 2 * B * dk * H + B * dk * hkv + B * hkv * dv + B * H * dv
+                + B * H + H + dk * H)
 
 
 def decode_flops(B, H, dk, dv):
@@ -53,11 +55,13 @@ def decode_flops(B, H, dk, dv):
     return 7 * B * H * dk * dv
 
 
-def prefill_bytes(ntok, H, dk, dv, n_states, init_state, ejk=False, io_bytes=2):
-    # q, k, v in; g (KDA: [dk] per token-head, EJK: one decay) and beta fp32; o out;
-    # final states written, initial states read when given; a_log, dt_bias (KDA)
+def prefill_bytes(ntok, H, dk, dv, n_states, init_state, ejk=False, io_bytes=2, hkv=None):
+    # q (H heads), k, v (Hkv heads) in; g (KDA: [dk] per token-head, EJK: one decay)
+    # and beta fp32; o out; final states written, initial states read when given;
+    # a_log, dt_bias (KDA)
+    hkv = H if hkv is None else hkv
     gate = 4 if ejk else dk * 4
-    per_tok = H * ((2 * dk + dv) * io_bytes + gate + 4 + dv * io_bytes)
+    per_tok = H * (dk * io_bytes + gate + 4 + dv * io_bytes) + hkv * (dk + dv) * io_bytes
     states = n_states * H * dk * dv * 4 * (2 if init_state else 1)
     return ntok * per_tok + states + (0 if ejk else H * 4 + dk * H * 4)
 
@@ -96,19 +100,24 @@ def _counter_traffic(name, src_hash):
 
 
 def bench_decode(steps, warmup, nbuf=5):
+    from gated_delta_rule_90_amd import workloads
+    return _decode_run(workloads.decode_b64_h32_d128(), steps, warmup, nbuf)
+
+
+def _decode_run(inp, steps, warmup, nbuf=5):
+    """Time kda.decode_step with the state rotating over nbuf buffers."""
     import torch
     import gated_delta_rule_90_amd as kda
-    from gated_delta_rule_90_amd import workloads
-    inp = workloads.decode_b64_h32_d128()
     f = torch.float32
     d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", f)
     q, k, v, g, beta = d(inp.q), d(inp.k), d(inp.v), d(inp.g), d(inp.beta)
     a_log, dtb = d(inp.a_log), d(inp.dt_bias)
     S0 = d(inp.S)
     states = [S0.clone() for _ in range(nbuf)]
-    out = torch.empty_like(v)
     B, dk, H = inp.q.shape
+    hkv = inp.k.shape[2]
     dv = inp.v.shape[-1]
+    out = torch.empty((B, H, dv), dtype=f, device="cuda")   # [B, H, dv]: v has Hkv heads
 
     def step(i):
         kda.decode_step(q, k, v, g, beta, a_log, dtb, states[i % nbuf], scale=inp.scale,
@@ -126,7 +135,7 @@ def bench_decode(steps, warmup, nbuf=5):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    nbytes = decode_bytes(B, H, dk, dv)
+    nbytes = decode_bytes(B, H, dk, dv, hkv)
     achieved = nbytes / (ms * 1e-3) / 1e9
     sh = _src_hash("kda_decode.hip", "kda_device.h")
     traffic = _counter_traffic("decode_b64_h32_d128", sh)
@@ -227,7 +236,7 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False):
     ms = e0.elapsed_time(e1) / steps
     ntok = B * T if cu is None else int(inp.cu_seqlens[-1])
     io_bytes = 2 if inp.dtype == "bf16" else 4
-    nbytes = prefill_bytes(ntok, H, dk, dv, nst, s0 is not None, inp.ejk, io_bytes)
+    nbytes = prefill_bytes(ntok, H, dk, dv, nst, s0 is not None, inp.ejk, io_bytes, inp.k.shape[2])
     res = {"tokens_per_s": round(ntok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
            "alg_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "path": "chunked MFMA" if chunked else "token-by-token"}
@@ -327,6 +336,14 @@ def bench_configs(steps, warmup):
         out[name] = res
         del inp
         gc.collect()
+    # grouped key/value heads (ejkernel "recurrent": num_kv_heads)
+    res = _prefill_run(workloads.prefill_grouped_b4_t4096_h16_hkv4_d128(), steps, warmup, nsets=2)
+    out["prefill_grouped_b4_t4096_h16_hkv4_d128"] = res
+    gc.collect()
+    _, dres = _decode_run(workloads.decode_grouped_b64_h32_hkv8_d128(), steps, warmup)
+    out["decode_grouped_b64_h32_hkv8_d128"] = {
+        "steps_per_s": round(dres["steps_per_s"], 2), "ms_per_step": round(dres["ms"], 5),
+        "alg_bytes": dres["bytes"], "hbm_frac": dres["roofline"]["frac"]}
     return out
 
 

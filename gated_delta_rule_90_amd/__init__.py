@@ -49,12 +49,12 @@ def lib() -> ctypes.CDLL:
     vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     i32, u32, f32 = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
     L.kda_prefill.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, fp, fp, ip, i32, i32, i32,
-                              i32, i32, i32, f32, f32, i32, u32, vp, ctypes.c_int, fp, vp,
+                              i32, i32, i32, i32, f32, f32, i32, u32, vp, ctypes.c_int, fp, vp,
                               ctypes.c_size_t, vp]
     L.kda_prefill.restype = ctypes.c_int
     L.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, u32]
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
-    L.kda_decode_step.argtypes = [fp, fp, fp, fp, fp, fp, fp, f32, f32, i32, i32, i32, i32, u32,
+    L.kda_decode_step.argtypes = [fp, fp, fp, fp, fp, fp, fp, f32, f32, i32, i32, i32, i32, i32, u32,
                                   fp, fp, vp]
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_last_error.argtypes = []
@@ -103,8 +103,10 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
             scale=None, lower_bound=-5.0, chunk_size=64, use_qk_l2norm=True, use_chunked=True,
             ejk=False, return_state=False, out_dtype=None, out=None, final_state=None,
             stream=None):
-    """KDA over whole sequences.  q, k [B, T, H, dk] and v [B, T, H, dv] in bf16
-    or fp32; g [B, T, H, dk] raw gate (EJK: [B, T, H] log-decay or None);
+    """KDA over whole sequences.  q [B, T, H, dk], k [B, T, Hkv, dk] and
+    v [B, T, Hkv, dv] in bf16 or fp32 (Hkv divides H: head h reads the key and
+    value of head h // (H // Hkv)); g [B, T, H, dk] raw gate (EJK: [B, T, H]
+    log-decay or None);
     beta [B, T, H] (KDA logits / EJK activated); a_log [H]; dt_bias [dk, H];
     initial_state [N, H, dk, dv]; cu_seqlens [N + 1] int32 with B == 1.
     Returns o, or (o, final_state) when return_state (final_state may be passed
@@ -122,9 +124,11 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
     _dev("dt_bias", dt_bias, f, dev)
     _dev("initial_state", initial_state, f, dev)
     _dev("cu_seqlens", cu_seqlens, (torch.int32,), dev)
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
-        raise ValueError("q, k must be [B, T, H, dk] and v [B, T, H, dv]")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape[:2] != q.shape[:2] or \
+            k.shape[3] != q.shape[3] or v.shape[:3] != k.shape[:3] or q.shape[2] % k.shape[2] != 0:
+        raise ValueError("q must be [B, T, H, dk], k [B, T, Hkv, dk] and v [B, T, Hkv, dv], Hkv dividing H")
     B, T, H, dk = q.shape
+    Hkv = k.shape[2]
     dv = v.shape[3]
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
     if beta.shape != (B, T, H):
@@ -162,7 +166,7 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
     _check(lib().kda_prefill(
         _ptr(q), _ptr(k), _ptr(v), BF16 if q.dtype == torch.bfloat16 else F32,
         _ptr(g), _ptr(beta), _ptr(a_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_seqlens),
-        nseq, B, T, H, dk, dv, sc, float(lower_bound), int(chunk_size), flags,
+        nseq, B, T, H, Hkv, dk, dv, sc, float(lower_bound), int(chunk_size), flags,
         _ptr(out), BF16 if odt == torch.bfloat16 else F32, _ptr(final_state), _ptr(ws), wsb,
         _stream(dev, stream)))
     if return_state:
@@ -173,7 +177,8 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
 def decode_step(q, k, v, g, beta, a_log, dt_bias, S, *, scale=None, lower_bound=-5.0,
                 use_qk_l2norm=True, ejk=False, out=None, stream=None):
     """One token for each of B requests, kda_tkg layouts (all fp32):
-    q, k, g [B, dk, H] (EJK: g [B, 1, H] or None); v [B, H, dv]; beta [B, 1, H];
+    q, g [B, dk, H] (EJK: g [B, 1, H] or None); k [B, dk, Hkv]; v [B, Hkv, dv]
+    (Hkv divides H); beta [B, 1, H];
     a_log [1, H]; dt_bias [dk, H]; S [B, H, dk, dv] advanced in place.
     Returns out [B, H, dv]."""
     import torch
@@ -182,23 +187,32 @@ def decode_step(q, k, v, g, beta, a_log, dt_bias, S, *, scale=None, lower_bound=
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("a_log", a_log),
                     ("dt_bias", dt_bias), ("S", S)):
         _dev(name, t, f, dev)
-    if q.dim() != 3 or k.shape != q.shape:
-        raise ValueError("q, k must be [B, dk, H]")
+    if q.dim() != 3 or k.dim() != 3 or k.shape[:2] != q.shape[:2] or q.shape[2] % k.shape[2] != 0:
+        raise ValueError("q must be [B, dk, H] and k [B, dk, Hkv], Hkv dividing H")
     B, dk, H = q.shape
+    Hkv = k.shape[2]
     if S.dim() != 4 or tuple(S.shape[:3]) != (B, H, dk):
         raise ValueError("S must be [B, H, dk, dv]")
     dv = S.shape[3]
-    if tuple(v.shape) != (B, H, dv) or beta.numel() != B * H:
-        raise ValueError("v must be [B, H, dv] and beta [B, 1, H]")
+    if tuple(v.shape) != (B, Hkv, dv) or beta.numel() != B * H:
+        raise ValueError("v must be [B, Hkv, dv] and beta [B, 1, H]")
     if g is not None and g.numel() != (B * H if ejk else B * dk * H):
         raise ValueError("g must be [B, dk, H] (EJK: [B, 1, H])")
+    if not ejk and g is None:
+        raise ValueError("KDA mode needs g")
+    if a_log is not None and a_log.numel() != H:
+        raise ValueError("a_log must hold H values")
+    if dt_bias is not None and tuple(dt_bias.shape) != (dk, H):
+        raise ValueError("dt_bias must be [dk, H]")
     if out is None:
         out = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
     else:
         _dev("out", out, f, dev)
+        if tuple(out.shape) != (B, H, dv):
+            raise ValueError("out must be [B, H, dv]")
     flags = (QK_L2NORM if use_qk_l2norm else 0) | (EJK if ejk else 0)
     sc = -1.0 if scale is None else float(scale)
     _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(g), _ptr(v), _ptr(beta), _ptr(a_log),
-                                 _ptr(dt_bias), sc, float(lower_bound), B, H, dk, dv, flags,
+                                 _ptr(dt_bias), sc, float(lower_bound), B, H, Hkv, dk, dv, flags,
                                  _ptr(out), _ptr(S), _stream(dev, stream)))
     return out

@@ -70,7 +70,7 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
                          const float* g, const float* beta, const float* a_log,
                          const float* dt_bias, const float* initial_state,
                          const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
-                         int32_t H, int32_t dk, int32_t dv, float scale, float lower_bound,
+                         int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale, float lower_bound,
                          int32_t chunk_size, uint32_t flags, void* o, kda_dtype_t out_dtype,
                          float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream)
@@ -88,6 +88,9 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
     } else if (num_seqs != 0 && num_seqs != B) {
         return fail(KDA_EINVAL, "kda_prefill: num_seqs (%d) must be 0 or B (%d) without cu_seqlens", num_seqs, B);
     }
+    if (Hkv == 0) Hkv = H;
+    if (Hkv < 0 || H % Hkv != 0)
+        return fail(KDA_EINVAL, "kda_prefill: Hkv (%d) must divide H (%d)", Hkv, H);
     const int N = cu_seqlens ? num_seqs : B;
     const bool has_tokens = (cu_seqlens ? (T > 0 && N > 0) : (B > 0 && T > 0));
     if (has_tokens) {
@@ -116,6 +119,7 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
     a.N = N;
     a.T = T;
     a.H = H; a.dk = dk; a.dv = dv;
+    a.Hkv = Hkv;
     a.scale = (scale > 0.f) ? scale : 1.0f / std::sqrt((float)dk);  // NaN also selects the default
     a.lower_bound = lower_bound;
     a.l2norm = (flags & KDA_QK_L2NORM) != 0;
@@ -145,14 +149,17 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
 
 kda_status_t kda_decode_step(const float* q, const float* k, const float* g, const float* v,
                              const float* beta, const float* a_log, const float* dt_bias,
-                             float scale, float lower_bound, int32_t B, int32_t H, int32_t dk,
-                             int32_t dv, uint32_t flags, float* out, float* S, void* stream)
+                             float scale, float lower_bound, int32_t B, int32_t H, int32_t Hkv,
+                             int32_t dk, int32_t dv, uint32_t flags, float* out, float* S, void* stream)
 {
     if (flags & ~(KDA_QK_L2NORM | KDA_EJK))
         return fail(KDA_EINVAL, "kda_decode_step: unsupported flag bits 0x%x", flags & ~(KDA_QK_L2NORM | KDA_EJK));
     const bool ejk = (flags & KDA_EJK) != 0;
     if (B < 0 || H <= 0 || dk <= 0 || dv <= 0)
         return fail(KDA_EINVAL, "kda_decode_step: bad sizes B=%d H=%d dk=%d dv=%d", B, H, dk, dv);
+    if (Hkv == 0) Hkv = H;
+    if (Hkv < 0 || H % Hkv != 0)
+        return fail(KDA_EINVAL, "kda_decode_step: Hkv (%d) must divide H (%d)", Hkv, H);
     if (B > 0) {
         if (!q || !k || !v || !beta || !out || !S) return fail(KDA_EINVAL, "kda_decode_step: q, k, v, beta, out and S are required");
         if (!ejk && (!g || !a_log)) return fail(KDA_EINVAL, "kda_decode_step: KDA mode needs g and a_log");
@@ -168,6 +175,7 @@ kda_status_t kda_decode_step(const float* q, const float* k, const float* g, con
     a.scale = (scale > 0.f) ? scale : 1.0f / std::sqrt((float)dk);
     a.lower_bound = lower_bound;
     a.B = B; a.H = H; a.dk = dk; a.dv = dv;
+    a.Hkv = Hkv;
     a.l2norm = (flags & KDA_QK_L2NORM) != 0;
     a.ejk = ejk;
     a.out = out;

@@ -311,17 +311,20 @@ struct PrepRaw {
 // PART 0 loads q, k and beta, PART 1 the gates (half of the bytes), PART 2 both.
 template <bool EJK, int PART = 2>
 __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const bf16_t* q, const bf16_t* k,
-                                          const float* g, const float* beta, int H, int lane, int blk)
+                                          const float* g, const float* beta, int H, int HKV, int lane, int blk)
 {
     const size_t base = ((size_t)it.c0 * H + it.h) * DK;   // channel 0 of the item's first row
     const size_t rstride = (size_t)H * DK;
     if constexpr (PART != 1) {
+        // k: the key/value head of head h, rows HKV heads apart
+        const size_t kbase = ((size_t)it.c0 * HKV + it.h / (H / HKV)) * DK;
+        const size_t kstride = (size_t)HKV * DK;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * blk + 4 * i + (lane >> 4);
-            const size_t off = base + (size_t)((row < it.len) ? row : 0) * rstride + 8 * (lane & 15);
-            r.q[i] = *reinterpret_cast<const u32x4_t*>(q + off);
-            r.k[i] = *reinterpret_cast<const u32x4_t*>(k + off);
+            const int rr = (row < it.len) ? row : 0;
+            r.q[i] = *reinterpret_cast<const u32x4_t*>(q + base + (size_t)rr * rstride + 8 * (lane & 15));
+            r.k[i] = *reinterpret_cast<const u32x4_t*>(k + kbase + (size_t)rr * kstride + 8 * (lane & 15));
         }
         const int rb = 16 * blk + (lane & 15);
         r.beta = beta[(size_t)(it.c0 + ((rb < it.len) ? rb : 0)) * H + it.h];
@@ -348,7 +351,7 @@ template <bool EJK>
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const float* __restrict__ a_log, const float* __restrict__ dt_bias,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ off, int N, int T, int H, int nslots,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ off, int N, int T, int H, int HKV, int nslots,
     float scale, float lower_bound, int l2norm, unsigned char* __restrict__ ws)
 {
     __shared__ __attribute__((aligned(16))) unsigned char smem[PREP_LDS];
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     int item = blockIdx.x;
     PrepItem it = prep_item(item, nitems, H, cu, off, N, T);
     PrepRaw cur;
-    if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, threadIdx.x & 63, threadIdx.x >> 6);
+    if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, HKV, threadIdx.x & 63, threadIdx.x >> 6);
     for (; item < nitems; item += gridDim.x) {
         // Thread indices are re-read opaquely in every iteration, so that the
         // per-lane address arithmetic derived from them is recomputed where it
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         const PrepItem me = it;
         if (!me.valid) {   // a slot past the packed chunk count: only move on
             it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
-            if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, lane, blk);
+            if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, HKV, lane, blk);
             continue;
         }
         const int h = me.h;
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         // item, which keeps the loaded registers out of a branch)
         it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
         const PrepItem nx = it.valid ? it : me;
-        prep_load<EJK, 0>(cur, nx, q, k, g, beta, H, lane, blk);
+        prep_load<EJK, 0>(cur, nx, q, k, g, beta, H, HKV, lane, blk);
         lds_barrier();
 
         // ---------------- phase 1b: decay factors; QL, KL, KRd and Kg^T in LDS; Qg, Kc^T out
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         }
         lds_barrier();
 
-        prep_load<EJK, 1>(cur, nx, q, k, g, beta, H, lane, blk);
+        prep_load<EJK, 1>(cur, nx, q, k, g, beta, H, HKV, lane, blk);
 
         // ---------------- phase 2: A and P on 16x16 block pairs (I >= J)
         f32x4_t accA[3], accP[3];
@@ -849,7 +852,7 @@ struct Frags {
 // part 0 = V tile, T', P, e^{b_C}; part 1 = W, Qg; part 2 = Kc^T.
 template <int NJB, int PART>
 __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* rec, const bf16_t* v, int c0,
-                                           int len, int H, int h, int DV, int j0, int I, int lane, int tid)
+                                           int len, int HKV, int hk, int DV, int j0, int I, int lane, int tid)
 {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int fo = l16 * 32 + 8 * g4;   // lane offset inside a 16x32 fragment
@@ -866,7 +869,7 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
             const int s = min(seg / (DVT / 8), C - 1);
             const int jj = (seg % (DVT / 8)) * 8;
             const int ss = (s < len) ? s : 0;
-            f.v[it] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * H + h) * DV + j0 + jj);
+            f.v[it] = *reinterpret_cast<const uint4*>(v + ((size_t)(c0 + ss) * HKV + hk) * DV + j0 + jj);
         }
         // T' and P are lower triangular: k-slice 1 (columns 32..63) of the first
         // two row blocks is zero and is not stored.  Those two fragments are
@@ -904,7 +907,7 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
 template <int NJB, typename Tout>
 __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ init, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ order, int N, int T, int H, int DV,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ order, int N, int T, int H, int HKV, int DV,
     const unsigned char* __restrict__ ws, Tout* __restrict__ o, float* __restrict__ final_state)
 {
     using Sh = ScanShape<NJB>;
@@ -935,6 +938,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const int h = urank - nrank * H;
     const int n = order ? order[nrank] : nrank;   // packed batches: longest sequences first
     const int unit = n * H + h;
+    const int hk = h / (H / HKV);   // the key/value head of head h
     const int j0 = tile * DVT;
 
     int t_begin, t_end;
@@ -975,7 +979,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
         const int cc = min(c, nch - 1);
         const int c0 = t_begin + cc * C;
         load_frags<NJB, decltype(part)::value>(f, ws + ((size_t)(slot0 + cc) * H + h) * REC_BYTES, v, c0,
-                                               min(C, t_end - c0), H, h, DV, j0, I, lane, tid);
+                                               min(C, t_end - c0), HKV, hk, DV, j0, I, lane, tid);
     };
     using Part0 = std::integral_constant<int, 0>;
     using Part1 = std::integral_constant<int, 1>;
@@ -1145,12 +1149,12 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         const bf16_t* kk = static_cast<const bf16_t*>(a.k);
         if (a.ejk)
             hipLaunchKernelGGL(chunk_prep_kernel<true>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
-                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, (int)slots, a.scale, a.lower_bound,
-                               (int)a.l2norm, recs);
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.Hkv, (int)slots, a.scale,
+                               a.lower_bound, (int)a.l2norm, recs);
         else
             hipLaunchKernelGGL(chunk_prep_kernel<false>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
-                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, (int)slots, a.scale, a.lower_bound,
-                               (int)a.l2norm, recs);
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.Hkv, (int)slots, a.scale,
+                               a.lower_bound, (int)a.l2norm, recs);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1163,13 +1167,13 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     Tout* oo = static_cast<Tout*>(a.o);
     if (njb == 4)
         hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.dv, recs, oo, a.final_state);
+                           order, a.N, a.T, a.H, a.Hkv, a.dv, recs, oo, a.final_state);
     else if (njb == 2)
         hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.dv, recs, oo, a.final_state);
+                           order, a.N, a.T, a.H, a.Hkv, a.dv, recs, oo, a.final_state);
     else
         hipLaunchKernelGGL((chunk_scan_kernel<1, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.dv, recs, oo, a.final_state);
+                           order, a.N, a.T, a.H, a.Hkv, a.dv, recs, oo, a.final_state);
     return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ template <int DK, int DV, bool EJK>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ a_log,
-    const float* __restrict__ dt_bias, float scale, float lower_bound, int B, int H, int l2norm,
+    const float* __restrict__ dt_bias, float scale, float lower_bound, int B, int H, int HKV, int l2norm,
     float* __restrict__ out, float* __restrict__ S)
 {
     using Sh = DecodeShape<DK, DV>;
@@ -77,6 +77,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     const int h = idx % H;
     if (b >= B) return;
     const int item = b * H + h;
+    const int hk = h / (H / HKV);          // the key/value head of head h
+    const int kvitem = b * HKV + hk;
     const int t = threadIdx.x;
     const int cg = t % NCG;
     const int rg = t / NCG;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     if (t < DK) {
         const size_t off = ((size_t)b * DK + t) * H + h;
         qi = q[off];
-        ki = k[off];
+        ki = k[((size_t)b * DK + t) * HKV + hk];
         if (!EJK) {
             gi = g[off];
             di = dt_bias ? dt_bias[(size_t)t * H + h] : 0.f;
@@ -182,7 +184,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
     }
 
     // 4. delta, output, new state (in place)
-    const float4 vv = *reinterpret_cast<const float4*>(v + (size_t)item * DV + cg * 4);
+    const float4 vv = *reinterpret_cast<const float4*>(v + (size_t)kvitem * DV + cg * 4);
     float4 d;
     d.x = bt * (vv.x - u.x); d.y = bt * (vv.y - u.y);
     d.z = bt * (vv.z - u.z); d.w = bt * (vv.w - u.w);
@@ -212,11 +214,11 @@ hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t stream)
     const dim3 block(DecodeShape<DK, DV>::THREADS);
     if (a.ejk)
         hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, 0, stream, a.q, a.k, a.g, a.v,
-                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.B, a.H, (int)a.l2norm,
+                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.B, a.H, a.Hkv, (int)a.l2norm,
                            a.out, a.S);
     else
         hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, 0, stream, a.q, a.k, a.g, a.v,
-                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.B, a.H, (int)a.l2norm,
+                           a.beta, a.a_log, a.dt_bias, a.scale, a.lower_bound, a.B, a.H, a.Hkv, (int)a.l2norm,
                            a.out, a.S);
     return hipGetLastError();
 }

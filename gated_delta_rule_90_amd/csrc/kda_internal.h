@@ -22,6 +22,7 @@ struct PrefillArgs {
     int N;                 // number of sequences (dense: B)
     int T;                 // dense: tokens per sequence; packed: total tokens
     int H, dk, dv;
+    int Hkv;               // key/value heads: head h reads k and v of head h / (H / Hkv)
     float scale;
     float lower_bound;
     bool l2norm;
@@ -44,6 +45,7 @@ struct DecodeArgs {
     float scale;
     float lower_bound;
     int B, H, dk, dv;
+    int Hkv;               // key/value heads (k [B, dk, Hkv], v [B, Hkv, dv])
     bool l2norm;
     bool ejk;
     float* out;

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, const float* __restrict__ init,
-    const int32_t* __restrict__ cu, int T, int H, int DV, float scale, float lower_bound,
+    const int32_t* __restrict__ cu, int T, int H, int HKV, int DV, float scale, float lower_bound,
     int l2norm, Tout* __restrict__ o, float* __restrict__ final_state)
 {
     constexpr int PER_LANE = (DK + kWave - 1) / kWave;  // prologue channels per lane
@@ -101,6 +101,7 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     const int part = lane % LPC;         // rows part * RPL .. part * RPL + RPL - 1
     const int c = blockIdx.x * CPW + lane / LPC;
     const int h = blockIdx.y;
+    const int hk = h / (H / HKV);   // the key/value head of head h
     const int n = blockIdx.z;
     const bool active = c < DV;
 
@@ -160,19 +161,20 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     auto load = [&](Raw& r, const int tp) __attribute__((always_inline)) {
         const int tl = min(tp + ltok, t1 - 1);
         const size_t th = (size_t)tl * H + h;
+        const size_t tkv = (size_t)tl * HKV + hk;
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
             const int i = lch + p * kWave;
             const int ic = (i < DK) ? i : 0;   // lanes past dk read channel 0 and are zeroed on use
             r.q[p] = q[th * DK + ic];
-            r.k[p] = k[th * DK + ic];
+            r.k[p] = k[tkv * DK + ic];
             if (!EJK) r.z[p] = g[th * DK + ic];
         }
         r.bt = beta[th + vz];
         if (EJK) r.z[0] = g ? g[th + vz] : 0.f;   // EJK: the token's scalar log-decay
 #pragma unroll
         for (int tk = 0; tk < TPP; ++tk)
-            r.vc[tk] = to_f32(v[((size_t)min(tp + tk, t1 - 1) * H + h) * DV + cc]);
+            r.vc[tk] = to_f32(v[((size_t)min(tp + tk, t1 - 1) * HKV + hk) * DV + cc]);
     };
     Raw ring[NSLOT];
     if (t0 < t1) {
@@ -329,11 +331,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     Tout* o = static_cast<Tout*>(a.o);
     if (a.ejk)
         hipLaunchKernelGGL((recurrent_kernel<DK, LPC, Tin, Tout, true>), grid, block, 0, stream, q, k, v,
-                           a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.dv, a.scale,
+                           a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
                            a.lower_bound, (int)a.l2norm, o, a.final_state);
     else
         hipLaunchKernelGGL((recurrent_kernel<DK, LPC, Tin, Tout, false>), grid, block, 0, stream, q, k, v,
-                           a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.dv, a.scale,
+                           a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
                            a.lower_bound, (int)a.l2norm, o, a.final_state);
     return hipGetLastError();
 }

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -66,13 +66,17 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * initial_state, softmax_scale, chunk_size, use_qk_l2norm, use_chunked,
  * return_state; varlen packing as in ejkernel "recurrent" run(): cu_seqlens).
  *
- * Shapes (dense batch): q, k [B, T, H, dk]; v [B, T, H, dv]; o [B, T, H, dv];
- * states [B, H, dk, dv].  With cu_seqlens ([num_seqs + 1] int32, device,
+ * Shapes (dense batch): q [B, T, H, dk]; k [B, T, Hkv, dk]; v [B, T, Hkv, dv];
+ * o [B, T, H, dv]; states [B, H, dk, dv].  Grouped heads (ejkernel
+ * "recurrent" run(): key and value carry num_kv_heads, query, gates, state
+ * and output num_heads): head h reads the key and value of head
+ * h / (H / Hkv); Hkv must divide H, and Hkv = 0 means Hkv = H.  With cu_seqlens ([num_seqs + 1] int32, device,
  * cu[0] = 0, non-decreasing, cu[num_seqs] = T) the batch must be B = 1 and
  * sequence n covers tokens [cu[n], cu[n+1]); states are [num_seqs, H, dk, dv]
  * and every sequence restarts from its own initial state.
  *
  *   q, k, v        in_dtype (KDA_BF16 or KDA_F32)
+ *   Hkv            key/value heads (0 = H)
  *   g              KDA: raw gate [B, T, H, dk] float32 (required);
  *                  EJK: log-decay [B, T, H] float32, NULL = 0 (no decay)
  *   beta           KDA: logits [B, T, H]; EJK: activated [B, T, H]; float32
@@ -106,7 +110,7 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
                          const float* g, const float* beta, const float* a_log,
                          const float* dt_bias, const float* initial_state,
                          const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
-                         int32_t H, int32_t dk, int32_t dv, float scale, float lower_bound,
+                         int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale, float lower_bound,
                          int32_t chunk_size, uint32_t flags, void* o, kda_dtype_t out_dtype,
                          float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream);
@@ -126,8 +130,9 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
  * B requests (AWS Neuron "KDA TKG Kernel API Reference", kda_tkg: same
  * tensors, layouts and in-place state; scale and lower_bound are host floats
  * here instead of [1, 1] device tensors).  All float32:
- *   q, k, g   [B, dk, H] raw (EJK: g is the log-decay [B, 1, H], NULL = 0)
- *   v         [B, H, dv]
+ *   q, g      [B, dk, H] raw (EJK: g is the log-decay [B, 1, H], NULL = 0)
+ *   k         [B, dk, Hkv] raw;  v [B, Hkv, dv]: Hkv key/value heads, head h
+ *             reads those of head h / (H / Hkv) (Hkv divides H; 0 = H)
  *   beta      [B, 1, H] logits (EJK: activated)
  *   a_log     [1, H] (ignored for EJK);  dt_bias [dk, H] (NULL = 0)
  *   out       [B, H, dv], caller-allocated, written
@@ -137,8 +142,8 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
  */
 kda_status_t kda_decode_step(const float* q, const float* k, const float* g, const float* v,
                              const float* beta, const float* a_log, const float* dt_bias,
-                             float scale, float lower_bound, int32_t B, int32_t H, int32_t dk,
-                             int32_t dv, uint32_t flags, float* out, float* S, void* stream);
+                             float scale, float lower_bound, int32_t B, int32_t H, int32_t Hkv,
+                             int32_t dk, int32_t dv, uint32_t flags, float* out, float* S, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* kda_last_error(void);

@@ -46,24 +46,24 @@ def test_constants_match_header():
 
 def _prefill(**over):
     a = dict(q=P, k=P, v=P, in_dtype=kda.BF16, g=P, beta=P, a_log=P, dt_bias=P, init=None,
-             cu=None, num_seqs=0, B=2, T=128, H=4, dk=128, dv=128, scale=-1.0,
+             cu=None, num_seqs=0, B=2, T=128, H=4, Hkv=0, dk=128, dv=128, scale=-1.0,
              lower_bound=-5.0, chunk_size=64, flags=kda.QK_L2NORM | kda.CHUNKED, o=P,
              out_dtype=kda.BF16, final=None, ws=None, ws_bytes=0, stream=None)
     a.update(over)
     return kda.lib().kda_prefill(a["q"], a["k"], a["v"], a["in_dtype"], a["g"], a["beta"],
                                  a["a_log"], a["dt_bias"], a["init"], a["cu"], a["num_seqs"],
-                                 a["B"], a["T"], a["H"], a["dk"], a["dv"], a["scale"],
+                                 a["B"], a["T"], a["H"], a["Hkv"], a["dk"], a["dv"], a["scale"],
                                  a["lower_bound"], a["chunk_size"], a["flags"], a["o"],
                                  a["out_dtype"], a["final"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def _decode(**over):
     a = dict(q=P, k=P, g=P, v=P, beta=P, a_log=P, dt_bias=P, scale=-1.0, lower_bound=-5.0,
-             B=4, H=2, dk=128, dv=128, flags=kda.QK_L2NORM, out=P, S=P, stream=None)
+             B=4, H=2, Hkv=0, dk=128, dv=128, flags=kda.QK_L2NORM, out=P, S=P, stream=None)
     a.update(over)
     return kda.lib().kda_decode_step(a["q"], a["k"], a["g"], a["v"], a["beta"], a["a_log"],
                                      a["dt_bias"], a["scale"], a["lower_bound"], a["B"], a["H"],
-                                     a["dk"], a["dv"], a["flags"], a["out"], a["S"], a["stream"])
+                                     a["Hkv"], a["dk"], a["dv"], a["flags"], a["out"], a["S"], a["stream"])
 
 
 PREFILL_ERRORS = [
@@ -91,6 +91,9 @@ PREFILL_ERRORS = [
     (dict(v=P + 2), kda.KDA_EINVAL, "16-byte aligned"),
     (dict(o=P + 4), kda.KDA_EINVAL, "16-byte aligned"),
     (dict(g=P + 4), kda.KDA_EINVAL, "16-byte aligned"),
+    (dict(Hkv=3), kda.KDA_EINVAL, "must divide H"),
+    (dict(Hkv=-1), kda.KDA_EINVAL, "must divide H"),
+    (dict(Hkv=8), kda.KDA_EINVAL, "must divide H"),
 ]
 
 
@@ -123,6 +126,8 @@ DECODE_ERRORS = [
     (dict(lower_bound=1.0), kda.KDA_EINVAL, "lower_bound"),
     (dict(dk=200), kda.KDA_EUNSUPPORTED, "dk and dv"),
     (dict(dv=8), kda.KDA_EUNSUPPORTED, "dk and dv"),
+    (dict(Hkv=3), kda.KDA_EINVAL, "must divide H"),
+    (dict(Hkv=-2), kda.KDA_EINVAL, "must divide H"),
 ]
 
 

@@ -49,6 +49,16 @@ def test_prefill_bytes_initial_state_and_ejk():
     assert base - ejk == ntok * H * (dk - 1) * 4 + H * 4 + dk * H * 4
 
 
+def test_grouped_bytes():
+    # grouped key/value heads: k and v are read once per key/value head
+    B, H, hkv, dk, dv, f32 = 64, 32, 8, 128, 128, 4
+    assert bench.decode_bytes(B, H, dk, dv) - bench.decode_bytes(B, H, dk, dv, hkv) == \
+        (B * dk + B * dv) * (H - hkv) * f32
+    ntok, bf16 = 4 * 4096, 2
+    assert bench.prefill_bytes(ntok, 16, dk, dv, 4, False) - \
+        bench.prefill_bytes(ntok, 16, dk, dv, 4, False, hkv=4) == ntok * (16 - 4) * (dk + dv) * bf16
+
+
 def test_prefill_flops_per_token_head():
     # per chunk of C tokens (lower-triangular products count half): A = K K^T,
     # P = Q K^T and W = T' Kg each C^2 dk; U~ = T' V and P U each C^2 dv; the
