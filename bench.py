@@ -79,10 +79,10 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def _counter_traffic(name, src_hash):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary
-    (profiles/<name>_pmc.txt, "key: value" lines), if it was taken on the
-    current kernel source; else None."""
+def _profile_kv(name, src_hash):
+    """The "key: value" lines of a committed rocprofv3 --pmc summary
+    (profiles/<name>_pmc.txt) if it was taken on the current kernel source;
+    else None."""
     p = os.path.join(ROOT, "profiles", f"{name}_pmc.txt")
     if not os.path.exists(p):
         return None
@@ -91,12 +91,37 @@ def _counter_traffic(name, src_hash):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("src_hash") != src_hash:
-        return None
+    return kv if kv.get("src_hash") == src_hash else None
+
+
+def _counter_traffic(name, src_hash):
+    """HBM bytes per launch from a committed counter summary taken on the
+    current kernel source; else None."""
+    kv = _profile_kv(name, src_hash)
     try:
-        return int(float(kv["hbm_bytes_per_launch"]))
+        return int(float(kv["hbm_bytes_per_launch"])) if kv else None
     except (KeyError, ValueError):
         return None
+
+
+def prefill_counters(ms):
+    """Counter figures of the B4 T4096 H16 prefill call from its committed
+    summary (HBM traffic, executed bf16 MFMA flops, MFMA busy fraction), with
+    the executed flops turned into a fraction of peak over this run's time;
+    all None once the kernel source has changed since they were taken."""
+    sh = _src_hash("kda_chunked.hip", "kda_device.h")
+    kv = _profile_kv("chunked_prefill_b4_t4096_h16_d128", sh)
+    res = {"traffic": None, "mfma_flops": None, "mfma_frac": None, "mfma_busy_frac": None,
+           "src_hash": sh, "source": "profiles/chunked_prefill_b4_t4096_h16_d128_pmc.txt"}
+    if kv:
+        try:
+            fl = int(float(kv["mfma_bf16_flops_per_call"]))
+            res.update(traffic=int(float(kv["hbm_bytes_per_call"])), mfma_flops=fl,
+                       mfma_frac=round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS, 4),
+                       mfma_busy_frac=float(kv["mfma_busy_frac"]))
+        except (KeyError, ValueError):
+            pass
+    return res
 
 
 def bench_decode(steps, warmup, nbuf=5):
@@ -311,6 +336,7 @@ def bench_prefill(steps, warmup):
     inp = workloads.prefill_b4_t4096_h16_d128()
     res = _prefill_run(inp, steps, warmup, nsets=2)   # 2 x 408 MB: more than the Infinity Cache
     res.pop("path")
+    res["rocprof"] = prefill_counters(res["ms_per_call"])
     return dict({"workload": "kda_chunked_prefill_b4_t4096_h16_d128_bf16"}, **res)
 
 

@@ -84,3 +84,20 @@ def test_counter_traffic_only_for_matching_source():
     # within 1% of the algorithmic bytes: the state stream is read and written once
     assert abs(good - 273_703_040) / 273_703_040 < 0.01
     assert bench._counter_traffic("decode_b64_h32_d128", "0" * 16) is None
+
+
+def test_prefill_counters_only_for_matching_source(monkeypatch):
+    res = bench.prefill_counters(0.2574)
+    if res["mfma_flops"] is None:
+        pytest.skip("committed prefill counter summary predates the current chunked source")
+    # executed bf16 MFMA work lies between the triangle-aware algorithmic count
+    # and the count with every masked tile executed
+    tri = bench.prefill_flops(4 * 4096, 16, 128, 128)
+    dense = 4 * 4096 * 16 * (64 * (6 * 128 + 4 * 128) + 6 * 128 * 128)
+    assert tri <= res["mfma_flops"] <= dense
+    assert res["mfma_frac"] == round(res["mfma_flops"] / 0.2574e-3 / 1e12 / 2500.0, 4)
+    # the record round trip: more HBM traffic than the algorithmic bytes, within 3x
+    assert 407_904_320 < res["traffic"] < 3 * 407_904_320
+    monkeypatch.setattr(bench, "_src_hash", lambda *names: "0" * 16)
+    stale = bench.prefill_counters(0.2574)
+    assert stale["traffic"] is None and stale["mfma_frac"] is None
