@@ -80,3 +80,45 @@ def test_decode_empty_batch():
     out = kda.decode_step(z(0, 16, 2), z(0, 16, 2), z(0, 2, 16), z(0, 16, 2), z(0, 1, 2),
                           z(1, 2), z(16, 2), z(0, 2, 16, 16))
     assert out.shape == (0, 2, 16)
+
+
+def test_decode_state_beyond_2e31_elements():
+    """A batch whose state holds more than 2^31 elements (B=4100, H=32, dk=dv=128:
+    8.6 GB of fp32 state): items past element 2^31 are advanced like the first.
+    The state is drawn on the device from a seeded generator; the sampled items'
+    incoming states are copied back before the call and given to the oracle."""
+    import torch
+    import gated_delta_rule_90_amd as kda
+    from oracle import kda_oracle
+    from tests._common import dev
+    B, H, dk, dv = 4100, 32, 128, 128
+    assert B * H * dk * dv > 2 ** 31
+    rng = np.random.default_rng(4100)
+    q = rng.standard_normal((B, dk, H), dtype=np.float32)
+    k = rng.standard_normal((B, dk, H), dtype=np.float32)
+    g = rng.standard_normal((B, dk, H), dtype=np.float32)
+    v = rng.standard_normal((B, H, dv), dtype=np.float32)
+    beta = rng.standard_normal((B, 1, H), dtype=np.float32)
+    a_log = rng.uniform(-1.0, 1.0, size=(1, H)).astype(np.float32)
+    dt_bias = (0.1 * rng.standard_normal((dk, H))).astype(np.float32)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4100)
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda").normal_(0.0, 0.02, generator=gen)
+    # item b * H + h starts at element (b * H + h) * dk * dv: (4096, 0) starts exactly at 2^31
+    items = [(0, 0), (2049, 7), (4095, 31), (4096, 0), (4099, 17), (B - 1, H - 1)]
+    before = {it: S[it[0], it[1]].cpu().numpy() for it in items}
+    say("decode B=4100 H=32 dk=dv=128 (state > 2^31 elements)")
+    f = torch.float32
+    out = kda.decode_step(dev(q, f), dev(k, f), dev(v, f), dev(g, f), dev(beta, f), dev(a_log, f),
+                          dev(dt_bias, f), S, scale=1.0 / np.sqrt(dk), lower_bound=-5.0)
+    torch.cuda.synchronize()
+    for b, h in items:
+        ro, rS = kda_oracle.decode(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1], g[b:b + 1, :, h:h + 1],
+                                   v[b:b + 1, h:h + 1], beta[b:b + 1, :, h:h + 1], a_log[:, h:h + 1],
+                                   dt_bias[:, h:h + 1], before[(b, h)][None, None],
+                                   scale=1.0 / np.sqrt(dk), lower_bound=-5.0)
+        eo = rel_l2(out[b, h].cpu().numpy(), ro[0, 0])
+        es = rel_l2(S[b, h].cpu().numpy(), rS[0, 0])
+        assert eo <= TOL and es <= TOL, (b, h, eo, es)
+    del S
+    torch.cuda.empty_cache()
