@@ -11,7 +11,9 @@ The same JSON line also carries:
   roofline      the decode kernel against MI355X's 8 TB/s HBM (algorithmic
                 bytes per launch / mean launch time from HIP events)
   cpu_baseline  the float64 CPU oracle timed on the host on a bounded sample
-                (decode here; the prefill entry carries its own)
+                (decode here; the prefill entry carries its own), with the
+                parity (relative L2) of the GPU results of the benchmarked
+                configuration on that sample
   prefill       chunked prefill tokens/s for B=4, T=4096, H=16, dk=dv=128
                 (bf16 inputs) with its own roofline fractions (--no-prefill
                 skips it)
@@ -162,9 +164,17 @@ def _decode_run(inp, steps, warmup, nbuf=5):
     ms = e0.elapsed_time(e1) / steps
     nbytes = decode_bytes(B, H, dk, dv, hkv)
     achieved = nbytes / (ms * 1e-3) / 1e9
+    # one more step from the initial state, outside the timed region: its output
+    # and new state are compared with the oracle by the CPU leg
+    S1 = S0.clone()
+    out1 = kda.decode_step(q, k, v, g, beta, a_log, dtb, S1, scale=inp.scale, lower_bound=inp.lower_bound)
+    torch.cuda.synchronize()
+    check = (out1.cpu().numpy(), S1.cpu().numpy())
+    del S1, states
     sh = _src_hash("kda_decode.hip", "kda_device.h")
     traffic = _counter_traffic("decode_b64_h32_d128", sh)
     return inp, {
+        "check": check,
         "ms": ms, "wall_s": wall, "steps_per_s": 1e3 / ms, "bytes": nbytes,
         "flops": decode_flops(B, H, dk, dv),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -174,29 +184,49 @@ def _decode_run(inp, steps, warmup, nbuf=5):
     }
 
 
-def cpu_decode_baseline(inp, budget_s=10.0):
+def rel_l2(x, ref):
+    x = np.asarray(x, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
+
+
+def cpu_decode_baseline(inp, budget_s=10.0, check=None):
+    """The float64 oracle on full decode steps, repeated for about budget_s.
+    With check = (out, S_new) of the GPU's step from the same state, the first
+    oracle step also gives the parity of the benchmarked configuration."""
     from oracle import kda_oracle
     kda_oracle.build(force=False)
     threads = kda_oracle.max_threads()
     t0 = time.perf_counter()
-    kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
-                      scale=inp.scale, lower_bound=inp.lower_bound)
+    ro, rS = kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
+                               scale=inp.scale, lower_bound=inp.lower_bound)
     one = time.perf_counter() - t0
+    parity = None
+    if check is not None:
+        parity = {"rel_l2_out": rel_l2(check[0], ro), "rel_l2_state": rel_l2(check[1], rS), "bar": 1e-5,
+                  "sample": "one step of all 64 x 32 (request, head) items"}
+        parity["ok"] = parity["rel_l2_out"] <= 1e-5 and parity["rel_l2_state"] <= 1e-5
     reps = max(1, int(budget_s / max(one, 1e-3)))
     t0 = time.perf_counter()
     for _ in range(reps):
         kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
                           scale=inp.scale, lower_bound=inp.lower_bound)
     el = time.perf_counter() - t0
-    return {"value": round(reps / el, 3), "unit": "decode steps/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{reps} full decode steps (B=64, H=32, dk=dv=128, float64) in {el:.1f} s"}
+    res = {"value": round(reps / el, 3), "unit": "decode steps/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{reps} full decode steps (B=64, H=32, dk=dv=128, float64) in {el:.1f} s"}
+    if parity is not None:
+        res["parity"] = parity
+    return res
 
 
-def cpu_prefill_baseline(budget_s=5.0):
+def cpu_prefill_baseline(budget_s=5.0, check=None):
     """The float64 oracle on a bounded sample of the B4 T4096 H16 workload: all
     four sequences of the first few heads (enough (sequence, head) units for every
-    core), repeated for about budget_s; reported as tokens/s over all 16 heads."""
+    core), repeated for about budget_s; reported as tokens/s over all 16 heads.
+    With check = (o, final_state) of the timed GPU call, the first oracle run
+    also gives the parity of those heads."""
     from gated_delta_rule_90_amd import workloads
     from oracle import kda_oracle
     kda_oracle.build(force=False)
@@ -208,20 +238,29 @@ def cpu_prefill_baseline(budget_s=5.0):
     args = (inp.q[:, :, hs], inp.k[:, :, hs], inp.v[:, :, hs], inp.g[:, :, hs], inp.beta[:, :, hs],
             inp.a_log[hs], inp.dt_bias[:, hs])
     t0 = time.perf_counter()
-    kda_oracle.prefill(*args, scale=inp.scale, lower_bound=inp.lower_bound)
+    ro, rs = kda_oracle.prefill(*args, scale=inp.scale, lower_bound=inp.lower_bound)
     one = time.perf_counter() - t0
+    parity = None
+    if check is not None:
+        o_gpu, s_gpu = check
+        parity = {"rel_l2_o": rel_l2(o_gpu[:, :, hs], ro), "rel_l2_state": rel_l2(s_gpu[:, hs], rs),
+                  "bar": 2e-2, "sample": f"heads 0..{nh - 1} of all 4 sequences of the timed call"}
+        parity["ok"] = parity["rel_l2_o"] <= 2e-2 and parity["rel_l2_state"] <= 2e-2
     reps = max(1, int(budget_s / max(one, 1e-3)))
     t0 = time.perf_counter()
     for _ in range(reps):
         kda_oracle.prefill(*args, scale=inp.scale, lower_bound=inp.lower_bound)
     el = time.perf_counter() - t0
     token_heads = reps * B * T * nh
-    return {"value": round(token_heads / H / el, 1), "unit": "prefill tokens/s (all 16 heads)",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x (4 sequences x 4096 tokens x {nh} heads), float64, in {el:.1f} s"}
+    res = {"value": round(token_heads / H / el, 1), "unit": "prefill tokens/s (all 16 heads)",
+           "cores": threads, "kind": "oracle",
+           "sample": f"{reps} x (4 sequences x 4096 tokens x {nh} heads), float64, in {el:.1f} s"}
+    if parity is not None:
+        res["parity"] = parity
+    return res
 
 
-def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False):
+def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=False):
     """Time kda.prefill on one workload (inputs resident in HBM, nsets input
     copies used in turn so the Infinity Cache cannot hold them)."""
     import torch
@@ -327,6 +366,9 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False):
         res["split_at"] = split
         res["split_bitwise_equal"] = bool(torch.equal(torch.cat([o1, o2], 1), o_ref) and
                                           torch.equal(fin, fs_ref))
+    if keep:
+        # every input set holds the same values, so o and fs are the outputs of one call
+        res["check"] = (o.float().cpu().numpy(), fs.cpu().numpy())
     del sets
     return res
 
@@ -334,7 +376,7 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False):
 def bench_prefill(steps, warmup):
     from gated_delta_rule_90_amd import workloads
     inp = workloads.prefill_b4_t4096_h16_d128()
-    res = _prefill_run(inp, steps, warmup, nsets=2)   # 2 x 408 MB: more than the Infinity Cache
+    res = _prefill_run(inp, steps, warmup, nsets=2, keep=True)   # 2 x 408 MB: more than the Infinity Cache
     res.pop("path")
     res["rocprof"] = prefill_counters(res["ms_per_call"])
     return dict({"workload": "kda_chunked_prefill_b4_t4096_h16_d128_bf16"}, **res)
@@ -421,14 +463,17 @@ def main():
         "request_tokens_per_s": round(64 * dec["steps_per_s"], 1),
         "roofline": dec["roofline"],
     }
+    pcheck = None
     if not args.no_prefill:
         line["prefill"] = bench_prefill(max(5, args.steps // 10), max(2, args.warmup // 10))
+        pcheck = line["prefill"].pop("check")
     if not args.no_configs:
         line["configs"] = bench_configs(max(3, args.steps // 40), max(1, args.warmup // 10))
+    dcheck = dec.pop("check")
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_decode_baseline(inp, args.cpu_budget)
+        line["cpu_baseline"] = cpu_decode_baseline(inp, args.cpu_budget, check=dcheck)
         if "prefill" in line:
-            line["prefill"]["cpu_baseline"] = cpu_prefill_baseline(args.cpu_budget / 2)
+            line["prefill"]["cpu_baseline"] = cpu_prefill_baseline(args.cpu_budget / 2, check=pcheck)
     print(json.dumps(line), flush=True)
 
 

@@ -7,6 +7,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -101,3 +102,18 @@ def test_prefill_counters_only_for_matching_source(monkeypatch):
     monkeypatch.setattr(bench, "_src_hash", lambda *names: "0" * 16)
     stale = bench.prefill_counters(0.2574)
     assert stale["traffic"] is None and stale["mfma_frac"] is None
+
+
+def test_cpu_decode_leg_reports_parity_of_the_given_step():
+    from gated_delta_rule_90_amd import workloads
+    from oracle import kda_oracle
+    inp = workloads.decode_inputs(2, 3, 16, 16, seed=5)
+    ro, rS = kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
+                               scale=inp.scale, lower_bound=inp.lower_bound)
+    good = bench.cpu_decode_baseline(inp, budget_s=0.05, check=(ro.astype(np.float32), rS.astype(np.float32)))
+    assert good["parity"]["ok"] and good["parity"]["rel_l2_out"] < 1e-6
+    bad_out = ro.copy()
+    bad_out[0, 0, 0] += 0.01 * np.linalg.norm(ro)      # a 1% error in one element
+    bad = bench.cpu_decode_baseline(inp, budget_s=0.05, check=(bad_out, rS))
+    assert not bad["parity"]["ok"] and abs(bad["parity"]["rel_l2_out"] - 0.01) < 1e-3
+    assert "parity" not in bench.cpu_decode_baseline(inp, budget_s=0.05)
