@@ -260,7 +260,7 @@ def cpu_prefill_baseline(budget_s=5.0, check=None):
     return res
 
 
-def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=False):
+def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=False, use_chunked=None):
     """Time kda.prefill on one workload (inputs resident in HBM, nsets input
     copies used in turn so the Infinity Cache cannot hold them)."""
     import torch
@@ -287,7 +287,10 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=Fals
                            cu, scale=inp.scale, lower_bound=inp.lower_bound, ejk=inp.ejk,
                            use_chunked=use_chunked, out=out, final_state=fin)
 
-    chunked = inp.dtype == "bf16"
+    # bf16 inputs: the MFMA chunked kernel; float32 inputs: the token-by-token
+    # kernel unless use_chunked asks for the float32 chunked one
+    chunked = (inp.dtype == "bf16") if use_chunked is None else use_chunked
+    mfma = chunked and inp.dtype == "bf16"
     for i in range(warmup):
         call(i, use_chunked=chunked)
     torch.cuda.synchronize()
@@ -303,8 +306,8 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=Fals
     nbytes = prefill_bytes(ntok, H, dk, dv, nst, s0 is not None, inp.ejk, io_bytes, inp.k.shape[2])
     res = {"tokens_per_s": round(ntok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
            "alg_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "path": "chunked MFMA" if chunked else "token-by-token"}
-    if chunked:
+           "path": "chunked MFMA" if mfma else ("chunked float32" if chunked else "token-by-token")}
+    if mfma:
         fl = prefill_flops(ntok, H, dk, dv)
         tfs = fl / (ms * 1e-3) / 1e12
         floor_ms = max(nbytes / (HBM_PEAK_GBS * 1e9), fl / (BF16_MFMA_PEAK_TFS * 1e12)) * 1e3
@@ -393,6 +396,15 @@ def bench_configs(steps, warmup):
                                                note="64 dependent token steps per call: latency bound; "
                                                     "ms_per_call includes the host's per-call overhead, "
                                                     "graph_ms_per_call is the device time")
+    # the same workload through the float32 chunked kernel (4 chunks of 16 tokens)
+    out["chunked_fp32_b1_t64_h2_d16"] = dict(_prefill_run(inp, 10 * steps, warmup, graph=True, use_chunked=True),
+                                             note="4 dependent 16-token chunks per call; graph_ms_per_call "
+                                                  "is the device time")
+    # a larger float32 prefill on both float32 kernels
+    inp = workloads.prefill_fp32_b1_t4096_h16_d128()
+    out["prefill_fp32_b1_t4096_h16_d128_token_by_token"] = _prefill_run(inp, steps, warmup)
+    out["prefill_fp32_b1_t4096_h16_d128_chunked"] = _prefill_run(inp, steps, warmup, use_chunked=True)
+    del inp
     for name, make, kw in (
             ("prefill_long_t65536_h32_d128", workloads.prefill_long_t65536_h32_d128, {"split": 32768}),
             ("prefill_varlen_8seq_h32_d128", workloads.prefill_varlen_8seq_h32_d128, {}),

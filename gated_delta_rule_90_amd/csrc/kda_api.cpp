@@ -143,6 +143,13 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
             return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
         return hip_status(kda::launch_chunked(a, st), "kda_prefill (chunked)");
     }
+    if (has_tokens && chunked && kda::chunked_f32_supported(a)) {
+        // float32 inputs: the chunked kernel loads q, k and (KDA) g 16 bytes per
+        // lane; unaligned inputs take the token-by-token kernel instead
+        auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+        if (a16(q) && a16(k) && (ejk || a16(g)))
+            return hip_status(kda::launch_chunked_f32(a, st), "kda_prefill (chunked float32)");
+    }
     // token-by-token path; with T == 0 it only carries initial_state to final_state
     return hip_status(kda::launch_recurrent(a, st), "kda_prefill (recurrent)");
 }

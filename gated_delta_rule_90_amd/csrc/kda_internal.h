@@ -71,5 +71,8 @@ inline hipError_t launch_recurrent(const PrefillArgs& a, hipStream_t stream)
 hipError_t launch_chunked(const PrefillArgs& a, hipStream_t stream);
 bool chunked_supported(const PrefillArgs& a);
 size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed);
+// the float32 chunked kernel (16-token chunks on the vector ALUs)
+hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
+bool chunked_f32_supported(const PrefillArgs& a);
 
 }  // namespace kda

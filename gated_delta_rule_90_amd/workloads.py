@@ -155,6 +155,12 @@ def recurrent_fp32_small():
     return prefill_inputs(1, 64, 2, 16, 16, seed=1001, dtype="f32", zero_params=True, scale=0.25)
 
 
+def prefill_fp32_b1_t4096_h16_d128():
+    """One 4096-token sequence, H=16, dk=dv=128, float32 inputs (the float32
+    kernels at a prefill size), otherwise as the bf16 chunked workload."""
+    return prefill_inputs(1, 4096, 16, 128, 128, seed=1008, dtype="f32")
+
+
 def decode_b64_h32_d128():
     """kda_tkg-shaped decode: B=64 requests, H=32, dk=dv=128, fp32."""
     return decode_inputs(64, 32, 128, 128, seed=1002)

@@ -87,7 +87,9 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *   lower_bound    KDA gate bound, finite and <= 0; when the call takes the
  *                  MFMA chunked kernel it must be >= -5 (the kda_tkg documented
  *                  range [-5, 0]), else KDA_EUNSUPPORTED
- *   chunk_size     64 (the ejkernel default) when KDA_CHUNKED is set
+ *   chunk_size     64 (the ejkernel default) when KDA_CHUNKED is set; the
+ *                  float32 chunked kernel computes the same result in chunks
+ *                  of 16 (see Routing)
  *   o              out_dtype; KDA_BF16 output needs bf16 input
  *   final_state    [N, H, dk, dv] float32 or NULL (return_state = False);
  *                  may alias initial_state exactly (in-place carry)
@@ -97,14 +99,21 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * Dimensions: dk, dv in {16, 32, 64, 128} (kda_tkg: dk <= 128); H and the
  * number of sequences at most 65535.  B = 0 or
  * T = 0 is a no-op, except that final_state then receives initial_state (or
- * zeros).  Routing: KDA_CHUNKED with bf16 inputs and dk = 128 (any of the
- * dv above) runs the MFMA chunked kernel (KDA and EJK modes), which needs
- * q, k, v, o and (KDA) g 16-byte aligned (KDA_EINVAL otherwise); every
- * other combination runs the float32 token-by-token kernel, which computes
- * the same function step by step.  EJK decays are expected to be <= 0 (the ejkernel page
- * says so); the chunked kernel scales by e^{sum of decays} within a chunk,
- * so a positive decay large enough to overflow float32 there gives inf/NaN
- * where the token-by-token kernel would only overflow later.
+ * zeros).  Routing:
+ *   - KDA_CHUNKED with bf16 inputs and dk = 128 (any of the dv above) runs
+ *     the MFMA chunked kernel (64-token chunks; KDA and EJK modes), which
+ *     needs q, k, v, o and (KDA) g 16-byte aligned (KDA_EINVAL otherwise);
+ *   - KDA_CHUNKED with float32 inputs and output runs the float32 chunked
+ *     kernel (vector ALUs, 16-token chunks: the chunking changes rounding
+ *     only) when q, k and (KDA) g are 16-byte aligned and, in KDA mode,
+ *     lower_bound >= -5 (its decay factors over 16 tokens then stay inside
+ *     float32's normal range);
+ *   - every other combination runs the float32 token-by-token kernel, which
+ *     computes the same function step by step.
+ * EJK decays are expected to be <= 0 (the ejkernel page says so); the chunked
+ * kernels scale by e^{sum of decays} within a chunk, so a positive decay
+ * large enough to overflow float32 there gives inf/NaN where the
+ * token-by-token kernel would only overflow later.
  */
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
                          const float* g, const float* beta, const float* a_log,

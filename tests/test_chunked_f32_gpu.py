@@ -1,0 +1,167 @@
+"""The float32 chunked kernel (KDA_CHUNKED with float32 inputs: 16-token chunks
+on the vector ALUs) against the oracle, and its routing.
+
+Bar: relative L2 <= 1e-5 for o and the final state (float32 path, as for the
+token-by-token kernel); packed sequences and chunk-aligned splits bit for bit."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_90_amd import workloads
+from tests._common import prefill_gpu, prefill_oracle, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _check(inp, **kw):
+    o, s = prefill_gpu(inp, **kw)
+    ro, rs = prefill_oracle(inp)
+    eo, es = rel_l2(o, ro), rel_l2(s, rs)
+    assert eo <= TOL and es <= TOL, (eo, es)
+    return o, s
+
+
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 128])
+@pytest.mark.parametrize("ejk", [False, True])
+def test_chunked_f32_shapes(dk, dv, ejk):
+    inp = workloads.prefill_inputs(2, 37, 3, dk, dv, seed=300 + dk + dv, dtype="f32", ejk=ejk,
+                                   init_state=True)
+    say("chunked f32", dk, dv, "ejk" if ejk else "kda")
+    _check(inp)
+
+
+def test_chunked_f32_small_fp32_workload():
+    """B=1, T=64, H=2, dk=dv=16 (the small fp32 workload) through the chunked path."""
+    inp = workloads.recurrent_fp32_small()
+    say("chunked f32 B1 T64 H2 d16")
+    o, s = _check(inp)
+    orc, src = prefill_gpu(inp, use_chunked=False)
+    assert rel_l2(o, orc) <= TOL and rel_l2(s, src) <= TOL
+
+
+@pytest.mark.parametrize("ejk", [False, True])
+def test_chunked_f32_long_strong_decay(ejk):
+    """Many chunks, gates saturating at lower_bound = -5 (the factor range's edge)
+    and, in EJK mode, decays of -2|N(0,1)| per token."""
+    inp = workloads.prefill_inputs(1, 300, 2, 64, 32, seed=310, dtype="f32", ejk=ejk, init_state=True)
+    if ejk:
+        inp.g = (-2.0 * np.abs(np.random.default_rng(1).standard_normal(inp.g.shape))).astype(np.float32)
+    else:
+        inp.g = (inp.g + 8.0).astype(np.float32)   # sigmoid near 1: gamma near lower_bound
+    say("chunked f32 strong decay", "ejk" if ejk else "kda")
+    _check(inp)
+
+
+def test_chunked_f32_without_l2norm_custom_scale_and_grouped_heads():
+    inp = workloads.prefill_inputs(2, 45, 4, 32, 32, seed=320, dtype="f32", init_state=True, hkv=2,
+                                   scale=0.3)
+    say("chunked f32 grouped, custom scale")
+    _check(inp)
+    say("chunked f32 without l2 norm")
+    o, s = prefill_gpu(inp, use_qk_l2norm=False)
+    ro, rs = prefill_oracle(inp, use_qk_l2norm=False)
+    assert rel_l2(o, ro) <= TOL and rel_l2(s, rs) <= TOL
+
+
+@pytest.mark.parametrize("ejk", [False, True])
+def test_chunked_f32_varlen_bitwise_equal_to_separate_runs(ejk):
+    lens = [17, 0, 64, 1, 40, 3, 22, 16]
+    inp = workloads.prefill_inputs(1, 0, 3, 32, 32, seed=330, dtype="f32", lengths=lens, ejk=ejk,
+                                   init_state=True)
+    say("chunked f32 varlen", lens, "ejk" if ejk else "kda")
+    o, s = _check(inp)
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if a == b:
+            np.testing.assert_array_equal(s[n], inp.initial_state[n])
+            continue
+        sub = workloads.PrefillInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b],
+                                      None if inp.g is None else inp.g[:, a:b], inp.beta[:, a:b],
+                                      inp.a_log, inp.dt_bias, inp.initial_state[n:n + 1], None,
+                                      inp.dtype, inp.scale, inp.lower_bound, ejk=ejk)
+        on, sn = prefill_gpu(sub)
+        np.testing.assert_array_equal(o[:, a:b], on)
+        np.testing.assert_array_equal(s[n], sn[0])
+
+
+def test_chunked_f32_split_at_chunk_boundary_bitwise():
+    inp = workloads.prefill_inputs(2, 80, 2, 64, 32, seed=340, dtype="f32", init_state=True)
+    say("chunked f32 split")
+    o, s = prefill_gpu(inp)
+    cut = 48   # a multiple of the 16-token chunk
+    part = lambda x, a, b: x[:, a:b]
+    first = workloads.PrefillInputs(part(inp.q, 0, cut), part(inp.k, 0, cut), part(inp.v, 0, cut),
+                                    part(inp.g, 0, cut), part(inp.beta, 0, cut), inp.a_log, inp.dt_bias,
+                                    inp.initial_state, None, inp.dtype, inp.scale, inp.lower_bound)
+    o1, s1 = prefill_gpu(first)
+    second = workloads.PrefillInputs(part(inp.q, cut, 80), part(inp.k, cut, 80), part(inp.v, cut, 80),
+                                     part(inp.g, cut, 80), part(inp.beta, cut, 80), inp.a_log,
+                                     inp.dt_bias, s1, None, inp.dtype, inp.scale, inp.lower_bound)
+    o2, s2 = prefill_gpu(second)
+    np.testing.assert_array_equal(np.concatenate([o1, o2], axis=1), o)
+    np.testing.assert_array_equal(s2, s)
+
+
+def test_chunked_f32_extremes():
+    from tests.test_extremes_gpu import _extreme_prefill
+    inp = workloads.prefill_inputs(2, 40, 3, 32, 32, seed=350, dtype="f32", init_state=True)
+    inp = _extreme_prefill(inp, np.random.default_rng(3))
+    say("chunked f32 extremes")
+    o, s = _check(inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+
+
+def test_chunked_f32_in_place_alias_and_empty():
+    import torch
+    import gated_delta_rule_90_amd as kda
+    from tests._common import dev
+    inp = workloads.prefill_inputs(2, 33, 2, 16, 32, seed=360, dtype="f32", init_state=True)
+    f = torch.float32
+    st = dev(inp.initial_state, f)
+    say("chunked f32 in-place carry")
+    o = kda.prefill(dev(inp.q, f), dev(inp.k, f), dev(inp.v, f), dev(inp.g, f), dev(inp.beta, f),
+                    dev(inp.a_log, f), dev(inp.dt_bias, f), st, scale=inp.scale,
+                    lower_bound=inp.lower_bound, final_state=st)
+    torch.cuda.synchronize()
+    ro, rs = prefill_oracle(inp)
+    assert rel_l2(o.cpu().numpy(), ro) <= TOL and rel_l2(st.cpu().numpy(), rs) <= TOL
+    e = workloads.prefill_inputs(2, 0, 2, 16, 32, seed=361, dtype="f32", init_state=True)
+    _, se = prefill_gpu(e)
+    np.testing.assert_array_equal(se, e.initial_state)
+
+
+def test_chunked_f32_routing_falls_back_to_token_by_token():
+    """lower_bound < -5 (outside the factor range) and unaligned inputs take the
+    token-by-token kernel: bit for bit its result."""
+    import torch
+    import gated_delta_rule_90_amd as kda
+    inp = workloads.prefill_inputs(1, 30, 2, 32, 32, seed=370, dtype="f32", init_state=True,
+                                   lower_bound=-7.0)
+    say("chunked f32 routing: lower_bound -7")
+    o, s = prefill_gpu(inp)
+    orc, src = prefill_gpu(inp, use_chunked=False)
+    np.testing.assert_array_equal(o, orc)
+    np.testing.assert_array_equal(s, src)
+    ro, rs = prefill_oracle(inp)
+    assert rel_l2(o, ro) <= TOL
+
+    inp = workloads.prefill_inputs(1, 30, 2, 32, 32, seed=371, dtype="f32")
+    f = torch.float32
+
+    def unaligned(x):
+        flat = torch.empty(x.size + 1, dtype=f, device="cuda")
+        view = flat[1:].view(x.shape)          # 4 bytes past a 256-byte allocation boundary
+        view.copy_(torch.from_numpy(np.ascontiguousarray(x)).to("cuda"))
+        return view
+
+    args = [torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in
+            (inp.v, inp.g, inp.beta, inp.a_log, inp.dt_bias)]
+    say("chunked f32 routing: unaligned q")
+    o_u, s_u = kda.prefill(unaligned(inp.q), unaligned(inp.k), *args, scale=inp.scale,
+                           lower_bound=inp.lower_bound, return_state=True)
+    o_r, s_r = kda.prefill(unaligned(inp.q), unaligned(inp.k), *args, scale=inp.scale,
+                           lower_bound=inp.lower_bound, use_chunked=False, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_u, o_r) and torch.equal(s_u, s_r)
