@@ -3,13 +3,14 @@
 //
 // The chunk algebra is the bf16 MFMA kernel's (an exact regrouping of the
 // token recurrence: decay per key channel, residual against the decayed
-// state, o = S^T q), evaluated in float32 on the vector ALUs so that the
-// result meets the float32 bar.  For a chunk of C tokens with b_r the
+// state, o = S^T q), evaluated in float32 (float32 MFMA and vector ALU) so
+// that the result meets the float32 bar.  For a chunk of C tokens with b_r the
 // in-chunk cumulative log-decay (per channel, log2 units), beta_r the
 // activated beta and S0 the entering state:
 //     A_rs = beta_r sum_i kh_ri kh_si 2^{b_ri - b_si}   (s < r)
 //     P_rs = sum_i qh_ri kh_si 2^{b_ri - b_si}          (s <= r)
-//     T' = (I + A)^-1 diag(beta),  W = T' Kg,  U = T' V - W S0
+//     Y = V - Kg S0,  U = (I + A)^-1 diag(beta) Y   (= T' V - W S0 with T' =
+//     (I + A)^-1 diag(beta), W = T' Kg: U is solved for directly, no T' or W)
 //     O = Qg S0 + P U,  S = Diag(2^{b_C}) S0 + Kc^T U
 // with Kg_s = 2^{b_s} kh_s, Qg_r = 2^{b_r} qh_r, Kc_s = 2^{b_C - b_s} kh_s.
 //
@@ -27,13 +28,21 @@
 // 1 and is applied per (r, s) as a scalar.
 //
 // Work split: one 256-thread workgroup per (sequence, head, 16 state
-// columns).  The state tile [dk][16] stays in LDS in float32; the
-// column-independent quantities (prologue, A, P, T', W) are recomputed by
-// each column tile, which is cheap beside the state products at dk <= 128.
-// The next chunk's inputs are loaded into registers while the current chunk
-// computes.  Rows past a sequence's end are padded with exact neutral values
-// (q = k = v = 0, gamma = 0, beta = 0) and never stored, so a packed batch
-// equals each sequence run alone, bit for bit.
+// columns); the state tile [dk][16] stays in LDS in float32.  Per chunk:
+//   1. the raw rows go to LDS; row norms are summed from the load registers;
+//   2. lanes i < dk run the gate cumsum of channel i down the 16 rows;
+//   3. every thread scales its elements of q, k by the norms and decay factors;
+//   4. the four contractions over dk (A, P, Qg S0, Kg S0) run on 16x16x4
+//      float32 MFMA, one per wave and in parallel;
+//   5. 16 lanes solve (I + A) U = diag(beta) Y by forward substitution;
+//   6. O and the new state are MFMA products with K = 16.
+// The column-independent quantities (prologue, A, P) are recomputed by each
+// column tile, which is cheap beside the state products at dk <= 128.  The
+// inputs of the next chunks (four at dk <= 32, two above) are loaded into a
+// register ring while the current one computes: at small dk a chunk takes
+// less than a memory latency.  Rows past a sequence's end are padded with
+// exact neutral values (q = k = v = 0, gamma = 0, beta = 0) and never stored,
+// so a packed batch equals each sequence run alone, bit for bit.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -48,15 +57,15 @@ constexpr int F16 = FC + 1;
 template <int DK>
 struct F32Lds {
     static constexpr int RS = DK + 1;   // row stride of [16][DK] tiles: rows fall in different banks
-    float QL[FC * RS];    // qh_r 2^{b_r - b_0} (EJK: qh_r); later W
-    float KL[FC * RS];    // kh_r 2^{b_r - b_0} (EJK: kh_r)
+    float QL[FC * RS];    // raw q rows, then qh_r 2^{b_r - b_0} (EJK: qh_r)
+    float KL[FC * RS];    // raw k rows, then kh_r 2^{b_r - b_0} (EJK: kh_r)
     float KR[FC * RS];    // kh_r 2^{b_0 - b_r} (EJK: kh_r)
-    float GB[FC * RS];    // raw gates, then b_r (log2 units)
+    float GB[FC * RS];    // b_r per channel (log2 units, KDA)
     float SL[DK * F16];   // the state tile S[i][j]
     float VV[FC * F16];   // the value tile V[s][j]
     float AM[FC * F16];   // A (strict lower, beta-scaled)
     float PM[FC * F16];   // P (lower incl. diagonal)
-    float TP[FC * F16];   // T' = (I + A)^-1 diag(beta)
+    float YM[FC * F16];   // Y = V - Kg S0
     float UM[FC * F16];   // U
     float E0[DK];         // 2^{b_0}
     float NC[DK];         // 2^{b_C - b_0}
@@ -77,6 +86,28 @@ __device__ __forceinline__ void f32_seq_bounds(const int32_t* cu, int n, int T, 
     }
 }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D += A B on a 16x16x4 float32 MFMA: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[4 (l / 16) + e][l % 16] in element e.
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// x summed over each aligned group of N lanes (N = 4, 8, 16 or 32), in every
+// lane of the group.  The whole wave must be active.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x)
+{
+    x = xor_add<1>(x);
+    x = xor_add<2>(x);
+    if constexpr (N >= 8) x = xor_add<4>(x);
+    if constexpr (N >= 16) x = xor_add<8>(x);
+    if constexpr (N >= 32) x = xor_add<16>(x);
+    return x;
+}
+
 template <int DK, bool EJK>
 __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -86,15 +117,20 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     float* __restrict__ o, float* __restrict__ final_state)
 {
     constexpr int RS = F32Lds<DK>::RS;
-    constexpr int Q4 = FC * DK / 4;            // float4 pieces of a [16][DK] tile
+    constexpr int RL = DK / 4;                 // lanes per row in the q, k loads (4 channels each)
+    constexpr int Q4 = FC * RL;                // float4 pieces of a [16][DK] tile
     constexpr int QN = (Q4 + FT - 1) / FT;     // per thread
-    constexpr int EPT = FC * DK / FT;          // [16][DK] elements per thread (1..8)
-    static_assert(EPT >= 1 && EPT * FT == FC * DK, "dk in {16, 32, 64, 128}");
+    static_assert(RL >= 4 && RL <= 32 && FC * DK % FT == 0, "dk in {16, 32, 64, 128}");
     __shared__ F32Lds<DK> L;
 
     const int tid = threadIdx.x;
-    const int r16 = tid >> 4;   // row of a 16x16 tile
+    const int r16 = tid >> 4;   // row of a 16x16 tile (value loads)
     const int c16 = tid & 15;   // column of a 16x16 tile
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lm = lane & 15;   // MFMA: operand row / output column
+    const int lk = lane >> 4;   // MFMA: operand k / output row group
+    const int ro = 4 * lk;      // MFMA: first output row of this lane
     const int j0 = blockIdx.x * FJ;
     const int h = blockIdx.y;
     const int n = blockIdx.z;
@@ -112,95 +148,104 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const float lb2 = lower_bound * kLog2e;
     const float dtb = (!EJK && dt_bias && tid < DK) ? dt_bias[(size_t)tid * H + h] : 0.f;
 
-    // one chunk's inputs in registers: q, k, g as float4 pieces (row e / (DK/4),
-    // channels 4 (e % (DK/4)) ..), v at (row r16, column c16), beta and the EJK
-    // decay of row tid (tid < 16); rows past the sequence are zero
-    float4 rq[QN], rk[QN], rg[QN];
-    float rv = 0.f, rb = 0.f, rd = 0.f;
-    auto load = [&](int c) {
+    // One chunk's inputs in registers, rows past the sequence zero: q and k as
+    // float4 pieces (row e / RL, channels 4 (e % RL) ..); the KDA gates of
+    // channel tid (tid < DK) for the 16 rows, so that the in-chunk cumsum runs
+    // down a register column (each row's load is still one coalesced row);
+    // v at (row r16, column c16); beta and the EJK decay of row tid (tid < 16).
+    // Only the lanes that need a value load it (explicit branches keep these
+    // global loads: a load of "pointer or a local zero" becomes a flat load,
+    // which the LDS barriers also wait for); rows past the sequence read the
+    // chunk's first row and are zeroed by a select.
+    struct Raw {
+        float4 q[QN], k[QN], g[QN];
+        float v, b, d;
+    };
+    auto load = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
         const int len = min(FC, t1 - c0);
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int m = 0; m < QN; ++m) {
             const int e = tid + m * FT;
-            const int row = e / (DK / 4), c4 = e % (DK / 4);
-            const bool in = e < Q4 && row < len;
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-            rq[m] = in ? *reinterpret_cast<const float4*>(q + ((size_t)(c0 + row) * H + h) * DK + 4 * c4) : z;
-            rk[m] = in ? *reinterpret_cast<const float4*>(k + ((size_t)(c0 + row) * HKV + hk) * DK + 4 * c4) : z;
-            if constexpr (!EJK)
-                rg[m] = in ? *reinterpret_cast<const float4*>(g + ((size_t)(c0 + row) * H + h) * DK + 4 * c4) : z;
+            const int row = e / RL, c4 = e % RL;
+            R.q[m] = z;
+            R.k[m] = z;
+            R.g[m] = z;
+            if (e < Q4) {
+                const int rr = row < len ? row : 0;
+                const float4 xq = *reinterpret_cast<const float4*>(q + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
+                const float4 xk = *reinterpret_cast<const float4*>(k + ((size_t)(c0 + rr) * HKV + hk) * DK + 4 * c4);
+                R.q[m] = row < len ? xq : z;
+                R.k[m] = row < len ? xk : z;
+                if constexpr (!EJK) {
+                    const float4 xg = *reinterpret_cast<const float4*>(g + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
+                    R.g[m] = row < len ? xg : z;
+                }
+            }
         }
-        rv = (r16 < len) ? v[((size_t)(c0 + r16) * HKV + hk) * DV + j0 + c16] : 0.f;
+        {
+            const int rr = r16 < len ? r16 : 0;
+            const float x = v[((size_t)(c0 + rr) * HKV + hk) * DV + j0 + c16];
+            R.v = (r16 < len) ? x : 0.f;
+        }
+        R.b = 0.f;
+        R.d = 0.f;
         if (tid < FC) {
-            rb = (tid < len) ? beta[(size_t)(c0 + tid) * H + h] : 0.f;
-            if constexpr (EJK) rd = (tid < len && g) ? g[(size_t)(c0 + tid) * H + h] : 0.f;
+            const int rr = tid < len ? tid : 0;
+            const float xb = beta[(size_t)(c0 + rr) * H + h];
+            R.b = (tid < len) ? xb : 0.f;
+            if constexpr (EJK) {
+                if (g) {
+                    const float xd = g[(size_t)(c0 + rr) * H + h];
+                    R.d = (tid < len) ? xd : 0.f;
+                }
+            }
         }
     };
-    if (nch > 0) load(0);
+    // chunks loaded ahead: at small dk a chunk computes in less than a memory
+    // latency; at large dk two chunks cover it, and more would only queue requests
+    constexpr int FD = DK <= 32 ? 4 : 2;
+    Raw ring[FD];
+#pragma unroll
+    for (int u = 0; u < FD; ++u)
+        if (u < nch) load(ring[u], u);
 
-    for (int c = 0; c < nch; ++c) {
+    auto chunk = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
         const int len = min(FC, t1 - c0);
-        // ---- raw inputs to LDS, then fetch the next chunk's
+        // ---- prologue from the registers: raw rows to LDS, row norms (RL lanes
+        // per row), the gate cumsum of channel tid, beta; then fetch the next chunk
 #pragma unroll
         for (int m = 0; m < QN; ++m) {
             const int e = tid + m * FT;
+            const int row = e / RL, c4 = e % RL;
             if (e < Q4) {
-                const int row = e / (DK / 4), c4 = e % (DK / 4);
                 float* pq = L.QL + row * RS + 4 * c4;
                 float* pk = L.KL + row * RS + 4 * c4;
-                pq[0] = rq[m].x; pq[1] = rq[m].y; pq[2] = rq[m].z; pq[3] = rq[m].w;
-                pk[0] = rk[m].x; pk[1] = rk[m].y; pk[2] = rk[m].z; pk[3] = rk[m].w;
+                pq[0] = R.q[m].x; pq[1] = R.q[m].y; pq[2] = R.q[m].z; pq[3] = R.q[m].w;
+                pk[0] = R.k[m].x; pk[1] = R.k[m].y; pk[2] = R.k[m].z; pk[3] = R.k[m].w;
                 if constexpr (!EJK) {
                     float* pg = L.GB + row * RS + 4 * c4;
-                    pg[0] = rg[m].x; pg[1] = rg[m].y; pg[2] = rg[m].z; pg[3] = rg[m].w;
+                    pg[0] = R.g[m].x; pg[1] = R.g[m].y; pg[2] = R.g[m].z; pg[3] = R.g[m].w;
                 }
             }
+            float sq = R.q[m].x * R.q[m].x + R.q[m].y * R.q[m].y + R.q[m].z * R.q[m].z + R.q[m].w * R.q[m].w;
+            float sk = R.k[m].x * R.k[m].x + R.k[m].y * R.k[m].y + R.k[m].z * R.k[m].z + R.k[m].w * R.k[m].w;
+            sq = lane_group_sum<RL>(sq);
+            sk = lane_group_sum<RL>(sk);
+            if (e < Q4 && c4 == 0) {
+                L.NQ[row] = l2norm ? scale / sqrtf(sq + kNormEps) : scale;
+                L.NK[row] = l2norm ? 1.0f / sqrtf(sk + kNormEps) : 1.0f;
+            }
         }
-        L.VV[r16 * F16 + c16] = rv;
+        L.VV[r16 * F16 + c16] = R.v;
         if (tid < FC) {
-            L.BT[tid] = (tid < len) ? (EJK ? rb : sigmoid_f(rb)) : 0.f;
-            if constexpr (EJK) L.BR[tid] = rd * kLog2e;   // the row's log-decay, summed below
-        }
-        if (c + 1 < nch) load(c + 1);
-        lds_barrier();
-
-        // ---- prologue: row norms (16 lanes per row), gates and their in-chunk cumsum
-        {
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int m = 0; m < DK / 16; ++m) {
-                const float x = L.QL[r16 * RS + c16 + 16 * m], y = L.KL[r16 * RS + c16 + 16 * m];
-                sq = fmaf(x, x, sq);
-                sk = fmaf(y, y, sk);
-            }
-            sq = group_sum<16>(sq);
-            sk = group_sum<16>(sk);
-            if (c16 == 0) {
-                L.NQ[r16] = l2norm ? scale / sqrtf(sq + kNormEps) : scale;
-                L.NK[r16] = l2norm ? 1.0f / sqrtf(sk + kNormEps) : 1.0f;
-            }
-        }
-        if constexpr (!EJK) {
-            if (tid < DK) {
-                // gamma' = lb * log2(e) * sigmoid(exp(a_log) (g + dt_bias)); padded rows 0
-                float b = 0.f;
-#pragma unroll
-                for (int r = 0; r < FC; ++r) {
-                    const float x = L.GB[r * RS + tid];
-                    const float gm = (r < len) ? lb2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-ea * (x + dtb))) : 0.f;
-                    b += gm;
-                    L.GB[r * RS + tid] = b;
-                }
-                const float b0 = L.GB[tid];
-                L.E0[tid] = __builtin_amdgcn_exp2f(b0);
-                L.NC[tid] = __builtin_amdgcn_exp2f(b - b0);
-                L.DC[tid] = __builtin_amdgcn_exp2f(b);
-            }
-        } else {
-            if (tid < FC) {
-                // b_r and b_{r-1} of this row, summed in row order (the decays sit in BR)
+            L.BT[tid] = (tid < len) ? (EJK ? R.b : sigmoid_f(R.b)) : 0.f;
+            if constexpr (EJK) {
+                // b_r and b_{r-1} of row tid, summed in row order; these lanes are one
+                // wave, whose LDS operations take effect in issue order
+                L.BR[tid] = R.d * kLog2e;
                 float b = 0.f, bx = 0.f;
                 for (int s = 0; s <= tid; ++s) {
                     bx = b;
@@ -208,7 +253,6 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 }
                 float bc = 0.f;
                 for (int s = 0; s < FC; ++s) bc += L.BR[s];
-                // every lane has read BR before any writes it (one wave: LDS in issue order)
                 L.BX[tid] = bx;
                 L.EB[tid] = __builtin_amdgcn_exp2f(b);
                 L.EX[tid] = __builtin_amdgcn_exp2f(bx);
@@ -217,11 +261,33 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.BR[tid] = b;
             }
         }
+        if (c + FD < nch) load(R, c + FD);
         lds_barrier();
 
-        // ---- normalised rows with the decay factors
+        // ---- lane i < dk: the gate cumsum of channel i down the 16 rows
+        if constexpr (!EJK) {
+            if (tid < DK) {
+                const int i = tid;
+                // gamma' = lb * log2(e) * sigmoid(exp(a_log) (g + dt_bias)); padded rows 0
+                float b = 0.f, b0 = 0.f;
 #pragma unroll
-        for (int m = 0; m < EPT; ++m) {
+                for (int r = 0; r < FC; ++r) {
+                    const float x = L.GB[r * RS + i];
+                    const float gm = (r < len) ? lb2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-ea * (x + dtb))) : 0.f;
+                    b += gm;
+                    if (r == 0) b0 = b;
+                    L.GB[r * RS + i] = b;
+                }
+                L.E0[i] = __builtin_amdgcn_exp2f(b0);
+                L.NC[i] = __builtin_amdgcn_exp2f(b - b0);
+                L.DC[i] = __builtin_amdgcn_exp2f(b);
+            }
+            lds_barrier();
+        }
+
+        // ---- normalised rows with the decay factors L = 2^{b_r - b_0}, R = 1 / L
+#pragma unroll
+        for (int m = 0; m < FC * DK / FT; ++m) {
             const int e = tid + m * FT;
             const int r = e / DK, i = e % DK;
             const float qh = L.QL[r * RS + i] * L.NQ[r];
@@ -232,126 +298,111 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.KR[r * RS + i] = kh;
             } else {
                 const float d = L.GB[r * RS + i] - L.GB[i];   // b_r - b_0 <= 0
-                const float lf = __builtin_amdgcn_exp2f(d), rf = __builtin_amdgcn_exp2f(-d);
+                const float lf = __builtin_amdgcn_exp2f(d);
                 L.QL[r * RS + i] = qh * lf;
                 L.KL[r * RS + i] = kh * lf;
-                L.KR[r * RS + i] = kh * rf;
+                L.KR[r * RS + i] = kh * __builtin_amdgcn_exp2f(-d);
             }
         }
         lds_barrier();
 
-        // ---- A and P: thread (r, s) = (r16, c16)
-        {
-            const int r = r16, s = c16;
-            float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+        // ---- the four products over dk, one per wave (K = dk in MFMA steps of 4):
+        //   wave 0: A = KL KR^T,  wave 1: P = QL KR^T,  wave 2: Qg S0 (kept in
+        //   registers for O),  wave 3: Y = V - Kg S0, with Qg, Kg = 2^{b_0} QL, KL
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (wave <= 1) {
+            const float* X = (wave == 0) ? L.KL : L.QL;
 #pragma unroll 8
-            for (int i = 0; i < DK; i += 2) {
-                const float k0 = L.KR[s * RS + i], k1 = L.KR[s * RS + i + 1];
-                a0 = fmaf(L.KL[r * RS + i], k0, a0);
-                a1 = fmaf(L.KL[r * RS + i + 1], k1, a1);
-                p0 = fmaf(L.QL[r * RS + i], k0, p0);
-                p1 = fmaf(L.QL[r * RS + i + 1], k1, p1);
-            }
-            float a = a0 + a1, p = p0 + p1;
-            if constexpr (EJK) {
-                a *= (s < r) ? __builtin_amdgcn_exp2f(L.BX[r] - L.BR[s]) : 0.f;
-                p *= (s <= r) ? __builtin_amdgcn_exp2f(L.BR[r] - L.BR[s]) : 0.f;
-            }
-            L.AM[r * F16 + s] = (s < r) ? L.BT[r] * a : 0.f;
-            L.PM[r * F16 + s] = (s <= r) ? p : 0.f;
-        }
-        lds_barrier();
-
-        // ---- T' = (I + A)^-1 diag(beta): lane j < 16 solves column j by forward
-        // substitution; meanwhile every thread forms its (r, j) entry of Qg S0
-        if (tid < FC) {
-            const int j = tid;
-            float t[FC];
+            for (int k0 = 0; k0 < DK; k0 += 4)
+                acc = mfma4(X[lm * RS + k0 + lk], L.KR[lm * RS + k0 + lk], acc);
 #pragma unroll
-            for (int r = 0; r < FC; ++r) t[r] = (r == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int s = 0; s < FC - 1; ++s) {
-                const float ts = t[s];
-#pragma unroll
-                for (int r = s + 1; r < FC; ++r) t[r] = fmaf(-L.AM[r * F16 + s], ts, t[r]);
-            }
-            const float bj = L.BT[j];
-#pragma unroll
-            for (int r = 0; r < FC; ++r) L.TP[r * F16 + j] = t[r] * bj;
-        }
-        float oq;   // (Qg S0)[r16][c16]
-        {
-            float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < DK; i += 2) {
-                if constexpr (EJK) {
-                    o0 = fmaf(L.QL[r16 * RS + i], L.SL[i * F16 + c16], o0);
-                    o1 = fmaf(L.QL[r16 * RS + i + 1], L.SL[(i + 1) * F16 + c16], o1);
+            for (int e = 0; e < 4; ++e) {
+                const int r = ro + e, s = lm;   // acc[e] = (row r, column s)
+                float x = acc[e];
+                if (wave == 0) {
+                    if constexpr (EJK) x *= (s < r) ? __builtin_amdgcn_exp2f(L.BX[r] - L.BR[s]) : 0.f;
+                    L.AM[r * F16 + s] = (s < r) ? L.BT[r] * x : 0.f;
                 } else {
-                    o0 = fmaf(L.E0[i] * L.QL[r16 * RS + i], L.SL[i * F16 + c16], o0);
-                    o1 = fmaf(L.E0[i + 1] * L.QL[r16 * RS + i + 1], L.SL[(i + 1) * F16 + c16], o1);
+                    if constexpr (EJK) x *= (s <= r) ? __builtin_amdgcn_exp2f(L.BR[r] - L.BR[s]) : 0.f;
+                    L.PM[r * F16 + s] = (s <= r) ? x : 0.f;
                 }
             }
-            oq = o0 + o1;
-            if constexpr (EJK) oq *= L.EB[r16];
-        }
-        lds_barrier();
-
-        // ---- W = T' Kg (into QL's space) and this thread's entry of T' V
-#pragma unroll
-        for (int m = 0; m < EPT; ++m) {
-            const int e = tid + m * FT;
-            const int r = e / DK, i = e % DK;
-            float w = 0.f;
-#pragma unroll
-            for (int s = 0; s < FC; ++s) {
-                if constexpr (EJK)
-                    w = fmaf(L.TP[r * F16 + s], L.EX[s] * L.KL[s * RS + i], w);
-                else
-                    w = fmaf(L.TP[r * F16 + s], L.KL[s * RS + i], w);
-            }
-            L.QL[r * RS + i] = EJK ? w : L.E0[i] * w;
-        }
-        float ut = 0.f;   // (T' V)[r16][c16]
-#pragma unroll
-        for (int s = 0; s < FC; ++s) ut = fmaf(L.TP[r16 * F16 + s], L.VV[s * F16 + c16], ut);
-        lds_barrier();
-
-        // ---- U = T' V - W S0
-        {
-            float w0 = 0.f, w1 = 0.f;
+        } else {
+            const float* X = (wave == 2) ? L.QL : L.KL;
 #pragma unroll 8
-            for (int i = 0; i < DK; i += 2) {
-                w0 = fmaf(L.QL[r16 * RS + i], L.SL[i * F16 + c16], w0);
-                w1 = fmaf(L.QL[r16 * RS + i + 1], L.SL[(i + 1) * F16 + c16], w1);
+            for (int k0 = 0; k0 < DK; k0 += 4) {
+                const int kk = k0 + lk;
+                const float a = EJK ? X[lm * RS + kk] : L.E0[kk] * X[lm * RS + kk];
+                acc = mfma4(a, L.SL[kk * F16 + lm], acc);
             }
-            L.UM[r16 * F16 + c16] = ut - (w0 + w1);
+            if (wave == 2) {
+                if constexpr (EJK) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] *= L.EB[ro + e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = ro + e;
+                    const float z = EJK ? L.EX[r] * acc[e] : acc[e];
+                    L.YM[r * F16 + lm] = L.VV[r * F16 + lm] - z;
+                }
+            }
         }
         lds_barrier();
 
-        // ---- O = Qg S0 + P U (stored for the sequence's rows); S = Diag(2^{b_C}) S0 + Kc^T U
-        {
-            float ov = oq;
+        // ---- U = T' Y: lane j < 16 solves (I + A) u = diag(beta) y for column j
+        if (tid < FC) {
+            const int j = tid;
+            float u[FC];
 #pragma unroll
-            for (int s = 0; s < FC; ++s) ov = fmaf(L.PM[r16 * F16 + s], L.UM[s * F16 + c16], ov);
-            if (r16 < len) o[((size_t)(c0 + r16) * H + h) * DV + j0 + c16] = ov;
-        }
+            for (int r = 0; r < FC; ++r) u[r] = L.BT[r] * L.YM[r * F16 + j];
 #pragma unroll
-        for (int m = 0; m < DK / 16; ++m) {
-            const int i = r16 + 16 * m;
-            float acc = 0.f;
-            if constexpr (EJK) {
+            for (int s = 0; s < FC - 1; ++s) {
+                const float us = u[s];
 #pragma unroll
-                for (int s = 0; s < FC; ++s) acc = fmaf(L.EC[s] * L.KR[s * RS + i], L.UM[s * F16 + c16], acc);
-                L.SL[i * F16 + c16] = fmaf(L.DC[0], L.SL[i * F16 + c16], acc);
-            } else {
-                const float nc = L.NC[i];
-#pragma unroll
-                for (int s = 0; s < FC; ++s) acc = fmaf(nc * L.KR[s * RS + i], L.UM[s * F16 + c16], acc);
-                L.SL[i * F16 + c16] = fmaf(L.DC[i], L.SL[i * F16 + c16], acc);
+                for (int r = s + 1; r < FC; ++r) u[r] = fmaf(-L.AM[r * F16 + s], us, u[r]);
             }
+#pragma unroll
+            for (int r = 0; r < FC; ++r) L.UM[r * F16 + j] = u[r];
         }
         lds_barrier();
+
+        // ---- O = Qg S0 + P U (wave 2), S = Diag(2^{b_C}) S0 + Kc^T U (16-row tiles over the waves)
+        if (wave == 2) {
+#pragma unroll
+            for (int k0 = 0; k0 < FC; k0 += 4)
+                acc = mfma4(L.PM[lm * F16 + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (ro + e < len) o[((size_t)(c0 + ro + e) * H + h) * DV + j0 + lm] = acc[e];
+        }
+#pragma unroll
+        for (int t = wave; t < DK / 16; t += 4) {
+            const int ib = 16 * t;
+            f32x4_t sc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = ib + ro + e;
+                sc[e] = (EJK ? L.DC[0] : L.DC[i]) * L.SL[i * F16 + lm];
+            }
+            const int ia = ib + lm;   // A operand row: Kc^T[ia][s] = Kc[s][ia] = 2^{b_C - b_0} KR[s][ia]
+#pragma unroll
+            for (int k0 = 0; k0 < FC; k0 += 4) {
+                const int s = k0 + lk;
+                const float kc = (EJK ? L.EC[s] : L.NC[ia]) * L.KR[s * RS + ia];
+                sc = mfma4(kc, L.UM[s * F16 + lm], sc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.SL[(ib + ro + e) * F16 + lm] = sc[e];
+        }
+        lds_barrier();
+    };
+    // unrolled by the ring depth, so that every ring slot is a fixed set of registers
+    for (int cb = 0; cb < nch; cb += FD) {
+#pragma unroll
+        for (int u = 0; u < FD; ++u)
+            if (cb + u < nch) chunk(ring[u], cb + u);
     }
     if (nch == 0) lds_barrier();   // the initial state tile was written by other threads
 
