@@ -1,4 +1,5 @@
-// kda_chunked_f32.hip - chunk-parallel KDA prefill for float32 inputs
+// kda_chunked_f32.hip - chunk-parallel KDA prefill in float32 arithmetic: float32
+// inputs at any dk, bf16 inputs at dk < 128
 // (ejkernel "kernel_delta_attention": chunked mode, "Parallel within chunks").
 //
 // The chunk algebra is the bf16 MFMA kernel's (an exact regrouping of the
@@ -88,6 +89,25 @@ __device__ __forceinline__ void f32_seq_bounds(const int32_t* cu, int n, int T, 
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Four consecutive input channels as loaded: a float4 (float32 inputs) or
+// four bf16 in a uint2 (bf16 inputs), widened when used, so that a prefetched
+// load is not waited for where it is issued.
+template <typename Tin> struct Piece4;
+template <> struct Piece4<float> {
+    using type = float4;
+    static __device__ __forceinline__ float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    static __device__ __forceinline__ float4 widen(float4 x) { return x; }
+};
+template <> struct Piece4<bf16_t> {
+    using type = uint2;
+    static __device__ __forceinline__ uint2 zero() { return make_uint2(0u, 0u); }
+    static __device__ __forceinline__ float4 widen(uint2 x)
+    {
+        return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+    }
+};
+
 // D += A B on a 16x16x4 float32 MFMA: lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16] and holds D[4 (l / 16) + e][l % 16] in element e.
 __device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c)
@@ -108,13 +128,13 @@ __device__ __forceinline__ float lane_group_sum(float x)
     return x;
 }
 
-template <int DK, bool EJK>
+template <int DK, bool EJK, typename Tin, typename Tout>
 __global__ __launch_bounds__(FT) void chunk_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, const float* __restrict__ init, const int32_t* __restrict__ cu,
     int T, int H, int HKV, int DV, float scale, float lower_bound, int l2norm,
-    float* __restrict__ o, float* __restrict__ final_state)
+    Tout* __restrict__ o, float* __restrict__ final_state)
 {
     constexpr int RS = F32Lds<DK>::RS;
     constexpr int RL = DK / 4;                 // lanes per row in the q, k loads (4 channels each)
@@ -157,9 +177,13 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     // global loads: a load of "pointer or a local zero" becomes a flat load,
     // which the LDS barriers also wait for); rows past the sequence read the
     // chunk's first row and are zeroed by a select.
+    using P4 = Piece4<Tin>;
+    using piece_t = typename P4::type;
     struct Raw {
-        float4 q[QN], k[QN], g[QN];
-        float v, b, d;
+        piece_t q[QN], k[QN];
+        float4 g[QN];
+        Tin v;
+        float b, d;
     };
     auto load = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
@@ -169,15 +193,15 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         for (int m = 0; m < QN; ++m) {
             const int e = tid + m * FT;
             const int row = e / RL, c4 = e % RL;
-            R.q[m] = z;
-            R.k[m] = z;
+            R.q[m] = P4::zero();
+            R.k[m] = P4::zero();
             R.g[m] = z;
             if (e < Q4) {
                 const int rr = row < len ? row : 0;
-                const float4 xq = *reinterpret_cast<const float4*>(q + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
-                const float4 xk = *reinterpret_cast<const float4*>(k + ((size_t)(c0 + rr) * HKV + hk) * DK + 4 * c4);
-                R.q[m] = row < len ? xq : z;
-                R.k[m] = row < len ? xk : z;
+                const piece_t xq = *reinterpret_cast<const piece_t*>(q + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
+                const piece_t xk = *reinterpret_cast<const piece_t*>(k + ((size_t)(c0 + rr) * HKV + hk) * DK + 4 * c4);
+                R.q[m] = row < len ? xq : P4::zero();
+                R.k[m] = row < len ? xk : P4::zero();
                 if constexpr (!EJK) {
                     const float4 xg = *reinterpret_cast<const float4*>(g + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
                     R.g[m] = row < len ? xg : z;
@@ -186,8 +210,8 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         }
         {
             const int rr = r16 < len ? r16 : 0;
-            const float x = v[((size_t)(c0 + rr) * HKV + hk) * DV + j0 + c16];
-            R.v = (r16 < len) ? x : 0.f;
+            const Tin x = v[((size_t)(c0 + rr) * HKV + hk) * DV + j0 + c16];
+            R.v = (r16 < len) ? x : Tin{};
         }
         R.b = 0.f;
         R.d = 0.f;
@@ -223,15 +247,17 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             if (e < Q4) {
                 float* pq = L.QL + row * RS + 4 * c4;
                 float* pk = L.KL + row * RS + 4 * c4;
-                pq[0] = R.q[m].x; pq[1] = R.q[m].y; pq[2] = R.q[m].z; pq[3] = R.q[m].w;
-                pk[0] = R.k[m].x; pk[1] = R.k[m].y; pk[2] = R.k[m].z; pk[3] = R.k[m].w;
+                const float4 xq = P4::widen(R.q[m]), xk = P4::widen(R.k[m]);
+                pq[0] = xq.x; pq[1] = xq.y; pq[2] = xq.z; pq[3] = xq.w;
+                pk[0] = xk.x; pk[1] = xk.y; pk[2] = xk.z; pk[3] = xk.w;
                 if constexpr (!EJK) {
                     float* pg = L.GB + row * RS + 4 * c4;
                     pg[0] = R.g[m].x; pg[1] = R.g[m].y; pg[2] = R.g[m].z; pg[3] = R.g[m].w;
                 }
             }
-            float sq = R.q[m].x * R.q[m].x + R.q[m].y * R.q[m].y + R.q[m].z * R.q[m].z + R.q[m].w * R.q[m].w;
-            float sk = R.k[m].x * R.k[m].x + R.k[m].y * R.k[m].y + R.k[m].z * R.k[m].z + R.k[m].w * R.k[m].w;
+            const float4 wq = P4::widen(R.q[m]), wk = P4::widen(R.k[m]);
+            float sq = wq.x * wq.x + wq.y * wq.y + wq.z * wq.z + wq.w * wq.w;
+            float sk = wk.x * wk.x + wk.y * wk.y + wk.z * wk.z + wk.w * wk.w;
             sq = lane_group_sum<RL>(sq);
             sk = lane_group_sum<RL>(sk);
             if (e < Q4 && c4 == 0) {
@@ -239,7 +265,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.NK[row] = l2norm ? 1.0f / sqrtf(sk + kNormEps) : 1.0f;
             }
         }
-        L.VV[r16 * F16 + c16] = R.v;
+        L.VV[r16 * F16 + c16] = to_f32(R.v);
         if (tid < FC) {
             L.BT[tid] = (tid < len) ? (EJK ? R.b : sigmoid_f(R.b)) : 0.f;
             if constexpr (EJK) {
@@ -375,7 +401,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 acc = mfma4(L.PM[lm * F16 + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (ro + e < len) o[((size_t)(c0 + ro + e) * H + h) * DV + j0 + lm] = acc[e];
+                if (ro + e < len) o[((size_t)(c0 + ro + e) * H + h) * DV + j0 + lm] = from_f32<Tout>(acc[e]);
         }
 #pragma unroll
         for (int t = wave; t < DK / 16; t += 4) {
@@ -414,23 +440,31 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     }
 }
 
+template <int DK, typename Tin, typename Tout>
+hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(a.dv / FJ), (unsigned)a.H, (unsigned)a.N);
+    const Tin* q = static_cast<const Tin*>(a.q);
+    const Tin* k = static_cast<const Tin*>(a.k);
+    const Tin* v = static_cast<const Tin*>(a.v);
+    Tout* o = static_cast<Tout*>(a.o);
+    if (a.ejk)
+        hipLaunchKernelGGL((chunk_f32_kernel<DK, true, Tin, Tout>), grid, dim3(FT), 0, stream, q, k, v, a.g,
+                           a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
+                           a.lower_bound, (int)a.l2norm, o, a.final_state);
+    else
+        hipLaunchKernelGGL((chunk_f32_kernel<DK, false, Tin, Tout>), grid, dim3(FT), 0, stream, q, k, v, a.g,
+                           a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
+                           a.lower_bound, (int)a.l2norm, o, a.final_state);
+    return hipGetLastError();
+}
+
 template <int DK>
 hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(a.dv / FJ), (unsigned)a.H, (unsigned)a.N);
-    const float* q = static_cast<const float*>(a.q);
-    const float* k = static_cast<const float*>(a.k);
-    const float* v = static_cast<const float*>(a.v);
-    float* o = static_cast<float*>(a.o);
-    if (a.ejk)
-        hipLaunchKernelGGL((chunk_f32_kernel<DK, true>), grid, dim3(FT), 0, stream, q, k, v, a.g, a.beta,
-                           a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale, a.lower_bound,
-                           (int)a.l2norm, o, a.final_state);
-    else
-        hipLaunchKernelGGL((chunk_f32_kernel<DK, false>), grid, dim3(FT), 0, stream, q, k, v, a.g, a.beta,
-                           a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale, a.lower_bound,
-                           (int)a.l2norm, o, a.final_state);
-    return hipGetLastError();
+    if (!a.in_bf16) return launch_typed<DK, float, float>(a, stream);
+    if (a.out_bf16) return launch_typed<DK, bf16_t, bf16_t>(a, stream);
+    return launch_typed<DK, bf16_t, float>(a, stream);
 }
 
 }  // namespace
@@ -438,8 +472,11 @@ hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream)
 bool chunked_f32_supported(const PrefillArgs& a)
 {
     const bool dims = (a.dk == 16 || a.dk == 32 || a.dk == 64 || a.dk == 128) && a.dv % FJ == 0 && a.dv > 0;
-    // KDA needs the gate inputs and lower_bound >= -5 (the factor range above)
-    return !a.in_bf16 && !a.out_bf16 && dims && (a.ejk || (a.g != nullptr && a.a_log != nullptr && a.lower_bound >= -5.0f));
+    // float32 inputs at any dk; bf16 inputs below dk = 128 (dk = 128 takes the
+    // bf16 MFMA kernel).  KDA needs the gate inputs and lower_bound >= -5 (the
+    // factor range above).
+    return dims && (!a.in_bf16 || a.dk < 128) &&
+           (a.ejk || (a.g != nullptr && a.a_log != nullptr && a.lower_bound >= -5.0f));
 }
 
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream)

@@ -103,11 +103,11 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *   - KDA_CHUNKED with bf16 inputs and dk = 128 (any of the dv above) runs
  *     the MFMA chunked kernel (64-token chunks; KDA and EJK modes), which
  *     needs q, k, v, o and (KDA) g 16-byte aligned (KDA_EINVAL otherwise);
- *   - KDA_CHUNKED with float32 inputs and output runs the float32 chunked
- *     kernel (vector ALUs, 16-token chunks: the chunking changes rounding
- *     only) when q, k and (KDA) g are 16-byte aligned and, in KDA mode,
- *     lower_bound >= -5 (its decay factors over 16 tokens then stay inside
- *     float32's normal range);
+ *   - KDA_CHUNKED with float32 inputs (any dk) or bf16 inputs with dk < 128
+ *     runs the chunked kernel that computes in float32 (float32 MFMA,
+ *     16-token chunks: the chunking changes rounding only) when q, k and
+ *     (KDA) g are 16-byte aligned and, in KDA mode, lower_bound >= -5 (its
+ *     decay factors over 16 tokens then stay inside float32's normal range);
  *   - every other combination runs the float32 token-by-token kernel, which
  *     computes the same function step by step.
  * EJK decays are expected to be <= 0 (the ejkernel page says so); the chunked

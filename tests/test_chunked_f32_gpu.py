@@ -1,5 +1,6 @@
-"""The float32 chunked kernel (KDA_CHUNKED with float32 inputs: 16-token chunks
-on the vector ALUs) against the oracle, and its routing.
+"""The chunked kernel that computes in float32 (KDA_CHUNKED with float32 inputs,
+or bf16 inputs with dk < 128: 16-token chunks on float32 MFMA) against the
+oracle, and its routing.
 
 Bar: relative L2 <= 1e-5 for o and the final state (float32 path, as for the
 token-by-token kernel); packed sequences and chunk-aligned splits bit for bit."""
@@ -165,3 +166,43 @@ def test_chunked_f32_routing_falls_back_to_token_by_token():
                            lower_bound=inp.lower_bound, use_chunked=False, return_state=True)
     torch.cuda.synchronize()
     assert torch.equal(o_u, o_r) and torch.equal(s_u, s_r)
+
+
+@pytest.mark.parametrize("dk", [16, 32, 64])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("ejk", [False, True])
+def test_chunked_float32_arithmetic_on_bf16_inputs(dk, out, ejk):
+    """bf16 inputs with dk < 128 take the same kernel (float32 arithmetic on the
+    widened inputs): the state meets the float32 bar, the output too unless it
+    is rounded to bf16 (then the bf16-input bar)."""
+    import torch
+    inp = workloads.prefill_inputs(2, 45, 3, dk, 64, seed=380 + dk, ejk=ejk, init_state=True)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    say("chunked float32 arithmetic, bf16 inputs", dk, out, "ejk" if ejk else "kda")
+    o, s = prefill_gpu(inp, out_dtype=od)
+    ro, rs = prefill_oracle(inp)
+    assert rel_l2(s, rs) <= TOL, rel_l2(s, rs)
+    assert rel_l2(o, ro) <= (2e-2 if out == "bf16" else TOL), rel_l2(o, ro)
+    orc, src = prefill_gpu(inp, out_dtype=od, use_chunked=False)
+    assert rel_l2(s, src) <= TOL
+
+
+def test_chunked_float32_arithmetic_bf16_varlen_bitwise():
+    lens = [33, 0, 80, 5, 16]
+    inp = workloads.prefill_inputs(1, 0, 2, 64, 32, seed=390, lengths=lens, init_state=True)
+    say("chunked float32 arithmetic, bf16 varlen", lens)
+    o, s = prefill_gpu(inp)
+    ro, rs = prefill_oracle(inp)
+    assert rel_l2(o, ro) <= 2e-2 and rel_l2(s, rs) <= TOL
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if a == b:
+            np.testing.assert_array_equal(s[n], inp.initial_state[n])
+            continue
+        sub = workloads.PrefillInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b], inp.g[:, a:b],
+                                      inp.beta[:, a:b], inp.a_log, inp.dt_bias, inp.initial_state[n:n + 1],
+                                      None, inp.dtype, inp.scale, inp.lower_bound)
+        on, sn = prefill_gpu(sub)
+        np.testing.assert_array_equal(o[:, a:b], on)
+        np.testing.assert_array_equal(s[n], sn[0])
