@@ -68,6 +68,7 @@ struct F32Lds {
     float PM[FC * F16];   // P (lower incl. diagonal)
     float YM[FC * F16];   // Y = V - Kg S0
     float UM[FC * F16];   // U
+    float OM[FC * F16];   // O of the chunk, stored by every thread
     float E0[DK];         // 2^{b_0}
     float NC[DK];         // 2^{b_C - b_0}
     float DC[DK];         // 2^{b_C}
@@ -168,15 +169,13 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const float lb2 = lower_bound * kLog2e;
     const float dtb = (!EJK && dt_bias && tid < DK) ? dt_bias[(size_t)tid * H + h] : 0.f;
 
-    // One chunk's inputs in registers, rows past the sequence zero: q and k as
-    // float4 pieces (row e / RL, channels 4 (e % RL) ..); the KDA gates of
-    // channel tid (tid < DK) for the 16 rows, so that the in-chunk cumsum runs
-    // down a register column (each row's load is still one coalesced row);
-    // v at (row r16, column c16); beta and the EJK decay of row tid (tid < 16).
-    // Only the lanes that need a value load it (explicit branches keep these
-    // global loads: a load of "pointer or a local zero" becomes a flat load,
-    // which the LDS barriers also wait for); rows past the sequence read the
-    // chunk's first row and are zeroed by a select.
+    // One chunk's inputs as loaded into registers: q, k and (KDA) g as pieces of
+    // four channels (row e / RL, channels 4 (e % RL) ..), v at (row r16,
+    // column c16), beta and the EJK decay of row tid.  Every lane loads from a
+    // valid address (rows past the sequence, and lanes with no piece, read the
+    // chunk's first row) and the values are masked where they are used, so that
+    // no load is waited for where it is issued and every path issues the same
+    // loads (the wait before a chunk's first use then covers only its own).
     using P4 = Piece4<Tin>;
     using piece_t = typename P4::type;
     struct Raw {
@@ -188,74 +187,55 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     auto load = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
         const int len = min(FC, t1 - c0);
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int m = 0; m < QN; ++m) {
             const int e = tid + m * FT;
             const int row = e / RL, c4 = e % RL;
-            R.q[m] = P4::zero();
-            R.k[m] = P4::zero();
-            R.g[m] = z;
-            if (e < Q4) {
-                const int rr = row < len ? row : 0;
-                const piece_t xq = *reinterpret_cast<const piece_t*>(q + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
-                const piece_t xk = *reinterpret_cast<const piece_t*>(k + ((size_t)(c0 + rr) * HKV + hk) * DK + 4 * c4);
-                R.q[m] = row < len ? xq : P4::zero();
-                R.k[m] = row < len ? xk : P4::zero();
-                if constexpr (!EJK) {
-                    const float4 xg = *reinterpret_cast<const float4*>(g + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
-                    R.g[m] = row < len ? xg : z;
-                }
-            }
+            const int rr = (e < Q4 && row < len) ? row : 0;
+            R.q[m] = *reinterpret_cast<const piece_t*>(q + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
+            R.k[m] = *reinterpret_cast<const piece_t*>(k + ((size_t)(c0 + rr) * HKV + hk) * DK + 4 * c4);
+            if constexpr (!EJK)
+                R.g[m] = *reinterpret_cast<const float4*>(g + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
         }
-        {
-            const int rr = r16 < len ? r16 : 0;
-            const Tin x = v[((size_t)(c0 + rr) * HKV + hk) * DV + j0 + c16];
-            R.v = (r16 < len) ? x : Tin{};
-        }
-        R.b = 0.f;
-        R.d = 0.f;
-        if (tid < FC) {
-            const int rr = tid < len ? tid : 0;
-            const float xb = beta[(size_t)(c0 + rr) * H + h];
-            R.b = (tid < len) ? xb : 0.f;
-            if constexpr (EJK) {
-                if (g) {
-                    const float xd = g[(size_t)(c0 + rr) * H + h];
-                    R.d = (tid < len) ? xd : 0.f;
-                }
-            }
-        }
+        const int rv = r16 < len ? r16 : 0;
+        R.v = v[((size_t)(c0 + rv) * HKV + hk) * DV + j0 + c16];
+        const int rb = tid < len ? tid : 0;
+        R.b = beta[(size_t)(c0 + rb) * H + h];
+        if constexpr (EJK) R.d = (g ? g : beta)[(size_t)(c0 + rb) * H + h];   // NULL decay: zeroed at use
     };
     // chunks loaded ahead: at small dk a chunk computes in less than a memory
     // latency; at large dk two chunks cover it, and more would only queue requests
     constexpr int FD = DK <= 32 ? 4 : 2;
     Raw ring[FD];
+    if (nch > 0) {
 #pragma unroll
-    for (int u = 0; u < FD; ++u)
-        if (u < nch) load(ring[u], u);
+        for (int u = 0; u < FD; ++u) load(ring[u], min(u, nch - 1));
+    }
 
     auto chunk = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
-        const int len = min(FC, t1 - c0);
+        const int len = min(FC, t1 - c0);   // <= 0 for a padding chunk
         // ---- prologue from the registers: raw rows to LDS, row norms (RL lanes
         // per row), the gate cumsum of channel tid, beta; then fetch the next chunk
 #pragma unroll
         for (int m = 0; m < QN; ++m) {
             const int e = tid + m * FT;
             const int row = e / RL, c4 = e % RL;
+            const bool in = e < Q4 && row < len;
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 wq = in ? P4::widen(R.q[m]) : z, wk = in ? P4::widen(R.k[m]) : z;
             if (e < Q4) {
                 float* pq = L.QL + row * RS + 4 * c4;
                 float* pk = L.KL + row * RS + 4 * c4;
-                const float4 xq = P4::widen(R.q[m]), xk = P4::widen(R.k[m]);
+                const float4 xq = wq, xk = wk;
                 pq[0] = xq.x; pq[1] = xq.y; pq[2] = xq.z; pq[3] = xq.w;
                 pk[0] = xk.x; pk[1] = xk.y; pk[2] = xk.z; pk[3] = xk.w;
                 if constexpr (!EJK) {
                     float* pg = L.GB + row * RS + 4 * c4;
-                    pg[0] = R.g[m].x; pg[1] = R.g[m].y; pg[2] = R.g[m].z; pg[3] = R.g[m].w;
+                    const float4 xg = in ? R.g[m] : z;
+                    pg[0] = xg.x; pg[1] = xg.y; pg[2] = xg.z; pg[3] = xg.w;
                 }
             }
-            const float4 wq = P4::widen(R.q[m]), wk = P4::widen(R.k[m]);
             float sq = wq.x * wq.x + wq.y * wq.y + wq.z * wq.z + wq.w * wq.w;
             float sk = wk.x * wk.x + wk.y * wk.y + wk.z * wk.z + wk.w * wk.w;
             sq = lane_group_sum<RL>(sq);
@@ -265,13 +245,13 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.NK[row] = l2norm ? 1.0f / sqrtf(sk + kNormEps) : 1.0f;
             }
         }
-        L.VV[r16 * F16 + c16] = to_f32(R.v);
+        L.VV[r16 * F16 + c16] = (r16 < len) ? to_f32(R.v) : 0.f;
         if (tid < FC) {
-            L.BT[tid] = (tid < len) ? (EJK ? R.b : sigmoid_f(R.b)) : 0.f;
+            L.BT[tid] = (tid < len) ? (EJK ? R.b : sigmoid_f(R.b)) : 0.f;   // R.b read for every lane
             if constexpr (EJK) {
                 // b_r and b_{r-1} of row tid, summed in row order; these lanes are one
                 // wave, whose LDS operations take effect in issue order
-                L.BR[tid] = R.d * kLog2e;
+                L.BR[tid] = (tid < len && g) ? R.d * kLog2e : 0.f;
                 float b = 0.f, bx = 0.f;
                 for (int s = 0; s <= tid; ++s) {
                     bx = b;
@@ -287,7 +267,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.BR[tid] = b;
             }
         }
-        if (c + FD < nch) load(R, c + FD);
+        load(R, min(c + FD, nch - 1));   // past the end this reloads the last chunk
         lds_barrier();
 
         // ---- lane i < dk: the gate cumsum of channel i down the 16 rows
@@ -400,8 +380,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             for (int k0 = 0; k0 < FC; k0 += 4)
                 acc = mfma4(L.PM[lm * F16 + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (ro + e < len) o[((size_t)(c0 + ro + e) * H + h) * DV + j0 + lm] = from_f32<Tout>(acc[e]);
+            for (int e = 0; e < 4; ++e) L.OM[(ro + e) * F16 + lm] = acc[e];
         }
 #pragma unroll
         for (int t = wave; t < DK / 16; t += 4) {
@@ -423,12 +402,29 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             for (int e = 0; e < 4; ++e) L.SL[(ib + ro + e) * F16 + lm] = sc[e];
         }
         lds_barrier();
+        // O row r16, column c16, through a buffer resource that ends after the
+        // chunk's last row: the buffer unit drops the stores of padded rows, so
+        // every lane issues the same store
+        {
+            Tout* obase = o + ((size_t)c0 * H + h) * DV + j0;
+            const int rec = len > 0 ? ((len - 1) * H * DV + FJ) * (int)sizeof(Tout) : 0;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, 0, rec, 0x00020000);
+            const int off = (r16 * H * DV + c16) * (int)sizeof(Tout);
+            const Tout val = from_f32<Tout>(L.OM[r16 * F16 + c16]);
+            if constexpr (sizeof(Tout) == 4)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, val), rs, off, 0, 0);
+        }
     };
-    // unrolled by the ring depth, so that every ring slot is a fixed set of registers
+    // Unrolled by the ring depth, so that every ring slot is a fixed set of
+    // registers.  The chunk count is padded to a multiple of the depth: a chunk
+    // past the end has no rows, so it stores nothing and its state update is
+    // exactly S <- 2^0 S.  Every path then issues the same memory operations,
+    // and the wait before a chunk's first use counts only that chunk's loads.
     for (int cb = 0; cb < nch; cb += FD) {
 #pragma unroll
-        for (int u = 0; u < FD; ++u)
-            if (cb + u < nch) chunk(ring[u], cb + u);
+        for (int u = 0; u < FD; ++u) chunk(ring[u], cb + u);
     }
     if (nch == 0) lds_barrier();   // the initial state tile was written by other threads
 
