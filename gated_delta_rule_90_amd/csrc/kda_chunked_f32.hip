@@ -64,7 +64,7 @@ struct F32Lds {
     float GB[FC * RS];    // b_r per channel (log2 units, KDA)
     float SL[DK * F16];   // the state tile S[i][j]
     float VV[FC * F16];   // the value tile V[s][j]
-    float AM[FC * F16];   // A (strict lower, beta-scaled)
+    alignas(16) float AM[FC * 20];   // A (strict lower, beta-scaled), 16-byte aligned rows
     float PM[FC * F16];   // P (lower incl. diagonal)
     float YM[FC * F16];   // Y = V - Kg S0
     float UM[FC * F16];   // U
@@ -167,7 +167,12 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     }
     const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) in log2 units
     const float lb2 = lower_bound * kLog2e;
-    const float dtb = (!EJK && dt_bias && tid < DK) ? dt_bias[(size_t)tid * H + h] : 0.f;
+    // dt_bias of the four channels of this lane's pieces (the piece column
+    // tid % RL is the same for every piece of the lane)
+    float dtb4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        dtb4[j] = (!EJK && dt_bias) ? dt_bias[(size_t)(4 * (tid % RL) + j) * H + h] : 0.f;
 
     // One chunk's inputs as loaded into registers: q, k and (KDA) g as pieces of
     // four channels (row e / RL, channels 4 (e % RL) ..), v at (row r16,
@@ -231,9 +236,13 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 pq[0] = xq.x; pq[1] = xq.y; pq[2] = xq.z; pq[3] = xq.w;
                 pk[0] = xk.x; pk[1] = xk.y; pk[2] = xk.z; pk[3] = xk.w;
                 if constexpr (!EJK) {
+                    // gamma' = lb * log2(e) * sigmoid(exp(a_log) (g + dt_bias)), element by
+                    // element here, where every lane holds four; padded rows 0
                     float* pg = L.GB + row * RS + 4 * c4;
-                    const float4 xg = in ? R.g[m] : z;
-                    pg[0] = xg.x; pg[1] = xg.y; pg[2] = xg.z; pg[3] = xg.w;
+                    const float xg[4] = {R.g[m].x, R.g[m].y, R.g[m].z, R.g[m].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pg[j] = in ? lb2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-ea * (xg[j] + dtb4[j]))) : 0.f;
                 }
             }
             float sq = wq.x * wq.x + wq.y * wq.y + wq.z * wq.z + wq.w * wq.w;
@@ -241,13 +250,14 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             sq = lane_group_sum<RL>(sq);
             sk = lane_group_sum<RL>(sk);
             if (e < Q4 && c4 == 0) {
-                L.NQ[row] = l2norm ? scale / sqrtf(sq + kNormEps) : scale;
-                L.NK[row] = l2norm ? 1.0f / sqrtf(sk + kNormEps) : 1.0f;
+                L.NQ[row] = l2norm ? scale * __builtin_amdgcn_rsqf(sq + kNormEps) : scale;
+                L.NK[row] = l2norm ? __builtin_amdgcn_rsqf(sk + kNormEps) : 1.0f;
             }
         }
         L.VV[r16 * F16 + c16] = (r16 < len) ? to_f32(R.v) : 0.f;
         if (tid < FC) {
-            L.BT[tid] = (tid < len) ? (EJK ? R.b : sigmoid_f(R.b)) : 0.f;   // R.b read for every lane
+            // beta = 1 / (1 + 2^{-logit log2(e)}); R.b was loaded by every lane
+            L.BT[tid] = (tid < len) ? (EJK ? R.b : __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * R.b))) : 0.f;
             if constexpr (EJK) {
                 // b_r and b_{r-1} of row tid, summed in row order; these lanes are one
                 // wave, whose LDS operations take effect in issue order
@@ -274,13 +284,13 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         if constexpr (!EJK) {
             if (tid < DK) {
                 const int i = tid;
-                // gamma' = lb * log2(e) * sigmoid(exp(a_log) (g + dt_bias)); padded rows 0
+                float gm[FC];
+#pragma unroll
+                for (int r = 0; r < FC; ++r) gm[r] = L.GB[r * RS + i];
                 float b = 0.f, b0 = 0.f;
 #pragma unroll
                 for (int r = 0; r < FC; ++r) {
-                    const float x = L.GB[r * RS + i];
-                    const float gm = (r < len) ? lb2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-ea * (x + dtb))) : 0.f;
-                    b += gm;
+                    b += gm[r];
                     if (r == 0) b0 = b;
                     L.GB[r * RS + i] = b;
                 }
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 float x = acc[e];
                 if (wave == 0) {
                     if constexpr (EJK) x *= (s < r) ? __builtin_amdgcn_exp2f(L.BX[r] - L.BR[s]) : 0.f;
-                    L.AM[r * F16 + s] = (s < r) ? L.BT[r] * x : 0.f;
+                    L.AM[r * 20 + s] = (s < r) ? L.BT[r] * x : 0.f;
                 } else {
                     if constexpr (EJK) x *= (s <= r) ? __builtin_amdgcn_exp2f(L.BR[r] - L.BR[s]) : 0.f;
                     L.PM[r * F16 + s] = (s <= r) ? x : 0.f;
@@ -360,14 +370,22 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         // ---- U = T' Y: lane j < 16 solves (I + A) u = diag(beta) y for column j
         if (tid < FC) {
             const int j = tid;
-            float u[FC];
+            float u[FC], am[FC][FC];
 #pragma unroll
             for (int r = 0; r < FC; ++r) u[r] = L.BT[r] * L.YM[r * F16 + j];
+            // A's rows as 16-byte reads, all issued before the substitution
+#pragma unroll
+            for (int r = 1; r < FC; ++r)
+#pragma unroll
+                for (int s4 = 0; s4 < r; s4 += 4) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(L.AM + r * 20 + s4);
+                    am[r][s4] = a4.x; am[r][s4 + 1] = a4.y; am[r][s4 + 2] = a4.z; am[r][s4 + 3] = a4.w;
+                }
 #pragma unroll
             for (int s = 0; s < FC - 1; ++s) {
                 const float us = u[s];
 #pragma unroll
-                for (int r = s + 1; r < FC; ++r) u[r] = fmaf(-L.AM[r * F16 + s], us, u[r]);
+                for (int r = s + 1; r < FC; ++r) u[r] = fmaf(-am[r][s], us, u[r]);
             }
 #pragma unroll
             for (int r = 0; r < FC; ++r) L.UM[r * F16 + j] = u[r];
