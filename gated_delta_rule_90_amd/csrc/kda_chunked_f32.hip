@@ -44,6 +44,8 @@
 // less than a memory latency.  Rows past a sequence's end are padded with
 // exact neutral values (q = k = v = 0, gamma = 0, beta = 0) and never stored,
 // so a packed batch equals each sequence run alone, bit for bit.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -97,11 +99,27 @@ template <typename Tin> struct Piece4;
 template <> struct Piece4<float> {
     using type = float4;
     static __device__ __forceinline__ float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    static __device__ __forceinline__ float4 load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    }
+    static __device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
     static __device__ __forceinline__ float4 widen(float4 x) { return x; }
 };
 template <> struct Piece4<bf16_t> {
     using type = uint2;
     static __device__ __forceinline__ uint2 zero() { return make_uint2(0u, 0u); }
+    static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    }
+    static __device__ __forceinline__ bf16_t load1(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        return bf16_t{__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)};
+    }
     static __device__ __forceinline__ float4 widen(uint2 x)
     {
         return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
@@ -114,6 +132,13 @@ template <> struct Piece4<bf16_t> {
 __device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Lane K's x in every lane of its quad (DPP quad_perm K, K, K, K).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xF, 0xF, false));
 }
 
 // x summed over each aligned group of N lanes (N = 4, 8, 16 or 32), in every
@@ -176,11 +201,14 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
 
     // One chunk's inputs as loaded into registers: q, k and (KDA) g as pieces of
     // four channels (row e / RL, channels 4 (e % RL) ..), v at (row r16,
-    // column c16), beta and the EJK decay of row tid.  Every lane loads from a
-    // valid address (rows past the sequence, and lanes with no piece, read the
-    // chunk's first row) and the values are masked where they are used, so that
-    // no load is waited for where it is issued and every path issues the same
-    // loads (the wait before a chunk's first use then covers only its own).
+    // column c16), beta and the EJK decay of row tid.  The loads go through
+    // buffer resources that end after the sequence's last row, so rows past
+    // the sequence read zeros; each address is a per-lane offset fixed for the
+    // whole sequence plus a per-chunk scalar offset.  The values are masked
+    // where they are used, so no load is waited for where it is issued and
+    // every path issues the same loads (the wait before a chunk's first use
+    // then covers only its own).  A sequence's spans fit 31-bit offsets (the
+    // host routes longer ones to the token-by-token kernel).
     using P4 = Piece4<Tin>;
     using piece_t = typename P4::type;
     struct Raw {
@@ -189,24 +217,37 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         Tin v;
         float b, d;
     };
+    constexpr int SI = (int)sizeof(Tin);
+    const int nseq = t1 - t0;
+    auto rsrc = [](const void* base, long long bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+    };
+    const long long last = nseq > 0 ? nseq - 1 : 0;
+    const __amdgpu_buffer_rsrc_t rq_ = rsrc(q + ((size_t)t0 * H + h) * DK, (last * H * DK + DK) * SI);
+    const __amdgpu_buffer_rsrc_t rk_ = rsrc(k + ((size_t)t0 * HKV + hk) * DK, (last * HKV * DK + DK) * SI);
+    const __amdgpu_buffer_rsrc_t rg_ = rsrc((EJK ? (g ? g : beta) : g) + (EJK ? (size_t)t0 * H + h : ((size_t)t0 * H + h) * DK),
+                                           EJK ? (last * H + 1) * 4 : (last * H * DK + DK) * 4);
+    const __amdgpu_buffer_rsrc_t rv_ = rsrc(v + ((size_t)t0 * HKV + hk) * DV + j0, (last * HKV * DV + FJ) * SI);
+    const __amdgpu_buffer_rsrc_t rb_ = rsrc(beta + (size_t)t0 * H + h, (last * H + 1) * 4);
+    int vq[QN], vk[QN];
+#pragma unroll
+    for (int m = 0; m < QN; ++m) {
+        const int e = tid + m * FT;
+        const int row = e / RL, c4 = e % RL;
+        vq[m] = row * H * DK + 4 * c4;     // in elements; q and g share it
+        vk[m] = row * HKV * DK + 4 * c4;
+    }
     auto load = [&](Raw& R, int c) {
-        const int c0 = t0 + c * FC;
-        const int len = min(FC, t1 - c0);
+        const int r0 = c * FC;   // the chunk's first row within the sequence
 #pragma unroll
         for (int m = 0; m < QN; ++m) {
-            const int e = tid + m * FT;
-            const int row = e / RL, c4 = e % RL;
-            const int rr = (e < Q4 && row < len) ? row : 0;
-            R.q[m] = *reinterpret_cast<const piece_t*>(q + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
-            R.k[m] = *reinterpret_cast<const piece_t*>(k + ((size_t)(c0 + rr) * HKV + hk) * DK + 4 * c4);
-            if constexpr (!EJK)
-                R.g[m] = *reinterpret_cast<const float4*>(g + ((size_t)(c0 + rr) * H + h) * DK + 4 * c4);
+            R.q[m] = P4::load(rq_, vq[m] * SI, r0 * H * DK * SI);
+            R.k[m] = P4::load(rk_, vk[m] * SI, r0 * HKV * DK * SI);
+            if constexpr (!EJK) R.g[m] = Piece4<float>::load(rg_, vq[m] * 4, r0 * H * DK * 4);
         }
-        const int rv = r16 < len ? r16 : 0;
-        R.v = v[((size_t)(c0 + rv) * HKV + hk) * DV + j0 + c16];
-        const int rb = tid < len ? tid : 0;
-        R.b = beta[(size_t)(c0 + rb) * H + h];
-        if constexpr (EJK) R.d = (g ? g : beta)[(size_t)(c0 + rb) * H + h];   // NULL decay: zeroed at use
+        R.v = P4::load1(rv_, (r16 * HKV * DV + c16) * SI, r0 * HKV * DV * SI);
+        R.b = Piece4<float>::load1(rb_, tid * H * 4, r0 * H * 4);
+        if constexpr (EJK) R.d = Piece4<float>::load1(rg_, tid * H * 4, r0 * H * 4);   // NULL decay: zeroed at use
     };
     // chunks loaded ahead: at small dk a chunk computes in less than a memory
     // latency; at large dk two chunks cover it, and more would only queue requests
@@ -367,28 +408,40 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         }
         lds_barrier();
 
-        // ---- U = T' Y: lane j < 16 solves (I + A) u = diag(beta) y for column j
-        if (tid < FC) {
-            const int j = tid;
-            float u[FC], am[FC][FC];
+        // ---- U = T' Y: (I + A) u = diag(beta) y by forward substitution, column j on
+        // the four lanes of quad j of wave 0, rows 4p .. 4p + 3 on its lane p.  At step
+        // s the owner of row s broadcasts u_s within the quad (DPP) and every lane
+        // updates its rows; A is zero on and above the diagonal, so rows r <= s keep
+        // their value without a mask.
+        if (wave == 0) {
+            const int jq = lane >> 2, p = lane & 3;
+            float u[4], am[4][FC];
 #pragma unroll
-            for (int r = 0; r < FC; ++r) u[r] = L.BT[r] * L.YM[r * F16 + j];
-            // A's rows as 16-byte reads, all issued before the substitution
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * p + e;
+                u[e] = L.BT[r] * L.YM[r * F16 + jq];
 #pragma unroll
-            for (int r = 1; r < FC; ++r)
-#pragma unroll
-                for (int s4 = 0; s4 < r; s4 += 4) {
+                for (int s4 = 0; s4 < FC; s4 += 4) {
                     const float4 a4 = *reinterpret_cast<const float4*>(L.AM + r * 20 + s4);
-                    am[r][s4] = a4.x; am[r][s4 + 1] = a4.y; am[r][s4 + 2] = a4.z; am[r][s4 + 3] = a4.w;
+                    am[e][s4] = a4.x; am[e][s4 + 1] = a4.y; am[e][s4 + 2] = a4.z; am[e][s4 + 3] = a4.w;
                 }
-#pragma unroll
-            for (int s = 0; s < FC - 1; ++s) {
-                const float us = u[s];
-#pragma unroll
-                for (int r = s + 1; r < FC; ++r) u[r] = fmaf(-am[r][s], us, u[r]);
             }
+            auto level = [&](auto sc) {
+                constexpr int S = decltype(sc)::value;
+                const float us = quad_bcast<S / 4>(u[S % 4]);
 #pragma unroll
-            for (int r = 0; r < FC; ++r) L.UM[r * F16 + j] = u[r];
+                for (int e = 0; e < 4; ++e) u[e] = fmaf(-am[e][S], us, u[e]);
+            };
+            level(std::integral_constant<int, 0>{});  level(std::integral_constant<int, 1>{});
+            level(std::integral_constant<int, 2>{});  level(std::integral_constant<int, 3>{});
+            level(std::integral_constant<int, 4>{});  level(std::integral_constant<int, 5>{});
+            level(std::integral_constant<int, 6>{});  level(std::integral_constant<int, 7>{});
+            level(std::integral_constant<int, 8>{});  level(std::integral_constant<int, 9>{});
+            level(std::integral_constant<int, 10>{}); level(std::integral_constant<int, 11>{});
+            level(std::integral_constant<int, 12>{}); level(std::integral_constant<int, 13>{});
+            level(std::integral_constant<int, 14>{});
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.UM[(4 * p + e) * F16 + jq] = u[e];
         }
         lds_barrier();
 
@@ -489,7 +542,10 @@ bool chunked_f32_supported(const PrefillArgs& a)
     // float32 inputs at any dk; bf16 inputs below dk = 128 (dk = 128 takes the
     // bf16 MFMA kernel).  KDA needs the gate inputs and lower_bound >= -5 (the
     // factor range above).
-    return dims && (!a.in_bf16 || a.dk < 128) &&
+    // A sequence's rows are addressed with 31-bit byte offsets (T bounds every
+    // sequence's length, packed or not).
+    const bool spans = (long long)a.T * a.H * (a.dk > a.dv ? a.dk : a.dv) * 4 < (1LL << 31);
+    return dims && spans && (!a.in_bf16 || a.dk < 128) &&
            (a.ejk || (a.g != nullptr && a.a_log != nullptr && a.lower_bound >= -5.0f));
 }
 
