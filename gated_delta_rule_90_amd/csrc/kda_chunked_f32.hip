@@ -98,7 +98,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <typename Tin> struct Piece4;
 template <> struct Piece4<float> {
     using type = float4;
-    static __device__ __forceinline__ float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
     static __device__ __forceinline__ float4 load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
     {
         return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -111,7 +110,6 @@ template <> struct Piece4<float> {
 };
 template <> struct Piece4<bf16_t> {
     using type = uint2;
-    static __device__ __forceinline__ uint2 zero() { return make_uint2(0u, 0u); }
     static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
     {
         return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
@@ -261,8 +259,8 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     auto chunk = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
         const int len = min(FC, t1 - c0);   // <= 0 for a padding chunk
-        // ---- prologue from the registers: raw rows to LDS, row norms (RL lanes
-        // per row), the gate cumsum of channel tid, beta; then fetch the next chunk
+        // ---- prologue from the registers: raw q, k rows to LDS, gate activations,
+        // row norms (RL lanes per row), beta; then fetch the next chunk
 #pragma unroll
         for (int m = 0; m < QN; ++m) {
             const int e = tid + m * FT;
