@@ -206,3 +206,22 @@ def test_chunked_float32_arithmetic_bf16_varlen_bitwise():
         on, sn = prefill_gpu(sub)
         np.testing.assert_array_equal(o[:, a:b], on)
         np.testing.assert_array_equal(s[n], sn[0])
+
+
+@pytest.mark.parametrize("dtype,use_chunked", [("f32", True), ("bf16", True), ("f32", False)])
+def test_ejkernel_worked_example_shapes(dtype, use_chunked):
+    """The ejkernel kda_attention example's shapes (tests/golden/ejkernel_example_shapes.json:
+    batch 2, 64 tokens, 8 heads, head_dim 32, beta = sigmoid(N(0,1)), decay of scale -0.01, sign
+    fixed to the documented <= 0) in EJK mode, through the chunked and token-by-token paths,
+    returning the state: output [2, 64, 8, 32] and state [2, 8, 32, 32] against the oracle."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "ejkernel_example_shapes.json")))
+    B, T, H, d = gold["batch"], gold["seq_len"], gold["num_heads"], gold["head_dim"]
+    inp = workloads.prefill_inputs(B, T, H, d, d, seed=2024, dtype=dtype, ejk=True)
+    say("ejkernel example shapes", dtype, "chunked" if use_chunked else "token-by-token")
+    o, s = prefill_gpu(inp, use_chunked=use_chunked)
+    assert list(o.shape) == gold["output_shape"] and list(s.shape) == gold["state_shape"]
+    ro, rs = prefill_oracle(inp)
+    assert rel_l2(s, rs) <= TOL
+    assert rel_l2(o, ro) <= (2e-2 if dtype == "bf16" else TOL)
