@@ -52,27 +52,33 @@
 namespace kda {
 namespace {
 
-constexpr int FC = 16;    // tokens per chunk
+constexpr int FB = 16;    // rows per block (each block has its own decay reference row)
 constexpr int FT = 256;   // threads per workgroup
 constexpr int FJ = 16;    // state columns per workgroup
-constexpr int F16 = FC + 1;
+constexpr int F16 = FJ + 1;   // row stride of [rows][16] tiles
 
-template <int DK>
+// A chunk is NB blocks of 16 rows (NB = 1 or 2).
+template <int DK, int NB>
 struct F32Lds {
-    static constexpr int RS = DK + 1;   // row stride of [16][DK] tiles: rows fall in different banks
-    float QL[FC * RS];    // raw q rows, then qh_r 2^{b_r - b_0} (EJK: qh_r)
-    float KL[FC * RS];    // raw k rows, then kh_r 2^{b_r - b_0} (EJK: kh_r)
-    float KR[FC * RS];    // kh_r 2^{b_0 - b_r} (EJK: kh_r)
-    float GB[FC * RS];    // b_r per channel (log2 units, KDA)
+    static constexpr int FC = FB * NB;
+    static constexpr int FA = FC + 4;    // row stride of A (16-byte aligned rows)
+    static constexpr int FP = FC + 1;    // row stride of P
+    static constexpr int RS = DK + 1;   // row stride of [rows][DK] tiles: rows fall in different banks
+    float QL[FC * RS];    // raw q rows, then qh_r 2^{b_r - b_f} (f: the row's block reference; EJK: qh_r)
+    float KL[FC * RS];    // raw k rows, then kh_r 2^{b_r - b_f} (EJK: kh_r)
+    float KR[FC * RS];    // kh_r 2^{b_f - b_r} (EJK: kh_r)
+    float K1[NB == 2 ? FB * RS : 1];   // block-0 rows referenced to row 16: kh_r 2^{b_16 - b_r} (<= 1)
+    float GB[FC * RS];    // gamma', then b_r per channel (log2 units, KDA)
     float SL[DK * F16];   // the state tile S[i][j]
     float VV[FC * F16];   // the value tile V[s][j]
-    alignas(16) float AM[FC * 20];   // A (strict lower, beta-scaled), 16-byte aligned rows
-    float PM[FC * F16];   // P (lower incl. diagonal)
-    float YM[FC * F16];   // Y = V - Kg S0
+    alignas(16) float AM[FC * FA];   // A (strict lower, beta-scaled)
+    float PM[FC * FP];    // P (lower incl. diagonal)
+    float YM[FC * F16];   // Y = V - Kg S0, then block 1's right-hand side
     float UM[FC * F16];   // U
     float OM[FC * F16];   // O of the chunk, stored by every thread
     float E0[DK];         // 2^{b_0}
-    float NC[DK];         // 2^{b_C - b_0}
+    float E1[DK];         // 2^{b_f} of the last block's reference row f
+    float N1[DK];         // 2^{b_C - b_f} of the last block's reference row f
     float DC[DK];         // 2^{b_C}
     float NQ[FC], NK[FC], BT[FC];   // query scale / norm, key 1 / norm, activated beta
     float EB[FC], EX[FC], EC[FC];   // EJK: 2^{b_r}, 2^{b_{r-1}}, 2^{b_C - b_r}
@@ -152,7 +158,7 @@ __device__ __forceinline__ float lane_group_sum(float x)
     return x;
 }
 
-template <int DK, bool EJK, typename Tin, typename Tout>
+template <int DK, int NB, bool EJK, typename Tin, typename Tout>
 __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ a_log,
@@ -160,15 +166,18 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     int T, int H, int HKV, int DV, float scale, float lower_bound, int l2norm,
     Tout* __restrict__ o, float* __restrict__ final_state)
 {
-    constexpr int RS = F32Lds<DK>::RS;
+    using LT = F32Lds<DK, NB>;
+    constexpr int RS = LT::RS;
+    constexpr int FC = LT::FC, FA = LT::FA, FP = LT::FP;
+    constexpr int FL = FB * (NB - 1);   // the last block's reference row
     constexpr int RL = DK / 4;                 // lanes per row in the q, k loads (4 channels each)
-    constexpr int Q4 = FC * RL;                // float4 pieces of a [16][DK] tile
+    constexpr int Q4 = FC * RL;                // pieces of four channels in a [32][DK] tile
     constexpr int QN = (Q4 + FT - 1) / FT;     // per thread
     static_assert(RL >= 4 && RL <= 32 && FC * DK % FT == 0, "dk in {16, 32, 64, 128}");
-    __shared__ F32Lds<DK> L;
+    __shared__ LT L;
 
     const int tid = threadIdx.x;
-    const int r16 = tid >> 4;   // row of a 16x16 tile (value loads)
+    const int r16 = tid >> 4;   // row of a 16x16 tile (value loads, output stores)
     const int c16 = tid & 15;   // column of a 16x16 tile
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -198,11 +207,11 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         dtb4[j] = (!EJK && dt_bias) ? dt_bias[(size_t)(4 * (tid % RL) + j) * H + h] : 0.f;
 
     // One chunk's inputs as loaded into registers: q, k and (KDA) g as pieces of
-    // four channels (row e / RL, channels 4 (e % RL) ..), v at (row r16,
-    // column c16), beta and the EJK decay of row tid.  The loads go through
-    // buffer resources that end after the sequence's last row, so rows past
-    // the sequence read zeros; each address is a per-lane offset fixed for the
-    // whole sequence plus a per-chunk scalar offset.  The values are masked
+    // four channels (row e / RL, channels 4 (e % RL) ..), v at (rows r16 + 16 hv,
+    // column c16), beta and the EJK decay of row tid.  The loads go
+    // through buffer resources that end after the sequence's last row, so rows
+    // past the sequence read zeros; each address is a per-lane offset fixed for
+    // the whole sequence plus a per-chunk scalar offset.  The values are masked
     // where they are used, so no load is waited for where it is issued and
     // every path issues the same loads (the wait before a chunk's first use
     // then covers only its own).  A sequence's spans fit 31-bit offsets (the
@@ -212,7 +221,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     struct Raw {
         piece_t q[QN], k[QN];
         float4 g[QN];
-        Tin v;
+        Tin v[NB];
         float b, d;
     };
     constexpr int SI = (int)sizeof(Tin);
@@ -243,18 +252,57 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             R.k[m] = P4::load(rk_, vk[m] * SI, r0 * HKV * DK * SI);
             if constexpr (!EJK) R.g[m] = Piece4<float>::load(rg_, vq[m] * 4, r0 * H * DK * 4);
         }
-        R.v = P4::load1(rv_, (r16 * HKV * DV + c16) * SI, r0 * HKV * DV * SI);
+#pragma unroll
+        for (int hv = 0; hv < NB; ++hv)
+            R.v[hv] = P4::load1(rv_, ((r16 + FB * hv) * HKV * DV + c16) * SI, r0 * HKV * DV * SI);
         R.b = Piece4<float>::load1(rb_, tid * H * 4, r0 * H * 4);
         if constexpr (EJK) R.d = Piece4<float>::load1(rg_, tid * H * 4, r0 * H * 4);   // NULL decay: zeroed at use
     };
     // chunks loaded ahead: at small dk a chunk computes in less than a memory
-    // latency; at large dk two chunks cover it, and more would only queue requests
-    constexpr int FD = DK <= 32 ? 4 : 2;
+    // latency (64 tokens ahead); at large dk 32 tokens cover it
+    constexpr int FD = (DK <= 32 ? 4 : 2) / NB;
     Raw ring[FD];
     if (nch > 0) {
 #pragma unroll
         for (int u = 0; u < FD; ++u) load(ring[u], min(u, nch - 1));
     }
+
+    // Forward substitution of one 16-row block on wave 0: column j on the four
+    // lanes of quad j, rows 4p .. 4p + 3 of the block on lane p.  At step s the
+    // owner of row s broadcasts u_s within the quad (DPP) and every lane updates
+    // its rows; A is zero on and above the diagonal, so rows r <= s keep their
+    // value without a mask.  Reads the right-hand side from YM (scaled by beta
+    // for block 0), writes U.
+    auto solve16 = [&](int rb, bool scale_by_beta) {
+        const int jq = lane >> 2, p = lane & 3;
+        float u[4], am[4][FB];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rb + 4 * p + e;
+            u[e] = (scale_by_beta ? L.BT[r] : 1.f) * L.YM[r * F16 + jq];
+#pragma unroll
+            for (int s4 = 0; s4 < FB; s4 += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(L.AM + r * FA + rb + s4);
+                am[e][s4] = a4.x; am[e][s4 + 1] = a4.y; am[e][s4 + 2] = a4.z; am[e][s4 + 3] = a4.w;
+            }
+        }
+        auto level = [&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            const float us = quad_bcast<S / 4>(u[S % 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = fmaf(-am[e][S], us, u[e]);
+        };
+        level(std::integral_constant<int, 0>{});  level(std::integral_constant<int, 1>{});
+        level(std::integral_constant<int, 2>{});  level(std::integral_constant<int, 3>{});
+        level(std::integral_constant<int, 4>{});  level(std::integral_constant<int, 5>{});
+        level(std::integral_constant<int, 6>{});  level(std::integral_constant<int, 7>{});
+        level(std::integral_constant<int, 8>{});  level(std::integral_constant<int, 9>{});
+        level(std::integral_constant<int, 10>{}); level(std::integral_constant<int, 11>{});
+        level(std::integral_constant<int, 12>{}); level(std::integral_constant<int, 13>{});
+        level(std::integral_constant<int, 14>{});
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.UM[(rb + 4 * p + e) * F16 + jq] = u[e];
+    };
 
     auto chunk = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
@@ -271,9 +319,8 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             if (e < Q4) {
                 float* pq = L.QL + row * RS + 4 * c4;
                 float* pk = L.KL + row * RS + 4 * c4;
-                const float4 xq = wq, xk = wk;
-                pq[0] = xq.x; pq[1] = xq.y; pq[2] = xq.z; pq[3] = xq.w;
-                pk[0] = xk.x; pk[1] = xk.y; pk[2] = xk.z; pk[3] = xk.w;
+                pq[0] = wq.x; pq[1] = wq.y; pq[2] = wq.z; pq[3] = wq.w;
+                pk[0] = wk.x; pk[1] = wk.y; pk[2] = wk.z; pk[3] = wk.w;
                 if constexpr (!EJK) {
                     // gamma' = lb * log2(e) * sigmoid(exp(a_log) (g + dt_bias)), element by
                     // element here, where every lane holds four; padded rows 0
@@ -293,7 +340,9 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.NK[row] = l2norm ? __builtin_amdgcn_rsqf(sk + kNormEps) : 1.0f;
             }
         }
-        L.VV[r16 * F16 + c16] = (r16 < len) ? to_f32(R.v) : 0.f;
+#pragma unroll
+        for (int hv = 0; hv < NB; ++hv)
+            L.VV[(r16 + FB * hv) * F16 + c16] = (r16 + FB * hv < len) ? to_f32(R.v[hv]) : 0.f;
         if (tid < FC) {
             // beta = 1 / (1 + 2^{-logit log2(e)}); R.b was loaded by every lane
             L.BT[tid] = (tid < len) ? (EJK ? R.b : __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * R.b))) : 0.f;
@@ -319,28 +368,31 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         load(R, min(c + FD, nch - 1));   // past the end this reloads the last chunk
         lds_barrier();
 
-        // ---- lane i < dk: the gate cumsum of channel i down the 16 rows
+        // ---- lane i < dk: the gate cumsum of channel i down the chunk's rows
         if constexpr (!EJK) {
             if (tid < DK) {
                 const int i = tid;
                 float gm[FC];
 #pragma unroll
                 for (int r = 0; r < FC; ++r) gm[r] = L.GB[r * RS + i];
-                float b = 0.f, b0 = 0.f;
+                float b = 0.f, b0 = 0.f, bl = 0.f;
 #pragma unroll
                 for (int r = 0; r < FC; ++r) {
                     b += gm[r];
                     if (r == 0) b0 = b;
+                    if (r == FL) bl = b;
                     L.GB[r * RS + i] = b;
                 }
                 L.E0[i] = __builtin_amdgcn_exp2f(b0);
-                L.NC[i] = __builtin_amdgcn_exp2f(b - b0);
+                L.E1[i] = __builtin_amdgcn_exp2f(bl);
+                L.N1[i] = __builtin_amdgcn_exp2f(b - bl);
                 L.DC[i] = __builtin_amdgcn_exp2f(b);
             }
             lds_barrier();
         }
 
-        // ---- normalised rows with the decay factors L = 2^{b_r - b_0}, R = 1 / L
+        // ---- normalised rows with the decay factors of their block: L = 2^{b_r - b_f},
+        // R = 1 / L (f = 0 or 16); block-0 keys also referenced to row 16 (K1 <= 1)
 #pragma unroll
         for (int m = 0; m < FC * DK / FT; ++m) {
             const int e = tid + m * FT;
@@ -352,104 +404,127 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.KL[r * RS + i] = kh;
                 L.KR[r * RS + i] = kh;
             } else {
-                const float d = L.GB[r * RS + i] - L.GB[i];   // b_r - b_0 <= 0
+                const float br = L.GB[r * RS + i];
+                const float d = br - L.GB[(r < FB ? 0 : FB) * RS + i];   // b_r - b_f <= 0
                 const float lf = __builtin_amdgcn_exp2f(d);
                 L.QL[r * RS + i] = qh * lf;
                 L.KL[r * RS + i] = kh * lf;
                 L.KR[r * RS + i] = kh * __builtin_amdgcn_exp2f(-d);
+                if constexpr (NB == 2)
+                    if (r < FB) L.K1[r * RS + i] = kh * __builtin_amdgcn_exp2f(L.GB[FB * RS + i] - br);
             }
         }
         lds_barrier();
 
-        // ---- the four products over dk, one per wave (K = dk in MFMA steps of 4):
-        //   wave 0: A = KL KR^T,  wave 1: P = QL KR^T,  wave 2: Qg S0 (kept in
-        //   registers for O),  wave 3: Y = V - Kg S0, with Qg, Kg = 2^{b_0} QL, KL
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // ---- the products over dk (K = dk in MFMA steps of 4), waves in parallel:
+        //   wave 0: the blocks (0,0), (1,1), (1,0) of A,  wave 1: the same of P,
+        //   wave 2: Qg S0 for both row blocks (kept in registers for O),
+        //   wave 3: Y = V - Kg S0 for both row blocks.
+        // Block (1,0) pairs rows referenced to row 16 with block-0 keys referenced to
+        // row 16 too, so both factors are at most 1.
+        f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
         if (wave <= 1) {
             const float* X = (wave == 0) ? L.KL : L.QL;
-#pragma unroll 8
-            for (int k0 = 0; k0 < DK; k0 += 4)
-                acc = mfma4(X[lm * RS + k0 + lk], L.KR[lm * RS + k0 + lk], acc);
+            const float* RB = (EJK || NB == 1) ? L.KR : L.K1;   // right operand of block (1,0)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = ro + e, s = lm;   // acc[e] = (row r, column s)
-                float x = acc[e];
-                if (wave == 0) {
-                    if constexpr (EJK) x *= (s < r) ? __builtin_amdgcn_exp2f(L.BX[r] - L.BR[s]) : 0.f;
-                    L.AM[r * 20 + s] = (s < r) ? L.BT[r] * x : 0.f;
-                } else {
-                    if constexpr (EJK) x *= (s <= r) ? __builtin_amdgcn_exp2f(L.BR[r] - L.BR[s]) : 0.f;
-                    L.PM[r * F16 + s] = (s <= r) ? x : 0.f;
+            for (int blk = 0; blk < (NB == 2 ? 3 : 1); ++blk) {
+                const int I = blk == 0 ? 0 : 1, J = blk == 1 ? 1 : 0;   // (0,0), (1,1), (1,0)
+                const float* RR = (blk == 2) ? RB : L.KR;
+                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+                for (int k0 = 0; k0 < DK; k0 += 4)
+                    acc = mfma4(X[(FB * I + lm) * RS + k0 + lk], RR[(FB * J + lm) * RS + k0 + lk], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = FB * I + ro + e, s = FB * J + lm;   // acc[e] = (row r, column s)
+                    float x = acc[e];
+                    if (wave == 0) {
+                        if constexpr (EJK) x *= (s < r) ? __builtin_amdgcn_exp2f(L.BX[r] - L.BR[s]) : 0.f;
+                        L.AM[r * FA + s] = (s < r) ? L.BT[r] * x : 0.f;
+                    } else {
+                        if constexpr (EJK) x *= (s <= r) ? __builtin_amdgcn_exp2f(L.BR[r] - L.BR[s]) : 0.f;
+                        L.PM[r * FP + s] = (s <= r) ? x : 0.f;
+                    }
                 }
             }
         } else {
+            // A operand: Qg (wave 2) or Kg (wave 3) = 2^{b_f} X per channel (KDA);
+            // the EJK row factor is applied to the result
             const float* X = (wave == 2) ? L.QL : L.KL;
 #pragma unroll 8
             for (int k0 = 0; k0 < DK; k0 += 4) {
                 const int kk = k0 + lk;
-                const float a = EJK ? X[lm * RS + kk] : L.E0[kk] * X[lm * RS + kk];
-                acc = mfma4(a, L.SL[kk * F16 + lm], acc);
+                const float a0 = EJK ? X[lm * RS + kk] : L.E0[kk] * X[lm * RS + kk];
+                const float sb = L.SL[kk * F16 + lm];
+                acc0 = mfma4(a0, sb, acc0);
+                if constexpr (NB == 2) {
+                    const float a1 = EJK ? X[(FB + lm) * RS + kk] : L.E1[kk] * X[(FB + lm) * RS + kk];
+                    acc1 = mfma4(a1, sb, acc1);
+                }
             }
             if (wave == 2) {
                 if constexpr (EJK) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] *= L.EB[ro + e];
+                    for (int e = 0; e < 4; ++e) {
+                        acc0[e] *= L.EB[ro + e];
+                        if constexpr (NB == 2) acc1[e] *= L.EB[FB + ro + e];
+                    }
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = ro + e;
-                    const float z = EJK ? L.EX[r] * acc[e] : acc[e];
-                    L.YM[r * F16 + lm] = L.VV[r * F16 + lm] - z;
+                    const int r0 = ro + e;
+                    const float z0 = EJK ? L.EX[r0] * acc0[e] : acc0[e];
+                    L.YM[r0 * F16 + lm] = L.VV[r0 * F16 + lm] - z0;
+                    if constexpr (NB == 2) {
+                        const int r1 = FB + ro + e;
+                        const float z1 = EJK ? L.EX[r1] * acc1[e] : acc1[e];
+                        L.YM[r1 * F16 + lm] = L.VV[r1 * F16 + lm] - z1;
+                    }
                 }
             }
         }
         lds_barrier();
 
-        // ---- U = T' Y: (I + A) u = diag(beta) y by forward substitution, column j on
-        // the four lanes of quad j of wave 0, rows 4p .. 4p + 3 on its lane p.  At step
-        // s the owner of row s broadcasts u_s within the quad (DPP) and every lane
-        // updates its rows; A is zero on and above the diagonal, so rows r <= s keep
-        // their value without a mask.
+        // ---- U: (I + A) U = diag(beta) Y blockwise on wave 0 (its LDS operations
+        // take effect in issue order): block 0, then block 1's right-hand side
+        // beta Y_1 - A_10 U_0 on MFMA, then block 1
         if (wave == 0) {
-            const int jq = lane >> 2, p = lane & 3;
-            float u[4], am[4][FC];
+            solve16(0, true);
+        }
+        if constexpr (NB == 2) {
+          if (wave == 0) {
+            f32x4_t y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 4 * p + e;
-                u[e] = L.BT[r] * L.YM[r * F16 + jq];
-#pragma unroll
-                for (int s4 = 0; s4 < FC; s4 += 4) {
-                    const float4 a4 = *reinterpret_cast<const float4*>(L.AM + r * 20 + s4);
-                    am[e][s4] = a4.x; am[e][s4 + 1] = a4.y; am[e][s4 + 2] = a4.z; am[e][s4 + 3] = a4.w;
-                }
+                const int r = FB + ro + e;
+                y[e] = L.BT[r] * L.YM[r * F16 + lm];
             }
-            auto level = [&](auto sc) {
-                constexpr int S = decltype(sc)::value;
-                const float us = quad_bcast<S / 4>(u[S % 4]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) u[e] = fmaf(-am[e][S], us, u[e]);
-            };
-            level(std::integral_constant<int, 0>{});  level(std::integral_constant<int, 1>{});
-            level(std::integral_constant<int, 2>{});  level(std::integral_constant<int, 3>{});
-            level(std::integral_constant<int, 4>{});  level(std::integral_constant<int, 5>{});
-            level(std::integral_constant<int, 6>{});  level(std::integral_constant<int, 7>{});
-            level(std::integral_constant<int, 8>{});  level(std::integral_constant<int, 9>{});
-            level(std::integral_constant<int, 10>{}); level(std::integral_constant<int, 11>{});
-            level(std::integral_constant<int, 12>{}); level(std::integral_constant<int, 13>{});
-            level(std::integral_constant<int, 14>{});
+            for (int k0 = 0; k0 < FB; k0 += 4)
+                y = mfma4(-L.AM[(FB + lm) * FA + k0 + lk], L.UM[(k0 + lk) * F16 + lm], y);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.UM[(4 * p + e) * F16 + jq] = u[e];
+            for (int e = 0; e < 4; ++e) L.YM[(FB + ro + e) * F16 + lm] = y[e];
+            solve16(FB, false);
+          }
         }
         lds_barrier();
 
         // ---- O = Qg S0 + P U (wave 2), S = Diag(2^{b_C}) S0 + Kc^T U (16-row tiles over the waves)
         if (wave == 2) {
 #pragma unroll
-            for (int k0 = 0; k0 < FC; k0 += 4)
-                acc = mfma4(L.PM[lm * F16 + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc);
+            for (int k0 = 0; k0 < FB; k0 += 4)
+                acc0 = mfma4(L.PM[lm * FP + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc0);
+            if constexpr (NB == 2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.OM[(ro + e) * F16 + lm] = acc[e];
+                for (int k0 = 0; k0 < FC; k0 += 4)
+                    acc1 = mfma4(L.PM[(FB + lm) * FP + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc1);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                L.OM[(ro + e) * F16 + lm] = acc0[e];
+                if constexpr (NB == 2) L.OM[(FB + ro + e) * F16 + lm] = acc1[e];
+            }
         }
 #pragma unroll
         for (int t = wave; t < DK / 16; t += 4) {
@@ -460,30 +535,37 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 const int i = ib + ro + e;
                 sc[e] = (EJK ? L.DC[0] : L.DC[i]) * L.SL[i * F16 + lm];
             }
-            const int ia = ib + lm;   // A operand row: Kc^T[ia][s] = Kc[s][ia] = 2^{b_C - b_0} KR[s][ia]
+            // A operand: Kc^T[ia][s] = 2^{b_C - b_s} kh_s = N1 K1[s] (block 0) or N1 KR[s] (block 1)
+            const int ia = ib + lm;
 #pragma unroll
             for (int k0 = 0; k0 < FC; k0 += 4) {
                 const int s = k0 + lk;
-                const float kc = (EJK ? L.EC[s] : L.NC[ia]) * L.KR[s * RS + ia];
+                float kc;
+                if constexpr (EJK) kc = L.EC[s] * L.KR[s * RS + ia];
+                else kc = L.N1[ia] * ((NB == 2 && k0 < FB) ? L.K1[s * RS + ia] : L.KR[s * RS + ia]);
                 sc = mfma4(kc, L.UM[s * F16 + lm], sc);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) L.SL[(ib + ro + e) * F16 + lm] = sc[e];
         }
         lds_barrier();
-        // O row r16, column c16, through a buffer resource that ends after the
-        // chunk's last row: the buffer unit drops the stores of padded rows, so
-        // every lane issues the same store
+        // O rows r16 and r16 + 16, column c16, through a buffer resource that ends
+        // after the chunk's last row: the buffer unit drops the stores of padded
+        // rows, so every lane issues the same stores
         {
             Tout* obase = o + ((size_t)c0 * H + h) * DV + j0;
             const int rec = len > 0 ? ((len - 1) * H * DV + FJ) * (int)sizeof(Tout) : 0;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, 0, rec, 0x00020000);
-            const int off = (r16 * H * DV + c16) * (int)sizeof(Tout);
-            const Tout val = from_f32<Tout>(L.OM[r16 * F16 + c16]);
-            if constexpr (sizeof(Tout) == 4)
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, off, 0, 0);
-            else
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, val), rs, off, 0, 0);
+#pragma unroll
+            for (int hv = 0; hv < NB; ++hv) {
+                const int r = r16 + FB * hv;
+                const int off = (r * H * DV + c16) * (int)sizeof(Tout);
+                const Tout val = from_f32<Tout>(L.OM[r * F16 + c16]);
+                if constexpr (sizeof(Tout) == 4)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, val), rs, off, 0, 0);
+            }
         }
     };
     // Unrolled by the ring depth, so that every ring slot is a fixed set of
@@ -513,12 +595,14 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     const Tin* k = static_cast<const Tin*>(a.k);
     const Tin* v = static_cast<const Tin*>(a.v);
     Tout* o = static_cast<Tout*>(a.o);
+    // two 16-row blocks per chunk at small dk, where the per-chunk latency dominates
+    constexpr int NB = DK <= 32 ? 2 : 1;
     if (a.ejk)
-        hipLaunchKernelGGL((chunk_f32_kernel<DK, true, Tin, Tout>), grid, dim3(FT), 0, stream, q, k, v, a.g,
+        hipLaunchKernelGGL((chunk_f32_kernel<DK, NB, true, Tin, Tout>), grid, dim3(FT), 0, stream, q, k, v, a.g,
                            a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
                            a.lower_bound, (int)a.l2norm, o, a.final_state);
     else
-        hipLaunchKernelGGL((chunk_f32_kernel<DK, false, Tin, Tout>), grid, dim3(FT), 0, stream, q, k, v, a.g,
+        hipLaunchKernelGGL((chunk_f32_kernel<DK, NB, false, Tin, Tout>), grid, dim3(FT), 0, stream, q, k, v, a.g,
                            a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
                            a.lower_bound, (int)a.l2norm, o, a.final_state);
     return hipGetLastError();

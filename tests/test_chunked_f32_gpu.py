@@ -91,7 +91,7 @@ def test_chunked_f32_split_at_chunk_boundary_bitwise():
     inp = workloads.prefill_inputs(2, 80, 2, 64, 32, seed=340, dtype="f32", init_state=True)
     say("chunked f32 split")
     o, s = prefill_gpu(inp)
-    cut = 48   # a multiple of the 16-token chunk
+    cut = 64   # a multiple of the kernel's 32-token chunk
     part = lambda x, a, b: x[:, a:b]
     first = workloads.PrefillInputs(part(inp.q, 0, cut), part(inp.k, 0, cut), part(inp.v, 0, cut),
                                     part(inp.g, 0, cut), part(inp.beta, 0, cut), inp.a_log, inp.dt_bias,
