@@ -15,13 +15,18 @@
 //     O = Qg S0 + P U,  S = Diag(2^{b_C}) S0 + Kc^T U
 // with Kg_s = 2^{b_s} kh_s, Qg_r = 2^{b_r} qh_r, Kc_s = 2^{b_C - b_s} kh_s.
 //
-// Chunks are C = 16 tokens.  With lower_bound >= -5 a channel's log-decay
-// over 16 tokens is at most 16 * 5 * log2(e) < 116 in log2 units, so one
-// reference row per chunk keeps every factor inside float32's normal range:
-//     L_r = 2^{b_r - b_0} in [2^-116, 1],   R_s = 2^{b_0 - b_s} in [1, 2^116]
+// A chunk is one 16-row block at dk >= 64 and two at dk <= 32 (where the
+// per-chunk latency dominates).  With lower_bound >= -5 a channel's log-decay
+// over 16 tokens is at most 16 * 5 * log2(e) < 116 in log2 units, so a
+// reference row per block (its first row f) keeps every factor inside
+// float32's normal range:
+//     L_r = 2^{b_r - b_f} in [2^-116, 1],   R_s = 2^{b_f - b_s} in [1, 2^116]
 // and 2^{b_r - b_s} = L_r R_s for the kept pairs (s <= r) is a product of
-// two normal numbers, at most 1.  Kc = 2^{b_C - b_0} R (at most 1 per term)
-// and Qg = 2^{b_0} L keep every summand of the state products bounded.
+// two normal numbers, at most 1.  The off-diagonal block of a two-block chunk
+// pairs rows referenced to row 16 with block-0 keys referenced to row 16 too
+// (2^{b_16 - b_s} <= 1), so both factors are at most 1 and an underflow is of
+// a value below 2^-126.  Kc = 2^{b_C - b_16} (R or the row-16-referenced
+// keys) and Qg = 2^{b_f} L keep every summand of the state products bounded.
 //
 // EJK mode (scalar per-head decay d_t, beta used as given, residual against
 // the undecayed state): A_rs carries 2^{b_{r-1} - b_s} and Kg_r = 2^{b_{r-1}}
@@ -30,18 +35,20 @@
 //
 // Work split: one 256-thread workgroup per (sequence, head, 16 state
 // columns); the state tile [dk][16] stays in LDS in float32.  Per chunk:
-//   1. the raw rows go to LDS; row norms are summed from the load registers;
-//   2. lanes i < dk run the gate cumsum of channel i down the 16 rows;
+//   1. the raw q, k rows go to LDS; gate activations element by element; row
+//      norms summed from the load registers;
+//   2. lanes i < dk run the gate cumsum of channel i down the chunk's rows;
 //   3. every thread scales its elements of q, k by the norms and decay factors;
-//   4. the four contractions over dk (A, P, Qg S0, Kg S0) run on 16x16x4
-//      float32 MFMA, one per wave and in parallel;
-//   5. 16 lanes solve (I + A) U = diag(beta) Y by forward substitution;
-//   6. O and the new state are MFMA products with K = 16.
+//   4. the contractions over dk (the blocks of A, of P, Qg S0, Kg S0) run on
+//      16x16x4 float32 MFMA, one kind per wave and in parallel;
+//   5. one wave solves (I + A) U = diag(beta) Y by forward substitution, 16
+//      rows at a time (the coupling of the second block on MFMA);
+//   6. O and the new state are MFMA products with K = the chunk length.
 // The column-independent quantities (prologue, A, P) are recomputed by each
 // column tile, which is cheap beside the state products at dk <= 128.  The
-// inputs of the next chunks (four at dk <= 32, two above) are loaded into a
-// register ring while the current one computes: at small dk a chunk takes
-// less than a memory latency.  Rows past a sequence's end are padded with
+// inputs of the next chunks (64 tokens ahead at dk <= 32, 32 above) are
+// loaded into a register ring while the current one computes: at small dk a
+// chunk takes less than a memory latency.  Rows past a sequence's end are padded with
 // exact neutral values (q = k = v = 0, gamma = 0, beta = 0) and never stored,
 // so a packed batch equals each sequence run alone, bit for bit.
 #include <type_traits>

@@ -88,8 +88,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *                  MFMA chunked kernel it must be >= -5 (the kda_tkg documented
  *                  range [-5, 0]), else KDA_EUNSUPPORTED
  *   chunk_size     64 (the ejkernel default) when KDA_CHUNKED is set; the
- *                  float32 chunked kernel computes the same result in chunks
- *                  of 16 (see Routing)
+ *                  float32-arithmetic chunked kernel computes the same result
+ *                  in chunks of 16 or 32 (see Routing)
  *   o              out_dtype; KDA_BF16 output needs bf16 input
  *   final_state    [N, H, dk, dv] float32 or NULL (return_state = False);
  *                  may alias initial_state exactly (in-place carry)
@@ -105,7 +105,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *     needs q, k, v, o and (KDA) g 16-byte aligned (KDA_EINVAL otherwise);
  *   - KDA_CHUNKED with float32 inputs (any dk) or bf16 inputs with dk < 128
  *     runs the chunked kernel that computes in float32 (float32 MFMA,
- *     16-token chunks: the chunking changes rounding only) when q, k and
+ *     chunks of 32 tokens at dk <= 32 and 16 above: the chunking changes
+ *     rounding only) when q, k and
  *     (KDA) g are 16-byte aligned and, in KDA mode, lower_bound >= -5 (its
  *     decay factors over 16 tokens then stay inside float32's normal range);
  *   - every other combination runs the float32 token-by-token kernel, which
