@@ -908,7 +908,7 @@ template <int NJB, typename Tout>
 __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ init, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ off, const int32_t* __restrict__ order, int N, int T, int H, int HKV, int DV,
-    const unsigned char* __restrict__ ws, Tout* __restrict__ o, float* __restrict__ final_state)
+    int nslots, const unsigned char* __restrict__ ws, Tout* __restrict__ o, float* __restrict__ final_state)
 {
     using Sh = ScanShape<NJB>;
     constexpr int DVT = Sh::DVT;
@@ -943,8 +943,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
 
     int t_begin, t_end;
     seq_bounds(cu, n, T, t_begin, t_end);
-    const int nch = (t_end - t_begin + C - 1) / C;
     const int slot0 = off ? off[n] : n * ((T + C - 1) / C);
+    // Valid cu_seqlens never need the clamp: a packed batch has at most T / C + N
+    // chunks.  Overlapping ranges (a decreasing pair) can count more; their
+    // chunks past the workspace's slots are not read (those results are
+    // undefined, the memory accesses stay inside the buffers).
+    const int nch = max(0, min((t_end - t_begin + C - 1) / C, nslots - slot0));
 
     // state: rows [32I, 32I+32) x this wave's NJW column blocks
     f32x4_t S[2][NJW];
@@ -986,7 +990,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     using Part2 = std::integral_constant<int, 2>;
     auto step = [&](const Frags<NJB>& cur, Frags<NJB>& nxt, int c) {
         const int c0 = t_begin + c * C;
-        const int len = min(C, t_end - c0);
+        // a step past the last chunk (the padding, or the clamp above) has no rows
+        const int len = c < nch ? min(C, t_end - c0) : 0;
         prefetch(Part0{}, nxt, c + 1);
         // V tile, transposed: VT[j][s]
 #pragma unroll
@@ -1080,8 +1085,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
         __builtin_amdgcn_sched_barrier(0);
         prefetch(Part2{}, fa, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // the chunk count is padded to even; a step past the end stores nothing
-        // and leaves the state as it is
+        // the chunk count is padded to even; a step past the end (len 0) stores
+        // nothing and leaves the state as it is
         for (int c = 0; c < nch; c += 2) {
             step(fa, fb, c);
             step(fb, fa, c + 1);
@@ -1167,13 +1172,13 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     Tout* oo = static_cast<Tout*>(a.o);
     if (njb == 4)
         hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.Hkv, a.dv, recs, oo, a.final_state);
+                           order, a.N, a.T, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
     else if (njb == 2)
         hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.Hkv, a.dv, recs, oo, a.final_state);
+                           order, a.N, a.T, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
     else
         hipLaunchKernelGGL((chunk_scan_kernel<1, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.Hkv, a.dv, recs, oo, a.final_state);
+                           order, a.N, a.T, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
     return hipGetLastError();
 }
 

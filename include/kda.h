@@ -28,7 +28,9 @@
  *    call is made and enqueue nothing.  Device-side values are not
  *    inspected: NaN/Inf propagate, and out-of-range cu_seqlens entries are
  *    clamped to [0, T] (a decreasing pair is an empty sequence) so they can
- *    never address memory outside the buffers.
+ *    never address memory outside the buffers.  Ranges that overlap are
+ *    memory-safe too, but their outputs and states are then unspecified
+ *    (several sequences write the same rows).
  *  - kda_last_error() returns a thread-local message for the last non-OK
  *    status of the calling thread.  The library holds no other mutable state
  *    and is re-entrant; calls on one stream execute in order.
