@@ -287,10 +287,11 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=Fals
                            cu, scale=inp.scale, lower_bound=inp.lower_bound, ejk=inp.ejk,
                            use_chunked=use_chunked, out=out, final_state=fin)
 
-    # bf16 inputs: the MFMA chunked kernel; float32 inputs: the token-by-token
-    # kernel unless use_chunked asks for the float32 chunked one
+    # bf16 inputs: the chunked kernels (the MFMA one at dk = 128, the float32 one
+    # below); float32 inputs: the token-by-token kernel unless use_chunked asks
+    # for the float32 chunked one
     chunked = (inp.dtype == "bf16") if use_chunked is None else use_chunked
-    mfma = chunked and inp.dtype == "bf16"
+    mfma = chunked and inp.dtype == "bf16" and dk == 128
     for i in range(warmup):
         call(i, use_chunked=chunked)
     torch.cuda.synchronize()
