@@ -397,9 +397,9 @@ def bench_configs(steps, warmup):
                                                note="64 dependent token steps per call: latency bound; "
                                                     "ms_per_call includes the host's per-call overhead, "
                                                     "graph_ms_per_call is the device time")
-    # the same workload through the float32 chunked kernel (4 chunks of 16 tokens)
+    # the same workload through the float32 chunked kernel (2 chunks of 32 tokens)
     out["chunked_fp32_b1_t64_h2_d16"] = dict(_prefill_run(inp, 10 * steps, warmup, graph=True, use_chunked=True),
-                                             note="4 dependent 16-token chunks per call; graph_ms_per_call "
+                                             note="2 dependent 32-token chunks per call; graph_ms_per_call "
                                                   "is the device time")
     # a larger float32 prefill on both float32 kernels
     inp = workloads.prefill_fp32_b1_t4096_h16_d128()
@@ -421,7 +421,9 @@ def bench_configs(steps, warmup):
     res = _prefill_run(workloads.prefill_grouped_b4_t4096_h16_hkv4_d128(), steps, warmup, nsets=2)
     out["prefill_grouped_b4_t4096_h16_hkv4_d128"] = res
     gc.collect()
-    _, dres = _decode_run(workloads.decode_grouped_b64_h32_hkv8_d128(), steps, warmup)
+    # a decode step takes ~50 us: 20x the steps of the prefill configs, so that the
+    # mean is not set by the first few calls
+    _, dres = _decode_run(workloads.decode_grouped_b64_h32_hkv8_d128(), 20 * steps, 2 * warmup)
     out["decode_grouped_b64_h32_hkv8_d128"] = {
         "steps_per_s": round(dres["steps_per_s"], 2), "ms_per_step": round(dres["ms"], 5),
         "alg_bytes": dres["bytes"], "hbm_frac": dres["roofline"]["frac"]}
