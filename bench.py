@@ -455,7 +455,7 @@ def main():
                     help="run a 256 MiB device copy first (profiler counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the KDA path runs on one GPU only (asked for --gpus {args.gpus}); "
               "the KDA kernels use no collectives and the pass does not shard", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -357,7 +357,7 @@ hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream)
 
 }  // namespace
 
-// One object per key dimension (KDA_RECURRENT_DK set by the build), so the
+// One object per key dimension (KDA_RECURRENT_DK set by build.py), so the
 // instantiations compile in parallel; the dispatch over dk is in kda_api.cpp.
 #ifndef KDA_RECURRENT_DK
 #error "build kda_recurrent.hip with -DKDA_RECURRENT_DK=16, 32, 64 or 128"
