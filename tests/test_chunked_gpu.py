@@ -6,8 +6,9 @@ chunk boundary with state passthrough must equal the unsplit run bitwise."""
 import numpy as np
 import pytest
 
+import gated_delta_rule_90_amd as kda
 from gated_delta_rule_90_amd import workloads
-from tests._common import prefill_gpu, prefill_oracle, rel_l2, say
+from tests._common import dev, prefill_gpu, prefill_oracle, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -120,6 +121,29 @@ def test_chunked_split_at_chunk_boundary_is_bitwise():
     o2, s2 = prefill_gpu(part(cut, 384, s1))
     np.testing.assert_array_equal(np.concatenate([o1, o2], axis=1), o)
     np.testing.assert_array_equal(s2, s)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_chunked_in_place_state_carry(packed):
+    """initial_state passed again as final_state: the carried state and the output
+    equal the out-of-place call bit for bit (each scan workgroup reads its state
+    tile before it writes the same tile)."""
+    import torch
+    if packed:
+        inp = workloads.prefill_inputs(1, 0, 4, 128, 128, seed=710, lengths=[70, 0, 200, 64], init_state=True)
+    else:
+        inp = workloads.prefill_inputs(3, 150, 4, 128, 128, seed=711, init_state=True)
+    say("chunked in-place state carry", "packed" if packed else "dense")
+    o_ref, s_ref = prefill_gpu(inp)
+    bf, f = torch.bfloat16, torch.float32
+    st = dev(inp.initial_state, f)
+    o, fs = kda.prefill(dev(inp.q, bf), dev(inp.k, bf), dev(inp.v, bf), dev(inp.g, f), dev(inp.beta, f),
+                        dev(inp.a_log, f), dev(inp.dt_bias, f), st, dev(inp.cu_seqlens, torch.int32),
+                        scale=inp.scale, lower_bound=inp.lower_bound, return_state=True, final_state=st)
+    torch.cuda.synchronize()
+    assert fs is st
+    np.testing.assert_array_equal(o.float().cpu().numpy(), o_ref)
+    np.testing.assert_array_equal(st.cpu().numpy(), s_ref)
 
 
 def test_chunked_matches_recurrent_kernel():
