@@ -40,7 +40,8 @@
 //   2. lanes i < dk run the gate cumsum of channel i down the chunk's rows;
 //   3. every thread scales its elements of q, k by the norms and decay factors;
 //   4. the contractions over dk (the blocks of A, of P, Qg S0, Kg S0) run on
-//      16x16x4 float32 MFMA, one kind per wave and in parallel;
+//      16x16x4 float32 MFMA, one kind per wave and in parallel, with the row
+//      operands read four channels (16 bytes) per lane;
 //   5. one wave solves (I + A) U = diag(beta) Y by forward substitution, 16
 //      rows at a time (the coupling of the second block on MFMA);
 //   6. O and the new state are MFMA products with K = the chunk length.
@@ -70,7 +71,7 @@ struct F32Lds {
     static constexpr int FC = FB * NB;
     static constexpr int FA = FC + 4;    // row stride of A (16-byte aligned rows)
     static constexpr int FP = FC + 1;    // row stride of P
-    static constexpr int RS = DK + 1;   // row stride of [rows][DK] tiles: rows fall in different banks
+    static constexpr int RS = DK + 4;   // row stride of [rows][DK] tiles: 16-byte rows, 16 rows in 16 distinct bank groups
     float QL[FC * RS];    // raw q rows, then qh_r 2^{b_r - b_f} (f: the row's block reference; EJK: qh_r)
     float KL[FC * RS];    // raw k rows, then kh_r 2^{b_r - b_f} (EJK: kh_r)
     float KR[FC * RS];    // kh_r 2^{b_f - b_r} (EJK: kh_r)
@@ -83,8 +84,8 @@ struct F32Lds {
     float YM[FC * F16];   // Y = V - Kg S0, then block 1's right-hand side
     float UM[FC * F16];   // U
     float OM[FC * F16];   // O of the chunk, stored by every thread
-    float E0[DK];         // 2^{b_0}
-    float E1[DK];         // 2^{b_f} of the last block's reference row f
+    alignas(16) float E0[DK];   // 2^{b_0}
+    alignas(16) float E1[DK];   // 2^{b_f} of the last block's reference row f
     float N1[DK];         // 2^{b_C - b_f} of the last block's reference row f
     float DC[DK];         // 2^{b_C}
     float NQ[FC], NK[FC], BT[FC];   // query scale / norm, key 1 / norm, activated beta
@@ -438,9 +439,18 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 const int I = blk == 0 ? 0 : 1, J = blk == 1 ? 1 : 0;   // (0,0), (1,1), (1,0)
                 const float* RR = (blk == 2) ? RB : L.KR;
                 f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-                for (int k0 = 0; k0 < DK; k0 += 4)
-                    acc = mfma4(X[(FB * I + lm) * RS + k0 + lk], RR[(FB * J + lm) * RS + k0 + lk], acc);
+                // at step j of a 16-channel block k0, lane group lk supplies channel
+                // k0 + 4 lk + j: every channel once, and both operands (rows over the
+                // channels) are read four channels at a time
+#pragma unroll 4
+                for (int k0 = 0; k0 < DK; k0 += 16) {
+                    const float4 xa = *reinterpret_cast<const float4*>(X + (FB * I + lm) * RS + k0 + 4 * lk);
+                    const float4 xb = *reinterpret_cast<const float4*>(RR + (FB * J + lm) * RS + k0 + 4 * lk);
+                    acc = mfma4(xa.x, xb.x, acc);
+                    acc = mfma4(xa.y, xb.y, acc);
+                    acc = mfma4(xa.z, xb.z, acc);
+                    acc = mfma4(xa.w, xb.w, acc);
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = FB * I + ro + e, s = FB * J + lm;   // acc[e] = (row r, column s)
@@ -458,15 +468,26 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             // A operand: Qg (wave 2) or Kg (wave 3) = 2^{b_f} X per channel (KDA);
             // the EJK row factor is applied to the result
             const float* X = (wave == 2) ? L.QL : L.KL;
-#pragma unroll 8
-            for (int k0 = 0; k0 < DK; k0 += 4) {
-                const int kk = k0 + lk;
-                const float a0 = EJK ? X[lm * RS + kk] : L.E0[kk] * X[lm * RS + kk];
-                const float sb = L.SL[kk * F16 + lm];
-                acc0 = mfma4(a0, sb, acc0);
+            // channels in the order of the A and P products: k0 + 4 lk + j at step j
+#pragma unroll 4
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+                const int kq = k0 + 4 * lk;
+                const float4 x0 = *reinterpret_cast<const float4*>(X + lm * RS + kq);
+                const float4 e0 = EJK ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(L.E0 + kq);
+                float sb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sb[j] = L.SL[(kq + j) * F16 + lm];
+                acc0 = mfma4(e0.x * x0.x, sb[0], acc0);
+                acc0 = mfma4(e0.y * x0.y, sb[1], acc0);
+                acc0 = mfma4(e0.z * x0.z, sb[2], acc0);
+                acc0 = mfma4(e0.w * x0.w, sb[3], acc0);
                 if constexpr (NB == 2) {
-                    const float a1 = EJK ? X[(FB + lm) * RS + kk] : L.E1[kk] * X[(FB + lm) * RS + kk];
-                    acc1 = mfma4(a1, sb, acc1);
+                    const float4 x1 = *reinterpret_cast<const float4*>(X + (FB + lm) * RS + kq);
+                    const float4 e1 = EJK ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(L.E1 + kq);
+                    acc1 = mfma4(e1.x * x1.x, sb[0], acc1);
+                    acc1 = mfma4(e1.y * x1.y, sb[1], acc1);
+                    acc1 = mfma4(e1.z * x1.z, sb[2], acc1);
+                    acc1 = mfma4(e1.w * x1.w, sb[3], acc1);
                 }
             }
             if (wave == 2) {
