@@ -72,11 +72,11 @@ struct F32Lds {
     static constexpr int FA = FC + 4;    // row stride of A (16-byte aligned rows)
     static constexpr int FP = FC + 1;    // row stride of P
     static constexpr int RS = DK + 4;   // row stride of [rows][DK] tiles: 16-byte rows, 16 rows in 16 distinct bank groups
-    float QL[FC * RS];    // raw q rows, then qh_r 2^{b_r - b_f} (f: the row's block reference; EJK: qh_r)
-    float KL[FC * RS];    // raw k rows, then kh_r 2^{b_r - b_f} (EJK: kh_r)
-    float KR[FC * RS];    // kh_r 2^{b_f - b_r} (EJK: kh_r)
-    float K1[NB == 2 ? FB * RS : 1];   // block-0 rows referenced to row 16: kh_r 2^{b_16 - b_r} (<= 1)
-    float GB[FC * RS];    // gamma', then b_r per channel (log2 units, KDA)
+    alignas(16) float QL[FC * RS];    // raw q rows, then qh_r 2^{b_r - b_f} (f: the row's block reference; EJK: qh_r)
+    alignas(16) float KL[FC * RS];    // raw k rows, then kh_r 2^{b_r - b_f} (EJK: kh_r)
+    alignas(16) float KR[FC * RS];    // kh_r 2^{b_f - b_r} (EJK: kh_r)
+    alignas(16) float K1[NB == 2 ? FB * RS : 4];   // block-0 rows referenced to row 16: kh_r 2^{b_16 - b_r} (<= 1)
+    alignas(16) float GB[FC * RS];    // gamma', then b_r per channel (log2 units, KDA)
     float SL[DK * F16];   // the state tile S[i][j]
     float VV[FC * F16];   // the value tile V[s][j]
     alignas(16) float AM[FC * FA];   // A (strict lower, beta-scaled)
@@ -325,18 +325,17 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
             const float4 wq = in ? P4::widen(R.q[m]) : z, wk = in ? P4::widen(R.k[m]) : z;
             if (e < Q4) {
-                float* pq = L.QL + row * RS + 4 * c4;
-                float* pk = L.KL + row * RS + 4 * c4;
-                pq[0] = wq.x; pq[1] = wq.y; pq[2] = wq.z; pq[3] = wq.w;
-                pk[0] = wk.x; pk[1] = wk.y; pk[2] = wk.z; pk[3] = wk.w;
+                *reinterpret_cast<float4*>(L.QL + row * RS + 4 * c4) = wq;
+                *reinterpret_cast<float4*>(L.KL + row * RS + 4 * c4) = wk;
                 if constexpr (!EJK) {
                     // gamma' = lb * log2(e) * sigmoid(exp(a_log) (g + dt_bias)), element by
                     // element here, where every lane holds four; padded rows 0
-                    float* pg = L.GB + row * RS + 4 * c4;
                     const float xg[4] = {R.g[m].x, R.g[m].y, R.g[m].z, R.g[m].w};
+                    float gp[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        pg[j] = in ? lb2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-ea * (xg[j] + dtb4[j]))) : 0.f;
+                        gp[j] = in ? lb2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-ea * (xg[j] + dtb4[j]))) : 0.f;
+                    *reinterpret_cast<float4*>(L.GB + row * RS + 4 * c4) = make_float4(gp[0], gp[1], gp[2], gp[3]);
                 }
             }
             float sq = wq.x * wq.x + wq.y * wq.y + wq.z * wq.z + wq.w * wq.w;
@@ -401,25 +400,48 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
 
         // ---- normalised rows with the decay factors of their block: L = 2^{b_r - b_f},
         // R = 1 / L (f = 0 or 16); block-0 keys also referenced to row 16 (K1 <= 1)
+        // VW consecutive channels per thread (four, or two where a chunk has fewer
+        // than four elements per thread): 16- or 8-byte LDS accesses.
+        constexpr int VW = (FC * DK >= 4 * FT) ? 4 : 2;
+        typedef float vw_t __attribute__((ext_vector_type(VW)));
+        constexpr int DQ = DK / VW;                   // pieces per row
+        constexpr int NQD = (FC * DQ + FT - 1) / FT;  // pieces per thread
 #pragma unroll
-        for (int m = 0; m < FC * DK / FT; ++m) {
+        for (int m = 0; m < NQD; ++m) {
             const int e = tid + m * FT;
-            const int r = e / DK, i = e % DK;
-            const float qh = L.QL[r * RS + i] * L.NQ[r];
-            const float kh = L.KL[r * RS + i] * L.NK[r];
-            if constexpr (EJK) {
-                L.QL[r * RS + i] = qh;
-                L.KL[r * RS + i] = kh;
-                L.KR[r * RS + i] = kh;
-            } else {
-                const float br = L.GB[r * RS + i];
-                const float d = br - L.GB[(r < FB ? 0 : FB) * RS + i];   // b_r - b_f <= 0
-                const float lf = __builtin_amdgcn_exp2f(d);
-                L.QL[r * RS + i] = qh * lf;
-                L.KL[r * RS + i] = kh * lf;
-                L.KR[r * RS + i] = kh * __builtin_amdgcn_exp2f(-d);
-                if constexpr (NB == 2)
-                    if (r < FB) L.K1[r * RS + i] = kh * __builtin_amdgcn_exp2f(L.GB[FB * RS + i] - br);
+            if ((FC * DQ) % FT == 0 || e < FC * DQ) {
+                const int r = e / DQ, i = VW * (e % DQ);
+                vw_t* pq = reinterpret_cast<vw_t*>(L.QL + r * RS + i);
+                vw_t* pk = reinterpret_cast<vw_t*>(L.KL + r * RS + i);
+                vw_t* pr = reinterpret_cast<vw_t*>(L.KR + r * RS + i);
+                const vw_t qh = *pq * L.NQ[r];
+                const vw_t kh = *pk * L.NK[r];
+                if constexpr (EJK) {
+                    *pq = qh;
+                    *pk = kh;
+                    *pr = kh;
+                } else {
+                    const vw_t br = *reinterpret_cast<const vw_t*>(L.GB + r * RS + i);
+                    const vw_t d = br - *reinterpret_cast<const vw_t*>(L.GB + (r < FB ? 0 : FB) * RS + i);   // b_r - b_f <= 0
+                    vw_t lf, rf;
+#pragma unroll
+                    for (int j = 0; j < VW; ++j) {
+                        lf[j] = __builtin_amdgcn_exp2f(d[j]);
+                        rf[j] = __builtin_amdgcn_exp2f(-d[j]);
+                    }
+                    *pq = qh * lf;
+                    *pk = kh * lf;
+                    *pr = kh * rf;
+                    if constexpr (NB == 2) {
+                        if (r < FB) {
+                            const vw_t g16 = *reinterpret_cast<const vw_t*>(L.GB + FB * RS + i);
+                            vw_t k1;
+#pragma unroll
+                            for (int j = 0; j < VW; ++j) k1[j] = kh[j] * __builtin_amdgcn_exp2f(g16[j] - br[j]);
+                            *reinterpret_cast<vw_t*>(L.K1 + r * RS + i) = k1;
+                        }
+                    }
+                }
             }
         }
         lds_barrier();
