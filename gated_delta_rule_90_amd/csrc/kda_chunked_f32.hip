@@ -34,7 +34,7 @@
 // 1 and is applied per (r, s) as a scalar.
 //
 // Work split: one 256-thread workgroup per (sequence, head, 16 state
-// columns); the state tile [dk][16] stays in LDS in float32.  Per chunk:
+// columns); the state tile stays in LDS in float32, transposed ([16][dk]).  Per chunk:
 //   1. the raw q, k rows go to LDS; gate activations element by element; row
 //      norms summed from the load registers;
 //   2. lanes i < dk run the gate cumsum of channel i down the chunk's rows;
@@ -77,7 +77,8 @@ struct F32Lds {
     alignas(16) float KR[FC * RS];    // kh_r 2^{b_f - b_r} (EJK: kh_r)
     alignas(16) float K1[NB == 2 ? FB * RS : 4];   // block-0 rows referenced to row 16: kh_r 2^{b_16 - b_r} (<= 1)
     alignas(16) float GB[FC * RS];    // gamma', then b_r per channel (log2 units, KDA)
-    float SL[DK * F16];   // the state tile S[i][j]
+    static constexpr int SRS = DK + 4;   // row stride of the transposed state tile
+    alignas(16) float ST[FJ * SRS];   // the state tile, transposed: S[i][j] at ST[j * SRS + i]
     float VV[FC * F16];   // the value tile V[s][j]
     alignas(16) float AM[FC * FA];   // A (strict lower, beta-scaled)
     float PM[FC * FP];    // P (lower incl. diagonal)
@@ -87,7 +88,7 @@ struct F32Lds {
     alignas(16) float E0[DK];   // 2^{b_0}
     alignas(16) float E1[DK];   // 2^{b_f} of the last block's reference row f
     float N1[DK];         // 2^{b_C - b_f} of the last block's reference row f
-    float DC[DK];         // 2^{b_C}
+    alignas(16) float DC[DK];   // 2^{b_C}
     float NQ[FC], NK[FC], BT[FC];   // query scale / norm, key 1 / norm, activated beta
     float EB[FC], EX[FC], EC[FC];   // EJK: 2^{b_r}, 2^{b_{r-1}}, 2^{b_C - b_r}
     float BR[FC], BX[FC];           // EJK: b_r, b_{r-1}
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
 
     for (int e = tid; e < DK * FJ; e += FT) {
         const int i = e / FJ, j = e % FJ;
-        L.SL[i * F16 + j] = init ? init[soff + (size_t)i * DV + j0 + j] : 0.f;
+        L.ST[j * LT::SRS + i] = init ? init[soff + (size_t)i * DV + j0 + j] : 0.f;
     }
     const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) in log2 units
     const float lb2 = lower_bound * kLog2e;
@@ -496,9 +497,8 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 const int kq = k0 + 4 * lk;
                 const float4 x0 = *reinterpret_cast<const float4*>(X + lm * RS + kq);
                 const float4 e0 = EJK ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(L.E0 + kq);
-                float sb[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sb[j] = L.SL[(kq + j) * F16 + lm];
+                const float4 s4 = *reinterpret_cast<const float4*>(L.ST + lm * LT::SRS + kq);   // S[kq ..][lm]
+                const float sb[4] = {s4.x, s4.y, s4.z, s4.w};
                 acc0 = mfma4(e0.x * x0.x, sb[0], acc0);
                 acc0 = mfma4(e0.y * x0.y, sb[1], acc0);
                 acc0 = mfma4(e0.z * x0.z, sb[2], acc0);
@@ -579,12 +579,11 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
 #pragma unroll
         for (int t = wave; t < DK / 16; t += 4) {
             const int ib = 16 * t;
-            f32x4_t sc;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = ib + ro + e;
-                sc[e] = (EJK ? L.DC[0] : L.DC[i]) * L.SL[i * F16 + lm];
-            }
+            // S[ib + ro + e][lm], e = 0..3, and their decay factors: 16 bytes each
+            const float4 s4 = *reinterpret_cast<const float4*>(L.ST + lm * LT::SRS + ib + ro);
+            const float4 dc4 = EJK ? make_float4(L.DC[0], L.DC[0], L.DC[0], L.DC[0])
+                                   : *reinterpret_cast<const float4*>(L.DC + ib + ro);
+            f32x4_t sc = f32x4_t{dc4.x * s4.x, dc4.y * s4.y, dc4.z * s4.z, dc4.w * s4.w};
             // A operand: Kc^T[ia][s] = 2^{b_C - b_s} kh_s = N1 K1[s] (block 0) or N1 KR[s] (block 1)
             const int ia = ib + lm;
 #pragma unroll
@@ -595,8 +594,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 else kc = L.N1[ia] * ((NB == 2 && k0 < FB) ? L.K1[s * RS + ia] : L.KR[s * RS + ia]);
                 sc = mfma4(kc, L.UM[s * F16 + lm], sc);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) L.SL[(ib + ro + e) * F16 + lm] = sc[e];
+            *reinterpret_cast<float4*>(L.ST + lm * LT::SRS + ib + ro) = make_float4(sc[0], sc[1], sc[2], sc[3]);
         }
         lds_barrier();
         // O rows r16 and r16 + 16, column c16, through a buffer resource that ends
@@ -632,7 +630,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     if (final_state) {
         for (int e = tid; e < DK * FJ; e += FT) {
             const int i = e / FJ, j = e % FJ;
-            final_state[soff + (size_t)i * DV + j0 + j] = L.SL[i * F16 + j];
+            final_state[soff + (size_t)i * DV + j0 + j] = L.ST[j * LT::SRS + i];
         }
     }
 }
