@@ -70,7 +70,8 @@ template <int DK, int NB>
 struct F32Lds {
     static constexpr int FC = FB * NB;
     static constexpr int FA = FC + 4;    // row stride of A (16-byte aligned rows)
-    static constexpr int FP = FC + 1;    // row stride of P
+    static constexpr int FP = FC + 4;    // row stride of P (16-byte aligned rows)
+    static constexpr int SU = FC + 4;    // row stride of the transposed U tile
     static constexpr int RS = DK + 4;   // row stride of [rows][DK] tiles: 16-byte rows, 16 rows in 16 distinct bank groups
     alignas(16) float QL[FC * RS];    // raw q rows, then qh_r 2^{b_r - b_f} (f: the row's block reference; EJK: qh_r)
     alignas(16) float KL[FC * RS];    // raw k rows, then kh_r 2^{b_r - b_f} (EJK: kh_r)
@@ -81,9 +82,9 @@ struct F32Lds {
     alignas(16) float ST[FJ * SRS];   // the state tile, transposed: S[i][j] at ST[j * SRS + i]
     float VV[FC * F16];   // the value tile V[s][j]
     alignas(16) float AM[FC * FA];   // A (strict lower, beta-scaled)
-    float PM[FC * FP];    // P (lower incl. diagonal)
+    alignas(16) float PM[FC * FP];   // P (lower incl. diagonal)
     float YM[FC * F16];   // Y = V - Kg S0, then block 1's right-hand side
-    float UM[FC * F16];   // U
+    alignas(16) float UT[FJ * SU];   // U, transposed: U[s][j] at UT[j * SU + s]
     float OM[FC * F16];   // O of the chunk, stored by every thread
     alignas(16) float E0[DK];   // 2^{b_0}
     alignas(16) float E1[DK];   // 2^{b_f} of the last block's reference row f
@@ -309,8 +310,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         level(std::integral_constant<int, 10>{}); level(std::integral_constant<int, 11>{});
         level(std::integral_constant<int, 12>{}); level(std::integral_constant<int, 13>{});
         level(std::integral_constant<int, 14>{});
-#pragma unroll
-        for (int e = 0; e < 4; ++e) L.UM[(rb + 4 * p + e) * F16 + jq] = u[e];
+        *reinterpret_cast<float4*>(L.UT + jq * LT::SU + rb + 4 * p) = make_float4(u[0], u[1], u[2], u[3]);
     };
 
     auto chunk = [&](Raw& R, int c) {
@@ -550,9 +550,16 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 const int r = FB + ro + e;
                 y[e] = L.BT[r] * L.YM[r * F16 + lm];
             }
-#pragma unroll
-            for (int k0 = 0; k0 < FB; k0 += 4)
-                y = mfma4(-L.AM[(FB + lm) * FA + k0 + lk], L.UM[(k0 + lk) * F16 + lm], y);
+            // token s = 4 lk + j at step j (as in the products over dk): A rows and
+            // the transposed U read 16 bytes per lane
+            {
+                const float4 a4 = *reinterpret_cast<const float4*>(L.AM + (FB + lm) * FA + 4 * lk);
+                const float4 u4 = *reinterpret_cast<const float4*>(L.UT + lm * LT::SU + 4 * lk);
+                y = mfma4(-a4.x, u4.x, y);
+                y = mfma4(-a4.y, u4.y, y);
+                y = mfma4(-a4.z, u4.z, y);
+                y = mfma4(-a4.w, u4.w, y);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) L.YM[(FB + ro + e) * F16 + lm] = y[e];
             solve16(FB, false);
@@ -562,13 +569,24 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
 
         // ---- O = Qg S0 + P U (wave 2), S = Diag(2^{b_C}) S0 + Kc^T U (16-row tiles over the waves)
         if (wave == 2) {
+            // tokens k0 + 4 lk + j at step j: P rows and the transposed U, 16 bytes per lane
 #pragma unroll
-            for (int k0 = 0; k0 < FB; k0 += 4)
-                acc0 = mfma4(L.PM[lm * FP + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc0);
-            if constexpr (NB == 2) {
-#pragma unroll
-                for (int k0 = 0; k0 < FC; k0 += 4)
-                    acc1 = mfma4(L.PM[(FB + lm) * FP + k0 + lk], L.UM[(k0 + lk) * F16 + lm], acc1);
+            for (int k0 = 0; k0 < FC; k0 += 16) {
+                const float4 u4 = *reinterpret_cast<const float4*>(L.UT + lm * LT::SU + k0 + 4 * lk);
+                if (k0 < FB) {
+                    const float4 p4 = *reinterpret_cast<const float4*>(L.PM + lm * FP + k0 + 4 * lk);
+                    acc0 = mfma4(p4.x, u4.x, acc0);
+                    acc0 = mfma4(p4.y, u4.y, acc0);
+                    acc0 = mfma4(p4.z, u4.z, acc0);
+                    acc0 = mfma4(p4.w, u4.w, acc0);
+                }
+                if constexpr (NB == 2) {
+                    const float4 p4 = *reinterpret_cast<const float4*>(L.PM + (FB + lm) * FP + k0 + 4 * lk);
+                    acc1 = mfma4(p4.x, u4.x, acc1);
+                    acc1 = mfma4(p4.y, u4.y, acc1);
+                    acc1 = mfma4(p4.z, u4.z, acc1);
+                    acc1 = mfma4(p4.w, u4.w, acc1);
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -586,13 +604,19 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             f32x4_t sc = f32x4_t{dc4.x * s4.x, dc4.y * s4.y, dc4.z * s4.z, dc4.w * s4.w};
             // A operand: Kc^T[ia][s] = 2^{b_C - b_s} kh_s = N1 K1[s] (block 0) or N1 KR[s] (block 1)
             const int ia = ib + lm;
+            // token s = k0 + 4 lk + j at step j; the transposed U read 16 bytes per lane
 #pragma unroll
-            for (int k0 = 0; k0 < FC; k0 += 4) {
-                const int s = k0 + lk;
-                float kc;
-                if constexpr (EJK) kc = L.EC[s] * L.KR[s * RS + ia];
-                else kc = L.N1[ia] * ((NB == 2 && k0 < FB) ? L.K1[s * RS + ia] : L.KR[s * RS + ia]);
-                sc = mfma4(kc, L.UM[s * F16 + lm], sc);
+            for (int k0 = 0; k0 < FC; k0 += 16) {
+                const float4 u4 = *reinterpret_cast<const float4*>(L.UT + lm * LT::SU + k0 + 4 * lk);
+                const float uj[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = k0 + 4 * lk + j;
+                    float kc;
+                    if constexpr (EJK) kc = L.EC[s] * L.KR[s * RS + ia];
+                    else kc = L.N1[ia] * ((NB == 2 && k0 < FB) ? L.K1[s * RS + ia] : L.KR[s * RS + ia]);
+                    sc = mfma4(kc, uj[j], sc);
+                }
             }
             *reinterpret_cast<float4*>(L.ST + lm * LT::SRS + ib + ro) = make_float4(sc[0], sc[1], sc[2], sc[3]);
         }
