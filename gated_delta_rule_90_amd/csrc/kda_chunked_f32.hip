@@ -37,7 +37,8 @@
 // columns); the state tile stays in LDS in float32, transposed ([16][dk]).  Per chunk:
 //   1. the raw q, k rows go to LDS; gate activations element by element; row
 //      norms summed from the load registers;
-//   2. lanes i < dk run the gate cumsum of channel i down the chunk's rows;
+//   2. the gate cumsum of each channel down the chunk's rows (two-block
+//      chunks: 8-row segments on adjacent lanes joined by a prefix);
 //   3. every thread scales its elements of q, k by the norms and decay factors;
 //   4. the contractions over dk (the blocks of A, of P, Qg S0, Kg S0) run on
 //      16x16x4 float32 MFMA, one kind per wave and in parallel, with the row
@@ -376,25 +377,51 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         load(R, min(c + FD, nch - 1));   // past the end this reloads the last chunk
         lds_barrier();
 
-        // ---- lane i < dk: the gate cumsum of channel i down the chunk's rows
+        // ---- the gate cumsum of every channel down the chunk's rows.  Two-block
+        // chunks: NSEG = 4 adjacent lanes per channel each sum 8 rows, and an
+        // exclusive prefix of the segment sums over those lanes (whole waves: dk * 4
+        // is a multiple of 64) joins them; one-block chunks: one lane per channel.
         if constexpr (!EJK) {
-            if (tid < DK) {
-                const int i = tid;
-                float gm[FC];
+            constexpr int NSEG = NB == 2 ? 4 : 1;
+            constexpr int SEGL = FC / NSEG;   // rows per segment
+            static_assert(NSEG == 1 || (DK * NSEG) % 64 == 0, "whole waves of segment lanes");
+            if (tid < DK * NSEG) {
+                const int i = tid / NSEG, seg = tid % NSEG;
+                float gm[SEGL];
 #pragma unroll
-                for (int r = 0; r < FC; ++r) gm[r] = L.GB[r * RS + i];
-                float b = 0.f, b0 = 0.f, bl = 0.f;
+                for (int k = 0; k < SEGL; ++k) gm[k] = L.GB[(SEGL * seg + k) * RS + i];
+                float b = 0.f;
+                const int base = lane - seg;   // the lane of this channel's first segment
+                if constexpr (NSEG > 1) {
+                    float ssum = 0.f;
 #pragma unroll
-                for (int r = 0; r < FC; ++r) {
-                    b += gm[r];
-                    if (r == 0) b0 = b;
-                    if (r == FL) bl = b;
-                    L.GB[r * RS + i] = b;
+                    for (int k = 0; k < SEGL; ++k) ssum += gm[k];
+#pragma unroll
+                    for (int s2 = 0; s2 < NSEG - 1; ++s2) {
+                        const float o = __shfl(ssum, base + s2);
+                        b += (s2 < seg) ? o : 0.f;
+                    }
                 }
-                L.E0[i] = __builtin_amdgcn_exp2f(b0);
-                L.E1[i] = __builtin_amdgcn_exp2f(bl);
-                L.N1[i] = __builtin_amdgcn_exp2f(b - bl);
-                L.DC[i] = __builtin_amdgcn_exp2f(b);
+                float bfirst = 0.f;
+#pragma unroll
+                for (int k = 0; k < SEGL; ++k) {
+                    b += gm[k];
+                    if (k == 0) bfirst = b;
+                    L.GB[(SEGL * seg + k) * RS + i] = b;
+                }
+                // b_0 and b_FL (first rows of segments 0 and FL / SEGL), b_C (end of the last)
+                float b0 = bfirst, bl = bfirst, bc = b;
+                if constexpr (NSEG > 1) {
+                    b0 = __shfl(bfirst, base);
+                    bl = __shfl(bfirst, base + FL / SEGL);
+                    bc = __shfl(b, base + NSEG - 1);
+                }
+                if (seg == 0) {
+                    L.E0[i] = __builtin_amdgcn_exp2f(b0);
+                    L.E1[i] = __builtin_amdgcn_exp2f(bl);
+                    L.N1[i] = __builtin_amdgcn_exp2f(bc - bl);
+                    L.DC[i] = __builtin_amdgcn_exp2f(bc);
+                }
             }
             lds_barrier();
         }
