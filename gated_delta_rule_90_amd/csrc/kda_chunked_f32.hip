@@ -81,10 +81,10 @@ struct F32Lds {
     alignas(16) float GB[FC * RS];    // gamma', then b_r per channel (log2 units, KDA)
     static constexpr int SRS = DK + 4;   // row stride of the transposed state tile
     alignas(16) float ST[FJ * SRS];   // the state tile, transposed: S[i][j] at ST[j * SRS + i]
-    float VV[FC * F16];   // the value tile V[s][j]
+    alignas(16) float VT[FJ * SU];   // the value tile, transposed: V[s][j] at VT[j * SU + s]
     alignas(16) float AM[FC * FA];   // A (strict lower, beta-scaled)
     alignas(16) float PM[FC * FP];   // P (lower incl. diagonal)
-    float YM[FC * F16];   // Y = V - Kg S0, then block 1's right-hand side
+    alignas(16) float YT[FJ * SU];   // Y = V - Kg S0, then block 1's right-hand side (transposed)
     alignas(16) float UT[FJ * SU];   // U, transposed: U[s][j] at UT[j * SU + s]
     float OM[FC * F16];   // O of the chunk, stored by every thread
     alignas(16) float E0[DK];   // 2^{b_0}
@@ -282,15 +282,17 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     // lanes of quad j, rows 4p .. 4p + 3 of the block on lane p.  At step s the
     // owner of row s broadcasts u_s within the quad (DPP) and every lane updates
     // its rows; A is zero on and above the diagonal, so rows r <= s keep their
-    // value without a mask.  Reads the right-hand side from YM (scaled by beta
+    // value without a mask.  Reads the right-hand side from YT (scaled by beta
     // for block 0), writes U.
     auto solve16 = [&](int rb, bool scale_by_beta) {
         const int jq = lane >> 2, p = lane & 3;
         float u[4], am[4][FB];
+        const float4 y4 = *reinterpret_cast<const float4*>(L.YT + jq * LT::SU + rb + 4 * p);
+        const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rb + 4 * p + e;
-            u[e] = (scale_by_beta ? L.BT[r] : 1.f) * L.YM[r * F16 + jq];
+            u[e] = (scale_by_beta ? L.BT[r] : 1.f) * yv[e];
 #pragma unroll
             for (int s4 = 0; s4 < FB; s4 += 4) {
                 const float4 a4 = *reinterpret_cast<const float4*>(L.AM + r * FA + rb + s4);
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         }
 #pragma unroll
         for (int hv = 0; hv < NB; ++hv)
-            L.VV[(r16 + FB * hv) * F16 + c16] = (r16 + FB * hv < len) ? to_f32(R.v[hv]) : 0.f;
+            L.VT[c16 * LT::SU + r16 + FB * hv] = (r16 + FB * hv < len) ? to_f32(R.v[hv]) : 0.f;
         if (tid < FC) {
             // beta = 1 / (1 + 2^{-logit log2(e)}); R.b was loaded by every lane
             L.BT[tid] = (tid < len) ? (EJK ? R.b : __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * R.b))) : 0.f;
@@ -548,16 +550,17 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                     }
                 }
             } else {
+                // rows ro .. ro + 3 (and FB + ro ..) of column lm: 16-byte accesses
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r0 = ro + e;
-                    const float z0 = EJK ? L.EX[r0] * acc0[e] : acc0[e];
-                    L.YM[r0 * F16 + lm] = L.VV[r0 * F16 + lm] - z0;
-                    if constexpr (NB == 2) {
-                        const int r1 = FB + ro + e;
-                        const float z1 = EJK ? L.EX[r1] * acc1[e] : acc1[e];
-                        L.YM[r1 * F16 + lm] = L.VV[r1 * F16 + lm] - z1;
-                    }
+                for (int hb = 0; hb < NB; ++hb) {
+                    const f32x4_t a = hb == 0 ? acc0 : acc1;
+                    const int r0 = FB * hb + ro;
+                    const float4 v4 = *reinterpret_cast<const float4*>(L.VT + lm * LT::SU + r0);
+                    float z[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) z[e] = EJK ? L.EX[r0 + e] * a[e] : a[e];
+                    *reinterpret_cast<float4*>(L.YT + lm * LT::SU + r0) =
+                        make_float4(v4.x - z[0], v4.y - z[1], v4.z - z[2], v4.w - z[3]);
                 }
             }
         }
@@ -571,12 +574,9 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         }
         if constexpr (NB == 2) {
           if (wave == 0) {
-            f32x4_t y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = FB + ro + e;
-                y[e] = L.BT[r] * L.YM[r * F16 + lm];
-            }
+            const float4 y4 = *reinterpret_cast<const float4*>(L.YT + lm * LT::SU + FB + ro);
+            f32x4_t y = f32x4_t{L.BT[FB + ro] * y4.x, L.BT[FB + ro + 1] * y4.y, L.BT[FB + ro + 2] * y4.z,
+                                L.BT[FB + ro + 3] * y4.w};
             // token s = 4 lk + j at step j (as in the products over dk): A rows and
             // the transposed U read 16 bytes per lane
             {
@@ -587,8 +587,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 y = mfma4(-a4.z, u4.z, y);
                 y = mfma4(-a4.w, u4.w, y);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) L.YM[(FB + ro + e) * F16 + lm] = y[e];
+            *reinterpret_cast<float4*>(L.YT + lm * LT::SU + FB + ro) = make_float4(y[0], y[1], y[2], y[3]);
             solve16(FB, false);
           }
         }
