@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -73,11 +74,19 @@ def prefill_flops(ntok, H, dk, dv, C=64):
     return ntok * H * (C * (3 * dk + 2 * dv) + 6 * dk * dv)
 
 
+def _code_only(text):
+    """Source text without comments and blank space, so that a counter summary
+    stays tied to the code it was taken on, not to the comments around it."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.strip() for line in text.splitlines() if line.strip())
+
+
 def _src_hash(*names):
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "gated_delta_rule_90_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_90_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

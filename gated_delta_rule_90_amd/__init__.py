@@ -16,6 +16,7 @@ calls raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -95,6 +96,15 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Make `stream` current while outputs and the workspace are allocated, so
+    torch's caching allocator ties those blocks to the stream the kernels run
+    on: the workspace freed on return is then reused only by work ordered
+    after them on that stream."""
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def prefill_workspace_bytes(num_seqs, B, T, H, dk, dv, flags, in_dtype=BF16) -> int:
     return int(lib().kda_prefill_workspace_bytes(num_seqs, B, T, H, dk, dv, in_dtype, flags))
 
@@ -144,31 +154,32 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
     if initial_state is not None and tuple(initial_state.shape) != (N, H, dk, dv):
         raise ValueError(f"initial_state must be [{N}, {H}, {dk}, {dv}]")
     odt = q.dtype if out_dtype is None else out_dtype
-    if out is None:
-        out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
-    else:
-        _dev("out", out, (odt,), dev)
-        if tuple(out.shape) != (B, T, H, dv):
-            raise ValueError("out must be [B, T, H, dv]")
-    if return_state and final_state is None:
-        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif final_state is not None:
-        _dev("final_state", final_state, f, dev)
-        if tuple(final_state.shape) != (N, H, dk, dv):
-            raise ValueError("final_state must be [N, H, dk, dv]")
-    flags = (QK_L2NORM if use_qk_l2norm else 0) | (CHUNKED if use_chunked else 0) | \
-        (EJK if ejk else 0)
-    nseq = N if cu_seqlens is not None else 0
-    idt = BF16 if q.dtype == torch.bfloat16 else F32
-    wsb = prefill_workspace_bytes(nseq, B, T, H, dk, dv, flags, idt)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb > 0 else None
-    sc = -1.0 if scale is None else float(scale)
-    _check(lib().kda_prefill(
-        _ptr(q), _ptr(k), _ptr(v), BF16 if q.dtype == torch.bfloat16 else F32,
-        _ptr(g), _ptr(beta), _ptr(a_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_seqlens),
-        nseq, B, T, H, Hkv, dk, dv, sc, float(lower_bound), int(chunk_size), flags,
-        _ptr(out), BF16 if odt == torch.bfloat16 else F32, _ptr(final_state), _ptr(ws), wsb,
-        _stream(dev, stream)))
+    with _on(stream):
+        if out is None:
+            out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
+        else:
+            _dev("out", out, (odt,), dev)
+            if tuple(out.shape) != (B, T, H, dv):
+                raise ValueError("out must be [B, T, H, dv]")
+        if return_state and final_state is None:
+            final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        elif final_state is not None:
+            _dev("final_state", final_state, f, dev)
+            if tuple(final_state.shape) != (N, H, dk, dv):
+                raise ValueError("final_state must be [N, H, dk, dv]")
+        flags = (QK_L2NORM if use_qk_l2norm else 0) | (CHUNKED if use_chunked else 0) | \
+            (EJK if ejk else 0)
+        nseq = N if cu_seqlens is not None else 0
+        idt = BF16 if q.dtype == torch.bfloat16 else F32
+        wsb = prefill_workspace_bytes(nseq, B, T, H, dk, dv, flags, idt)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb > 0 else None
+        sc = -1.0 if scale is None else float(scale)
+        _check(lib().kda_prefill(
+            _ptr(q), _ptr(k), _ptr(v), idt,
+            _ptr(g), _ptr(beta), _ptr(a_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_seqlens),
+            nseq, B, T, H, Hkv, dk, dv, sc, float(lower_bound), int(chunk_size), flags,
+            _ptr(out), BF16 if odt == torch.bfloat16 else F32, _ptr(final_state), _ptr(ws), wsb,
+            _stream(dev, stream)))
     if return_state:
         return out, final_state
     return out
@@ -204,12 +215,13 @@ def decode_step(q, k, v, g, beta, a_log, dt_bias, S, *, scale=None, lower_bound=
         raise ValueError("a_log must hold H values")
     if dt_bias is not None and tuple(dt_bias.shape) != (dk, H):
         raise ValueError("dt_bias must be [dk, H]")
-    if out is None:
-        out = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
-    else:
-        _dev("out", out, f, dev)
-        if tuple(out.shape) != (B, H, dv):
-            raise ValueError("out must be [B, H, dv]")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+        else:
+            _dev("out", out, f, dev)
+            if tuple(out.shape) != (B, H, dv):
+                raise ValueError("out must be [B, H, dv]")
     flags = (QK_L2NORM if use_qk_l2norm else 0) | (EJK if ejk else 0)
     sc = -1.0 if scale is None else float(scale)
     _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(g), _ptr(v), _ptr(beta), _ptr(a_log),

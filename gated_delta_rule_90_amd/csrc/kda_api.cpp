@@ -131,25 +131,22 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
     a.workspace_bytes = workspace_bytes;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (has_tokens && chunked && kda::chunked_supported(a)) {
-        if (!ejk && lower_bound < -5.0f)
-            return fail(KDA_EUNSUPPORTED, "kda_prefill: the chunked path needs lower_bound >= -5 (got %g)", (double)lower_bound);
-        // its kernels move q, k, v, o and the KDA gates 16 bytes per lane
-        auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-        if (!a16(q) || !a16(k) || !a16(v) || !a16(o) || (!ejk && !a16(g)))
-            return fail(KDA_EINVAL, "kda_prefill: the chunked path needs q, k, v, o and g 16-byte aligned");
+    // Both chunked kernels move q, k and (KDA) g 16 bytes per lane, and in KDA
+    // mode scale by decay factors that stay inside float32's range only for
+    // lower_bound >= -5.  A call outside that takes the token-by-token kernel,
+    // which computes the same function step by step, on every input dtype.
+    auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    const bool chunk_ok = has_tokens && chunked && (ejk || lower_bound >= -5.0f) &&
+                          a16(q) && a16(k) && (ejk || a16(g));
+    if (chunk_ok && kda::chunked_supported(a) && a16(v) && a16(o)) {
+        // the MFMA kernel also moves v and o 16 bytes per lane
         const size_t need = kda::chunked_workspace_bytes(N, T, H, dk, dv, cu_seqlens != nullptr);
         if (need > 0 && (!workspace || workspace_bytes < need))
             return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
         return hip_status(kda::launch_chunked(a, st), "kda_prefill (chunked)");
     }
-    if (has_tokens && chunked && kda::chunked_f32_supported(a)) {
-        // float32 inputs: the chunked kernel loads q, k and (KDA) g 16 bytes per
-        // lane; unaligned inputs take the token-by-token kernel instead
-        auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-        if (a16(q) && a16(k) && (ejk || a16(g)))
-            return hip_status(kda::launch_chunked_f32(a, st), "kda_prefill (chunked float32)");
-    }
+    if (chunk_ok && kda::chunked_f32_supported(a))
+        return hip_status(kda::launch_chunked_f32(a, st), "kda_prefill (chunked float32)");
     // token-by-token path; with T == 0 it only carries initial_state to final_state
     return hip_status(kda::launch_recurrent(a, st), "kda_prefill (recurrent)");
 }

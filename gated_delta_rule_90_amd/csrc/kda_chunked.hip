@@ -1,6 +1,6 @@
-// kda_chunked.hip - chunk-parallel KDA prefill on gfx950 MFMA (ejkernel
-// "kernel_delta_attention": chunked mode, "Parallel within chunks", default
-// chunk_size 64).
+// kda_chunked.hip - chunk-parallel KDA prefill on gfx950 MFMA: the chunked
+// mode of the ejkernel "kernel_delta_attention" page (section "Algorithm
+// modes"; run() default chunk_size 64).
 //
 // The pages give no chunk formulas; the ones below are an exact algebraic
 // regrouping of the token recurrence (decay per key channel, residual

@@ -1,6 +1,7 @@
 // kda_chunked_f32.hip - chunk-parallel KDA prefill in float32 arithmetic: float32
 // inputs at any dk, bf16 inputs at dk < 128
-// (ejkernel "kernel_delta_attention": chunked mode, "Parallel within chunks").
+// (the chunked mode of the ejkernel "kernel_delta_attention" page, section
+// "Algorithm modes").
 //
 // The chunk algebra is the bf16 MFMA kernel's (an exact regrouping of the
 // token recurrence: decay per key channel, residual against the decayed

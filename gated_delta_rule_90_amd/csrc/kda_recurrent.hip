@@ -1,5 +1,6 @@
-// kda_recurrent.hip - token-by-token KDA prefill (ejkernel use_chunked=False:
-// "Recurrent: Pure sequential scan for memory efficiency").
+// kda_recurrent.hip - token-by-token KDA prefill: the recurrent mode of the
+// ejkernel "kernel_delta_attention" page (section "Algorithm modes"; run()
+// with use_chunked=False), one step per token.
 //
 // Grid (column tiles, H, N sequences); one wave per block.  Each state column
 // is held in registers by LPC adjacent lanes (16 at dk = 128, 8 at dk = 32

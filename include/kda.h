@@ -3,9 +3,10 @@
  * Delta Attention (KDA) gated delta-rule recurrence.
  *
  * What is computed.  For every (sequence n, head h) the library carries a
- * float32 state S in R^{dk x dv} (ejkernel "kernel_delta_attention":
- * "Memory matrix: [num_heads, head_dim, value_dim] per batch"; AWS Neuron
- * "KDA TKG Kernel API Reference", parameter S: [B, num_head, dk, dv]).
+ * float32 state S in R^{dk x dv} (ejkernel "kernel_delta_attention" page,
+ * module description: one memory matrix of key by value dimension per head
+ * and batch item; AWS Neuron "KDA TKG Kernel API Reference", parameter S:
+ * [B, num_head, dk, dv]).
  * Per token, from raw inputs (kda_tkg parameters q, k, g, beta, a_log,
  * dt_bias, scale, lower_bound):
  *     qh    = scale * q / sqrt(sum q^2 + 1e-6)       (scale folded into the query)
@@ -86,9 +87,9 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *   dt_bias        [dk, H] float32 (KDA; NULL = 0)
  *   initial_state  [N, H, dk, dv] float32, NULL = zeros
  *   scale          query scale; <= 0 or NaN selects 1/sqrt(dk)
- *   lower_bound    KDA gate bound, finite and <= 0; when the call takes the
- *                  MFMA chunked kernel it must be >= -5 (the kda_tkg documented
- *                  range [-5, 0]), else KDA_EUNSUPPORTED
+ *   lower_bound    KDA gate bound, finite and <= 0 (the kda_tkg documented
+ *                  range is [-5, 0]; below -5 the call takes the
+ *                  token-by-token kernel, see Routing)
  *   chunk_size     64 (the ejkernel default) when KDA_CHUNKED is set; the
  *                  float32-arithmetic chunked kernel computes the same result
  *                  in chunks of 16 or 32 (see Routing)
@@ -101,18 +102,21 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * Dimensions: dk, dv in {16, 32, 64, 128} (kda_tkg: dk <= 128); H and the
  * number of sequences at most 65535.  B = 0 or
  * T = 0 is a no-op, except that final_state then receives initial_state (or
- * zeros).  Routing:
+ * zeros).  Routing (which kernel runs; every route computes the same function
+ * and meets the same accuracy bar):
  *   - KDA_CHUNKED with bf16 inputs and dk = 128 (any of the dv above) runs
- *     the MFMA chunked kernel (64-token chunks; KDA and EJK modes), which
- *     needs q, k, v, o and (KDA) g 16-byte aligned (KDA_EINVAL otherwise);
+ *     the MFMA chunked kernel (64-token chunks; KDA and EJK modes) when q, k,
+ *     v, o and (KDA) g are 16-byte aligned and, in KDA mode,
+ *     lower_bound >= -5 (its decay factors then stay inside the bf16/float32
+ *     exponent range); this is the only route that uses the workspace;
  *   - KDA_CHUNKED with float32 inputs (any dk) or bf16 inputs with dk < 128
  *     runs the chunked kernel that computes in float32 (float32 MFMA,
  *     chunks of 32 tokens at dk <= 32 and 16 above: the chunking changes
- *     rounding only) when q, k and
- *     (KDA) g are 16-byte aligned and, in KDA mode, lower_bound >= -5 (its
- *     decay factors over 16 tokens then stay inside float32's normal range);
- *   - every other combination runs the float32 token-by-token kernel, which
- *     computes the same function step by step.
+ *     rounding only) when q, k and (KDA) g are 16-byte aligned and, in KDA
+ *     mode, lower_bound >= -5;
+ *   - every other call (KDA_CHUNKED clear, unaligned pointers, or
+ *     lower_bound < -5 in KDA mode), whatever its input dtype, runs the
+ *     float32 token-by-token kernel.
  * EJK decays are expected to be <= 0 (the ejkernel page says so); the chunked
  * kernels scale by e^{sum of decays} within a chunk, so a positive decay
  * large enough to overflow float32 there gives inf/NaN where the

@@ -34,8 +34,8 @@
  *   The page writes h_{t-1} @ k_t and h_t @ q_t; with a [dk, dv] state and a
  *   [.., v_head_dim] output the contraction is over dk, i.e. S^T k and S^T q.
  *
- *   Variable-length packing (ejkernel "recurrent" page, run(): cu_seqlens
- *   "Cumulative sequence lengths"): sequence n covers tokens
+ *   Variable-length packing (ejkernel "recurrent" page, run() parameter
+ *   cu_seqlens, cumulative sequence lengths): sequence n covers tokens
  *   [cu[n], cu[n+1]); each sequence starts from its own initial state (or
  *   zeros) and returns its own final state.
  *

@@ -77,3 +77,40 @@ def decode_oracle(inp, S=None, **kw):
     return kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias,
                              inp.S if S is None else S, scale=inp.scale,
                              lower_bound=inp.lower_bound, ejk=inp.ejk, **kw)
+
+
+def unit_errors(o, ro, s, rs, cu=None):
+    """Relative L2 of every (sequence, head) unit, for o and the final state.
+
+    o, ro: [B, T, H, dv] (with cu, B == 1 and sequence n is rows cu[n]:cu[n+1]);
+    s, rs: [N, H, dk, dv].  Returns (eo [N, H], es [N, H]); an empty sequence
+    has eo = 0."""
+    N, H = rs.shape[:2]
+    eo = np.zeros((N, H))
+    es = np.zeros((N, H))
+    for n in range(N):
+        if cu is None:
+            on, ron = o[n], ro[n]
+        else:
+            a, b = int(cu[n]), int(cu[n + 1])
+            on, ron = o[0, a:b], ro[0, a:b]
+        for h in range(H):
+            if on.shape[0]:
+                eo[n, h] = rel_l2(on[:, h], ron[:, h])
+            es[n, h] = rel_l2(s[n, h], rs[n, h])
+    return eo, es
+
+
+def check_units(o, ro, s, rs, tol, margin=None, cu=None, label=""):
+    """Assert the worst per-unit relative L2 of o and of the state; record it."""
+    eo, es = unit_errors(o, ro, s, rs, cu)
+    wo, ws = np.unravel_index(np.argmax(eo), eo.shape), np.unravel_index(np.argmax(es), es.shape)
+    msg = (f"{label} worst unit o={eo[wo]:.3e} at (seq, head) {tuple(int(x) for x in wo)}, "
+           f"S={es[ws]:.3e} at {tuple(int(x) for x in ws)}; {eo.size} units, bar {tol:g}")
+    say("  " + msg)
+    if margin is not None:
+        margin(f"{label} o".strip(), eo[wo], tol)
+        margin(f"{label} S".strip(), es[ws], tol)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s)), msg
+    assert eo[wo] <= tol and es[ws] <= tol, msg
+    return eo, es

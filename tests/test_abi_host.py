@@ -86,11 +86,6 @@ PREFILL_ERRORS = [
     (dict(dv=48), kda.KDA_EUNSUPPORTED, "dk and dv"),
     (dict(in_dtype=kda.F32, out_dtype=kda.BF16), kda.KDA_EUNSUPPORTED, "bf16 output"),
     (dict(chunk_size=32), kda.KDA_EUNSUPPORTED, "chunk_size"),
-    (dict(lower_bound=-6.0), kda.KDA_EUNSUPPORTED, "lower_bound >= -5"),
-    (dict(q=P + 8), kda.KDA_EINVAL, "16-byte aligned"),
-    (dict(v=P + 2), kda.KDA_EINVAL, "16-byte aligned"),
-    (dict(o=P + 4), kda.KDA_EINVAL, "16-byte aligned"),
-    (dict(g=P + 4), kda.KDA_EINVAL, "16-byte aligned"),
     (dict(Hkv=3), kda.KDA_EINVAL, "must divide H"),
     (dict(Hkv=-1), kda.KDA_EINVAL, "must divide H"),
     (dict(Hkv=8), kda.KDA_EINVAL, "must divide H"),
@@ -109,6 +104,37 @@ def test_prefill_accepts_recurrent_lower_bound_below_minus_five_and_ejk_without_
     assert _prefill(lower_bound=-6.0, flags=kda.QK_L2NORM, B=0) == kda.KDA_OK
     assert _prefill(flags=kda.EJK | kda.CHUNKED, g=None, a_log=None, B=0) == kda.KDA_OK
     assert kda.lib().kda_last_error().decode() == ""
+
+
+ROUTES = [
+    # bf16, dk = 128: the MFMA chunked kernel when aligned and lower_bound >= -5
+    (dict(ws=P, ws_bytes=1 << 30), "(chunked)"),
+    (dict(ws=P, ws_bytes=1 << 30, flags=kda.EJK | kda.CHUNKED, lower_bound=-9.0), "(chunked)"),
+    # ... else the token-by-token kernel, whatever the workspace
+    (dict(lower_bound=-6.0), "(recurrent)"),
+    (dict(q=P + 8), "(recurrent)"),
+    (dict(k=P + 4, ws=P, ws_bytes=1 << 30), "(recurrent)"),
+    (dict(v=P + 2, ws=P, ws_bytes=1 << 30), "(recurrent)"),
+    (dict(o=P + 4, ws=P, ws_bytes=1 << 30), "(recurrent)"),
+    (dict(g=P + 4, ws=P, ws_bytes=1 << 30), "(recurrent)"),
+    (dict(flags=kda.QK_L2NORM), "(recurrent)"),
+    # float32 inputs (any dk), bf16 below dk = 128: the float32 chunked kernel
+    (dict(in_dtype=kda.F32, out_dtype=kda.F32), "(chunked float32)"),
+    (dict(dk=64), "(chunked float32)"),
+    (dict(in_dtype=kda.F32, out_dtype=kda.F32, lower_bound=-5.5), "(recurrent)"),
+    (dict(in_dtype=kda.F32, out_dtype=kda.F32, q=P + 4), "(recurrent)"),
+    (dict(in_dtype=kda.F32, out_dtype=kda.F32, v=P + 4, o=P + 4), "(chunked float32)"),
+]
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="launches with placeholder pointers: "
+                    "only on a host without a GPU, where the launch itself fails")
+@pytest.mark.parametrize("over,kernel", ROUTES, ids=[str(i) for i in range(len(ROUTES))])
+def test_prefill_routing(over, kernel):
+    """Which kernel a valid call takes: with no GPU the launch fails with
+    KDA_EHIP, and the message names the kernel that was chosen."""
+    assert _prefill(**over) == kda.KDA_EHIP
+    assert kernel + ":" in kda.lib().kda_last_error().decode()
 
 
 def test_prefill_empty_problems_are_no_ops():

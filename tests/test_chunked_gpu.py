@@ -8,7 +8,7 @@ import pytest
 
 import gated_delta_rule_90_amd as kda
 from gated_delta_rule_90_amd import workloads
-from tests._common import dev, prefill_gpu, prefill_oracle, rel_l2, say
+from tests._common import check_units, dev, prefill_gpu, prefill_oracle, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -155,21 +155,44 @@ def test_chunked_matches_recurrent_kernel():
     assert rel_l2(oc, orc) <= TOL and rel_l2(sc, src) <= TOL
 
 
-def test_chunked_full_size_b4_t4096_h16_sampled():
-    """Launch shape of the benchmark; the oracle checks three (batch, head) items."""
+def test_chunked_full_size_b4_t4096_h16_every_unit(margin):
+    """Launch shape of the benchmark: all 64 (batch, head) units against the
+    oracle, each with its own relative L2."""
     inp = workloads.prefill_b4_t4096_h16_d128()
     say("chunked full size B=4 T=4096 H=16")
-    _check(inp, units=[0, 37, 63])
+    o, s = prefill_gpu(inp)
+    ro, rs = prefill_oracle(inp)
+    check_units(o, ro, s, rs, TOL, margin, label="B4 T4096 H16")
 
 
-def test_chunked_varlen_8seq_sampled():
-    inp = workloads.prefill_varlen_8seq_h32_d128()
-    say("chunked varlen 8 seqs", inp.meta["lengths"])
-    H = 32
-    # the longest sequence's first and last head, and one head of the shortest
-    lens = inp.meta["lengths"]
-    nl, ns = int(np.argmax(lens)), int(np.argmin(lens))
-    _check(inp, units=[nl * H, nl * H + H - 1, ns * H + 5])
+def _packed_equals_separate(inp, o, s):
+    """Each sequence of a packed batch run alone gives bitwise the packed result."""
+    cu = inp.cu_seqlens
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sub = workloads.PrefillInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b],
+                                      None if inp.g is None else inp.g[:, a:b], inp.beta[:, a:b],
+                                      inp.a_log, inp.dt_bias,
+                                      None if inp.initial_state is None else inp.initial_state[n:n + 1],
+                                      None, inp.dtype, inp.scale, inp.lower_bound, ejk=inp.ejk)
+        on, sn = prefill_gpu(sub)
+        assert np.array_equal(o[:, a:b], on), f"sequence {n}: packed o differs from the separate run"
+        assert np.array_equal(s[n], sn[0]), f"sequence {n}: packed state differs from the separate run"
+
+
+@pytest.mark.parametrize("ejk", [False, True], ids=["kda", "ejk"])
+def test_chunked_varlen_8seq_every_sequence(ejk, margin):
+    """The 8-sequence varlen batch: every (sequence, head) unit against the
+    oracle, and every sequence run alone equal to the packed run bit for bit."""
+    inp = workloads.prefill_varlen_8seq_h32_d128(ejk=ejk)
+    say("chunked varlen 8 seqs", "EJK" if ejk else "KDA", inp.meta["lengths"])
+    o, s = prefill_gpu(inp)
+    ro, rs = prefill_oracle(inp)
+    check_units(o, ro, s, rs, TOL, margin, cu=inp.cu_seqlens,
+                label="varlen 8 seqs " + ("EJK" if ejk else "KDA"))
+    del ro, rs
+    say("  packed vs separate")
+    _packed_equals_separate(inp, o, s)
 
 
 @pytest.mark.parametrize("T", [64, 1, 200])
@@ -200,19 +223,10 @@ def test_chunked_ejk_matches_recurrent_kernel():
     assert rel_l2(oc, orc) <= TOL and rel_l2(sc, src) <= TOL
 
 
-def test_chunked_ejk_varlen_8seq_sampled():
-    inp = workloads.prefill_varlen_8seq_h32_d128(ejk=True)
-    say("chunked EJK varlen 8 seqs", inp.meta["lengths"])
-    H = 32
-    lens = inp.meta["lengths"]
-    nl, ns = int(np.argmax(lens)), int(np.argmin(lens))
-    _check(inp, units=[nl * H + 3, ns * H, ns * H + H - 1])
-
-
-def test_chunked_long_context_t65536_h32_split_and_sampled():
+def test_chunked_long_context_t65536_h32_split_and_every_head(margin):
     """One 65536-token sequence, 32 heads, nonzero initial state: the call split
     at 32768 with the state passed through equals the unsplit call bitwise, and
-    two heads (first and last) match the oracle."""
+    every head matches the oracle."""
     inp = workloads.prefill_long_t65536_h32_d128()
     say("chunked long context T=65536 H=32")
     o, s = prefill_gpu(inp)
@@ -229,16 +243,9 @@ def test_chunked_long_context_t65536_h32_split_and_sampled():
     assert np.array_equal(np.concatenate([o1, o2], axis=1), o)
     assert np.array_equal(s2, s)
     del o1, o2
-    heads = [0, 31]
-    sub = workloads.PrefillInputs(inp.q[:, :, heads], inp.k[:, :, heads], inp.v[:, :, heads],
-                                  inp.g[:, :, heads], inp.beta[:, :, heads], inp.a_log[heads],
-                                  inp.dt_bias[:, heads], inp.initial_state[:, heads], None,
-                                  inp.dtype, inp.scale, inp.lower_bound)
-    say("  oracle on heads", heads)
-    ro, rs = prefill_oracle(sub)
-    eo, es = rel_l2(o[:, :, heads], ro), rel_l2(s[:, heads], rs)
-    say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
-    assert eo <= TOL and es <= TOL, (eo, es)
+    say("  oracle on all 32 heads")
+    ro, rs = prefill_oracle(inp)
+    check_units(o, ro, s, rs, TOL, margin, label="T65536 H32")
 
 
 @pytest.mark.parametrize("nseq", [300, 2100])
@@ -256,3 +263,40 @@ def test_chunked_varlen_many_sequences(nseq):
     o, s = _check(inp)
     empty = np.flatnonzero(lens == 0)
     np.testing.assert_array_equal(s[empty], inp.initial_state[empty])
+
+
+def test_chunked_bf16_routing_falls_back_to_token_by_token():
+    """bf16 inputs at dk = 128 with lower_bound < -5, or with an unaligned
+    pointer, take the token-by-token kernel: bit for bit its result, and
+    within the bar of the oracle."""
+    import torch
+    inp = workloads.prefill_inputs(2, 150, 2, 128, 64, seed=1300, init_state=True, lower_bound=-7.0)
+    say("chunked bf16 routing: lower_bound -7")
+    o, s = prefill_gpu(inp)
+    orc, src = prefill_gpu(inp, use_chunked=False)
+    np.testing.assert_array_equal(o, orc)
+    np.testing.assert_array_equal(s, src)
+    ro, rs = prefill_oracle(inp)
+    assert rel_l2(o, ro) <= TOL and rel_l2(s, rs) <= TOL
+
+    inp = workloads.prefill_inputs(1, 100, 2, 128, 128, seed=1301, init_state=True)
+    bf, f = torch.bfloat16, torch.float32
+
+    def unaligned(x, dtype):
+        flat = torch.empty(x.size + 1, dtype=dtype, device="cuda")
+        view = flat[1:].view(x.shape)          # 2 or 4 bytes past an allocation boundary
+        view.copy_(torch.from_numpy(np.ascontiguousarray(x)).to(dtype).to("cuda"))
+        return view
+
+    rest = [dev(x, f) for x in (inp.g, inp.beta, inp.a_log, inp.dt_bias, inp.initial_state)]
+    for name in ("q", "v"):
+        say("chunked bf16 routing: unaligned", name)
+        q = unaligned(inp.q, bf) if name == "q" else dev(inp.q, bf)
+        v = unaligned(inp.v, bf) if name == "v" else dev(inp.v, bf)
+        k = dev(inp.k, bf)
+        o_u, s_u = kda.prefill(q, k, v, *rest, scale=inp.scale, lower_bound=inp.lower_bound,
+                               return_state=True)
+        o_r, s_r = kda.prefill(q, k, v, *rest, scale=inp.scale, lower_bound=inp.lower_bound,
+                               use_chunked=False, return_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_u, o_r) and torch.equal(s_u, s_r)

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_90_amd import workloads
-from tests._common import decode_gpu, decode_oracle, prefill_gpu, prefill_oracle, rel_l2, say
+from tests._common import check_units, decode_gpu, decode_oracle, prefill_gpu, prefill_oracle, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -71,11 +71,17 @@ def test_chunked_grouped_ejk_varlen():
     _check_prefill(inp, 2e-2)
 
 
-def test_chunked_grouped_full_size_b4_t4096_h16_hkv4_sampled():
-    """The grouped benchmark workload; the oracle checks three (batch, head) items."""
+def test_chunked_grouped_full_size_b4_t4096_h16_hkv4_every_unit(margin):
+    """The grouped benchmark workload: bitwise equal to the ungrouped run on
+    repeated keys and values, and all 64 (batch, head) units against the oracle."""
     inp = workloads.prefill_grouped_b4_t4096_h16_hkv4_d128()
     say("chunked grouped B=4 T=4096 H=16 Hkv=4")
-    _check_prefill(inp, 2e-2, units=[0, 21, 63])
+    o, s = prefill_gpu(inp)
+    oe, se = prefill_gpu(_expanded(inp))
+    assert np.array_equal(o, oe) and np.array_equal(s, se)
+    del oe, se
+    ro, rs = prefill_oracle(inp)
+    check_units(o, ro, s, rs, 2e-2, margin, label="grouped B4 T4096 H16 Hkv4")
 
 
 @pytest.mark.parametrize("dk,dv,H,hkv,ejk", [(128, 128, 8, 2, False), (16, 64, 6, 3, False),
@@ -93,9 +99,9 @@ def test_decode_grouped(dk, dv, H, hkv, ejk):
     assert rel_l2(out, ro) <= 1e-5 and rel_l2(S, rS) <= 1e-5, (rel_l2(out, ro), rel_l2(S, rS))
 
 
-def test_decode_grouped_full_size_b64_h32_hkv8():
+def test_decode_grouped_full_size_b64_h32_hkv8(margin):
     inp = workloads.decode_grouped_b64_h32_hkv8_d128()
     say("decode grouped B=64 H=32 Hkv=8")
     out, S = decode_gpu(inp)
     ro, rS = decode_oracle(inp)
-    assert rel_l2(out, ro) <= 1e-5 and rel_l2(S, rS) <= 1e-5, (rel_l2(out, ro), rel_l2(S, rS))
+    check_units(out[:, None], ro[:, None], S, rS, 1e-5, margin, label="decode grouped B64 H32 Hkv8")
