@@ -20,7 +20,7 @@ import contextlib
 import ctypes
 import os
 
-__all__ = ["prefill", "decode_step", "KdaError", "lib", "LIB_PATH",
+__all__ = ["prefill", "prefill_noalloc", "decode_step", "KdaError", "lib", "LIB_PATH",
            "QK_L2NORM", "CHUNKED", "EJK", "F32", "BF16", "prefill_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
                               i32, i32, i32, i32, f32, f32, i32, u32, vp, ctypes.c_int, fp, vp,
                               ctypes.c_size_t, vp]
     L.kda_prefill.restype = ctypes.c_int
+    L.kda_prefill_noalloc.argtypes = L.kda_prefill.argtypes[:24] + [vp]
+    L.kda_prefill_noalloc.restype = ctypes.c_int
     L.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, u32]
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_decode_step.argtypes = [fp, fp, fp, fp, fp, fp, fp, f32, f32, i32, i32, i32, i32, i32, u32,
@@ -112,7 +114,7 @@ def prefill_workspace_bytes(num_seqs, B, T, H, dk, dv, flags, in_dtype=BF16) -> 
 def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_seqlens=None, *,
             scale=None, lower_bound=-5.0, chunk_size=64, use_qk_l2norm=True, use_chunked=True,
             ejk=False, return_state=False, out_dtype=None, out=None, final_state=None,
-            stream=None):
+            stream=None, _noalloc=False):
     """KDA over whole sequences.  q [B, T, H, dk], k [B, T, Hkv, dk] and
     v [B, T, Hkv, dv] in bf16 or fp32 (Hkv divides H: head h reads the key and
     value of head h // (H // Hkv)); g [B, T, H, dk] raw gate (EJK: [B, T, H]
@@ -171,18 +173,30 @@ def prefill(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_s
             (EJK if ejk else 0)
         nseq = N if cu_seqlens is not None else 0
         idt = BF16 if q.dtype == torch.bfloat16 else F32
-        wsb = prefill_workspace_bytes(nseq, B, T, H, dk, dv, flags, idt)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb > 0 else None
         sc = -1.0 if scale is None else float(scale)
-        _check(lib().kda_prefill(
-            _ptr(q), _ptr(k), _ptr(v), idt,
-            _ptr(g), _ptr(beta), _ptr(a_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_seqlens),
-            nseq, B, T, H, Hkv, dk, dv, sc, float(lower_bound), int(chunk_size), flags,
-            _ptr(out), BF16 if odt == torch.bfloat16 else F32, _ptr(final_state), _ptr(ws), wsb,
-            _stream(dev, stream)))
+        common = (_ptr(q), _ptr(k), _ptr(v), idt,
+                  _ptr(g), _ptr(beta), _ptr(a_log), _ptr(dt_bias), _ptr(initial_state), _ptr(cu_seqlens),
+                  nseq, B, T, H, Hkv, dk, dv, sc, float(lower_bound), int(chunk_size), flags,
+                  _ptr(out), BF16 if odt == torch.bfloat16 else F32, _ptr(final_state))
+        if _noalloc:
+            _check(lib().kda_prefill_noalloc(*common, _stream(dev, stream)))
+        else:
+            wsb = prefill_workspace_bytes(nseq, B, T, H, dk, dv, flags, idt)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb > 0 else None
+            _check(lib().kda_prefill(*common, _ptr(ws), wsb, _stream(dev, stream)))
     if return_state:
         return out, final_state
     return out
+
+
+def prefill_noalloc(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None,
+                    cu_seqlens=None, **kw):
+    """prefill() through kda_prefill_noalloc: the library call allocates
+    nothing; the chunked path's scratch is the library's fixed device array of
+    KDA_NOALLOC_SCRATCH_BYTES per GPU (shared by every call on that GPU, so
+    calls that overlap in time on one GPU race).  Pass ``out`` (and
+    ``final_state``) to keep this wrapper from allocating them with torch."""
+    return prefill(q, k, v, g, beta, a_log, dt_bias, initial_state, cu_seqlens, _noalloc=True, **kw)
 
 
 def decode_step(q, k, v, g, beta, a_log, dt_bias, S, *, scale=None, lower_bound=-5.0,

@@ -66,14 +66,17 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
     return kda::chunked_workspace_bytes(N, T, H, dk, dv, packed);
 }
 
-kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
-                         const float* g, const float* beta, const float* a_log,
-                         const float* dt_bias, const float* initial_state,
-                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
-                         int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale, float lower_bound,
-                         int32_t chunk_size, uint32_t flags, void* o, kda_dtype_t out_dtype,
-                         float* final_state, void* workspace, size_t workspace_bytes,
-                         void* stream)
+// kda_prefill and kda_prefill_noalloc: with noalloc set, the chunked MFMA
+// route takes its workspace from the library's fixed scratch array instead of
+// workspace / workspace_bytes.
+static kda_status_t prefill_impl(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                                 const float* g, const float* beta, const float* a_log,
+                                 const float* dt_bias, const float* initial_state,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                 int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale,
+                                 float lower_bound, int32_t chunk_size, uint32_t flags, void* o,
+                                 kda_dtype_t out_dtype, float* final_state, void* workspace,
+                                 size_t workspace_bytes, void* stream, bool noalloc)
 {
     if (flags & ~kKnownFlags) return fail(KDA_EINVAL, "kda_prefill: unknown flag bits 0x%x", flags & ~kKnownFlags);
     const bool ejk = (flags & KDA_EJK) != 0;
@@ -141,14 +144,49 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
     if (chunk_ok && kda::chunked_supported(a) && a16(v) && a16(o)) {
         // the MFMA kernel also moves v and o 16 bytes per lane
         const size_t need = kda::chunked_workspace_bytes(N, T, H, dk, dv, cu_seqlens != nullptr);
-        if (need > 0 && (!workspace || workspace_bytes < need))
+        if (noalloc) {
+            if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+                return fail(KDA_EUNSUPPORTED, "kda_prefill_noalloc: the call needs %zu bytes of scratch, "
+                            "more than the library's fixed %zu", need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+            const hipError_t e = kda::noalloc_scratch(&a.workspace);
+            if (e != hipSuccess) return hip_status(e, "kda_prefill_noalloc: address of the scratch array");
+            a.workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+        } else if (need > 0 && (!workspace || workspace_bytes < need)) {
             return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        }
         return hip_status(kda::launch_chunked(a, st), "kda_prefill (chunked)");
     }
     if (chunk_ok && kda::chunked_f32_supported(a))
         return hip_status(kda::launch_chunked_f32(a, st), "kda_prefill (chunked float32)");
     // token-by-token path; with T == 0 it only carries initial_state to final_state
     return hip_status(kda::launch_recurrent(a, st), "kda_prefill (recurrent)");
+}
+
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                         const float* g, const float* beta, const float* a_log,
+                         const float* dt_bias, const float* initial_state,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                         int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale, float lower_bound,
+                         int32_t chunk_size, uint32_t flags, void* o, kda_dtype_t out_dtype,
+                         float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream)
+{
+    return prefill_impl(q, k, v, in_dtype, g, beta, a_log, dt_bias, initial_state, cu_seqlens, num_seqs,
+                        B, T, H, Hkv, dk, dv, scale, lower_bound, chunk_size, flags, o, out_dtype,
+                        final_state, workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                                 const float* g, const float* beta, const float* a_log,
+                                 const float* dt_bias, const float* initial_state,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                 int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale,
+                                 float lower_bound, int32_t chunk_size, uint32_t flags, void* o,
+                                 kda_dtype_t out_dtype, float* final_state, void* stream)
+{
+    return prefill_impl(q, k, v, in_dtype, g, beta, a_log, dt_bias, initial_state, cu_seqlens, num_seqs,
+                        B, T, H, Hkv, dk, dv, scale, lower_bound, chunk_size, flags, o, out_dtype,
+                        final_state, nullptr, 0, stream, true);
 }
 
 kda_status_t kda_decode_step(const float* q, const float* k, const float* g, const float* v,

@@ -74,5 +74,8 @@ size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
 // the float32 chunked kernel (16-token chunks on the vector ALUs)
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
+// device address, on the current device, of the fixed scratch array of
+// KDA_NOALLOC_SCRATCH_BYTES that kda_prefill_noalloc uses as its workspace
+hipError_t noalloc_scratch(void** out);
 
 }  // namespace kda

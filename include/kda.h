@@ -131,6 +131,32 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
                          float* final_state, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * kda_prefill_noalloc - kda_prefill without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Arguments, routing,
+ * results and status codes are those of kda_prefill; the call itself
+ * allocates nothing.  The chunked MFMA route takes its workspace from a fixed
+ * device array of KDA_NOALLOC_SCRATCH_BYTES (256 MiB) inside the library: one
+ * copy per GPU, held from the library's first use on that GPU until the
+ * process ends.  A call that takes that route and needs more than that
+ * (kda_prefill_workspace_bytes() of its arguments; about 1 KiB per token and
+ * head, e.g. 16384 tokens at H = 16) returns KDA_EUNSUPPORTED before any
+ * launch.  The array is used on the calling thread's current HIP device,
+ * which must be the device of `stream` and of the tensors.  Every call on one
+ * GPU shares the array and leaves its contents behind: calls that may overlap
+ * in time on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller; calls on one stream are ordered already.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                                 const float* g, const float* beta, const float* a_log,
+                                 const float* dt_bias, const float* initial_state,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                 int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale,
+                                 float lower_bound, int32_t chunk_size, uint32_t flags, void* o,
+                                 kda_dtype_t out_dtype, float* final_state, void* stream);
+
 /* Device workspace (bytes) kda_prefill needs for these arguments; 0 = none.
  * Only the chunked MFMA path uses it: per (chunk, head) it holds the
  * state-independent operands of that chunk (64.5 KiB), plus the chunk

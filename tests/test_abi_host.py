@@ -137,6 +137,23 @@ def test_prefill_routing(over, kernel):
     assert kernel + ":" in kda.lib().kda_last_error().decode()
 
 
+def test_prefill_noalloc_rejects_calls_beyond_its_scratch():
+    """The size check is on the host, before any HIP call (placeholder pointers)."""
+    text = open(HEADER).read()
+    assert re.search(r"KDA_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)256 << 20\)", text)
+    L = kda.lib()
+    need = L.kda_prefill_workspace_bytes(0, 1, 1 << 16, 16, 128, 128, kda.BF16, kda.QK_L2NORM | kda.CHUNKED)
+    assert need > (256 << 20)
+    st = L.kda_prefill_noalloc(P, P, P, kda.BF16, P, P, P, P, None, None, 0, 1, 1 << 16, 16, 0, 128, 128,
+                               -1.0, -5.0, 64, kda.QK_L2NORM | kda.CHUNKED, P, kda.BF16, None, None)
+    assert st == kda.KDA_EUNSUPPORTED
+    assert "scratch" in L.kda_last_error().decode()
+    # argument errors come first, as for kda_prefill
+    st = L.kda_prefill_noalloc(None, P, P, kda.BF16, P, P, P, P, None, None, 0, 1, 1 << 16, 16, 0, 128, 128,
+                               -1.0, -5.0, 64, kda.QK_L2NORM | kda.CHUNKED, P, kda.BF16, None, None)
+    assert st == kda.KDA_EINVAL
+
+
 def test_prefill_empty_problems_are_no_ops():
     assert _prefill(B=0) == kda.KDA_OK
     assert _prefill(T=0) == kda.KDA_OK  # no final_state requested: nothing to do
