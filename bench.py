@@ -115,20 +115,24 @@ def _counter_traffic(name, src_hash):
         return None
 
 
-def prefill_counters(ms):
-    """Counter figures of the B4 T4096 H16 prefill call from its committed
-    summary (HBM traffic, executed bf16 MFMA flops, MFMA busy fraction), with
-    the executed flops turned into a fraction of peak over this run's time;
-    all None once the kernel source has changed since they were taken."""
+def prefill_counters(ms, name="chunked_prefill_b4_t4096_h16_d128", alg_bytes=None):
+    """Counter figures of a chunked prefill workload from its committed summary
+    (profiles/<name>_pmc.txt: HBM traffic, executed bf16 MFMA flops, MFMA busy
+    fraction), with the executed flops turned into a fraction of peak over this
+    run's time and the traffic into a ratio to the algorithmic bytes; all None
+    once the kernel source has changed since they were taken."""
     sh = _src_hash("kda_chunked.hip", "kda_device.h")
-    kv = _profile_kv("chunked_prefill_b4_t4096_h16_d128", sh)
-    res = {"traffic": None, "mfma_flops": None, "mfma_frac": None, "mfma_busy_frac": None,
-           "src_hash": sh, "source": "profiles/chunked_prefill_b4_t4096_h16_d128_pmc.txt"}
+    kv = _profile_kv(name, sh)
+    res = {"traffic": None, "traffic_over_alg": None, "mfma_flops": None, "mfma_frac": None,
+           "mfma_busy_frac": None, "src_hash": sh, "source": f"profiles/{name}_pmc.txt"}
     if kv:
         try:
+            tr = int(float(kv["hbm_bytes_per_call"]))
+            res["traffic"] = tr
+            if alg_bytes:
+                res["traffic_over_alg"] = round(tr / alg_bytes, 3)
             fl = int(float(kv["mfma_bf16_flops_per_call"]))
-            res.update(traffic=int(float(kv["hbm_bytes_per_call"])), mfma_flops=fl,
-                       mfma_frac=round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS, 4),
+            res.update(mfma_flops=fl, mfma_frac=round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS, 4),
                        mfma_busy_frac=float(kv["mfma_busy_frac"]))
         except (KeyError, ValueError):
             pass
@@ -200,13 +204,61 @@ def rel_l2(x, ref):
     return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
 
 
-def cpu_decode_baseline(inp, budget_s=10.0, check=None):
-    """The float64 oracle on full decode steps, repeated for about budget_s.
-    With check = (out, S_new) of the GPU's step from the same state, the first
-    oracle step also gives the parity of the benchmarked configuration."""
+def _unit_worst(o, ro, s, rs, cu=None):
+    """Worst relative L2 over (sequence, head) units, for o [B, T, H, dv] (packed:
+    B = 1, sequence n is rows cu[n]:cu[n+1]) and states [N, H, dk, dv]."""
+    N, H = rs.shape[:2]
+    wo = ws = 0.0
+    for n in range(N):
+        if cu is None:
+            on, ron = o[n], ro[n]
+        else:
+            on, ron = o[0, int(cu[n]):int(cu[n + 1])], ro[0, int(cu[n]):int(cu[n + 1])]
+        for h in range(H):
+            if on.shape[0]:
+                wo = max(wo, rel_l2(on[:, h], ron[:, h]))
+            ws = max(ws, rel_l2(s[n, h], rs[n, h]))
+    return wo, ws
+
+
+def cpu_info():
+    """Host figures reported with every CPU leg: logical CPUs of the machine,
+    its CPU model, and the oracle's OpenMP thread count (the cores it uses)."""
     from oracle import kda_oracle
     kda_oracle.build(force=False)
-    threads = kda_oracle.max_threads()
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = None
+    return {"cores": kda_oracle.max_threads(), "threads": kda_oracle.max_threads(),
+            "nproc": os.cpu_count(), "cpus_available": avail, "cpu_model": model}
+
+
+def _median3(fn, runs=3):
+    """Wall times of `runs` calls of fn (steady clock); (median, all)."""
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), [round(t, 3) for t in ts]
+
+
+def cpu_decode_baseline(inp, budget_s=10.0, check=None):
+    """The float64 oracle on full decode steps: a sample of n steps, timed three
+    times, median reported (n set so the three take about budget_s).  With
+    check = (out, S_new) of the GPU's step from the same state, the first
+    oracle step also gives the parity of the benchmarked configuration."""
+    from oracle import kda_oracle
+    info = cpu_info()
     t0 = time.perf_counter()
     ro, rS = kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
                                scale=inp.scale, lower_bound=inp.lower_bound)
@@ -216,26 +268,68 @@ def cpu_decode_baseline(inp, budget_s=10.0, check=None):
         parity = {"rel_l2_out": rel_l2(check[0], ro), "rel_l2_state": rel_l2(check[1], rS), "bar": 1e-5,
                   "sample": "one step of all 64 x 32 (request, head) items"}
         parity["ok"] = parity["rel_l2_out"] <= 1e-5 and parity["rel_l2_state"] <= 1e-5
-    reps = max(1, int(budget_s / max(one, 1e-3)))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
-                          scale=inp.scale, lower_bound=inp.lower_bound)
-    el = time.perf_counter() - t0
-    res = {"value": round(reps / el, 3), "unit": "decode steps/s", "cores": threads,
-           "kind": "oracle",
-           "sample": f"{reps} full decode steps (B=64, H=32, dk=dv=128, float64) in {el:.1f} s"}
+    reps = max(1, int(budget_s / 3 / max(one, 1e-3)))
+
+    def run():
+        for _ in range(reps):
+            kda_oracle.decode(inp.q, inp.k, inp.g, inp.v, inp.beta, inp.a_log, inp.dt_bias, inp.S,
+                              scale=inp.scale, lower_bound=inp.lower_bound)
+
+    el, runs = _median3(run)
+    res = dict({"value": round(reps / el, 3), "unit": "decode steps/s", "kind": "oracle",
+                "sample": f"{reps} full decode steps (B=64, H=32, dk=dv=128, float64) per run; "
+                          f"median of 3 runs {runs} s"}, **info)
     if parity is not None:
         res["parity"] = parity
     return res
 
 
+def _cpu_prefill_leg(inp, heads, runs, what, check=None):
+    """The float64 oracle on the given heads of a prefill workload (every
+    sequence of it), timed `runs` times; reported as tokens/s over all heads
+    (the sample's time scaled by H / len(heads)).  With check = (o, final
+    state) of the GPU call on the same inputs, the first run also gives the
+    parity of those heads, per (sequence, head) unit."""
+    from oracle import kda_oracle
+    info = cpu_info()
+    H = inp.q.shape[2]
+    hs = list(heads)
+    hkv = inp.k.shape[2]
+    kv = sorted({h // (H // hkv) for h in hs})
+    kmap = [kv.index(h // (H // hkv)) for h in hs]
+    if len(hs) % len(kv) or kmap != [i // (len(hs) // len(kv)) for i in range(len(hs))]:
+        raise ValueError("sampled heads must be whole, equal groups of their key/value heads")
+    args = (inp.q[:, :, hs], inp.k[:, :, kv], inp.v[:, :, kv],
+            None if inp.g is None else inp.g[:, :, hs], inp.beta[:, :, hs],
+            None if inp.ejk else inp.a_log[hs], None if inp.ejk else inp.dt_bias[:, hs],
+            None if inp.initial_state is None else inp.initial_state[:, hs], inp.cu_seqlens)
+    kw = dict(scale=inp.scale, lower_bound=inp.lower_bound, ejk=inp.ejk)
+    out = {}
+
+    def run():
+        out["r"] = kda_oracle.prefill(*args, **kw)
+
+    el, times = _median3(run, runs)
+    ntok = int(inp.q.shape[0] * inp.q.shape[1])
+    res = dict({"value": round(ntok / (el * H / len(hs)), 1), "unit": f"prefill tokens/s (all {H} heads)",
+                "kind": "oracle",
+                "sample": f"{what}, heads {hs[0]}..{hs[-1]} ({len(hs)} of {H}), float64; "
+                          + (f"median of {runs} runs {times} s" if runs > 1 else f"one run {times} s")}, **info)
+    if check is not None:
+        ro, rs = out["r"]
+        o_gpu, s_gpu = check
+        wo, ws = _unit_worst(o_gpu[:, :, hs], ro, s_gpu[:, hs], rs, inp.cu_seqlens)
+        bar = 2e-2 if inp.dtype == "bf16" else 1e-5
+        res["parity"] = {"worst_unit_rel_l2_o": wo, "worst_unit_rel_l2_state": ws, "bar": bar,
+                         "ok": wo <= bar and ws <= bar,
+                         "sample": "every (sequence, head) unit of the sampled heads of the timed call"}
+    return res
+
+
 def cpu_prefill_baseline(budget_s=5.0, check=None):
     """The float64 oracle on a bounded sample of the B4 T4096 H16 workload: all
-    four sequences of the first few heads (enough (sequence, head) units for every
-    core), repeated for about budget_s; reported as tokens/s over all 16 heads.
-    With check = (o, final_state) of the timed GPU call, the first oracle run
-    also gives the parity of those heads."""
+    four sequences of the first few heads (enough (sequence, head) units for
+    every core), median of three runs; reported as tokens/s over all 16 heads."""
     from gated_delta_rule_90_amd import workloads
     from oracle import kda_oracle
     kda_oracle.build(force=False)
@@ -243,30 +337,7 @@ def cpu_prefill_baseline(budget_s=5.0, check=None):
     inp = workloads.prefill_b4_t4096_h16_d128()
     B, T, H, _ = inp.q.shape
     nh = min(H, max(1, -(-threads // B)))
-    hs = slice(0, nh)
-    args = (inp.q[:, :, hs], inp.k[:, :, hs], inp.v[:, :, hs], inp.g[:, :, hs], inp.beta[:, :, hs],
-            inp.a_log[hs], inp.dt_bias[:, hs])
-    t0 = time.perf_counter()
-    ro, rs = kda_oracle.prefill(*args, scale=inp.scale, lower_bound=inp.lower_bound)
-    one = time.perf_counter() - t0
-    parity = None
-    if check is not None:
-        o_gpu, s_gpu = check
-        parity = {"rel_l2_o": rel_l2(o_gpu[:, :, hs], ro), "rel_l2_state": rel_l2(s_gpu[:, hs], rs),
-                  "bar": 2e-2, "sample": f"heads 0..{nh - 1} of all 4 sequences of the timed call"}
-        parity["ok"] = parity["rel_l2_o"] <= 2e-2 and parity["rel_l2_state"] <= 2e-2
-    reps = max(1, int(budget_s / max(one, 1e-3)))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        kda_oracle.prefill(*args, scale=inp.scale, lower_bound=inp.lower_bound)
-    el = time.perf_counter() - t0
-    token_heads = reps * B * T * nh
-    res = {"value": round(token_heads / H / el, 1), "unit": "prefill tokens/s (all 16 heads)",
-           "cores": threads, "kind": "oracle",
-           "sample": f"{reps} x (4 sequences x 4096 tokens x {nh} heads), float64, in {el:.1f} s"}
-    if parity is not None:
-        res["parity"] = parity
-    return res
+    return _cpu_prefill_leg(inp, range(nh), 3, "4 sequences x 4096 tokens", check)
 
 
 def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=False, use_chunked=None):
@@ -391,11 +462,57 @@ def bench_prefill(steps, warmup):
     inp = workloads.prefill_b4_t4096_h16_d128()
     res = _prefill_run(inp, steps, warmup, nsets=2, keep=True)   # 2 x 408 MB: more than the Infinity Cache
     res.pop("path")
-    res["rocprof"] = prefill_counters(res["ms_per_call"])
+    res["rocprof"] = prefill_counters(res["ms_per_call"], alg_bytes=res["alg_bytes"])
     return dict({"workload": "kda_chunked_prefill_b4_t4096_h16_d128_bf16"}, **res)
 
 
-def bench_configs(steps, warmup):
+def _mfma_configs():
+    """The bf16 chunked-prefill workloads timed as configs:
+    name -> (input maker, timing options, CPU-leg heads, CPU-leg runs, CPU-leg description)."""
+    from gated_delta_rule_90_amd import workloads
+    return {
+        "prefill_long_t65536_h32_d128": (workloads.prefill_long_t65536_h32_d128, {"split": 32768},
+                                         "threads", 1, "1 sequence x 65536 tokens"),
+        "prefill_varlen_8seq_h32_d128": (workloads.prefill_varlen_8seq_h32_d128, {}, "threads/8", 3,
+                                         "8 packed sequences"),
+        "prefill_varlen_8seq_h32_d128_ejk": (lambda: workloads.prefill_varlen_8seq_h32_d128(ejk=True), {},
+                                             "threads/8", 3, "8 packed sequences, EJK"),
+        "prefill_grouped_b4_t4096_h16_hkv4_d128": (workloads.prefill_grouped_b4_t4096_h16_hkv4_d128,
+                                                   {"nsets": 2}, "threads/4", 3, "4 sequences x 4096 tokens"),
+    }
+
+
+def bench_one_mfma_config(name, steps, warmup, cpu=True, extras=True):
+    """Time one bf16 chunked-prefill workload; with cpu, also its sampled CPU
+    oracle leg (and the parity of the sampled heads of the timed call).
+    extras=False leaves out the calls beyond the timed ones (the split check),
+    so that a profiler run sees only full calls."""
+    import gc
+    from oracle import kda_oracle
+    make, kw, heads, runs, what = _mfma_configs()[name]
+    if not extras:
+        kw = {k: v for k, v in kw.items() if k != "split"}
+    inp = make()
+    res = _prefill_run(inp, steps, warmup, keep=cpu, **kw)
+    if inp.cu_seqlens is not None:
+        res["lengths"] = inp.meta["lengths"]
+    res["rocprof"] = prefill_counters(res["ms_per_call"], name, res["alg_bytes"])
+    if cpu:
+        check = res.pop("check")
+        H = inp.q.shape[2]
+        th = kda_oracle.max_threads()
+        nseq = inp.q.shape[0] if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
+        nh = min(H, max(1, th if heads == "threads" else -(-th // nseq)))
+        hkv = inp.k.shape[2]
+        nh = -(-nh // (H // hkv)) * (H // hkv)          # whole groups of key/value heads
+        res["cpu_baseline"] = _cpu_prefill_leg(inp, range(min(nh, H)), runs, what, check)
+        del check
+    del inp
+    gc.collect()
+    return res
+
+
+def bench_configs(steps, warmup, cpu=True):
     """The other workloads: each is generated on the host (seeded), uploaded,
     then timed; inputs are freed before the next one."""
     import gc
@@ -415,21 +532,9 @@ def bench_configs(steps, warmup):
     out["prefill_fp32_b1_t4096_h16_d128_token_by_token"] = _prefill_run(inp, steps, warmup)
     out["prefill_fp32_b1_t4096_h16_d128_chunked"] = _prefill_run(inp, steps, warmup, use_chunked=True)
     del inp
-    for name, make, kw in (
-            ("prefill_long_t65536_h32_d128", workloads.prefill_long_t65536_h32_d128, {"split": 32768}),
-            ("prefill_varlen_8seq_h32_d128", workloads.prefill_varlen_8seq_h32_d128, {}),
-            ("prefill_varlen_8seq_h32_d128_ejk", lambda: workloads.prefill_varlen_8seq_h32_d128(ejk=True), {})):
-        inp = make()
-        res = _prefill_run(inp, steps, warmup, **kw)
-        if inp.cu_seqlens is not None:
-            res["lengths"] = inp.meta["lengths"]
-        out[name] = res
-        del inp
-        gc.collect()
-    # grouped key/value heads (ejkernel "recurrent": num_kv_heads)
-    res = _prefill_run(workloads.prefill_grouped_b4_t4096_h16_hkv4_d128(), steps, warmup, nsets=2)
-    out["prefill_grouped_b4_t4096_h16_hkv4_d128"] = res
     gc.collect()
+    for name in _mfma_configs():
+        out[name] = bench_one_mfma_config(name, steps, warmup, cpu)
     # a decode step takes ~50 us: 20x the steps of the prefill configs, so that the
     # mean is not set by the first few calls
     _, dres = _decode_run(workloads.decode_grouped_b64_h32_hkv8_d128(), 20 * steps, 2 * warmup)
@@ -460,6 +565,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--config", default=None,
+                    help="time only this bf16 chunked-prefill workload (for profiler runs)")
     ap.add_argument("--calib", action="store_true",
                     help="run a 256 MiB device copy first (profiler counter calibration)")
     args = ap.parse_args()
@@ -473,6 +580,20 @@ def main():
         sys.exit(1)
     if args.calib:
         copy_calibration()
+    if args.config:
+        # one workload alone (profiling runs): its own timing only
+        if args.config == "prefill_b4_t4096_h16_d128":
+            res = bench_prefill(max(20, args.steps), args.warmup)
+            res.pop("check", None)
+        elif args.config in _mfma_configs():
+            res = bench_one_mfma_config(args.config, max(10, args.steps), args.warmup, cpu=False,
+                                        extras=False)
+        else:
+            print(f"bench.py: unknown --config {args.config}; one of prefill_b4_t4096_h16_d128, "
+                  + ", ".join(_mfma_configs()), file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"config": args.config, **res}), flush=True)
+        return
     inp, dec = bench_decode(args.steps, args.warmup)
     line = {
         "metric": METRIC,
@@ -489,10 +610,12 @@ def main():
     }
     pcheck = None
     if not args.no_prefill:
-        line["prefill"] = bench_prefill(max(5, args.steps // 10), max(2, args.warmup // 10))
+        # at least 20 calls (~5 ms of timed work) whatever --steps says
+        line["prefill"] = bench_prefill(max(20, args.steps), max(2, args.warmup // 2))
         pcheck = line["prefill"].pop("check")
     if not args.no_configs:
-        line["configs"] = bench_configs(max(3, args.steps // 40), max(1, args.warmup // 10))
+        line["configs"] = bench_configs(max(10, args.steps // 2), max(2, args.warmup // 2),
+                                        cpu=not args.no_cpu)
     dcheck = dec.pop("check")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_decode_baseline(inp, args.cpu_budget, check=dcheck)

@@ -117,3 +117,27 @@ def test_cpu_decode_leg_reports_parity_of_the_given_step():
     bad = bench.cpu_decode_baseline(inp, budget_s=0.05, check=(bad_out, rS))
     assert not bad["parity"]["ok"] and abs(bad["parity"]["rel_l2_out"] - 0.01) < 1e-3
     assert "parity" not in bench.cpu_decode_baseline(inp, budget_s=0.05)
+
+
+def test_cpu_info_and_prefill_leg_on_a_sample():
+    """The CPU prefill leg times the oracle on the sampled heads (median of the
+    runs), reports the host (cores, nproc, CPU model) and, with the GPU's
+    outputs, the worst per-unit parity of those heads."""
+    from gated_delta_rule_90_amd import workloads
+    from oracle import kda_oracle
+    info = bench.cpu_info()
+    assert info["cores"] == kda_oracle.max_threads() and info["nproc"] >= 1
+    inp = workloads.prefill_inputs(1, 0, 4, 16, 16, seed=9, lengths=[20, 0, 7], init_state=True, hkv=2)
+    ro, rs = kda_oracle.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.a_log, inp.dt_bias,
+                                inp.initial_state, inp.cu_seqlens, scale=inp.scale,
+                                lower_bound=inp.lower_bound)
+    res = bench._cpu_prefill_leg(inp, range(2), 3, "3 packed sequences",
+                                 check=(ro.astype(np.float32), rs.astype(np.float32)))
+    assert res["kind"] == "oracle" and res["value"] > 0 and "median of 3" in res["sample"]
+    assert res["parity"]["ok"] and res["parity"]["worst_unit_rel_l2_o"] < 1e-6
+    bad = ro.copy()
+    bad[0, 25, 1] *= 1.5                                 # one token of sequence 2, head 1
+    res = bench._cpu_prefill_leg(inp, range(2), 1, "3 packed sequences", check=(bad, rs))
+    assert not res["parity"]["ok"]
+    with pytest.raises(ValueError):
+        bench._cpu_prefill_leg(inp, [0, 1, 2], 1, "uneven groups")   # 2 + 1 heads per key/value head
