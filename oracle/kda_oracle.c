@@ -208,6 +208,266 @@ int kda_oracle_decode(const double* q, const double* k, const double* g, const d
     return 0;
 }
 
+/*
+ * Backward pass (reverse-mode gradient) of kda_oracle_prefill, token by token
+ * in float64.  The forward pass is the one above; the reverse sweep runs the
+ * chain rule back through each step, in reverse token order, then through the
+ * prologue.  Given dO = dL/do [Ntok, H, dv] and dS_T = dL/d(final state)
+ * (NULL = 0), it returns dL/d of every input: q, k, v, the raw gate g (KDA) or
+ * the decay d (EJK), the beta logits (KDA) or beta (EJK), a_log, dt_bias and
+ * the initial state.
+ *
+ * Per token, with S_prev the state before the step and S the state after it:
+ *   KDA forward: a = exp(gamma); Sd = Diag(a) S_prev; u = Sd^T kh; e = v - u;
+ *                S = Sd + beta kh e^T; o = S^T qh
+ *   reverse:     dS += qh dO^T;            dqh = S dO
+ *                de = beta dS^T kh;         dbeta = kh^T dS e;   dkh = beta dS e
+ *                dv = de;                   dSd = dS - kh de^T;  dkh -= Sd de
+ *                dgamma_i = a_i sum_j S_prev_ij dSd_ij;           dS <- Diag(a) dSd
+ *   EJK forward: u = S_prev^T kh; e = v - u; S = exp(d) S_prev + beta kh e^T; o = S^T qh
+ *   reverse:     as above with Sd = S_prev in the residual and
+ *                dd = exp(d) sum_ij S_prev_ij dS_ij;  dS <- exp(d) dS - kh de^T
+ *   prologue:    qh = s q / n_q, n_q = sqrt(q.q + eps): dq = s (dqh / n_q - q (q.dqh) / n_q^3)
+ *                kh = k / n_k:                        dk = dkh / n_k - k (k.dkh) / n_k^3
+ *                (without the L2 norm: dq = s dqh, dk = dkh)
+ *                gamma = lb sigmoid(x), x = exp(a_log) (g + dt_bias):
+ *                    dx = dgamma lb sigmoid(x) (1 - sigmoid(x));  dg = dx exp(a_log);
+ *                    d dt_bias += dg;  d a_log += dx x
+ *                beta = sigmoid(l): dl = dbeta beta (1 - beta)
+ * The states a reverse step needs are recomputed from checkpoints taken every
+ * 64 tokens by the forward pass (the same forward step, rerun).
+ * Grouped heads: dk and dv of a key/value head sum over the heads that read it.
+ */
+#define ORACLE_CKPT 64
+
+int kda_oracle_backward(const double* q, const double* k, const double* v, const double* g,
+                        const double* beta, const double* a_log, const double* dt_bias,
+                        const double* initial_state, const int64_t* cu_seqlens, int n_seqs,
+                        int H, int Hkv, int dk, int dv, double scale, double lower_bound, double eps,
+                        int use_l2norm, int ejk, const double* dO, const double* dS_final,
+                        double* dq, double* dk_out, double* dv_out, double* dg, double* dbeta,
+                        double* da_log, double* ddt_bias, double* dS0, int n_threads)
+{
+    if (n_seqs < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return 1;
+    scale = oracle_resolve_scale(scale, dk);
+    const int64_t ntok = n_seqs > 0 ? cu_seqlens[n_seqs] : 0;
+    const int G = H / Hkv;
+    /* per query head: dk and dv before the group sum; per unit: parameter partials */
+    double* dkq = (double*)calloc((size_t)(ntok > 0 ? ntok : 1) * H * dk, sizeof(double));
+    double* dvq = (double*)calloc((size_t)(ntok > 0 ? ntok : 1) * H * dv, sizeof(double));
+    double* da_part = (double*)calloc((size_t)(n_seqs > 0 ? n_seqs : 1) * H, sizeof(double));
+    double* ddt_part = (double*)calloc((size_t)(n_seqs > 0 ? n_seqs : 1) * H * dk, sizeof(double));
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int w = 0; w < n_seqs * H; ++w) {
+        const int n = w / H, h = w % H;
+        const int hk = h / G;
+        const int64_t t0 = cu_seqlens[n], t1 = cu_seqlens[n + 1];
+        const int64_t L = t1 - t0;
+        const size_t sz = (size_t)dk * dv;
+        const size_t soff = ((size_t)n * H + h) * sz;
+        const int nck = (int)((L + ORACLE_CKPT - 1) / ORACLE_CKPT);
+        double* ck = (double*)malloc(sizeof(double) * sz * (size_t)(nck + 1));
+        double* Sb = (double*)malloc(sizeof(double) * sz * (ORACLE_CKPT + 1));
+        double* dS = (double*)malloc(sizeof(double) * sz);
+        double* dSd = (double*)malloc(sizeof(double) * sz);
+        double* qh = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* kh = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* gam = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* de = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* otmp = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* dqh = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* dkh = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* dgam = (double*)malloc(sizeof(double) * (size_t)dk);
+        /* the prologue of token t (the same functions as the forward pass) */
+#define PROLOGUE(t)                                                                              \
+        const size_t th = (size_t)(t) * H + h, tkv = (size_t)(t) * Hkv + hk;                    \
+        oracle_normalise(q + th * dk, 1, dk, use_l2norm, eps, scale, qh);                        \
+        oracle_normalise(k + tkv * dk, 1, dk, use_l2norm, eps, 1.0, kh);                         \
+        double bt, dd = 0.0;                                                                     \
+        if (!ejk) {                                                                              \
+            oracle_gate(g + th * dk, 1, dt_bias, H, h, a_log[h], lower_bound, dk, gam);          \
+            bt = oracle_sigmoid(beta[th]);                                                       \
+        } else {                                                                                 \
+            dd = g ? g[th] : 0.0;                                                                \
+            bt = beta[th];                                                                       \
+        }
+        /* forward: checkpoints of the state before tokens 0, 64, 128, ... */
+        if (initial_state) memcpy(ck, initial_state + soff, sizeof(double) * sz);
+        else memset(ck, 0, sizeof(double) * sz);
+        memcpy(Sb, ck, sizeof(double) * sz);
+        for (int64_t j = 0; j < L; ++j) {
+            if (j > 0 && j % ORACLE_CKPT == 0) memcpy(ck + (size_t)(j / ORACLE_CKPT) * sz, Sb, sizeof(double) * sz);
+            PROLOGUE(t0 + j)
+            (void)dd;
+            oracle_step(Sb, dk, dv, qh, kh, v + tkv * dv, 1, gam, dd, bt, ejk, otmp, 1, u);
+        }
+        /* reverse sweep */
+        if (dS_final) memcpy(dS, dS_final + soff, sizeof(double) * sz);
+        else memset(dS, 0, sizeof(double) * sz);
+        double da = 0.0;
+        double* ddt = ddt_part + (size_t)w * dk;
+        for (int c = nck - 1; c >= 0; --c) {
+            const int64_t j0 = (int64_t)c * ORACLE_CKPT;
+            const int64_t j1 = (j0 + ORACLE_CKPT < L) ? j0 + ORACLE_CKPT : L;
+            /* Sb[m] = state before token j0 + m, Sb[j1 - j0] = state after the block */
+            memcpy(Sb, ck + (size_t)c * sz, sizeof(double) * sz);
+            for (int64_t j = j0; j < j1; ++j) {
+                double* Sn = Sb + (size_t)(j - j0 + 1) * sz;
+                memcpy(Sn, Sb + (size_t)(j - j0) * sz, sizeof(double) * sz);
+                PROLOGUE(t0 + j)
+                oracle_step(Sn, dk, dv, qh, kh, v + tkv * dv, 1, gam, dd, bt, ejk, otmp, 1, u);
+            }
+            for (int64_t j = j1 - 1; j >= j0; --j) {
+                const double* Sp = Sb + (size_t)(j - j0) * sz;      /* before the step */
+                const double* Sa = Sb + (size_t)(j - j0 + 1) * sz;  /* after the step */
+                PROLOGUE(t0 + j)
+                const double* vt = v + tkv * dv;
+                const double* dot = dO + th * dv;
+                /* Sd: the state the residual is taken against */
+                if (!ejk) {
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = exp(gam[i]);
+                        for (int jj = 0; jj < dv; ++jj) dSd[(size_t)i * dv + jj] = a * Sp[(size_t)i * dv + jj];
+                    }
+                } else {
+                    memcpy(dSd, Sp, sizeof(double) * sz);
+                }
+                const double* Sd = dSd;   /* holds Sd until it is overwritten below */
+                for (int jj = 0; jj < dv; ++jj) {
+                    double acc = 0.0;
+                    for (int i = 0; i < dk; ++i) acc += Sd[(size_t)i * dv + jj] * kh[i];
+                    e[jj] = vt[jj] - acc;
+                }
+                /* o = S^T qh */
+                for (int i = 0; i < dk; ++i)
+                    for (int jj = 0; jj < dv; ++jj) dS[(size_t)i * dv + jj] += qh[i] * dot[jj];
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int jj = 0; jj < dv; ++jj) acc += Sa[(size_t)i * dv + jj] * dot[jj];
+                    dqh[i] = acc;
+                }
+                /* S = Sd' + beta kh e^T (Sd' = Sd for KDA, exp(d) S_prev for EJK) */
+                double dbt = 0.0;
+                for (int jj = 0; jj < dv; ++jj) {
+                    double acc = 0.0;
+                    for (int i = 0; i < dk; ++i) acc += kh[i] * dS[(size_t)i * dv + jj];
+                    de[jj] = bt * acc;
+                    dbt += acc * e[jj];
+                }
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0, acc2 = 0.0;
+                    for (int jj = 0; jj < dv; ++jj) {
+                        acc += dS[(size_t)i * dv + jj] * e[jj];
+                        acc2 += Sd[(size_t)i * dv + jj] * de[jj];
+                    }
+                    dkh[i] = bt * acc - acc2;   /* e = v - Sd^T kh */
+                }
+                double* dvt = dvq + th * dv;
+                for (int jj = 0; jj < dv; ++jj) dvt[jj] = de[jj];
+                if (!ejk) {
+                    /* dSd = dS - kh de^T; dgamma_i = a_i sum_j S_prev_ij dSd_ij; dS <- Diag(a) dSd */
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = exp(gam[i]);
+                        double acc = 0.0;
+                        for (int jj = 0; jj < dv; ++jj) {
+                            const double x = dS[(size_t)i * dv + jj] - kh[i] * de[jj];
+                            acc += Sp[(size_t)i * dv + jj] * x;
+                            dS[(size_t)i * dv + jj] = a * x;
+                        }
+                        dgam[i] = a * acc;
+                    }
+                } else {
+                    /* S = exp(d) S_prev + beta kh (v - S_prev^T kh)^T */
+                    const double a = exp(dd);
+                    double acc = 0.0;
+                    for (int i = 0; i < dk; ++i)
+                        for (int jj = 0; jj < dv; ++jj) {
+                            acc += Sp[(size_t)i * dv + jj] * dS[(size_t)i * dv + jj];
+                            dS[(size_t)i * dv + jj] = a * dS[(size_t)i * dv + jj] - kh[i] * de[jj];
+                        }
+                    if (dg) dg[th] = a * acc;
+                }
+                /* prologue */
+                {
+                    const double* qr = q + th * dk;
+                    const double* kr = k + tkv * dk;
+                    double* dqr = dq + th * dk;
+                    double* dkr = dkq + th * dk;
+                    if (use_l2norm) {
+                        double ssq = 0.0, ssk = 0.0, pq = 0.0, pk = 0.0;
+                        for (int i = 0; i < dk; ++i) {
+                            ssq += qr[i] * qr[i]; ssk += kr[i] * kr[i];
+                            pq += qr[i] * dqh[i]; pk += kr[i] * dkh[i];
+                        }
+                        const double nq = sqrt(ssq + eps), nk = sqrt(ssk + eps);
+                        for (int i = 0; i < dk; ++i) {
+                            dqr[i] = scale * (dqh[i] / nq - qr[i] * pq / (nq * nq * nq));
+                            dkr[i] = dkh[i] / nk - kr[i] * pk / (nk * nk * nk);
+                        }
+                    } else {
+                        for (int i = 0; i < dk; ++i) { dqr[i] = scale * dqh[i]; dkr[i] = dkh[i]; }
+                    }
+                    if (!ejk) {
+                        const double ea = exp(a_log[h]);
+                        const double* gr = g + th * dk;
+                        for (int i = 0; i < dk; ++i) {
+                            const double x = ea * (gr[i] + (dt_bias ? dt_bias[(size_t)i * H + h] : 0.0));
+                            const double sg = oracle_sigmoid(x);
+                            const double dx = dgam[i] * lower_bound * sg * (1.0 - sg);
+                            dg[th * dk + i] = dx * ea;
+                            ddt[i] += dx * ea;
+                            da += dx * x;
+                        }
+                        dbeta[th] = dbt * bt * (1.0 - bt);
+                    } else {
+                        dbeta[th] = dbt;
+                    }
+                }
+            }
+        }
+        if (dS0) memcpy(dS0 + soff, dS, sizeof(double) * sz);
+        da_part[w] = da;
+#undef PROLOGUE
+        free(ck); free(Sb); free(dS); free(dSd); free(qh); free(kh); free(gam); free(u); free(e);
+        free(de); free(otmp); free(dqh); free(dkh); free(dgam);
+    }
+    /* group sums for k and v; parameter sums over sequences (fixed order) */
+    for (int64_t t = 0; t < ntok; ++t)
+        for (int hv = 0; hv < Hkv; ++hv) {
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int r = 0; r < G; ++r) acc += dkq[((size_t)t * H + hv * G + r) * dk + i];
+                dk_out[((size_t)t * Hkv + hv) * dk + i] = acc;
+            }
+            for (int jj = 0; jj < dv; ++jj) {
+                double acc = 0.0;
+                for (int r = 0; r < G; ++r) acc += dvq[((size_t)t * H + hv * G + r) * dv + jj];
+                dv_out[((size_t)t * Hkv + hv) * dv + jj] = acc;
+            }
+        }
+    if (!ejk) {
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int n = 0; n < n_seqs; ++n) acc += da_part[(size_t)n * H + h];
+            if (da_log) da_log[h] = acc;
+            for (int i = 0; i < dk; ++i) {
+                double a2 = 0.0;
+                for (int n = 0; n < n_seqs; ++n) a2 += ddt_part[((size_t)n * H + h) * dk + i];
+                if (ddt_bias) ddt_bias[(size_t)i * H + h] = a2;
+            }
+        }
+    }
+    free(dkq); free(dvq); free(da_part); free(ddt_part);
+    return 0;
+}
+
 int kda_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -50,6 +50,9 @@ def _load():
         lib.kda_oracle_decode.argtypes = [P, P, P, P, P, P, P, D, D, D, I, I, I, I, I, I, I, P, P, I]
         lib.kda_oracle_decode.restype = I
         lib.kda_oracle_max_threads.restype = I
+        lib.kda_oracle_backward.argtypes = [P, P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_int64), I, I, I,
+                                            I, I, D, D, D, I, I, P, P, P, P, P, P, P, P, P, P, I]
+        lib.kda_oracle_backward.restype = I
         _lib = lib
     return _lib
 
@@ -148,3 +151,50 @@ def decode(q, k, g, v, beta, a_log, dt_bias, S, scale=None, lower_bound=-5.0,
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments")
     return out, S_new
+
+
+def backward(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_seqlens=None,
+             d_o=None, d_final_state=None, scale=None, lower_bound=-5.0, use_qk_l2norm=True,
+             ejk=False, threads=0, eps=EPS):
+    """Gradients of the prefill (o and the final state) with respect to every
+    input, by a float64 reverse sweep of the token recurrence (see
+    kda_oracle_backward in kda_oracle.c).  Arguments as prefill(); d_o
+    [B, T, H, dv] is dL/do and d_final_state [N, H, dk, dv] dL/d(final state)
+    (None = 0).  Returns a dict with dq, dk, dv (shapes of q, k, v), dg (shape
+    of g: the raw gate for KDA, the decay for EJK, given even where g is None),
+    dbeta (dL/d beta logit for KDA, dL/d beta for EJK), da_log [H],
+    ddt_bias [dk, H] (KDA) and d_initial_state [N, H, dk, dv]."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, dk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("cu_seqlens requires batch 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n = cu.shape[0] - 1
+    g = _f64(g)
+    beta = _f64(beta)
+    a_log = _f64(np.zeros(H) if a_log is None else np.reshape(a_log, (H,)))
+    dt_bias = _f64(dt_bias)
+    s0 = _f64(initial_state)
+    do = _f64(np.zeros((B, T, H, dv)) if d_o is None else d_o)
+    dsf = _f64(d_final_state)
+    out = {"dq": np.zeros((B, T, H, dk)), "dk": np.zeros((B, T, Hkv, dk)), "dv": np.zeros((B, T, Hkv, dv)),
+           "dg": np.zeros((B, T, H) if ejk else (B, T, H, dk)), "dbeta": np.zeros((B, T, H)),
+           "da_log": np.zeros(H), "ddt_bias": np.zeros((dk, H)), "d_initial_state": np.zeros((n, H, dk, dv))}
+    sc = -1.0 if scale is None else float(scale)
+    rc = lib.kda_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(a_log), _ptr(dt_bias),
+                                 _ptr(s0), cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, H, Hkv, dk,
+                                 dv, sc, float(lower_bound), float(eps), int(bool(use_qk_l2norm)),
+                                 int(bool(ejk)), _ptr(do), _ptr(dsf), _ptr(out["dq"]), _ptr(out["dk"]),
+                                 _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["da_log"]),
+                                 _ptr(out["ddt_bias"]), _ptr(out["d_initial_state"]), int(threads))
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments")
+    if ejk:
+        del out["da_log"], out["ddt_bias"]
+    return out
