@@ -20,7 +20,7 @@ import contextlib
 import ctypes
 import os
 
-__all__ = ["prefill", "prefill_noalloc", "decode_step", "KdaError", "lib", "LIB_PATH",
+__all__ = ["prefill", "prefill_noalloc", "prefill_backward", "decode_step", "KdaError", "lib", "LIB_PATH",
            "QK_L2NORM", "CHUNKED", "EJK", "F32", "BF16", "prefill_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -55,6 +55,12 @@ def lib() -> ctypes.CDLL:
     L.kda_prefill.restype = ctypes.c_int
     L.kda_prefill_noalloc.argtypes = L.kda_prefill.argtypes[:24] + [vp]
     L.kda_prefill_noalloc.restype = ctypes.c_int
+    L.kda_prefill_backward.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, fp, fp, ip, i32, i32, i32, i32,
+                                       i32, i32, i32, f32, f32, u32, vp, ctypes.c_int, fp, fp, fp, fp, fp,
+                                       fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    L.kda_prefill_backward.restype = ctypes.c_int
+    L.kda_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.kda_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
     L.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, u32]
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_decode_step.argtypes = [fp, fp, fp, fp, fp, fp, fp, f32, f32, i32, i32, i32, i32, i32, u32,
@@ -197,6 +203,74 @@ def prefill_noalloc(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=No
     calls that overlap in time on one GPU race).  Pass ``out`` (and
     ``final_state``) to keep this wrapper from allocating them with torch."""
     return prefill(q, k, v, g, beta, a_log, dt_bias, initial_state, cu_seqlens, _noalloc=True, **kw)
+
+
+def prefill_backward(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_seqlens=None,
+                     d_o=None, d_final_state=None, *, scale=None, lower_bound=-5.0, use_qk_l2norm=True,
+                     ejk=False, stream=None):
+    """Gradients of prefill() (kda_prefill_backward).  Inputs as prefill();
+    d_o [B, T, H, dv] (float32 or bf16) is dL/do and d_final_state
+    [N, H, dk, dv] dL/d(final state) (None = 0).  Returns a dict of float32
+    tensors: dq, dk, dv (shapes of q, k, v), dg (shape of g: [B, T, H, dk]
+    for KDA, [B, T, H] for EJK), dbeta ([B, T, H]: dL/d logit for KDA,
+    dL/d beta for EJK), d_initial_state [N, H, dk, dv] and, for KDA,
+    da_log [H] and ddt_bias [dk, H]."""
+    import torch
+    dev = q.device
+    io = (torch.bfloat16, torch.float32)
+    f = (torch.float32,)
+    _dev("q", q, io, dev)
+    _dev("k", k, (q.dtype,), dev)
+    _dev("v", v, (q.dtype,), dev)
+    _dev("g", g, f, dev)
+    _dev("beta", beta, f, dev)
+    _dev("a_log", a_log, f, dev)
+    _dev("dt_bias", dt_bias, f, dev)
+    _dev("initial_state", initial_state, f, dev)
+    _dev("cu_seqlens", cu_seqlens, (torch.int32,), dev)
+    _dev("d_o", d_o, io, dev)
+    _dev("d_final_state", d_final_state, f, dev)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape[:2] != q.shape[:2] or \
+            k.shape[3] != q.shape[3] or v.shape[:3] != k.shape[:3] or q.shape[2] % k.shape[2] != 0:
+        raise ValueError("q must be [B, T, H, dk], k [B, T, Hkv, dk] and v [B, T, Hkv, dv], Hkv dividing H")
+    B, T, H, dk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[3]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    if d_o is None or tuple(d_o.shape) != (B, T, H, dv):
+        raise ValueError("d_o must be [B, T, H, dv]")
+    if beta.shape != (B, T, H):
+        raise ValueError("beta must be [B, T, H]")
+    if g is not None and tuple(g.shape) != ((B, T, H) if ejk else (B, T, H, dk)):
+        raise ValueError("g must be [B, T, H, dk] (EJK: [B, T, H])")
+    for name, t, shp in (("initial_state", initial_state, (N, H, dk, dv)),
+                         ("d_final_state", d_final_state, (N, H, dk, dv)), ("dt_bias", dt_bias, (dk, H))):
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be {list(shp)}")
+    if a_log is not None and a_log.numel() != H:
+        raise ValueError("a_log must hold H values")
+    with _on(stream):
+        e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+        out = {"dq": e(B, T, H, dk), "dk": e(B, T, Hkv, dk), "dv": e(B, T, Hkv, dv),
+               "dg": e(B, T, H) if ejk else e(B, T, H, dk), "dbeta": e(B, T, H),
+               "d_initial_state": e(N, H, dk, dv)}
+        if not ejk:
+            out["da_log"] = e(H)
+            out["ddt_bias"] = e(dk, H)
+        nseq = N if cu_seqlens is not None else 0
+        wsb = int(lib().kda_prefill_backward_workspace_bytes(nseq, B, T, H, Hkv, dk, dv))
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        flags = (QK_L2NORM if use_qk_l2norm else 0) | (EJK if ejk else 0)
+        sc = -1.0 if scale is None else float(scale)
+        idt = BF16 if q.dtype == torch.bfloat16 else F32
+        _check(lib().kda_prefill_backward(
+            _ptr(q), _ptr(k), _ptr(v), idt, _ptr(g), _ptr(beta), _ptr(a_log), _ptr(dt_bias),
+            _ptr(initial_state), _ptr(cu_seqlens), nseq, B, T, H, Hkv, dk, dv, sc, float(lower_bound), flags,
+            _ptr(d_o), BF16 if d_o.dtype == torch.bfloat16 else F32, _ptr(d_final_state),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+            _ptr(out.get("da_log")), _ptr(out.get("ddt_bias")), _ptr(out["d_initial_state"]), _ptr(ws), wsb,
+            _stream(dev, stream)))
+    return out
 
 
 def decode_step(q, k, v, g, beta, a_log, dt_bias, S, *, scale=None, lower_bound=-5.0,

@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libkda.so")
 # (source, object name, extra flags): the recurrent kernel is built once per key
 # dimension so that its instantiations compile in parallel
 SOURCES = [("kda_api.cpp", "kda_api", []), ("kda_noalloc.cpp", "kda_noalloc", []), ("kda_decode.hip", "kda_decode", []),
-           ("kda_chunked.hip", "kda_chunked", []), ("kda_chunked_f32.hip", "kda_chunked_f32", [])] + \
+           ("kda_chunked.hip", "kda_chunked", []), ("kda_chunked_f32.hip", "kda_chunked_f32", []),
+           ("kda_backward.hip", "kda_backward", [])] + \
     [("kda_recurrent.hip", f"kda_recurrent_dk{dk}", [f"-DKDA_RECURRENT_DK={dk}"]) for dk in (16, 32, 64, 128)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

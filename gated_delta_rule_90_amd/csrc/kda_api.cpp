@@ -189,6 +189,96 @@ kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, kd
                         final_state, nullptr, 0, stream, true);
 }
 
+size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t Hkv,
+                                            int32_t dk, int32_t dv)
+{
+    if (B < 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    if (Hkv == 0) Hkv = H;
+    if (Hkv < 0 || H % Hkv != 0) return 0;
+    const bool packed = num_seqs > 0 && B == 1;
+    return kda::backward_workspace_bytes(packed ? num_seqs : B, T, H, Hkv, dk, dv, packed);
+}
+
+kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                                  const float* g, const float* beta, const float* a_log,
+                                  const float* dt_bias, const float* initial_state,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                  int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale,
+                                  float lower_bound, uint32_t flags, const void* d_o, kda_dtype_t do_dtype,
+                                  const float* d_final_state, float* dq, float* dk_out, float* dv_out,
+                                  float* dg, float* dbeta, float* da_log, float* ddt_bias,
+                                  float* d_initial_state, void* workspace, size_t workspace_bytes,
+                                  void* stream)
+{
+    if (flags & ~kKnownFlags)
+        return fail(KDA_EINVAL, "kda_prefill_backward: unknown flag bits 0x%x", flags & ~kKnownFlags);
+    const bool ejk = (flags & KDA_EJK) != 0;
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_EINVAL, "kda_prefill_backward: bad sizes B=%d T=%d H=%d dk=%d dv=%d", B, T, H, dk, dv);
+    if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
+        return fail(KDA_EINVAL, "kda_prefill_backward: unknown in_dtype %d", (int)in_dtype);
+    if (do_dtype != KDA_F32 && do_dtype != KDA_BF16)
+        return fail(KDA_EINVAL, "kda_prefill_backward: unknown do_dtype %d", (int)do_dtype);
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_EINVAL, "kda_prefill_backward: cu_seqlens requires B == 1 (got %d)", B);
+        if (num_seqs < 0) return fail(KDA_EINVAL, "kda_prefill_backward: num_seqs must be >= 0 with cu_seqlens");
+    } else if (num_seqs != 0 && num_seqs != B) {
+        return fail(KDA_EINVAL, "kda_prefill_backward: num_seqs (%d) must be 0 or B (%d) without cu_seqlens",
+                    num_seqs, B);
+    }
+    if (Hkv == 0) Hkv = H;
+    if (Hkv < 0 || H % Hkv != 0)
+        return fail(KDA_EINVAL, "kda_prefill_backward: Hkv (%d) must divide H (%d)", Hkv, H);
+    const int N = cu_seqlens ? num_seqs : B;
+    const bool has_tokens = (cu_seqlens ? (T > 0 && N > 0) : (B > 0 && T > 0));
+    if (has_tokens) {
+        if (!q || !k || !v || !beta || !d_o || !dq || !dk_out || !dv_out || !dbeta)
+            return fail(KDA_EINVAL, "kda_prefill_backward: q, k, v, beta, d_o, dq, dk, dv and dbeta are required");
+        if (!ejk && (!g || !a_log || !dg))
+            return fail(KDA_EINVAL, "kda_prefill_backward: KDA mode needs g, a_log and dg");
+    }
+    if (!ejk && !(std::isfinite(lower_bound) && lower_bound <= 0.f))
+        return fail(KDA_EINVAL, "kda_prefill_backward: lower_bound must be finite and <= 0 (got %g)",
+                    (double)lower_bound);
+    if (!dim_ok(dk) || !dim_ok(dv))
+        return fail(KDA_EUNSUPPORTED, "kda_prefill_backward: dk and dv must be in {16, 32, 64, 128} (got %d, %d)",
+                    dk, dv);
+    if (!ejk && lower_bound < -5.0f)
+        return fail(KDA_EUNSUPPORTED, "kda_prefill_backward: KDA mode needs lower_bound >= -5 (got %g)",
+                    (double)lower_bound);
+    if (H > 65535 || N > 65535)
+        return fail(KDA_EUNSUPPORTED, "kda_prefill_backward: H and the number of sequences must be <= 65535");
+    if (!cu_seqlens && (long long)B * T > 0x7fffffffLL)
+        return fail(KDA_EUNSUPPORTED, "kda_prefill_backward: B * T must fit in 31 bits");
+    // with no tokens the passes still run: they carry dL/d(final state) to
+    // dL/d(initial state) and give zero parameter gradients
+    if (N == 0) return ok();
+    const size_t need = kda::backward_workspace_bytes(N, T, H, Hkv, dk, dv, cu_seqlens != nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(KDA_EINVAL, "kda_prefill_backward: workspace of %zu bytes required (got %zu)", need,
+                    workspace_bytes);
+    kda::BackwardArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.g = g; a.beta = beta; a.a_log = a_log; a.dt_bias = dt_bias;
+    a.init = initial_state;
+    a.cu = cu_seqlens;
+    a.N = N; a.T = T; a.H = H; a.Hkv = Hkv; a.dk = dk; a.dv = dv;
+    a.scale = (scale > 0.f) ? scale : 1.0f / std::sqrt((float)dk);
+    a.lower_bound = lower_bound;
+    a.l2norm = (flags & KDA_QK_L2NORM) != 0;
+    a.ejk = ejk;
+    a.d_o = d_o;
+    a.do_bf16 = do_dtype == KDA_BF16;
+    a.d_final_state = d_final_state;
+    a.dq = dq; a.dk_out = dk_out; a.dv_out = dv_out; a.dg = dg; a.dbeta = dbeta;
+    a.da_log = ejk ? nullptr : da_log;
+    a.ddt_bias = ejk ? nullptr : ddt_bias;
+    a.d_initial_state = d_initial_state;
+    a.workspace = workspace;
+    return hip_status(kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream)), "kda_prefill_backward");
+}
+
 kda_status_t kda_decode_step(const float* q, const float* k, const float* g, const float* v,
                              const float* beta, const float* a_log, const float* dt_bias,
                              float scale, float lower_bound, int32_t B, int32_t H, int32_t Hkv,

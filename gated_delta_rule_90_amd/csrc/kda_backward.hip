@@ -1,0 +1,841 @@
+// kda_backward.hip - backward pass (gradients) of the KDA prefill: the
+// chunked mode of the ejkernel "kernel_delta_attention" page (section
+// "Algorithm modes"), whose chunk parallelism the page offers for training.
+//
+// The pages give no backward formulas.  The ones below are the adjoint of the
+// exact chunk regrouping of the token recurrence that the forward kernels use,
+// here with chunks of C = 16 tokens and float32 arithmetic throughout.  With
+// b_r = sum_{s<=r} gamma_s (per key channel for KDA, one scalar per token for
+// EJK, restarting at the chunk start), b' = b for KDA and b'_r = b_{r-1}
+// (b'_0 = 0) for EJK, and S0 the state entering the chunk:
+//     GA_rs = sum_i kh_ri kh_si e^{b'_ri - b_si} (s < r),  A = diag(beta) GA
+//     GP_rs = sum_i qh_ri kh_si e^{b_ri - b_si}  (s <= r),  P = GP
+//     Kg = e^{b'} kh,  Qg = e^{b} qh,  Kc = e^{b_C - b} kh  (b_C: last row)
+//     Y = V - Kg S0,  (I + A) U = diag(beta) Y
+//     O = Qg S0 + P U,  S1 = Diag(e^{b_C}) S0 + Kc^T U
+// Given dO and dS1 = dL/dS1 the adjoint is
+//     dU = P^T dO + Kc dS1,  (I + A)^T Z = dU,  dY = diag(beta) Z,  dV = dY
+//     dS0 = Qg^T dO + Diag(e^{b_C}) dS1 - Kg^T dY
+//     dA = -strict_lower(Z U^T),  dP = lower(dO U^T)
+//     dbeta_r = Z_r . Y_r + sum_s dA_rs GA_rs
+//     dQg = dO S0^T,  dKg = -dY S0^T,  dKc = U dS1^T
+// then through the two Gram products (each row and column role) and the
+// decay factors into dqh, dkh and db, db' (db' joins db on the same row for
+// KDA, on the row before for EJK), db_C (the carry and Kc) on the last row,
+// and dgamma, the reverse cumulative sum of db over the chunk; finally
+// through the prologue (L2 norms, gate activation, beta sigmoid).
+//
+// Three passes:
+//   1. bwd_fwd_scan: per (sequence, head, 16 state columns), the forward
+//      state carry over the chunks, storing the state entering every chunk;
+//   2. bwd_rev_scan: per (sequence, head, 16 columns), the state gradient
+//      carried backward over the chunks, storing dL/d(state leaving the
+//      chunk) for every chunk (and dL/d(initial state) at the end).  Both
+//      recurrences are independent per state column, so column tiles run in
+//      parallel;
+//   3. bwd_local: per (chunk, head), all columns, every chunk in parallel:
+//      the chunk's own gradients from its two stored states.
+// A last small kernel sums the parameter gradients over chunks (and the key
+// and value gradients over the heads of a group when heads are grouped).
+//
+// Range: within 16 tokens the KDA log-decay of a channel is at least
+// 16 * lower_bound >= -80 (lower_bound >= -5), so e^{+-b} stays inside
+// float32's normal range and the Gram products are factorised per channel.
+// EJK decays have no lower bound, so the scalar factors e^{b'_r - b_s} are
+// formed element by element (masked entries are never exponentiated).
+#include <algorithm>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int BC = 16;    // chunk length
+constexpr int BT = 256;   // threads per workgroup
+constexpr int TV = 16;    // state columns per scan workgroup
+constexpr int MAXD = 128;
+constexpr int SR = MAXD + 4;   // row stride of [16][<=128] tiles
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    int in_bf16;
+    const float* g;
+    const float* beta;
+    const float* a_log;
+    const float* dt_bias;
+    const float* init;
+    const int32_t* cu;
+    int N, T, H, Hkv, dv;
+    float scale, lb;
+    int l2norm;
+    const void* d_o;
+    int do_bf16;
+    const float* dSf;
+    float* dq;
+    float* dk;        // [Ntok, Hkv, dk], or per query head [Ntok, H, dk] when grouped
+    float* dv_out;    // [Ntok, Hkv, dv], or per query head [Ntok, H, dv] when grouped
+    float* dg;
+    float* dbeta;
+    float* dS0;
+    const int32_t* off;   // [N + 1] chunk offsets
+    float* ckS;           // [slots, H, dk, dv]  state entering each chunk
+    float* ckdS;          // [slots, H, dk, dv]  dL/d(state leaving each chunk)
+    float* part_a;        // [slots, H]          a_log gradient per chunk
+    float* part_dt;       // [slots, H, dk]      dt_bias gradient per chunk
+};
+
+__device__ __forceinline__ float ldx(const void* p, size_t i, int bf)
+{
+    if (bf) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+    return static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int T, int& t0, int& t1)
+{
+    if (cu) {
+        t0 = min(max(cu[n], 0), T);
+        t1 = min(max(cu[n + 1], t0), T);
+    } else {
+        t0 = n * T;
+        t1 = t0 + T;
+    }
+}
+
+// Chunk offsets: off[n] = sum_{m<n} ceil(len_m / 16), capped at the
+// workspace's chunk slots (only ranges that overlap can count more chunks
+// than the slots; those sequences then lose their last chunks, and their
+// results are unspecified, but every access stays inside the workspace).
+__global__ void bwd_plan_kernel(const int32_t* __restrict__ cu, int N, int T, int slots,
+                                int32_t* __restrict__ off)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int acc = 0;
+    for (int n = 0; n < N; ++n) {
+        int t0, t1;
+        seq_bounds(cu, n, T, t0, t1);
+        off[n] = acc;
+        acc = min(acc + (t1 - t0 + BC - 1) / BC, slots);
+    }
+    off[N] = acc;
+}
+
+// Chunks of sequence n: its length in chunks, within its slots.
+__device__ __forceinline__ int seq_chunks(const int32_t* off, int n, int t0, int t1)
+{
+    return min((t1 - t0 + BC - 1) / BC, off[n + 1] - off[n]);
+}
+
+// ---------------------------------------------------------------------------
+// The state-independent part of one chunk, in LDS: normalised rows, decay
+// factors, the Gram products GA (strict lower, without beta) and GP (lower).
+template <int DK, bool EJK>
+struct ChunkLds {
+    float qh[BC][SR];
+    float kh[BC][SR];
+    float eb[BC][SR];    // KDA: e^{b}   (first the gate, then b, then e^b)
+    float ein[BC][SR];   // KDA: e^{-b}
+    float ecb[BC][SR];   // KDA: e^{b_C - b}
+    float ec[MAXD];      // KDA: e^{b_C}
+    float beta[BC];
+    float nq[BC], nk[BC];
+    float sb[BC], seb[BC], sebp[BC], secb[BC];   // EJK: b, e^b, e^{b'}, e^{b_C - b}
+    float sec;                                   // EJK: e^{b_C}
+    float GA[BC][BC + 1];
+    float GP[BC][BC + 1];
+    float DA[BC][BC + 1];   // EJK: e^{b'_r - b_s} (s < r)
+    float DP[BC][BC + 1];   // EJK: e^{b_r - b_s} (s <= r)
+
+    __device__ float ebr(int r, int i) const { return EJK ? seb[r] : eb[r][i]; }
+    __device__ float ebpr(int r, int i) const { return EJK ? sebp[r] : eb[r][i]; }
+    __device__ float ecbr(int r, int i) const { return EJK ? secb[r] : ecb[r][i]; }
+    __device__ float ecc(int i) const { return EJK ? sec : ec[i]; }
+    __device__ float kg(int r, int i) const { return kh[r][i] * ebpr(r, i); }
+    __device__ float qg(int r, int i) const { return qh[r][i] * ebr(r, i); }
+    __device__ float kc(int r, int i) const { return kh[r][i] * ecbr(r, i); }
+};
+
+// Rows [c0, c0 + nr) of head h (nr <= 16); rows past nr are neutral
+// (q = k = 0, gamma = 0, beta = 0).  Ends with a barrier.
+template <int DK, bool EJK>
+__device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, int nr, int h, int hk)
+{
+    const int tid = threadIdx.x;
+    const int H = p.H, Hkv = p.Hkv;
+    const float ea = EJK ? 0.f : expf(p.a_log[h]);
+    for (int e = tid; e < BC * DK; e += BT) {
+        const int r = e / DK, i = e % DK;
+        const bool valid = r < nr;
+        const size_t tok = (size_t)(c0 + (valid ? r : 0));
+        L.qh[r][i] = valid ? ldx(p.q, (tok * H + h) * DK + i, p.in_bf16) : 0.f;
+        L.kh[r][i] = valid ? ldx(p.k, (tok * Hkv + hk) * DK + i, p.in_bf16) : 0.f;
+        if (!EJK) {
+            float gam = 0.f;
+            if (valid) {
+                const float x = ea * (p.g[(tok * H + h) * DK + i] + (p.dt_bias ? p.dt_bias[(size_t)i * H + h] : 0.f));
+                gam = p.lb * sigmoid_f(x);
+            }
+            L.eb[r][i] = gam;
+        }
+    }
+    if (tid < BC) {
+        const int r = tid;
+        const bool valid = r < nr;
+        const size_t tok = (size_t)(c0 + (valid ? r : 0));
+        if (EJK) {
+            L.beta[r] = valid ? p.beta[tok * H + h] : 0.f;
+            L.sb[r] = (valid && p.g) ? p.g[tok * H + h] : 0.f;
+        } else {
+            L.beta[r] = valid ? sigmoid_f(p.beta[tok * H + h]) : 0.f;
+        }
+    }
+    __syncthreads();
+    if (tid < 2 * BC) {
+        const int r = tid % BC;
+        const float* row = tid < BC ? L.qh[r] : L.kh[r];
+        float ss = 0.f;
+        for (int i = 0; i < DK; ++i) ss = fmaf(row[i], row[i], ss);
+        (tid < BC ? L.nq : L.nk)[r] = sqrtf(ss + kNormEps);
+    }
+    if (!EJK) {
+        for (int i = tid; i < DK; i += BT) {
+            float acc = 0.f;
+            for (int r = 0; r < BC; ++r) {
+                acc += L.eb[r][i];
+                L.eb[r][i] = acc;
+            }
+        }
+    } else if (tid == BT - 1) {
+        float acc = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            acc += L.sb[r];
+            L.sb[r] = acc;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < BC * DK; e += BT) {
+        const int r = e / DK, i = e % DK;
+        L.qh[r][i] = p.l2norm ? p.scale * L.qh[r][i] / L.nq[r] : p.scale * L.qh[r][i];
+        L.kh[r][i] = p.l2norm ? L.kh[r][i] / L.nk[r] : L.kh[r][i];
+        if (!EJK) {
+            const float b = L.eb[r][i], bC = L.eb[BC - 1][i];
+            L.ein[r][i] = expf(-b);
+            L.ecb[r][i] = expf(bC - b);
+            if (r == BC - 1) L.ec[i] = expf(bC);
+        }
+    }
+    if (EJK && tid < BC) {
+        const int r = tid;
+        const float b = L.sb[r], bp = r > 0 ? L.sb[r - 1] : 0.f, bC = L.sb[BC - 1];
+        L.seb[r] = expf(b);
+        L.sebp[r] = expf(bp);
+        L.secb[r] = expf(bC - b);
+        if (r == 0) L.sec = expf(bC);
+    }
+    __syncthreads();
+    if (!EJK) {
+        for (int e = tid; e < BC * DK; e += BT) {
+            const int r = e / DK, i = e % DK;
+            L.eb[r][i] = expf(L.eb[r][i]);
+        }
+        __syncthreads();
+    }
+    {
+        const int r = tid >> 4, s = tid & 15;
+        float ga = 0.f, gp = 0.f;
+        if (s <= r) {
+            if (!EJK) {
+                for (int i = 0; i < DK; ++i) {
+                    const float ki = L.kh[s][i] * L.ein[s][i];
+                    ga = fmaf(L.kh[r][i] * L.eb[r][i], ki, ga);
+                    gp = fmaf(L.qh[r][i] * L.eb[r][i], ki, gp);
+                }
+            } else {
+                for (int i = 0; i < DK; ++i) {
+                    ga = fmaf(L.kh[r][i], L.kh[s][i], ga);
+                    gp = fmaf(L.qh[r][i], L.kh[s][i], gp);
+                }
+                const float bp = r > 0 ? L.sb[r - 1] : 0.f;
+                const float da = s < r ? expf(bp - L.sb[s]) : 0.f;
+                const float dp = expf(L.sb[r] - L.sb[s]);
+                L.DA[r][s] = da;
+                L.DP[r][s] = dp;
+                ga *= da;
+                gp *= dp;
+            }
+        } else if (EJK) {
+            L.DA[r][s] = 0.f;
+            L.DP[r][s] = 0.f;
+        }
+        L.GA[r][s] = s < r ? ga : 0.f;
+        L.GP[r][s] = gp;
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: forward state carry per (column tile, head, sequence); stores the
+// state entering every chunk.
+template <int DK, bool EJK>
+__global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
+{
+    __shared__ ChunkLds<DK, EJK> L;
+    __shared__ float S[DK][TV];
+    __shared__ float Y[BC][TV + 1];
+    __shared__ float U[BC][TV + 1];
+    const int tid = threadIdx.x;
+    const int j0 = blockIdx.x * TV, h = blockIdx.y, n = blockIdx.z;
+    const int H = p.H, dv = p.dv;
+    const int hk = h / (H / p.Hkv);
+    int t0, t1;
+    seq_bounds(p.cu, n, p.T, t0, t1);
+    for (int e = tid; e < DK * TV; e += BT) {
+        const int i = e / TV, j = e % TV;
+        S[i][j] = p.init ? p.init[(((size_t)n * H + h) * DK + i) * dv + j0 + j] : 0.f;
+    }
+    const int nck = seq_chunks(p.off, n, t0, t1);
+    const int slot0 = p.off[n];
+    for (int c = 0; c < nck; ++c) {
+        __syncthreads();
+        float* dst = p.ckS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0;
+        for (int e = tid; e < DK * TV; e += BT) {
+            const int i = e / TV, j = e % TV;
+            dst[(size_t)i * dv + j] = S[i][j];
+        }
+        const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
+        chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
+        {
+            const int r = tid / TV, j = tid % TV;
+            float acc = 0.f;
+            for (int i = 0; i < DK; ++i) acc = fmaf(L.kg(r, i), S[i][j], acc);
+            const float vv = r < nr ? ldx(p.v, ((size_t)(c0 + r) * p.Hkv + hk) * dv + j0 + j, p.in_bf16) : 0.f;
+            Y[r][j] = vv - acc;
+        }
+        __syncthreads();
+        if (tid < TV) {
+            const int j = tid;
+            float u[BC];
+#pragma unroll
+            for (int r = 0; r < BC; ++r) {
+                float x = Y[r][j];
+#pragma unroll
+                for (int s = 0; s < r; ++s) x = fmaf(-L.GA[r][s], u[s], x);
+                u[r] = L.beta[r] * x;
+                U[r][j] = u[r];
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < DK * TV; e += BT) {
+            const int i = e / TV, j = e % TV;
+            float acc = L.ecc(i) * S[i][j];
+            for (int r = 0; r < BC; ++r) acc = fmaf(L.kc(r, i), U[r][j], acc);
+            S[i][j] = acc;
+        }
+    }
+}
+
+// Pass 2: the state gradient carried backward per (column tile, head,
+// sequence); stores dL/d(state leaving) of every chunk, and at the end
+// dL/d(initial state).
+template <int DK, bool EJK>
+__global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
+{
+    __shared__ ChunkLds<DK, EJK> L;
+    __shared__ float dS[DK][TV];
+    __shared__ float dO[BC][TV + 1];
+    __shared__ float dU[BC][TV + 1];
+    __shared__ float dY[BC][TV + 1];
+    const int tid = threadIdx.x;
+    const int j0 = blockIdx.x * TV, h = blockIdx.y, n = blockIdx.z;
+    const int H = p.H, dv = p.dv;
+    const int hk = h / (H / p.Hkv);
+    int t0, t1;
+    seq_bounds(p.cu, n, p.T, t0, t1);
+    for (int e = tid; e < DK * TV; e += BT) {
+        const int i = e / TV, j = e % TV;
+        dS[i][j] = p.dSf ? p.dSf[(((size_t)n * H + h) * DK + i) * dv + j0 + j] : 0.f;
+    }
+    const int nck = seq_chunks(p.off, n, t0, t1);
+    const int slot0 = p.off[n];
+    for (int c = nck - 1; c >= 0; --c) {
+        __syncthreads();
+        float* dst = p.ckdS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0;
+        for (int e = tid; e < DK * TV; e += BT) {
+            const int i = e / TV, j = e % TV;
+            dst[(size_t)i * dv + j] = dS[i][j];
+        }
+        const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
+        {
+            const int r = tid / TV, j = tid % TV;
+            dO[r][j] = r < nr ? ldx(p.d_o, ((size_t)(c0 + r) * H + h) * dv + j0 + j, p.do_bf16) : 0.f;
+        }
+        chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
+        {
+            const int r = tid / TV, j = tid % TV;
+            float acc = 0.f;
+            for (int s = r; s < BC; ++s) acc = fmaf(L.GP[s][r], dO[s][j], acc);
+            for (int i = 0; i < DK; ++i) acc = fmaf(L.kc(r, i), dS[i][j], acc);
+            dU[r][j] = acc;
+        }
+        __syncthreads();
+        if (tid < TV) {
+            const int j = tid;
+            float z[BC];
+#pragma unroll
+            for (int r = BC - 1; r >= 0; --r) {
+                float x = dU[r][j];
+#pragma unroll
+                for (int s = r + 1; s < BC; ++s) x = fmaf(-L.beta[s] * L.GA[s][r], z[s], x);
+                z[r] = x;
+                dY[r][j] = L.beta[r] * x;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < DK * TV; e += BT) {
+            const int i = e / TV, j = e % TV;
+            float acc = L.ecc(i) * dS[i][j];
+            for (int r = 0; r < BC; ++r) acc = fmaf(L.qg(r, i), dO[r][j], fmaf(-L.kg(r, i), dY[r][j], acc));
+            dS[i][j] = acc;
+        }
+    }
+    __syncthreads();
+    if (p.dS0) {
+        for (int e = tid; e < DK * TV; e += BT) {
+            const int i = e / TV, j = e % TV;
+            p.dS0[(((size_t)n * H + h) * DK + i) * dv + j0 + j] = dS[i][j];
+        }
+    }
+}
+
+// Pass 3: the gradients of one chunk's rows, from the state entering it and
+// the gradient of the state leaving it; one workgroup per (chunk, head) with
+// all state columns.
+template <int DK, bool EJK>
+__global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
+{
+    __shared__ ChunkLds<DK, EJK> L;
+    __shared__ float dO[BC][SR];
+    __shared__ float Y[BC][SR];    // V, then Y = V - Kg S0
+    __shared__ float W[BC][SR];    // dU, then dqh
+    __shared__ float U[BC][SR];
+    __shared__ float Z[BC][SR];
+    __shared__ float Gk[BC][SR];   // dkh
+    __shared__ float Gb[BC][SR];   // db (KDA: db + db'), then dgamma
+    __shared__ float Gp[BC][SR];   // EJK: db'
+    __shared__ float MA[BC][BC + 1], MP[BC][BC + 1], dA[BC][BC + 1];
+    __shared__ float dbt[BC], pq[BC], pk[BC];
+    __shared__ float dbc[2][MAXD];
+    __shared__ float red[BT / kWave];
+    const int tid = threadIdx.x;
+    const int slot = blockIdx.x, h = blockIdx.y;
+    const int H = p.H, Hkv = p.Hkv, dv = p.dv;
+    const int hk = h / (H / Hkv);
+    if (slot >= p.off[p.N]) return;
+    // the sequence of this chunk: the last n with off[n] <= slot
+    int lo = 0, hi = p.N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.off[mid] <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
+    int t0, t1;
+    seq_bounds(p.cu, n, p.T, t0, t1);
+    const int c0 = t0 + (slot - p.off[n]) * BC, nr = min(BC, t1 - c0);
+    for (int e = tid; e < BC * MAXD; e += BT) {
+        const int r = e / MAXD, j = e % MAXD;
+        const bool ok = r < nr && j < dv;
+        dO[r][j] = ok ? ldx(p.d_o, ((size_t)(c0 + r) * H + h) * dv + j, p.do_bf16) : 0.f;
+        Y[r][j] = ok ? ldx(p.v, ((size_t)(c0 + r) * Hkv + hk) * dv + j, p.in_bf16) : 0.f;
+    }
+    chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
+    const float* S0 = p.ckS + ((size_t)slot * H + h) * DK * dv;
+    const float* dS1 = p.ckdS + ((size_t)slot * H + h) * DK * dv;
+    // (a) Y = V - Kg S0 and dU = P^T dO + Kc dS1: thread (column j, 8 rows)
+    {
+        const int j = tid % MAXD, r0 = (tid / MAXD) * 8;
+        if (j < dv) {
+            float ay[8], au[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) ay[m] = au[m] = 0.f;
+            for (int i = 0; i < DK; ++i) {
+                const float s0 = S0[(size_t)i * dv + j], d1 = dS1[(size_t)i * dv + j];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    ay[m] = fmaf(L.kg(r0 + m, i), s0, ay[m]);
+                    au[m] = fmaf(L.kc(r0 + m, i), d1, au[m]);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int r = r0 + m;
+                float acc = au[m];
+                for (int s = r; s < BC; ++s) acc = fmaf(L.GP[s][r], dO[s][j], acc);
+                W[r][j] = acc;
+                Y[r][j] -= ay[m];
+            }
+        }
+    }
+    __syncthreads();
+    // (b) (I + A) U = diag(beta) Y and (I + A)^T Z = dU, one column per thread
+    if (tid < dv) {
+        const int j = tid;
+        float u[BC], z[BC];
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            float x = Y[r][j];
+#pragma unroll
+            for (int s = 0; s < r; ++s) x = fmaf(-L.GA[r][s], u[s], x);
+            u[r] = L.beta[r] * x;
+            U[r][j] = u[r];
+        }
+#pragma unroll
+        for (int r = BC - 1; r >= 0; --r) {
+            float x = W[r][j];
+#pragma unroll
+            for (int s = r + 1; s < BC; ++s) x = fmaf(-L.beta[s] * L.GA[s][r], z[s], x);
+            z[r] = x;
+            Z[r][j] = x;
+        }
+    }
+    __syncthreads();
+    // (c) dA = -strict_lower(Z U^T), dP = lower(dO U^T); the Gram-product
+    // gradients MA = diag(beta) dA, MP = dP (EJK: times the decay factors)
+    {
+        const int r = tid >> 4, s = tid & 15;
+        float a = 0.f, b = 0.f;
+        if (s <= r) {
+            for (int j = 0; j < dv; ++j) {
+                a = fmaf(Z[r][j], U[s][j], a);
+                b = fmaf(dO[r][j], U[s][j], b);
+            }
+        }
+        const float da = s < r ? -a : 0.f;
+        dA[r][s] = da;
+        MA[r][s] = EJK ? L.beta[r] * da * L.DA[r][s] : L.beta[r] * da;
+        MP[r][s] = EJK ? b * L.DP[r][s] : b;
+    }
+    __syncthreads();
+    if (tid < BC) {
+        const int r = tid;
+        float acc = 0.f;
+        for (int j = 0; j < dv; ++j) acc = fmaf(Z[r][j], Y[r][j], acc);
+        for (int s = 0; s < r; ++s) acc = fmaf(dA[r][s], L.GA[r][s], acc);
+        dbt[r] = acc;
+    }
+    // (d) per channel i and 8 rows: dQg = dO S0^T, dKg = -dY S0^T, dKc = U dS1^T,
+    // the Gram roles, and the row gradients dqh, dkh, db, db'
+    {
+        const int i = tid % MAXD, r0 = (tid / MAXD) * 8, rg = tid / MAXD;
+        if (i < DK) {
+            float aq[8], ag[8], ac[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) aq[m] = ag[m] = ac[m] = 0.f;
+            float sdot = 0.f;
+            const float* s0r = S0 + (size_t)i * dv;
+            const float* d1r = dS1 + (size_t)i * dv;
+            for (int j = 0; j < dv; ++j) {
+                const float s0 = s0r[j], d1 = d1r[j];
+                sdot = fmaf(s0, d1, sdot);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int r = r0 + m;
+                    aq[m] = fmaf(dO[r][j], s0, aq[m]);
+                    ag[m] = fmaf(-L.beta[r] * Z[r][j], s0, ag[m]);
+                    ac[m] = fmaf(U[r][j], d1, ac[m]);
+                }
+            }
+            float bc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int r = r0 + m;
+                float rowA = 0.f, colA = 0.f, rowP = 0.f, colP = 0.f;
+                if (!EJK) {
+                    for (int s = 0; s < BC; ++s) {
+                        const float ki = L.kh[s][i] * L.ein[s][i];
+                        rowA = fmaf(MA[r][s], ki, rowA);
+                        rowP = fmaf(MP[r][s], ki, rowP);
+                        colA = fmaf(MA[s][r], L.kh[s][i] * L.eb[s][i], colA);
+                        colP = fmaf(MP[s][r], L.qh[s][i] * L.eb[s][i], colP);
+                    }
+                    rowA *= L.eb[r][i];
+                    rowP *= L.eb[r][i];
+                    colA *= L.ein[r][i];
+                    colP *= L.ein[r][i];
+                } else {
+                    for (int s = 0; s < BC; ++s) {
+                        rowA = fmaf(MA[r][s], L.kh[s][i], rowA);
+                        rowP = fmaf(MP[r][s], L.kh[s][i], rowP);
+                        colA = fmaf(MA[s][r], L.kh[s][i], colA);
+                        colP = fmaf(MP[s][r], L.qh[s][i], colP);
+                    }
+                }
+                const float qh = L.qh[r][i], kh = L.kh[r][i];
+                const float ebr = L.ebr(r, i), ebpr = L.ebpr(r, i), ecbr = L.ecbr(r, i);
+                const float qg = qh * ebr, kg = kh * ebpr, kc = kh * ecbr;
+                W[r][i] = rowP + ebr * aq[m];
+                Gk[r][i] = rowA + colA + colP + ebpr * ag[m] + ecbr * ac[m];
+                const float db = qh * rowP - kh * colA - kh * colP + qg * aq[m] - kc * ac[m];
+                const float dbp = kh * rowA + kg * ag[m];
+                if (EJK) {
+                    Gb[r][i] = db;
+                    Gp[r][i] = dbp;
+                } else {
+                    Gb[r][i] = db + dbp;
+                }
+                bc = fmaf(kc, ac[m], bc);
+            }
+            dbc[rg][i] = bc + (rg == 0 ? L.ecc(i) * sdot : 0.f);
+        }
+    }
+    __syncthreads();
+    // (e) dgamma: the carry's db_C on the last row, reverse cumulative sum
+    if (!EJK) {
+        if (tid < DK) {
+            const int i = tid;
+            float run = dbc[0][i] + dbc[1][i];
+            for (int r = BC - 1; r >= 0; --r) {
+                run += Gb[r][i];
+                Gb[r][i] = run;
+            }
+        }
+    } else {
+        if (tid < BC) {
+            const int r = tid;
+            float a = 0.f, b = 0.f;
+            for (int i = 0; i < DK; ++i) {
+                a += Gb[r][i];
+                b += Gp[r][i];
+            }
+            dA[r][0] = a;    // dA is free now: per-row db and db'
+            dA[r][1] = b;
+        } else if (tid == BC) {
+            float a = 0.f;
+            for (int i = 0; i < DK; ++i) a += dbc[0][i] + dbc[1][i];
+            dA[0][2] = a;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float run = dA[0][2];
+            for (int r = BC - 1; r >= 0; --r) {
+                run += dA[r][0] + (r + 1 < BC ? dA[r + 1][1] : 0.f);
+                Gb[r][0] = run;
+            }
+        }
+    }
+    // row dots of the L2-norm backward
+    if (tid < 2 * BC) {
+        const int r = tid % BC;
+        const float* a = tid < BC ? L.qh[r] : L.kh[r];
+        const float* b = tid < BC ? W[r] : Gk[r];
+        float acc = 0.f;
+        for (int i = 0; i < DK; ++i) acc = fmaf(a[i], b[i], acc);
+        (tid < BC ? pq : pk)[r] = acc;
+    }
+    __syncthreads();
+    // (f) the prologue's backward and the stores
+    const bool grouped = Hkv != H;
+    const float ea = EJK ? 0.f : expf(p.a_log[h]);
+    float apart = 0.f;
+    for (int e = tid; e < BC * DK; e += BT) {
+        const int r = e / DK, i = e % DK;
+        if (r >= nr) continue;
+        const size_t tok = (size_t)(c0 + r);
+        float dq, dk;
+        if (p.l2norm) {
+            const float inq = 1.f / L.nq[r], ink = 1.f / L.nk[r];
+            dq = p.scale * inq * (W[r][i] - L.qh[r][i] * pq[r] / (p.scale * p.scale));
+            dk = ink * (Gk[r][i] - L.kh[r][i] * pk[r]);
+        } else {
+            dq = p.scale * W[r][i];
+            dk = Gk[r][i];
+        }
+        p.dq[(tok * H + h) * DK + i] = dq;
+        p.dk[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * DK + i] = dk;
+        if (!EJK) {
+            const float x = ea * (p.g[(tok * H + h) * DK + i] + (p.dt_bias ? p.dt_bias[(size_t)i * H + h] : 0.f));
+            const float sg = sigmoid_f(x);
+            const float dx = Gb[r][i] * p.lb * sg * (1.f - sg);
+            p.dg[(tok * H + h) * DK + i] = dx * ea;
+            apart = fmaf(dx, x, apart);
+            Gk[r][i] = dx * ea;     // dg, for the dt_bias partial below
+        }
+    }
+    for (int e = tid; e < BC * MAXD; e += BT) {
+        const int r = e / MAXD, j = e % MAXD;
+        if (r < nr && j < dv) {
+            const size_t tok = (size_t)(c0 + r);
+            p.dv_out[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * dv + j] = L.beta[r] * Z[r][j];
+        }
+    }
+    if (tid < BC && tid < nr) {
+        const int r = tid;
+        const size_t tok = (size_t)(c0 + r);
+        const float b = L.beta[r];
+        p.dbeta[tok * H + h] = EJK ? dbt[r] : dbt[r] * b * (1.f - b);
+        if (EJK && p.dg) p.dg[tok * H + h] = Gb[r][0];
+    }
+    if (!EJK) {
+        apart = wave_sum(apart);
+        if ((tid & (kWave - 1)) == 0) red[tid / kWave] = apart;
+        __syncthreads();
+        if (tid == 0) {
+            float a = 0.f;
+            for (int w = 0; w < BT / kWave; ++w) a += red[w];
+            p.part_a[(size_t)slot * H + h] = a;
+        }
+        if (tid < DK) {
+            const int i = tid;
+            float a = 0.f;
+            for (int r = 0; r < nr; ++r) a += Gk[r][i];
+            p.part_dt[((size_t)slot * H + h) * DK + i] = a;
+        }
+    }
+}
+
+// Parameter gradients summed over chunks (fixed order), and key/value
+// gradients summed over the heads of a group.
+__global__ void bwd_param_kernel(const float* __restrict__ part_a, const float* __restrict__ part_dt,
+                                 const int32_t* __restrict__ off, int N, int H, int dk,
+                                 float* __restrict__ da_log, float* __restrict__ ddt_bias)
+{
+    const int slots = off[N];
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < H * dk && ddt_bias) {
+        const int h = e / dk, i = e % dk;
+        float a = 0.f;
+        for (int s = 0; s < slots; ++s) a += part_dt[((size_t)s * H + h) * dk + i];
+        ddt_bias[(size_t)i * H + h] = a;
+    }
+    if (e < H && da_log) {
+        float a = 0.f;
+        for (int s = 0; s < slots; ++s) a += part_a[(size_t)s * H + e];
+        da_log[e] = a;
+    }
+}
+
+__global__ void bwd_group_sum_kernel(const float* __restrict__ src, size_t ntok, int H, int Hkv, int d,
+                                     float* __restrict__ dst)
+{
+    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= ntok * Hkv * d) return;
+    const int i = (int)(e % d);
+    const size_t th = e / d;
+    const int hv = (int)(th % Hkv);
+    const size_t t = th / Hkv;
+    const int G = H / Hkv;
+    float a = 0.f;
+    for (int r = 0; r < G; ++r) a += src[(t * H + (size_t)hv * G + r) * d + i];
+    dst[e] = a;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t bwd_slots(int N, int T, bool packed)
+{
+    if (packed) return (size_t)(T / BC) + (size_t)N;
+    return (size_t)N * (size_t)((T + BC - 1) / BC);
+}
+
+template <int DK, bool EJK>
+hipError_t launch_dk(const BwdParams& p, size_t slots, hipStream_t st)
+{
+    const dim3 sgrid((unsigned)(p.dv / TV), (unsigned)p.H, (unsigned)p.N);
+    hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK>), sgrid, dim3(BT), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_rev_scan<DK, EJK>), sgrid, dim3(BT), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (slots > 0) {
+        hipLaunchKernelGGL((bwd_local<DK, EJK>), dim3((unsigned)slots, (unsigned)p.H), dim3(BT), 0, st, p);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bool packed)
+{
+    if (N <= 0 || T <= 0) return align256((size_t)(N + 1) * 4);
+    const size_t slots = bwd_slots(N, T, packed);
+    const size_t ntok = packed ? (size_t)T : (size_t)N * T;
+    size_t b = align256((size_t)(N + 1) * 4);
+    b += 2 * align256(slots * H * dk * dv * 4);
+    b += align256(slots * H * 4) + align256(slots * H * dk * 4);
+    if (Hkv != H) b += align256(ntok * H * dk * 4) + align256(ntok * H * dv * 4);
+    return b;
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
+{
+    const bool packed = a.cu != nullptr;
+    const size_t slots = bwd_slots(a.N, a.T, packed);
+    const size_t ntok = packed ? (size_t)a.T : (size_t)a.N * a.T;
+    unsigned char* w = static_cast<unsigned char*>(a.workspace);
+    BwdParams p{};
+    p.q = a.q; p.k = a.k; p.v = a.v; p.in_bf16 = a.in_bf16;
+    p.g = a.g; p.beta = a.beta; p.a_log = a.a_log; p.dt_bias = a.dt_bias;
+    p.init = a.init; p.cu = a.cu;
+    p.N = a.N; p.T = a.T; p.H = a.H; p.Hkv = a.Hkv; p.dv = a.dv;
+    p.scale = a.scale; p.lb = a.lower_bound; p.l2norm = a.l2norm;
+    p.d_o = a.d_o; p.do_bf16 = a.do_bf16; p.dSf = a.d_final_state;
+    p.dq = a.dq; p.dg = a.dg; p.dbeta = a.dbeta; p.dS0 = a.d_initial_state;
+    int32_t* off = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)(a.N + 1) * 4);
+    p.off = off;
+    p.ckS = reinterpret_cast<float*>(w);
+    w += align256(slots * a.H * a.dk * a.dv * 4);
+    p.ckdS = reinterpret_cast<float*>(w);
+    w += align256(slots * a.H * a.dk * a.dv * 4);
+    p.part_a = reinterpret_cast<float*>(w);
+    w += align256(slots * a.H * 4);
+    p.part_dt = reinterpret_cast<float*>(w);
+    w += align256(slots * a.H * a.dk * 4);
+    const bool grouped = a.Hkv != a.H;
+    float* dkq = nullptr;
+    float* dvq = nullptr;
+    if (grouped) {
+        dkq = reinterpret_cast<float*>(w);
+        w += align256(ntok * a.H * a.dk * 4);
+        dvq = reinterpret_cast<float*>(w);
+    }
+    p.dk = grouped ? dkq : a.dk_out;
+    p.dv_out = grouped ? dvq : a.dv_out;
+    hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(64), 0, st, a.cu, a.N, a.T, (int)slots, off);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (a.dk * 2 + (a.ejk ? 1 : 0)) {
+    case 32: e = launch_dk<16, false>(p, slots, st); break;
+    case 33: e = launch_dk<16, true>(p, slots, st); break;
+    case 64: e = launch_dk<32, false>(p, slots, st); break;
+    case 65: e = launch_dk<32, true>(p, slots, st); break;
+    case 128: e = launch_dk<64, false>(p, slots, st); break;
+    case 129: e = launch_dk<64, true>(p, slots, st); break;
+    case 256: e = launch_dk<128, false>(p, slots, st); break;
+    default: e = launch_dk<128, true>(p, slots, st); break;
+    }
+    if (e != hipSuccess) return e;
+    if (!a.ejk && (a.da_log || a.ddt_bias)) {
+        const int n = a.H * a.dk;
+        hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p.part_a,
+                           p.part_dt, off, a.N, a.H, a.dk, a.da_log, a.ddt_bias);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (grouped && ntok > 0) {
+        size_t n = ntok * a.Hkv * a.dk;
+        hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dkq, ntok,
+                           a.H, a.Hkv, a.dk, a.dk_out);
+        n = ntok * a.Hkv * a.dv;
+        hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dvq, ntok,
+                           a.H, a.Hkv, a.dv, a.dv_out);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace kda

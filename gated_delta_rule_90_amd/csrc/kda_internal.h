@@ -52,6 +52,36 @@ struct DecodeArgs {
     float* S;
 };
 
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int in_bf16;
+    const float* g;
+    const float* beta;
+    const float* a_log;
+    const float* dt_bias;
+    const float* init;
+    const int32_t* cu;
+    int N, T, H, Hkv, dk, dv;
+    float scale;
+    float lower_bound;
+    int l2norm;
+    bool ejk;
+    const void* d_o;
+    int do_bf16;
+    const float* d_final_state;
+    float* dq;
+    float* dk_out;
+    float* dv_out;
+    float* dg;
+    float* dbeta;
+    float* da_log;
+    float* ddt_bias;
+    float* d_initial_state;
+    void* workspace;
+};
+
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // the recurrent kernel, one object per key dimension
@@ -74,6 +104,9 @@ size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
 // the float32 chunked kernel (16-token chunks on the vector ALUs)
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
+// the prefill backward (kda_backward.hip)
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bool packed);
 // device address, on the current device, of the fixed scratch array of
 // KDA_NOALLOC_SCRATCH_BYTES that kda_prefill_noalloc uses as its workspace
 hipError_t noalloc_scratch(void** out);

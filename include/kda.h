@@ -168,6 +168,48 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
                                    uint32_t flags);
 
 /*
+ * kda_prefill_backward - gradients of kda_prefill: the training pass that the
+ * chunked mode of the ejkernel "kernel_delta_attention" page (section
+ * "Algorithm modes"; run() use_chunked) is there for.  Given dL/do and
+ * dL/d(final state), it writes dL/d of every input of the same call.
+ * Inputs q ... lower_bound, cu_seqlens, num_seqs, B, T, H, Hkv, dk, dv and
+ * the flags KDA_QK_L2NORM / KDA_EJK are kda_prefill's, with the same shapes
+ * and meaning (KDA_CHUNKED is accepted and changes nothing: the backward is
+ * always chunk-parallel, in float32 arithmetic, chunks of 16 tokens).
+ *   d_o              [B, T, H, dv] in do_dtype (KDA_F32 or KDA_BF16)
+ *   d_final_state    [N, H, dk, dv] float32, NULL = 0
+ * Outputs (device, float32, caller-allocated, fully written):
+ *   dq [B, T, H, dk]; dk_out [B, T, Hkv, dk]; dv_out [B, T, Hkv, dv] (grouped heads:
+ *   summed over the heads that read each key/value head)
+ *   dg     KDA: [B, T, H, dk], dL/d(raw gate g) (required);
+ *          EJK: [B, T, H], dL/d(decay) (NULL = not wanted; also given where
+ *          g itself is NULL, as the gradient at a zero decay)
+ *   dbeta  [B, T, H]: dL/d(beta logit) for KDA, dL/d(beta) for EJK
+ *   da_log [H], ddt_bias [dk, H]: KDA only, each NULL = not wanted
+ *   d_initial_state [N, H, dk, dv] or NULL
+ * KDA mode needs lower_bound >= -5 (KDA_EUNSUPPORTED otherwise): within 16
+ * tokens the decay factors then stay inside float32's normal range.
+ * The workspace (kda_prefill_backward_workspace_bytes) holds the state
+ * entering and the state gradient leaving every 16-token chunk (2 x dk x dv x
+ * 4 bytes per chunk and head), per-chunk parameter partials and, with
+ * grouped heads, per-head key/value gradients; it is caller-owned and must
+ * not be shared by calls that may run concurrently.  With no tokens the call
+ * still writes d_initial_state (= d_final_state, or 0) and zero parameter
+ * gradients.
+ */
+size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t Hkv,
+                                            int32_t dk, int32_t dv);
+kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                                  const float* g, const float* beta, const float* a_log,
+                                  const float* dt_bias, const float* initial_state,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                  int32_t H, int32_t Hkv, int32_t dk, int32_t dv, float scale,
+                                  float lower_bound, uint32_t flags, const void* d_o, kda_dtype_t do_dtype,
+                                  const float* d_final_state, float* dq, float* dk_out, float* dv_out, float* dg,
+                                  float* dbeta, float* da_log, float* ddt_bias, float* d_initial_state,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kda_decode_step - advance the recurrence by exactly one token for each of
  * B requests (AWS Neuron "KDA TKG Kernel API Reference", kda_tkg: same
  * tensors, layouts and in-place state; scale and lower_bound are host floats

@@ -211,3 +211,46 @@ def test_error_message_is_thread_local():
     th.join()
     assert seen["msg"] == ""
     assert "dk and dv" in kda.lib().kda_last_error().decode()
+
+
+def _backward(**over):
+    a = dict(q=P, k=P, v=P, in_dtype=kda.BF16, g=P, beta=P, a_log=P, dt_bias=P, init=None, cu=None,
+             num_seqs=0, B=2, T=64, H=4, Hkv=0, dk=128, dv=128, scale=-1.0, lower_bound=-5.0,
+             flags=kda.QK_L2NORM, d_o=P, do_dtype=kda.BF16, dsf=None, dq=P, dk_out=P, dv_out=P, dg=P,
+             dbeta=P, da_log=None, ddt=None, ds0=None, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return kda.lib().kda_prefill_backward(
+        a["q"], a["k"], a["v"], a["in_dtype"], a["g"], a["beta"], a["a_log"], a["dt_bias"], a["init"],
+        a["cu"], a["num_seqs"], a["B"], a["T"], a["H"], a["Hkv"], a["dk"], a["dv"], a["scale"],
+        a["lower_bound"], a["flags"], a["d_o"], a["do_dtype"], a["dsf"], a["dq"], a["dk_out"], a["dv_out"],
+        a["dg"], a["dbeta"], a["da_log"], a["ddt"], a["ds0"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+BACKWARD_ERRORS = [
+    (dict(flags=1 << 9), kda.KDA_EINVAL, "unknown flag"),
+    (dict(d_o=None), kda.KDA_EINVAL, "required"),
+    (dict(dq=None), kda.KDA_EINVAL, "required"),
+    (dict(dg=None), kda.KDA_EINVAL, "needs g, a_log and dg"),
+    (dict(do_dtype=5), kda.KDA_EINVAL, "do_dtype"),
+    (dict(Hkv=3), kda.KDA_EINVAL, "must divide H"),
+    (dict(lower_bound=-6.0), kda.KDA_EUNSUPPORTED, "lower_bound >= -5"),
+    (dict(dk=48), kda.KDA_EUNSUPPORTED, "dk and dv"),
+    (dict(ws=None), kda.KDA_EINVAL, "workspace"),
+    (dict(ws=P, ws_bytes=1024), kda.KDA_EINVAL, "workspace"),
+]
+
+
+@pytest.mark.parametrize("over,status,msg", BACKWARD_ERRORS, ids=[str(i) for i in range(len(BACKWARD_ERRORS))])
+def test_backward_rejects_before_any_hip_call(over, status, msg):
+    assert _backward(**over) == status
+    assert msg in kda.lib().kda_last_error().decode()
+
+
+def test_backward_workspace_bytes():
+    L = kda.lib()
+    # dense B2 T64 H4 d128: 8 chunk slots x 4 heads x 2 states of 64 KiB, partials, offsets
+    need = L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 0, 128, 128)
+    assert need >= 2 * 8 * 4 * 128 * 128 * 4
+    assert L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 2, 128, 128) > need   # grouped: per-head dk, dv
+    assert L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 0, 48, 128) == 0
+    assert _backward(lower_bound=-6.0, flags=kda.EJK | kda.QK_L2NORM, B=0) == kda.KDA_OK   # EJK: no bound
