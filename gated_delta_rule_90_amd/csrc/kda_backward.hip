@@ -424,9 +424,10 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
     __shared__ float Gk[BC][SR];   // dkh
     __shared__ float Gb[BC][SR];   // db (KDA: db + db'), then dgamma
     __shared__ float Gp[BC][SR];   // EJK: db'
+    __shared__ float Kd[BC][SR];   // Kc dKc, elementwise
     __shared__ float MA[BC][BC + 1], MP[BC][BC + 1], dA[BC][BC + 1];
     __shared__ float dbt[BC], pq[BC], pk[BC];
-    __shared__ float dbc[2][MAXD];
+    __shared__ float dbc[MAXD];
     __shared__ float red[BT / kWave];
     const int tid = threadIdx.x;
     const int slot = blockIdx.x, h = blockIdx.y;
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
             float aq[8], ag[8], ac[8];
 #pragma unroll
             for (int m = 0; m < 8; ++m) aq[m] = ag[m] = ac[m] = 0.f;
-            float sdot = 0.f;
+            float sdot = 0.f;   // sum_j S0_ij dS1_ij
             const float* s0r = S0 + (size_t)i * dv;
             const float* d1r = dS1 + (size_t)i * dv;
             for (int j = 0; j < dv; ++j) {
@@ -547,18 +548,24 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
                     ac[m] = fmaf(U[r][j], d1, ac[m]);
                 }
             }
-            float bc = 0.f;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int r = r0 + m;
-                float rowA = 0.f, colA = 0.f, rowP = 0.f, colP = 0.f;
+                // Gram roles; the pair terms whose row and column roles fall on
+                // the same b (the diagonal of P, and for EJK the first
+                // sub-diagonal of A) are kept apart: they enter dqh and dkh but
+                // cancel exactly in dgamma, so they are left out of db
+                float rowA = 0.f, colA = 0.f, rowP = 0.f, colP = 0.f, subA = 0.f, subAc = 0.f;
+                const float mpd = MP[r][r];
                 if (!EJK) {
                     for (int s = 0; s < BC; ++s) {
                         const float ki = L.kh[s][i] * L.ein[s][i];
                         rowA = fmaf(MA[r][s], ki, rowA);
-                        rowP = fmaf(MP[r][s], ki, rowP);
                         colA = fmaf(MA[s][r], L.kh[s][i] * L.eb[s][i], colA);
-                        colP = fmaf(MP[s][r], L.qh[s][i] * L.eb[s][i], colP);
+                        if (s != r) {
+                            rowP = fmaf(MP[r][s], ki, rowP);
+                            colP = fmaf(MP[s][r], L.qh[s][i] * L.eb[s][i], colP);
+                        }
                     }
                     rowA *= L.eb[r][i];
                     rowP *= L.eb[r][i];
@@ -566,18 +573,22 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
                     colP *= L.ein[r][i];
                 } else {
                     for (int s = 0; s < BC; ++s) {
-                        rowA = fmaf(MA[r][s], L.kh[s][i], rowA);
-                        rowP = fmaf(MP[r][s], L.kh[s][i], rowP);
-                        colA = fmaf(MA[s][r], L.kh[s][i], colA);
-                        colP = fmaf(MP[s][r], L.qh[s][i], colP);
+                        if (s + 1 == r) subA = MA[r][s] * L.kh[s][i];
+                        else rowA = fmaf(MA[r][s], L.kh[s][i], rowA);
+                        if (s == r + 1) subAc = MA[s][r] * L.kh[s][i];
+                        else colA = fmaf(MA[s][r], L.kh[s][i], colA);
+                        if (s != r) {
+                            rowP = fmaf(MP[r][s], L.kh[s][i], rowP);
+                            colP = fmaf(MP[s][r], L.qh[s][i], colP);
+                        }
                     }
                 }
                 const float qh = L.qh[r][i], kh = L.kh[r][i];
                 const float ebr = L.ebr(r, i), ebpr = L.ebpr(r, i), ecbr = L.ecbr(r, i);
                 const float qg = qh * ebr, kg = kh * ebpr, kc = kh * ecbr;
-                W[r][i] = rowP + ebr * aq[m];
-                Gk[r][i] = rowA + colA + colP + ebpr * ag[m] + ecbr * ac[m];
-                const float db = qh * rowP - kh * colA - kh * colP + qg * aq[m] - kc * ac[m];
+                W[r][i] = rowP + mpd * kh + ebr * aq[m];
+                Gk[r][i] = rowA + subA + colA + subAc + colP + mpd * qh + ebpr * ag[m] + ecbr * ac[m];
+                const float db = qh * rowP - kh * colA - kh * colP + qg * aq[m];
                 const float dbp = kh * rowA + kg * ag[m];
                 if (EJK) {
                     Gb[r][i] = db;
@@ -585,43 +596,60 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
                 } else {
                     Gb[r][i] = db + dbp;
                 }
-                bc = fmaf(kc, ac[m], bc);
+                Kd[r][i] = kc * ac[m];
             }
-            dbc[rg][i] = bc + (rg == 0 ? L.ecc(i) * sdot : 0.f);
+            if (rg == 0) dbc[i] = L.ecc(i) * sdot;
         }
     }
     __syncthreads();
-    // (e) dgamma: the carry's db_C on the last row, reverse cumulative sum
+    // (e) dgamma_u: the reverse cumulative sum of db, the carry's e^{b_C} term
+    // (on every row) and the Kc terms of the rows before u
     if (!EJK) {
         if (tid < DK) {
             const int i = tid;
-            float run = dbc[0][i] + dbc[1][i];
+            float pre[BC];
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < BC; ++r) {
+                pre[r] = acc;
+                acc += Kd[r][i];
+            }
+            float run = dbc[i];
+#pragma unroll
             for (int r = BC - 1; r >= 0; --r) {
                 run += Gb[r][i];
-                Gb[r][i] = run;
+                Gb[r][i] = run + pre[r];
             }
         }
     } else {
         if (tid < BC) {
             const int r = tid;
-            float a = 0.f, b = 0.f;
+            float a = 0.f, b = 0.f, c = 0.f;
             for (int i = 0; i < DK; ++i) {
                 a += Gb[r][i];
                 b += Gp[r][i];
+                c += Kd[r][i];
             }
-            dA[r][0] = a;    // dA is free now: per-row db and db'
+            dA[r][0] = a;    // dA is free now: per-row db, db' and Kc terms
             dA[r][1] = b;
+            dA[r][2] = c;
         } else if (tid == BC) {
             float a = 0.f;
-            for (int i = 0; i < DK; ++i) a += dbc[0][i] + dbc[1][i];
-            dA[0][2] = a;
+            for (int i = 0; i < DK; ++i) a += dbc[i];
+            dA[0][3] = a;
         }
         __syncthreads();
         if (tid == 0) {
-            float run = dA[0][2];
+            float pre[BC];
+            float acc = 0.f;
+            for (int r = 0; r < BC; ++r) {
+                pre[r] = acc;
+                acc += dA[r][2];
+            }
+            float run = dA[0][3];
             for (int r = BC - 1; r >= 0; --r) {
                 run += dA[r][0] + (r + 1 < BC ? dA[r + 1][1] : 0.f);
-                Gb[r][0] = run;
+                Gb[r][0] = run + pre[r];
             }
         }
     }
@@ -656,8 +684,9 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
         p.dk[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * DK + i] = dk;
         if (!EJK) {
             const float x = ea * (p.g[(tok * H + h) * DK + i] + (p.dt_bias ? p.dt_bias[(size_t)i * H + h] : 0.f));
-            const float sg = sigmoid_f(x);
-            const float dx = Gb[r][i] * p.lb * sg * (1.f - sg);
+            // sigma'(x) = sigma(x) sigma(-x): no cancellation in 1 - sigma(x)
+            // when the gate saturates
+            const float dx = Gb[r][i] * p.lb * sigmoid_f(x) * sigmoid_f(-x);
             p.dg[(tok * H + h) * DK + i] = dx * ea;
             apart = fmaf(dx, x, apart);
             Gk[r][i] = dx * ea;     // dg, for the dt_bias partial below
@@ -673,8 +702,12 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
     if (tid < BC && tid < nr) {
         const int r = tid;
         const size_t tok = (size_t)(c0 + r);
-        const float b = L.beta[r];
-        p.dbeta[tok * H + h] = EJK ? dbt[r] : dbt[r] * b * (1.f - b);
+        if (EJK) {
+            p.dbeta[tok * H + h] = dbt[r];
+        } else {
+            const float l = p.beta[tok * H + h];
+            p.dbeta[tok * H + h] = dbt[r] * sigmoid_f(l) * sigmoid_f(-l);
+        }
         if (EJK && p.dg) p.dg[tok * H + h] = Gb[r][0];
     }
     if (!EJK) {

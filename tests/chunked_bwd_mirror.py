@@ -18,8 +18,11 @@ and, given dO and dS1 = dL/dS1, its adjoint is
     dQg = dO S0^T,   dKg = -dY S0^T,   dKc = U dS1^T
 then through the Gram products (a row and a column role each) and the
 elementwise decay factors into dqh, dkh and db, db' (db' folds into db: same
-row for KDA, the row before for EJK), db_C (the carry and Kc) added to the
-last row, and dgamma = the reverse cumulative sum of db.  Chunks are chained
+row for KDA, the row before for EJK), and dgamma = the reverse cumulative sum
+of db, plus the carry's e^{b_C} term on every row and the Kc terms summed over
+the rows before (pair terms whose two roles fall on the same b are left out
+of db: they cancel exactly, and in float32 would leave rounding of the size of
+the undecayed terms).  Chunks are chained
 by the forward states S0 (forward over chunks) and the state gradients dS1
 (backward over chunks).
 """
@@ -102,16 +105,31 @@ def _chunk_local(R, F, S0, dO, dS1, ejk):
     colP = np.einsum("rs,ri,rsi->si", dP, qh, F["DP"])
     dqh = rowP + F["eb"] * dQg
     dkh = rowA + colA + colP + F["ebp"] * dKg + F["ecb"] * dKc
-    db = qh * rowP - kh * colA - kh * colP + F["Qg"] * dQg - F["Kc"] * dKc
-    dbp = kh * rowA + F["Kg"] * dKg
-    dbC = np.sum(F["Kc"] * dKc, 0) + F["eC"] * np.sum(S0 * dS1, 1)
+    # dgamma_u collects, from each pair term of a Gram product, the pairs whose
+    # row-role index rho and column-role index kappa straddle it (kappa < u <=
+    # rho); pairs with rho == kappa (the diagonal of P; for EJK the first
+    # sub-diagonal of A, whose row role sits on b_{r-1}) contribute nothing and
+    # are left out, and the Kc terms (kappa = s, rho = the last row) are summed
+    # as the prefix over s < u: no large terms that cancel.
+    dPd = np.diag(dP)
+    rowP_nd = rowP - dPd[:, None] * kh
+    colP_nd = colP - dPd[:, None] * qh
+    rowA_nd, colA_nd = rowA.copy(), colA.copy()
     if ejk:
-        db, dbp, dbC = db.sum(1), dbp.sum(1), dbC.sum()
+        sub = np.diag(dGA, -1)                      # dGA[r, r-1], with DA = 1 there
+        rowA_nd[1:] -= sub[:, None] * kh[:-1]
+        colA_nd[:-1] -= sub[:, None] * kh[1:]
+    db = qh * rowP_nd - kh * colA_nd - kh * colP_nd + F["Qg"] * dQg
+    dbp = kh * rowA_nd + F["Kg"] * dKg
+    kcd = F["Kc"] * dKc
+    dbC = F["eC"] * np.sum(S0 * dS1, 1)
+    if ejk:
+        db, dbp, kcd, dbC = db.sum(1), dbp.sum(1), kcd.sum(1), dbC.sum()
         db[:-1] += dbp[1:]
     else:
         db = db + dbp
-    db[-1] += dbC
-    dgam = np.cumsum(db[::-1], axis=0)[::-1]
+    pre = np.concatenate([np.zeros_like(kcd[:1]), np.cumsum(kcd, axis=0)[:-1]])
+    dgam = np.cumsum(db[::-1], axis=0)[::-1] + dbC + pre
     return dict(dqh=dqh, dkh=dkh, dV=dY, dgam=dgam, dbt=dbt)
 
 
