@@ -468,6 +468,69 @@ int kda_oracle_backward(const double* q, const double* k, const double* v, const
     return 0;
 }
 
+/*
+ * Gated recurrent attention (ejkernel "recurrent" page, recurrent_attention():
+ * query, key, value, the gates g, g_gamma, gk, gv, softmax_scale,
+ * initial_state, reverse, cu_seqlens), token by token in float64.  The page
+ * gives no formula; the reading taken (every gate a log-space factor, used
+ * as given):
+ *     S <- exp(g_gamma[b, h]) * Diag(exp(gk_t)) S Diag(exp(gv_t))   (layer, key and value gates)
+ *     S <- S + k_t v_t^T
+ *     o_t = S^T (scale * exp(g_t) * q_t)                              (query gate)
+ * with tokens taken in order, or from the last to the first with reverse.
+ * Absent gates are 0 (no decay).  Layouts: q, g, gk [Ntok, H, dk]; k
+ * [Ntok, Hkv, dk]; v [Ntok, Hkv, dv]; gv [Ntok, H, dv]; g_gamma [Bg, H] with
+ * row min(n, Bg - 1) for sequence n (Bg = B for a dense batch, 1 packed);
+ * states [N, H, dk, dv]; o [Ntok, H, dv].
+ */
+int kda_oracle_gated_recurrent(const double* q, const double* k, const double* v, const double* g,
+                               const double* g_gamma, int g_gamma_rows, const double* gk,
+                               const double* gv, const double* initial_state,
+                               const int64_t* cu_seqlens, int n_seqs, int H, int Hkv, int dk, int dv,
+                               double scale, int reverse, double* o, double* final_state, int n_threads)
+{
+    if (n_seqs < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return 1;
+    scale = oracle_resolve_scale(scale, dk);
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int w = 0; w < n_seqs * H; ++w) {
+        const int n = w / H, h = w % H;
+        const int hk = h / (H / Hkv);
+        const size_t sz = (size_t)dk * dv;
+        const size_t soff = ((size_t)n * H + h) * sz;
+        double* S = (double*)malloc(sizeof(double) * sz);
+        double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+        if (initial_state) memcpy(S, initial_state + soff, sizeof(double) * sz);
+        else memset(S, 0, sizeof(double) * sz);
+        const double lg = g_gamma ? g_gamma[(size_t)(n < g_gamma_rows ? n : g_gamma_rows - 1) * H + h] : 0.0;
+        const int64_t t0 = cu_seqlens[n], t1 = cu_seqlens[n + 1];
+        for (int64_t m = 0; m < t1 - t0; ++m) {
+            const int64_t t = reverse ? t1 - 1 - m : t0 + m;
+            const size_t th = (size_t)t * H + h, tkv = (size_t)t * Hkv + hk;
+            for (int i = 0; i < dk; ++i) {
+                const double ri = lg + (gk ? gk[th * dk + i] : 0.0);
+                for (int j = 0; j < dv; ++j) {
+                    const double f = exp(ri + (gv ? gv[th * dv + j] : 0.0));
+                    S[(size_t)i * dv + j] = f * S[(size_t)i * dv + j] + k[tkv * dk + i] * v[tkv * dv + j];
+                }
+            }
+            for (int i = 0; i < dk; ++i) qt[i] = scale * exp(g ? g[th * dk + i] : 0.0) * q[th * dk + i];
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * qt[i];
+                o[th * dv + j] = acc;
+            }
+        }
+        if (final_state) memcpy(final_state + soff, S, sizeof(double) * sz);
+        free(S); free(qt);
+    }
+    return 0;
+}
+
 int kda_oracle_max_threads(void)
 {
 #ifdef _OPENMP

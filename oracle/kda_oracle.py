@@ -53,6 +53,9 @@ def _load():
         lib.kda_oracle_backward.argtypes = [P, P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_int64), I, I, I,
                                             I, I, D, D, D, I, I, P, P, P, P, P, P, P, P, P, P, I]
         lib.kda_oracle_backward.restype = I
+        lib.kda_oracle_gated_recurrent.argtypes = [P, P, P, P, P, I, P, P, P, ctypes.POINTER(ctypes.c_int64),
+                                                   I, I, I, I, I, D, I, P, P, I]
+        lib.kda_oracle_gated_recurrent.restype = I
         _lib = lib
     return _lib
 
@@ -198,3 +201,36 @@ def backward(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=None, cu_
     if ejk:
         del out["da_log"], out["ddt_bias"]
     return out
+
+
+def gated_recurrent(q, k, v, g=None, g_gamma=None, gk=None, gv=None, initial_state=None,
+                    cu_seqlens=None, scale=None, reverse=False, threads=0):
+    """The gated recurrent attention of the ejkernel "recurrent" page, token by
+    token in float64 (see kda_oracle_gated_recurrent in kda_oracle.c for the
+    reading of the gates).  q [B, T, H, dk]; k [B, T, Hkv, dk]; v
+    [B, T, Hkv, dv]; g, gk [B, T, H, dk]; gv [B, T, H, dv]; g_gamma [B, H];
+    initial_state [N, H, dk, dv].  Returns (o [B, T, H, dv], final_state)."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, dk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("cu_seqlens requires batch 1")
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n = cu.shape[0] - 1
+    gg = _f64(g_gamma)
+    rows = 0 if gg is None else gg.reshape(-1, H).shape[0]
+    o = np.zeros((B, T, H, dv))
+    fs = np.zeros((n, H, dk, dv))
+    sc = -1.0 if scale is None else float(scale)
+    rc = lib.kda_oracle_gated_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(_f64(g)), _ptr(gg), int(rows),
+                                        _ptr(_f64(gk)), _ptr(_f64(gv)), _ptr(_f64(initial_state)),
+                                        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, H, Hkv, dk, dv,
+                                        sc, int(bool(reverse)), _ptr(o), _ptr(fs), int(threads))
+    if rc != 0:
+        raise ValueError("oracle gated_recurrent rejected its arguments")
+    return o, fs
