@@ -20,7 +20,7 @@ import contextlib
 import ctypes
 import os
 
-__all__ = ["prefill", "prefill_noalloc", "prefill_backward", "decode_step", "KdaError", "lib", "LIB_PATH",
+__all__ = ["prefill", "prefill_noalloc", "prefill_backward", "recurrent_attention", "decode_step", "KdaError", "lib", "LIB_PATH",
            "QK_L2NORM", "CHUNKED", "EJK", "F32", "BF16", "prefill_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
     L.kda_prefill_backward.restype = ctypes.c_int
     L.kda_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.kda_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_recurrent_attention.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, fp, fp, ip, i32, i32, i32,
+                                          i32, i32, i32, i32, f32, i32, vp, ctypes.c_int, fp, vp]
+    L.kda_recurrent_attention.restype = ctypes.c_int
     L.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, u32]
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_decode_step.argtypes = [fp, fp, fp, fp, fp, fp, fp, f32, f32, i32, i32, i32, i32, i32, u32,
@@ -270,6 +273,62 @@ def prefill_backward(q, k, v, g, beta, a_log=None, dt_bias=None, initial_state=N
             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
             _ptr(out.get("da_log")), _ptr(out.get("ddt_bias")), _ptr(out["d_initial_state"]), _ptr(ws), wsb,
             _stream(dev, stream)))
+    return out
+
+
+def recurrent_attention(query, key, value, g=None, g_gamma=None, gk=None, gv=None, initial_state=None,
+                        cu_seqlens=None, *, softmax_scale=None, reverse=False, return_state=False,
+                        out_dtype=None, out=None, final_state=None, stream=None):
+    """The gated recurrent attention of the ejkernel "recurrent" page
+    (kda_recurrent_attention): query [B, T, H, dk], key [B, T, Hkv, dk],
+    value [B, T, Hkv, dv] (bf16 or float32); g, gk [B, T, H, dk], gv
+    [B, T, H, dv], g_gamma [B, H] float32 log-space gates (None = absent);
+    initial_state [N, H, dk, dv]; cu_seqlens [N + 1] int32 with B == 1.
+    Returns o, or (o, final_state) when return_state."""
+    import torch
+    q, k, v = query, key, value
+    dev = q.device
+    io = (torch.bfloat16, torch.float32)
+    f = (torch.float32,)
+    _dev("query", q, io, dev)
+    _dev("key", k, (q.dtype,), dev)
+    _dev("value", v, (q.dtype,), dev)
+    for name, t in (("g", g), ("g_gamma", g_gamma), ("gk", gk), ("gv", gv), ("initial_state", initial_state)):
+        _dev(name, t, f, dev)
+    _dev("cu_seqlens", cu_seqlens, (torch.int32,), dev)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape[:2] != q.shape[:2] or \
+            k.shape[3] != q.shape[3] or v.shape[:3] != k.shape[:3] or q.shape[2] % k.shape[2] != 0:
+        raise ValueError("query must be [B, T, H, dk], key [B, T, Hkv, dk] and value [B, T, Hkv, dv]")
+    B, T, H, dk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[3]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    for name, t, shp in (("g", g, (B, T, H, dk)), ("gk", gk, (B, T, H, dk)), ("gv", gv, (B, T, H, dv)),
+                         ("g_gamma", g_gamma, (B, H)), ("initial_state", initial_state, (N, H, dk, dv))):
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be {list(shp)}")
+    odt = q.dtype if out_dtype is None else out_dtype
+    with _on(stream):
+        if out is None:
+            out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
+        else:
+            _dev("out", out, (odt,), dev)
+            if tuple(out.shape) != (B, T, H, dv):
+                raise ValueError("out must be [B, T, H, dv]")
+        if return_state and final_state is None:
+            final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        elif final_state is not None:
+            _dev("final_state", final_state, f, dev)
+            if tuple(final_state.shape) != (N, H, dk, dv):
+                raise ValueError("final_state must be [N, H, dk, dv]")
+        sc = -1.0 if softmax_scale is None else float(softmax_scale)
+        _check(lib().kda_recurrent_attention(
+            _ptr(q), _ptr(k), _ptr(v), BF16 if q.dtype == torch.bfloat16 else F32, _ptr(g), _ptr(g_gamma),
+            _ptr(gk), _ptr(gv), _ptr(initial_state), _ptr(cu_seqlens), N if cu_seqlens is not None else 0,
+            B, T, H, Hkv, dk, dv, sc, int(bool(reverse)), _ptr(out), BF16 if odt == torch.bfloat16 else F32,
+            _ptr(final_state), _stream(dev, stream)))
+    if return_state:
+        return out, final_state
     return out
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libkda.so")
 # dimension so that its instantiations compile in parallel
 SOURCES = [("kda_api.cpp", "kda_api", []), ("kda_noalloc.cpp", "kda_noalloc", []), ("kda_decode.hip", "kda_decode", []),
            ("kda_chunked.hip", "kda_chunked", []), ("kda_chunked_f32.hip", "kda_chunked_f32", []),
-           ("kda_backward.hip", "kda_backward", [])] + \
+           ("kda_backward.hip", "kda_backward", []), ("kda_gated.hip", "kda_gated", [])] + \
     [("kda_recurrent.hip", f"kda_recurrent_dk{dk}", [f"-DKDA_RECURRENT_DK={dk}"]) for dk in (16, 32, 64, 128)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

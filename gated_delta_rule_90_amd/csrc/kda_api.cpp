@@ -279,6 +279,56 @@ kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, k
     return hip_status(kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream)), "kda_prefill_backward");
 }
 
+kda_status_t kda_recurrent_attention(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                                     const float* g, const float* g_gamma, const float* gk, const float* gv,
+                                     const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                                     int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t dk, int32_t dv,
+                                     float scale, int32_t reverse, void* o, kda_dtype_t out_dtype,
+                                     float* final_state, void* stream)
+{
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_EINVAL, "kda_recurrent_attention: bad sizes B=%d T=%d H=%d dk=%d dv=%d", B, T, H, dk, dv);
+    if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
+        return fail(KDA_EINVAL, "kda_recurrent_attention: unknown in_dtype %d", (int)in_dtype);
+    if (out_dtype != KDA_F32 && out_dtype != KDA_BF16)
+        return fail(KDA_EINVAL, "kda_recurrent_attention: unknown out_dtype %d", (int)out_dtype);
+    if (reverse != 0 && reverse != 1)
+        return fail(KDA_EINVAL, "kda_recurrent_attention: reverse must be 0 or 1 (got %d)", reverse);
+    if (cu_seqlens) {
+        if (B != 1) return fail(KDA_EINVAL, "kda_recurrent_attention: cu_seqlens requires B == 1 (got %d)", B);
+        if (num_seqs < 0) return fail(KDA_EINVAL, "kda_recurrent_attention: num_seqs must be >= 0 with cu_seqlens");
+    } else if (num_seqs != 0 && num_seqs != B) {
+        return fail(KDA_EINVAL, "kda_recurrent_attention: num_seqs (%d) must be 0 or B (%d) without cu_seqlens",
+                    num_seqs, B);
+    }
+    if (Hkv == 0) Hkv = H;
+    if (Hkv < 0 || H % Hkv != 0)
+        return fail(KDA_EINVAL, "kda_recurrent_attention: Hkv (%d) must divide H (%d)", Hkv, H);
+    const int N = cu_seqlens ? num_seqs : B;
+    const bool has_tokens = (cu_seqlens ? (T > 0 && N > 0) : (B > 0 && T > 0));
+    if (has_tokens && (!q || !k || !v || !o))
+        return fail(KDA_EINVAL, "kda_recurrent_attention: q, k, v and o are required");
+    if (!dim_ok(dk) || !dim_ok(dv))
+        return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: dk and dv must be in {16, 32, 64, 128} (got %d, %d)",
+                    dk, dv);
+    if (in_dtype == KDA_F32 && out_dtype == KDA_BF16)
+        return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: bf16 output needs bf16 input");
+    if (H > 65535 || N > 65535)
+        return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: H and the number of sequences must be <= 65535");
+    if (!cu_seqlens && (long long)B * T > 0x7fffffffLL)
+        return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: B * T must fit in 31 bits");
+    if (N == 0 || (!has_tokens && !final_state)) return ok();
+    kda::GatedArgs a{};
+    a.q = q; a.k = k; a.v = v; a.in_bf16 = in_dtype == KDA_BF16;
+    a.g = g; a.g_gamma = g_gamma; a.g_gamma_rows = cu_seqlens ? 1 : B; a.gk = gk; a.gv = gv;
+    a.init = initial_state; a.cu = cu_seqlens;
+    a.N = N; a.T = T; a.H = H; a.Hkv = Hkv; a.dk = dk; a.dv = dv;
+    a.scale = (scale > 0.f) ? scale : 1.0f / std::sqrt((float)dk);
+    a.reverse = reverse;
+    a.o = o; a.out_bf16 = out_dtype == KDA_BF16; a.final_state = final_state;
+    return hip_status(kda::launch_gated(a, reinterpret_cast<hipStream_t>(stream)), "kda_recurrent_attention");
+}
+
 kda_status_t kda_decode_step(const float* q, const float* k, const float* g, const float* v,
                              const float* beta, const float* a_log, const float* dt_bias,
                              float scale, float lower_bound, int32_t B, int32_t H, int32_t Hkv,

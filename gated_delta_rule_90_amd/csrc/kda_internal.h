@@ -82,6 +82,26 @@ struct BackwardArgs {
     void* workspace;
 };
 
+struct GatedArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int in_bf16;
+    const float* g;
+    const float* g_gamma;
+    int g_gamma_rows;
+    const float* gk;
+    const float* gv;
+    const float* init;
+    const int32_t* cu;
+    int N, T, H, Hkv, dk, dv;
+    float scale;
+    int reverse;
+    void* o;
+    int out_bf16;
+    float* final_state;
+};
+
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // the recurrent kernel, one object per key dimension
@@ -104,6 +124,8 @@ size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
 // the float32 chunked kernel (16-token chunks on the vector ALUs)
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
+// the gated recurrent attention (kda_gated.hip)
+hipError_t launch_gated(const GatedArgs& a, hipStream_t stream);
 // the prefill backward (kda_backward.hip)
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bool packed);

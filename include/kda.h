@@ -210,6 +210,33 @@ kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, k
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_recurrent_attention - the gated recurrent attention of the ejkernel
+ * "recurrent" page (recurrent_attention(): query, key, value, g, g_gamma,
+ * gk, gv, softmax_scale, initial_state, reverse, cu_seqlens, return_state).
+ * The page gives the gates' names and shapes but no formula; the reading
+ * implemented (every gate a log-space factor, used as given; absent = 0):
+ *     S <- exp(g_gamma[b, h]) Diag(exp(gk_t)) S Diag(exp(gv_t))   layer, key, value gates
+ *     S <- S + k_t v_t^T
+ *     o_t = S^T (scale exp(g_t) q_t)                              query gate
+ * with the tokens of each sequence taken in order, or last to first when
+ * reverse = 1 (o_t is then read after the tokens t..end).  No delta rule, no
+ * L2 norm.  Shapes: q [B, T, H, dk]; k [B, T, Hkv, dk]; v [B, T, Hkv, dv]
+ * (in_dtype); g, gk [B, T, H, dk]; gv [B, T, H, dv]; g_gamma [B, H] (packed:
+ * [1, H]) - float32, each NULL = absent; states [N, H, dk, dv] float32
+ * (initial NULL = zeros; final NULL = not returned); o [B, T, H, dv]
+ * (out_dtype; bf16 needs bf16 input).  scale <= 0 or NaN selects 1/sqrt(dk).
+ * Grouped heads, cu_seqlens and num_seqs as for kda_prefill.  dk, dv in
+ * {16, 32, 64, 128}.  One float32 kernel (token by token, the state in
+ * registers) serves every case.
+ */
+kda_status_t kda_recurrent_attention(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
+                                     const float* g, const float* g_gamma, const float* gk, const float* gv,
+                                     const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                                     int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t dk, int32_t dv,
+                                     float scale, int32_t reverse, void* o, kda_dtype_t out_dtype,
+                                     float* final_state, void* stream);
+
+/*
  * kda_decode_step - advance the recurrence by exactly one token for each of
  * B requests (AWS Neuron "KDA TKG Kernel API Reference", kda_tkg: same
  * tensors, layouts and in-place state; scale and lower_bound are host floats

@@ -1,0 +1,76 @@
+"""kda_recurrent_attention (the gated recurrent attention of the ejkernel
+"recurrent" page) against the float64 oracle: each gate type alone (g, gk,
+gv, g_gamma), all together, none, reverse, packed sequences with an empty one,
+grouped heads, bf16 inputs and output, every dk.  Bar: relative L2 <= 1e-5
+(float32 arithmetic; bf16 output: <= 2e-2 after the output rounding)."""
+import numpy as np
+import pytest
+
+import gated_delta_rule_90_amd as kda
+from oracle import kda_oracle
+from tests._common import dev, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, B, T, H, hkv, dk, dv, gates, lengths=None, bf16=False):
+    r = np.random.default_rng(seed)
+    if lengths is not None:
+        B, T = 1, int(sum(lengths))
+    x = dict(q=r.normal(size=(B, T, H, dk)), k=r.normal(size=(B, T, hkv, dk)) / np.sqrt(dk),
+             v=r.normal(size=(B, T, hkv, dv)))
+    if bf16:
+        import torch
+        for n in ("q", "k", "v"):
+            x[n] = torch.from_numpy(x[n].astype(np.float32)).bfloat16().float().numpy()
+    x = {n: a.astype(np.float32) for n, a in x.items()}
+    N = B if lengths is None else len(lengths)
+    x["initial_state"] = (0.3 * r.normal(size=(N, H, dk, dv))).astype(np.float32)
+    x["g"] = (0.3 * r.normal(size=(B, T, H, dk))).astype(np.float32) if "g" in gates else None
+    x["gk"] = (-np.abs(0.5 * r.normal(size=(B, T, H, dk)))).astype(np.float32) if "gk" in gates else None
+    x["gv"] = (-np.abs(0.5 * r.normal(size=(B, T, H, dv)))).astype(np.float32) if "gv" in gates else None
+    x["g_gamma"] = (-np.abs(0.1 * r.normal(size=(B, H)))).astype(np.float32) if "g_gamma" in gates else None
+    x["cu"] = None if lengths is None else np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return x
+
+
+def _check(x, reverse=False, bf16=False, tol=1e-5, scale=None):
+    import torch
+    io = torch.bfloat16 if bf16 else torch.float32
+    f = torch.float32
+    o, fs = kda.recurrent_attention(dev(x["q"], io), dev(x["k"], io), dev(x["v"], io), dev(x["g"], f),
+                                    dev(x["g_gamma"], f), dev(x["gk"], f), dev(x["gv"], f),
+                                    dev(x["initial_state"], f), dev(x["cu"], torch.int32),
+                                    softmax_scale=scale, reverse=reverse, return_state=True)
+    torch.cuda.synchronize()
+    ro, rs = kda_oracle.gated_recurrent(x["q"], x["k"], x["v"], x["g"], x["g_gamma"], x["gk"], x["gv"],
+                                        x["initial_state"], x["cu"], scale=scale, reverse=reverse)
+    eo, es = rel_l2(o.float().cpu().numpy(), ro), rel_l2(fs.cpu().numpy(), rs)
+    say(f"  rel-L2 o={eo:.2e} S={es:.2e}")
+    assert eo <= tol and es <= 1e-5, (eo, es)
+
+
+GATES = [(), ("g",), ("gk",), ("gv",), ("g_gamma",), ("g", "gk", "gv", "g_gamma")]
+
+
+@pytest.mark.parametrize("gates", GATES, ids=["none", "g", "gk", "gv", "g_gamma", "all"])
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_gated_each_gate(gates, reverse):
+    x = _inputs(50 + len(gates), 2, 77, 3, 3, 64, 32, gates)
+    say("gated", gates, "reverse" if reverse else "forward")
+    _check(x, reverse)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 128), (128, 64), (128, 128)])
+def test_gated_shapes(dk, dv):
+    x = _inputs(60 + dk + dv, 1, 130, 2, 2, dk, dv, ("g", "gk", "gv", "g_gamma"))
+    say("gated shapes", dk, dv)
+    _check(x, scale=0.3)
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_gated_varlen_grouped_bf16(reverse):
+    x = _inputs(70 + reverse, 0, 0, 4, 2, 128, 128, ("g", "gk", "gv", "g_gamma"), lengths=[40, 0, 129, 1],
+                bf16=True)
+    say("gated varlen grouped bf16", "reverse" if reverse else "forward")
+    _check(x, reverse, bf16=True, tol=2e-2)
