@@ -74,3 +74,20 @@ def test_gated_varlen_grouped_bf16(reverse):
                 bf16=True)
     say("gated varlen grouped bf16", "reverse" if reverse else "forward")
     _check(x, reverse, bf16=True, tol=2e-2)
+
+
+def test_gated_unaligned_rows_take_the_scalar_loads():
+    """A query 4 bytes past an allocation boundary: the kernel's scalar-load
+    variant, bitwise equal to the aligned call on the same values."""
+    import torch
+    x = _inputs(80, 1, 50, 2, 2, 32, 32, ("g", "gk", "gv", "g_gamma"))
+    f = torch.float32
+    flat = torch.empty(x["q"].size + 1, dtype=f, device="cuda")
+    qu = flat[1:].view(x["q"].shape)
+    qu.copy_(dev(x["q"], f))
+    rest = [dev(x[n], f) for n in ("k", "v", "g", "g_gamma", "gk", "gv", "initial_state")]
+    say("gated unaligned query")
+    o_u = kda.recurrent_attention(qu, *rest)
+    o_a = kda.recurrent_attention(dev(x["q"], f), *rest)
+    torch.cuda.synchronize()
+    assert torch.equal(o_u, o_a)
