@@ -512,6 +512,115 @@ def bench_one_mfma_config(name, steps, warmup, cpu=True, extras=True):
     return res
 
 
+def backward_bytes(ntok, H, dk, dv, io_bytes=2, do_bytes=2):
+    """Algorithmic bytes of one prefill backward: q, k, v (input dtype), g, beta
+    and dO read; dq, dk, dv, dg, dbeta written (float32)."""
+    return ntok * H * ((2 * dk + dv) * io_bytes + 4 * dk + 4 + dv * do_bytes + 4 * (3 * dk + dv) + 4)
+
+
+def bench_backward(steps, warmup, cpu=True):
+    """kda_prefill_backward on the B4 T4096 H16 bf16 workload (dO bf16, no
+    final-state gradient), with a sampled CPU oracle leg."""
+    import torch
+    import gated_delta_rule_90_amd as kda
+    from gated_delta_rule_90_amd import workloads
+    inp = workloads.prefill_b4_t4096_h16_d128()
+    bf, f = torch.bfloat16, torch.float32
+    d = lambda x, t: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(t)
+    B, T, H, dk = inp.q.shape
+    dv = inp.v.shape[-1]
+    d_o_np = workloads.round_to_bf16(np.random.default_rng(1003).standard_normal((B, T, H, dv), np.float32))
+    args = (d(inp.q, bf), d(inp.k, bf), d(inp.v, bf), d(inp.g, f), d(inp.beta, f), d(inp.a_log, f),
+            d(inp.dt_bias, f), None, None, d(d_o_np, bf))
+
+    def call():
+        return kda.prefill_backward(*args, scale=inp.scale, lower_bound=inp.lower_bound)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = backward_bytes(B * T, H, dk, dv)
+    res = {"workload": "kda_prefill_backward_b4_t4096_h16_d128_bf16", "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+           "ms_per_call": round(ms, 4), "alg_bytes": nbytes,
+           "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "note": "float32 arithmetic; chunks of 16 tokens: forward state scan, reverse state-gradient "
+                   "scan, chunk-parallel local gradients"}
+    if cpu:
+        from oracle import kda_oracle
+        gr = call()
+        torch.cuda.synchronize()
+        hs = list(range(min(H, max(1, -(-kda_oracle.max_threads() // B)))))
+        sub = lambda x: x[:, :, hs]
+        t0 = time.perf_counter()
+        ref = kda_oracle.backward(sub(inp.q), sub(inp.k), sub(inp.v), sub(inp.g), sub(inp.beta),
+                                  inp.a_log[hs], inp.dt_bias[:, hs], None, None, d_o=sub(d_o_np),
+                                  scale=inp.scale, lower_bound=inp.lower_bound)
+        el = time.perf_counter() - t0
+        # every one of these has the head axis third: [B, T, H, ...]
+        worst = max(rel_l2(gr[n][:, :, hs].cpu().numpy(), ref[n]) for n in ("dq", "dk", "dv", "dg", "dbeta"))
+        res["cpu_baseline"] = dict({"value": round(B * T / (el * H / len(hs)), 1),
+                                    "unit": f"backward tokens/s (all {H} heads)", "kind": "oracle",
+                                    "sample": f"4 sequences x 4096 tokens, heads 0..{hs[-1]}, float64; one run {el:.2f} s",
+                                    "parity": {"worst_rel_l2": worst, "bar": 2e-2, "ok": worst <= 2e-2,
+                                               "over": "dq, dk, dv, dg, dbeta of the sampled heads"}},
+                                   **cpu_info())
+    return res
+
+
+def gated_bytes(ntok, H, dk, dv, gates, io_bytes=2):
+    """Algorithmic bytes of one gated recurrent attention call: q, k, v in,
+    the given per-token gates (float32), o out."""
+    per = (2 * dk + dv) * io_bytes + dv * io_bytes
+    per += 4 * dk * (("g" in gates) + ("gk" in gates)) + 4 * dv * ("gv" in gates)
+    return ntok * H * per + (4 * H if "g_gamma" in gates else 0)
+
+
+def bench_gated(steps, warmup):
+    """kda_recurrent_attention on the B4 T4096 H16 d128 bf16 shape with the key
+    gate (the GLA-style forget gate) and, separately, with all four gates."""
+    import torch
+    import gated_delta_rule_90_amd as kda
+    from gated_delta_rule_90_amd import workloads
+    inp = workloads.prefill_b4_t4096_h16_d128()
+    bf, f = torch.bfloat16, torch.float32
+    d = lambda x, t: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(t)
+    B, T, H, dk = inp.q.shape
+    dv = inp.v.shape[-1]
+    rng = np.random.default_rng(1008)
+    gk = -np.abs(0.05 * rng.standard_normal((B, T, H, dk), np.float32))
+    gv = -np.abs(0.05 * rng.standard_normal((B, T, H, dv), np.float32))
+    g = 0.1 * rng.standard_normal((B, T, H, dk), np.float32)
+    gg = -np.abs(0.01 * rng.standard_normal((B, H), np.float32))
+    q, k, v = d(inp.q, bf), d(inp.k, bf), d(inp.v, bf)
+    out = {}
+    for name, gates in (("gk", {"gk": d(gk, f)}),
+                        ("all", {"g": d(g, f), "gk": d(gk, f), "gv": d(gv, f), "g_gamma": d(gg, f)})):
+        call = lambda: kda.recurrent_attention(q, k, v, **gates)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes = gated_bytes(B * T, H, dk, dv, gates)
+        out[f"gated_recurrent_b4_t4096_h16_d128_bf16_{name}"] = {
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1), "ms_per_call": round(ms, 4), "alg_bytes": nbytes,
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "gates": sorted(gates),
+            "path": "token by token, float32"}
+    return out
+
+
 def bench_configs(steps, warmup, cpu=True):
     """The other workloads: each is generated on the host (seeded), uploaded,
     then timed; inputs are freed before the next one."""
@@ -535,6 +644,10 @@ def bench_configs(steps, warmup, cpu=True):
     gc.collect()
     for name in _mfma_configs():
         out[name] = bench_one_mfma_config(name, steps, warmup, cpu)
+    out["backward_b4_t4096_h16_d128_bf16"] = bench_backward(max(3, steps // 4), 1, cpu)
+    gc.collect()
+    out.update(bench_gated(max(3, steps // 4), 1))
+    gc.collect()
     # a decode step takes ~50 us: 20x the steps of the prefill configs, so that the
     # mean is not set by the first few calls
     _, dres = _decode_run(workloads.decode_grouped_b64_h32_hkv8_d128(), 20 * steps, 2 * warmup)
