@@ -168,9 +168,14 @@ def _decode_run(inp, steps, warmup, nbuf=5):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    # One more untimed step goes in first, so that e0's timestamp is taken when
+    # it ends with the first timed step already queued behind it: the device
+    # time of the K steps does not include the host's latency to submit the
+    # first one after the synchronisation (the wall time below does).
+    step(warmup)
     e0.record()
     for i in range(steps):
-        step(i)
+        step(warmup + 1 + i)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -376,17 +381,20 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=Fals
         call(i, use_chunked=chunked)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    call(warmup, use_chunked=chunked)   # untimed lead call: see _decode_run
     e0.record()
     for i in range(steps):
-        call(i, use_chunked=chunked)
+        call(warmup + 1 + i, use_chunked=chunked)
     e1.record()
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
     ntok = B * T if cu is None else int(inp.cu_seqlens[-1])
     io_bytes = 2 if inp.dtype == "bf16" else 4
     nbytes = prefill_bytes(ntok, H, dk, dv, nst, s0 is not None, inp.ejk, io_bytes, inp.k.shape[2])
     res = {"tokens_per_s": round(ntok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
-           "alg_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "wall_ms_per_call": round(wall * 1e3 / (steps + 1), 4), "alg_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "path": "chunked MFMA" if mfma else ("chunked float32" if chunked else "token-by-token")}
     if mfma:
         fl = prefill_flops(ntok, H, dk, dv)
