@@ -26,8 +26,10 @@
 // through the prologue (L2 norms, gate activation, beta sigmoid).
 //
 // Three passes:
-//   1. bwd_fwd_scan: per (sequence, head, 16 state columns), the forward
-//      state carry over the chunks, storing the state entering every chunk;
+//   1. the forward state carry over the chunks, storing the state entering
+//      every chunk: the forward's float32 chunked kernel in 16-token chunks
+//      where it takes the inputs (16-byte aligned rows), else bwd_fwd_scan,
+//      per (sequence, head, 16 state columns);
 //   2. bwd_rev_scan: per (sequence, head, 16 columns), the state gradient
 //      carried backward over the chunks, storing dL/d(state leaving the
 //      chunk) for every chunk (and dL/d(initial state) at the end).  Both
@@ -773,12 +775,15 @@ size_t bwd_slots(int N, int T, bool packed)
 }
 
 template <int DK, bool EJK>
-hipError_t launch_dk(const BwdParams& p, size_t slots, hipStream_t st)
+hipError_t launch_dk(const BwdParams& p, size_t slots, bool states_done, hipStream_t st)
 {
     const dim3 sgrid((unsigned)(p.dv / TV), (unsigned)p.H, (unsigned)p.N);
-    hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK>), sgrid, dim3(BT), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!states_done) {
+        hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK>), sgrid, dim3(BT), 0, st, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_rev_scan<DK, EJK>), sgrid, dim3(BT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -841,15 +846,28 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(64), 0, st, a.cu, a.N, a.T, (int)slots, off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // Pass 1 on the forward's float32 chunked kernel (16-token chunks, storing
+    // the state entering each chunk) where it takes the inputs: 16-byte aligned
+    // rows and 31-bit sequence spans; else on bwd_fwd_scan.
+    PrefillArgs pa{};
+    pa.q = a.q; pa.k = a.k; pa.v = a.v; pa.in_bf16 = a.in_bf16 != 0;
+    pa.g = a.g; pa.beta = a.beta; pa.a_log = a.a_log; pa.dt_bias = a.dt_bias; pa.init = a.init; pa.cu = a.cu;
+    pa.N = a.N; pa.T = a.T; pa.H = a.H; pa.dk = a.dk; pa.dv = a.dv; pa.Hkv = a.Hkv;
+    pa.scale = a.scale; pa.lower_bound = a.lower_bound; pa.l2norm = a.l2norm != 0; pa.ejk = a.ejk;
+    const bool states_done = chunk_states_f32_supported(pa);
+    if (states_done) {
+        e = launch_chunk_states_f32(pa, off, p.ckS, st);
+        if (e != hipSuccess) return e;
+    }
     switch (a.dk * 2 + (a.ejk ? 1 : 0)) {
-    case 32: e = launch_dk<16, false>(p, slots, st); break;
-    case 33: e = launch_dk<16, true>(p, slots, st); break;
-    case 64: e = launch_dk<32, false>(p, slots, st); break;
-    case 65: e = launch_dk<32, true>(p, slots, st); break;
-    case 128: e = launch_dk<64, false>(p, slots, st); break;
-    case 129: e = launch_dk<64, true>(p, slots, st); break;
-    case 256: e = launch_dk<128, false>(p, slots, st); break;
-    default: e = launch_dk<128, true>(p, slots, st); break;
+    case 32: e = launch_dk<16, false>(p, slots, states_done, st); break;
+    case 33: e = launch_dk<16, true>(p, slots, states_done, st); break;
+    case 64: e = launch_dk<32, false>(p, slots, states_done, st); break;
+    case 65: e = launch_dk<32, true>(p, slots, states_done, st); break;
+    case 128: e = launch_dk<64, false>(p, slots, states_done, st); break;
+    case 129: e = launch_dk<64, true>(p, slots, states_done, st); break;
+    case 256: e = launch_dk<128, false>(p, slots, states_done, st); break;
+    default: e = launch_dk<128, true>(p, slots, states_done, st); break;
     }
     if (e != hipSuccess) return e;
     if (!a.ejk && (a.da_log || a.ddt_bias)) {

@@ -124,6 +124,10 @@ size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
 // the float32 chunked kernel (16-token chunks on the vector ALUs)
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
+// the same kernel with 16-token chunks storing the state entering every chunk
+// at ck[(off[n] + c) * H + h] instead of the output (the backward's first pass)
+hipError_t launch_chunk_states_f32(const PrefillArgs& a, const int32_t* off, float* ck, hipStream_t stream);
+bool chunk_states_f32_supported(const PrefillArgs& a);
 // the gated recurrent attention (kda_gated.hip)
 hipError_t launch_gated(const GatedArgs& a, hipStream_t stream);
 // the prefill backward (kda_backward.hip)

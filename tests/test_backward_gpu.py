@@ -119,3 +119,26 @@ def test_backward_b2_t1024_h8_d128_bf16(margin):
     inp = workloads.prefill_inputs(2, 1024, 8, 128, 128, seed=1740, init_state=True)
     say("backward bf16 B2 T1024 H8 d128")
     _check(inp, 2e-2, seed=10, do_bf16=True, margin=margin, label="B2 T1024 H8")
+
+
+def test_backward_unaligned_inputs_take_the_own_forward_scan():
+    """A query 4 bytes past an allocation boundary: the first pass runs on the
+    backward's own forward scan instead of the float32 chunked kernel (which
+    needs 16-byte aligned rows); both against the oracle."""
+    import torch
+    inp = workloads.prefill_inputs(1, 70, 2, 64, 32, seed=1750, dtype="f32", init_state=True)
+    r = np.random.default_rng(11)
+    d_o = r.normal(size=(1, 70, 2, 32)).astype(np.float32)
+    f = torch.float32
+    flat = torch.empty(inp.q.size + 1, dtype=f, device="cuda")
+    qu = flat[1:].view(inp.q.shape)
+    qu.copy_(dev(inp.q, f))
+    say("backward with an unaligned query")
+    gr = kda.prefill_backward(qu, dev(inp.k, f), dev(inp.v, f), dev(inp.g, f), dev(inp.beta, f),
+                              dev(inp.a_log, f), dev(inp.dt_bias, f), dev(inp.initial_state, f), None,
+                              dev(d_o, f), None, scale=inp.scale, lower_bound=inp.lower_bound)
+    torch.cuda.synchronize()
+    ref = kda_oracle.backward(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.a_log, inp.dt_bias, inp.initial_state,
+                              None, d_o=d_o, scale=inp.scale, lower_bound=inp.lower_bound)
+    for name, want in ref.items():
+        assert rel_l2(gr[name].cpu().numpy(), want) <= 1e-5, name
