@@ -1,7 +1,8 @@
 """kda_recurrent_attention (the gated recurrent attention of the ejkernel
-"recurrent" page) against the float64 oracle: each gate type alone (g, gk,
-gv, g_gamma), all together, none, reverse, packed sequences with an empty one,
-grouped heads, bf16 inputs and output, every dk.  Bar: relative L2 <= 1e-5
+"recurrent" page; its kernel works in 16-token chunks) against the float64
+oracle: each gate type alone (g, gk, gv, g_gamma), all together, none,
+reverse, packed sequences with an empty one and ragged tails, grouped heads,
+bf16 inputs and output, every dk, strong decay.  Bar: relative L2 <= 1e-5
 (float32 arithmetic; bf16 output: <= 2e-2 after the output rounding)."""
 import numpy as np
 import pytest
@@ -76,9 +77,9 @@ def test_gated_varlen_grouped_bf16(reverse):
     _check(x, reverse, bf16=True, tol=2e-2)
 
 
-def test_gated_unaligned_rows_take_the_scalar_loads():
-    """A query 4 bytes past an allocation boundary: the kernel's scalar-load
-    variant, bitwise equal to the aligned call on the same values."""
+def test_gated_unaligned_rows():
+    """A query 4 bytes past an allocation boundary: bitwise equal to the
+    aligned call on the same values (the kernel's loads need no alignment)."""
     import torch
     x = _inputs(80, 1, 50, 2, 2, 32, 32, ("g", "gk", "gv", "g_gamma"))
     f = torch.float32
@@ -91,3 +92,14 @@ def test_gated_unaligned_rows_take_the_scalar_loads():
     o_a = kda.recurrent_attention(dev(x["q"], f), *rest)
     torch.cuda.synchronize()
     assert torch.equal(o_u, o_a)
+
+
+def test_gated_strong_decay_and_positive_query_gate():
+    """Key and value gates down to -12 per token (factors far below float32's
+    range over a chunk, formed element by element) and a positive query gate."""
+    x = _inputs(90, 1, 100, 2, 2, 128, 32, ("g", "gk", "gv", "g_gamma"))
+    x["gk"] = (x["gk"] * 20.0).astype(np.float32)
+    x["gv"] = (x["gv"] * 20.0).astype(np.float32)
+    x["g"] = np.abs(x["g"]).astype(np.float32)
+    say("gated strong decay")
+    _check(x)
