@@ -46,6 +46,7 @@
 // EJK decays have no lower bound, so the scalar factors e^{b'_r - b_s} are
 // formed element by element (masked entries are never exponentiated).
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -88,6 +89,15 @@ struct BwdParams {
     float* part_a;        // [slots, H]          a_log gradient per chunk
     float* part_dt;       // [slots, H, dk]      dt_bias gradient per chunk
 };
+
+typedef float bf32x4_t __attribute__((ext_vector_type(4)));
+
+// D += A B on a 16x16x4 float32 MFMA: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[4 (l / 16) + e][l % 16] in element e.
+__device__ __forceinline__ bf32x4_t bmfma4(float a, float b, bf32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ float ldx(const void* p, size_t i, int bf)
 {
@@ -161,52 +171,86 @@ struct ChunkLds {
 
 // Rows [c0, c0 + nr) of head h (nr <= 16); rows past nr are neutral
 // (q = k = 0, gamma = 0, beta = 0).  Ends with a barrier.
+// The cumulative log-decays are formed in log2 units (the gate times log2 e)
+// and the factors with exp2; products such as Qg * dQg, from which the
+// gradients are built, do not depend on the unit.
 template <int DK, bool EJK>
 __device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, int nr, int h, int hk)
 {
     const int tid = threadIdx.x;
     const int H = p.H, Hkv = p.Hkv;
     const float ea = EJK ? 0.f : expf(p.a_log[h]);
-    for (int e = tid; e < BC * DK; e += BT) {
-        const int r = e / DK, i = e % DK;
-        const bool valid = r < nr;
-        const size_t tok = (size_t)(c0 + (valid ? r : 0));
-        L.qh[r][i] = valid ? ldx(p.q, (tok * H + h) * DK + i, p.in_bf16) : 0.f;
-        L.kh[r][i] = valid ? ldx(p.k, (tok * Hkv + hk) * DK + i, p.in_bf16) : 0.f;
-        if (!EJK) {
-            float gam = 0.f;
-            if (valid) {
+    const float lb2 = p.lb * kLog2e;
+    constexpr int NE = BC * DK / BT;   // row elements per thread (1 .. 8)
+    // 1. rows to LDS (a branch per input dtype outside the loop, so the loads
+    // of a thread go out together), gate activations in log2 units
+    auto load_rows = [&](auto bf) {
+        using T = std::conditional_t<decltype(bf)::value, uint16_t, float>;
+        const T* qq = static_cast<const T*>(p.q);
+        const T* kk = static_cast<const T*>(p.k);
+        auto f = [](T x) {
+            if constexpr (decltype(bf)::value) return __uint_as_float((uint32_t)x << 16);
+            else return x;
+        };
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / DK, i = e % DK;
+            const bool valid = r < nr;
+            const size_t tok = (size_t)(c0 + (valid ? r : 0));
+            const float qv = f(qq[(tok * H + h) * DK + i]);
+            const float kv = f(kk[(tok * Hkv + hk) * DK + i]);
+            L.qh[r][i] = valid ? qv : 0.f;
+            L.kh[r][i] = valid ? kv : 0.f;
+            if (!EJK) {
                 const float x = ea * (p.g[(tok * H + h) * DK + i] + (p.dt_bias ? p.dt_bias[(size_t)i * H + h] : 0.f));
-                gam = p.lb * sigmoid_f(x);
+                L.eb[r][i] = valid ? lb2 * sigmoid_f(x) : 0.f;
             }
-            L.eb[r][i] = gam;
         }
-    }
+    };
+    if (p.in_bf16) load_rows(std::true_type{});
+    else load_rows(std::false_type{});
     if (tid < BC) {
         const int r = tid;
         const bool valid = r < nr;
         const size_t tok = (size_t)(c0 + (valid ? r : 0));
         if (EJK) {
             L.beta[r] = valid ? p.beta[tok * H + h] : 0.f;
-            L.sb[r] = (valid && p.g) ? p.g[tok * H + h] : 0.f;
+            L.sb[r] = (valid && p.g) ? p.g[tok * H + h] * kLog2e : 0.f;
         } else {
             L.beta[r] = valid ? sigmoid_f(p.beta[tok * H + h]) : 0.f;
         }
     }
     __syncthreads();
-    if (tid < 2 * BC) {
-        const int r = tid % BC;
-        const float* row = tid < BC ? L.qh[r] : L.kh[r];
+    // 2. row norms: eight lanes per (row, q or k), summed by DPP and swizzle;
+    // cumulative log-decays and their factors: a thread per key channel
+    {
+        const int pr = tid >> 3, part = tid & 7;   // 32 (row, q/k) pairs
+        const int r = pr & 15;
+        const float* row = pr < 16 ? L.qh[r] : L.kh[r];
         float ss = 0.f;
-        for (int i = 0; i < DK; ++i) ss = fmaf(row[i], row[i], ss);
-        (tid < BC ? L.nq : L.nk)[r] = sqrtf(ss + kNormEps);
+        for (int i = part; i < DK; i += 8) ss = fmaf(row[i], row[i], ss);
+        ss = xor_add<1>(ss);
+        ss = xor_add<2>(ss);
+        ss = xor_add<4>(ss);
+        if (part == 0) (pr < 16 ? L.nq : L.nk)[r] = sqrtf(ss + kNormEps);
     }
     if (!EJK) {
-        for (int i = tid; i < DK; i += BT) {
+        if (tid < DK) {
+            const int i = tid;
+            float b[BC];
             float acc = 0.f;
+#pragma unroll
             for (int r = 0; r < BC; ++r) {
                 acc += L.eb[r][i];
-                L.eb[r][i] = acc;
+                b[r] = acc;
+            }
+            L.ec[i] = __builtin_amdgcn_exp2f(acc);
+#pragma unroll
+            for (int r = 0; r < BC; ++r) {
+                L.eb[r][i] = __builtin_amdgcn_exp2f(b[r]);
+                L.ein[r][i] = __builtin_amdgcn_exp2f(-b[r]);
+                L.ecb[r][i] = __builtin_amdgcn_exp2f(acc - b[r]);
             }
         }
     } else if (tid == BT - 1) {
@@ -217,62 +261,66 @@ __device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, in
         }
     }
     __syncthreads();
-    for (int e = tid; e < BC * DK; e += BT) {
+    // 3. normalised rows; EJK row factors
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+        const int e = tid + m * BT;
         const int r = e / DK, i = e % DK;
         L.qh[r][i] = p.l2norm ? p.scale * L.qh[r][i] / L.nq[r] : p.scale * L.qh[r][i];
         L.kh[r][i] = p.l2norm ? L.kh[r][i] / L.nk[r] : L.kh[r][i];
-        if (!EJK) {
-            const float b = L.eb[r][i], bC = L.eb[BC - 1][i];
-            L.ein[r][i] = expf(-b);
-            L.ecb[r][i] = expf(bC - b);
-            if (r == BC - 1) L.ec[i] = expf(bC);
-        }
     }
     if (EJK && tid < BC) {
         const int r = tid;
         const float b = L.sb[r], bp = r > 0 ? L.sb[r - 1] : 0.f, bC = L.sb[BC - 1];
-        L.seb[r] = expf(b);
-        L.sebp[r] = expf(bp);
-        L.secb[r] = expf(bC - b);
-        if (r == 0) L.sec = expf(bC);
+        L.seb[r] = __builtin_amdgcn_exp2f(b);
+        L.sebp[r] = __builtin_amdgcn_exp2f(bp);
+        L.secb[r] = __builtin_amdgcn_exp2f(bC - b);
+        if (r == 0) L.sec = __builtin_amdgcn_exp2f(bC);
     }
     __syncthreads();
-    if (!EJK) {
-        for (int e = tid; e < BC * DK; e += BT) {
-            const int r = e / DK, i = e % DK;
-            L.eb[r][i] = expf(L.eb[r][i]);
-        }
-        __syncthreads();
-    }
+    // 4. the Gram products on 16x16x4 float32 MFMA: wave 0 GA (kh e^{b'} against
+    // kh e^{-b}), wave 1 GP (qh e^{b} against kh e^{-b}); EJK: the plain dots,
+    // scaled by the element factors.  Lane (lm, lk) supplies channel
+    // k0 + 4 lk + u of row lm of both operands and holds rows 4 lk + e of
+    // column lm.
     {
-        const int r = tid >> 4, s = tid & 15;
-        float ga = 0.f, gp = 0.f;
-        if (s <= r) {
-            if (!EJK) {
-                for (int i = 0; i < DK; ++i) {
-                    const float ki = L.kh[s][i] * L.ein[s][i];
-                    ga = fmaf(L.kh[r][i] * L.eb[r][i], ki, ga);
-                    gp = fmaf(L.qh[r][i] * L.eb[r][i], ki, gp);
+        const int lane = tid & 63, wave = tid >> 6;
+        const int lm = lane & 15, lk = lane >> 4;
+        if (wave < 2) {
+            const float (*X)[SR] = wave == 0 ? L.kh : L.qh;
+            bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int kk = k0 + 4 * lk + u;
+                    const float a = EJK ? X[lm][kk] : X[lm][kk] * L.eb[lm][kk];
+                    const float b = EJK ? L.kh[lm][kk] : L.kh[lm][kk] * L.ein[lm][kk];
+                    acc = bmfma4(a, b, acc);
                 }
-            } else {
-                for (int i = 0; i < DK; ++i) {
-                    ga = fmaf(L.kh[r][i], L.kh[s][i], ga);
-                    gp = fmaf(L.qh[r][i], L.kh[s][i], gp);
-                }
-                const float bp = r > 0 ? L.sb[r - 1] : 0.f;
-                const float da = s < r ? expf(bp - L.sb[s]) : 0.f;
-                const float dp = expf(L.sb[r] - L.sb[s]);
-                L.DA[r][s] = da;
-                L.DP[r][s] = dp;
-                ga *= da;
-                gp *= dp;
             }
-        } else if (EJK) {
-            L.DA[r][s] = 0.f;
-            L.DP[r][s] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e, s = lm;
+                float x = acc[e];
+                if (wave == 0) {
+                    if (EJK) {
+                        const float bp = r > 0 ? L.sb[r - 1] : 0.f;
+                        const float da = s < r ? __builtin_amdgcn_exp2f(bp - L.sb[s]) : 0.f;
+                        L.DA[r][s] = da;
+                        x *= da;
+                    }
+                    L.GA[r][s] = s < r ? x : 0.f;
+                } else {
+                    if (EJK) {
+                        const float dp = s <= r ? __builtin_amdgcn_exp2f(L.sb[r] - L.sb[s]) : 0.f;
+                        L.DP[r][s] = dp;
+                        x *= dp;
+                    }
+                    L.GP[r][s] = s <= r ? x : 0.f;
+                }
+            }
         }
-        L.GA[r][s] = s < r ? ga : 0.f;
-        L.GP[r][s] = gp;
     }
     __syncthreads();
 }
@@ -456,28 +504,33 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
     chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
     const float* S0 = p.ckS + ((size_t)slot * H + h) * DK * dv;
     const float* dS1 = p.ckdS + ((size_t)slot * H + h) * DK * dv;
-    // (a) Y = V - Kg S0 and dU = P^T dO + Kc dS1: thread (column j, 8 rows)
+    // (a) Y = V - Kg S0 and dU = P^T dO + Kc dS1.  The products over dk run on
+    // 16x16x4 float32 MFMA, a 16-column tile of the state per step (tiles
+    // dealt over the waves): lane (lm, lk) supplies Kg[lm][k], Kc[lm][k] and
+    // S0[k][lm], dS1[k][lm] for k = k0 + 4 lk + u at step u, and holds rows
+    // 4 lk + e of column lm of the result.
     {
-        const int j = tid % MAXD, r0 = (tid / MAXD) * 8;
-        if (j < dv) {
-            float ay[8], au[8];
+        const int lane = tid & 63, wave = tid >> 6;
+        const int lm = lane & 15, lk = lane >> 4;
+        for (int jt = wave; jt < dv / 16; jt += BT / 64) {
+            const int j = 16 * jt + lm;
+            bf32x4_t ay = bf32x4_t{0.f, 0.f, 0.f, 0.f}, au = ay;
+#pragma unroll 2
+            for (int k0 = 0; k0 < DK; k0 += 16) {
 #pragma unroll
-            for (int m = 0; m < 8; ++m) ay[m] = au[m] = 0.f;
-            for (int i = 0; i < DK; ++i) {
-                const float s0 = S0[(size_t)i * dv + j], d1 = dS1[(size_t)i * dv + j];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    ay[m] = fmaf(L.kg(r0 + m, i), s0, ay[m]);
-                    au[m] = fmaf(L.kc(r0 + m, i), d1, au[m]);
+                for (int u = 0; u < 4; ++u) {
+                    const int kk = k0 + 4 * lk + u;
+                    ay = bmfma4(L.kg(lm, kk), S0[(size_t)kk * dv + j], ay);
+                    au = bmfma4(L.kc(lm, kk), dS1[(size_t)kk * dv + j], au);
                 }
             }
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int r = r0 + m;
-                float acc = au[m];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e;
+                float acc = au[e];
                 for (int s = r; s < BC; ++s) acc = fmaf(L.GP[s][r], dO[s][j], acc);
                 W[r][j] = acc;
-                Y[r][j] -= ay[m];
+                Y[r][j] -= ay[e];
             }
         }
     }
@@ -528,27 +581,60 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
         for (int s = 0; s < r; ++s) acc = fmaf(dA[r][s], L.GA[r][s], acc);
         dbt[r] = acc;
     }
-    // (d) per channel i and 8 rows: dQg = dO S0^T, dKg = -dY S0^T, dKc = U dS1^T,
-    // the Gram roles, and the row gradients dqh, dkh, db, db'
+    // (d1) dQg = dO S0^T, dKg = -dY S0^T and dKc = U dS1^T on MFMA, a 16-channel
+    // tile per step: lane (lm, lk) supplies dO[lm][j], dY[lm][j], U[lm][j] and
+    // S0[i][j], dS1[i][j] (i = 16 tt + lm, j = j0 + 4 lk + u at step u) and
+    // holds rows 4 lk + e of channel i of the results, which go to W, Gk and
+    // Kd (each element is read back, and overwritten, by the thread that
+    // owns it in (d2)).  The same S0, dS1 elements give sum_j S0_ij dS1_ij.
+    __syncthreads();   // dbt above still reads Y; W's dU is consumed
     {
-        const int i = tid % MAXD, r0 = (tid / MAXD) * 8, rg = tid / MAXD;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int lm = lane & 15, lk = lane >> 4;
+        for (int tt = wave; tt < DK / 16; tt += BT / 64) {
+            const int i = 16 * tt + lm;
+            bf32x4_t aq = bf32x4_t{0.f, 0.f, 0.f, 0.f}, ag = aq, ac = aq;
+            float sdot = 0.f;
+            const float* s0r = S0 + (size_t)i * dv;
+            const float* d1r = dS1 + (size_t)i * dv;
+            for (int j0 = 0; j0 < dv; j0 += 16) {
+                const float4 s4 = *reinterpret_cast<const float4*>(s0r + j0 + 4 * lk);
+                const float4 d4 = *reinterpret_cast<const float4*>(d1r + j0 + 4 * lk);
+                const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int jj = j0 + 4 * lk + u;
+                    aq = bmfma4(dO[lm][jj], sv[u], aq);
+                    ag = bmfma4(-L.beta[lm] * Z[lm][jj], sv[u], ag);
+                    ac = bmfma4(U[lm][jj], dv4[u], ac);
+                    sdot = fmaf(sv[u], dv4[u], sdot);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e;
+                W[r][i] = aq[e];
+                Gk[r][i] = ag[e];
+                Kd[r][i] = ac[e];
+            }
+            // sum over the four lane groups (lanes lm, lm + 16, lm + 32, lm + 48)
+            sdot = xor_add<16>(sdot);
+            sdot = xor_add<32>(sdot);
+            if (lk == 0) dbc[i] = L.ecc(i) * sdot;
+        }
+    }
+    __syncthreads();
+    // (d2) per channel i and 8 rows: the Gram roles and the row gradients dqh,
+    // dkh, db, db'
+    {
+        const int i = tid % MAXD, r0 = (tid / MAXD) * 8;
         if (i < DK) {
             float aq[8], ag[8], ac[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) aq[m] = ag[m] = ac[m] = 0.f;
-            float sdot = 0.f;   // sum_j S0_ij dS1_ij
-            const float* s0r = S0 + (size_t)i * dv;
-            const float* d1r = dS1 + (size_t)i * dv;
-            for (int j = 0; j < dv; ++j) {
-                const float s0 = s0r[j], d1 = d1r[j];
-                sdot = fmaf(s0, d1, sdot);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int r = r0 + m;
-                    aq[m] = fmaf(dO[r][j], s0, aq[m]);
-                    ag[m] = fmaf(-L.beta[r] * Z[r][j], s0, ag[m]);
-                    ac[m] = fmaf(U[r][j], d1, ac[m]);
-                }
+            for (int m = 0; m < 8; ++m) {
+                aq[m] = W[r0 + m][i];
+                ag[m] = Gk[r0 + m][i];
+                ac[m] = Kd[r0 + m][i];
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -600,7 +686,6 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
                 }
                 Kd[r][i] = kc * ac[m];
             }
-            if (rg == 0) dbc[i] = L.ecc(i) * sdot;
         }
     }
     __syncthreads();
