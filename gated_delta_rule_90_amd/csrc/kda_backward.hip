@@ -386,75 +386,335 @@ __global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
     }
 }
 
-// Pass 2: the state gradient carried backward per (column tile, head,
+// Pass 2: the state gradient carried backward per (16 state columns, head,
 // sequence); stores dL/d(state leaving) of every chunk, and at the end
-// dL/d(initial state).
+// dL/d(initial state).  The dk x 16 gradient tile stays in the accumulator
+// registers of 16x16x4 float32 MFMA, 16 rows per tile (tiles dealt over the
+// waves); the element e of a lane (lm, lk) holds row 4 lk + e, column lm,
+// which is also what that lane supplies as the B operand at step e of a
+// product over those rows.  Per chunk, last to first:
+//     dU = Kc dS + GP^T dO            (a partial per wave, summed in LDS)
+//     (I + A)^T Z = dU, dY = diag(beta) Z   (back substitution, a lane per column)
+//     dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
+// with Qg, Kg, Kc formed once per chunk in LDS (EJK: qh, kh, the scalar row
+// factors applied to dO, dY and dU rows).  The inputs of the chunk before are
+// loaded into registers while the current one computes.
 template <int DK, bool EJK>
+struct RevLds {
+    static constexpr int RS = DK + 4;   // 16-byte rows; 16 rows in distinct bank groups
+    static constexpr int XS = EJK ? 4 : BC * RS;
+    alignas(16) float QG[BC * RS];   // raw q, then Qg (EJK: qh)
+    alignas(16) float KG[BC * RS];   // raw k, then Kg (EJK: kh)
+    alignas(16) float KC[XS];        // KDA: Kc
+    alignas(16) float KI[XS];        // KDA: kh e^{-b}
+    alignas(16) float GT[XS];        // KDA: gate activations (log2 units)
+    float DO[BC][TV + 1];
+    float DY[BC][TV + 1];            // dY (EJK: e^{b'} dY)
+    float PU[BT / kWave][BC][TV + 1];
+    float CA[BC][BC + 1];            // beta_r GA_rs (s < r), else 0
+    float EC[DK];                    // KDA: e^{b_C}
+    float NQ[BC], NK[BC], BE[BC];    // query / key row scales, beta
+    float SB[BC], SBC[BC], SBP[BC];  // EJK: gates (log2), b, b'
+    float SEB[BC], SEBP[BC], SECB[BC], SEC;   // EJK: e^{b}, e^{b'}, e^{b_C - b}, e^{b_C}
+};
+
+template <int DK, bool EJK, typename Tin>
+struct RevInputs {
+    static constexpr int NE = BC * DK / BT;
+    Tin q[NE], k[NE];
+    float g[EJK ? 1 : NE];
+    float d, b, gs;
+};
+
+template <typename Tin>
+__device__ __forceinline__ float widen(Tin x)
+{
+    if constexpr (std::is_same_v<Tin, float>) return x;
+    else return __uint_as_float((uint32_t)x << 16);
+}
+
+template <int DK, bool EJK, typename Tin>
+__device__ __forceinline__ void rev_load(RevInputs<DK, EJK, Tin>& in, const BwdParams& p, int c0, int nr, int h,
+                                         int hk, int j0)
+{
+    const int tid = threadIdx.x;
+    const Tin* qq = static_cast<const Tin*>(p.q);
+    const Tin* kk = static_cast<const Tin*>(p.k);
+#pragma unroll
+    for (int m = 0; m < in.NE; ++m) {
+        const int e = tid + m * BT;
+        const int r = e / DK, i = e % DK;
+        const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
+        in.q[m] = qq[(tok * p.H + h) * DK + i];
+        in.k[m] = kk[(tok * p.Hkv + hk) * DK + i];
+        if (!EJK) in.g[m] = p.g[(tok * p.H + h) * DK + i];
+    }
+    {
+        const int r = tid / TV, j = tid % TV;
+        const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
+        in.d = ldx(p.d_o, (tok * p.H + h) * p.dv + j0 + j, p.do_bf16);
+    }
+    if (tid < BC) {
+        const size_t tok = (size_t)(c0 + (tid < nr ? tid : 0));
+        in.b = p.beta[tok * p.H + h];
+        in.gs = (EJK && p.g) ? p.g[tok * p.H + h] : 0.f;
+    }
+}
+
+template <int DK, bool EJK, typename Tin>
 __global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
 {
-    __shared__ ChunkLds<DK, EJK> L;
-    __shared__ float dS[DK][TV];
-    __shared__ float dO[BC][TV + 1];
-    __shared__ float dU[BC][TV + 1];
-    __shared__ float dY[BC][TV + 1];
+    using LT = RevLds<DK, EJK>;
+    constexpr int RS = LT::RS;
+    constexpr int NT = DK / 16;              // 16-row tiles of the gradient
+    constexpr int NW = BT / kWave;
+    constexpr int TPW = (NT + NW - 1) / NW;  // tiles per wave
+    __shared__ LT L;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lm = lane & 15, lk = lane >> 4;
     const int j0 = blockIdx.x * TV, h = blockIdx.y, n = blockIdx.z;
     const int H = p.H, dv = p.dv;
     const int hk = h / (H / p.Hkv);
+    const float ea = EJK ? 0.f : expf(p.a_log[h]);
+    const float lb2 = p.lb * kLog2e;
+    const float dtb = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
-    for (int e = tid; e < DK * TV; e += BT) {
-        const int i = e / TV, j = e % TV;
-        dS[i][j] = p.dSf ? p.dSf[(((size_t)n * H + h) * DK + i) * dv + j0 + j] : 0.f;
+    bf32x4_t dS[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int t = wave + NW * x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * t + 4 * lk + e;
+            dS[x][e] = (t < NT && p.dSf) ? p.dSf[(((size_t)n * H + h) * DK + i) * dv + j0 + lm] : 0.f;
+        }
     }
     const int nck = seq_chunks(p.off, n, t0, t1);
     const int slot0 = p.off[n];
+    RevInputs<DK, EJK, Tin> in;
+    if (nck > 0) {
+        const int c0 = t0 + (nck - 1) * BC;
+        rev_load(in, p, c0, min(BC, t1 - c0), h, hk, j0);
+    }
     for (int c = nck - 1; c >= 0; --c) {
-        __syncthreads();
-        float* dst = p.ckdS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0;
-        for (int e = tid; e < DK * TV; e += BT) {
-            const int i = e / TV, j = e % TV;
-            dst[(size_t)i * dv + j] = dS[i][j];
-        }
         const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
         {
-            const int r = tid / TV, j = tid % TV;
-            dO[r][j] = r < nr ? ldx(p.d_o, ((size_t)(c0 + r) * H + h) * dv + j0 + j, p.do_bf16) : 0.f;
-        }
-        chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
-        {
-            const int r = tid / TV, j = tid % TV;
-            float acc = 0.f;
-            for (int s = r; s < BC; ++s) acc = fmaf(L.GP[s][r], dO[s][j], acc);
-            for (int i = 0; i < DK; ++i) acc = fmaf(L.kc(r, i), dS[i][j], acc);
-            dU[r][j] = acc;
+            float* dst = p.ckdS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0 + lm;
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * t + 4 * lk + e) * dv] = dS[x][e];
+                }
+            }
         }
         __syncthreads();
+        // 1. this chunk's inputs to LDS (rows past nr neutral); the chunk
+        // before is loaded meanwhile
+#pragma unroll
+        for (int m = 0; m < in.NE; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / DK, i = e % DK;
+            const bool ok = r < nr;
+            L.QG[r * RS + i] = ok ? widen(in.q[m]) : 0.f;
+            L.KG[r * RS + i] = ok ? widen(in.k[m]) : 0.f;
+            if (!EJK) L.GT[r * RS + i] = ok ? lb2 * sigmoid_f(ea * (in.g[m] + dtb)) : 0.f;
+        }
+        L.DO[tid / TV][tid % TV] = tid / TV < nr ? in.d : 0.f;
+        if (tid < BC) {
+            const bool ok = tid < nr;
+            L.BE[tid] = ok ? (EJK ? in.b : sigmoid_f(in.b)) : 0.f;
+            if (EJK) L.SB[tid] = ok ? in.gs * kLog2e : 0.f;
+        }
+        if (c > 0) {
+            const int cp = c0 - BC;
+            rev_load(in, p, cp, BC, h, hk, j0);
+        }
+        __syncthreads();
+        // 2. row scales (eight lanes per row, summed by DPP / swizzle); EJK:
+        // the scalar cumulative decays, each of 16 lanes summing in row order
+        {
+            const int pr = tid >> 3, part = tid & 7;
+            const int r = pr & 15;
+            const float* row = (pr < 16 ? L.QG : L.KG) + r * RS;
+            float ss = 0.f;
+#pragma unroll
+            for (int i = part; i < DK; i += 8) ss = fmaf(row[i], row[i], ss);
+            ss = xor_add<1>(ss);
+            ss = xor_add<2>(ss);
+            ss = xor_add<4>(ss);
+            if (part == 0) {
+                const float rn = p.l2norm ? 1.f / sqrtf(ss + kNormEps) : 1.f;
+                if (pr < 16) L.NQ[r] = p.scale * rn;
+                else L.NK[r] = rn;
+            }
+        }
+        if (EJK && tid >= BT - BC) {
+            const int r = tid - (BT - BC);
+            float acc = 0.f, b = 0.f, bp = 0.f;
+#pragma unroll
+            for (int s = 0; s < BC; ++s) {
+                if (s == r) bp = acc;
+                acc += L.SB[s];
+                if (s == r) b = acc;
+            }
+            L.SBC[r] = b;
+            L.SBP[r] = bp;
+            L.SEB[r] = __builtin_amdgcn_exp2f(b);
+            L.SEBP[r] = __builtin_amdgcn_exp2f(bp);
+            L.SECB[r] = __builtin_amdgcn_exp2f(acc - b);
+            if (r == 0) L.SEC = __builtin_amdgcn_exp2f(acc);
+        }
+        __syncthreads();
+        // 3. normalised and decayed rows: KDA a thread per (channel, rows of
+        // its part), the channel's prefix sums in registers
+        if constexpr (!EJK) {
+            constexpr int NP = BT / DK, RP = BC / NP;
+            const int i = tid % DK, part = tid / DK;
+            float bo[RP];
+            float b = 0.f;
+#pragma unroll
+            for (int s = 0; s < BC; ++s) {
+                b += L.GT[s * RS + i];
+#pragma unroll
+                for (int x = 0; x < RP; ++x)
+                    if (s == part * RP + x) bo[x] = b;
+            }
+            if (part == 0) L.EC[i] = __builtin_amdgcn_exp2f(b);
+#pragma unroll
+            for (int x = 0; x < RP; ++x) {
+                const int r = part * RP + x;
+                const float qn = L.QG[r * RS + i] * L.NQ[r];
+                const float kn = L.KG[r * RS + i] * L.NK[r];
+                const float f = __builtin_amdgcn_exp2f(bo[x]);
+                L.QG[r * RS + i] = qn * f;
+                L.KG[r * RS + i] = kn * f;
+                L.KI[r * RS + i] = kn * __builtin_amdgcn_exp2f(-bo[x]);
+                L.KC[r * RS + i] = kn * __builtin_amdgcn_exp2f(b - bo[x]);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < in.NE; ++m) {
+                const int e = tid + m * BT;
+                const int r = e / DK, i = e % DK;
+                L.QG[r * RS + i] *= L.NQ[r];
+                L.KG[r * RS + i] *= L.NK[r];
+            }
+        }
+        __syncthreads();
+        // 4. MFMA: each wave its tiles' part of Kc dS; wave 0 the Gram A, wave
+        // 1 the Gram P and P^T dO (its P accumulator is that product's A operand)
+        {
+            const float* KCsrc = EJK ? L.KG : L.KC;
+            const float* KIsrc = EJK ? L.KG : L.KI;
+            bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+                    const float4 a = *reinterpret_cast<const float4*>(KCsrc + lm * RS + 16 * t + 4 * lk);
+                    acc = bmfma4(a.x, dS[x][0], acc);
+                    acc = bmfma4(a.y, dS[x][1], acc);
+                    acc = bmfma4(a.z, dS[x][2], acc);
+                    acc = bmfma4(a.w, dS[x][3], acc);
+                }
+            }
+            if (EJK) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= L.SECB[4 * lk + e];
+            }
+            if (wave < 2) {
+                const float* X = wave == 0 ? L.KG : L.QG;
+                bf32x4_t gm = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += 16) {
+                    const float4 a = *reinterpret_cast<const float4*>(X + lm * RS + k0 + 4 * lk);
+                    const float4 b = *reinterpret_cast<const float4*>(KIsrc + lm * RS + k0 + 4 * lk);
+                    gm = bmfma4(a.x, b.x, gm);
+                    gm = bmfma4(a.y, b.y, gm);
+                    gm = bmfma4(a.z, b.z, gm);
+                    gm = bmfma4(a.w, b.w, gm);
+                }
+                // gm[e] = Gram[r][s], r = 4 lk + e, s = lm
+                if (wave == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * lk + e, s = lm;
+                        float x = gm[e];
+                        if (EJK) x *= s < r ? __builtin_amdgcn_exp2f(L.SBP[r] - L.SBC[s]) : 0.f;
+                        L.CA[r][s] = s < r ? L.BE[r] * x : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * lk + e, s = lm;
+                        float x = gm[e];
+                        if (EJK) x *= s <= r ? __builtin_amdgcn_exp2f(L.SBC[r] - L.SBC[s]) : 0.f;
+                        gm[e] = s <= r ? x : 0.f;
+                    }
+                    // (P^T dO)[m][j] = sum_s P[s][m] dO[s][j]: at step e the lane
+                    // supplies P[4 lk + e][lm], its own gm[e]
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc = bmfma4(gm[e], L.DO[4 * lk + e][lm], acc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
+        }
+        __syncthreads();
+        // 5. (I + A)^T Z = dU by back substitution, a lane per column
         if (tid < TV) {
             const int j = tid;
             float z[BC];
 #pragma unroll
-            for (int r = BC - 1; r >= 0; --r) {
-                float x = dU[r][j];
+            for (int r = 0; r < BC; ++r) z[r] = (L.PU[0][r][j] + L.PU[1][r][j]) + (L.PU[2][r][j] + L.PU[3][r][j]);
 #pragma unroll
-                for (int s = r + 1; s < BC; ++s) x = fmaf(-L.beta[s] * L.GA[s][r], z[s], x);
-                z[r] = x;
-                dY[r][j] = L.beta[r] * x;
+            for (int s = BC - 1; s >= 0; --s) {
+                const float zs = z[s];
+                const float dy = L.BE[s] * zs;
+                L.DY[s][j] = EJK ? dy * L.SEBP[s] : dy;
+#pragma unroll
+                for (int r = 0; r < s; ++r) z[r] = fmaf(-L.CA[s][r], zs, z[r]);
             }
         }
         __syncthreads();
-        for (int e = tid; e < DK * TV; e += BT) {
-            const int i = e / TV, j = e % TV;
-            float acc = L.ecc(i) * dS[i][j];
-            for (int r = 0; r < BC; ++r) acc = fmaf(L.qg(r, i), dO[r][j], fmaf(-L.kg(r, i), dY[r][j], acc));
-            dS[i][j] = acc;
+        // 6. dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            if (t < NT) {
+                bf32x4_t a = dS[x];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] *= EJK ? L.SEC : L.EC[16 * t + 4 * lk + e];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * lk + u;
+                    const float d = EJK ? L.DO[r][lm] * L.SEB[r] : L.DO[r][lm];
+                    a = bmfma4(L.QG[r * RS + 16 * t + lm], d, a);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * lk + u;
+                    a = bmfma4(-L.KG[r * RS + 16 * t + lm], L.DY[r][lm], a);
+                }
+                dS[x] = a;
+            }
         }
     }
-    __syncthreads();
     if (p.dS0) {
-        for (int e = tid; e < DK * TV; e += BT) {
-            const int i = e / TV, j = e % TV;
-            p.dS0[(((size_t)n * H + h) * DK + i) * dv + j0 + j] = dS[i][j];
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            if (t < NT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * t + 4 * lk + e;
+                    p.dS0[(((size_t)n * H + h) * DK + i) * dv + j0 + lm] = dS[x][e];
+                }
+            }
         }
     }
 }
@@ -817,22 +1077,44 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
 
 // Parameter gradients summed over chunks (fixed order), and key/value
 // gradients summed over the heads of a group.
-__global__ void bwd_param_kernel(const float* __restrict__ part_a, const float* __restrict__ part_dt,
-                                 const int32_t* __restrict__ off, int N, int H, int dk,
-                                 float* __restrict__ da_log, float* __restrict__ ddt_bias)
+__global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict__ part_a,
+                                                        const float* __restrict__ part_dt,
+                                                        const int32_t* __restrict__ off, int N, int H, int dk,
+                                                        float* __restrict__ da_log, float* __restrict__ ddt_bias)
 {
+    // a workgroup per (32 channels, head): eight lanes per channel take every
+    // eighth chunk, then a fixed-order sum (the result does not depend on timing)
+    __shared__ float red[8][33];
+    __shared__ float ra[256];
     const int slots = off[N];
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e < H * dk && ddt_bias) {
-        const int h = e / dk, i = e % dk;
-        float a = 0.f;
-        for (int s = 0; s < slots; ++s) a += part_dt[((size_t)s * H + h) * dk + i];
-        ddt_bias[(size_t)i * H + h] = a;
+    const int tid = threadIdx.x, h = blockIdx.y;
+    const int i = blockIdx.x * 32 + (tid & 31), grp = tid >> 5;
+    float a = 0.f;
+    if (ddt_bias && i < dk) {
+#pragma unroll 8
+        for (int s = grp; s < slots; s += 8) a += part_dt[((size_t)s * H + h) * dk + i];
     }
-    if (e < H && da_log) {
-        float a = 0.f;
-        for (int s = 0; s < slots; ++s) a += part_a[(size_t)s * H + e];
-        da_log[e] = a;
+    red[grp][tid & 31] = a;
+    const bool do_a = da_log && blockIdx.x == 0;
+    float b = 0.f;
+    if (do_a) {
+#pragma unroll 4
+        for (int s = tid; s < slots; s += 256) b += part_a[(size_t)s * H + h];
+    }
+    ra[tid] = b;
+    __syncthreads();
+    if (tid < 32 && ddt_bias && i < dk) {
+        float t = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < 8; ++g2) t += red[g2][tid];
+        ddt_bias[(size_t)i * H + h] = t;
+    }
+    if (do_a) {
+        for (int w = 128; w > 0; w >>= 1) {
+            if (tid < w) ra[tid] += ra[tid + w];
+            __syncthreads();
+        }
+        if (tid == 0) da_log[h] = ra[0];
     }
 }
 
@@ -869,7 +1151,8 @@ hipError_t launch_dk(const BwdParams& p, size_t slots, bool states_done, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_rev_scan<DK, EJK>), sgrid, dim3(BT), 0, st, p);
+    if (p.in_bf16) hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, uint16_t>), sgrid, dim3(BT), 0, st, p);
+    else hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, float>), sgrid, dim3(BT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (slots > 0) {
@@ -956,8 +1239,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     }
     if (e != hipSuccess) return e;
     if (!a.ejk && (a.da_log || a.ddt_bias)) {
-        const int n = a.H * a.dk;
-        hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p.part_a,
+        hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)((a.dk + 31) / 32), (unsigned)a.H), dim3(256), 0, st, p.part_a,
                            p.part_dt, off, a.N, a.H, a.dk, a.da_log, a.ddt_bias);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
