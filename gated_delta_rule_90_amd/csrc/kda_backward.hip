@@ -25,6 +25,10 @@
 // and dgamma, the reverse cumulative sum of db over the chunk; finally
 // through the prologue (L2 norms, gate activation, beta sigmoid).
 //
+// Barriers wait for LDS only (lds_barrier): no workgroup reads global memory
+// that another of its waves wrote, so prefetched loads and stores stay in
+// flight across them.
+//
 // Three passes:
 //   1. the forward state carry over the chunks, storing the state entering
 //      every chunk: the forward's float32 chunked kernel in 16-token chunks
@@ -86,6 +90,8 @@ struct BwdParams {
     const int32_t* off;   // [N + 1] chunk offsets
     float* ckS;           // [slots, H, dk, dv]  state entering each chunk
     float* ckdS;          // [slots, H, dk, dv]  dL/d(state leaving each chunk)
+    float* ckYU;          // [slots, H, 2, 16, dv]  Y = V - Kg S0 and U of each chunk
+    float* ckZ;           // [slots, H, 16, dv]  Z of each chunk ((I + A)^T Z = dU)
     float* part_a;        // [slots, H]          a_log gradient per chunk
     float* part_dt;       // [slots, H, dk]      dt_bias gradient per chunk
 };
@@ -174,6 +180,118 @@ struct ChunkLds {
 // The cumulative log-decays are formed in log2 units (the gate times log2 e)
 // and the factors with exp2; products such as Qg * dQg, from which the
 // gradients are built, do not depend on the unit.
+// Steps 2-4 of the set-up, once the raw rows (qh, kh), the gate activations
+// (KDA: eb, log2 units), beta and the EJK gates (sb, log2 units) are in LDS.
+// Begins and ends with a barrier.
+template <int DK, bool EJK>
+__device__ void setup_rest(ChunkLds<DK, EJK>& L, const BwdParams& p)
+{
+    const int tid = threadIdx.x;
+    constexpr int NE = BC * DK / BT;   // row elements per thread (1 .. 8)
+    lds_barrier();
+    // 2. row norms: eight lanes per (row, q or k), summed by DPP and swizzle;
+    // cumulative log-decays and their factors: a thread per key channel
+    {
+        const int pr = tid >> 3, part = tid & 7;   // 32 (row, q/k) pairs
+        const int r = pr & 15;
+        const float* row = pr < 16 ? L.qh[r] : L.kh[r];
+        float ss = 0.f;
+        for (int i = part; i < DK; i += 8) ss = fmaf(row[i], row[i], ss);
+        ss = xor_add<1>(ss);
+        ss = xor_add<2>(ss);
+        ss = xor_add<4>(ss);
+        if (part == 0) (pr < 16 ? L.nq : L.nk)[r] = sqrtf(ss + kNormEps);
+    }
+    if (!EJK) {
+        if (tid < DK) {
+            const int i = tid;
+            float b[BC];
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < BC; ++r) {
+                acc += L.eb[r][i];
+                b[r] = acc;
+            }
+            L.ec[i] = __builtin_amdgcn_exp2f(acc);
+#pragma unroll
+            for (int r = 0; r < BC; ++r) {
+                L.eb[r][i] = __builtin_amdgcn_exp2f(b[r]);
+                L.ein[r][i] = __builtin_amdgcn_exp2f(-b[r]);
+                L.ecb[r][i] = __builtin_amdgcn_exp2f(acc - b[r]);
+            }
+        }
+    } else if (tid == BT - 1) {
+        float acc = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            acc += L.sb[r];
+            L.sb[r] = acc;
+        }
+    }
+    lds_barrier();
+    // 3. normalised rows; EJK row factors
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+        const int e = tid + m * BT;
+        const int r = e / DK, i = e % DK;
+        L.qh[r][i] = p.l2norm ? p.scale * L.qh[r][i] / L.nq[r] : p.scale * L.qh[r][i];
+        L.kh[r][i] = p.l2norm ? L.kh[r][i] / L.nk[r] : L.kh[r][i];
+    }
+    if (EJK && tid < BC) {
+        const int r = tid;
+        const float b = L.sb[r], bp = r > 0 ? L.sb[r - 1] : 0.f, bC = L.sb[BC - 1];
+        L.seb[r] = __builtin_amdgcn_exp2f(b);
+        L.sebp[r] = __builtin_amdgcn_exp2f(bp);
+        L.secb[r] = __builtin_amdgcn_exp2f(bC - b);
+        if (r == 0) L.sec = __builtin_amdgcn_exp2f(bC);
+    }
+    lds_barrier();
+    // 4. the Gram products on 16x16x4 float32 MFMA: wave 0 GA (kh e^{b'} against
+    // kh e^{-b}), wave 1 GP (qh e^{b} against kh e^{-b}); EJK: the plain dots,
+    // scaled by the element factors.  Lane (lm, lk) supplies channel
+    // k0 + 4 lk + u of row lm of both operands and holds rows 4 lk + e of
+    // column lm.
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        const int lm = lane & 15, lk = lane >> 4;
+        if (wave < 2) {
+            const float (*X)[SR] = wave == 0 ? L.kh : L.qh;
+            bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int kk = k0 + 4 * lk + u;
+                    const float a = EJK ? X[lm][kk] : X[lm][kk] * L.eb[lm][kk];
+                    const float b = EJK ? L.kh[lm][kk] : L.kh[lm][kk] * L.ein[lm][kk];
+                    acc = bmfma4(a, b, acc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e, s = lm;
+                float x = acc[e];
+                if (wave == 0) {
+                    if (EJK) {
+                        const float bp = r > 0 ? L.sb[r - 1] : 0.f;
+                        const float da = s < r ? __builtin_amdgcn_exp2f(bp - L.sb[s]) : 0.f;
+                        L.DA[r][s] = da;
+                        x *= da;
+                    }
+                    L.GA[r][s] = s < r ? x : 0.f;
+                } else {
+                    if (EJK) {
+                        const float dp = s <= r ? __builtin_amdgcn_exp2f(L.sb[r] - L.sb[s]) : 0.f;
+                        L.DP[r][s] = dp;
+                        x *= dp;
+                    }
+                    L.GP[r][s] = s <= r ? x : 0.f;
+                }
+            }
+        }
+    }
+    lds_barrier();
+}
+
 template <int DK, bool EJK>
 __device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, int nr, int h, int hk)
 {
@@ -221,113 +339,12 @@ __device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, in
             L.beta[r] = valid ? sigmoid_f(p.beta[tok * H + h]) : 0.f;
         }
     }
-    __syncthreads();
-    // 2. row norms: eight lanes per (row, q or k), summed by DPP and swizzle;
-    // cumulative log-decays and their factors: a thread per key channel
-    {
-        const int pr = tid >> 3, part = tid & 7;   // 32 (row, q/k) pairs
-        const int r = pr & 15;
-        const float* row = pr < 16 ? L.qh[r] : L.kh[r];
-        float ss = 0.f;
-        for (int i = part; i < DK; i += 8) ss = fmaf(row[i], row[i], ss);
-        ss = xor_add<1>(ss);
-        ss = xor_add<2>(ss);
-        ss = xor_add<4>(ss);
-        if (part == 0) (pr < 16 ? L.nq : L.nk)[r] = sqrtf(ss + kNormEps);
-    }
-    if (!EJK) {
-        if (tid < DK) {
-            const int i = tid;
-            float b[BC];
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 0; r < BC; ++r) {
-                acc += L.eb[r][i];
-                b[r] = acc;
-            }
-            L.ec[i] = __builtin_amdgcn_exp2f(acc);
-#pragma unroll
-            for (int r = 0; r < BC; ++r) {
-                L.eb[r][i] = __builtin_amdgcn_exp2f(b[r]);
-                L.ein[r][i] = __builtin_amdgcn_exp2f(-b[r]);
-                L.ecb[r][i] = __builtin_amdgcn_exp2f(acc - b[r]);
-            }
-        }
-    } else if (tid == BT - 1) {
-        float acc = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            acc += L.sb[r];
-            L.sb[r] = acc;
-        }
-    }
-    __syncthreads();
-    // 3. normalised rows; EJK row factors
-#pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + m * BT;
-        const int r = e / DK, i = e % DK;
-        L.qh[r][i] = p.l2norm ? p.scale * L.qh[r][i] / L.nq[r] : p.scale * L.qh[r][i];
-        L.kh[r][i] = p.l2norm ? L.kh[r][i] / L.nk[r] : L.kh[r][i];
-    }
-    if (EJK && tid < BC) {
-        const int r = tid;
-        const float b = L.sb[r], bp = r > 0 ? L.sb[r - 1] : 0.f, bC = L.sb[BC - 1];
-        L.seb[r] = __builtin_amdgcn_exp2f(b);
-        L.sebp[r] = __builtin_amdgcn_exp2f(bp);
-        L.secb[r] = __builtin_amdgcn_exp2f(bC - b);
-        if (r == 0) L.sec = __builtin_amdgcn_exp2f(bC);
-    }
-    __syncthreads();
-    // 4. the Gram products on 16x16x4 float32 MFMA: wave 0 GA (kh e^{b'} against
-    // kh e^{-b}), wave 1 GP (qh e^{b} against kh e^{-b}); EJK: the plain dots,
-    // scaled by the element factors.  Lane (lm, lk) supplies channel
-    // k0 + 4 lk + u of row lm of both operands and holds rows 4 lk + e of
-    // column lm.
-    {
-        const int lane = tid & 63, wave = tid >> 6;
-        const int lm = lane & 15, lk = lane >> 4;
-        if (wave < 2) {
-            const float (*X)[SR] = wave == 0 ? L.kh : L.qh;
-            bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int k0 = 0; k0 < DK; k0 += 16) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int kk = k0 + 4 * lk + u;
-                    const float a = EJK ? X[lm][kk] : X[lm][kk] * L.eb[lm][kk];
-                    const float b = EJK ? L.kh[lm][kk] : L.kh[lm][kk] * L.ein[lm][kk];
-                    acc = bmfma4(a, b, acc);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lk + e, s = lm;
-                float x = acc[e];
-                if (wave == 0) {
-                    if (EJK) {
-                        const float bp = r > 0 ? L.sb[r - 1] : 0.f;
-                        const float da = s < r ? __builtin_amdgcn_exp2f(bp - L.sb[s]) : 0.f;
-                        L.DA[r][s] = da;
-                        x *= da;
-                    }
-                    L.GA[r][s] = s < r ? x : 0.f;
-                } else {
-                    if (EJK) {
-                        const float dp = s <= r ? __builtin_amdgcn_exp2f(L.sb[r] - L.sb[s]) : 0.f;
-                        L.DP[r][s] = dp;
-                        x *= dp;
-                    }
-                    L.GP[r][s] = s <= r ? x : 0.f;
-                }
-            }
-        }
-    }
-    __syncthreads();
+    setup_rest<DK, EJK>(L, p);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 1: forward state carry per (column tile, head, sequence); stores the
-// state entering every chunk.
+// state entering every chunk and the chunk's Y and U.
 template <int DK, bool EJK>
 __global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
 {
@@ -348,7 +365,7 @@ __global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
     const int nck = seq_chunks(p.off, n, t0, t1);
     const int slot0 = p.off[n];
     for (int c = 0; c < nck; ++c) {
-        __syncthreads();
+        lds_barrier();
         float* dst = p.ckS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0;
         for (int e = tid; e < DK * TV; e += BT) {
             const int i = e / TV, j = e % TV;
@@ -363,7 +380,7 @@ __global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
             const float vv = r < nr ? ldx(p.v, ((size_t)(c0 + r) * p.Hkv + hk) * dv + j0 + j, p.in_bf16) : 0.f;
             Y[r][j] = vv - acc;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < TV) {
             const int j = tid;
             float u[BC];
@@ -376,7 +393,13 @@ __global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
                 U[r][j] = u[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
+        {
+            const int r = tid / TV, j = tid % TV;
+            float* yu = p.ckYU + ((size_t)(slot0 + c) * H + h) * 2 * BC * dv + j0;
+            yu[(size_t)r * dv + j] = Y[r][j];
+            yu[(size_t)(BC + r) * dv + j] = U[r][j];
+        }
         for (int e = tid; e < DK * TV; e += BT) {
             const int i = e / TV, j = e % TV;
             float acc = L.ecc(i) * S[i][j];
@@ -387,7 +410,7 @@ __global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
 }
 
 // Pass 2: the state gradient carried backward per (16 state columns, head,
-// sequence); stores dL/d(state leaving) of every chunk, and at the end
+// sequence); stores dL/d(state leaving) and Z of every chunk, and at the end
 // dL/d(initial state).  The dk x 16 gradient tile stays in the accumulator
 // registers of 16x16x4 float32 MFMA, 16 rows per tile (tiles dealt over the
 // waves); the element e of a lane (lm, lk) holds row 4 lk + e, column lm,
@@ -461,8 +484,11 @@ __device__ __forceinline__ void rev_load(RevInputs<DK, EJK, Tin>& in, const BwdP
     }
 }
 
+// Two workgroups per CU (512 registers per lane shared by two waves per SIMD):
+// the (sequence, head, column tile) grid is then resident in one round at
+// the usual sizes.
 template <int DK, bool EJK, typename Tin>
-__global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rev_scan(BwdParams p)
 {
     using LT = RevLds<DK, EJK>;
     constexpr int RS = LT::RS;
@@ -511,7 +537,7 @@ __global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // 1. this chunk's inputs to LDS (rows past nr neutral); the chunk
         // before is loaded meanwhile
 #pragma unroll
@@ -533,7 +559,7 @@ __global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
             const int cp = c0 - BC;
             rev_load(in, p, cp, BC, h, hk, j0);
         }
-        __syncthreads();
+        lds_barrier();
         // 2. row scales (eight lanes per row, summed by DPP / swizzle); EJK:
         // the scalar cumulative decays, each of 16 lanes summing in row order
         {
@@ -568,7 +594,7 @@ __global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
             L.SECB[r] = __builtin_amdgcn_exp2f(acc - b);
             if (r == 0) L.SEC = __builtin_amdgcn_exp2f(acc);
         }
-        __syncthreads();
+        lds_barrier();
         // 3. normalised and decayed rows: KDA a thread per (channel, rows of
         // its part), the channel's prefix sums in registers
         if constexpr (!EJK) {
@@ -604,7 +630,7 @@ __global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
                 L.KG[r * RS + i] *= L.NK[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // 4. MFMA: each wave its tiles' part of Kc dS; wave 0 the Gram A, wave
         // 1 the Gram P and P^T dO (its P accumulator is that product's A operand)
         {
@@ -664,23 +690,25 @@ __global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
         }
-        __syncthreads();
+        lds_barrier();
         // 5. (I + A)^T Z = dU by back substitution, a lane per column
         if (tid < TV) {
             const int j = tid;
+            float* zd = p.ckZ + ((size_t)(slot0 + c) * H + h) * BC * dv + j0 + j;
             float z[BC];
 #pragma unroll
             for (int r = 0; r < BC; ++r) z[r] = (L.PU[0][r][j] + L.PU[1][r][j]) + (L.PU[2][r][j] + L.PU[3][r][j]);
 #pragma unroll
             for (int s = BC - 1; s >= 0; --s) {
                 const float zs = z[s];
+                zd[(size_t)s * dv] = zs;
                 const float dy = L.BE[s] * zs;
                 L.DY[s][j] = EJK ? dy * L.SEBP[s] : dy;
 #pragma unroll
                 for (int r = 0; r < s; ++r) z[r] = fmaf(-L.CA[s][r], zs, z[r]);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // 6. dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
@@ -719,30 +747,41 @@ __global__ __launch_bounds__(BT) void bwd_rev_scan(BwdParams p)
     }
 }
 
-// Pass 3: the gradients of one chunk's rows, from the state entering it and
-// the gradient of the state leaving it; one workgroup per (chunk, head) with
-// all state columns.
-template <int DK, bool EJK>
-__global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
+// Pass 3: the gradients of one chunk's rows, from the state entering it
+// (S0), the gradient of the state leaving it (dS1), the chunk's Y and U (pass
+// 1) and Z (pass 2); one workgroup per (chunk, head) with all state columns.
+// Every global load of the chunk is issued first.  The products run on
+// 16x16x4 float32 MFMA; from the Gram-role products on, each lane keeps the
+// elements (row 4 lk + e, channel 16 t + lm) of its tiles in registers up to
+// their stores, so LDS holds the set-up, dO, U, Z and small per-row arrays,
+// and two workgroups share a CU.
+template <int DK, bool EJK, typename Tin>
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_local(BwdParams p)
 {
+    constexpr int NT = DK / 16;               // 16-channel tiles
+    constexpr int NW = BT / kWave;
+    constexpr int TPW = (NT + NW - 1) / NW;   // tiles per wave
+    constexpr int NJ = MAXD / 16;
+    constexpr int NE = BC * DK / BT;          // q, k elements per thread
+    constexpr int NV = BC * MAXD / BT;        // [16][MAXD] elements per thread
+    static_assert(BT == 2 * MAXD && NW == 4, "a [16][MAXD] row spans two waves");
     __shared__ ChunkLds<DK, EJK> L;
     __shared__ float dO[BC][SR];
-    __shared__ float Y[BC][SR];    // V, then Y = V - Kg S0
-    __shared__ float W[BC][SR];    // dU, then dqh
     __shared__ float U[BC][SR];
     __shared__ float Z[BC][SR];
-    __shared__ float Gk[BC][SR];   // dkh
-    __shared__ float Gb[BC][SR];   // db (KDA: db + db'), then dgamma
-    __shared__ float Gp[BC][SR];   // EJK: db'
-    __shared__ float Kd[BC][SR];   // Kc dKc, elementwise
     __shared__ float MA[BC][BC + 1], MP[BC][BC + 1], dA[BC][BC + 1];
-    __shared__ float dbt[BC], pq[BC], pk[BC];
-    __shared__ float dbc[MAXD];
-    __shared__ float red[BT / kWave];
+    __shared__ float zyw[NW][NV];               // Z.Y partials, row 2 m + (wave >> 1)
+    __shared__ float rq[NW][BC], rk[NW][BC];    // row dots of the L2-norm backward, per wave
+    __shared__ float ra[NW][BC], rb[NW][BC], rc[NW][BC], rd[NW];   // EJK row sums, per wave
+    __shared__ float dbt[BC], dgs[BC];
+    __shared__ float red[NW];
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lm = lane & 15, lk = lane >> 4;
     const int slot = blockIdx.x, h = blockIdx.y;
     const int H = p.H, Hkv = p.Hkv, dv = p.dv;
     const int hk = h / (H / Hkv);
+    const bool grouped = Hkv != H;
     if (slot >= p.off[p.N]) return;
     // the sequence of this chunk: the last n with off[n] <= slot
     int lo = 0, hi = p.N - 1;
@@ -755,295 +794,433 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
     const int c0 = t0 + (slot - p.off[n]) * BC, nr = min(BC, t1 - c0);
-    for (int e = tid; e < BC * MAXD; e += BT) {
-        const int r = e / MAXD, j = e % MAXD;
-        const bool ok = r < nr && j < dv;
-        dO[r][j] = ok ? ldx(p.d_o, ((size_t)(c0 + r) * H + h) * dv + j, p.do_bf16) : 0.f;
-        Y[r][j] = ok ? ldx(p.v, ((size_t)(c0 + r) * Hkv + hk) * dv + j, p.in_bf16) : 0.f;
-    }
-    chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
-    const float* S0 = p.ckS + ((size_t)slot * H + h) * DK * dv;
-    const float* dS1 = p.ckdS + ((size_t)slot * H + h) * DK * dv;
-    // (a) Y = V - Kg S0 and dU = P^T dO + Kc dS1.  The products over dk run on
-    // 16x16x4 float32 MFMA, a 16-column tile of the state per step (tiles
-    // dealt over the waves): lane (lm, lk) supplies Kg[lm][k], Kc[lm][k] and
-    // S0[k][lm], dS1[k][lm] for k = k0 + 4 lk + u at step u, and holds rows
-    // 4 lk + e of column lm of the result.
+    const int nj = dv / 16;
+    const float ea = EJK ? 0.f : expf(p.a_log[h]);
+    // ---- loads.  S0 and dS1 rows of this wave's channel tiles, 16 bytes per
+    // lane per 16 columns (lane (lm, lk): row 16 t + lm, columns 16 jb + 4 lk ..)
+    float4 s0r[TPW][NJ], d1r[TPW][NJ];
     {
-        const int lane = tid & 63, wave = tid >> 6;
-        const int lm = lane & 15, lk = lane >> 4;
-        for (int jt = wave; jt < dv / 16; jt += BT / 64) {
-            const int j = 16 * jt + lm;
-            bf32x4_t ay = bf32x4_t{0.f, 0.f, 0.f, 0.f}, au = ay;
-#pragma unroll 2
-            for (int k0 = 0; k0 < DK; k0 += 16) {
+        const float* S0 = p.ckS + ((size_t)slot * H + h) * DK * dv;
+        const float* dS1 = p.ckdS + ((size_t)slot * H + h) * DK * dv;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int kk = k0 + 4 * lk + u;
-                    ay = bmfma4(L.kg(lm, kk), S0[(size_t)kk * dv + j], ay);
-                    au = bmfma4(L.kc(lm, kk), dS1[(size_t)kk * dv + j], au);
-                }
-            }
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lk + e;
-                float acc = au[e];
-                for (int s = r; s < BC; ++s) acc = fmaf(L.GP[s][r], dO[s][j], acc);
-                W[r][j] = acc;
-                Y[r][j] -= ay[e];
+            for (int jb = 0; jb < NJ; ++jb) {
+                const bool ok = t < NT && jb < nj;
+                const size_t o = (size_t)(16 * t + lm) * dv + 16 * jb + 4 * lk;
+                s0r[x][jb] = ok ? *reinterpret_cast<const float4*>(S0 + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+                d1r[x][jb] = ok ? *reinterpret_cast<const float4*>(dS1 + o) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
     }
-    __syncthreads();
-    // (b) (I + A) U = diag(beta) Y and (I + A)^T Z = dU, one column per thread
-    if (tid < dv) {
-        const int j = tid;
-        float u[BC], z[BC];
+    // the rows of q, k and the gate (element e = tid + m BT: row e / DK, channel e % DK)
+    const Tin* qq = static_cast<const Tin*>(p.q);
+    const Tin* kk = static_cast<const Tin*>(p.k);
+    Tin xq[NE], xk[NE];
+    float xg[EJK ? 1 : NE];
 #pragma unroll
-        for (int r = 0; r < BC; ++r) {
-            float x = Y[r][j];
-#pragma unroll
-            for (int s = 0; s < r; ++s) x = fmaf(-L.GA[r][s], u[s], x);
-            u[r] = L.beta[r] * x;
-            U[r][j] = u[r];
-        }
-#pragma unroll
-        for (int r = BC - 1; r >= 0; --r) {
-            float x = W[r][j];
-#pragma unroll
-            for (int s = r + 1; s < BC; ++s) x = fmaf(-L.beta[s] * L.GA[s][r], z[s], x);
-            z[r] = x;
-            Z[r][j] = x;
-        }
+    for (int m = 0; m < NE; ++m) {
+        const int e = tid + m * BT;
+        const int r = e / DK, i = e % DK;
+        const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
+        xq[m] = qq[(tok * H + h) * DK + i];
+        xk[m] = kk[(tok * Hkv + hk) * DK + i];
+        if (!EJK) xg[m] = p.g[(tok * H + h) * DK + i];
     }
-    __syncthreads();
-    // (c) dA = -strict_lower(Z U^T), dP = lower(dO U^T); the Gram-product
-    // gradients MA = diag(beta) dA, MP = dP (EJK: times the decay factors)
+    const float dtb_row = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
+    // dO (raw bits), U, Z, Y: element e = tid + m BT, row e / MAXD, column e % MAXD
+    uint32_t xo[NV];
+    float xu[NV], xz[NV], xy[NV];
     {
-        const int r = tid >> 4, s = tid & 15;
-        float a = 0.f, b = 0.f;
-        if (s <= r) {
-            for (int j = 0; j < dv; ++j) {
-                a = fmaf(Z[r][j], U[s][j], a);
-                b = fmaf(dO[r][j], U[s][j], b);
-            }
+        const float* yu = p.ckYU + ((size_t)slot * H + h) * 2 * BC * dv;
+        const float* zz = p.ckZ + ((size_t)slot * H + h) * BC * dv;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / MAXD, j = e % MAXD;
+            const bool ok = j < dv;   // rows past nr: Y, U and Z are stored as zero
+            const size_t od = ((size_t)(c0 + (r < nr ? r : 0)) * H + h) * dv + j;
+            if (p.do_bf16) xo[m] = ok && r < nr ? (uint32_t)static_cast<const uint16_t*>(p.d_o)[od] << 16 : 0u;
+            else xo[m] = ok && r < nr ? __float_as_uint(static_cast<const float*>(p.d_o)[od]) : 0u;
+            xy[m] = ok ? yu[(size_t)r * dv + j] : 0.f;
+            xu[m] = ok ? yu[(size_t)(BC + r) * dv + j] : 0.f;
+            xz[m] = ok ? zz[(size_t)r * dv + j] : 0.f;
         }
-        const float da = s < r ? -a : 0.f;
-        dA[r][s] = da;
-        MA[r][s] = EJK ? L.beta[r] * da * L.DA[r][s] : L.beta[r] * da;
-        MP[r][s] = EJK ? b * L.DP[r][s] : b;
     }
-    __syncthreads();
+    float xb = 0.f, xgs = 0.f;
     if (tid < BC) {
-        const int r = tid;
-        float acc = 0.f;
-        for (int j = 0; j < dv; ++j) acc = fmaf(Z[r][j], Y[r][j], acc);
-        for (int s = 0; s < r; ++s) acc = fmaf(dA[r][s], L.GA[r][s], acc);
-        dbt[r] = acc;
+        const size_t tok = (size_t)(c0 + (tid < nr ? tid : 0));
+        xb = p.beta[tok * H + h];
+        xgs = (EJK && p.g) ? p.g[tok * H + h] : 0.f;
     }
-    // (d1) dQg = dO S0^T, dKg = -dY S0^T and dKc = U dS1^T on MFMA, a 16-channel
-    // tile per step: lane (lm, lk) supplies dO[lm][j], dY[lm][j], U[lm][j] and
-    // S0[i][j], dS1[i][j] (i = 16 tt + lm, j = j0 + 4 lk + u at step u) and
-    // holds rows 4 lk + e of channel i of the results, which go to W, Gk and
-    // Kd (each element is read back, and overwritten, by the thread that
-    // owns it in (d2)).  The same S0, dS1 elements give sum_j S0_ij dS1_ij.
-    __syncthreads();   // dbt above still reads Y; W's dU is consumed
+    // KDA: the gate and dt_bias of the elements this lane owns in the MFMA layout
+    float gl[TPW][4], dtl[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int t = wave + NW * x;
+        const bool ok = !EJK && t < NT;
+        dtl[x] = ok && p.dt_bias ? p.dt_bias[(size_t)(16 * t + lm) * H + h] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lk + e;
+            const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
+            gl[x][e] = ok ? p.g[(tok * H + h) * DK + 16 * t + lm] : 0.f;
+        }
+    }
+    // ---- to LDS: the raw rows, gate activations (log2 units), beta; dO, U, Z
     {
-        const int lane = tid & 63, wave = tid >> 6;
-        const int lm = lane & 15, lk = lane >> 4;
-        for (int tt = wave; tt < DK / 16; tt += BT / 64) {
-            const int i = 16 * tt + lm;
-            bf32x4_t aq = bf32x4_t{0.f, 0.f, 0.f, 0.f}, ag = aq, ac = aq;
-            float sdot = 0.f;
-            const float* s0r = S0 + (size_t)i * dv;
-            const float* d1r = dS1 + (size_t)i * dv;
-            for (int j0 = 0; j0 < dv; j0 += 16) {
-                const float4 s4 = *reinterpret_cast<const float4*>(s0r + j0 + 4 * lk);
-                const float4 d4 = *reinterpret_cast<const float4*>(d1r + j0 + 4 * lk);
-                const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float lb2 = p.lb * kLog2e;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int jj = j0 + 4 * lk + u;
-                    aq = bmfma4(dO[lm][jj], sv[u], aq);
-                    ag = bmfma4(-L.beta[lm] * Z[lm][jj], sv[u], ag);
-                    ac = bmfma4(U[lm][jj], dv4[u], ac);
-                    sdot = fmaf(sv[u], dv4[u], sdot);
-                }
+        for (int m = 0; m < NE; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / DK, i = e % DK;
+            const bool ok = r < nr;
+            L.qh[r][i] = ok ? widen(xq[m]) : 0.f;
+            L.kh[r][i] = ok ? widen(xk[m]) : 0.f;
+            if (!EJK) L.eb[r][i] = ok ? lb2 * sigmoid_f(ea * (xg[m] + dtb_row)) : 0.f;
+        }
+        if (tid < BC) {
+            const bool ok = tid < nr;
+            L.beta[tid] = ok ? (EJK ? xb : sigmoid_f(xb)) : 0.f;
+            if (EJK) L.sb[tid] = ok ? xgs * kLog2e : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / MAXD, j = e % MAXD;
+            dO[r][j] = __uint_as_float(xo[m]);
+            U[r][j] = xu[m];
+            Z[r][j] = xz[m];
+            // Z.Y of row r: a partial per wave (each wave covers half a row)
+            const float zy = wave_sum(xz[m] * xy[m]);
+            if (lane == 0) zyw[wave][m] = zy;
+        }
+    }
+    setup_rest<DK, EJK>(L, p);
+    // (c) over the columns: wave 0 dA = -strict_lower(Z U^T), wave 1 dP =
+    // lower(dO U^T); the Gram-product gradients MA = diag(beta) dA, MP = dP
+    // (EJK: times the decay factors).  Lane (lm, lk) supplies row lm of both
+    // operands at columns 16 jb + 4 lk + u.
+    if (wave < 2) {
+        const float (*A)[SR] = wave == 1 ? dO : Z;
+        bf32x4_t m = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int jb = 0; jb < nj; ++jb) {
+            const float4 a = *reinterpret_cast<const float4*>(&A[lm][16 * jb + 4 * lk]);
+            const float4 b = *reinterpret_cast<const float4*>(&U[lm][16 * jb + 4 * lk]);
+            m = bmfma4(a.x, b.x, m);
+            m = bmfma4(a.y, b.y, m);
+            m = bmfma4(a.z, b.z, m);
+            m = bmfma4(a.w, b.w, m);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lk + e, s = lm;
+            if (wave == 0) {
+                const float da = s < r ? -m[e] : 0.f;
+                dA[r][s] = da;
+                MA[r][s] = EJK ? L.beta[r] * da * L.DA[r][s] : L.beta[r] * da;
+            } else {
+                const float b = s <= r ? m[e] : 0.f;
+                MP[r][s] = EJK ? b * L.DP[r][s] : b;
             }
+        }
+    }
+    // (d1) dQg = dO S0^T, dKg = -dY S0^T and dKc = U dS1^T, a 16-channel tile
+    // per step: lane (lm, lk) supplies dO[lm][j], dY[lm][j], U[lm][j] and
+    // S0[i][j], dS1[i][j] (i = 16 t + lm, j = 16 jb + 4 lk + u at step u) and
+    // holds rows 4 lk + e of channel i.  The same S0, dS1 elements give
+    // dbc_i = e^{b_C,i} sum_j S0_ij dS1_ij.
+    bf32x4_t aq[TPW], ag[TPW], ac[TPW];
+    float dbcv[TPW];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lk + e;
-                W[r][i] = aq[e];
-                Gk[r][i] = ag[e];
-                Kd[r][i] = ac[e];
+    for (int x = 0; x < TPW; ++x) {
+        const int t = wave + NW * x;
+        aq[x] = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+        ag[x] = aq[x];
+        ac[x] = aq[x];
+        dbcv[x] = 0.f;
+        if (t < NT) {
+            float sdot = 0.f;
+            const float nb = -L.beta[lm];
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) {
+                if (jb < nj) {
+                    const float4 s4 = s0r[x][jb], d4 = d1r[x][jb];
+                    const float4 o4 = *reinterpret_cast<const float4*>(&dO[lm][16 * jb + 4 * lk]);
+                    const float4 z4 = *reinterpret_cast<const float4*>(&Z[lm][16 * jb + 4 * lk]);
+                    const float4 u4 = *reinterpret_cast<const float4*>(&U[lm][16 * jb + 4 * lk]);
+                    aq[x] = bmfma4(o4.x, s4.x, aq[x]);
+                    aq[x] = bmfma4(o4.y, s4.y, aq[x]);
+                    aq[x] = bmfma4(o4.z, s4.z, aq[x]);
+                    aq[x] = bmfma4(o4.w, s4.w, aq[x]);
+                    ag[x] = bmfma4(nb * z4.x, s4.x, ag[x]);
+                    ag[x] = bmfma4(nb * z4.y, s4.y, ag[x]);
+                    ag[x] = bmfma4(nb * z4.z, s4.z, ag[x]);
+                    ag[x] = bmfma4(nb * z4.w, s4.w, ag[x]);
+                    ac[x] = bmfma4(u4.x, d4.x, ac[x]);
+                    ac[x] = bmfma4(u4.y, d4.y, ac[x]);
+                    ac[x] = bmfma4(u4.z, d4.z, ac[x]);
+                    ac[x] = bmfma4(u4.w, d4.w, ac[x]);
+                    sdot = fmaf(s4.x, d4.x, sdot);
+                    sdot = fmaf(s4.y, d4.y, sdot);
+                    sdot = fmaf(s4.z, d4.z, sdot);
+                    sdot = fmaf(s4.w, d4.w, sdot);
+                }
             }
             // sum over the four lane groups (lanes lm, lm + 16, lm + 32, lm + 48)
             sdot = xor_add<16>(sdot);
             sdot = xor_add<32>(sdot);
-            if (lk == 0) dbc[i] = L.ecc(i) * sdot;
+            dbcv[x] = L.ecc(16 * t + lm) * sdot;
         }
     }
-    __syncthreads();
-    // (d2) per channel i and 8 rows: the Gram roles and the row gradients dqh,
-    // dkh, db, db'
-    {
-        const int i = tid % MAXD, r0 = (tid / MAXD) * 8;
-        if (i < DK) {
-            float aq[8], ag[8], ac[8];
+    lds_barrier();
+    if (tid < BC) {
+        const int r = tid;
+        // rows 2 m + half were covered by waves 2 half and 2 half + 1
+        const int m = r >> 1, w0 = 2 * (r & 1);
+        float acc = zyw[w0][m] + zyw[w0 + 1][m];
+        for (int s = 0; s < r; ++s) acc = fmaf(dA[r][s], L.GA[r][s], acc);
+        dbt[r] = acc;
+    }
+    // (d2) the Gram roles on MFMA, per 16-channel tile: D[r][i] = sum_s M[r][s]
+    // X[s][i] with the lane supplying M[lm][s] (or M[s][lm] for M^T) and
+    // X[s][16 t + lm] for s = 4 lk + u at step u.  The pair terms whose row and
+    // column roles fall on the same b (the diagonal of P, and for EJK the first
+    // sub-diagonal of A) are kept apart: they enter dqh and dkh but cancel
+    // exactly in dgamma, so they are left out of db.  Then the row gradients
+    // dqh, dkh, db, db' and Kc dKc of the lane's elements.
+    float dqh[TPW][4], dkh[TPW][4], gb[TPW][4], gp[TPW][4], kd[TPW][4];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                aq[m] = W[r0 + m][i];
-                ag[m] = Gk[r0 + m][i];
-                ac[m] = Kd[r0 + m][i];
+    for (int x = 0; x < TPW; ++x) {
+        const int t = wave + NW * x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dqh[x][e] = dkh[x][e] = gb[x][e] = gp[x][e] = kd[x][e] = 0.f;
+        if (t < NT) {
+            const int i = 16 * t + lm;
+            bf32x4_t R1 = bf32x4_t{0.f, 0.f, 0.f, 0.f}, R2 = R1, R3 = R1, R4 = R1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = 4 * lk + u;
+                float a1 = MA[lm][s], a2 = MA[s][lm];
+                const float a3 = s != lm ? MP[lm][s] : 0.f, a4 = s != lm ? MP[s][lm] : 0.f;
+                if (EJK) {
+                    if (s + 1 == lm) a1 = 0.f;
+                    if (lm + 1 == s) a2 = 0.f;
+                }
+                const float khs = L.kh[s][i], qhs = L.qh[s][i];
+                float b1, b2, b4;
+                if (EJK) {
+                    b1 = khs;
+                    b2 = khs;
+                    b4 = qhs;
+                } else {
+                    const float eb = L.eb[s][i];
+                    b1 = khs * L.ein[s][i];
+                    b2 = khs * eb;
+                    b4 = qhs * eb;
+                }
+                R1 = bmfma4(a1, b1, R1);   // rowA (before the row factor)
+                R2 = bmfma4(a2, b2, R2);   // colA
+                R3 = bmfma4(a3, b1, R3);   // rowP
+                R4 = bmfma4(a4, b4, R4);   // colP
             }
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int r = r0 + m;
-                // Gram roles; the pair terms whose row and column roles fall on
-                // the same b (the diagonal of P, and for EJK the first
-                // sub-diagonal of A) are kept apart: they enter dqh and dkh but
-                // cancel exactly in dgamma, so they are left out of db
-                float rowA = 0.f, colA = 0.f, rowP = 0.f, colP = 0.f, subA = 0.f, subAc = 0.f;
-                const float mpd = MP[r][r];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e;
+                float rowA = R1[e], colA = R2[e], rowP = R3[e], colP = R4[e], subA = 0.f, subAc = 0.f;
                 if (!EJK) {
-                    for (int s = 0; s < BC; ++s) {
-                        const float ki = L.kh[s][i] * L.ein[s][i];
-                        rowA = fmaf(MA[r][s], ki, rowA);
-                        colA = fmaf(MA[s][r], L.kh[s][i] * L.eb[s][i], colA);
-                        if (s != r) {
-                            rowP = fmaf(MP[r][s], ki, rowP);
-                            colP = fmaf(MP[s][r], L.qh[s][i] * L.eb[s][i], colP);
-                        }
-                    }
-                    rowA *= L.eb[r][i];
-                    rowP *= L.eb[r][i];
-                    colA *= L.ein[r][i];
-                    colP *= L.ein[r][i];
+                    const float eb = L.eb[r][i], ein = L.ein[r][i];
+                    rowA *= eb;
+                    rowP *= eb;
+                    colA *= ein;
+                    colP *= ein;
                 } else {
-                    for (int s = 0; s < BC; ++s) {
-                        if (s + 1 == r) subA = MA[r][s] * L.kh[s][i];
-                        else rowA = fmaf(MA[r][s], L.kh[s][i], rowA);
-                        if (s == r + 1) subAc = MA[s][r] * L.kh[s][i];
-                        else colA = fmaf(MA[s][r], L.kh[s][i], colA);
-                        if (s != r) {
-                            rowP = fmaf(MP[r][s], L.kh[s][i], rowP);
-                            colP = fmaf(MP[s][r], L.qh[s][i], colP);
-                        }
-                    }
+                    subA = r > 0 ? MA[r][r - 1] * L.kh[r - 1][i] : 0.f;
+                    subAc = r + 1 < BC ? MA[r + 1][r] * L.kh[r + 1][i] : 0.f;
                 }
+                const float mpd = MP[r][r];
                 const float qh = L.qh[r][i], kh = L.kh[r][i];
                 const float ebr = L.ebr(r, i), ebpr = L.ebpr(r, i), ecbr = L.ecbr(r, i);
                 const float qg = qh * ebr, kg = kh * ebpr, kc = kh * ecbr;
-                W[r][i] = rowP + mpd * kh + ebr * aq[m];
-                Gk[r][i] = rowA + subA + colA + subAc + colP + mpd * qh + ebpr * ag[m] + ecbr * ac[m];
-                const float db = qh * rowP - kh * colA - kh * colP + qg * aq[m];
-                const float dbp = kh * rowA + kg * ag[m];
-                if (EJK) {
-                    Gb[r][i] = db;
-                    Gp[r][i] = dbp;
-                } else {
-                    Gb[r][i] = db + dbp;
-                }
-                Kd[r][i] = kc * ac[m];
+                dqh[x][e] = rowP + mpd * kh + ebr * aq[x][e];
+                dkh[x][e] = rowA + subA + colA + subAc + colP + mpd * qh + ebpr * ag[x][e] + ecbr * ac[x][e];
+                const float db = qh * rowP - kh * colA - kh * colP + qg * aq[x][e];
+                const float dbp = kh * rowA + kg * ag[x][e];
+                gb[x][e] = EJK ? db : db + dbp;
+                gp[x][e] = dbp;
+                kd[x][e] = kc * ac[x][e];
             }
         }
     }
-    __syncthreads();
-    // (e) dgamma_u: the reverse cumulative sum of db, the carry's e^{b_C} term
-    // (on every row) and the Kc terms of the rows before u
-    if (!EJK) {
-        if (tid < DK) {
-            const int i = tid;
-            float pre[BC];
-            float acc = 0.f;
+    // ---- per-row sums over the channels: a partial per lane over its tiles,
+    // summed over the 16 lanes of a row group, one value per wave and row
+    {
+        float sq[4], sk[4], sa[4], sb2[4], sc[4], sd = 0.f;
 #pragma unroll
-            for (int r = 0; r < BC; ++r) {
-                pre[r] = acc;
-                acc += Kd[r][i];
+        for (int e = 0; e < 4; ++e) sq[e] = sk[e] = sa[e] = sb2[e] = sc[e] = 0.f;
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            if (t < NT) {
+                const int i = 16 * t + lm;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * lk + e;
+                    sq[e] = fmaf(L.qh[r][i], dqh[x][e], sq[e]);
+                    sk[e] = fmaf(L.kh[r][i], dkh[x][e], sk[e]);
+                    if (EJK) {
+                        sa[e] += gb[x][e];
+                        sb2[e] += gp[x][e];
+                        sc[e] += kd[x][e];
+                    }
+                }
+                if (EJK && lk == 0) sd += dbcv[x];
             }
-            float run = dbc[i];
+        }
+        auto row16 = [](float v) {
+            v = xor_add<1>(v);
+            v = xor_add<2>(v);
+            v = xor_add<4>(v);
+            return xor_add<8>(v);
+        };
 #pragma unroll
-            for (int r = BC - 1; r >= 0; --r) {
-                run += Gb[r][i];
-                Gb[r][i] = run + pre[r];
+        for (int e = 0; e < 4; ++e) {
+            const float q = row16(sq[e]), k = row16(sk[e]);
+            if (lm == 0) {
+                rq[wave][4 * lk + e] = q;
+                rk[wave][4 * lk + e] = k;
+            }
+            if (EJK) {
+                const float a = row16(sa[e]), b = row16(sb2[e]), c = row16(sc[e]);
+                if (lm == 0) {
+                    ra[wave][4 * lk + e] = a;
+                    rb[wave][4 * lk + e] = b;
+                    rc[wave][4 * lk + e] = c;
+                }
+            }
+        }
+        if (EJK) {
+            sd = row16(sd);
+            if (lane == 0) rd[wave] = sd;
+        }
+    }
+    lds_barrier();
+    // ---- dgamma.  KDA, per element: the reverse cumulative sum of db down the
+    // chunk, the carry's e^{b_C} term (dbc, on every row) and the Kc terms of
+    // the rows before.  A channel's rows are split over the four lane groups
+    // (rows 4 lk .. 4 lk + 3), joined through the group totals.
+    // EJK, per row: the same over the per-row sums, in one lane.
+    float dgm[TPW][4];
+    if (!EJK) {
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            float G = 0.f, K = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                G += gb[x][e];
+                K += kd[x][e];
+            }
+            float sufG = 0.f, preK = 0.f;
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                const float g2 = __shfl(G, lm + 16 * l);
+                const float k2 = __shfl(K, lm + 16 * l);
+                if (l > lk) sufG += g2;
+                if (l < lk) preK += k2;
+            }
+            float run = dbcv[x] + sufG;
+            float pre[4];
+            float acc = preK;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pre[e] = acc;
+                acc += kd[x][e];
+            }
+#pragma unroll
+            for (int e = 3; e >= 0; --e) {
+                run += gb[x][e];
+                dgm[x][e] = run + pre[e];
             }
         }
     } else {
-        if (tid < BC) {
-            const int r = tid;
-            float a = 0.f, b = 0.f, c = 0.f;
-            for (int i = 0; i < DK; ++i) {
-                a += Gb[r][i];
-                b += Gp[r][i];
-                c += Kd[r][i];
-            }
-            dA[r][0] = a;    // dA is free now: per-row db, db' and Kc terms
-            dA[r][1] = b;
-            dA[r][2] = c;
-        } else if (tid == BC) {
-            float a = 0.f;
-            for (int i = 0; i < DK; ++i) a += dbc[i];
-            dA[0][3] = a;
-        }
-        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < TPW; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dgm[x][e] = 0.f;
         if (tid == 0) {
+            float A[BC], B[BC], C[BC];
+            for (int r = 0; r < BC; ++r) {
+                A[r] = (ra[0][r] + ra[1][r]) + (ra[2][r] + ra[3][r]);
+                B[r] = (rb[0][r] + rb[1][r]) + (rb[2][r] + rb[3][r]);
+                C[r] = (rc[0][r] + rc[1][r]) + (rc[2][r] + rc[3][r]);
+            }
             float pre[BC];
             float acc = 0.f;
             for (int r = 0; r < BC; ++r) {
                 pre[r] = acc;
-                acc += dA[r][2];
+                acc += C[r];
             }
-            float run = dA[0][3];
+            float run = (rd[0] + rd[1]) + (rd[2] + rd[3]);
             for (int r = BC - 1; r >= 0; --r) {
-                run += dA[r][0] + (r + 1 < BC ? dA[r + 1][1] : 0.f);
-                Gb[r][0] = run + pre[r];
+                run += A[r] + (r + 1 < BC ? B[r + 1] : 0.f);
+                dgs[r] = run + pre[r];
             }
         }
+        lds_barrier();
     }
-    // row dots of the L2-norm backward
-    if (tid < 2 * BC) {
-        const int r = tid % BC;
-        const float* a = tid < BC ? L.qh[r] : L.kh[r];
-        const float* b = tid < BC ? W[r] : Gk[r];
-        float acc = 0.f;
-        for (int i = 0; i < DK; ++i) acc = fmaf(a[i], b[i], acc);
-        (tid < BC ? pq : pk)[r] = acc;
-    }
-    __syncthreads();
-    // (f) the prologue's backward and the stores
-    const bool grouped = Hkv != H;
-    const float ea = EJK ? 0.f : expf(p.a_log[h]);
+    // ---- the prologue's backward and the stores
     float apart = 0.f;
-    for (int e = tid; e < BC * DK; e += BT) {
-        const int r = e / DK, i = e % DK;
-        if (r >= nr) continue;
-        const size_t tok = (size_t)(c0 + r);
-        float dq, dk;
-        if (p.l2norm) {
-            const float inq = 1.f / L.nq[r], ink = 1.f / L.nk[r];
-            dq = p.scale * inq * (W[r][i] - L.qh[r][i] * pq[r] / (p.scale * p.scale));
-            dk = ink * (Gk[r][i] - L.kh[r][i] * pk[r]);
-        } else {
-            dq = p.scale * W[r][i];
-            dk = Gk[r][i];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int t = wave + NW * x;
+        float pdt = 0.f;
+        if (t < NT) {
+            const int i = 16 * t + lm;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e;
+                if (r < nr) {
+                    const size_t tok = (size_t)(c0 + r);
+                    const float pq = (rq[0][r] + rq[1][r]) + (rq[2][r] + rq[3][r]);
+                    const float pk = (rk[0][r] + rk[1][r]) + (rk[2][r] + rk[3][r]);
+                    float dq, dk;
+                    if (p.l2norm) {
+                        const float inq = 1.f / L.nq[r], ink = 1.f / L.nk[r];
+                        dq = p.scale * inq * (dqh[x][e] - L.qh[r][i] * pq / (p.scale * p.scale));
+                        dk = ink * (dkh[x][e] - L.kh[r][i] * pk);
+                    } else {
+                        dq = p.scale * dqh[x][e];
+                        dk = dkh[x][e];
+                    }
+                    p.dq[(tok * H + h) * DK + i] = dq;
+                    p.dk[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * DK + i] = dk;
+                    if (!EJK) {
+                        const float xx = ea * (gl[x][e] + dtl[x]);
+                        // sigma'(x) = sigma(x) sigma(-x): no cancellation in
+                        // 1 - sigma(x) when the gate saturates
+                        const float dx = dgm[x][e] * p.lb * sigmoid_f(xx) * sigmoid_f(-xx);
+                        p.dg[(tok * H + h) * DK + i] = dx * ea;
+                        apart = fmaf(dx, xx, apart);
+                        pdt += dx * ea;
+                    }
+                }
+            }
         }
-        p.dq[(tok * H + h) * DK + i] = dq;
-        p.dk[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * DK + i] = dk;
         if (!EJK) {
-            const float x = ea * (p.g[(tok * H + h) * DK + i] + (p.dt_bias ? p.dt_bias[(size_t)i * H + h] : 0.f));
-            // sigma'(x) = sigma(x) sigma(-x): no cancellation in 1 - sigma(x)
-            // when the gate saturates
-            const float dx = Gb[r][i] * p.lb * sigmoid_f(x) * sigmoid_f(-x);
-            p.dg[(tok * H + h) * DK + i] = dx * ea;
-            apart = fmaf(dx, x, apart);
-            Gk[r][i] = dx * ea;     // dg, for the dt_bias partial below
+            // dt_bias partial of channel i: the sum over the four lane groups
+            pdt = xor_add<16>(pdt);
+            pdt = xor_add<32>(pdt);
+            if (t < NT && lk == 0) p.part_dt[((size_t)slot * H + h) * DK + 16 * t + lm] = pdt;
         }
     }
-    for (int e = tid; e < BC * MAXD; e += BT) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+        const int e = tid + m * BT;
         const int r = e / MAXD, j = e % MAXD;
         if (r < nr && j < dv) {
             const size_t tok = (size_t)(c0 + r);
-            p.dv_out[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * dv + j] = L.beta[r] * Z[r][j];
+            p.dv_out[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * dv + j] = L.beta[r] * xz[m];
         }
     }
     if (tid < BC && tid < nr) {
@@ -1051,27 +1228,16 @@ __global__ __launch_bounds__(BT) void bwd_local(BwdParams p)
         const size_t tok = (size_t)(c0 + r);
         if (EJK) {
             p.dbeta[tok * H + h] = dbt[r];
+            if (p.dg) p.dg[tok * H + h] = dgs[r];
         } else {
-            const float l = p.beta[tok * H + h];
-            p.dbeta[tok * H + h] = dbt[r] * sigmoid_f(l) * sigmoid_f(-l);
+            p.dbeta[tok * H + h] = dbt[r] * sigmoid_f(xb) * sigmoid_f(-xb);
         }
-        if (EJK && p.dg) p.dg[tok * H + h] = Gb[r][0];
     }
     if (!EJK) {
         apart = wave_sum(apart);
-        if ((tid & (kWave - 1)) == 0) red[tid / kWave] = apart;
-        __syncthreads();
-        if (tid == 0) {
-            float a = 0.f;
-            for (int w = 0; w < BT / kWave; ++w) a += red[w];
-            p.part_a[(size_t)slot * H + h] = a;
-        }
-        if (tid < DK) {
-            const int i = tid;
-            float a = 0.f;
-            for (int r = 0; r < nr; ++r) a += Gk[r][i];
-            p.part_dt[((size_t)slot * H + h) * DK + i] = a;
-        }
+        if (lane == 0) red[wave] = apart;
+        lds_barrier();
+        if (tid == 0) p.part_a[(size_t)slot * H + h] = (red[0] + red[1]) + (red[2] + red[3]);
     }
 }
 
@@ -1102,7 +1268,7 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict_
         for (int s = tid; s < slots; s += 256) b += part_a[(size_t)s * H + h];
     }
     ra[tid] = b;
-    __syncthreads();
+    lds_barrier();
     if (tid < 32 && ddt_bias && i < dk) {
         float t = 0.f;
 #pragma unroll
@@ -1112,7 +1278,7 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict_
     if (do_a) {
         for (int w = 128; w > 0; w >>= 1) {
             if (tid < w) ra[tid] += ra[tid + w];
-            __syncthreads();
+            lds_barrier();
         }
         if (tid == 0) da_log[h] = ra[0];
     }
@@ -1156,7 +1322,9 @@ hipError_t launch_dk(const BwdParams& p, size_t slots, bool states_done, hipStre
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (slots > 0) {
-        hipLaunchKernelGGL((bwd_local<DK, EJK>), dim3((unsigned)slots, (unsigned)p.H), dim3(BT), 0, st, p);
+        const dim3 lgrid((unsigned)slots, (unsigned)p.H);
+        if (p.in_bf16) hipLaunchKernelGGL((bwd_local<DK, EJK, uint16_t>), lgrid, dim3(BT), 0, st, p);
+        else hipLaunchKernelGGL((bwd_local<DK, EJK, float>), lgrid, dim3(BT), 0, st, p);
         e = hipGetLastError();
     }
     return e;
@@ -1171,6 +1339,7 @@ size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bo
     const size_t ntok = packed ? (size_t)T : (size_t)N * T;
     size_t b = align256((size_t)(N + 1) * 4);
     b += 2 * align256(slots * H * dk * dv * 4);
+    b += align256(slots * H * 2 * BC * dv * 4) + align256(slots * H * BC * dv * 4);
     b += align256(slots * H * 4) + align256(slots * H * dk * 4);
     if (Hkv != H) b += align256(ntok * H * dk * 4) + align256(ntok * H * dv * 4);
     return b;
@@ -1197,6 +1366,10 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     w += align256(slots * a.H * a.dk * a.dv * 4);
     p.ckdS = reinterpret_cast<float*>(w);
     w += align256(slots * a.H * a.dk * a.dv * 4);
+    p.ckYU = reinterpret_cast<float*>(w);
+    w += align256(slots * a.H * 2 * BC * a.dv * 4);
+    p.ckZ = reinterpret_cast<float*>(w);
+    w += align256(slots * a.H * BC * a.dv * 4);
     p.part_a = reinterpret_cast<float*>(w);
     w += align256(slots * a.H * 4);
     p.part_dt = reinterpret_cast<float*>(w);
@@ -1224,7 +1397,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     pa.scale = a.scale; pa.lower_bound = a.lower_bound; pa.l2norm = a.l2norm != 0; pa.ejk = a.ejk;
     const bool states_done = chunk_states_f32_supported(pa);
     if (states_done) {
-        e = launch_chunk_states_f32(pa, off, p.ckS, st);
+        e = launch_chunk_states_f32(pa, off, p.ckS, p.ckYU, st);
         if (e != hipSuccess) return e;
     }
     switch (a.dk * 2 + (a.ejk ? 1 : 0)) {

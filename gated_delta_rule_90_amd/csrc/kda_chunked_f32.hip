@@ -171,8 +171,10 @@ __device__ __forceinline__ float lane_group_sum(float x)
 }
 
 // CK: instead of the output, store the state entering every chunk at
-// ck_states[(ck_off[n] + c) * H + h] ([dk][dv] float32): the forward pass of
-// the prefill's backward (chunks of 16 tokens, NB = 1).
+// ck_states[(ck_off[n] + c) * H + h] ([dk][dv] float32), and the chunk's
+// Y = V - Kg S0 and U at ck_yu[(ck_off[n] + c) * H + h] ([2][16][dv] float32,
+// padded rows zero): the forward pass of the prefill's backward (chunks of 16
+// tokens, NB = 1).
 template <int DK, int NB, bool EJK, typename Tin, typename Tout, bool CK = false>
 __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const float* __restrict__ dt_bias, const float* __restrict__ init, const int32_t* __restrict__ cu,
     int T, int H, int HKV, int DV, float scale, float lower_bound, int l2norm,
     Tout* __restrict__ o, float* __restrict__ final_state, const int32_t* __restrict__ ck_off = nullptr,
-    float* __restrict__ ck_states = nullptr)
+    float* __restrict__ ck_states = nullptr, float* __restrict__ ck_yu = nullptr)
 {
     using LT = F32Lds<DK, NB>;
     constexpr int RS = LT::RS;
@@ -607,9 +609,16 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
           }
         }
         lds_barrier();
+        if constexpr (CK) {
+            if (c < nch && c < ck_off[n + 1] - ck_off[n]) {
+                float* dst = ck_yu + ((size_t)(ck_off[n] + c) * H + h) * 2 * FB * DV + j0;
+                dst[(size_t)r16 * DV + c16] = L.YT[c16 * LT::SU + r16];
+                dst[(size_t)(FB + r16) * DV + c16] = L.UT[c16 * LT::SU + r16];
+            }
+        }
 
         // ---- O = Qg S0 + P U (wave 2), S = Diag(2^{b_C}) S0 + Kc^T U (16-row tiles over the waves)
-        if (wave == 2) {
+        if (!CK && wave == 2) {
             // tokens k0 + 4 lk + j at step j: P rows and the transposed U, 16 bytes per lane
 #pragma unroll
             for (int k0 = 0; k0 < FC; k0 += 16) {
@@ -730,7 +739,8 @@ hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream)
 }
 
 template <int DK, typename Tin>
-hipError_t launch_states_typed(const PrefillArgs& a, const int32_t* off, float* ck, hipStream_t stream)
+hipError_t launch_states_typed(const PrefillArgs& a, const int32_t* off, float* ck, float* ck_yu,
+                               hipStream_t stream)
 {
     const dim3 grid((unsigned)(a.dv / FJ), (unsigned)a.H, (unsigned)a.N);
     const Tin* q = static_cast<const Tin*>(a.q);
@@ -739,11 +749,11 @@ hipError_t launch_states_typed(const PrefillArgs& a, const int32_t* off, float* 
     if (a.ejk)
         hipLaunchKernelGGL((chunk_f32_kernel<DK, 1, true, Tin, float, true>), grid, dim3(FT), 0, stream, q, k, v,
                            a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
-                           a.lower_bound, (int)a.l2norm, nullptr, nullptr, off, ck);
+                           a.lower_bound, (int)a.l2norm, nullptr, nullptr, off, ck, ck_yu);
     else
         hipLaunchKernelGGL((chunk_f32_kernel<DK, 1, false, Tin, float, true>), grid, dim3(FT), 0, stream, q, k, v,
                            a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
-                           a.lower_bound, (int)a.l2norm, nullptr, nullptr, off, ck);
+                           a.lower_bound, (int)a.l2norm, nullptr, nullptr, off, ck, ck_yu);
     return hipGetLastError();
 }
 
@@ -758,17 +768,18 @@ bool chunk_states_f32_supported(const PrefillArgs& a)
            (a.ejk || (a.g != nullptr && a.a_log != nullptr && a.lower_bound >= -5.0f));
 }
 
-hipError_t launch_chunk_states_f32(const PrefillArgs& a, const int32_t* off, float* ck, hipStream_t stream)
+hipError_t launch_chunk_states_f32(const PrefillArgs& a, const int32_t* off, float* ck, float* ck_yu,
+                                  hipStream_t stream)
 {
     switch (a.dk * 2 + (a.in_bf16 ? 1 : 0)) {
-    case 32: return launch_states_typed<16, float>(a, off, ck, stream);
-    case 33: return launch_states_typed<16, bf16_t>(a, off, ck, stream);
-    case 64: return launch_states_typed<32, float>(a, off, ck, stream);
-    case 65: return launch_states_typed<32, bf16_t>(a, off, ck, stream);
-    case 128: return launch_states_typed<64, float>(a, off, ck, stream);
-    case 129: return launch_states_typed<64, bf16_t>(a, off, ck, stream);
-    case 256: return launch_states_typed<128, float>(a, off, ck, stream);
-    default: return launch_states_typed<128, bf16_t>(a, off, ck, stream);
+    case 32: return launch_states_typed<16, float>(a, off, ck, ck_yu, stream);
+    case 33: return launch_states_typed<16, bf16_t>(a, off, ck, ck_yu, stream);
+    case 64: return launch_states_typed<32, float>(a, off, ck, ck_yu, stream);
+    case 65: return launch_states_typed<32, bf16_t>(a, off, ck, ck_yu, stream);
+    case 128: return launch_states_typed<64, float>(a, off, ck, ck_yu, stream);
+    case 129: return launch_states_typed<64, bf16_t>(a, off, ck, ck_yu, stream);
+    case 256: return launch_states_typed<128, float>(a, off, ck, ck_yu, stream);
+    default: return launch_states_typed<128, bf16_t>(a, off, ck, ck_yu, stream);
     }
 }
 
