@@ -29,18 +29,20 @@
 // that another of its waves wrote, so prefetched loads and stores stay in
 // flight across them.
 //
-// Three passes:
-//   1. the forward state carry over the chunks, storing the state entering
-//      every chunk: the forward's float32 chunked kernel in 16-token chunks
-//      where it takes the inputs (16-byte aligned rows), else bwd_fwd_scan,
-//      per (sequence, head, 16 state columns);
+// Four kernels (and two small ones):
+//   0. bwd_prep: per (chunk, head), every chunk in parallel: the chunk's
+//      column-independent operands (normalised, decayed rows Qg, Kg, Kc, the
+//      Gram products, the decay factors), formed once for both scans;
+//   1. bwd_fwd_scan: per (sequence, head, 16 state columns), the state carried
+//      forward over the chunks, storing the state entering every chunk and the
+//      chunk's Y and U;
 //   2. bwd_rev_scan: per (sequence, head, 16 columns), the state gradient
 //      carried backward over the chunks, storing dL/d(state leaving the
-//      chunk) for every chunk (and dL/d(initial state) at the end).  Both
-//      recurrences are independent per state column, so column tiles run in
-//      parallel;
+//      chunk) and Z for every chunk (and dL/d(initial state) at the end).
+//      Both recurrences are independent per state column, so column tiles
+//      run in parallel;
 //   3. bwd_local: per (chunk, head), all columns, every chunk in parallel:
-//      the chunk's own gradients from its two stored states.
+//      the chunk's own gradients from its two stored states and Y, U, Z.
 // A last small kernel sums the parameter gradients over chunks (and the key
 // and value gradients over the heads of a group when heads are grouped).
 //
@@ -92,6 +94,7 @@ struct BwdParams {
     float* ckdS;          // [slots, H, dk, dv]  dL/d(state leaving each chunk)
     float* ckYU;          // [slots, H, 2, 16, dv]  Y = V - Kg S0 and U of each chunk
     float* ckZ;           // [slots, H, 16, dv]  Z of each chunk ((I + A)^T Z = dU)
+    float* prep;          // [slots, H, PrepLayout<dk>::SIZE]  column-independent chunk operands
     float* part_a;        // [slots, H]          a_log gradient per chunk
     float* part_dt;       // [slots, H, dk]      dt_bias gradient per chunk
 };
@@ -343,112 +346,15 @@ __device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, in
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: forward state carry per (column tile, head, sequence); stores the
-// state entering every chunk and the chunk's Y and U.
-template <int DK, bool EJK>
-__global__ __launch_bounds__(BT) void bwd_fwd_scan(BwdParams p)
-{
-    __shared__ ChunkLds<DK, EJK> L;
-    __shared__ float S[DK][TV];
-    __shared__ float Y[BC][TV + 1];
-    __shared__ float U[BC][TV + 1];
-    const int tid = threadIdx.x;
-    const int j0 = blockIdx.x * TV, h = blockIdx.y, n = blockIdx.z;
-    const int H = p.H, dv = p.dv;
-    const int hk = h / (H / p.Hkv);
-    int t0, t1;
-    seq_bounds(p.cu, n, p.T, t0, t1);
-    for (int e = tid; e < DK * TV; e += BT) {
-        const int i = e / TV, j = e % TV;
-        S[i][j] = p.init ? p.init[(((size_t)n * H + h) * DK + i) * dv + j0 + j] : 0.f;
-    }
-    const int nck = seq_chunks(p.off, n, t0, t1);
-    const int slot0 = p.off[n];
-    for (int c = 0; c < nck; ++c) {
-        lds_barrier();
-        float* dst = p.ckS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0;
-        for (int e = tid; e < DK * TV; e += BT) {
-            const int i = e / TV, j = e % TV;
-            dst[(size_t)i * dv + j] = S[i][j];
-        }
-        const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
-        chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
-        {
-            const int r = tid / TV, j = tid % TV;
-            float acc = 0.f;
-            for (int i = 0; i < DK; ++i) acc = fmaf(L.kg(r, i), S[i][j], acc);
-            const float vv = r < nr ? ldx(p.v, ((size_t)(c0 + r) * p.Hkv + hk) * dv + j0 + j, p.in_bf16) : 0.f;
-            Y[r][j] = vv - acc;
-        }
-        lds_barrier();
-        if (tid < TV) {
-            const int j = tid;
-            float u[BC];
-#pragma unroll
-            for (int r = 0; r < BC; ++r) {
-                float x = Y[r][j];
-#pragma unroll
-                for (int s = 0; s < r; ++s) x = fmaf(-L.GA[r][s], u[s], x);
-                u[r] = L.beta[r] * x;
-                U[r][j] = u[r];
-            }
-        }
-        lds_barrier();
-        {
-            const int r = tid / TV, j = tid % TV;
-            float* yu = p.ckYU + ((size_t)(slot0 + c) * H + h) * 2 * BC * dv + j0;
-            yu[(size_t)r * dv + j] = Y[r][j];
-            yu[(size_t)(BC + r) * dv + j] = U[r][j];
-        }
-        for (int e = tid; e < DK * TV; e += BT) {
-            const int i = e / TV, j = e % TV;
-            float acc = L.ecc(i) * S[i][j];
-            for (int r = 0; r < BC; ++r) acc = fmaf(L.kc(r, i), U[r][j], acc);
-            S[i][j] = acc;
-        }
-    }
-}
-
-// Pass 2: the state gradient carried backward per (16 state columns, head,
-// sequence); stores dL/d(state leaving) and Z of every chunk, and at the end
-// dL/d(initial state).  The dk x 16 gradient tile stays in the accumulator
-// registers of 16x16x4 float32 MFMA, 16 rows per tile (tiles dealt over the
-// waves); the element e of a lane (lm, lk) holds row 4 lk + e, column lm,
-// which is also what that lane supplies as the B operand at step e of a
-// product over those rows.  Per chunk, last to first:
-//     dU = Kc dS + GP^T dO            (a partial per wave, summed in LDS)
-//     (I + A)^T Z = dU, dY = diag(beta) Z   (back substitution, a lane per column)
-//     dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
-// with Qg, Kg, Kc formed once per chunk in LDS (EJK: qh, kh, the scalar row
-// factors applied to dO, dY and dU rows).  The inputs of the chunk before are
-// loaded into registers while the current one computes.
-template <int DK, bool EJK>
-struct RevLds {
-    static constexpr int RS = DK + 4;   // 16-byte rows; 16 rows in distinct bank groups
-    static constexpr int XS = EJK ? 4 : BC * RS;
-    alignas(16) float QG[BC * RS];   // raw q, then Qg (EJK: qh)
-    alignas(16) float KG[BC * RS];   // raw k, then Kg (EJK: kh)
-    alignas(16) float KC[XS];        // KDA: Kc
-    alignas(16) float KI[XS];        // KDA: kh e^{-b}
-    alignas(16) float GT[XS];        // KDA: gate activations (log2 units)
-    float DO[BC][TV + 1];
-    float DY[BC][TV + 1];            // dY (EJK: e^{b'} dY)
-    float PU[BT / kWave][BC][TV + 1];
-    float CA[BC][BC + 1];            // beta_r GA_rs (s < r), else 0
-    float EC[DK];                    // KDA: e^{b_C}
-    float NQ[BC], NK[BC], BE[BC];    // query / key row scales, beta
-    float SB[BC], SBC[BC], SBP[BC];  // EJK: gates (log2), b, b'
-    float SEB[BC], SEBP[BC], SECB[BC], SEC;   // EJK: e^{b}, e^{b'}, e^{b_C - b}, e^{b_C}
-};
-
-template <int DK, bool EJK, typename Tin>
-struct RevInputs {
-    static constexpr int NE = BC * DK / BT;
-    Tin q[NE], k[NE];
-    float g[EJK ? 1 : NE];
-    float d, b, gs;
-};
-
+// The column-independent operands of one chunk, formed once per (chunk, head)
+// by bwd_prep for the two state scans (each of which runs per 16 state
+// columns).  In global memory, floats, rows of RS = dk + 4 (the scans copy the
+// block to LDS as it is, and rows 16 bytes apart by a multiple of 4 banks
+// keep their 16-byte reads conflict-free):
+//     QG [16][RS]  Qg (EJK: qh)          KG [16][RS]  Kg (EJK: kh)
+//     KC [16][RS]  Kc (KDA)              CA [16][16]  A_rs = beta_r GA_rs (s < r)
+//     GP [16][16]  P (s <= r)            EC [dk]      e^{b_C} (KDA)
+//     BE [16]      beta                  RF [4][16]   EJK: e^{b}, e^{b'}, e^{b_C - b}, e^{b_C}
 template <typename Tin>
 __device__ __forceinline__ float widen(Tin x)
 {
@@ -456,55 +362,265 @@ __device__ __forceinline__ float widen(Tin x)
     else return __uint_as_float((uint32_t)x << 16);
 }
 
-template <int DK, bool EJK, typename Tin>
-__device__ __forceinline__ void rev_load(RevInputs<DK, EJK, Tin>& in, const BwdParams& p, int c0, int nr, int h,
-                                         int hk, int j0)
+template <int DK>
+struct PrepLayout {
+    static constexpr int RS = DK + 4;
+    static constexpr int QG = 0, KG = BC * RS, KC = 2 * BC * RS, CA = 3 * BC * RS, GP = CA + BC * BC;
+    static constexpr int EC = GP + BC * BC, BE = EC + DK, RF = BE + BC;
+    static constexpr int SIZE = (RF + 4 * BC + 63) / 64 * 64;
+};
+
+// The sequence, first row and row count of chunk slot `slot`.
+__device__ __forceinline__ void slot_rows(const BwdParams& p, int slot, int& n, int& c0, int& nr)
 {
+    int lo = 0, hi = p.N - 1;   // the last n with off[n] <= slot
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.off[mid] <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    n = lo;
+    int t0, t1;
+    seq_bounds(p.cu, n, p.T, t0, t1);
+    c0 = t0 + (slot - p.off[n]) * BC;
+    nr = min(BC, t1 - c0);
+}
+
+template <int DK, bool EJK>
+__global__ __launch_bounds__(BT) void bwd_prep(BwdParams p)
+{
+    using PL = PrepLayout<DK>;
+    __shared__ ChunkLds<DK, EJK> L;
     const int tid = threadIdx.x;
-    const Tin* qq = static_cast<const Tin*>(p.q);
-    const Tin* kk = static_cast<const Tin*>(p.k);
-#pragma unroll
-    for (int m = 0; m < in.NE; ++m) {
-        const int e = tid + m * BT;
+    const int slot = blockIdx.x, h = blockIdx.y;
+    const int hk = h / (p.H / p.Hkv);
+    if (slot >= p.off[p.N]) return;
+    int n, c0, nr;
+    slot_rows(p, slot, n, c0, nr);
+    chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
+    float* o = p.prep + ((size_t)slot * p.H + h) * PL::SIZE;
+    for (int e = tid; e < BC * DK; e += BT) {
         const int r = e / DK, i = e % DK;
-        const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
-        in.q[m] = qq[(tok * p.H + h) * DK + i];
-        in.k[m] = kk[(tok * p.Hkv + hk) * DK + i];
-        if (!EJK) in.g[m] = p.g[(tok * p.H + h) * DK + i];
+        const float qh = L.qh[r][i], kh = L.kh[r][i];
+        o[PL::QG + r * PL::RS + i] = EJK ? qh : qh * L.eb[r][i];
+        o[PL::KG + r * PL::RS + i] = EJK ? kh : kh * L.eb[r][i];
+        if (!EJK) o[PL::KC + r * PL::RS + i] = kh * L.ecb[r][i];
     }
     {
-        const int r = tid / TV, j = tid % TV;
-        const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
-        in.d = ldx(p.d_o, (tok * p.H + h) * p.dv + j0 + j, p.do_bf16);
+        const int r = tid >> 4, s = tid & 15;
+        o[PL::CA + tid] = s < r ? L.beta[r] * L.GA[r][s] : 0.f;
+        o[PL::GP + tid] = L.GP[r][s];
     }
+    if (!EJK && tid < DK) o[PL::EC + tid] = L.ec[tid];
     if (tid < BC) {
-        const size_t tok = (size_t)(c0 + (tid < nr ? tid : 0));
-        in.b = p.beta[tok * p.H + h];
-        in.gs = (EJK && p.g) ? p.g[tok * p.H + h] : 0.f;
+        o[PL::BE + tid] = L.beta[tid];
+        if (EJK) {
+            o[PL::RF + tid] = L.seb[tid];
+            o[PL::RF + BC + tid] = L.sebp[tid];
+            o[PL::RF + 2 * BC + tid] = L.secb[tid];
+            o[PL::RF + 3 * BC + tid] = L.sec;
+        }
     }
 }
 
-// Two workgroups per CU (512 registers per lane shared by two waves per SIMD):
-// the (sequence, head, column tile) grid is then resident in one round at
-// the usual sizes.
-template <int DK, bool EJK, typename Tin>
-__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rev_scan(BwdParams p)
+// The (16 state columns, head, sequence) unit of a scan workgroup.  Linear
+// workgroup ids are dealt to the 8 XCDs in turn, so the column tiles of one
+// (head, sequence), which read the same chunk operands, are given ids that
+// are equal modulo 8: they run on one XCD and share its L2.  Returns false
+// for the padding ids past the last (head, sequence).
+__device__ __forceinline__ bool scan_unit(const BwdParams& p, int& j0, int& h, int& n)
 {
-    using LT = RevLds<DK, EJK>;
-    constexpr int RS = LT::RS;
-    constexpr int NT = DK / 16;              // 16-row tiles of the gradient
-    constexpr int NW = BT / kWave;
-    constexpr int TPW = (NT + NW - 1) / NW;  // tiles per wave
-    __shared__ LT L;
+    const int ntile = p.dv / TV;
+    const int id = blockIdx.x;
+    const int xcd = id & 7, q = id >> 3;
+    const int grp = (q / ntile) * 8 + xcd;
+    if (grp >= p.H * p.N) return false;
+    j0 = (q % ntile) * TV;
+    h = grp % p.H;
+    n = grp / p.H;
+    return true;
+}
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// The chunk's operand block, 16 bytes per thread and step, into registers.
+template <int NP, int N4>
+__device__ __forceinline__ void fetch_block(f4v (&pf)[NP], const float* src)
+{
+    const f4v* s4 = reinterpret_cast<const f4v*>(src);
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+        const int idx = threadIdx.x + m * BT;
+        pf[m] = idx < N4 ? s4[idx] : f4v{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+template <int NP, int N4>
+__device__ __forceinline__ void store_block(float* dst, const f4v (&pf)[NP])
+{
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+        const int idx = threadIdx.x + m * BT;
+        if (idx < N4) reinterpret_cast<f4v*>(dst)[idx] = pf[m];
+    }
+}
+
+// The scans' register layout: the dk x 16 state (or state gradient) tile is
+// held in the accumulators of 16x16x4 float32 MFMA, 16 rows per tile (tiles
+// dealt over the waves); element e of lane (lm, lk) holds row 4 lk + e,
+// column lm, which is also what that lane supplies as the B operand at step
+// e of a product over those rows.  Per chunk the scan copies the chunk's
+// operand block (prefetched into registers while the chunk before computed)
+// to LDS; four barriers, waiting for LDS only.
+template <int DK>
+struct ScanLds {
+    alignas(16) float P[PrepLayout<DK>::SIZE];
+    float X[BC][TV + 1];             // V (pass 1) or dO (pass 2) of the tile
+    float W[BC][TV + 1];             // U (pass 1, EJK: e^{b_C - b} U) or dY (pass 2, EJK: e^{b'} dY)
+    float PU[BT / kWave][BC][TV + 1];
+};
+
+// Pass 1: the forward state carry per (16 state columns, head, sequence);
+// stores the state entering every chunk and the chunk's Y and U:
+//     Y = V - Kg S,  (I + A) U = diag(beta) Y  (forward substitution, a lane per column)
+//     S <- Diag(e^{b_C}) S + Kc^T U
+template <int DK, bool EJK, typename Tin>
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_fwd_scan(BwdParams p)
+{
+    using PL = PrepLayout<DK>;
+    constexpr int RS = PL::RS;
+    constexpr int NT = DK / 16, NW = BT / kWave, TPW = (NT + NW - 1) / NW;
+    constexpr int N4 = PL::SIZE / 4, NP = (N4 + BT - 1) / BT;
+    __shared__ ScanLds<DK> L;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lm = lane & 15, lk = lane >> 4;
-    const int j0 = blockIdx.x * TV, h = blockIdx.y, n = blockIdx.z;
+    int j0, h, n;
+    if (!scan_unit(p, j0, h, n)) return;
     const int H = p.H, dv = p.dv;
     const int hk = h / (H / p.Hkv);
-    const float ea = EJK ? 0.f : expf(p.a_log[h]);
-    const float lb2 = p.lb * kLog2e;
-    const float dtb = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
+    int t0, t1;
+    seq_bounds(p.cu, n, p.T, t0, t1);
+    bf32x4_t S[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int t = wave + NW * x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * t + 4 * lk + e;
+            S[x][e] = (t < NT && p.init) ? p.init[(((size_t)n * H + h) * DK + i) * dv + j0 + lm] : 0.f;
+        }
+    }
+    const int nck = seq_chunks(p.off, n, t0, t1);
+    const int slot0 = p.off[n];
+    const Tin* vv = static_cast<const Tin*>(p.v);
+    f4v pf[NP];
+    Tin pv = 0;
+    const int rr = tid / TV, jj = tid % TV;
+    if (nck > 0) {
+        fetch_block<NP, N4>(pf, p.prep + ((size_t)slot0 * H + h) * PL::SIZE);
+        pv = vv[((size_t)(t0 + (t0 + rr < t1 ? rr : 0)) * p.Hkv + hk) * dv + j0 + jj];
+    }
+    for (int c = 0; c < nck; ++c) {
+        const int c0 = t0 + c * BC;
+        {
+            float* dst = p.ckS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0 + lm;
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * t + 4 * lk + e) * dv] = S[x][e];
+                }
+            }
+        }
+        lds_barrier();
+        store_block<NP, N4>(L.P, pf);
+        L.X[rr][jj] = c0 + rr < t1 ? widen(pv) : 0.f;
+        if (c + 1 < nck) {
+            const int cn = c0 + BC;
+            fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c + 1) * H + h) * PL::SIZE);
+            pv = vv[((size_t)(cn + (cn + rr < t1 ? rr : 0)) * p.Hkv + hk) * dv + j0 + jj];
+        }
+        lds_barrier();
+        // Kg S: each wave its tiles' part (A = Kg rows, 16 bytes per lane)
+        {
+            bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+                    const float4 a = *reinterpret_cast<const float4*>(L.P + PL::KG + lm * RS + 16 * t + 4 * lk);
+                    acc = bmfma4(a.x, S[x][0], acc);
+                    acc = bmfma4(a.y, S[x][1], acc);
+                    acc = bmfma4(a.z, S[x][2], acc);
+                    acc = bmfma4(a.w, S[x][3], acc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
+        }
+        lds_barrier();
+        // Y and U, a lane per column
+        if (tid < TV) {
+            const int j = tid;
+            float* yu = p.ckYU + ((size_t)(slot0 + c) * H + h) * 2 * BC * dv + j0 + j;
+            float u[BC];
+#pragma unroll
+            for (int r = 0; r < BC; ++r) {
+                float ks = (L.PU[0][r][j] + L.PU[1][r][j]) + (L.PU[2][r][j] + L.PU[3][r][j]);
+                if (EJK) ks *= L.P[PL::RF + BC + r];
+                const float y = L.X[r][j] - ks;
+                yu[(size_t)r * dv] = y;
+                float x = L.P[PL::BE + r] * y;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) x = fmaf(-L.P[PL::CA + r * BC + s2], u[s2], x);
+                u[r] = x;
+                yu[(size_t)(BC + r) * dv] = x;
+                L.W[r][j] = EJK ? x * L.P[PL::RF + 2 * BC + r] : x;
+            }
+        }
+        lds_barrier();
+        // S <- Diag(e^{b_C}) S + Kc^T U (EJK: kh^T (e^{b_C - b} U))
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            if (t < NT) {
+                bf32x4_t a = S[x];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] *= EJK ? L.P[PL::RF + 3 * BC] : L.P[PL::EC + 16 * t + 4 * lk + e];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * lk + u;
+                    a = bmfma4(L.P[(EJK ? PL::KG : PL::KC) + r * RS + 16 * t + lm], L.W[r][lm], a);
+                }
+                S[x] = a;
+            }
+        }
+    }
+}
+
+// Pass 2: the state gradient carried backward per (16 state columns, head,
+// sequence); stores dL/d(state leaving) and Z of every chunk, and at the end
+// dL/d(initial state).  Per chunk, last to first:
+//     dU = Kc dS + P^T dO            (a partial per wave, summed in LDS)
+//     (I + A)^T Z = dU, dY = diag(beta) Z   (back substitution, a lane per column)
+//     dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
+// (EJK: qh, kh with the scalar row factors applied to dO, dY and dU rows).
+template <int DK, bool EJK, typename Tin>
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rev_scan(BwdParams p)
+{
+    using PL = PrepLayout<DK>;
+    constexpr int RS = PL::RS;
+    constexpr int NT = DK / 16, NW = BT / kWave, TPW = (NT + NW - 1) / NW;
+    constexpr int N4 = PL::SIZE / 4, NP = (N4 + BT - 1) / BT;
+    __shared__ ScanLds<DK> L;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lm = lane & 15, lk = lane >> 4;
+    int j0, h, n;
+    if (!scan_unit(p, j0, h, n)) return;
+    const int H = p.H, dv = p.dv;
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
     bf32x4_t dS[TPW];
@@ -519,13 +635,16 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     }
     const int nck = seq_chunks(p.off, n, t0, t1);
     const int slot0 = p.off[n];
-    RevInputs<DK, EJK, Tin> in;
+    f4v pf[NP];
+    float pd = 0.f;
+    const int rr = tid / TV, jj = tid % TV;
     if (nck > 0) {
-        const int c0 = t0 + (nck - 1) * BC;
-        rev_load(in, p, c0, min(BC, t1 - c0), h, hk, j0);
+        const int cl = t0 + (nck - 1) * BC;
+        fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + nck - 1) * H + h) * PL::SIZE);
+        pd = ldx(p.d_o, ((size_t)(cl + (cl + rr < t1 ? rr : 0)) * H + h) * dv + j0 + jj, p.do_bf16);
     }
     for (int c = nck - 1; c >= 0; --c) {
-        const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
+        const int c0 = t0 + c * BC;
         {
             float* dst = p.ckdS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0 + lm;
 #pragma unroll
@@ -538,110 +657,23 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             }
         }
         lds_barrier();
-        // 1. this chunk's inputs to LDS (rows past nr neutral); the chunk
-        // before is loaded meanwhile
-#pragma unroll
-        for (int m = 0; m < in.NE; ++m) {
-            const int e = tid + m * BT;
-            const int r = e / DK, i = e % DK;
-            const bool ok = r < nr;
-            L.QG[r * RS + i] = ok ? widen(in.q[m]) : 0.f;
-            L.KG[r * RS + i] = ok ? widen(in.k[m]) : 0.f;
-            if (!EJK) L.GT[r * RS + i] = ok ? lb2 * sigmoid_f(ea * (in.g[m] + dtb)) : 0.f;
-        }
-        L.DO[tid / TV][tid % TV] = tid / TV < nr ? in.d : 0.f;
-        if (tid < BC) {
-            const bool ok = tid < nr;
-            L.BE[tid] = ok ? (EJK ? in.b : sigmoid_f(in.b)) : 0.f;
-            if (EJK) L.SB[tid] = ok ? in.gs * kLog2e : 0.f;
-        }
+        store_block<NP, N4>(L.P, pf);
+        L.X[rr][jj] = c0 + rr < t1 ? pd : 0.f;
         if (c > 0) {
-            const int cp = c0 - BC;
-            rev_load(in, p, cp, BC, h, hk, j0);
+            const int cp = c0 - BC;   // a whole chunk
+            fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c - 1) * H + h) * PL::SIZE);
+            pd = ldx(p.d_o, ((size_t)(cp + rr) * H + h) * dv + j0 + jj, p.do_bf16);
         }
         lds_barrier();
-        // 2. row scales (eight lanes per row, summed by DPP / swizzle); EJK:
-        // the scalar cumulative decays, each of 16 lanes summing in row order
+        // dU: each wave its tiles' part of Kc dS; wave 1 adds P^T dO
         {
-            const int pr = tid >> 3, part = tid & 7;
-            const int r = pr & 15;
-            const float* row = (pr < 16 ? L.QG : L.KG) + r * RS;
-            float ss = 0.f;
-#pragma unroll
-            for (int i = part; i < DK; i += 8) ss = fmaf(row[i], row[i], ss);
-            ss = xor_add<1>(ss);
-            ss = xor_add<2>(ss);
-            ss = xor_add<4>(ss);
-            if (part == 0) {
-                const float rn = p.l2norm ? 1.f / sqrtf(ss + kNormEps) : 1.f;
-                if (pr < 16) L.NQ[r] = p.scale * rn;
-                else L.NK[r] = rn;
-            }
-        }
-        if (EJK && tid >= BT - BC) {
-            const int r = tid - (BT - BC);
-            float acc = 0.f, b = 0.f, bp = 0.f;
-#pragma unroll
-            for (int s = 0; s < BC; ++s) {
-                if (s == r) bp = acc;
-                acc += L.SB[s];
-                if (s == r) b = acc;
-            }
-            L.SBC[r] = b;
-            L.SBP[r] = bp;
-            L.SEB[r] = __builtin_amdgcn_exp2f(b);
-            L.SEBP[r] = __builtin_amdgcn_exp2f(bp);
-            L.SECB[r] = __builtin_amdgcn_exp2f(acc - b);
-            if (r == 0) L.SEC = __builtin_amdgcn_exp2f(acc);
-        }
-        lds_barrier();
-        // 3. normalised and decayed rows: KDA a thread per (channel, rows of
-        // its part), the channel's prefix sums in registers
-        if constexpr (!EJK) {
-            constexpr int NP = BT / DK, RP = BC / NP;
-            const int i = tid % DK, part = tid / DK;
-            float bo[RP];
-            float b = 0.f;
-#pragma unroll
-            for (int s = 0; s < BC; ++s) {
-                b += L.GT[s * RS + i];
-#pragma unroll
-                for (int x = 0; x < RP; ++x)
-                    if (s == part * RP + x) bo[x] = b;
-            }
-            if (part == 0) L.EC[i] = __builtin_amdgcn_exp2f(b);
-#pragma unroll
-            for (int x = 0; x < RP; ++x) {
-                const int r = part * RP + x;
-                const float qn = L.QG[r * RS + i] * L.NQ[r];
-                const float kn = L.KG[r * RS + i] * L.NK[r];
-                const float f = __builtin_amdgcn_exp2f(bo[x]);
-                L.QG[r * RS + i] = qn * f;
-                L.KG[r * RS + i] = kn * f;
-                L.KI[r * RS + i] = kn * __builtin_amdgcn_exp2f(-bo[x]);
-                L.KC[r * RS + i] = kn * __builtin_amdgcn_exp2f(b - bo[x]);
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < in.NE; ++m) {
-                const int e = tid + m * BT;
-                const int r = e / DK, i = e % DK;
-                L.QG[r * RS + i] *= L.NQ[r];
-                L.KG[r * RS + i] *= L.NK[r];
-            }
-        }
-        lds_barrier();
-        // 4. MFMA: each wave its tiles' part of Kc dS; wave 0 the Gram A, wave
-        // 1 the Gram P and P^T dO (its P accumulator is that product's A operand)
-        {
-            const float* KCsrc = EJK ? L.KG : L.KC;
-            const float* KIsrc = EJK ? L.KG : L.KI;
             bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int x = 0; x < TPW; ++x) {
                 const int t = wave + NW * x;
                 if (t < NT) {
-                    const float4 a = *reinterpret_cast<const float4*>(KCsrc + lm * RS + 16 * t + 4 * lk);
+                    const float4 a = *reinterpret_cast<const float4*>(L.P + (EJK ? PL::KG : PL::KC) + lm * RS +
+                                                                      16 * t + 4 * lk);
                     acc = bmfma4(a.x, dS[x][0], acc);
                     acc = bmfma4(a.y, dS[x][1], acc);
                     acc = bmfma4(a.z, dS[x][2], acc);
@@ -650,48 +682,21 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             }
             if (EJK) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] *= L.SECB[4 * lk + e];
+                for (int e = 0; e < 4; ++e) acc[e] *= L.P[PL::RF + 2 * BC + 4 * lk + e];
             }
-            if (wave < 2) {
-                const float* X = wave == 0 ? L.KG : L.QG;
-                bf32x4_t gm = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (wave == 1) {
+                // (P^T dO)[m][j] = sum_s P[s][m] dO[s][j], s = 4 lk + u at step u
 #pragma unroll
-                for (int k0 = 0; k0 < DK; k0 += 16) {
-                    const float4 a = *reinterpret_cast<const float4*>(X + lm * RS + k0 + 4 * lk);
-                    const float4 b = *reinterpret_cast<const float4*>(KIsrc + lm * RS + k0 + 4 * lk);
-                    gm = bmfma4(a.x, b.x, gm);
-                    gm = bmfma4(a.y, b.y, gm);
-                    gm = bmfma4(a.z, b.z, gm);
-                    gm = bmfma4(a.w, b.w, gm);
-                }
-                // gm[e] = Gram[r][s], r = 4 lk + e, s = lm
-                if (wave == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * lk + e, s = lm;
-                        float x = gm[e];
-                        if (EJK) x *= s < r ? __builtin_amdgcn_exp2f(L.SBP[r] - L.SBC[s]) : 0.f;
-                        L.CA[r][s] = s < r ? L.BE[r] * x : 0.f;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * lk + e, s = lm;
-                        float x = gm[e];
-                        if (EJK) x *= s <= r ? __builtin_amdgcn_exp2f(L.SBC[r] - L.SBC[s]) : 0.f;
-                        gm[e] = s <= r ? x : 0.f;
-                    }
-                    // (P^T dO)[m][j] = sum_s P[s][m] dO[s][j]: at step e the lane
-                    // supplies P[4 lk + e][lm], its own gm[e]
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc = bmfma4(gm[e], L.DO[4 * lk + e][lm], acc);
+                for (int u = 0; u < 4; ++u) {
+                    const int s2 = 4 * lk + u;
+                    acc = bmfma4(L.P[PL::GP + s2 * BC + lm], L.X[s2][lm], acc);
                 }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
         }
         lds_barrier();
-        // 5. (I + A)^T Z = dU by back substitution, a lane per column
+        // (I + A)^T Z = dU by back substitution, a lane per column
         if (tid < TV) {
             const int j = tid;
             float* zd = p.ckZ + ((size_t)(slot0 + c) * H + h) * BC * dv + j0 + j;
@@ -699,34 +704,34 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
             for (int r = 0; r < BC; ++r) z[r] = (L.PU[0][r][j] + L.PU[1][r][j]) + (L.PU[2][r][j] + L.PU[3][r][j]);
 #pragma unroll
-            for (int s = BC - 1; s >= 0; --s) {
-                const float zs = z[s];
-                zd[(size_t)s * dv] = zs;
-                const float dy = L.BE[s] * zs;
-                L.DY[s][j] = EJK ? dy * L.SEBP[s] : dy;
+            for (int s2 = BC - 1; s2 >= 0; --s2) {
+                const float zs = z[s2];
+                zd[(size_t)s2 * dv] = zs;
+                const float dy = L.P[PL::BE + s2] * zs;
+                L.W[s2][j] = EJK ? dy * L.P[PL::RF + BC + s2] : dy;
 #pragma unroll
-                for (int r = 0; r < s; ++r) z[r] = fmaf(-L.CA[s][r], zs, z[r]);
+                for (int r = 0; r < s2; ++r) z[r] = fmaf(-L.P[PL::CA + s2 * BC + r], zs, z[r]);
             }
         }
         lds_barrier();
-        // 6. dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
+        // dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
             const int t = wave + NW * x;
             if (t < NT) {
                 bf32x4_t a = dS[x];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] *= EJK ? L.SEC : L.EC[16 * t + 4 * lk + e];
+                for (int e = 0; e < 4; ++e) a[e] *= EJK ? L.P[PL::RF + 3 * BC] : L.P[PL::EC + 16 * t + 4 * lk + e];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int r = 4 * lk + u;
-                    const float d = EJK ? L.DO[r][lm] * L.SEB[r] : L.DO[r][lm];
-                    a = bmfma4(L.QG[r * RS + 16 * t + lm], d, a);
+                    const float d = EJK ? L.X[r][lm] * L.P[PL::RF + r] : L.X[r][lm];
+                    a = bmfma4(L.P[PL::QG + r * RS + 16 * t + lm], d, a);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int r = 4 * lk + u;
-                    a = bmfma4(-L.KG[r * RS + 16 * t + lm], L.DY[r][lm], a);
+                    a = bmfma4(-L.P[PL::KG + r * RS + 16 * t + lm], L.W[r][lm], a);
                 }
                 dS[x] = a;
             }
@@ -1307,27 +1312,43 @@ size_t bwd_slots(int N, int T, bool packed)
     return (size_t)N * (size_t)((T + BC - 1) / BC);
 }
 
-template <int DK, bool EJK>
-hipError_t launch_dk(const BwdParams& p, size_t slots, bool states_done, hipStream_t st)
+size_t prep_floats(int dk)
 {
-    const dim3 sgrid((unsigned)(p.dv / TV), (unsigned)p.H, (unsigned)p.N);
+    switch (dk) {
+    case 16: return PrepLayout<16>::SIZE;
+    case 32: return PrepLayout<32>::SIZE;
+    case 64: return PrepLayout<64>::SIZE;
+    default: return PrepLayout<128>::SIZE;
+    }
+}
+
+template <int DK, bool EJK>
+hipError_t launch_dk(const BwdParams& p, size_t slots, hipStream_t st)
+{
+    const dim3 lgrid((unsigned)slots, (unsigned)p.H);
     hipError_t e = hipSuccess;
-    if (!states_done) {
-        hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK>), sgrid, dim3(BT), 0, st, p);
+    if (slots > 0) {
+        hipLaunchKernelGGL((bwd_prep<DK, EJK>), lgrid, dim3(BT), 0, st, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // scan ids: (head, sequence) groups padded to a multiple of 8, times the
+    // column tiles; the scans also run for sequences without rows (the reverse
+    // one then passes dL/d(final state) on as dL/d(initial state))
+    const unsigned groups8 = (unsigned)((p.H * p.N + 7) / 8 * 8);
+    if (groups8 == 0) return hipSuccess;
+    const dim3 sgrid(groups8 * (unsigned)(p.dv / TV));
+    if (p.in_bf16) hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, uint16_t>), sgrid, dim3(BT), 0, st, p);
+    else hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, float>), sgrid, dim3(BT), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (p.in_bf16) hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, uint16_t>), sgrid, dim3(BT), 0, st, p);
     else hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, float>), sgrid, dim3(BT), 0, st, p);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (slots > 0) {
-        const dim3 lgrid((unsigned)slots, (unsigned)p.H);
-        if (p.in_bf16) hipLaunchKernelGGL((bwd_local<DK, EJK, uint16_t>), lgrid, dim3(BT), 0, st, p);
-        else hipLaunchKernelGGL((bwd_local<DK, EJK, float>), lgrid, dim3(BT), 0, st, p);
-        e = hipGetLastError();
-    }
-    return e;
+    if (e != hipSuccess || slots == 0) return e;
+    if (p.in_bf16) hipLaunchKernelGGL((bwd_local<DK, EJK, uint16_t>), lgrid, dim3(BT), 0, st, p);
+    else hipLaunchKernelGGL((bwd_local<DK, EJK, float>), lgrid, dim3(BT), 0, st, p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1340,6 +1361,7 @@ size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bo
     size_t b = align256((size_t)(N + 1) * 4);
     b += 2 * align256(slots * H * dk * dv * 4);
     b += align256(slots * H * 2 * BC * dv * 4) + align256(slots * H * BC * dv * 4);
+    b += align256(slots * H * prep_floats(dk) * 4);
     b += align256(slots * H * 4) + align256(slots * H * dk * 4);
     if (Hkv != H) b += align256(ntok * H * dk * 4) + align256(ntok * H * dv * 4);
     return b;
@@ -1370,6 +1392,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     w += align256(slots * a.H * 2 * BC * a.dv * 4);
     p.ckZ = reinterpret_cast<float*>(w);
     w += align256(slots * a.H * BC * a.dv * 4);
+    p.prep = reinterpret_cast<float*>(w);
+    w += align256(slots * a.H * prep_floats(a.dk) * 4);
     p.part_a = reinterpret_cast<float*>(w);
     w += align256(slots * a.H * 4);
     p.part_dt = reinterpret_cast<float*>(w);
@@ -1387,28 +1411,15 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(64), 0, st, a.cu, a.N, a.T, (int)slots, off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // Pass 1 on the forward's float32 chunked kernel (16-token chunks, storing
-    // the state entering each chunk) where it takes the inputs: 16-byte aligned
-    // rows and 31-bit sequence spans; else on bwd_fwd_scan.
-    PrefillArgs pa{};
-    pa.q = a.q; pa.k = a.k; pa.v = a.v; pa.in_bf16 = a.in_bf16 != 0;
-    pa.g = a.g; pa.beta = a.beta; pa.a_log = a.a_log; pa.dt_bias = a.dt_bias; pa.init = a.init; pa.cu = a.cu;
-    pa.N = a.N; pa.T = a.T; pa.H = a.H; pa.dk = a.dk; pa.dv = a.dv; pa.Hkv = a.Hkv;
-    pa.scale = a.scale; pa.lower_bound = a.lower_bound; pa.l2norm = a.l2norm != 0; pa.ejk = a.ejk;
-    const bool states_done = chunk_states_f32_supported(pa);
-    if (states_done) {
-        e = launch_chunk_states_f32(pa, off, p.ckS, p.ckYU, st);
-        if (e != hipSuccess) return e;
-    }
     switch (a.dk * 2 + (a.ejk ? 1 : 0)) {
-    case 32: e = launch_dk<16, false>(p, slots, states_done, st); break;
-    case 33: e = launch_dk<16, true>(p, slots, states_done, st); break;
-    case 64: e = launch_dk<32, false>(p, slots, states_done, st); break;
-    case 65: e = launch_dk<32, true>(p, slots, states_done, st); break;
-    case 128: e = launch_dk<64, false>(p, slots, states_done, st); break;
-    case 129: e = launch_dk<64, true>(p, slots, states_done, st); break;
-    case 256: e = launch_dk<128, false>(p, slots, states_done, st); break;
-    default: e = launch_dk<128, true>(p, slots, states_done, st); break;
+    case 32: e = launch_dk<16, false>(p, slots, st); break;
+    case 33: e = launch_dk<16, true>(p, slots, st); break;
+    case 64: e = launch_dk<32, false>(p, slots, st); break;
+    case 65: e = launch_dk<32, true>(p, slots, st); break;
+    case 128: e = launch_dk<64, false>(p, slots, st); break;
+    case 129: e = launch_dk<64, true>(p, slots, st); break;
+    case 256: e = launch_dk<128, false>(p, slots, st); break;
+    default: e = launch_dk<128, true>(p, slots, st); break;
     }
     if (e != hipSuccess) return e;
     if (!a.ejk && (a.da_log || a.ddt_bias)) {

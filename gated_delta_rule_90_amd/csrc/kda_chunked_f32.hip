@@ -170,19 +170,13 @@ __device__ __forceinline__ float lane_group_sum(float x)
     return x;
 }
 
-// CK: instead of the output, store the state entering every chunk at
-// ck_states[(ck_off[n] + c) * H + h] ([dk][dv] float32), and the chunk's
-// Y = V - Kg S0 and U at ck_yu[(ck_off[n] + c) * H + h] ([2][16][dv] float32,
-// padded rows zero): the forward pass of the prefill's backward (chunks of 16
-// tokens, NB = 1).
-template <int DK, int NB, bool EJK, typename Tin, typename Tout, bool CK = false>
+template <int DK, int NB, bool EJK, typename Tin, typename Tout>
 __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, const float* __restrict__ init, const int32_t* __restrict__ cu,
     int T, int H, int HKV, int DV, float scale, float lower_bound, int l2norm,
-    Tout* __restrict__ o, float* __restrict__ final_state, const int32_t* __restrict__ ck_off = nullptr,
-    float* __restrict__ ck_states = nullptr, float* __restrict__ ck_yu = nullptr)
+    Tout* __restrict__ o, float* __restrict__ final_state)
 {
     using LT = F32Lds<DK, NB>;
     constexpr int RS = LT::RS;
@@ -385,16 +379,6 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         }
         load(R, min(c + FD, nch - 1));   // past the end this reloads the last chunk
         lds_barrier();
-        if constexpr (CK) {
-            // the state entering this chunk (the tile is only rewritten at the chunk's end)
-            if (c < nch && c < ck_off[n + 1] - ck_off[n]) {
-                float* dst = ck_states + ((size_t)(ck_off[n] + c) * H + h) * DK * DV + j0;
-                for (int e = tid; e < DK * FJ; e += FT) {
-                    const int i = e / FJ, j = e % FJ;
-                    dst[(size_t)i * DV + j] = L.ST[j * LT::SRS + i];
-                }
-            }
-        }
 
         // ---- the gate cumsum of every channel down the chunk's rows.  Two-block
         // chunks: NSEG = 4 adjacent lanes per channel each sum 8 rows, and an
@@ -609,16 +593,9 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
           }
         }
         lds_barrier();
-        if constexpr (CK) {
-            if (c < nch && c < ck_off[n + 1] - ck_off[n]) {
-                float* dst = ck_yu + ((size_t)(ck_off[n] + c) * H + h) * 2 * FB * DV + j0;
-                dst[(size_t)r16 * DV + c16] = L.YT[c16 * LT::SU + r16];
-                dst[(size_t)(FB + r16) * DV + c16] = L.UT[c16 * LT::SU + r16];
-            }
-        }
 
         // ---- O = Qg S0 + P U (wave 2), S = Diag(2^{b_C}) S0 + Kc^T U (16-row tiles over the waves)
-        if (!CK && wave == 2) {
+        if (wave == 2) {
             // tokens k0 + 4 lk + j at step j: P rows and the transposed U, 16 bytes per lane
 #pragma unroll
             for (int k0 = 0; k0 < FC; k0 += 16) {
@@ -674,7 +651,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         // O rows r16 and r16 + 16, column c16, through a buffer resource that ends
         // after the chunk's last row: the buffer unit drops the stores of padded
         // rows, so every lane issues the same stores
-        if constexpr (!CK) {
+        {
             Tout* obase = o + ((size_t)c0 * H + h) * DV + j0;
             const int rec = len > 0 ? ((len - 1) * H * DV + FJ) * (int)sizeof(Tout) : 0;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, 0, rec, 0x00020000);
@@ -738,50 +715,7 @@ hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream)
     return launch_typed<DK, bf16_t, float>(a, stream);
 }
 
-template <int DK, typename Tin>
-hipError_t launch_states_typed(const PrefillArgs& a, const int32_t* off, float* ck, float* ck_yu,
-                               hipStream_t stream)
-{
-    const dim3 grid((unsigned)(a.dv / FJ), (unsigned)a.H, (unsigned)a.N);
-    const Tin* q = static_cast<const Tin*>(a.q);
-    const Tin* k = static_cast<const Tin*>(a.k);
-    const Tin* v = static_cast<const Tin*>(a.v);
-    if (a.ejk)
-        hipLaunchKernelGGL((chunk_f32_kernel<DK, 1, true, Tin, float, true>), grid, dim3(FT), 0, stream, q, k, v,
-                           a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
-                           a.lower_bound, (int)a.l2norm, nullptr, nullptr, off, ck, ck_yu);
-    else
-        hipLaunchKernelGGL((chunk_f32_kernel<DK, 1, false, Tin, float, true>), grid, dim3(FT), 0, stream, q, k, v,
-                           a.g, a.beta, a.a_log, a.dt_bias, a.init, a.cu, a.T, a.H, a.Hkv, a.dv, a.scale,
-                           a.lower_bound, (int)a.l2norm, nullptr, nullptr, off, ck, ck_yu);
-    return hipGetLastError();
-}
-
 }  // namespace
-
-bool chunk_states_f32_supported(const PrefillArgs& a)
-{
-    auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    const bool dims = (a.dk == 16 || a.dk == 32 || a.dk == 64 || a.dk == 128) && a.dv % FJ == 0 && a.dv > 0;
-    const bool spans = (long long)a.T * a.H * (a.dk > a.dv ? a.dk : a.dv) * 4 < (1LL << 31);
-    return dims && spans && a16(a.q) && a16(a.k) && (a.ejk || a16(a.g)) &&
-           (a.ejk || (a.g != nullptr && a.a_log != nullptr && a.lower_bound >= -5.0f));
-}
-
-hipError_t launch_chunk_states_f32(const PrefillArgs& a, const int32_t* off, float* ck, float* ck_yu,
-                                  hipStream_t stream)
-{
-    switch (a.dk * 2 + (a.in_bf16 ? 1 : 0)) {
-    case 32: return launch_states_typed<16, float>(a, off, ck, ck_yu, stream);
-    case 33: return launch_states_typed<16, bf16_t>(a, off, ck, ck_yu, stream);
-    case 64: return launch_states_typed<32, float>(a, off, ck, ck_yu, stream);
-    case 65: return launch_states_typed<32, bf16_t>(a, off, ck, ck_yu, stream);
-    case 128: return launch_states_typed<64, float>(a, off, ck, ck_yu, stream);
-    case 129: return launch_states_typed<64, bf16_t>(a, off, ck, ck_yu, stream);
-    case 256: return launch_states_typed<128, float>(a, off, ck, ck_yu, stream);
-    default: return launch_states_typed<128, bf16_t>(a, off, ck, ck_yu, stream);
-    }
-}
 
 bool chunked_f32_supported(const PrefillArgs& a)
 {

@@ -124,13 +124,6 @@ size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
 // the float32 chunked kernel (16-token chunks on the vector ALUs)
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
-// the same kernel with 16-token chunks storing the state entering every chunk
-// at ck[(off[n] + c) * H + h] ([dk][dv]) and the chunk's Y = V - Kg S0 and U
-// at ck_yu[(off[n] + c) * H + h] ([2][16][dv]) instead of the output (the
-// backward's first pass)
-hipError_t launch_chunk_states_f32(const PrefillArgs& a, const int32_t* off, float* ck, float* ck_yu,
-                                  hipStream_t stream);
-bool chunk_states_f32_supported(const PrefillArgs& a);
 // the gated recurrent attention (kda_gated.hip)
 hipError_t launch_gated(const GatedArgs& a, hipStream_t stream);
 // the prefill backward (kda_backward.hip)
