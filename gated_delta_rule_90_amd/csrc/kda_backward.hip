@@ -90,8 +90,10 @@ struct BwdParams {
     float* dbeta;
     float* dS0;
     const int32_t* off;   // [N + 1] chunk offsets
-    float* ckS;           // [slots, H, dk, dv]  state entering each chunk
-    float* ckdS;          // [slots, H, dk, dv]  dL/d(state leaving each chunk)
+    // the checkpoints, per (chunk, head) in 16-column tiles: [dv / 16][dk][16],
+    // so that a scan workgroup's tile is one contiguous 8 KB block (dk 128)
+    float* ckS;           // [slots, H, dv / 16, dk, 16]  state entering each chunk
+    float* ckdS;          // [slots, H, dv / 16, dk, 16]  dL/d(state leaving each chunk)
     float* ckYU;          // [slots, H, 2, 16, dv]  Y = V - Kg S0 and U of each chunk
     float* ckZ;           // [slots, H, 16, dv]  Z of each chunk ((I + A)^T Z = dU)
     float* prep;          // [slots, H, PrepLayout<dk>::SIZE]  column-independent chunk operands
@@ -106,12 +108,6 @@ typedef float bf32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf32x4_t bmfma4(float a, float b, bf32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float ldx(const void* p, size_t i, int bf)
-{
-    if (bf) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
-    return static_cast<const float*>(p)[i];
 }
 
 __device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int T, int& t0, int& t1)
@@ -352,9 +348,11 @@ __device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, in
 // block to LDS as it is, and rows 16 bytes apart by a multiple of 4 banks
 // keep their 16-byte reads conflict-free):
 //     QG [16][RS]  Qg (EJK: qh)          KG [16][RS]  Kg (EJK: kh)
-//     KC [16][RS]  Kc (KDA)              CA [16][16]  A_rs = beta_r GA_rs (s < r)
+//     KC [16][RS]  Kc (KDA)              TI [16][16]  (I + A)^-1, A_rs = beta_r GA_rs (s < r)
 //     GP [16][16]  P (s <= r)            EC [dk]      e^{b_C} (KDA)
 //     BE [16]      beta                  RF [4][16]   EJK: e^{b}, e^{b'}, e^{b_C - b}, e^{b_C}
+// With T = (I + A)^-1 the two triangular systems of a chunk are products:
+// U = T diag(beta) Y, and Z = T^T dU.
 template <typename Tin>
 __device__ __forceinline__ float widen(Tin x)
 {
@@ -365,7 +363,7 @@ __device__ __forceinline__ float widen(Tin x)
 template <int DK>
 struct PrepLayout {
     static constexpr int RS = DK + 4;
-    static constexpr int QG = 0, KG = BC * RS, KC = 2 * BC * RS, CA = 3 * BC * RS, GP = CA + BC * BC;
+    static constexpr int QG = 0, KG = BC * RS, KC = 2 * BC * RS, TI = 3 * BC * RS, GP = TI + BC * BC;
     static constexpr int EC = GP + BC * BC, BE = EC + DK, RF = BE + BC;
     static constexpr int SIZE = (RF + 4 * BC + 63) / 64 * 64;
 };
@@ -406,10 +404,19 @@ __global__ __launch_bounds__(BT) void bwd_prep(BwdParams p)
         o[PL::KG + r * PL::RS + i] = EJK ? kh : kh * L.eb[r][i];
         if (!EJK) o[PL::KC + r * PL::RS + i] = kh * L.ecb[r][i];
     }
-    {
-        const int r = tid >> 4, s = tid & 15;
-        o[PL::CA + tid] = s < r ? L.beta[r] * L.GA[r][s] : 0.f;
-        o[PL::GP + tid] = L.GP[r][s];
+    o[PL::GP + tid] = L.GP[tid >> 4][tid & 15];
+    if (tid < BC) {
+        // column s of (I + A)^-1 by forward substitution
+        const int s = tid;
+        float x[BC];
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            float v = r == s ? 1.f : 0.f;
+#pragma unroll
+            for (int t = 0; t < r; ++t) v = fmaf(-L.beta[r] * L.GA[r][t], x[t], v);
+            x[r] = v;
+            o[PL::TI + r * BC + s] = v;
+        }
     }
     if (!EJK && tid < DK) o[PL::EC + tid] = L.ec[tid];
     if (tid < BC) {
@@ -444,46 +451,70 @@ __device__ __forceinline__ bool scan_unit(const BwdParams& p, int& j0, int& h, i
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 // The chunk's operand block, 16 bytes per thread and step, into registers.
+// Every thread issues the same loads (an index past the block is clamped to
+// its last piece, stored again to the same place), so the count of memory
+// operations in flight is the same on every path and the waits for a load
+// issued chunks earlier stay exact.
 template <int NP, int N4>
 __device__ __forceinline__ void fetch_block(f4v (&pf)[NP], const float* src)
 {
     const f4v* s4 = reinterpret_cast<const f4v*>(src);
 #pragma unroll
-    for (int m = 0; m < NP; ++m) {
-        const int idx = threadIdx.x + m * BT;
-        pf[m] = idx < N4 ? s4[idx] : f4v{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int m = 0; m < NP; ++m) pf[m] = s4[min((int)threadIdx.x + m * BT, N4 - 1)];
 }
 
 template <int NP, int N4>
 __device__ __forceinline__ void store_block(float* dst, const f4v (&pf)[NP])
 {
 #pragma unroll
-    for (int m = 0; m < NP; ++m) {
-        const int idx = threadIdx.x + m * BT;
-        if (idx < N4) reinterpret_cast<f4v*>(dst)[idx] = pf[m];
-    }
+    for (int m = 0; m < NP; ++m) reinterpret_cast<f4v*>(dst)[min((int)threadIdx.x + m * BT, N4 - 1)] = pf[m];
+}
+
+// An empty use of each register: the compiler waits here for the loads that
+// write them.
+template <int N>
+__device__ __forceinline__ void settle(bf32x4_t (&v)[N])
+{
+#pragma unroll
+    for (int x = 0; x < N; ++x) asm volatile("" : "+v"(v[x]));
+}
+
+// A buffer resource over [base, base + bytes): the buffer unit drops stores
+// at offsets past the end, so a store that only some waves must make is
+// issued by all of them, the others given bytes = 0 (no branch, and the same
+// count of memory operations on every path).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_range(const float* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void store_at(__amdgpu_buffer_rsrc_t r, int byte_off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
 }
 
 // The scans' register layout: the dk x 16 state (or state gradient) tile is
 // held in the accumulators of 16x16x4 float32 MFMA, 16 rows per tile (tiles
 // dealt over the waves); element e of lane (lm, lk) holds row 4 lk + e,
 // column lm, which is also what that lane supplies as the B operand at step
-// e of a product over those rows.  Per chunk the scan copies the chunk's
-// operand block (prefetched into registers while the chunk before computed)
-// to LDS; four barriers, waiting for LDS only.
+// e of a product over those rows.  The 16x16 products U = T diag(beta) Y and
+// Z = T^T dU are formed by every wave in the same layout, so each feeds its
+// own state update without another exchange.  Per chunk the scan copies the
+// chunk's operand block (prefetched into registers while the chunk before
+// computed) to one of two LDS buffers; two barriers, waiting for LDS only:
+// one after the copy, one after the per-wave partials of the product over
+// dk.  A buffer is rewritten two chunks later, after every wave has passed
+// the next chunk's first barrier.
 template <int DK>
 struct ScanLds {
-    alignas(16) float P[PrepLayout<DK>::SIZE];
-    float X[BC][TV + 1];             // V (pass 1) or dO (pass 2) of the tile
-    float W[BC][TV + 1];             // U (pass 1, EJK: e^{b_C - b} U) or dY (pass 2, EJK: e^{b'} dY)
+    alignas(16) float P[2][PrepLayout<DK>::SIZE];
+    float X[2][BC][TV + 1];          // V (pass 1) or dO (pass 2) of the tile
     float PU[BT / kWave][BC][TV + 1];
 };
 
 // Pass 1: the forward state carry per (16 state columns, head, sequence);
 // stores the state entering every chunk and the chunk's Y and U:
-//     Y = V - Kg S,  (I + A) U = diag(beta) Y  (forward substitution, a lane per column)
-//     S <- Diag(e^{b_C}) S + Kc^T U
+//     Y = V - Kg S,  U = T diag(beta) Y,  S <- Diag(e^{b_C}) S + Kc^T U
 template <int DK, bool EJK, typename Tin>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_fwd_scan(BwdParams p)
 {
@@ -511,100 +542,117 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             S[x][e] = (t < NT && p.init) ? p.init[(((size_t)n * H + h) * DK + i) * dv + j0 + lm] : 0.f;
         }
     }
+    // the initial tile is used here, before the loop: else its loads stay
+    // pending into the loop body, whose first use would then wait for every
+    // load in flight, the next chunk's prefetch included
+    settle(S);
     const int nck = seq_chunks(p.off, n, t0, t1);
     const int slot0 = p.off[n];
     const Tin* vv = static_cast<const Tin*>(p.v);
-    f4v pf[NP];
-    Tin pv = 0;
+    // a ring of two register sets: the inputs of chunk c + 2 are loaded while
+    // chunk c computes (the loop is unrolled by two, so each set is fixed)
+    f4v pfa[NP], pfb[NP];
+    Tin pva = 0, pvb = 0;
     const int rr = tid / TV, jj = tid % TV;
+    auto fetch = [&](f4v (&pf)[NP], Tin& pv, int c) __attribute__((always_inline)) {
+        const int cs = t0 + c * BC;
+        fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
+        pv = vv[((size_t)(cs + (cs + rr < t1 ? rr : 0)) * p.Hkv + hk) * dv + j0 + jj];
+    };
     if (nck > 0) {
-        fetch_block<NP, N4>(pf, p.prep + ((size_t)slot0 * H + h) * PL::SIZE);
-        pv = vv[((size_t)(t0 + (t0 + rr < t1 ? rr : 0)) * p.Hkv + hk) * dv + j0 + jj];
+        fetch(pfa, pva, 0);
+        fetch(pfb, pvb, min(1, nck - 1));
     }
-    for (int c = 0; c < nck; ++c) {
-        const int c0 = t0 + c * BC;
-        {
-            float* dst = p.ckS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0 + lm;
+    auto chunk = [&](f4v (&pf)[NP], Tin& pv, int c, auto bsel) __attribute__((always_inline)) {
+        constexpr int b = decltype(bsel)::value;
+            const int c0 = t0 + c * BC;
+            const float* P = L.P[b];
+            // the prefetched block to LDS first, then the state stores: a later
+            // wait for a load then never waits for these stores as well
+            store_block<NP, N4>(L.P[b], pf);
+            L.X[b][rr][jj] = c0 + rr < t1 ? widen(pv) : 0.f;
+            {
+                // tiles t >= NT (idle waves at small dk) fall past the range
+                const auto rs = store_range(p.ckS + (((size_t)(slot0 + c) * H + h) * (dv / TV) + j0 / TV) * DK * TV,
+                                            DK * TV * 4);
 #pragma unroll
-            for (int x = 0; x < TPW; ++x) {
-                const int t = wave + NW * x;
-                if (t < NT) {
+                for (int x = 0; x < TPW; ++x) {
+                    const int t = wave + NW * x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * t + 4 * lk + e) * dv] = S[x][e];
+                    for (int e = 0; e < 4; ++e) store_at(rs, ((16 * t + 4 * lk + e) * TV + lm) * 4, S[x][e]);
                 }
             }
-        }
-        lds_barrier();
-        store_block<NP, N4>(L.P, pf);
-        L.X[rr][jj] = c0 + rr < t1 ? widen(pv) : 0.f;
-        if (c + 1 < nck) {
-            const int cn = c0 + BC;
-            fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c + 1) * H + h) * PL::SIZE);
-            pv = vv[((size_t)(cn + (cn + rr < t1 ? rr : 0)) * p.Hkv + hk) * dv + j0 + jj];
-        }
-        lds_barrier();
-        // Kg S: each wave its tiles' part (A = Kg rows, 16 bytes per lane)
-        {
-            bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+            fetch(pf, pv, min(c + 2, nck - 1));   // past the end: the last chunk again
+            lds_barrier();
+            // Kg S: each wave its tiles' part (A = Kg rows, 16 bytes per lane)
+            {
+                bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int x = 0; x < TPW; ++x) {
-                const int t = wave + NW * x;
-                if (t < NT) {
-                    const float4 a = *reinterpret_cast<const float4*>(L.P + PL::KG + lm * RS + 16 * t + 4 * lk);
-                    acc = bmfma4(a.x, S[x][0], acc);
-                    acc = bmfma4(a.y, S[x][1], acc);
-                    acc = bmfma4(a.z, S[x][2], acc);
-                    acc = bmfma4(a.w, S[x][3], acc);
+                for (int x = 0; x < TPW; ++x) {
+                    const int t = wave + NW * x;
+                    if (t < NT) {
+                        const float4 a = *reinterpret_cast<const float4*>(P + PL::KG + lm * RS + 16 * t + 4 * lk);
+                        acc = bmfma4(a.x, S[x][0], acc);
+                        acc = bmfma4(a.y, S[x][1], acc);
+                        acc = bmfma4(a.z, S[x][2], acc);
+                        acc = bmfma4(a.w, S[x][3], acc);
+                    }
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
             }
+            lds_barrier();
+            // Y (rows 4 lk + u of column lm) and U = T diag(beta) Y, in every wave
+            bf32x4_t U = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+            float y[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
-        }
-        lds_barrier();
-        // Y and U, a lane per column
-        if (tid < TV) {
-            const int j = tid;
-            float* yu = p.ckYU + ((size_t)(slot0 + c) * H + h) * 2 * BC * dv + j0 + j;
-            float u[BC];
-#pragma unroll
-            for (int r = 0; r < BC; ++r) {
-                float ks = (L.PU[0][r][j] + L.PU[1][r][j]) + (L.PU[2][r][j] + L.PU[3][r][j]);
-                if (EJK) ks *= L.P[PL::RF + BC + r];
-                const float y = L.X[r][j] - ks;
-                yu[(size_t)r * dv] = y;
-                float x = L.P[PL::BE + r] * y;
-#pragma unroll
-                for (int s2 = 0; s2 < r; ++s2) x = fmaf(-L.P[PL::CA + r * BC + s2], u[s2], x);
-                u[r] = x;
-                yu[(size_t)(BC + r) * dv] = x;
-                L.W[r][j] = EJK ? x * L.P[PL::RF + 2 * BC + r] : x;
+            for (int u = 0; u < 4; ++u) {
+                const int k = 4 * lk + u;
+                float ks = (L.PU[0][k][lm] + L.PU[1][k][lm]) + (L.PU[2][k][lm] + L.PU[3][k][lm]);
+                if (EJK) ks *= P[PL::RF + BC + k];
+                y[u] = L.X[b][k][lm] - ks;
+                U = bmfma4(P[PL::TI + lm * BC + k], P[PL::BE + k] * y[u], U);
             }
-        }
-        lds_barrier();
-        // S <- Diag(e^{b_C}) S + Kc^T U (EJK: kh^T (e^{b_C - b} U))
-#pragma unroll
-        for (int x = 0; x < TPW; ++x) {
-            const int t = wave + NW * x;
-            if (t < NT) {
-                bf32x4_t a = S[x];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] *= EJK ? L.P[PL::RF + 3 * BC] : L.P[PL::EC + 16 * t + 4 * lk + e];
+            {
+                // wave 0 stores Y and U (the others' range is empty)
+                const auto rs = store_range(p.ckYU + ((size_t)(slot0 + c) * H + h) * 2 * BC * dv,
+                                            wave == 0 ? 2 * BC * dv * 4 : 0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * lk + u;
-                    a = bmfma4(L.P[(EJK ? PL::KG : PL::KC) + r * RS + 16 * t + lm], L.W[r][lm], a);
+                    store_at(rs, ((4 * lk + u) * dv + j0 + lm) * 4, y[u]);
+                    store_at(rs, ((BC + 4 * lk + u) * dv + j0 + lm) * 4, U[u]);
                 }
-                S[x] = a;
             }
-        }
+            // S <- Diag(e^{b_C}) S + Kc^T U (EJK: kh^T (e^{b_C - b} U))
+            if (EJK) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) U[u] *= P[PL::RF + 2 * BC + 4 * lk + u];
+            }
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+                    bf32x4_t a = S[x];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] *= EJK ? P[PL::RF + 3 * BC] : P[PL::EC + 16 * t + 4 * lk + e];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        a = bmfma4(P[(EJK ? PL::KG : PL::KC) + (4 * lk + u) * RS + 16 * t + lm], U[u], a);
+                    S[x] = a;
+                }
+            }
+    };
+    for (int c = 0; c < nck; c += 2) {
+        chunk(pfa, pva, c, std::integral_constant<int, 0>{});
+        if (c + 1 < nck) chunk(pfb, pvb, c + 1, std::integral_constant<int, 1>{});
     }
 }
 
 // Pass 2: the state gradient carried backward per (16 state columns, head,
 // sequence); stores dL/d(state leaving) and Z of every chunk, and at the end
 // dL/d(initial state).  Per chunk, last to first:
-//     dU = Kc dS + P^T dO            (a partial per wave, summed in LDS)
-//     (I + A)^T Z = dU, dY = diag(beta) Z   (back substitution, a lane per column)
+//     dU = Kc dS + P^T dO   (a partial per wave, summed in LDS)
+//     Z = T^T dU,  dY = diag(beta) Z
 //     dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
 // (EJK: qh, kh with the scalar row factors applied to dO, dY and dU rows).
 template <int DK, bool EJK, typename Tin>
@@ -633,109 +681,123 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             dS[x][e] = (t < NT && p.dSf) ? p.dSf[(((size_t)n * H + h) * DK + i) * dv + j0 + lm] : 0.f;
         }
     }
+    settle(dS);   // as in the forward scan
     const int nck = seq_chunks(p.off, n, t0, t1);
     const int slot0 = p.off[n];
-    f4v pf[NP];
-    float pd = 0.f;
+    // a ring of two register sets: the inputs of chunk c - 2 are loaded while
+    // chunk c computes (the loop is unrolled by two, so each set is fixed);
+    // dO as loaded (bf16 or float32 bits), widened where used
+    f4v pfa[NP], pfb[NP];
+    uint32_t pda = 0, pdb = 0;
     const int rr = tid / TV, jj = tid % TV;
+    auto fetch = [&](f4v (&pf)[NP], uint32_t& pd, int c) __attribute__((always_inline)) {
+        const int cs = t0 + c * BC;
+        fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
+        const size_t i = ((size_t)(cs + (cs + rr < t1 ? rr : 0)) * H + h) * dv + j0 + jj;
+        pd = p.do_bf16 ? (uint32_t)static_cast<const uint16_t*>(p.d_o)[i] : static_cast<const uint32_t*>(p.d_o)[i];
+    };
     if (nck > 0) {
-        const int cl = t0 + (nck - 1) * BC;
-        fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + nck - 1) * H + h) * PL::SIZE);
-        pd = ldx(p.d_o, ((size_t)(cl + (cl + rr < t1 ? rr : 0)) * H + h) * dv + j0 + jj, p.do_bf16);
+        fetch(pfa, pda, nck - 1);
+        fetch(pfb, pdb, max(nck - 2, 0));
     }
-    for (int c = nck - 1; c >= 0; --c) {
-        const int c0 = t0 + c * BC;
-        {
-            float* dst = p.ckdS + ((size_t)(slot0 + c) * H + h) * DK * dv + j0 + lm;
+    auto chunk = [&](f4v (&pf)[NP], uint32_t& pd, int c, auto bsel) __attribute__((always_inline)) {
+        constexpr int b = decltype(bsel)::value;
+            const int c0 = t0 + c * BC;
+            const float* P = L.P[b];
+            store_block<NP, N4>(L.P[b], pf);
+            L.X[b][rr][jj] = c0 + rr < t1 ? __uint_as_float(p.do_bf16 ? pd << 16 : pd) : 0.f;
+            {
+                // tiles t >= NT (idle waves at small dk) fall past the range
+                const auto rs = store_range(p.ckdS + (((size_t)(slot0 + c) * H + h) * (dv / TV) + j0 / TV) * DK * TV,
+                                            DK * TV * 4);
+#pragma unroll
+                for (int x = 0; x < TPW; ++x) {
+                    const int t = wave + NW * x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) store_at(rs, ((16 * t + 4 * lk + e) * TV + lm) * 4, dS[x][e]);
+                }
+            }
+            fetch(pf, pd, max(c - 2, 0));   // before the start: the first chunk again
+            lds_barrier();
+            // dU: each wave its tiles' part of Kc dS; wave 1 adds P^T dO
+            {
+                bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int x = 0; x < TPW; ++x) {
+                    const int t = wave + NW * x;
+                    if (t < NT) {
+                        const float4 a = *reinterpret_cast<const float4*>(P + (EJK ? PL::KG : PL::KC) + lm * RS +
+                                                                          16 * t + 4 * lk);
+                        acc = bmfma4(a.x, dS[x][0], acc);
+                        acc = bmfma4(a.y, dS[x][1], acc);
+                        acc = bmfma4(a.z, dS[x][2], acc);
+                        acc = bmfma4(a.w, dS[x][3], acc);
+                    }
+                }
+                if (EJK) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] *= P[PL::RF + 2 * BC + 4 * lk + e];
+                }
+                if (wave == 1) {
+                    // (P^T dO)[m][j] = sum_s P[s][m] dO[s][j], s = 4 lk + u at step u
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int s2 = 4 * lk + u;
+                        acc = bmfma4(P[PL::GP + s2 * BC + lm], L.X[b][s2][lm], acc);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
+            }
+            lds_barrier();
+            // Z = T^T dU in every wave: at step u the lane supplies T[4 lk + u][lm]
+            // and dU[4 lk + u][lm]
+            bf32x4_t Z = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = 4 * lk + u;
+                const float du = (L.PU[0][k][lm] + L.PU[1][k][lm]) + (L.PU[2][k][lm] + L.PU[3][k][lm]);
+                Z = bmfma4(P[PL::TI + k * BC + lm], du, Z);
+            }
+            {
+                // wave 0 stores Z (the others' range is empty)
+                const auto rs = store_range(p.ckZ + ((size_t)(slot0 + c) * H + h) * BC * dv,
+                                            wave == 0 ? BC * dv * 4 : 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) store_at(rs, ((4 * lk + e) * dv + j0 + lm) * 4, Z[e]);
+            }
+            // dY (EJK: e^{b'} dY), rows 4 lk + e: the B operand of Kg^T dY
+            float dy[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = 4 * lk + e;
+                dy[e] = P[PL::BE + k] * Z[e];
+                if (EJK) dy[e] *= P[PL::RF + BC + k];
+            }
+            // dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
 #pragma unroll
             for (int x = 0; x < TPW; ++x) {
                 const int t = wave + NW * x;
                 if (t < NT) {
+                    bf32x4_t a = dS[x];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * t + 4 * lk + e) * dv] = dS[x][e];
+                    for (int e = 0; e < 4; ++e) a[e] *= EJK ? P[PL::RF + 3 * BC] : P[PL::EC + 16 * t + 4 * lk + e];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 4 * lk + u;
+                        const float d = EJK ? L.X[b][r][lm] * P[PL::RF + r] : L.X[b][r][lm];
+                        a = bmfma4(P[PL::QG + r * RS + 16 * t + lm], d, a);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        a = bmfma4(-P[PL::KG + (4 * lk + u) * RS + 16 * t + lm], dy[u], a);
+                    dS[x] = a;
                 }
             }
-        }
-        lds_barrier();
-        store_block<NP, N4>(L.P, pf);
-        L.X[rr][jj] = c0 + rr < t1 ? pd : 0.f;
-        if (c > 0) {
-            const int cp = c0 - BC;   // a whole chunk
-            fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c - 1) * H + h) * PL::SIZE);
-            pd = ldx(p.d_o, ((size_t)(cp + rr) * H + h) * dv + j0 + jj, p.do_bf16);
-        }
-        lds_barrier();
-        // dU: each wave its tiles' part of Kc dS; wave 1 adds P^T dO
-        {
-            bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int x = 0; x < TPW; ++x) {
-                const int t = wave + NW * x;
-                if (t < NT) {
-                    const float4 a = *reinterpret_cast<const float4*>(L.P + (EJK ? PL::KG : PL::KC) + lm * RS +
-                                                                      16 * t + 4 * lk);
-                    acc = bmfma4(a.x, dS[x][0], acc);
-                    acc = bmfma4(a.y, dS[x][1], acc);
-                    acc = bmfma4(a.z, dS[x][2], acc);
-                    acc = bmfma4(a.w, dS[x][3], acc);
-                }
-            }
-            if (EJK) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] *= L.P[PL::RF + 2 * BC + 4 * lk + e];
-            }
-            if (wave == 1) {
-                // (P^T dO)[m][j] = sum_s P[s][m] dO[s][j], s = 4 lk + u at step u
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int s2 = 4 * lk + u;
-                    acc = bmfma4(L.P[PL::GP + s2 * BC + lm], L.X[s2][lm], acc);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
-        }
-        lds_barrier();
-        // (I + A)^T Z = dU by back substitution, a lane per column
-        if (tid < TV) {
-            const int j = tid;
-            float* zd = p.ckZ + ((size_t)(slot0 + c) * H + h) * BC * dv + j0 + j;
-            float z[BC];
-#pragma unroll
-            for (int r = 0; r < BC; ++r) z[r] = (L.PU[0][r][j] + L.PU[1][r][j]) + (L.PU[2][r][j] + L.PU[3][r][j]);
-#pragma unroll
-            for (int s2 = BC - 1; s2 >= 0; --s2) {
-                const float zs = z[s2];
-                zd[(size_t)s2 * dv] = zs;
-                const float dy = L.P[PL::BE + s2] * zs;
-                L.W[s2][j] = EJK ? dy * L.P[PL::RF + BC + s2] : dy;
-#pragma unroll
-                for (int r = 0; r < s2; ++r) z[r] = fmaf(-L.P[PL::CA + s2 * BC + r], zs, z[r]);
-            }
-        }
-        lds_barrier();
-        // dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
-#pragma unroll
-        for (int x = 0; x < TPW; ++x) {
-            const int t = wave + NW * x;
-            if (t < NT) {
-                bf32x4_t a = dS[x];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] *= EJK ? L.P[PL::RF + 3 * BC] : L.P[PL::EC + 16 * t + 4 * lk + e];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * lk + u;
-                    const float d = EJK ? L.X[r][lm] * L.P[PL::RF + r] : L.X[r][lm];
-                    a = bmfma4(L.P[PL::QG + r * RS + 16 * t + lm], d, a);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * lk + u;
-                    a = bmfma4(-L.P[PL::KG + r * RS + 16 * t + lm], L.W[r][lm], a);
-                }
-                dS[x] = a;
-            }
-        }
+    };
+    for (int k = 0; k < nck; k += 2) {
+        chunk(pfa, pda, nck - 1 - k, std::integral_constant<int, 0>{});
+        if (k + 1 < nck) chunk(pfb, pdb, nck - 2 - k, std::integral_constant<int, 1>{});
     }
     if (p.dS0) {
 #pragma unroll
@@ -802,7 +864,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const int nj = dv / 16;
     const float ea = EJK ? 0.f : expf(p.a_log[h]);
     // ---- loads.  S0 and dS1 rows of this wave's channel tiles, 16 bytes per
-    // lane per 16 columns (lane (lm, lk): row 16 t + lm, columns 16 jb + 4 lk ..)
+    // lane per 16 columns (lane (lm, lk): row 16 t + lm, columns 16 jb + 4 lk ..;
+    // a 16-column tile's rows are 64 bytes apart)
     float4 s0r[TPW][NJ], d1r[TPW][NJ];
     {
         const float* S0 = p.ckS + ((size_t)slot * H + h) * DK * dv;
@@ -813,7 +876,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
             for (int jb = 0; jb < NJ; ++jb) {
                 const bool ok = t < NT && jb < nj;
-                const size_t o = (size_t)(16 * t + lm) * dv + 16 * jb + 4 * lk;
+                const size_t o = ((size_t)jb * DK + 16 * t + lm) * TV + 4 * lk;
                 s0r[x][jb] = ok ? *reinterpret_cast<const float4*>(S0 + o) : make_float4(0.f, 0.f, 0.f, 0.f);
                 d1r[x][jb] = ok ? *reinterpret_cast<const float4*>(dS1 + o) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
