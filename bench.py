@@ -625,7 +625,7 @@ def bench_gated(steps, warmup):
         out[f"gated_recurrent_b4_t4096_h16_d128_bf16_{name}"] = {
             "tokens_per_s": round(B * T / (ms * 1e-3), 1), "ms_per_call": round(ms, 4), "alg_bytes": nbytes,
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "gates": sorted(gates),
-            "path": "token by token, float32"}
+            "path": "16-token chunks, float32 (MFMA)"}
     return out
 
 
