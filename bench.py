@@ -226,6 +226,22 @@ def _unit_worst(o, ro, s, rs, cu=None):
     return wo, ws
 
 
+def kernel_counters(name, sources, alg_bytes):
+    """HBM traffic per call of a workload from its committed counter summary
+    (profiles/<name>_pmc.txt, taken on the current source of `sources`) and
+    its ratio to the algorithmic bytes; None once the source has changed."""
+    sh = _src_hash(*sources)
+    kv = _profile_kv(name, sh)
+    res = {"traffic": None, "traffic_over_alg": None, "src_hash": sh, "source": f"profiles/{name}_pmc.txt"}
+    if kv:
+        try:
+            tr = int(float(kv["hbm_bytes_per_call"]))
+            res.update(traffic=tr, traffic_over_alg=round(tr / alg_bytes, 3) if alg_bytes else None)
+        except (KeyError, ValueError):
+            pass
+    return res
+
+
 def cpu_info():
     """Host figures reported with every CPU leg: logical CPUs of the machine,
     its CPU model, and the oracle's OpenMP thread count (the cores it uses)."""
@@ -558,8 +574,10 @@ def bench_backward(steps, warmup, cpu=True):
     res = {"workload": "kda_prefill_backward_b4_t4096_h16_d128_bf16", "tokens_per_s": round(B * T / (ms * 1e-3), 1),
            "ms_per_call": round(ms, 4), "alg_bytes": nbytes,
            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "note": "float32 arithmetic; chunks of 16 tokens: forward state scan, reverse state-gradient "
-                   "scan, chunk-parallel local gradients"}
+           "note": "float32 arithmetic; chunks of 16 tokens: chunk operands formed once, forward state "
+                   "scan, reverse state-gradient scan, chunk-parallel local gradients",
+           "rocprof": kernel_counters("backward_b4_t4096_h16_d128_bf16", ("kda_backward.hip", "kda_device.h"),
+                                      nbytes)}
     if cpu:
         from oracle import kda_oracle
         gr = call()
@@ -590,9 +608,14 @@ def gated_bytes(ntok, H, dk, dv, gates, io_bytes=2):
     return ntok * H * per + (4 * H if "g_gamma" in gates else 0)
 
 
-def bench_gated(steps, warmup):
-    """kda_recurrent_attention on the B4 T4096 H16 d128 bf16 shape with the key
-    gate (the GLA-style forget gate) and, separately, with all four gates."""
+GATED_CONFIGS = ["gated_recurrent_b4_t4096_h16_d128_bf16_gk", "gated_recurrent_b4_t4096_h16_d128_bf16_all"]
+
+
+def bench_gated(steps, warmup, cpu=True, only=None):
+    """recurrent_attention on the B4 T4096 H16 bf16 workload, with the key
+    gate alone and with all four gates; each with a sampled CPU oracle leg
+    (the float64 token loop on the first heads, every sequence) that also
+    gives the parity of those heads."""
     import torch
     import gated_delta_rule_90_amd as kda
     from gated_delta_rule_90_amd import workloads
@@ -608,8 +631,11 @@ def bench_gated(steps, warmup):
     gg = -np.abs(0.01 * rng.standard_normal((B, H), np.float32))
     q, k, v = d(inp.q, bf), d(inp.k, bf), d(inp.v, bf)
     out = {}
-    for name, gates in (("gk", {"gk": d(gk, f)}),
-                        ("all", {"g": d(g, f), "gk": d(gk, f), "gv": d(gv, f), "g_gamma": d(gg, f)})):
+    for name, gates_np in (("gk", {"gk": gk}), ("all", {"g": g, "gk": gk, "gv": gv, "g_gamma": gg})):
+        key = f"gated_recurrent_b4_t4096_h16_d128_bf16_{name}"
+        if only is not None and key != only:
+            continue
+        gates = {n: d(x, f) for n, x in gates_np.items()}
         call = lambda: kda.recurrent_attention(q, k, v, **gates)
         for _ in range(warmup):
             call()
@@ -622,10 +648,33 @@ def bench_gated(steps, warmup):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
         nbytes = gated_bytes(B * T, H, dk, dv, gates)
-        out[f"gated_recurrent_b4_t4096_h16_d128_bf16_{name}"] = {
-            "tokens_per_s": round(B * T / (ms * 1e-3), 1), "ms_per_call": round(ms, 4), "alg_bytes": nbytes,
-            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "gates": sorted(gates),
-            "path": "16-token chunks, float32 (MFMA)"}
+        res = {"tokens_per_s": round(B * T / (ms * 1e-3), 1), "ms_per_call": round(ms, 4), "alg_bytes": nbytes,
+               "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "gates": sorted(gates),
+               "path": "16-token chunks, float32 (MFMA)",
+               "rocprof": kernel_counters(key, ("kda_gated.hip", "kda_device.h"), nbytes)}
+        if cpu:
+            from oracle import kda_oracle
+            o_gpu = call().float().cpu().numpy()
+            hs = list(range(min(H, max(1, -(-kda_oracle.max_threads() // B)))))
+            sub = lambda x: None if x is None else x[:, :, hs]
+            qs, ks, vs = (workloads.round_to_bf16(x[:, :, hs]) for x in (inp.q, inp.k, inp.v))
+            kw = dict(g=sub(gates_np.get("g")), gk=sub(gates_np.get("gk")), gv=sub(gates_np.get("gv")),
+                      g_gamma=None if "g_gamma" not in gates_np else gates_np["g_gamma"][:, hs])
+            box = {}
+
+            def run():
+                box["o"], _ = kda_oracle.gated_recurrent(qs, ks, vs, **kw)
+
+            el, times = _median3(run, 3)
+            worst = max(rel_l2(o_gpu[bb, :, h], box["o"][bb, :, j]) for bb in range(B) for j, h in enumerate(hs))
+            res["cpu_baseline"] = dict({"value": round(B * T / (el * H / len(hs)), 1),
+                                        "unit": f"tokens/s (all {H} heads)", "kind": "oracle",
+                                        "sample": f"4 sequences x 4096 tokens, heads 0..{hs[-1]} ({len(hs)} of "
+                                                  f"{H}), float64; median of 3 runs {times} s",
+                                        "parity": {"worst_unit_rel_l2_o": worst, "bar": 2e-2, "ok": worst <= 2e-2,
+                                                   "sample": "every (sequence, head) unit of the sampled heads"}},
+                                       **cpu_info())
+        out[key] = res
     return out
 
 
@@ -636,32 +685,49 @@ def bench_configs(steps, warmup, cpu=True):
     from gated_delta_rule_90_amd import workloads
     out = {}
     inp = workloads.recurrent_fp32_small()
-    out["recurrent_fp32_b1_t64_h2_d16"] = dict(_prefill_run(inp, 10 * steps, warmup, graph=True),
-                                               note="64 dependent token steps per call: latency bound; "
-                                                    "ms_per_call includes the host's per-call overhead, "
-                                                    "graph_ms_per_call is the device time")
+    r = _prefill_run(inp, 10 * steps, warmup, graph=True, keep=cpu)
+    c1 = r.pop("check", None)
+    out["recurrent_fp32_b1_t64_h2_d16"] = dict(r, note="64 dependent token steps per call: latency bound; "
+                                                       "ms_per_call includes the host's per-call overhead, "
+                                                       "graph_ms_per_call is the device time")
     # the same workload through the float32 chunked kernel (2 chunks of 32 tokens)
-    out["chunked_fp32_b1_t64_h2_d16"] = dict(_prefill_run(inp, 10 * steps, warmup, graph=True, use_chunked=True),
-                                             note="2 dependent 32-token chunks per call; graph_ms_per_call "
-                                                  "is the device time")
+    r2 = _prefill_run(inp, 10 * steps, warmup, graph=True, use_chunked=True, keep=cpu)
+    c2 = r2.pop("check", None)
+    out["chunked_fp32_b1_t64_h2_d16"] = dict(r2, note="2 dependent 32-token chunks per call; graph_ms_per_call "
+                                                      "is the device time")
+    if cpu:
+        # the whole workload (both heads)
+        for key, ck in (("recurrent_fp32_b1_t64_h2_d16", c1), ("chunked_fp32_b1_t64_h2_d16", c2)):
+            out[key]["cpu_baseline"] = _cpu_prefill_leg(inp, range(inp.q.shape[2]), 3, "the whole workload",
+                                                        check=ck)
     # a larger float32 prefill on both float32 kernels
     inp = workloads.prefill_fp32_b1_t4096_h16_d128()
-    out["prefill_fp32_b1_t4096_h16_d128_token_by_token"] = _prefill_run(inp, steps, warmup)
-    out["prefill_fp32_b1_t4096_h16_d128_chunked"] = _prefill_run(inp, steps, warmup, use_chunked=True)
+    out["prefill_fp32_b1_t4096_h16_d128_token_by_token"] = _prefill_run(inp, steps, warmup, keep=cpu)
+    out["prefill_fp32_b1_t4096_h16_d128_chunked"] = _prefill_run(inp, steps, warmup, use_chunked=True, keep=cpu)
+    if cpu:
+        from oracle import kda_oracle
+        nh = min(inp.q.shape[2], max(1, kda_oracle.max_threads()))
+        for key in ("prefill_fp32_b1_t4096_h16_d128_token_by_token", "prefill_fp32_b1_t4096_h16_d128_chunked"):
+            out[key]["cpu_baseline"] = _cpu_prefill_leg(inp, range(nh), 3, "1 sequence x 4096 tokens",
+                                                        check=out[key].pop("check"))
     del inp
     gc.collect()
     for name in _mfma_configs():
         out[name] = bench_one_mfma_config(name, steps, warmup, cpu)
     out["backward_b4_t4096_h16_d128_bf16"] = bench_backward(max(3, steps // 4), 1, cpu)
     gc.collect()
-    out.update(bench_gated(max(3, steps // 4), 1))
+    out.update(bench_gated(max(3, steps // 4), 1, cpu))
     gc.collect()
     # a decode step takes ~50 us: 20x the steps of the prefill configs, so that the
     # mean is not set by the first few calls
-    _, dres = _decode_run(workloads.decode_grouped_b64_h32_hkv8_d128(), 20 * steps, 2 * warmup)
+    ginp = workloads.decode_grouped_b64_h32_hkv8_d128()
+    _, dres = _decode_run(ginp, 20 * steps, 2 * warmup)
     out["decode_grouped_b64_h32_hkv8_d128"] = {
         "steps_per_s": round(dres["steps_per_s"], 2), "ms_per_step": round(dres["ms"], 5),
         "alg_bytes": dres["bytes"], "hbm_frac": dres["roofline"]["frac"]}
+    if cpu:
+        out["decode_grouped_b64_h32_hkv8_d128"]["cpu_baseline"] = cpu_decode_baseline(ginp, 5.0,
+                                                                                      check=dres.get("check"))
     return out
 
 
@@ -709,9 +775,14 @@ def main():
         elif args.config in _mfma_configs():
             res = bench_one_mfma_config(args.config, max(10, args.steps), args.warmup, cpu=False,
                                         extras=False)
+        elif args.config == "backward_b4_t4096_h16_d128_bf16":
+            res = bench_backward(args.steps, args.warmup, cpu=False)
+        elif args.config in GATED_CONFIGS:
+            res = bench_gated(args.steps, args.warmup, cpu=False, only=args.config)[args.config]
         else:
             print(f"bench.py: unknown --config {args.config}; one of prefill_b4_t4096_h16_d128, "
-                  + ", ".join(_mfma_configs()), file=sys.stderr)
+                  + ", ".join(list(_mfma_configs()) + ["backward_b4_t4096_h16_d128_bf16"] + GATED_CONFIGS),
+                  file=sys.stderr)
             sys.exit(2)
         print(json.dumps({"config": args.config, **res}), flush=True)
         return

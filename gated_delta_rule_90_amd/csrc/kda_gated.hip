@@ -102,8 +102,16 @@ __global__ __launch_bounds__(GTH) void gated_chunk_kernel(GatedParams p)
     const int lane = tid & 63, wave = tid >> 6;
     const int lm = lane & 15, lk = lane >> 4;
     const int r16 = tid >> 4, c16 = tid & 15;
-    const int j0 = blockIdx.x * GJ, h = blockIdx.y, n = blockIdx.z;
     const int H = p.H, HKV = p.Hkv, DV = p.dv;
+    // Linear workgroup ids are dealt to the 8 XCDs in turn: the column tiles of
+    // one (sequence, head), which read the same q, k and gate rows, get ids
+    // equal modulo 8, so they run on one XCD and share its L2.  Ids past the
+    // last (sequence, head) (the count is padded to a multiple of 8) exit.
+    const int ntile = DV / GJ;
+    const int xcd = blockIdx.x & 7, qd = blockIdx.x >> 3;
+    const int grp = (qd / ntile) * 8 + xcd;
+    if (grp >= H * p.N) return;
+    const int j0 = (qd % ntile) * GJ, h = grp % H, n = grp / H;
     const int hk = h / (H / HKV);
     int t0, t1;
     if (p.cu) {
@@ -325,7 +333,9 @@ __global__ __launch_bounds__(GTH) void gated_chunk_kernel(GatedParams p)
 template <int DK, typename Tin, typename Tout>
 hipError_t launch_chunk(const GatedParams& p, hipStream_t st)
 {
-    const dim3 grid((unsigned)(p.dv / GJ), (unsigned)p.H, (unsigned)p.N);
+    const unsigned groups8 = (unsigned)((p.H * p.N + 7) / 8 * 8);
+    if (groups8 == 0) return hipSuccess;
+    const dim3 grid(groups8 * (unsigned)(p.dv / GJ));
     hipLaunchKernelGGL((gated_chunk_kernel<DK, Tin, Tout>), grid, dim3(GTH), 0, st, p);
     return hipGetLastError();
 }
