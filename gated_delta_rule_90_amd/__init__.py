@@ -62,8 +62,11 @@ def lib() -> ctypes.CDLL:
     L.kda_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.kda_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
     L.kda_recurrent_attention.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, fp, fp, ip, i32, i32, i32,
-                                          i32, i32, i32, i32, f32, i32, vp, ctypes.c_int, fp, vp]
+                                          i32, i32, i32, i32, f32, i32, vp, ctypes.c_int, fp, vp,
+                                          ctypes.c_size_t, vp]
     L.kda_recurrent_attention.restype = ctypes.c_int
+    L.kda_recurrent_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.kda_recurrent_attention_workspace_bytes.restype = ctypes.c_size_t
     L.kda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, u32]
     L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kda_decode_step.argtypes = [fp, fp, fp, fp, fp, fp, fp, f32, f32, i32, i32, i32, i32, i32, u32,
@@ -322,11 +325,14 @@ def recurrent_attention(query, key, value, g=None, g_gamma=None, gk=None, gv=Non
             if tuple(final_state.shape) != (N, H, dk, dv):
                 raise ValueError("final_state must be [N, H, dk, dv]")
         sc = -1.0 if softmax_scale is None else float(softmax_scale)
+        nseq = N if cu_seqlens is not None else 0
+        wsb = int(lib().kda_recurrent_attention_workspace_bytes(nseq, B, T, H, dk, dv))
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
         _check(lib().kda_recurrent_attention(
             _ptr(q), _ptr(k), _ptr(v), BF16 if q.dtype == torch.bfloat16 else F32, _ptr(g), _ptr(g_gamma),
-            _ptr(gk), _ptr(gv), _ptr(initial_state), _ptr(cu_seqlens), N if cu_seqlens is not None else 0,
+            _ptr(gk), _ptr(gv), _ptr(initial_state), _ptr(cu_seqlens), nseq,
             B, T, H, Hkv, dk, dv, sc, int(bool(reverse)), _ptr(out), BF16 if odt == torch.bfloat16 else F32,
-            _ptr(final_state), _stream(dev, stream)))
+            _ptr(final_state), _ptr(ws), wsb, _stream(dev, stream)))
     if return_state:
         return out, final_state
     return out

@@ -279,12 +279,21 @@ kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, k
     return hip_status(kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream)), "kda_prefill_backward");
 }
 
+size_t kda_recurrent_attention_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk,
+                                               int32_t dv)
+{
+    const bool packed = num_seqs > 0;
+    const int N = packed ? num_seqs : B;
+    if (N < 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv) || (packed && B != 1)) return 0;
+    return kda::gated_workspace_bytes(N, T, H, dk, packed);
+}
+
 kda_status_t kda_recurrent_attention(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
                                      const float* g, const float* g_gamma, const float* gk, const float* gv,
                                      const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
                                      int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t dk, int32_t dv,
                                      float scale, int32_t reverse, void* o, kda_dtype_t out_dtype,
-                                     float* final_state, void* stream)
+                                     float* final_state, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0)
         return fail(KDA_EINVAL, "kda_recurrent_attention: bad sizes B=%d T=%d H=%d dk=%d dv=%d", B, T, H, dk, dv);
@@ -318,6 +327,10 @@ kda_status_t kda_recurrent_attention(const void* q, const void* k, const void* v
     if (!cu_seqlens && (long long)B * T > 0x7fffffffLL)
         return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: B * T must fit in 31 bits");
     if (N == 0 || (!has_tokens && !final_state)) return ok();
+    const size_t need = kda::gated_workspace_bytes(N, T, H, dk, cu_seqlens != nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(KDA_EINVAL, "kda_recurrent_attention: workspace of %zu bytes required (got %zu)", need,
+                    workspace_bytes);
     kda::GatedArgs a{};
     a.q = q; a.k = k; a.v = v; a.in_bf16 = in_dtype == KDA_BF16;
     a.g = g; a.g_gamma = g_gamma; a.g_gamma_rows = cu_seqlens ? 1 : B; a.gk = gk; a.gv = gv;
@@ -326,6 +339,7 @@ kda_status_t kda_recurrent_attention(const void* q, const void* k, const void* v
     a.scale = (scale > 0.f) ? scale : 1.0f / std::sqrt((float)dk);
     a.reverse = reverse;
     a.o = o; a.out_bf16 = out_dtype == KDA_BF16; a.final_state = final_state;
+    a.workspace = workspace;
     return hip_status(kda::launch_gated(a, reinterpret_cast<hipStream_t>(stream)), "kda_recurrent_attention");
 }
 

@@ -25,22 +25,39 @@
 // no bound on the gates, so a chunk that spans more forms e^{bk_ri - bk_si}
 // element by element (a per-chunk, workgroup-uniform choice).  The value-axis
 // factors e^{bv_rj - bv_sj} are formed element by element.  For s <= r these
-// factors are at most 1 when the gates are at most 0.  The inter-chunk
-// read-out and the state update run on 16x16x4 float32 MFMA.  One 256-thread
-// workgroup per (sequence, head, 16 state columns); the state tile stays in
-// LDS, transposed.  Rows past the sequence are neutral (q = k = v = 0, every
-// gate 0).  The next two chunks' inputs are in flight in a register ring.
+// factors are at most 1 when the gates are at most 0.
+//
+// Two kernels.  gated_prep, one workgroup per (chunk, head), every chunk in
+// parallel, forms what does not depend on the value columns: the read-out
+// rows qt e^{bk}, the carry rows e^{bk_C - bk} k, A (16 x 16) and e^{bk_C},
+// into a per-(chunk, head) block of the caller's workspace.  gated_scan, one
+// workgroup per (sequence, head, 16 state columns), walks the chunks in
+// order with the dk x 16 state tile in the accumulator registers of 16x16x4
+// float32 MFMA: per chunk the inter-chunk read-out (each wave its tiles'
+// part, summed in LDS), the intra-chunk term A (e^{bv_0 - bv} v) on MFMA with
+// the value-axis factors referenced to the chunk's first row (element by
+// element when a column's log-decay over the chunk leaves the factor range),
+// and the state update.  The chunk's operand block is copied to one of two
+// LDS buffers from registers loaded two chunks ahead; two barriers per chunk,
+// for LDS only.  Rows past a sequence's end are neutral (q = k = v = 0, every
+// gate 0) and their outputs are dropped by the store's buffer range.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
+constexpr int GC = 16;    // chunk rows
+constexpr int GJ = 16;    // state columns per scan workgroup
+constexpr int GTH = 256;  // threads per workgroup
+constexpr int GNW = GTH / kWave;
+
 struct GatedParams {
     const void* q;
     const void* k;
     const void* v;
-    int in_bf16;
     const float* g;
     const float* g_gamma;
     int g_gamma_rows;
@@ -52,34 +69,64 @@ struct GatedParams {
     float scale;
     int reverse;
     void* o;
-    int out_bf16;
     float* final_state;
+    const int32_t* off;   // [N + 1] chunk offsets
+    float* prep;          // [slots, H, GPrep<dk>::SIZE]
 };
 
-constexpr int GC = 16;    // chunk rows
-constexpr int GJ = 16;    // state columns per workgroup
-constexpr int GTH = 256;  // threads per workgroup
-
+// The column-independent operands of one (chunk, head), floats, rows of
+// RS = dk + 4 (copied to LDS as they are; 16-byte rows 4 banks apart):
+//     QE [16][RS]  qt e^{bk}             KC [16][RS]  e^{bk_C - bk} k
+//     AM [16][16]  A (s <= r, else 0)    EKC [dk]     e^{bk_C}
 template <int DK>
-struct GatedLds {
-    static constexpr int RS = DK + 4;   // row stride of [16][dk] tiles: 16-byte aligned rows
-    alignas(16) float QT[GC * RS];   // scale e^{g} q
-    alignas(16) float KT[GC * RS];   // k
-    alignas(16) float BK[GC * RS];   // gk + g_gamma, then its cumulative sum bk
-    alignas(16) float QE[GC * RS];   // qt e^{bk}
-    alignas(16) float KC[GC * RS];   // e^{bk_C - bk} k
-    alignas(16) float QF[GC * RS];   // qt e^{bk - bk_0}  (A's left factor)
-    alignas(16) float KF[GC * RS];   // k e^{bk_0 - bk}   (A's right factor)
-    alignas(16) float ST[GJ * RS];   // the state tile, transposed: S[i][j] at ST[j * RS + i]
-    float VV[GC][GJ + 1];   // v
-    float BV[GC][GJ + 1];   // gv, then its cumulative sum bv
-    float VC[GC][GJ + 1];   // e^{bv_C - bv} v
-    float AM[GC][GC + 1];   // A (s <= r)
-    float OI[GC][GJ + 1];   // the inter-chunk part of O, before its e^{bv} factor
-    float EKC[DK];          // e^{bk_C}
-    float EVC[GJ];          // e^{bv_C}
-    int wide;               // some channel's log-decay spans more than the factor range
+struct GPrep {
+    static constexpr int RS = DK + 4;
+    static constexpr int QE = 0, KC = GC * RS, AM = 2 * GC * RS, EKC = AM + GC * GC;
+    static constexpr int SIZE = (EKC + DK + 63) / 64 * 64;
 };
+
+size_t gprep_floats(int dk)
+{
+    switch (dk) {
+    case 16: return GPrep<16>::SIZE;
+    case 32: return GPrep<32>::SIZE;
+    case 64: return GPrep<64>::SIZE;
+    default: return GPrep<128>::SIZE;
+    }
+}
+
+__device__ __forceinline__ void gseq_bounds(const GatedParams& p, int n, int& t0, int& t1)
+{
+    if (p.cu) {
+        t0 = min(max(p.cu[n], 0), p.T);
+        t1 = min(max(p.cu[n + 1], t0), p.T);
+    } else {
+        t0 = n * p.T;
+        t1 = t0 + p.T;
+    }
+}
+
+// Chunk offsets: off[n] = sum_{m<n} ceil(len_m / 16), capped at the slots
+// (only overlapping ranges can ask for more; their last chunks are dropped).
+__global__ void gated_plan_kernel(GatedParams p, int slots, int32_t* __restrict__ off)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int acc = 0;
+    for (int n = 0; n < p.N; ++n) {
+        int t0, t1;
+        gseq_bounds(p, n, t0, t1);
+        off[n] = acc;
+        acc = min(acc + (t1 - t0 + GC - 1) / GC, slots);
+    }
+    off[p.N] = acc;
+}
+
+template <typename T>
+__device__ __forceinline__ float widen(T x)
+{
+    if constexpr (std::is_same_v<T, float>) return x;
+    else return __uint_as_float((uint32_t)x << 16);
+}
 
 typedef float gf32x4_t __attribute__((ext_vector_type(4)));
 
@@ -90,280 +137,431 @@ __device__ __forceinline__ gf32x4_t gmfma4(float a, float b, gf32x4_t c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int DK, typename Tin, typename Tout>
-__global__ __launch_bounds__(GTH) void gated_chunk_kernel(GatedParams p)
+template <int DK>
+struct GPrepLds {
+    static constexpr int RS = DK + 4;
+    alignas(16) float QT[GC * RS];   // scale e^{g} q
+    alignas(16) float KT[GC * RS];   // k
+    alignas(16) float BK[GC * RS];   // gk + g_gamma (log2 units), then its cumulative sum bk
+    alignas(16) float QF[GC * RS];   // qt 2^{bk - bk_0}  (A's left factor)
+    alignas(16) float KF[GC * RS];   // k 2^{bk_0 - bk}   (A's right factor)
+    int wide;
+};
+
+// One workgroup per (chunk slot, head).  Tin: uint16_t (bf16 bits) or float.
+template <int DK, typename Tin>
+__global__ __launch_bounds__(GTH) void gated_prep(GatedParams p)
 {
-    using LT = GatedLds<DK>;
-    constexpr int RS = LT::RS;
-    constexpr int NE = GC * DK / GTH;   // row elements of q, k and the gates per thread
-    static_assert(NE >= 1 && NE * GTH == GC * DK && DK + GJ <= GTH, "dk in {16, 32, 64, 128}");
-    __shared__ LT L;
+    using PL = GPrep<DK>;
+    constexpr int RS = PL::RS;
+    constexpr int NE = GC * DK / GTH;   // row elements per thread
+    static_assert(NE >= 1 && NE * GTH == GC * DK, "dk in {16, 32, 64, 128}");
+    __shared__ GPrepLds<DK> L;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int lm = lane & 15, lk = lane >> 4;
-    const int r16 = tid >> 4, c16 = tid & 15;
-    const int H = p.H, HKV = p.Hkv, DV = p.dv;
-    // Linear workgroup ids are dealt to the 8 XCDs in turn: the column tiles of
-    // one (sequence, head), which read the same q, k and gate rows, get ids
-    // equal modulo 8, so they run on one XCD and share its L2.  Ids past the
-    // last (sequence, head) (the count is padded to a multiple of 8) exit.
-    const int ntile = DV / GJ;
-    const int xcd = blockIdx.x & 7, qd = blockIdx.x >> 3;
-    const int grp = (qd / ntile) * 8 + xcd;
-    if (grp >= H * p.N) return;
-    const int j0 = (qd % ntile) * GJ, h = grp % H, n = grp / H;
-    const int hk = h / (H / HKV);
+    const int slot = blockIdx.x, h = blockIdx.y;
+    const int H = p.H;
+    const int hk = h / (H / p.Hkv);
+    if (slot >= p.off[p.N]) return;
+    int lo = 0, hi = p.N - 1;   // the last n with off[n] <= slot
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.off[mid] <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
     int t0, t1;
-    if (p.cu) {
-        t0 = min(max(p.cu[n], 0), p.T);
-        t1 = min(max(p.cu[n + 1], t0), p.T);
-    } else {
-        t0 = n * p.T;
-        t1 = t0 + p.T;
-    }
-    const int len = t1 - t0;
-    const int nch = (len + GC - 1) / GC;
-    const size_t soff = ((size_t)n * H + h) * DK;
-    for (int e = tid; e < DK * GJ; e += GTH) {
-        const int i = e / GJ, j = e % GJ;
-        L.ST[j * RS + i] = p.init ? p.init[(soff + i) * DV + j0 + j] : 0.f;
-    }
+    gseq_bounds(p, n, t0, t1);
+    const int len = t1 - t0, c = slot - p.off[n];
+    const int lc = min(GC, len - c * GC);
     const float lg = p.g_gamma ? p.g_gamma[(size_t)min(n, p.g_gamma_rows - 1) * H + h] : 0.f;
     const Tin* q = static_cast<const Tin*>(p.q);
     const Tin* k = static_cast<const Tin*>(p.k);
-    const Tin* v = static_cast<const Tin*>(p.v);
-    // the token of step m of the sequence (m clamped into it: rows past the end
-    // read a valid row and are zeroed where used)
-    auto tok = [&](int m) -> size_t {
-        m = min(m, len - 1);
-        return (size_t)(p.reverse ? t1 - 1 - m : t0 + m);
-    };
-    struct Raw {
-        Tin q[NE], k[NE];
-        float g[NE], gk[NE];
-        Tin v;
-        float gv;
-    };
-    auto load = [&](Raw& R, int c) {
+    // 1. the rows to LDS, zero past the chunk's rows; the gates in log2 units
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + m * GTH;
-            const int r = e / DK, i = e % DK;
-            const size_t t = tok(c * GC + r);
-            R.q[m] = q[(t * H + h) * DK + i];
-            R.k[m] = k[(t * HKV + hk) * DK + i];
-            R.g[m] = p.g ? p.g[(t * H + h) * DK + i] : 0.f;
-            R.gk[m] = p.gk ? p.gk[(t * H + h) * DK + i] : 0.f;
-        }
-        const size_t t = tok(c * GC + r16);
-        R.v = v[(t * HKV + hk) * DV + j0 + c16];
-        R.gv = p.gv ? p.gv[(t * H + h) * DV + j0 + c16] : 0.f;
-    };
-    constexpr int FD = 2;   // chunks in flight ahead
-    Raw ring[FD];
-    if (nch > 0) {
-#pragma unroll
-        for (int u = 0; u < FD; ++u) load(ring[u], min(u, nch - 1));
+    for (int m = 0; m < NE; ++m) {
+        const int e = tid + m * GTH;
+        const int r = e / DK, i = e % DK;
+        const bool in = r < lc;
+        const int mm = c * GC + (in ? r : 0);
+        const size_t t = (size_t)(p.reverse ? t1 - 1 - mm : t0 + mm);
+        const float qv = widen(q[(t * H + h) * DK + i]);
+        const float kv = widen(k[(t * p.Hkv + hk) * DK + i]);
+        const float gq = p.g ? p.g[(t * H + h) * DK + i] : 0.f;
+        const float gkv = p.gk ? p.gk[(t * H + h) * DK + i] : 0.f;
+        L.QT[r * RS + i] = in ? p.scale * __builtin_amdgcn_exp2f(gq * kLog2e) * qv : 0.f;
+        L.KT[r * RS + i] = in ? kv : 0.f;
+        L.BK[r * RS + i] = in ? (gkv + lg) * kLog2e : 0.f;
     }
-    auto chunk = [&](Raw& R, int c) {
-        const int lc = min(GC, len - c * GC);   // rows of this chunk (<= 0: a padding chunk)
-        // 1. the inputs to LDS, zero past the rows
+    if (tid == 0) L.wide = 0;
+    __syncthreads();
+    float* o = p.prep + ((size_t)slot * H + h) * PL::SIZE;
+    // 2. per key channel: the cumulative log-decay down the rows, the read-out
+    // and carry rows (to the block), A's factors when in range
+    if (tid < DK) {
+        const int i = tid;
+        float b[GC];
+        float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + m * GTH;
-            const int r = e / DK, i = e % DK;
-            const bool in = r < lc;
-            // the gates in log2 units from here on
-            L.QT[r * RS + i] = in ? p.scale * __builtin_amdgcn_exp2f(R.g[m] * kLog2e) * to_f32(R.q[m]) : 0.f;
-            L.KT[r * RS + i] = in ? to_f32(R.k[m]) : 0.f;
-            L.BK[r * RS + i] = in ? (R.gk[m] + lg) * kLog2e : 0.f;
+        for (int r = 0; r < GC; ++r) {
+            acc += L.BK[r * RS + i];
+            b[r] = acc;
         }
-        {
-            const bool in = r16 < lc;
-            L.VV[r16][c16] = in ? to_f32(R.v) : 0.f;
-            L.BV[r16][c16] = in ? R.gv * kLog2e : 0.f;
+        o[PL::EKC + i] = __builtin_amdgcn_exp2f(acc);
+        // A = (qt 2^{bk - bk_0}) (k 2^{bk_0 - bk})^T when every such factor stays
+        // inside float32's range (|bk_r - bk_0| <= 120 in log2 units); else A is
+        // formed element by element
+        bool wide = false;
+#pragma unroll
+        for (int r = 0; r < GC; ++r) {
+            const float d = b[r] - b[0];
+            wide |= !(fabsf(d) <= 120.f);
+            const float qt = L.QT[r * RS + i], kt = L.KT[r * RS + i];
+            o[PL::QE + r * RS + i] = qt * __builtin_amdgcn_exp2f(b[r]);
+            o[PL::KC + r * RS + i] = kt * __builtin_amdgcn_exp2f(acc - b[r]);
+            L.QF[r * RS + i] = qt * __builtin_amdgcn_exp2f(d);
+            L.KF[r * RS + i] = kt * __builtin_amdgcn_exp2f(-d);
+            L.BK[r * RS + i] = b[r];
         }
-        if (tid == 0) L.wide = 0;
-        load(R, min(c + FD, nch - 1));   // past the end this reloads the last chunk
-        __syncthreads();
-        // 2. cumulative log-decays and the decay-scaled tiles: a thread per key
-        // channel, a thread per state column
-        if (tid < DK) {
-            const int i = tid;
-            float b[GC];
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 0; r < GC; ++r) {
-                acc += L.BK[r * RS + i];
-                b[r] = acc;
-            }
-            L.EKC[i] = __builtin_amdgcn_exp2f(acc);
-            // A = (qt 2^{bk - bk_0}) (k 2^{bk_0 - bk})^T when every such factor
-            // stays inside float32's range (|bk_r - bk_0| <= 120 in log2 units);
-            // else A is formed element by element
-            bool wide = false;
-#pragma unroll
-            for (int r = 0; r < GC; ++r) {
-                const float d = b[r] - b[0];
-                wide |= !(fabsf(d) <= 120.f);
-                const float qt = L.QT[r * RS + i], kt = L.KT[r * RS + i];
-                L.QE[r * RS + i] = qt * __builtin_amdgcn_exp2f(b[r]);
-                L.KC[r * RS + i] = kt * __builtin_amdgcn_exp2f(acc - b[r]);
-                L.QF[r * RS + i] = qt * __builtin_amdgcn_exp2f(d);
-                L.KF[r * RS + i] = kt * __builtin_amdgcn_exp2f(-d);
-                L.BK[r * RS + i] = b[r];
-            }
-            if (wide) L.wide = 1;
-        } else if (tid < DK + GJ) {
-            const int j = tid - DK;
-            float b[GC];
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 0; r < GC; ++r) {
-                acc += L.BV[r][j];
-                b[r] = acc;
-            }
-            L.EVC[j] = __builtin_amdgcn_exp2f(acc);
-#pragma unroll
-            for (int r = 0; r < GC; ++r) {
-                L.VC[r][j] = L.VV[r][j] * __builtin_amdgcn_exp2f(acc - b[r]);
-                L.BV[r][j] = b[r];
-            }
-        }
-        __syncthreads();
-        // 3. wave 0: the inter-chunk read-out sum_i QE_ri S0_ij on MFMA (lane
-        // group lk supplies channel k0 + 4 lk + u at step u: every channel once);
-        // waves 1-3: A_rs for the 136 pairs s <= r, a thread per pair
+        if (wide) L.wide = 1;
+    }
+    __syncthreads();
+    // 3. A: wave 0 on MFMA (lane (lm, lk) supplies channel k0 + 4 lk + u of row
+    // lm of both factors at step u), or element by element, a thread per entry
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lm = lane & 15, lk = lane >> 4;
+    if (!L.wide) {
         if (wave == 0) {
             gf32x4_t acc = gf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
             for (int k0 = 0; k0 < DK; k0 += 16) {
-                const float4 xa = *reinterpret_cast<const float4*>(L.QE + lm * RS + k0 + 4 * lk);
-                const float4 xb = *reinterpret_cast<const float4*>(L.ST + lm * RS + k0 + 4 * lk);
+                const float4 xa = *reinterpret_cast<const float4*>(L.QF + lm * RS + k0 + 4 * lk);
+                const float4 xb = *reinterpret_cast<const float4*>(L.KF + lm * RS + k0 + 4 * lk);
                 acc = gmfma4(xa.x, xb.x, acc);
                 acc = gmfma4(xa.y, xb.y, acc);
                 acc = gmfma4(xa.z, xb.z, acc);
                 acc = gmfma4(xa.w, xb.w, acc);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.OI[4 * lk + e][lm] = acc[e];
-        } else if (!L.wide) {
-            if (wave == 1) {
-                gf32x4_t acc = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e;
+                o[PL::AM + r * GC + lm] = lm <= r ? acc[e] : 0.f;   // the masked pairs may be out of range
+            }
+        }
+    } else {
+        const int r = tid >> 4, s2 = tid & 15;
+        float a = 0.f;
+        if (s2 <= r) {
 #pragma unroll 4
-                for (int k0 = 0; k0 < DK; k0 += 16) {
-                    const float4 xa = *reinterpret_cast<const float4*>(L.QF + lm * RS + k0 + 4 * lk);
-                    const float4 xb = *reinterpret_cast<const float4*>(L.KF + lm * RS + k0 + 4 * lk);
-                    acc = gmfma4(xa.x, xb.x, acc);
-                    acc = gmfma4(xa.y, xb.y, acc);
-                    acc = gmfma4(xa.z, xb.z, acc);
-                    acc = gmfma4(xa.w, xb.w, acc);
-                }
+            for (int i = 0; i < DK; i += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(L.QT + r * RS + i);
+                const float4 y = *reinterpret_cast<const float4*>(L.KT + s2 * RS + i);
+                const float4 br = *reinterpret_cast<const float4*>(L.BK + r * RS + i);
+                const float4 bs = *reinterpret_cast<const float4*>(L.BK + s2 * RS + i);
+                a = fmaf(x.x * y.x, __builtin_amdgcn_exp2f(br.x - bs.x), a);
+                a = fmaf(x.y * y.y, __builtin_amdgcn_exp2f(br.y - bs.y), a);
+                a = fmaf(x.z * y.z, __builtin_amdgcn_exp2f(br.z - bs.z), a);
+                a = fmaf(x.w * y.w, __builtin_amdgcn_exp2f(br.w - bs.w), a);
+            }
+        }
+        o[PL::AM + tid] = a;
+    }
+}
+
+typedef float gf4v __attribute__((ext_vector_type(4)));
+
+// The chunk's operand block, 16 bytes per thread and step: every thread
+// issues the same loads and stores (an index past the block is clamped to its
+// last piece), so the count of memory operations in flight is the same on
+// every path and the waits for a load issued chunks earlier stay exact.
+template <int NP, int N4>
+__device__ __forceinline__ void gfetch_block(gf4v (&pf)[NP], const float* src)
+{
+    const gf4v* s4 = reinterpret_cast<const gf4v*>(src);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * lk + e;
-                    L.AM[r][lm] = lm <= r ? acc[e] : 0.f;   // the masked pairs may be out of range
+    for (int m = 0; m < NP; ++m) pf[m] = s4[min((int)threadIdx.x + m * GTH, N4 - 1)];
+}
+
+template <int NP, int N4>
+__device__ __forceinline__ void gstore_block(float* dst, const gf4v (&pf)[NP])
+{
+#pragma unroll
+    for (int m = 0; m < NP; ++m) reinterpret_cast<gf4v*>(dst)[min((int)threadIdx.x + m * GTH, N4 - 1)] = pf[m];
+}
+
+template <int DK>
+struct GScanLds {
+    alignas(16) float P[2][GPrep<DK>::SIZE];
+    float X[2][GC][GJ + 1];    // v of the tile
+    float GV[2][GC][GJ + 1];   // gv of the tile (log2 units)
+    float PU[GNW][GC][GJ + 1];
+    float VC[GC][GJ + 1];      // e^{bv_C - bv} v
+    float VF[GC][GJ + 1];      // e^{bv_0 - bv} v
+    float ER[GC][GJ + 1];      // e^{bv}
+    float EL[GC][GJ + 1];      // e^{bv - bv_0}
+    float EVC[GJ];             // e^{bv_C}
+    int vwide;                 // some column's value log-decay leaves the factor range
+};
+
+// One workgroup per (16 state columns, head, sequence); ids dealt so that the
+// column tiles of one (sequence, head), which read the same blocks, share an
+// XCD (ids equal modulo 8).
+template <int DK, typename Tin, typename Tout>
+__global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void gated_scan(GatedParams p)
+{
+    using PL = GPrep<DK>;
+    constexpr int RS = PL::RS;
+    constexpr int NT = DK / 16, TPW = (NT + GNW - 1) / GNW;
+    constexpr int N4 = PL::SIZE / 4, NP = (N4 + GTH - 1) / GTH;
+    __shared__ GScanLds<DK> L;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lm = lane & 15, lk = lane >> 4;
+    const int H = p.H, DV = p.dv;
+    const int ntile = DV / GJ;
+    const int xcd = blockIdx.x & 7, qd = blockIdx.x >> 3;
+    const int grp = (qd / ntile) * 8 + xcd;
+    if (grp >= H * p.N) return;
+    const int j0 = (qd % ntile) * GJ, h = grp % H, n = grp / H;
+    const int hk = h / (H / p.Hkv);
+    int t0, t1;
+    gseq_bounds(p, n, t0, t1);
+    const int len = t1 - t0;
+    const int nch = min((len + GC - 1) / GC, p.off[n + 1] - p.off[n]);
+    const int slot0 = p.off[n];
+    const size_t soff = ((size_t)n * H + h) * DK;
+    const bool hv = p.gv != nullptr;
+    gf32x4_t S[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        const int t = wave + GNW * x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * t + 4 * lk + e;
+            S[x][e] = (t < NT && p.init) ? p.init[(soff + i) * DV + j0 + lm] : 0.f;
+        }
+    }
+    // the initial tile is used here, before the loop: else its loads stay
+    // pending into the loop body, whose first use would wait for every load in
+    // flight, the prefetched chunks' included
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) asm volatile("" : "+v"(S[x]));
+    const Tin* vv = static_cast<const Tin*>(p.v);
+    const int rr = tid / GJ, jj = tid % GJ;
+    auto tok = [&](int m) -> size_t {
+        m = min(m, len - 1);
+        return (size_t)(p.reverse ? t1 - 1 - m : t0 + m);
+    };
+    // a ring of two register sets: the inputs of chunk c + 2 are loaded while
+    // chunk c computes (the loop is unrolled by two, so each set is fixed)
+    gf4v pfa[NP], pfb[NP];
+    Tin pva = 0, pvb = 0;
+    float pga = 0.f, pgb = 0.f;
+    auto fetch = [&](gf4v (&pf)[NP], Tin& pv, float& pg, int c) __attribute__((always_inline)) {
+        gfetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
+        const size_t t = tok(c * GC + rr);
+        pv = vv[(t * p.Hkv + hk) * DV + j0 + jj];
+        pg = hv ? p.gv[(t * H + h) * DV + j0 + jj] : 0.f;
+    };
+    if (nch > 0) {
+        fetch(pfa, pva, pga, 0);
+        fetch(pfb, pvb, pgb, min(1, nch - 1));
+    }
+    auto chunk = [&](gf4v (&pf)[NP], Tin& pv, float& pg, int c, auto bsel) __attribute__((always_inline)) {
+        constexpr int b = decltype(bsel)::value;
+        const float* P = L.P[b];
+        const int lc = min(GC, len - c * GC);
+        gstore_block<NP, N4>(L.P[b], pf);
+        L.X[b][rr][jj] = rr < lc ? widen(pv) : 0.f;
+        L.GV[b][rr][jj] = rr < lc ? pg * kLog2e : 0.f;
+        if (tid == 0) L.vwide = 0;
+        fetch(pf, pv, pg, min(c + 2, nch - 1));   // past the end: the last chunk again
+        lds_barrier();
+        // the inter-chunk read-out sum_i QE_ri S_ij: each wave its tiles' part
+        {
+            gf32x4_t acc = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + GNW * x;
+                if (t < NT) {
+                    const float4 a = *reinterpret_cast<const float4*>(P + PL::QE + lm * RS + 16 * t + 4 * lk);
+                    acc = gmfma4(a.x, S[x][0], acc);
+                    acc = gmfma4(a.y, S[x][1], acc);
+                    acc = gmfma4(a.z, S[x][2], acc);
+                    acc = gmfma4(a.w, S[x][3], acc);
                 }
             }
-        } else {
-            const int pr = tid - 64;
-            if (pr < GC * (GC + 1) / 2) {
-                int r = 0;
-                while ((r + 1) * (r + 2) / 2 <= pr) ++r;
-                const int s = pr - r * (r + 1) / 2;
-                float a = 0.f;
-#pragma unroll 4
-                for (int i = 0; i < DK; i += 4) {
-                    const float4 x = *reinterpret_cast<const float4*>(L.QT + r * RS + i);
-                    const float4 y = *reinterpret_cast<const float4*>(L.KT + s * RS + i);
-                    const float4 br = *reinterpret_cast<const float4*>(L.BK + r * RS + i);
-                    const float4 bs = *reinterpret_cast<const float4*>(L.BK + s * RS + i);
-                    a = fmaf(x.x * y.x, __builtin_amdgcn_exp2f(br.x - bs.x), a);
-                    a = fmaf(x.y * y.y, __builtin_amdgcn_exp2f(br.y - bs.y), a);
-                    a = fmaf(x.z * y.z, __builtin_amdgcn_exp2f(br.z - bs.z), a);
-                    a = fmaf(x.w * y.w, __builtin_amdgcn_exp2f(br.w - bs.w), a);
-                }
-                L.AM[r][s] = a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
+        }
+        // the value-axis factors, a thread per (row rr, column jj): the column's
+        // cumulative log-decay to row rr and over the chunk
+        if (hv) {
+            float bc = 0.f, br = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < GC; ++s2) {
+                bc += L.GV[b][s2][jj];
+                if (s2 == rr) br = bc;
             }
+            const float b0 = L.GV[b][0][jj];
+            const float x = L.X[b][rr][jj];
+            L.VC[rr][jj] = x * __builtin_amdgcn_exp2f(bc - br);
+            L.ER[rr][jj] = __builtin_amdgcn_exp2f(br);
+            L.VF[rr][jj] = x * __builtin_amdgcn_exp2f(b0 - br);
+            L.EL[rr][jj] = __builtin_amdgcn_exp2f(br - b0);
+            if (!(fabsf(br - b0) <= 120.f)) L.vwide = 1;
+            if (rr == GC - 1) L.EVC[jj] = __builtin_amdgcn_exp2f(bc);
         }
-        __syncthreads();
-        // 4. the outputs: thread (row r16, column c16)
-        if (r16 < lc) {
-            const int r = r16, j = c16;
-            const float bvr = L.BV[r][j];
-            float o = __builtin_amdgcn_exp2f(bvr) * L.OI[r][j];
-            for (int s = 0; s <= r; ++s)
-                o = fmaf(L.AM[r][s] * __builtin_amdgcn_exp2f(bvr - L.BV[s][j]), L.VV[s][j], o);
-            const size_t t = tok(c * GC + r);
-            static_cast<Tout*>(p.o)[(t * H + h) * DV + j0 + j] = from_f32<Tout>(o);
-        }
-        // 5. the state update on MFMA: rows [16 tt, +16) of the tile per step,
-        // S1 = e^{bk_C + bv_C} S0 + Kc^T Vc (K = the 16 rows)
-        for (int tt = wave; tt < DK / 16; tt += 4) {
-            const int i0 = 16 * tt;
-            gf32x4_t acc;
+        lds_barrier();
+        // the outputs (wave 0): O = e^{bv} (QE S) + e^{bv - bv_0} A (e^{bv_0 - bv} v),
+        // the second product on MFMA (lane (lm, lk) supplies A[lm][4 lk + u] and
+        // the scaled v[4 lk + u][lm] at step u); element by element when wide
+        if (wave == 0) {
+            gf32x4_t ai = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+            const bool ew = hv && L.vwide;
+            if (!ew) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s2 = 4 * lk + u;
+                    ai = gmfma4(P[PL::AM + lm * GC + s2], hv ? L.VF[s2][lm] : L.X[b][s2][lm], ai);
+                }
+            }
+            float bvs[GC];
+            if (ew) {
+                float acc = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < GC; ++s2) {
+                    acc += L.GV[b][s2][lm];
+                    bvs[s2] = acc;
+                }
+            }
+            // rows 4 lk + e of column lm; rows past the chunk fall outside the
+            // store's range: forward order from the chunk's first token, reverse
+            // order from its last one backwards
+            const int tb = p.reverse ? t1 - c * GC - lc : t0 + c * GC;
+            Tout* ob = static_cast<Tout*>(p.o) + ((size_t)tb * H + h) * DV + j0;
+            const int range = ((lc - 1) * H * DV + GJ) * (int)sizeof(Tout);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ob, 0, range, 0x00020000);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = i0 + 4 * lk + e;
-                acc[e] = L.EKC[i] * L.EVC[lm] * L.ST[lm * RS + i];
+                const int r = 4 * lk + e;
+                const float oi = (L.PU[0][r][lm] + L.PU[1][r][lm]) + (L.PU[2][r][lm] + L.PU[3][r][lm]);
+                float o;
+                if (!hv) {
+                    o = oi + ai[e];
+                } else if (!ew) {
+                    o = L.ER[r][lm] * oi + L.EL[r][lm] * ai[e];
+                } else {
+                    o = L.ER[r][lm] * oi;
+                    for (int s2 = 0; s2 <= r; ++s2)
+                        o = fmaf(P[PL::AM + r * GC + s2] * __builtin_amdgcn_exp2f(bvs[r] - bvs[s2]), L.X[b][s2][lm], o);
+                }
+                const int trow = p.reverse ? lc - 1 - r : r;   // negative past the chunk: out of range
+                const int boff = (trow * H * DV + lm) * (int)sizeof(Tout);
+                const Tout ov = from_f32<Tout>(o);
+                if constexpr (sizeof(Tout) == 4)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), rs, boff, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, ov), rs, boff, 0, 0);
             }
-#pragma unroll
-            for (int s0 = 0; s0 < GC; s0 += 4)
-                acc = gmfma4(L.KC[(s0 + lk) * RS + i0 + lm], L.VC[s0 + lk][lm], acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) L.ST[lm * RS + i0 + 4 * lk + e] = acc[e];
         }
-        __syncthreads();
-    };
-    // unrolled by the ring depth so that every ring slot is a fixed set of registers
-    for (int cb = 0; cb < nch; cb += FD) {
+        // the state update: S <- e^{bk_C + bv_C} S + Kc^T (e^{bv_C - bv} v)
 #pragma unroll
-        for (int u = 0; u < FD; ++u)
-            if (cb + u < nch) chunk(ring[u], cb + u);
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + GNW * x;
+            if (t < NT) {
+                gf32x4_t a = S[x];
+                const float evc = hv ? L.EVC[lm] : 1.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] *= P[PL::EKC + 16 * t + 4 * lk + e] * evc;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s2 = 4 * lk + u;
+                    a = gmfma4(P[PL::KC + s2 * RS + 16 * t + lm], hv ? L.VC[s2][lm] : L.X[b][s2][lm], a);
+                }
+                S[x] = a;
+            }
+        }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        chunk(pfa, pva, pga, c, std::integral_constant<int, 0>{});
+        if (c + 1 < nch) chunk(pfb, pvb, pgb, c + 1, std::integral_constant<int, 1>{});
     }
-    __syncthreads();
     if (p.final_state) {
-        for (int e = tid; e < DK * GJ; e += GTH) {
-            const int i = e / GJ, j = e % GJ;
-            p.final_state[(soff + i) * DV + j0 + j] = L.ST[j * RS + i];
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + GNW * x;
+            if (t < NT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * t + 4 * lk + e;
+                    p.final_state[(soff + i) * DV + j0 + lm] = S[x][e];
+                }
+            }
         }
     }
 }
 
-template <int DK, typename Tin, typename Tout>
-hipError_t launch_chunk(const GatedParams& p, hipStream_t st)
+size_t galign(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t gslots(int N, int T, bool packed)
 {
+    if (packed) return (size_t)(T / GC) + (size_t)N;
+    return (size_t)N * (size_t)((T + GC - 1) / GC);
+}
+
+template <int DK, typename Tin, typename Tout>
+hipError_t launch_typed(const GatedParams& p, size_t slots, hipStream_t st)
+{
+    if (slots > 0) {
+        hipLaunchKernelGGL((gated_prep<DK, Tin>), dim3((unsigned)slots, (unsigned)p.H), dim3(GTH), 0, st, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const unsigned groups8 = (unsigned)((p.H * p.N + 7) / 8 * 8);
     if (groups8 == 0) return hipSuccess;
-    const dim3 grid(groups8 * (unsigned)(p.dv / GJ));
-    hipLaunchKernelGGL((gated_chunk_kernel<DK, Tin, Tout>), grid, dim3(GTH), 0, st, p);
+    hipLaunchKernelGGL((gated_scan<DK, Tin, Tout>), dim3(groups8 * (unsigned)(p.dv / GJ)), dim3(GTH), 0, st, p);
     return hipGetLastError();
 }
 
 template <int DK>
-hipError_t launch_dk(const GatedParams& p, hipStream_t st)
+hipError_t launch_dk(const GatedParams& p, size_t slots, bool in_bf16, bool out_bf16, hipStream_t st)
 {
-    if (!p.in_bf16) return launch_chunk<DK, float, float>(p, st);
-    if (p.out_bf16) return launch_chunk<DK, bf16_t, bf16_t>(p, st);
-    return launch_chunk<DK, bf16_t, float>(p, st);
+    if (!in_bf16) return launch_typed<DK, float, float>(p, slots, st);
+    if (out_bf16) return launch_typed<DK, uint16_t, bf16_t>(p, slots, st);
+    return launch_typed<DK, uint16_t, float>(p, slots, st);
 }
 
 }  // namespace
 
+size_t gated_workspace_bytes(int N, int T, int H, int dk, bool packed)
+{
+    const size_t slots = (N > 0 && T > 0) ? gslots(N, T, packed) : 0;
+    return galign((size_t)(N + 1) * 4) + galign(slots * H * gprep_floats(dk) * 4);
+}
+
 hipError_t launch_gated(const GatedArgs& a, hipStream_t st)
 {
+    const bool packed = a.cu != nullptr;
+    const size_t slots = (a.N > 0 && a.T > 0) ? gslots(a.N, a.T, packed) : 0;
     GatedParams p{};
-    p.q = a.q; p.k = a.k; p.v = a.v; p.in_bf16 = a.in_bf16;
+    p.q = a.q; p.k = a.k; p.v = a.v;
     p.g = a.g; p.g_gamma = a.g_gamma; p.g_gamma_rows = a.g_gamma_rows; p.gk = a.gk; p.gv = a.gv;
     p.init = a.init; p.cu = a.cu;
     p.N = a.N; p.T = a.T; p.H = a.H; p.Hkv = a.Hkv; p.dv = a.dv;
     p.scale = a.scale; p.reverse = a.reverse;
-    p.o = a.o; p.out_bf16 = a.out_bf16; p.final_state = a.final_state;
+    p.o = a.o; p.final_state = a.final_state;
+    unsigned char* w = static_cast<unsigned char*>(a.workspace);
+    int32_t* off = reinterpret_cast<int32_t*>(w);
+    p.off = off;
+    p.prep = reinterpret_cast<float*>(w + galign((size_t)(a.N + 1) * 4));
+    hipLaunchKernelGGL(gated_plan_kernel, dim3(1), dim3(64), 0, st, p, (int)slots, off);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     switch (a.dk) {
-    case 16: return launch_dk<16>(p, st);
-    case 32: return launch_dk<32>(p, st);
-    case 64: return launch_dk<64>(p, st);
-    default: return launch_dk<128>(p, st);
+    case 16: return launch_dk<16>(p, slots, a.in_bf16 != 0, a.out_bf16 != 0, st);
+    case 32: return launch_dk<32>(p, slots, a.in_bf16 != 0, a.out_bf16 != 0, st);
+    case 64: return launch_dk<64>(p, slots, a.in_bf16 != 0, a.out_bf16 != 0, st);
+    default: return launch_dk<128>(p, slots, a.in_bf16 != 0, a.out_bf16 != 0, st);
     }
 }
 

@@ -100,6 +100,7 @@ struct GatedArgs {
     void* o;
     int out_bf16;
     float* final_state;
+    void* workspace;   // gated_workspace_bytes(N, T, H, dk, packed) bytes
 };
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
@@ -126,6 +127,7 @@ hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
 // the gated recurrent attention (kda_gated.hip)
 hipError_t launch_gated(const GatedArgs& a, hipStream_t stream);
+size_t gated_workspace_bytes(int N, int T, int H, int dk, bool packed);
 // the prefill backward (kda_backward.hip)
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bool packed);

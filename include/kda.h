@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -227,15 +227,24 @@ kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, k
  * (initial NULL = zeros; final NULL = not returned); o [B, T, H, dv]
  * (out_dtype; bf16 needs bf16 input).  scale <= 0 or NaN selects 1/sqrt(dk).
  * Grouped heads, cu_seqlens and num_seqs as for kda_prefill.  dk, dv in
- * {16, 32, 64, 128}.  One float32 kernel (token by token, the state in
- * registers) serves every case.
+ * {16, 32, 64, 128}.  Computed in float32 in chunks of 16 tokens (an exact
+ * regrouping of the token loop): the chunks' key-axis operands are formed
+ * in parallel into the workspace, then each (sequence, head, 16 state
+ * columns) walks its chunks in order.  The workspace
+ * (kda_recurrent_attention_workspace_bytes, caller-owned, device memory,
+ * not to be shared by calls that may run concurrently) holds about
+ * 18.4 KiB per 16-token chunk and head at dk = 128; a smaller one gives
+ * KDA_EINVAL.
  */
+size_t kda_recurrent_attention_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t dk,
+                                               int32_t dv);
 kda_status_t kda_recurrent_attention(const void* q, const void* k, const void* v, kda_dtype_t in_dtype,
                                      const float* g, const float* g_gamma, const float* gk, const float* gv,
                                      const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
                                      int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t dk, int32_t dv,
                                      float scale, int32_t reverse, void* o, kda_dtype_t out_dtype,
-                                     float* final_state, void* stream);
+                                     float* final_state, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * kda_decode_step - advance the recurrence by exactly one token for each of

@@ -255,3 +255,44 @@ def test_backward_workspace_bytes():
     assert L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 2, 128, 128) > need   # grouped: per-head dk, dv
     assert L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 0, 48, 128) == 0
     assert _backward(lower_bound=-6.0, flags=kda.EJK | kda.QK_L2NORM, B=0) == kda.KDA_OK   # EJK: no bound
+
+
+def _gated(**over):
+    a = dict(q=P, k=P, v=P, in_dtype=kda.BF16, g=None, g_gamma=None, gk=P, gv=None, init=None, cu=None,
+             num_seqs=0, B=2, T=64, H=4, Hkv=0, dk=128, dv=128, scale=-1.0, reverse=0, o=P,
+             out_dtype=kda.BF16, fs=None, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return kda.lib().kda_recurrent_attention(
+        a["q"], a["k"], a["v"], a["in_dtype"], a["g"], a["g_gamma"], a["gk"], a["gv"], a["init"], a["cu"],
+        a["num_seqs"], a["B"], a["T"], a["H"], a["Hkv"], a["dk"], a["dv"], a["scale"], a["reverse"], a["o"],
+        a["out_dtype"], a["fs"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+GATED_ERRORS = [
+    (dict(reverse=2), kda.KDA_EINVAL, "reverse"),
+    (dict(o=None), kda.KDA_EINVAL, "required"),
+    (dict(Hkv=3), kda.KDA_EINVAL, "must divide H"),
+    (dict(dk=48), kda.KDA_EUNSUPPORTED, "dk and dv"),
+    (dict(in_dtype=kda.F32), kda.KDA_EUNSUPPORTED, "bf16 output needs bf16 input"),
+    (dict(ws=None), kda.KDA_EINVAL, "workspace"),
+    (dict(ws=P, ws_bytes=1024), kda.KDA_EINVAL, "workspace"),
+]
+
+
+@pytest.mark.parametrize("over,status,msg", GATED_ERRORS, ids=[str(i) for i in range(len(GATED_ERRORS))])
+def test_gated_rejects_before_any_hip_call(over, status, msg):
+    assert _gated(**over) == status
+    assert msg in kda.lib().kda_last_error().decode()
+
+
+def test_gated_workspace_bytes():
+    L = kda.lib()
+    # dense B2 T64 H4 dk128: 8 chunk slots x 4 heads x (the read-out and carry
+    # rows [16][132], A [16][16], e^{bk_C} [128] floats), plus the offsets
+    need = L.kda_recurrent_attention_workspace_bytes(0, 2, 64, 4, 128, 128)
+    assert need >= 8 * 4 * (2 * 16 * 132 + 256 + 128) * 4
+    # packed: T / 16 + N slots
+    assert L.kda_recurrent_attention_workspace_bytes(3, 1, 64, 4, 128, 128) >= (4 + 3) * 4 * (2 * 16 * 132 + 384) * 4
+    assert L.kda_recurrent_attention_workspace_bytes(0, 2, 64, 4, 48, 128) == 0
+    assert L.kda_recurrent_attention_workspace_bytes(0, 2, 0, 4, 128, 128) <= 256   # no chunks: offsets only
+    assert _gated(B=0) == kda.KDA_OK
