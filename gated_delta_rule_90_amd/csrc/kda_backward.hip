@@ -174,14 +174,14 @@ struct ChunkLds {
     __device__ float kc(int r, int i) const { return kh[r][i] * ecbr(r, i); }
 };
 
-// Rows [c0, c0 + nr) of head h (nr <= 16); rows past nr are neutral
-// (q = k = 0, gamma = 0, beta = 0).  Ends with a barrier.
-// The cumulative log-decays are formed in log2 units (the gate times log2 e)
-// and the factors with exp2; products such as Qg * dQg, from which the
-// gradients are built, do not depend on the unit.
-// Steps 2-4 of the set-up, once the raw rows (qh, kh), the gate activations
-// (KDA: eb, log2 units), beta and the EJK gates (sb, log2 units) are in LDS.
-// Begins and ends with a barrier.
+
+// Steps 2-4 of a chunk's set-up (step 1, the rows into LDS, is the caller's),
+// once the raw rows (qh, kh), the gate activations (KDA: eb, log2 units),
+// beta and the EJK gates (sb, log2 units) are in LDS; rows past the chunk's
+// end are neutral (q = k = 0, gamma = 0, beta = 0).  The cumulative
+// log-decays are formed in log2 units and the factors with exp2; products
+// such as Qg * dQg, from which the gradients are built, do not depend on the
+// unit.  Begins and ends with a barrier.
 template <int DK, bool EJK>
 __device__ void setup_rest(ChunkLds<DK, EJK>& L, const BwdParams& p)
 {
@@ -291,56 +291,6 @@ __device__ void setup_rest(ChunkLds<DK, EJK>& L, const BwdParams& p)
     lds_barrier();
 }
 
-template <int DK, bool EJK>
-__device__ void chunk_setup(ChunkLds<DK, EJK>& L, const BwdParams& p, int c0, int nr, int h, int hk)
-{
-    const int tid = threadIdx.x;
-    const int H = p.H, Hkv = p.Hkv;
-    const float ea = EJK ? 0.f : expf(p.a_log[h]);
-    const float lb2 = p.lb * kLog2e;
-    constexpr int NE = BC * DK / BT;   // row elements per thread (1 .. 8)
-    // 1. rows to LDS (a branch per input dtype outside the loop, so the loads
-    // of a thread go out together), gate activations in log2 units
-    auto load_rows = [&](auto bf) {
-        using T = std::conditional_t<decltype(bf)::value, uint16_t, float>;
-        const T* qq = static_cast<const T*>(p.q);
-        const T* kk = static_cast<const T*>(p.k);
-        auto f = [](T x) {
-            if constexpr (decltype(bf)::value) return __uint_as_float((uint32_t)x << 16);
-            else return x;
-        };
-#pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + m * BT;
-            const int r = e / DK, i = e % DK;
-            const bool valid = r < nr;
-            const size_t tok = (size_t)(c0 + (valid ? r : 0));
-            const float qv = f(qq[(tok * H + h) * DK + i]);
-            const float kv = f(kk[(tok * Hkv + hk) * DK + i]);
-            L.qh[r][i] = valid ? qv : 0.f;
-            L.kh[r][i] = valid ? kv : 0.f;
-            if (!EJK) {
-                const float x = ea * (p.g[(tok * H + h) * DK + i] + (p.dt_bias ? p.dt_bias[(size_t)i * H + h] : 0.f));
-                L.eb[r][i] = valid ? lb2 * sigmoid_f(x) : 0.f;
-            }
-        }
-    };
-    if (p.in_bf16) load_rows(std::true_type{});
-    else load_rows(std::false_type{});
-    if (tid < BC) {
-        const int r = tid;
-        const bool valid = r < nr;
-        const size_t tok = (size_t)(c0 + (valid ? r : 0));
-        if (EJK) {
-            L.beta[r] = valid ? p.beta[tok * H + h] : 0.f;
-            L.sb[r] = (valid && p.g) ? p.g[tok * H + h] * kLog2e : 0.f;
-        } else {
-            L.beta[r] = valid ? sigmoid_f(p.beta[tok * H + h]) : 0.f;
-        }
-    }
-    setup_rest<DK, EJK>(L, p);
-}
-
 // ---------------------------------------------------------------------------
 // The column-independent operands of one chunk, formed once per (chunk, head)
 // by bwd_prep for the two state scans (each of which runs per 16 state
@@ -384,48 +334,197 @@ __device__ __forceinline__ void slot_rows(const BwdParams& p, int slot, int& n, 
     nr = min(BC, t1 - c0);
 }
 
+// LDS of bwd_prep: the rows as loaded, then the decayed operands in place.
 template <int DK, bool EJK>
+struct PrepLds {
+    static constexpr int RS = DK + 4;
+    alignas(16) float QG[BC * RS];   // raw q, then Qg (EJK: qh)
+    alignas(16) float KG[BC * RS];   // raw k, then Kg (EJK: kh)
+    alignas(16) float KI[BC * RS];   // KDA: gate activations (log2 units), then kh e^{-b}
+    float GA[BC][BC + 1];
+    float NQ[BC], NK[BC], BE[BC];
+    float SB[BC], SBC[BC], SBP[BC];  // EJK: gates (log2), b, b'
+};
+
+// One workgroup per (chunk slot, head): the operand block of the chunk (see
+// PrepLayout).  Tin: uint16_t (bf16 bits) or float.
+template <int DK, bool EJK, typename Tin>
 __global__ __launch_bounds__(BT) void bwd_prep(BwdParams p)
 {
     using PL = PrepLayout<DK>;
-    __shared__ ChunkLds<DK, EJK> L;
+    using LT = PrepLds<DK, EJK>;
+    constexpr int RS = LT::RS;
+    static_assert(RS == PL::RS, "row strides");
+    constexpr int NE = BC * DK / BT;   // row elements per thread
+    __shared__ LT L;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lm = lane & 15, lk = lane >> 4;
     const int slot = blockIdx.x, h = blockIdx.y;
-    const int hk = h / (p.H / p.Hkv);
+    const int H = p.H, Hkv = p.Hkv;
+    const int hk = h / (H / Hkv);
     if (slot >= p.off[p.N]) return;
     int n, c0, nr;
     slot_rows(p, slot, n, c0, nr);
-    chunk_setup<DK, EJK>(L, p, c0, nr, h, hk);
-    float* o = p.prep + ((size_t)slot * p.H + h) * PL::SIZE;
-    for (int e = tid; e < BC * DK; e += BT) {
-        const int r = e / DK, i = e % DK;
-        const float qh = L.qh[r][i], kh = L.kh[r][i];
-        o[PL::QG + r * PL::RS + i] = EJK ? qh : qh * L.eb[r][i];
-        o[PL::KG + r * PL::RS + i] = EJK ? kh : kh * L.eb[r][i];
-        if (!EJK) o[PL::KC + r * PL::RS + i] = kh * L.ecb[r][i];
+    float* o = p.prep + ((size_t)slot * H + h) * PL::SIZE;
+    // 1. the rows to LDS (rows past nr neutral), gate activations in log2 units
+    {
+        const float ea = EJK ? 0.f : expf(p.a_log[h]);
+        const float lb2 = p.lb * kLog2e;
+        const float dtb = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
+        const Tin* qq = static_cast<const Tin*>(p.q);
+        const Tin* kk = static_cast<const Tin*>(p.k);
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / DK, i = e % DK;
+            const bool ok = r < nr;
+            const size_t tok = (size_t)(c0 + (ok ? r : 0));
+            const float qv = widen(qq[(tok * H + h) * DK + i]);
+            const float kv = widen(kk[(tok * Hkv + hk) * DK + i]);
+            L.QG[r * RS + i] = ok ? qv : 0.f;
+            L.KG[r * RS + i] = ok ? kv : 0.f;
+            if (!EJK) {
+                const float x = ea * (p.g[(tok * H + h) * DK + i] + dtb);
+                L.KI[r * RS + i] = ok ? lb2 * sigmoid_f(x) : 0.f;
+            }
+        }
+        if (tid < BC) {
+            const bool ok = tid < nr;
+            const size_t tok = (size_t)(c0 + (ok ? tid : 0));
+            const float bl = p.beta[tok * H + h];
+            L.BE[tid] = ok ? (EJK ? bl : sigmoid_f(bl)) : 0.f;
+            if (EJK) L.SB[tid] = (ok && p.g) ? p.g[tok * H + h] * kLog2e : 0.f;
+        }
     }
-    o[PL::GP + tid] = L.GP[tid >> 4][tid & 15];
+    __syncthreads();
+    // 2. row scales (eight lanes per row, summed by DPP / swizzle); EJK: the
+    // scalar cumulative decays, each of 16 lanes summing in row order; KDA:
+    // every thread reads its channel's 16 gates (its rows are rewritten below)
+    {
+        const int pr = tid >> 3, part = tid & 7;
+        const int r = pr & 15;
+        const float* row = (pr < 16 ? L.QG : L.KG) + r * RS;
+        float ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < DK / 8; ++m) ss = fmaf(row[part + 8 * m], row[part + 8 * m], ss);
+        ss = xor_add<1>(ss);
+        ss = xor_add<2>(ss);
+        ss = xor_add<4>(ss);
+        if (part == 0) {
+            const float rn = p.l2norm ? 1.f / sqrtf(ss + kNormEps) : 1.f;
+            if (pr < 16) L.NQ[r] = p.scale * rn;
+            else L.NK[r] = rn;
+        }
+    }
+    if (EJK && tid >= BT - BC) {
+        const int r = tid - (BT - BC);
+        float acc = 0.f, b = 0.f, bp = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < BC; ++s2) {
+            if (s2 == r) bp = acc;
+            acc += L.SB[s2];
+            if (s2 == r) b = acc;
+        }
+        L.SBC[r] = b;
+        L.SBP[r] = bp;
+        o[PL::RF + r] = __builtin_amdgcn_exp2f(b);
+        o[PL::RF + BC + r] = __builtin_amdgcn_exp2f(bp);
+        o[PL::RF + 2 * BC + r] = __builtin_amdgcn_exp2f(acc - b);
+        o[PL::RF + 3 * BC + r] = __builtin_amdgcn_exp2f(acc);
+    }
+    constexpr int NPRT = BT / DK, RP = BC / NPRT;   // KDA: parts per channel, rows per part
+    float gcol[EJK ? 1 : BC];
+    if (!EJK) {
+#pragma unroll
+        for (int s2 = 0; s2 < BC; ++s2) gcol[s2] = L.KI[s2 * RS + tid % DK];
+    }
+    __syncthreads();
+    // 3. the normalised, decayed rows: in LDS for the Gram products and, for
+    // the thread's own rows, to the block
+    if constexpr (!EJK) {
+        const int i = tid % DK, part = tid / DK;
+        float bo[RP];
+        float b = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < BC; ++s2) {
+            b += gcol[s2];
+#pragma unroll
+            for (int x = 0; x < RP; ++x)
+                if (s2 == part * RP + x) bo[x] = b;
+        }
+        if (part == 0) o[PL::EC + i] = __builtin_amdgcn_exp2f(b);
+#pragma unroll
+        for (int x = 0; x < RP; ++x) {
+            const int r = part * RP + x;
+            const float qn = L.QG[r * RS + i] * L.NQ[r];
+            const float kn = L.KG[r * RS + i] * L.NK[r];
+            const float f = __builtin_amdgcn_exp2f(bo[x]);
+            const float qg = qn * f, kg = kn * f;
+            L.QG[r * RS + i] = qg;
+            L.KG[r * RS + i] = kg;
+            L.KI[r * RS + i] = kn * __builtin_amdgcn_exp2f(-bo[x]);
+            o[PL::QG + r * RS + i] = qg;
+            o[PL::KG + r * RS + i] = kg;
+            o[PL::KC + r * RS + i] = kn * __builtin_amdgcn_exp2f(b - bo[x]);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / DK, i = e % DK;
+            const float qn = L.QG[r * RS + i] * L.NQ[r];
+            const float kn = L.KG[r * RS + i] * L.NK[r];
+            L.QG[r * RS + i] = qn;
+            L.KG[r * RS + i] = kn;
+            o[PL::QG + r * RS + i] = qn;
+            o[PL::KG + r * RS + i] = kn;
+        }
+    }
+    if (tid < BC) o[PL::BE + tid] = L.BE[tid];
+    __syncthreads();
+    // 4. the Gram products on 16x16x4 float32 MFMA: wave 0 GA (Kg against
+    // kh e^{-b}), wave 1 P (Qg against kh e^{-b}); EJK: the plain dots scaled
+    // by the element factors.  Lane (lm, lk) supplies channel k0 + 4 lk + u of
+    // row lm of both operands and holds rows 4 lk + e of column lm.
+    if (wave < 2) {
+        const float* X = wave == 0 ? L.KG : L.QG;
+        const float* Y = EJK ? L.KG : L.KI;
+        bf32x4_t acc = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 16) {
+            const float4 a4 = *reinterpret_cast<const float4*>(X + lm * RS + k0 + 4 * lk);
+            const float4 b4 = *reinterpret_cast<const float4*>(Y + lm * RS + k0 + 4 * lk);
+            acc = bmfma4(a4.x, b4.x, acc);
+            acc = bmfma4(a4.y, b4.y, acc);
+            acc = bmfma4(a4.z, b4.z, acc);
+            acc = bmfma4(a4.w, b4.w, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lk + e, s2 = lm;
+            float x = acc[e];
+            if (wave == 0) {
+                if (EJK) x *= s2 < r ? __builtin_amdgcn_exp2f(L.SBP[r] - L.SBC[s2]) : 0.f;
+                L.GA[r][s2] = s2 < r ? x : 0.f;
+            } else {
+                if (EJK) x *= s2 <= r ? __builtin_amdgcn_exp2f(L.SBC[r] - L.SBC[s2]) : 0.f;
+                o[PL::GP + r * BC + s2] = s2 <= r ? x : 0.f;
+            }
+        }
+    }
+    __syncthreads();
     if (tid < BC) {
-        // column s of (I + A)^-1 by forward substitution
-        const int s = tid;
+        // column s of (I + A)^-1, A_rt = beta_r GA_rt, by forward substitution
+        const int s2 = tid;
         float x[BC];
 #pragma unroll
         for (int r = 0; r < BC; ++r) {
-            float v = r == s ? 1.f : 0.f;
+            float v = r == s2 ? 1.f : 0.f;
 #pragma unroll
-            for (int t = 0; t < r; ++t) v = fmaf(-L.beta[r] * L.GA[r][t], x[t], v);
+            for (int t = 0; t < r; ++t) v = fmaf(-L.BE[r] * L.GA[r][t], x[t], v);
             x[r] = v;
-            o[PL::TI + r * BC + s] = v;
-        }
-    }
-    if (!EJK && tid < DK) o[PL::EC + tid] = L.ec[tid];
-    if (tid < BC) {
-        o[PL::BE + tid] = L.beta[tid];
-        if (EJK) {
-            o[PL::RF + tid] = L.seb[tid];
-            o[PL::RF + BC + tid] = L.sebp[tid];
-            o[PL::RF + 2 * BC + tid] = L.secb[tid];
-            o[PL::RF + 3 * BC + tid] = L.sec;
+            o[PL::TI + r * BC + s2] = v;
         }
     }
 }
@@ -1391,7 +1490,8 @@ hipError_t launch_dk(const BwdParams& p, size_t slots, hipStream_t st)
     const dim3 lgrid((unsigned)slots, (unsigned)p.H);
     hipError_t e = hipSuccess;
     if (slots > 0) {
-        hipLaunchKernelGGL((bwd_prep<DK, EJK>), lgrid, dim3(BT), 0, st, p);
+        if (p.in_bf16) hipLaunchKernelGGL((bwd_prep<DK, EJK, uint16_t>), lgrid, dim3(BT), 0, st, p);
+        else hipLaunchKernelGGL((bwd_prep<DK, EJK, float>), lgrid, dim3(BT), 0, st, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

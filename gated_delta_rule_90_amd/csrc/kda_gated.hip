@@ -140,11 +140,9 @@ __device__ __forceinline__ gf32x4_t gmfma4(float a, float b, gf32x4_t c)
 template <int DK>
 struct GPrepLds {
     static constexpr int RS = DK + 4;
-    alignas(16) float QT[GC * RS];   // scale e^{g} q
-    alignas(16) float KT[GC * RS];   // k
+    alignas(16) float QT[GC * RS];   // scale e^{g} q, then (in range) qt 2^{bk - bk_0}, A's left factor
+    alignas(16) float KT[GC * RS];   // k, then (in range) k 2^{bk_0 - bk}, A's right factor
     alignas(16) float BK[GC * RS];   // gk + g_gamma (log2 units), then its cumulative sum bk
-    alignas(16) float QF[GC * RS];   // qt 2^{bk - bk_0}  (A's left factor)
-    alignas(16) float KF[GC * RS];   // k 2^{bk_0 - bk}   (A's right factor)
     int wide;
 };
 
@@ -195,38 +193,48 @@ __global__ __launch_bounds__(GTH) void gated_prep(GatedParams p)
     if (tid == 0) L.wide = 0;
     __syncthreads();
     float* o = p.prep + ((size_t)slot * H + h) * PL::SIZE;
-    // 2. per key channel: the cumulative log-decay down the rows, the read-out
-    // and carry rows (to the block), A's factors when in range
+    // 2. per key channel: the cumulative log-decay down the rows and the range
+    // test; then the read-out and carry rows (to the block) and, when every
+    // channel is in range, A's factors in place of the rows.  A =
+    // (qt 2^{bk - bk_0}) (k 2^{bk_0 - bk})^T when every such factor stays inside
+    // float32's range (|bk_r - bk_0| <= 120 in log2 units); else A is formed
+    // element by element from the rows and bk.
+    float b[GC];
+    float bc = 0.f;
     if (tid < DK) {
         const int i = tid;
-        float b[GC];
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < GC; ++r) {
-            acc += L.BK[r * RS + i];
-            b[r] = acc;
-        }
-        o[PL::EKC + i] = __builtin_amdgcn_exp2f(acc);
-        // A = (qt 2^{bk - bk_0}) (k 2^{bk_0 - bk})^T when every such factor stays
-        // inside float32's range (|bk_r - bk_0| <= 120 in log2 units); else A is
-        // formed element by element
         bool wide = false;
 #pragma unroll
         for (int r = 0; r < GC; ++r) {
-            const float d = b[r] - b[0];
-            wide |= !(fabsf(d) <= 120.f);
-            const float qt = L.QT[r * RS + i], kt = L.KT[r * RS + i];
-            o[PL::QE + r * RS + i] = qt * __builtin_amdgcn_exp2f(b[r]);
-            o[PL::KC + r * RS + i] = kt * __builtin_amdgcn_exp2f(acc - b[r]);
-            L.QF[r * RS + i] = qt * __builtin_amdgcn_exp2f(d);
-            L.KF[r * RS + i] = kt * __builtin_amdgcn_exp2f(-d);
-            L.BK[r * RS + i] = b[r];
+            bc += L.BK[r * RS + i];
+            b[r] = bc;
+            wide |= !(fabsf(b[r] - b[0]) <= 120.f);
         }
         if (wide) L.wide = 1;
     }
     __syncthreads();
+    if (tid < DK) {
+        const int i = tid;
+        const bool inplace = !L.wide;
+        o[PL::EKC + i] = __builtin_amdgcn_exp2f(bc);
+#pragma unroll
+        for (int r = 0; r < GC; ++r) {
+            const float qt = L.QT[r * RS + i], kt = L.KT[r * RS + i];
+            o[PL::QE + r * RS + i] = qt * __builtin_amdgcn_exp2f(b[r]);
+            o[PL::KC + r * RS + i] = kt * __builtin_amdgcn_exp2f(bc - b[r]);
+            if (inplace) {
+                const float d = b[r] - b[0];
+                L.QT[r * RS + i] = qt * __builtin_amdgcn_exp2f(d);
+                L.KT[r * RS + i] = kt * __builtin_amdgcn_exp2f(-d);
+            } else {
+                L.BK[r * RS + i] = b[r];
+            }
+        }
+    }
+    __syncthreads();
     // 3. A: wave 0 on MFMA (lane (lm, lk) supplies channel k0 + 4 lk + u of row
     // lm of both factors at step u), or element by element, a thread per entry
+    // (the rows and bk as loaded)
     const int lane = tid & 63, wave = tid >> 6;
     const int lm = lane & 15, lk = lane >> 4;
     if (!L.wide) {
@@ -234,8 +242,8 @@ __global__ __launch_bounds__(GTH) void gated_prep(GatedParams p)
             gf32x4_t acc = gf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
             for (int k0 = 0; k0 < DK; k0 += 16) {
-                const float4 xa = *reinterpret_cast<const float4*>(L.QF + lm * RS + k0 + 4 * lk);
-                const float4 xb = *reinterpret_cast<const float4*>(L.KF + lm * RS + k0 + 4 * lk);
+                const float4 xa = *reinterpret_cast<const float4*>(L.QT + lm * RS + k0 + 4 * lk);
+                const float4 xb = *reinterpret_cast<const float4*>(L.KT + lm * RS + k0 + 4 * lk);
                 acc = gmfma4(xa.x, xb.x, acc);
                 acc = gmfma4(xa.y, xb.y, acc);
                 acc = gmfma4(xa.z, xb.z, acc);
