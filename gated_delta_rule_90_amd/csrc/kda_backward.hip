@@ -90,10 +90,12 @@ struct BwdParams {
     float* dbeta;
     float* dS0;
     const int32_t* off;   // [N + 1] chunk offsets
-    // the checkpoints, per (chunk, head) in 16-column tiles: [dv / 16][dk][16],
-    // so that a scan workgroup's tile is one contiguous 8 KB block (dk 128)
-    float* ckS;           // [slots, H, dv / 16, dk, 16]  state entering each chunk
-    float* ckdS;          // [slots, H, dv / 16, dk, 16]  dL/d(state leaving each chunk)
+    const int32_t* poff;  // [N + 1] offsets of the pairs of consecutive chunks
+    // the checkpoints, per (pair of chunks, head) in 16-column tiles:
+    // [dv / 16][dk][16], so that a scan workgroup's tile is one contiguous 8 KB
+    // block (dk 128)
+    float* ckS;           // [pairs, H, dv / 16, dk, 16]  state entering a pair's first chunk
+    float* ckdS;          // [pairs, H, dv / 16, dk, 16]  dL/d(state leaving a pair's last chunk)
     float* ckYU;          // [slots, H, 2, 16, dv]  Y = V - Kg S0 and U of each chunk
     float* ckZ;           // [slots, H, 16, dv]  Z of each chunk ((I + A)^T Z = dU)
     float* prep;          // [slots, H, PrepLayout<dk>::SIZE]  column-independent chunk operands
@@ -124,19 +126,24 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int T, int&
 // Chunk offsets: off[n] = sum_{m<n} ceil(len_m / 16), capped at the
 // workspace's chunk slots (only ranges that overlap can count more chunks
 // than the slots; those sequences then lose their last chunks, and their
-// results are unspecified, but every access stays inside the workspace).
-__global__ void bwd_plan_kernel(const int32_t* __restrict__ cu, int N, int T, int slots,
-                                int32_t* __restrict__ off)
+// results are unspecified, but every access stays inside the workspace);
+// pair offsets poff[n] = sum_{m<n} ceil(chunks_m / 2), capped likewise.
+__global__ void bwd_plan_kernel(const int32_t* __restrict__ cu, int N, int T, int slots, int pslots,
+                                int32_t* __restrict__ off, int32_t* __restrict__ poff)
 {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    int acc = 0;
+    int acc = 0, pacc = 0;
     for (int n = 0; n < N; ++n) {
         int t0, t1;
         seq_bounds(cu, n, T, t0, t1);
         off[n] = acc;
-        acc = min(acc + (t1 - t0 + BC - 1) / BC, slots);
+        poff[n] = pacc;
+        const int na = min(acc + (t1 - t0 + BC - 1) / BC, slots);
+        pacc = min(pacc + (na - acc + 1) / 2, pslots);
+        acc = na;
     }
     off[N] = acc;
+    poff[N] = pacc;
 }
 
 // Chunks of sequence n: its length in chunks, within its slots.
@@ -670,10 +677,13 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             // wait for a load then never waits for these stores as well
             store_block<NP, N4>(L.P[b], pf);
             L.X[b][rr][jj] = c0 + rr < t1 ? widen(pv) : 0.f;
-            {
-                // tiles t >= NT (idle waves at small dk) fall past the range
-                const auto rs = store_range(p.ckS + (((size_t)(slot0 + c) * H + h) * (dv / TV) + j0 / TV) * DK * TV,
-                                            DK * TV * 4);
+            if constexpr (b == 0) {
+                // the state entering a pair's first chunk (c even); tiles t >= NT
+                // (idle waves at small dk) fall past the range
+                // (pairs past the capped count of overlapping ranges store nothing)
+                const int pi = p.poff[n] + c / 2;
+                const auto rs = store_range(p.ckS + (((size_t)pi * H + h) * (dv / TV) + j0 / TV) * DK * TV,
+                                            pi < p.poff[n + 1] ? DK * TV * 4 : 0);
 #pragma unroll
                 for (int x = 0; x < TPW; ++x) {
                     const int t = wave + NW * x;
@@ -806,9 +816,13 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             store_block<NP, N4>(L.P[b], pf);
             L.X[b][rr][jj] = c0 + rr < t1 ? __uint_as_float(p.do_bf16 ? pd << 16 : pd) : 0.f;
             {
-                // tiles t >= NT (idle waves at small dk) fall past the range
-                const auto rs = store_range(p.ckdS + (((size_t)(slot0 + c) * H + h) * (dv / TV) + j0 / TV) * DK * TV,
-                                            DK * TV * 4);
+                // the state gradient leaving a pair's last chunk (c odd, or the
+                // sequence's last); the other chunks' stores get an empty range, as
+                // do tiles t >= NT (idle waves at small dk)
+                const int pi = p.poff[n] + c / 2;
+                const bool keep = ((c & 1) || c == nck - 1) && pi < p.poff[n + 1];
+                const auto rs = store_range(p.ckdS + (((size_t)pi * H + h) * (dv / TV) + j0 / TV) * DK * TV,
+                                            keep ? DK * TV * 4 : 0);
 #pragma unroll
                 for (int x = 0; x < TPW; ++x) {
                     const int t = wave + NW * x;
@@ -913,14 +927,20 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     }
 }
 
-// Pass 3: the gradients of one chunk's rows, from the state entering it
-// (S0), the gradient of the state leaving it (dS1), the chunk's Y and U (pass
-// 1) and Z (pass 2); one workgroup per (chunk, head) with all state columns.
-// Every global load of the chunk is issued first.  The products run on
-// 16x16x4 float32 MFMA; from the Gram-role products on, each lane keeps the
-// elements (row 4 lk + e, channel 16 t + lm) of its tiles in registers up to
-// their stores, so LDS holds the set-up, dO, U, Z and small per-row arrays,
-// and two workgroups share a CU.
+// Pass 3: the gradients of the chunks' rows, one workgroup per (pair of
+// consecutive chunks of a sequence, head) with all state columns.  The scans
+// store the state entering the first chunk of a pair and the state gradient
+// leaving its second chunk (checkpoints every 32 tokens); the pair's other two
+// are one step of each recurrence away, taken here on MFMA:
+//     S entering the second chunk = Diag(e^{b_C}) S0 + Kc^T U   (first chunk's Kc, U)
+//     dS leaving the first chunk  = Diag(e^{b_C}) dS1 + Qg^T dO - Kg^T dY   (second chunk's)
+// The second chunk is done first (its inputs then still in LDS give the
+// backward step), then the first.  A chunk's gradients come from its S0,
+// dS1, Y and U (pass 1) and Z (pass 2).  The products run on 16x16x4 float32
+// MFMA; from the Gram-role products on, each lane keeps the elements (row
+// 4 lk + e, channel 16 t + lm) of its tiles in registers up to their stores,
+// so LDS holds the set-up, dO, U, Z and small per-row arrays, and two
+// workgroups share a CU.
 template <int DK, bool EJK, typename Tin>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_local(BwdParams p)
 {
@@ -948,27 +968,29 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const int H = p.H, Hkv = p.Hkv, dv = p.dv;
     const int hk = h / (H / Hkv);
     const bool grouped = Hkv != H;
-    if (slot >= p.off[p.N]) return;
-    // the sequence of this chunk: the last n with off[n] <= slot
+    const int ps = slot;   // the pair slot
+    if (ps >= p.poff[p.N]) return;
+    // the sequence of this pair: the last n with poff[n] <= ps
     int lo = 0, hi = p.N - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (p.off[mid] <= slot) lo = mid;
+        if (p.poff[mid] <= ps) lo = mid;
         else hi = mid - 1;
     }
     const int n = lo;
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
-    const int c0 = t0 + (slot - p.off[n]) * BC, nr = min(BC, t1 - c0);
+    const int nck = seq_chunks(p.off, n, t0, t1);
+    const int ca = 2 * (ps - p.poff[n]);   // the pair's chunks: ca and, if it exists, ca + 1
+    const bool has_b = ca + 1 < nck;
     const int nj = dv / 16;
     const float ea = EJK ? 0.f : expf(p.a_log[h]);
     // ---- loads.  S0 and dS1 rows of this wave's channel tiles, 16 bytes per
     // lane per 16 columns (lane (lm, lk): row 16 t + lm, columns 16 jb + 4 lk ..;
     // a 16-column tile's rows are 64 bytes apart)
     float4 s0r[TPW][NJ], d1r[TPW][NJ];
-    {
-        const float* S0 = p.ckS + ((size_t)slot * H + h) * DK * dv;
-        const float* dS1 = p.ckdS + ((size_t)slot * H + h) * DK * dv;
+    const float* S0p = p.ckS + ((size_t)ps * H + h) * DK * dv;
+    auto load_tile = [&](float4 (&dst)[TPW][NJ], const float* src) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
             const int t = wave + NW * x;
@@ -976,436 +998,511 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             for (int jb = 0; jb < NJ; ++jb) {
                 const bool ok = t < NT && jb < nj;
                 const size_t o = ((size_t)jb * DK + 16 * t + lm) * TV + 4 * lk;
-                s0r[x][jb] = ok ? *reinterpret_cast<const float4*>(S0 + o) : make_float4(0.f, 0.f, 0.f, 0.f);
-                d1r[x][jb] = ok ? *reinterpret_cast<const float4*>(dS1 + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+                dst[x][jb] = ok ? *reinterpret_cast<const float4*>(src + o) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
-    }
-    // the rows of q, k and the gate (element e = tid + m BT: row e / DK, channel e % DK)
-    const Tin* qq = static_cast<const Tin*>(p.q);
-    const Tin* kk = static_cast<const Tin*>(p.k);
-    Tin xq[NE], xk[NE];
-    float xg[EJK ? 1 : NE];
-#pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + m * BT;
-        const int r = e / DK, i = e % DK;
-        const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
-        xq[m] = qq[(tok * H + h) * DK + i];
-        xk[m] = kk[(tok * Hkv + hk) * DK + i];
-        if (!EJK) xg[m] = p.g[(tok * H + h) * DK + i];
-    }
-    const float dtb_row = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
-    // dO (raw bits), U, Z, Y: element e = tid + m BT, row e / MAXD, column e % MAXD
-    uint32_t xo[NV];
-    float xu[NV], xz[NV], xy[NV];
-    {
-        const float* yu = p.ckYU + ((size_t)slot * H + h) * 2 * BC * dv;
-        const float* zz = p.ckZ + ((size_t)slot * H + h) * BC * dv;
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + m * BT;
-            const int r = e / MAXD, j = e % MAXD;
-            const bool ok = j < dv;   // rows past nr: Y, U and Z are stored as zero
-            const size_t od = ((size_t)(c0 + (r < nr ? r : 0)) * H + h) * dv + j;
-            if (p.do_bf16) xo[m] = ok && r < nr ? (uint32_t)static_cast<const uint16_t*>(p.d_o)[od] << 16 : 0u;
-            else xo[m] = ok && r < nr ? __float_as_uint(static_cast<const float*>(p.d_o)[od]) : 0u;
-            xy[m] = ok ? yu[(size_t)r * dv + j] : 0.f;
-            xu[m] = ok ? yu[(size_t)(BC + r) * dv + j] : 0.f;
-            xz[m] = ok ? zz[(size_t)r * dv + j] : 0.f;
-        }
-    }
-    float xb = 0.f, xgs = 0.f;
-    if (tid < BC) {
-        const size_t tok = (size_t)(c0 + (tid < nr ? tid : 0));
-        xb = p.beta[tok * H + h];
-        xgs = (EJK && p.g) ? p.g[tok * H + h] : 0.f;
-    }
-    // KDA: the gate and dt_bias of the elements this lane owns in the MFMA layout
-    float gl[TPW][4], dtl[TPW];
-#pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-        const int t = wave + NW * x;
-        const bool ok = !EJK && t < NT;
-        dtl[x] = ok && p.dt_bias ? p.dt_bias[(size_t)(16 * t + lm) * H + h] : 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * lk + e;
-            const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
-            gl[x][e] = ok ? p.g[(tok * H + h) * DK + 16 * t + lm] : 0.f;
-        }
-    }
-    // ---- to LDS: the raw rows, gate activations (log2 units), beta; dO, U, Z
-    {
-        const float lb2 = p.lb * kLog2e;
+    };
+    load_tile(s0r, S0p);
+    load_tile(d1r, p.ckdS + ((size_t)ps * H + h) * DK * dv);
+    // ---- one chunk: its inputs (S0, dS1 in s0r, d1r), its gradients
+    auto run_chunk = [&](const int c) __attribute__((always_inline)) {
+        const int slot = p.off[n] + c;
+        const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
+        // the rows of q, k and the gate (element e = tid + m BT: row e / DK, channel e % DK)
+        const Tin* qq = static_cast<const Tin*>(p.q);
+        const Tin* kk = static_cast<const Tin*>(p.k);
+        Tin xq[NE], xk[NE];
+        float xg[EJK ? 1 : NE];
 #pragma unroll
         for (int m = 0; m < NE; ++m) {
             const int e = tid + m * BT;
             const int r = e / DK, i = e % DK;
-            const bool ok = r < nr;
-            L.qh[r][i] = ok ? widen(xq[m]) : 0.f;
-            L.kh[r][i] = ok ? widen(xk[m]) : 0.f;
-            if (!EJK) L.eb[r][i] = ok ? lb2 * sigmoid_f(ea * (xg[m] + dtb_row)) : 0.f;
+            const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
+            xq[m] = qq[(tok * H + h) * DK + i];
+            xk[m] = kk[(tok * Hkv + hk) * DK + i];
+            if (!EJK) xg[m] = p.g[(tok * H + h) * DK + i];
         }
+        const float dtb_row = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
+        // dO (raw bits), U, Z, Y: element e = tid + m BT, row e / MAXD, column e % MAXD
+        uint32_t xo[NV];
+        float xu[NV], xz[NV], xy[NV];
+        {
+            const float* yu = p.ckYU + ((size_t)slot * H + h) * 2 * BC * dv;
+            const float* zz = p.ckZ + ((size_t)slot * H + h) * BC * dv;
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+                const int e = tid + m * BT;
+                const int r = e / MAXD, j = e % MAXD;
+                const bool ok = j < dv;   // rows past nr: Y, U and Z are stored as zero
+                const size_t od = ((size_t)(c0 + (r < nr ? r : 0)) * H + h) * dv + j;
+                if (p.do_bf16) xo[m] = ok && r < nr ? (uint32_t)static_cast<const uint16_t*>(p.d_o)[od] << 16 : 0u;
+                else xo[m] = ok && r < nr ? __float_as_uint(static_cast<const float*>(p.d_o)[od]) : 0u;
+                xy[m] = ok ? yu[(size_t)r * dv + j] : 0.f;
+                xu[m] = ok ? yu[(size_t)(BC + r) * dv + j] : 0.f;
+                xz[m] = ok ? zz[(size_t)r * dv + j] : 0.f;
+            }
+        }
+        float xb = 0.f, xgs = 0.f;
         if (tid < BC) {
-            const bool ok = tid < nr;
-            L.beta[tid] = ok ? (EJK ? xb : sigmoid_f(xb)) : 0.f;
-            if (EJK) L.sb[tid] = ok ? xgs * kLog2e : 0.f;
+            const size_t tok = (size_t)(c0 + (tid < nr ? tid : 0));
+            xb = p.beta[tok * H + h];
+            xgs = (EJK && p.g) ? p.g[tok * H + h] : 0.f;
         }
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + m * BT;
-            const int r = e / MAXD, j = e % MAXD;
-            dO[r][j] = __uint_as_float(xo[m]);
-            U[r][j] = xu[m];
-            Z[r][j] = xz[m];
-            // Z.Y of row r: a partial per wave (each wave covers half a row)
-            const float zy = wave_sum(xz[m] * xy[m]);
-            if (lane == 0) zyw[wave][m] = zy;
-        }
-    }
-    setup_rest<DK, EJK>(L, p);
-    // (c) over the columns: wave 0 dA = -strict_lower(Z U^T), wave 1 dP =
-    // lower(dO U^T); the Gram-product gradients MA = diag(beta) dA, MP = dP
-    // (EJK: times the decay factors).  Lane (lm, lk) supplies row lm of both
-    // operands at columns 16 jb + 4 lk + u.
-    if (wave < 2) {
-        const float (*A)[SR] = wave == 1 ? dO : Z;
-        bf32x4_t m = bf32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int jb = 0; jb < nj; ++jb) {
-            const float4 a = *reinterpret_cast<const float4*>(&A[lm][16 * jb + 4 * lk]);
-            const float4 b = *reinterpret_cast<const float4*>(&U[lm][16 * jb + 4 * lk]);
-            m = bmfma4(a.x, b.x, m);
-            m = bmfma4(a.y, b.y, m);
-            m = bmfma4(a.z, b.z, m);
-            m = bmfma4(a.w, b.w, m);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * lk + e, s = lm;
-            if (wave == 0) {
-                const float da = s < r ? -m[e] : 0.f;
-                dA[r][s] = da;
-                MA[r][s] = EJK ? L.beta[r] * da * L.DA[r][s] : L.beta[r] * da;
-            } else {
-                const float b = s <= r ? m[e] : 0.f;
-                MP[r][s] = EJK ? b * L.DP[r][s] : b;
-            }
-        }
-    }
-    // (d1) dQg = dO S0^T, dKg = -dY S0^T and dKc = U dS1^T, a 16-channel tile
-    // per step: lane (lm, lk) supplies dO[lm][j], dY[lm][j], U[lm][j] and
-    // S0[i][j], dS1[i][j] (i = 16 t + lm, j = 16 jb + 4 lk + u at step u) and
-    // holds rows 4 lk + e of channel i.  The same S0, dS1 elements give
-    // dbc_i = e^{b_C,i} sum_j S0_ij dS1_ij.
-    bf32x4_t aq[TPW], ag[TPW], ac[TPW];
-    float dbcv[TPW];
-#pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-        const int t = wave + NW * x;
-        aq[x] = bf32x4_t{0.f, 0.f, 0.f, 0.f};
-        ag[x] = aq[x];
-        ac[x] = aq[x];
-        dbcv[x] = 0.f;
-        if (t < NT) {
-            float sdot = 0.f;
-            const float nb = -L.beta[lm];
-#pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) {
-                if (jb < nj) {
-                    const float4 s4 = s0r[x][jb], d4 = d1r[x][jb];
-                    const float4 o4 = *reinterpret_cast<const float4*>(&dO[lm][16 * jb + 4 * lk]);
-                    const float4 z4 = *reinterpret_cast<const float4*>(&Z[lm][16 * jb + 4 * lk]);
-                    const float4 u4 = *reinterpret_cast<const float4*>(&U[lm][16 * jb + 4 * lk]);
-                    aq[x] = bmfma4(o4.x, s4.x, aq[x]);
-                    aq[x] = bmfma4(o4.y, s4.y, aq[x]);
-                    aq[x] = bmfma4(o4.z, s4.z, aq[x]);
-                    aq[x] = bmfma4(o4.w, s4.w, aq[x]);
-                    ag[x] = bmfma4(nb * z4.x, s4.x, ag[x]);
-                    ag[x] = bmfma4(nb * z4.y, s4.y, ag[x]);
-                    ag[x] = bmfma4(nb * z4.z, s4.z, ag[x]);
-                    ag[x] = bmfma4(nb * z4.w, s4.w, ag[x]);
-                    ac[x] = bmfma4(u4.x, d4.x, ac[x]);
-                    ac[x] = bmfma4(u4.y, d4.y, ac[x]);
-                    ac[x] = bmfma4(u4.z, d4.z, ac[x]);
-                    ac[x] = bmfma4(u4.w, d4.w, ac[x]);
-                    sdot = fmaf(s4.x, d4.x, sdot);
-                    sdot = fmaf(s4.y, d4.y, sdot);
-                    sdot = fmaf(s4.z, d4.z, sdot);
-                    sdot = fmaf(s4.w, d4.w, sdot);
-                }
-            }
-            // sum over the four lane groups (lanes lm, lm + 16, lm + 32, lm + 48)
-            sdot = xor_add<16>(sdot);
-            sdot = xor_add<32>(sdot);
-            dbcv[x] = L.ecc(16 * t + lm) * sdot;
-        }
-    }
-    lds_barrier();
-    if (tid < BC) {
-        const int r = tid;
-        // rows 2 m + half were covered by waves 2 half and 2 half + 1
-        const int m = r >> 1, w0 = 2 * (r & 1);
-        float acc = zyw[w0][m] + zyw[w0 + 1][m];
-        for (int s = 0; s < r; ++s) acc = fmaf(dA[r][s], L.GA[r][s], acc);
-        dbt[r] = acc;
-    }
-    // (d2) the Gram roles on MFMA, per 16-channel tile: D[r][i] = sum_s M[r][s]
-    // X[s][i] with the lane supplying M[lm][s] (or M[s][lm] for M^T) and
-    // X[s][16 t + lm] for s = 4 lk + u at step u.  The pair terms whose row and
-    // column roles fall on the same b (the diagonal of P, and for EJK the first
-    // sub-diagonal of A) are kept apart: they enter dqh and dkh but cancel
-    // exactly in dgamma, so they are left out of db.  Then the row gradients
-    // dqh, dkh, db, db' and Kc dKc of the lane's elements.
-    float dqh[TPW][4], dkh[TPW][4], gb[TPW][4], gp[TPW][4], kd[TPW][4];
-#pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-        const int t = wave + NW * x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dqh[x][e] = dkh[x][e] = gb[x][e] = gp[x][e] = kd[x][e] = 0.f;
-        if (t < NT) {
-            const int i = 16 * t + lm;
-            bf32x4_t R1 = bf32x4_t{0.f, 0.f, 0.f, 0.f}, R2 = R1, R3 = R1, R4 = R1;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int s = 4 * lk + u;
-                float a1 = MA[lm][s], a2 = MA[s][lm];
-                const float a3 = s != lm ? MP[lm][s] : 0.f, a4 = s != lm ? MP[s][lm] : 0.f;
-                if (EJK) {
-                    if (s + 1 == lm) a1 = 0.f;
-                    if (lm + 1 == s) a2 = 0.f;
-                }
-                const float khs = L.kh[s][i], qhs = L.qh[s][i];
-                float b1, b2, b4;
-                if (EJK) {
-                    b1 = khs;
-                    b2 = khs;
-                    b4 = qhs;
-                } else {
-                    const float eb = L.eb[s][i];
-                    b1 = khs * L.ein[s][i];
-                    b2 = khs * eb;
-                    b4 = qhs * eb;
-                }
-                R1 = bmfma4(a1, b1, R1);   // rowA (before the row factor)
-                R2 = bmfma4(a2, b2, R2);   // colA
-                R3 = bmfma4(a3, b1, R3);   // rowP
-                R4 = bmfma4(a4, b4, R4);   // colP
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lk + e;
-                float rowA = R1[e], colA = R2[e], rowP = R3[e], colP = R4[e], subA = 0.f, subAc = 0.f;
-                if (!EJK) {
-                    const float eb = L.eb[r][i], ein = L.ein[r][i];
-                    rowA *= eb;
-                    rowP *= eb;
-                    colA *= ein;
-                    colP *= ein;
-                } else {
-                    subA = r > 0 ? MA[r][r - 1] * L.kh[r - 1][i] : 0.f;
-                    subAc = r + 1 < BC ? MA[r + 1][r] * L.kh[r + 1][i] : 0.f;
-                }
-                const float mpd = MP[r][r];
-                const float qh = L.qh[r][i], kh = L.kh[r][i];
-                const float ebr = L.ebr(r, i), ebpr = L.ebpr(r, i), ecbr = L.ecbr(r, i);
-                const float qg = qh * ebr, kg = kh * ebpr, kc = kh * ecbr;
-                dqh[x][e] = rowP + mpd * kh + ebr * aq[x][e];
-                dkh[x][e] = rowA + subA + colA + subAc + colP + mpd * qh + ebpr * ag[x][e] + ecbr * ac[x][e];
-                const float db = qh * rowP - kh * colA - kh * colP + qg * aq[x][e];
-                const float dbp = kh * rowA + kg * ag[x][e];
-                gb[x][e] = EJK ? db : db + dbp;
-                gp[x][e] = dbp;
-                kd[x][e] = kc * ac[x][e];
-            }
-        }
-    }
-    // ---- per-row sums over the channels: a partial per lane over its tiles,
-    // summed over the 16 lanes of a row group, one value per wave and row
-    {
-        float sq[4], sk[4], sa[4], sb2[4], sc[4], sd = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sq[e] = sk[e] = sa[e] = sb2[e] = sc[e] = 0.f;
+        // KDA: the gate and dt_bias of the elements this lane owns in the MFMA layout
+        float gl[TPW][4], dtl[TPW];
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
             const int t = wave + NW * x;
+            const bool ok = !EJK && t < NT;
+            dtl[x] = ok && p.dt_bias ? p.dt_bias[(size_t)(16 * t + lm) * H + h] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e;
+                const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
+                gl[x][e] = ok ? p.g[(tok * H + h) * DK + 16 * t + lm] : 0.f;
+            }
+        }
+        // ---- to LDS: the raw rows, gate activations (log2 units), beta; dO, U, Z
+        {
+            const float lb2 = p.lb * kLog2e;
+#pragma unroll
+            for (int m = 0; m < NE; ++m) {
+                const int e = tid + m * BT;
+                const int r = e / DK, i = e % DK;
+                const bool ok = r < nr;
+                L.qh[r][i] = ok ? widen(xq[m]) : 0.f;
+                L.kh[r][i] = ok ? widen(xk[m]) : 0.f;
+                if (!EJK) L.eb[r][i] = ok ? lb2 * sigmoid_f(ea * (xg[m] + dtb_row)) : 0.f;
+            }
+            if (tid < BC) {
+                const bool ok = tid < nr;
+                L.beta[tid] = ok ? (EJK ? xb : sigmoid_f(xb)) : 0.f;
+                if (EJK) L.sb[tid] = ok ? xgs * kLog2e : 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+                const int e = tid + m * BT;
+                const int r = e / MAXD, j = e % MAXD;
+                dO[r][j] = __uint_as_float(xo[m]);
+                U[r][j] = xu[m];
+                Z[r][j] = xz[m];
+                // Z.Y of row r: a partial per wave (each wave covers half a row)
+                const float zy = wave_sum(xz[m] * xy[m]);
+                if (lane == 0) zyw[wave][m] = zy;
+            }
+        }
+        setup_rest<DK, EJK>(L, p);
+        // (c) over the columns: wave 0 dA = -strict_lower(Z U^T), wave 1 dP =
+        // lower(dO U^T); the Gram-product gradients MA = diag(beta) dA, MP = dP
+        // (EJK: times the decay factors).  Lane (lm, lk) supplies row lm of both
+        // operands at columns 16 jb + 4 lk + u.
+        if (wave < 2) {
+            const float (*A)[SR] = wave == 1 ? dO : Z;
+            bf32x4_t m = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int jb = 0; jb < nj; ++jb) {
+                const float4 a = *reinterpret_cast<const float4*>(&A[lm][16 * jb + 4 * lk]);
+                const float4 b = *reinterpret_cast<const float4*>(&U[lm][16 * jb + 4 * lk]);
+                m = bmfma4(a.x, b.x, m);
+                m = bmfma4(a.y, b.y, m);
+                m = bmfma4(a.z, b.z, m);
+                m = bmfma4(a.w, b.w, m);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e, s = lm;
+                if (wave == 0) {
+                    const float da = s < r ? -m[e] : 0.f;
+                    dA[r][s] = da;
+                    MA[r][s] = EJK ? L.beta[r] * da * L.DA[r][s] : L.beta[r] * da;
+                } else {
+                    const float b = s <= r ? m[e] : 0.f;
+                    MP[r][s] = EJK ? b * L.DP[r][s] : b;
+                }
+            }
+        }
+        // (d1) dQg = dO S0^T, dKg = -dY S0^T and dKc = U dS1^T, a 16-channel tile
+        // per step: lane (lm, lk) supplies dO[lm][j], dY[lm][j], U[lm][j] and
+        // S0[i][j], dS1[i][j] (i = 16 t + lm, j = 16 jb + 4 lk + u at step u) and
+        // holds rows 4 lk + e of channel i.  The same S0, dS1 elements give
+        // dbc_i = e^{b_C,i} sum_j S0_ij dS1_ij.
+        bf32x4_t aq[TPW], ag[TPW], ac[TPW];
+        float dbcv[TPW];
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            aq[x] = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+            ag[x] = aq[x];
+            ac[x] = aq[x];
+            dbcv[x] = 0.f;
+            if (t < NT) {
+                float sdot = 0.f;
+                const float nb = -L.beta[lm];
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb) {
+                    if (jb < nj) {
+                        const float4 s4 = s0r[x][jb], d4 = d1r[x][jb];
+                        const float4 o4 = *reinterpret_cast<const float4*>(&dO[lm][16 * jb + 4 * lk]);
+                        const float4 z4 = *reinterpret_cast<const float4*>(&Z[lm][16 * jb + 4 * lk]);
+                        const float4 u4 = *reinterpret_cast<const float4*>(&U[lm][16 * jb + 4 * lk]);
+                        aq[x] = bmfma4(o4.x, s4.x, aq[x]);
+                        aq[x] = bmfma4(o4.y, s4.y, aq[x]);
+                        aq[x] = bmfma4(o4.z, s4.z, aq[x]);
+                        aq[x] = bmfma4(o4.w, s4.w, aq[x]);
+                        ag[x] = bmfma4(nb * z4.x, s4.x, ag[x]);
+                        ag[x] = bmfma4(nb * z4.y, s4.y, ag[x]);
+                        ag[x] = bmfma4(nb * z4.z, s4.z, ag[x]);
+                        ag[x] = bmfma4(nb * z4.w, s4.w, ag[x]);
+                        ac[x] = bmfma4(u4.x, d4.x, ac[x]);
+                        ac[x] = bmfma4(u4.y, d4.y, ac[x]);
+                        ac[x] = bmfma4(u4.z, d4.z, ac[x]);
+                        ac[x] = bmfma4(u4.w, d4.w, ac[x]);
+                        sdot = fmaf(s4.x, d4.x, sdot);
+                        sdot = fmaf(s4.y, d4.y, sdot);
+                        sdot = fmaf(s4.z, d4.z, sdot);
+                        sdot = fmaf(s4.w, d4.w, sdot);
+                    }
+                }
+                // sum over the four lane groups (lanes lm, lm + 16, lm + 32, lm + 48)
+                sdot = xor_add<16>(sdot);
+                sdot = xor_add<32>(sdot);
+                dbcv[x] = L.ecc(16 * t + lm) * sdot;
+            }
+        }
+        lds_barrier();
+        if (tid < BC) {
+            const int r = tid;
+            // rows 2 m + half were covered by waves 2 half and 2 half + 1
+            const int m = r >> 1, w0 = 2 * (r & 1);
+            float acc = zyw[w0][m] + zyw[w0 + 1][m];
+            for (int s = 0; s < r; ++s) acc = fmaf(dA[r][s], L.GA[r][s], acc);
+            dbt[r] = acc;
+        }
+        // (d2) the Gram roles on MFMA, per 16-channel tile: D[r][i] = sum_s M[r][s]
+        // X[s][i] with the lane supplying M[lm][s] (or M[s][lm] for M^T) and
+        // X[s][16 t + lm] for s = 4 lk + u at step u.  The pair terms whose row and
+        // column roles fall on the same b (the diagonal of P, and for EJK the first
+        // sub-diagonal of A) are kept apart: they enter dqh and dkh but cancel
+        // exactly in dgamma, so they are left out of db.  Then the row gradients
+        // dqh, dkh, db, db' and Kc dKc of the lane's elements.
+        float dqh[TPW][4], dkh[TPW][4], gb[TPW][4], gp[TPW][4], kd[TPW][4];
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dqh[x][e] = dkh[x][e] = gb[x][e] = gp[x][e] = kd[x][e] = 0.f;
+            if (t < NT) {
+                const int i = 16 * t + lm;
+                bf32x4_t R1 = bf32x4_t{0.f, 0.f, 0.f, 0.f}, R2 = R1, R3 = R1, R4 = R1;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s = 4 * lk + u;
+                    float a1 = MA[lm][s], a2 = MA[s][lm];
+                    const float a3 = s != lm ? MP[lm][s] : 0.f, a4 = s != lm ? MP[s][lm] : 0.f;
+                    if (EJK) {
+                        if (s + 1 == lm) a1 = 0.f;
+                        if (lm + 1 == s) a2 = 0.f;
+                    }
+                    const float khs = L.kh[s][i], qhs = L.qh[s][i];
+                    float b1, b2, b4;
+                    if (EJK) {
+                        b1 = khs;
+                        b2 = khs;
+                        b4 = qhs;
+                    } else {
+                        const float eb = L.eb[s][i];
+                        b1 = khs * L.ein[s][i];
+                        b2 = khs * eb;
+                        b4 = qhs * eb;
+                    }
+                    R1 = bmfma4(a1, b1, R1);   // rowA (before the row factor)
+                    R2 = bmfma4(a2, b2, R2);   // colA
+                    R3 = bmfma4(a3, b1, R3);   // rowP
+                    R4 = bmfma4(a4, b4, R4);   // colP
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * lk + e;
+                    float rowA = R1[e], colA = R2[e], rowP = R3[e], colP = R4[e], subA = 0.f, subAc = 0.f;
+                    if (!EJK) {
+                        const float eb = L.eb[r][i], ein = L.ein[r][i];
+                        rowA *= eb;
+                        rowP *= eb;
+                        colA *= ein;
+                        colP *= ein;
+                    } else {
+                        subA = r > 0 ? MA[r][r - 1] * L.kh[r - 1][i] : 0.f;
+                        subAc = r + 1 < BC ? MA[r + 1][r] * L.kh[r + 1][i] : 0.f;
+                    }
+                    const float mpd = MP[r][r];
+                    const float qh = L.qh[r][i], kh = L.kh[r][i];
+                    const float ebr = L.ebr(r, i), ebpr = L.ebpr(r, i), ecbr = L.ecbr(r, i);
+                    const float qg = qh * ebr, kg = kh * ebpr, kc = kh * ecbr;
+                    dqh[x][e] = rowP + mpd * kh + ebr * aq[x][e];
+                    dkh[x][e] = rowA + subA + colA + subAc + colP + mpd * qh + ebpr * ag[x][e] + ecbr * ac[x][e];
+                    const float db = qh * rowP - kh * colA - kh * colP + qg * aq[x][e];
+                    const float dbp = kh * rowA + kg * ag[x][e];
+                    gb[x][e] = EJK ? db : db + dbp;
+                    gp[x][e] = dbp;
+                    kd[x][e] = kc * ac[x][e];
+                }
+            }
+        }
+        // ---- per-row sums over the channels: a partial per lane over its tiles,
+        // summed over the 16 lanes of a row group, one value per wave and row
+        {
+            float sq[4], sk[4], sa[4], sb2[4], sc[4], sd = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sq[e] = sk[e] = sa[e] = sb2[e] = sc[e] = 0.f;
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+                    const int i = 16 * t + lm;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * lk + e;
+                        sq[e] = fmaf(L.qh[r][i], dqh[x][e], sq[e]);
+                        sk[e] = fmaf(L.kh[r][i], dkh[x][e], sk[e]);
+                        if (EJK) {
+                            sa[e] += gb[x][e];
+                            sb2[e] += gp[x][e];
+                            sc[e] += kd[x][e];
+                        }
+                    }
+                    if (EJK && lk == 0) sd += dbcv[x];
+                }
+            }
+            auto row16 = [](float v) {
+                v = xor_add<1>(v);
+                v = xor_add<2>(v);
+                v = xor_add<4>(v);
+                return xor_add<8>(v);
+            };
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float q = row16(sq[e]), k = row16(sk[e]);
+                if (lm == 0) {
+                    rq[wave][4 * lk + e] = q;
+                    rk[wave][4 * lk + e] = k;
+                }
+                if (EJK) {
+                    const float a = row16(sa[e]), b = row16(sb2[e]), c = row16(sc[e]);
+                    if (lm == 0) {
+                        ra[wave][4 * lk + e] = a;
+                        rb[wave][4 * lk + e] = b;
+                        rc[wave][4 * lk + e] = c;
+                    }
+                }
+            }
+            if (EJK) {
+                sd = row16(sd);
+                if (lane == 0) rd[wave] = sd;
+            }
+        }
+        lds_barrier();
+        // ---- dgamma.  KDA, per element: the reverse cumulative sum of db down the
+        // chunk, the carry's e^{b_C} term (dbc, on every row) and the Kc terms of
+        // the rows before.  A channel's rows are split over the four lane groups
+        // (rows 4 lk .. 4 lk + 3), joined through the group totals.
+        // EJK, per row: the same over the per-row sums, in one lane.
+        float dgm[TPW][4];
+        if (!EJK) {
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                float G = 0.f, K = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    G += gb[x][e];
+                    K += kd[x][e];
+                }
+                float sufG = 0.f, preK = 0.f;
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    const float g2 = __shfl(G, lm + 16 * l);
+                    const float k2 = __shfl(K, lm + 16 * l);
+                    if (l > lk) sufG += g2;
+                    if (l < lk) preK += k2;
+                }
+                float run = dbcv[x] + sufG;
+                float pre[4];
+                float acc = preK;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pre[e] = acc;
+                    acc += kd[x][e];
+                }
+#pragma unroll
+                for (int e = 3; e >= 0; --e) {
+                    run += gb[x][e];
+                    dgm[x][e] = run + pre[e];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < TPW; ++x)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dgm[x][e] = 0.f;
+            if (tid == 0) {
+                float A[BC], B[BC], C[BC];
+                for (int r = 0; r < BC; ++r) {
+                    A[r] = (ra[0][r] + ra[1][r]) + (ra[2][r] + ra[3][r]);
+                    B[r] = (rb[0][r] + rb[1][r]) + (rb[2][r] + rb[3][r]);
+                    C[r] = (rc[0][r] + rc[1][r]) + (rc[2][r] + rc[3][r]);
+                }
+                float pre[BC];
+                float acc = 0.f;
+                for (int r = 0; r < BC; ++r) {
+                    pre[r] = acc;
+                    acc += C[r];
+                }
+                float run = (rd[0] + rd[1]) + (rd[2] + rd[3]);
+                for (int r = BC - 1; r >= 0; --r) {
+                    run += A[r] + (r + 1 < BC ? B[r + 1] : 0.f);
+                    dgs[r] = run + pre[r];
+                }
+            }
+            lds_barrier();
+        }
+        // ---- the prologue's backward and the stores
+        float apart = 0.f;
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            float pdt = 0.f;
             if (t < NT) {
                 const int i = 16 * t + lm;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * lk + e;
-                    sq[e] = fmaf(L.qh[r][i], dqh[x][e], sq[e]);
-                    sk[e] = fmaf(L.kh[r][i], dkh[x][e], sk[e]);
-                    if (EJK) {
-                        sa[e] += gb[x][e];
-                        sb2[e] += gp[x][e];
-                        sc[e] += kd[x][e];
+                    if (r < nr) {
+                        const size_t tok = (size_t)(c0 + r);
+                        const float pq = (rq[0][r] + rq[1][r]) + (rq[2][r] + rq[3][r]);
+                        const float pk = (rk[0][r] + rk[1][r]) + (rk[2][r] + rk[3][r]);
+                        float dq, dk;
+                        if (p.l2norm) {
+                            const float inq = 1.f / L.nq[r], ink = 1.f / L.nk[r];
+                            dq = p.scale * inq * (dqh[x][e] - L.qh[r][i] * pq / (p.scale * p.scale));
+                            dk = ink * (dkh[x][e] - L.kh[r][i] * pk);
+                        } else {
+                            dq = p.scale * dqh[x][e];
+                            dk = dkh[x][e];
+                        }
+                        p.dq[(tok * H + h) * DK + i] = dq;
+                        p.dk[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * DK + i] = dk;
+                        if (!EJK) {
+                            const float xx = ea * (gl[x][e] + dtl[x]);
+                            // sigma'(x) = sigma(x) sigma(-x): no cancellation in
+                            // 1 - sigma(x) when the gate saturates
+                            const float dx = dgm[x][e] * p.lb * sigmoid_f(xx) * sigmoid_f(-xx);
+                            p.dg[(tok * H + h) * DK + i] = dx * ea;
+                            apart = fmaf(dx, xx, apart);
+                            pdt += dx * ea;
+                        }
                     }
                 }
-                if (EJK && lk == 0) sd += dbcv[x];
+            }
+            if (!EJK) {
+                // dt_bias partial of channel i: the sum over the four lane groups
+                pdt = xor_add<16>(pdt);
+                pdt = xor_add<32>(pdt);
+                if (t < NT && lk == 0) p.part_dt[((size_t)slot * H + h) * DK + 16 * t + lm] = pdt;
             }
         }
-        auto row16 = [](float v) {
-            v = xor_add<1>(v);
-            v = xor_add<2>(v);
-            v = xor_add<4>(v);
-            return xor_add<8>(v);
-        };
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float q = row16(sq[e]), k = row16(sk[e]);
-            if (lm == 0) {
-                rq[wave][4 * lk + e] = q;
-                rk[wave][4 * lk + e] = k;
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + m * BT;
+            const int r = e / MAXD, j = e % MAXD;
+            if (r < nr && j < dv) {
+                const size_t tok = (size_t)(c0 + r);
+                p.dv_out[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * dv + j] = L.beta[r] * xz[m];
             }
+        }
+        if (tid < BC && tid < nr) {
+            const int r = tid;
+            const size_t tok = (size_t)(c0 + r);
             if (EJK) {
-                const float a = row16(sa[e]), b = row16(sb2[e]), c = row16(sc[e]);
-                if (lm == 0) {
-                    ra[wave][4 * lk + e] = a;
-                    rb[wave][4 * lk + e] = b;
-                    rc[wave][4 * lk + e] = c;
-                }
-            }
-        }
-        if (EJK) {
-            sd = row16(sd);
-            if (lane == 0) rd[wave] = sd;
-        }
-    }
-    lds_barrier();
-    // ---- dgamma.  KDA, per element: the reverse cumulative sum of db down the
-    // chunk, the carry's e^{b_C} term (dbc, on every row) and the Kc terms of
-    // the rows before.  A channel's rows are split over the four lane groups
-    // (rows 4 lk .. 4 lk + 3), joined through the group totals.
-    // EJK, per row: the same over the per-row sums, in one lane.
-    float dgm[TPW][4];
-    if (!EJK) {
-#pragma unroll
-        for (int x = 0; x < TPW; ++x) {
-            float G = 0.f, K = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                G += gb[x][e];
-                K += kd[x][e];
-            }
-            float sufG = 0.f, preK = 0.f;
-#pragma unroll
-            for (int l = 0; l < 4; ++l) {
-                const float g2 = __shfl(G, lm + 16 * l);
-                const float k2 = __shfl(K, lm + 16 * l);
-                if (l > lk) sufG += g2;
-                if (l < lk) preK += k2;
-            }
-            float run = dbcv[x] + sufG;
-            float pre[4];
-            float acc = preK;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pre[e] = acc;
-                acc += kd[x][e];
-            }
-#pragma unroll
-            for (int e = 3; e >= 0; --e) {
-                run += gb[x][e];
-                dgm[x][e] = run + pre[e];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int x = 0; x < TPW; ++x)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dgm[x][e] = 0.f;
-        if (tid == 0) {
-            float A[BC], B[BC], C[BC];
-            for (int r = 0; r < BC; ++r) {
-                A[r] = (ra[0][r] + ra[1][r]) + (ra[2][r] + ra[3][r]);
-                B[r] = (rb[0][r] + rb[1][r]) + (rb[2][r] + rb[3][r]);
-                C[r] = (rc[0][r] + rc[1][r]) + (rc[2][r] + rc[3][r]);
-            }
-            float pre[BC];
-            float acc = 0.f;
-            for (int r = 0; r < BC; ++r) {
-                pre[r] = acc;
-                acc += C[r];
-            }
-            float run = (rd[0] + rd[1]) + (rd[2] + rd[3]);
-            for (int r = BC - 1; r >= 0; --r) {
-                run += A[r] + (r + 1 < BC ? B[r + 1] : 0.f);
-                dgs[r] = run + pre[r];
-            }
-        }
-        lds_barrier();
-    }
-    // ---- the prologue's backward and the stores
-    float apart = 0.f;
-#pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-        const int t = wave + NW * x;
-        float pdt = 0.f;
-        if (t < NT) {
-            const int i = 16 * t + lm;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lk + e;
-                if (r < nr) {
-                    const size_t tok = (size_t)(c0 + r);
-                    const float pq = (rq[0][r] + rq[1][r]) + (rq[2][r] + rq[3][r]);
-                    const float pk = (rk[0][r] + rk[1][r]) + (rk[2][r] + rk[3][r]);
-                    float dq, dk;
-                    if (p.l2norm) {
-                        const float inq = 1.f / L.nq[r], ink = 1.f / L.nk[r];
-                        dq = p.scale * inq * (dqh[x][e] - L.qh[r][i] * pq / (p.scale * p.scale));
-                        dk = ink * (dkh[x][e] - L.kh[r][i] * pk);
-                    } else {
-                        dq = p.scale * dqh[x][e];
-                        dk = dkh[x][e];
-                    }
-                    p.dq[(tok * H + h) * DK + i] = dq;
-                    p.dk[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * DK + i] = dk;
-                    if (!EJK) {
-                        const float xx = ea * (gl[x][e] + dtl[x]);
-                        // sigma'(x) = sigma(x) sigma(-x): no cancellation in
-                        // 1 - sigma(x) when the gate saturates
-                        const float dx = dgm[x][e] * p.lb * sigmoid_f(xx) * sigmoid_f(-xx);
-                        p.dg[(tok * H + h) * DK + i] = dx * ea;
-                        apart = fmaf(dx, xx, apart);
-                        pdt += dx * ea;
-                    }
-                }
+                p.dbeta[tok * H + h] = dbt[r];
+                if (p.dg) p.dg[tok * H + h] = dgs[r];
+            } else {
+                p.dbeta[tok * H + h] = dbt[r] * sigmoid_f(xb) * sigmoid_f(-xb);
             }
         }
         if (!EJK) {
-            // dt_bias partial of channel i: the sum over the four lane groups
-            pdt = xor_add<16>(pdt);
-            pdt = xor_add<32>(pdt);
-            if (t < NT && lk == 0) p.part_dt[((size_t)slot * H + h) * DK + 16 * t + lm] = pdt;
+            apart = wave_sum(apart);
+            if (lane == 0) red[wave] = apart;
+            lds_barrier();
+            if (tid == 0) p.part_a[(size_t)slot * H + h] = (red[0] + red[1]) + (red[2] + red[3]);
         }
-    }
+    };
+    if (has_b) {
+        // S entering the second chunk: one forward step through the first
+        // (its U from pass 1, its Kc and e^{b_C} from its operand block), in
+        // the layout of s0r: D[j][i] = sum_r U[r][j] Kc[r][i] with the lane
+        // supplying U[4 lk + u][16 jb + lm] and Kc[4 lk + u][16 t + lm]
+        {
+            using PL = PrepLayout<DK>;
+            const int sa = p.off[n] + ca;
+            const float* yu = p.ckYU + ((size_t)sa * H + h) * 2 * BC * dv;
+            const float* pb = p.prep + ((size_t)sa * H + h) * PL::SIZE;
+            for (int e = tid; e < BC * MAXD; e += BT) {
+                const int r = e / MAXD, j = e % MAXD;
+                U[r][j] = j < dv ? yu[(size_t)(BC + r) * dv + j] : 0.f;
+                Z[r][j] = j < DK ? (EJK ? pb[PL::KG + r * PL::RS + j] * pb[PL::RF + 2 * BC + r]
+                                        : pb[PL::KC + r * PL::RS + j])
+                                 : 0.f;
+            }
+            if (tid < DK) L.ec[tid] = EJK ? pb[PL::RF + 3 * BC] : pb[PL::EC + tid];
+            lds_barrier();
 #pragma unroll
-    for (int m = 0; m < NV; ++m) {
-        const int e = tid + m * BT;
-        const int r = e / MAXD, j = e % MAXD;
-        if (r < nr && j < dv) {
-            const size_t tok = (size_t)(c0 + r);
-            p.dv_out[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * dv + j] = L.beta[r] * xz[m];
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+                    const float ec = L.ec[16 * t + lm];
+#pragma unroll
+                    for (int jb = 0; jb < NJ; ++jb) {
+                        if (jb < nj) {
+                            bf32x4_t a = bf32x4_t{ec * s0r[x][jb].x, ec * s0r[x][jb].y, ec * s0r[x][jb].z,
+                                                  ec * s0r[x][jb].w};
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                a = bmfma4(U[4 * lk + u][16 * jb + lm], Z[4 * lk + u][16 * t + lm], a);
+                            s0r[x][jb] = make_float4(a[0], a[1], a[2], a[3]);
+                        }
+                    }
+                }
+            }
+            lds_barrier();
         }
-    }
-    if (tid < BC && tid < nr) {
-        const int r = tid;
-        const size_t tok = (size_t)(c0 + r);
-        if (EJK) {
-            p.dbeta[tok * H + h] = dbt[r];
-            if (p.dg) p.dg[tok * H + h] = dgs[r];
-        } else {
-            p.dbeta[tok * H + h] = dbt[r] * sigmoid_f(xb) * sigmoid_f(-xb);
+        run_chunk(ca + 1);
+        // dS leaving the first chunk: one backward step through the second,
+        // from its set-up, dO and Z still in LDS
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            if (t < NT) {
+                const int i = 16 * t + lm;
+                const float ec = L.ecc(i);
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb) {
+                    if (jb < nj) {
+                        bf32x4_t a = bf32x4_t{ec * d1r[x][jb].x, ec * d1r[x][jb].y, ec * d1r[x][jb].z,
+                                              ec * d1r[x][jb].w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int r = 4 * lk + u;
+                            a = bmfma4(dO[r][16 * jb + lm], L.qg(r, i), a);
+                            a = bmfma4(-L.beta[r] * Z[r][16 * jb + lm], L.kg(r, i), a);
+                        }
+                        d1r[x][jb] = make_float4(a[0], a[1], a[2], a[3]);
+                    }
+                }
+            }
         }
-    }
-    if (!EJK) {
-        apart = wave_sum(apart);
-        if (lane == 0) red[wave] = apart;
+        load_tile(s0r, S0p);
         lds_barrier();
-        if (tid == 0) p.part_a[(size_t)slot * H + h] = (red[0] + red[1]) + (red[2] + red[3]);
     }
+    run_chunk(ca);
+
 }
 
 // Parameter gradients summed over chunks (fixed order), and key/value
@@ -1509,8 +1606,9 @@ hipError_t launch_dk(const BwdParams& p, size_t slots, hipStream_t st)
     else hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, float>), sgrid, dim3(BT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess || slots == 0) return e;
-    if (p.in_bf16) hipLaunchKernelGGL((bwd_local<DK, EJK, uint16_t>), lgrid, dim3(BT), 0, st, p);
-    else hipLaunchKernelGGL((bwd_local<DK, EJK, float>), lgrid, dim3(BT), 0, st, p);
+    const dim3 pgrid((unsigned)((slots + (size_t)p.N + 1) / 2), (unsigned)p.H);
+    if (p.in_bf16) hipLaunchKernelGGL((bwd_local<DK, EJK, uint16_t>), pgrid, dim3(BT), 0, st, p);
+    else hipLaunchKernelGGL((bwd_local<DK, EJK, float>), pgrid, dim3(BT), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1522,7 +1620,9 @@ size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bo
     const size_t slots = bwd_slots(N, T, packed);
     const size_t ntok = packed ? (size_t)T : (size_t)N * T;
     size_t b = align256((size_t)(N + 1) * 4);
-    b += 2 * align256(slots * H * dk * dv * 4);
+    const size_t pslots = (slots + (size_t)N + 1) / 2;
+    b += align256((size_t)(N + 1) * 4);
+    b += 2 * align256(pslots * H * dk * dv * 4);
     b += align256(slots * H * 2 * BC * dv * 4) + align256(slots * H * BC * dv * 4);
     b += align256(slots * H * prep_floats(dk) * 4);
     b += align256(slots * H * 4) + align256(slots * H * dk * 4);
@@ -1544,13 +1644,17 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     p.scale = a.scale; p.lb = a.lower_bound; p.l2norm = a.l2norm;
     p.d_o = a.d_o; p.do_bf16 = a.do_bf16; p.dSf = a.d_final_state;
     p.dq = a.dq; p.dg = a.dg; p.dbeta = a.dbeta; p.dS0 = a.d_initial_state;
+    const size_t pslots = (slots + (size_t)a.N + 1) / 2;
     int32_t* off = reinterpret_cast<int32_t*>(w);
     w += align256((size_t)(a.N + 1) * 4);
+    int32_t* poff = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)(a.N + 1) * 4);
     p.off = off;
+    p.poff = poff;
     p.ckS = reinterpret_cast<float*>(w);
-    w += align256(slots * a.H * a.dk * a.dv * 4);
+    w += align256(pslots * a.H * a.dk * a.dv * 4);
     p.ckdS = reinterpret_cast<float*>(w);
-    w += align256(slots * a.H * a.dk * a.dv * 4);
+    w += align256(pslots * a.H * a.dk * a.dv * 4);
     p.ckYU = reinterpret_cast<float*>(w);
     w += align256(slots * a.H * 2 * BC * a.dv * 4);
     p.ckZ = reinterpret_cast<float*>(w);
@@ -1571,7 +1675,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st)
     }
     p.dk = grouped ? dkq : a.dk_out;
     p.dv_out = grouped ? dvq : a.dv_out;
-    hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(64), 0, st, a.cu, a.N, a.T, (int)slots, off);
+    hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(64), 0, st, a.cu, a.N, a.T, (int)slots, (int)pslots, off,
+                       poff);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (a.dk * 2 + (a.ejk ? 1 : 0)) {

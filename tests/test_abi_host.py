@@ -248,10 +248,11 @@ def test_backward_rejects_before_any_hip_call(over, status, msg):
 
 def test_backward_workspace_bytes():
     L = kda.lib()
-    # dense B2 T64 H4 d128: 8 chunk slots x 4 heads x (2 states of 64 KiB and
-    # the chunk's Y, U, Z of 8 KiB each), partials, offsets
+    # dense B2 T64 H4 d128: 4 chunk pairs x 4 heads x 2 states of 64 KiB (the
+    # state entering the pair and the adjoint leaving it), 8 chunk slots x 4
+    # heads x the chunk's Y, U, Z of 8 KiB each, partials, offsets
     need = L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 0, 128, 128)
-    assert need >= 8 * 4 * (2 * 128 * 128 + 3 * 16 * 128) * 4
+    assert need >= 4 * 4 * 2 * 128 * 128 * 4 + 8 * 4 * 3 * 16 * 128 * 4
     assert L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 2, 128, 128) > need   # grouped: per-head dk, dv
     assert L.kda_prefill_backward_workspace_bytes(0, 2, 64, 4, 0, 48, 128) == 0
     assert _backward(lower_bound=-6.0, flags=kda.EJK | kda.QK_L2NORM, B=0) == kda.KDA_OK   # EJK: no bound
