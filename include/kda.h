@@ -190,10 +190,11 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
  * KDA mode needs lower_bound >= -5 (KDA_EUNSUPPORTED otherwise): within 16
  * tokens the decay factors then stay inside float32's normal range.
  * The workspace (kda_prefill_backward_workspace_bytes) holds the state
- * entering and the state gradient leaving every 16-token chunk (2 x dk x dv x
- * 4 bytes per chunk and head), the chunk's Y = V - Kg S0, U and Z (3 x 16 x
- * dv x 4 bytes per chunk and head), per-chunk parameter partials and, with
- * grouped heads, per-head key/value gradients; it is caller-owned and must
+ * entering and the state gradient leaving every pair of 16-token chunks
+ * (2 x dk x dv x 4 bytes per pair and head), each chunk's Y = V - Kg S0, U
+ * and Z (3 x 16 x dv x 4 bytes per chunk and head) and column-independent
+ * operands, per-chunk parameter partials and, with grouped heads, per-head
+ * key/value gradients; it is caller-owned and must
  * not be shared by calls that may run concurrently.  With no tokens the call
  * still writes d_initial_state (= d_final_state, or 0) and zero parameter
  * gradients.
