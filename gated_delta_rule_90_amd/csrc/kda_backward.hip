@@ -62,7 +62,8 @@ namespace {
 
 constexpr int BC = 16;    // chunk length
 constexpr int BT = 256;   // threads per workgroup
-constexpr int TV = 16;    // state columns per scan workgroup
+constexpr int TV = 16;    // state columns per scan tile (a scan workgroup takes one or two)
+constexpr int kCUs = 256; // compute units of an MI355X
 constexpr int MAXD = 128;
 constexpr int SR = MAXD + 4;   // row stride of [16][<=128] tiles
 
@@ -541,14 +542,14 @@ __global__ __launch_bounds__(BT) void bwd_prep(BwdParams p)
 // (head, sequence), which read the same chunk operands, are given ids that
 // are equal modulo 8: they run on one XCD and share its L2.  Returns false
 // for the padding ids past the last (head, sequence).
-__device__ __forceinline__ bool scan_unit(const BwdParams& p, int& j0, int& h, int& n)
+__device__ __forceinline__ bool scan_unit(const BwdParams& p, int ng, int& j0, int& h, int& n)
 {
-    const int ntile = p.dv / TV;
+    const int ntile = p.dv / (TV * ng);
     const int id = blockIdx.x;
     const int xcd = id & 7, q = id >> 3;
     const int grp = (q / ntile) * 8 + xcd;
     if (grp >= p.H * p.N) return false;
-    j0 = (q % ntile) * TV;
+    j0 = (q % ntile) * TV * ng;
     h = grp % p.H;
     n = grp / p.H;
     return true;
@@ -561,19 +562,19 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // its last piece, stored again to the same place), so the count of memory
 // operations in flight is the same on every path and the waits for a load
 // issued chunks earlier stay exact.
-template <int NP, int N4>
+template <int NP, int N4, int NTH>
 __device__ __forceinline__ void fetch_block(f4v (&pf)[NP], const float* src)
 {
     const f4v* s4 = reinterpret_cast<const f4v*>(src);
 #pragma unroll
-    for (int m = 0; m < NP; ++m) pf[m] = s4[min((int)threadIdx.x + m * BT, N4 - 1)];
+    for (int m = 0; m < NP; ++m) pf[m] = s4[min((int)threadIdx.x + m * NTH, N4 - 1)];
 }
 
-template <int NP, int N4>
+template <int NP, int N4, int NTH>
 __device__ __forceinline__ void store_block(float* dst, const f4v (&pf)[NP])
 {
 #pragma unroll
-    for (int m = 0; m < NP; ++m) reinterpret_cast<f4v*>(dst)[min((int)threadIdx.x + m * BT, N4 - 1)] = pf[m];
+    for (int m = 0; m < NP; ++m) reinterpret_cast<f4v*>(dst)[min((int)threadIdx.x + m * NTH, N4 - 1)] = pf[m];
 }
 
 // An empty use of each register: the compiler waits here for the loads that
@@ -611,29 +612,32 @@ __device__ __forceinline__ void store_at(__amdgpu_buffer_rsrc_t r, int byte_off,
 // one after the copy, one after the per-wave partials of the product over
 // dk.  A buffer is rewritten two chunks later, after every wave has passed
 // the next chunk's first barrier.
-template <int DK>
+template <int DK, int NG>
 struct ScanLds {
     alignas(16) float P[2][PrepLayout<DK>::SIZE];
-    float X[2][BC][TV + 1];          // V (pass 1) or dO (pass 2) of the tile
-    float PU[BT / kWave][BC][TV + 1];
+    float X[NG][2][BC][TV + 1];          // V (pass 1) or dO (pass 2) of each group's tile
+    float PU[NG][BT / kWave][BC][TV + 1];
 };
 
 // Pass 1: the forward state carry per (16 state columns, head, sequence);
 // stores the state entering every chunk and the chunk's Y and U:
 //     Y = V - Kg S,  U = T diag(beta) Y,  S <- Diag(e^{b_C}) S + Kc^T U
-template <int DK, bool EJK, typename Tin>
-__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_fwd_scan(BwdParams p)
+template <int DK, bool EJK, typename Tin, int NG>
+__global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_fwd_scan(BwdParams p)
 {
     using PL = PrepLayout<DK>;
     constexpr int RS = PL::RS;
     constexpr int NT = DK / 16, NW = BT / kWave, TPW = (NT + NW - 1) / NW;
-    constexpr int N4 = PL::SIZE / 4, NP = (N4 + BT - 1) / BT;
-    __shared__ ScanLds<DK> L;
-    const int tid = threadIdx.x;
+    constexpr int N4 = PL::SIZE / 4, NP = (N4 + NG * BT - 1) / (NG * BT);
+    __shared__ ScanLds<DK, NG> L;
+    // NG groups of four waves, each on its own 16 state columns, share the
+    // chunk's operand block in LDS
+    const int tid = threadIdx.x % BT, grp = threadIdx.x / BT;
     const int lane = tid & 63, wave = tid >> 6;
     const int lm = lane & 15, lk = lane >> 4;
     int j0, h, n;
-    if (!scan_unit(p, j0, h, n)) return;
+    if (!scan_unit(p, NG, j0, h, n)) return;
+    j0 += grp * TV;
     const int H = p.H, dv = p.dv;
     const int hk = h / (H / p.Hkv);
     int t0, t1;
@@ -662,7 +666,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const int rr = tid / TV, jj = tid % TV;
     auto fetch = [&](f4v (&pf)[NP], Tin& pv, int c) __attribute__((always_inline)) {
         const int cs = t0 + c * BC;
-        fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
+        fetch_block<NP, N4, NG * BT>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
         pv = vv[((size_t)(cs + (cs + rr < t1 ? rr : 0)) * p.Hkv + hk) * dv + j0 + jj];
     };
     if (nck > 0) {
@@ -675,8 +679,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             const float* P = L.P[b];
             // the prefetched block to LDS first, then the state stores: a later
             // wait for a load then never waits for these stores as well
-            store_block<NP, N4>(L.P[b], pf);
-            L.X[b][rr][jj] = c0 + rr < t1 ? widen(pv) : 0.f;
+            store_block<NP, N4, NG * BT>(L.P[b], pf);
+            L.X[grp][b][rr][jj] = c0 + rr < t1 ? widen(pv) : 0.f;
             if constexpr (b == 0) {
                 // the state entering a pair's first chunk (c even); tiles t >= NT
                 // (idle waves at small dk) fall past the range
@@ -708,7 +712,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                     }
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
+                for (int e = 0; e < 4; ++e) L.PU[grp][wave][4 * lk + e][lm] = acc[e];
             }
             lds_barrier();
             // Y (rows 4 lk + u of column lm) and U = T diag(beta) Y, in every wave
@@ -717,9 +721,9 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int k = 4 * lk + u;
-                float ks = (L.PU[0][k][lm] + L.PU[1][k][lm]) + (L.PU[2][k][lm] + L.PU[3][k][lm]);
+                float ks = (L.PU[grp][0][k][lm] + L.PU[grp][1][k][lm]) + (L.PU[grp][2][k][lm] + L.PU[grp][3][k][lm]);
                 if (EJK) ks *= P[PL::RF + BC + k];
-                y[u] = L.X[b][k][lm] - ks;
+                y[u] = L.X[grp][b][k][lm] - ks;
                 U = bmfma4(P[PL::TI + lm * BC + k], P[PL::BE + k] * y[u], U);
             }
             {
@@ -764,19 +768,22 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 //     Z = T^T dU,  dY = diag(beta) Z
 //     dS <- Diag(e^{b_C}) dS + Qg^T dO - Kg^T dY
 // (EJK: qh, kh with the scalar row factors applied to dO, dY and dU rows).
-template <int DK, bool EJK, typename Tin>
-__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rev_scan(BwdParams p)
+template <int DK, bool EJK, typename Tin, int NG>
+__global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rev_scan(BwdParams p)
 {
     using PL = PrepLayout<DK>;
     constexpr int RS = PL::RS;
     constexpr int NT = DK / 16, NW = BT / kWave, TPW = (NT + NW - 1) / NW;
-    constexpr int N4 = PL::SIZE / 4, NP = (N4 + BT - 1) / BT;
-    __shared__ ScanLds<DK> L;
-    const int tid = threadIdx.x;
+    constexpr int N4 = PL::SIZE / 4, NP = (N4 + NG * BT - 1) / (NG * BT);
+    __shared__ ScanLds<DK, NG> L;
+    // NG groups of four waves, each on its own 16 state columns, share the
+    // chunk's operand block in LDS
+    const int tid = threadIdx.x % BT, grp = threadIdx.x / BT;
     const int lane = tid & 63, wave = tid >> 6;
     const int lm = lane & 15, lk = lane >> 4;
     int j0, h, n;
-    if (!scan_unit(p, j0, h, n)) return;
+    if (!scan_unit(p, NG, j0, h, n)) return;
+    j0 += grp * TV;
     const int H = p.H, dv = p.dv;
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
@@ -801,7 +808,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const int rr = tid / TV, jj = tid % TV;
     auto fetch = [&](f4v (&pf)[NP], uint32_t& pd, int c) __attribute__((always_inline)) {
         const int cs = t0 + c * BC;
-        fetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
+        fetch_block<NP, N4, NG * BT>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
         const size_t i = ((size_t)(cs + (cs + rr < t1 ? rr : 0)) * H + h) * dv + j0 + jj;
         pd = p.do_bf16 ? (uint32_t)static_cast<const uint16_t*>(p.d_o)[i] : static_cast<const uint32_t*>(p.d_o)[i];
     };
@@ -813,8 +820,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
         constexpr int b = decltype(bsel)::value;
             const int c0 = t0 + c * BC;
             const float* P = L.P[b];
-            store_block<NP, N4>(L.P[b], pf);
-            L.X[b][rr][jj] = c0 + rr < t1 ? __uint_as_float(p.do_bf16 ? pd << 16 : pd) : 0.f;
+            store_block<NP, N4, NG * BT>(L.P[b], pf);
+            L.X[grp][b][rr][jj] = c0 + rr < t1 ? __uint_as_float(p.do_bf16 ? pd << 16 : pd) : 0.f;
             {
                 // the state gradient leaving a pair's last chunk (c odd, or the
                 // sequence's last); the other chunks' stores get an empty range, as
@@ -856,11 +863,11 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int s2 = 4 * lk + u;
-                        acc = bmfma4(P[PL::GP + s2 * BC + lm], L.X[b][s2][lm], acc);
+                        acc = bmfma4(P[PL::GP + s2 * BC + lm], L.X[grp][b][s2][lm], acc);
                     }
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
+                for (int e = 0; e < 4; ++e) L.PU[grp][wave][4 * lk + e][lm] = acc[e];
             }
             lds_barrier();
             // Z = T^T dU in every wave: at step u the lane supplies T[4 lk + u][lm]
@@ -869,7 +876,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int k = 4 * lk + u;
-                const float du = (L.PU[0][k][lm] + L.PU[1][k][lm]) + (L.PU[2][k][lm] + L.PU[3][k][lm]);
+                const float du = (L.PU[grp][0][k][lm] + L.PU[grp][1][k][lm]) + (L.PU[grp][2][k][lm] + L.PU[grp][3][k][lm]);
                 Z = bmfma4(P[PL::TI + k * BC + lm], du, Z);
             }
             {
@@ -898,7 +905,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int r = 4 * lk + u;
-                        const float d = EJK ? L.X[b][r][lm] * P[PL::RF + r] : L.X[b][r][lm];
+                        const float d = EJK ? L.X[grp][b][r][lm] * P[PL::RF + r] : L.X[grp][b][r][lm];
                         a = bmfma4(P[PL::QG + r * RS + 16 * t + lm], d, a);
                     }
 #pragma unroll
@@ -1597,13 +1604,26 @@ hipError_t launch_dk(const BwdParams& p, size_t slots, hipStream_t st)
     // one then passes dL/d(final state) on as dL/d(initial state))
     const unsigned groups8 = (unsigned)((p.H * p.N + 7) / 8 * 8);
     if (groups8 == 0) return hipSuccess;
-    const dim3 sgrid(groups8 * (unsigned)(p.dv / TV));
-    if (p.in_bf16) hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, uint16_t>), sgrid, dim3(BT), 0, st, p);
-    else hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, float>), sgrid, dim3(BT), 0, st, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (p.in_bf16) hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, uint16_t>), sgrid, dim3(BT), 0, st, p);
-    else hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, float>), sgrid, dim3(BT), 0, st, p);
+    // Two 16-column tiles per workgroup (one load of each operand block for
+    // both) once that still gives every CU a workgroup; else one, for twice
+    // the workgroups
+    if (p.dv >= 2 * TV && (size_t)p.H * p.N * (p.dv / (2 * TV)) >= kCUs) {
+        const dim3 sgrid(groups8 * (unsigned)(p.dv / (2 * TV)));
+        if (p.in_bf16) hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, uint16_t, 2>), sgrid, dim3(2 * BT), 0, st, p);
+        else hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, float, 2>), sgrid, dim3(2 * BT), 0, st, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (p.in_bf16) hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, uint16_t, 2>), sgrid, dim3(2 * BT), 0, st, p);
+        else hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, float, 2>), sgrid, dim3(2 * BT), 0, st, p);
+    } else {
+        const dim3 sgrid(groups8 * (unsigned)(p.dv / TV));
+        if (p.in_bf16) hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, uint16_t, 1>), sgrid, dim3(BT), 0, st, p);
+        else hipLaunchKernelGGL((bwd_fwd_scan<DK, EJK, float, 1>), sgrid, dim3(BT), 0, st, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (p.in_bf16) hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, uint16_t, 1>), sgrid, dim3(BT), 0, st, p);
+        else hipLaunchKernelGGL((bwd_rev_scan<DK, EJK, float, 1>), sgrid, dim3(BT), 0, st, p);
+    }
     e = hipGetLastError();
     if (e != hipSuccess || slots == 0) return e;
     const dim3 pgrid((unsigned)((slots + (size_t)p.N + 1) / 2), (unsigned)p.H);

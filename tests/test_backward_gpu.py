@@ -121,6 +121,25 @@ def test_backward_b2_t1024_h8_d128_bf16(margin):
     _check(inp, 2e-2, seed=10, do_bf16=True, margin=margin, label="B2 T1024 H8")
 
 
+@pytest.mark.parametrize("ejk", [False, True], ids=["kda", "ejk"])
+def test_backward_two_tiles_per_scan_workgroup(ejk, margin):
+    """Enough (sequence, head) units that each scan workgroup carries two
+    16-column tiles over one shared copy of the chunk operands: 256 units at
+    dv = 32 (float32), 256 at dv = 128 (bf16) and 64 packed sequences of 8
+    heads with grouped keys (ragged, with empty ones)."""
+    inp = workloads.prefill_inputs(4, 50, 64, 32, 32, seed=1760 + ejk, dtype="f32", ejk=ejk, init_state=True)
+    say("backward fp32 B4 T50 H64 d32", "EJK" if ejk else "KDA")
+    _check(inp, 1e-5, seed=12)
+    inp = workloads.prefill_inputs(8, 80, 32, 128, 128, seed=1762 + ejk, ejk=ejk, init_state=True)
+    say("backward bf16 B8 T80 H32 d128", "EJK" if ejk else "KDA")
+    _check(inp, 2e-2, seed=13, do_bf16=True, margin=margin, label="B8 T80 H32 (two tiles per scan workgroup)")
+    lengths = [int(x) for x in np.random.default_rng(1764 + ejk).integers(0, 70, size=64)]
+    inp = workloads.prefill_inputs(1, 0, 8, 64, 64, seed=1766 + ejk, dtype="f32", ejk=ejk, init_state=True,
+                                   lengths=lengths, hkv=2)
+    say("backward fp32 64 packed sequences H8 Hkv2 d64", "EJK" if ejk else "KDA")
+    _check(inp, 1e-5, seed=14)
+
+
 def test_backward_unaligned_inputs_take_the_own_forward_scan():
     """A query 4 bytes past an allocation boundary: the first pass runs on the
     backward's own forward scan instead of the float32 chunked kernel (which
