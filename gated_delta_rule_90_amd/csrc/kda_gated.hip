@@ -50,9 +50,10 @@ namespace kda {
 namespace {
 
 constexpr int GC = 16;    // chunk rows
-constexpr int GJ = 16;    // state columns per scan workgroup
+constexpr int GJ = 16;    // state columns per scan tile (a scan workgroup takes one or two)
 constexpr int GTH = 256;  // threads per workgroup
 constexpr int GNW = GTH / kWave;
+constexpr int kGCUs = 256;   // compute units of an MI355X
 
 struct GatedParams {
     const void* q;
@@ -281,55 +282,58 @@ typedef float gf4v __attribute__((ext_vector_type(4)));
 // issues the same loads and stores (an index past the block is clamped to its
 // last piece), so the count of memory operations in flight is the same on
 // every path and the waits for a load issued chunks earlier stay exact.
-template <int NP, int N4>
+template <int NP, int N4, int NTH>
 __device__ __forceinline__ void gfetch_block(gf4v (&pf)[NP], const float* src)
 {
     const gf4v* s4 = reinterpret_cast<const gf4v*>(src);
 #pragma unroll
-    for (int m = 0; m < NP; ++m) pf[m] = s4[min((int)threadIdx.x + m * GTH, N4 - 1)];
+    for (int m = 0; m < NP; ++m) pf[m] = s4[min((int)threadIdx.x + m * NTH, N4 - 1)];
 }
 
-template <int NP, int N4>
+template <int NP, int N4, int NTH>
 __device__ __forceinline__ void gstore_block(float* dst, const gf4v (&pf)[NP])
 {
 #pragma unroll
-    for (int m = 0; m < NP; ++m) reinterpret_cast<gf4v*>(dst)[min((int)threadIdx.x + m * GTH, N4 - 1)] = pf[m];
+    for (int m = 0; m < NP; ++m) reinterpret_cast<gf4v*>(dst)[min((int)threadIdx.x + m * NTH, N4 - 1)] = pf[m];
 }
 
-template <int DK>
+// The operand blocks are shared by the NG column groups of a workgroup; the
+// rest is per group (cg).
+template <int DK, int NG>
 struct GScanLds {
     alignas(16) float P[2][GPrep<DK>::SIZE];
-    float X[2][GC][GJ + 1];    // v of the tile
-    float GV[2][GC][GJ + 1];   // gv of the tile (log2 units)
-    float PU[GNW][GC][GJ + 1];
-    float VC[GC][GJ + 1];      // e^{bv_C - bv} v
-    float VF[GC][GJ + 1];      // e^{bv_0 - bv} v
-    float ER[GC][GJ + 1];      // e^{bv}
-    float EL[GC][GJ + 1];      // e^{bv - bv_0}
-    float EVC[GJ];             // e^{bv_C}
-    int vwide;                 // some column's value log-decay leaves the factor range
+    float X[NG][2][GC][GJ + 1];    // v of the tile
+    float GV[NG][2][GC][GJ + 1];   // gv of the tile (log2 units)
+    float PU[NG][GNW][GC][GJ + 1];
+    float VC[NG][GC][GJ + 1];      // e^{bv_C - bv} v
+    float VF[NG][GC][GJ + 1];      // e^{bv_0 - bv} v
+    float ER[NG][GC][GJ + 1];      // e^{bv}
+    float EL[NG][GC][GJ + 1];      // e^{bv - bv_0}
+    float EVC[NG][GJ];             // e^{bv_C}
+    int vwide[NG];                 // some column's value log-decay leaves the factor range
 };
 
-// One workgroup per (16 state columns, head, sequence); ids dealt so that the
-// column tiles of one (sequence, head), which read the same blocks, share an
-// XCD (ids equal modulo 8).
-template <int DK, typename Tin, typename Tout>
-__global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void gated_scan(GatedParams p)
+// One workgroup per (NG tiles of 16 state columns, head, sequence): NG groups
+// of four waves, one tile each, over one LDS copy of each chunk's operand
+// block; ids dealt so that the workgroups of one (sequence, head), which read
+// the same blocks, share an XCD (ids equal modulo 8).
+template <int DK, typename Tin, typename Tout, int NG>
+__global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) void gated_scan(GatedParams p)
 {
     using PL = GPrep<DK>;
     constexpr int RS = PL::RS;
     constexpr int NT = DK / 16, TPW = (NT + GNW - 1) / GNW;
-    constexpr int N4 = PL::SIZE / 4, NP = (N4 + GTH - 1) / GTH;
-    __shared__ GScanLds<DK> L;
-    const int tid = threadIdx.x;
+    constexpr int N4 = PL::SIZE / 4, NP = (N4 + NG * GTH - 1) / (NG * GTH);
+    __shared__ GScanLds<DK, NG> L;
+    const int tid = threadIdx.x % GTH, cg = threadIdx.x / GTH;
     const int lane = tid & 63, wave = tid >> 6;
     const int lm = lane & 15, lk = lane >> 4;
     const int H = p.H, DV = p.dv;
-    const int ntile = DV / GJ;
+    const int ntile = DV / (GJ * NG);
     const int xcd = blockIdx.x & 7, qd = blockIdx.x >> 3;
     const int grp = (qd / ntile) * 8 + xcd;
     if (grp >= H * p.N) return;
-    const int j0 = (qd % ntile) * GJ, h = grp % H, n = grp / H;
+    const int j0 = (qd % ntile) * GJ * NG + cg * GJ, h = grp % H, n = grp / H;
     const int hk = h / (H / p.Hkv);
     int t0, t1;
     gseq_bounds(p, n, t0, t1);
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     Tin pva = 0, pvb = 0;
     float pga = 0.f, pgb = 0.f;
     auto fetch = [&](gf4v (&pf)[NP], Tin& pv, float& pg, int c) __attribute__((always_inline)) {
-        gfetch_block<NP, N4>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
+        gfetch_block<NP, N4, NG * GTH>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
         const size_t t = tok(c * GC + rr);
         pv = vv[(t * p.Hkv + hk) * DV + j0 + jj];
         pg = hv ? p.gv[(t * H + h) * DV + j0 + jj] : 0.f;
@@ -378,10 +382,10 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         constexpr int b = decltype(bsel)::value;
         const float* P = L.P[b];
         const int lc = min(GC, len - c * GC);
-        gstore_block<NP, N4>(L.P[b], pf);
-        L.X[b][rr][jj] = rr < lc ? widen(pv) : 0.f;
-        L.GV[b][rr][jj] = rr < lc ? pg * kLog2e : 0.f;
-        if (tid == 0) L.vwide = 0;
+        gstore_block<NP, N4, NG * GTH>(L.P[b], pf);
+        L.X[cg][b][rr][jj] = rr < lc ? widen(pv) : 0.f;
+        L.GV[cg][b][rr][jj] = rr < lc ? pg * kLog2e : 0.f;
+        if (tid == 0) L.vwide[cg] = 0;
         fetch(pf, pv, pg, min(c + 2, nch - 1));   // past the end: the last chunk again
         lds_barrier();
         // the inter-chunk read-out sum_i QE_ri S_ij: each wave its tiles' part
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) L.PU[wave][4 * lk + e][lm] = acc[e];
+            for (int e = 0; e < 4; ++e) L.PU[cg][wave][4 * lk + e][lm] = acc[e];
         }
         // the value-axis factors, a thread per (row rr, column jj): the column's
         // cumulative log-decay to row rr and over the chunk
@@ -407,17 +411,17 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
             float bc = 0.f, br = 0.f;
 #pragma unroll
             for (int s2 = 0; s2 < GC; ++s2) {
-                bc += L.GV[b][s2][jj];
+                bc += L.GV[cg][b][s2][jj];
                 if (s2 == rr) br = bc;
             }
-            const float b0 = L.GV[b][0][jj];
-            const float x = L.X[b][rr][jj];
-            L.VC[rr][jj] = x * __builtin_amdgcn_exp2f(bc - br);
-            L.ER[rr][jj] = __builtin_amdgcn_exp2f(br);
-            L.VF[rr][jj] = x * __builtin_amdgcn_exp2f(b0 - br);
-            L.EL[rr][jj] = __builtin_amdgcn_exp2f(br - b0);
-            if (!(fabsf(br - b0) <= 120.f)) L.vwide = 1;
-            if (rr == GC - 1) L.EVC[jj] = __builtin_amdgcn_exp2f(bc);
+            const float b0 = L.GV[cg][b][0][jj];
+            const float x = L.X[cg][b][rr][jj];
+            L.VC[cg][rr][jj] = x * __builtin_amdgcn_exp2f(bc - br);
+            L.ER[cg][rr][jj] = __builtin_amdgcn_exp2f(br);
+            L.VF[cg][rr][jj] = x * __builtin_amdgcn_exp2f(b0 - br);
+            L.EL[cg][rr][jj] = __builtin_amdgcn_exp2f(br - b0);
+            if (!(fabsf(br - b0) <= 120.f)) L.vwide[cg] = 1;
+            if (rr == GC - 1) L.EVC[cg][jj] = __builtin_amdgcn_exp2f(bc);
         }
         lds_barrier();
         // the outputs (wave 0): O = e^{bv} (QE S) + e^{bv - bv_0} A (e^{bv_0 - bv} v),
@@ -425,12 +429,12 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         // the scaled v[4 lk + u][lm] at step u); element by element when wide
         if (wave == 0) {
             gf32x4_t ai = gf32x4_t{0.f, 0.f, 0.f, 0.f};
-            const bool ew = hv && L.vwide;
+            const bool ew = hv && L.vwide[cg];
             if (!ew) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int s2 = 4 * lk + u;
-                    ai = gmfma4(P[PL::AM + lm * GC + s2], hv ? L.VF[s2][lm] : L.X[b][s2][lm], ai);
+                    ai = gmfma4(P[PL::AM + lm * GC + s2], hv ? L.VF[cg][s2][lm] : L.X[cg][b][s2][lm], ai);
                 }
             }
             float bvs[GC];
@@ -438,7 +442,7 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                 float acc = 0.f;
 #pragma unroll
                 for (int s2 = 0; s2 < GC; ++s2) {
-                    acc += L.GV[b][s2][lm];
+                    acc += L.GV[cg][b][s2][lm];
                     bvs[s2] = acc;
                 }
             }
@@ -452,16 +456,16 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * lk + e;
-                const float oi = (L.PU[0][r][lm] + L.PU[1][r][lm]) + (L.PU[2][r][lm] + L.PU[3][r][lm]);
+                const float oi = (L.PU[cg][0][r][lm] + L.PU[cg][1][r][lm]) + (L.PU[cg][2][r][lm] + L.PU[cg][3][r][lm]);
                 float o;
                 if (!hv) {
                     o = oi + ai[e];
                 } else if (!ew) {
-                    o = L.ER[r][lm] * oi + L.EL[r][lm] * ai[e];
+                    o = L.ER[cg][r][lm] * oi + L.EL[cg][r][lm] * ai[e];
                 } else {
-                    o = L.ER[r][lm] * oi;
+                    o = L.ER[cg][r][lm] * oi;
                     for (int s2 = 0; s2 <= r; ++s2)
-                        o = fmaf(P[PL::AM + r * GC + s2] * __builtin_amdgcn_exp2f(bvs[r] - bvs[s2]), L.X[b][s2][lm], o);
+                        o = fmaf(P[PL::AM + r * GC + s2] * __builtin_amdgcn_exp2f(bvs[r] - bvs[s2]), L.X[cg][b][s2][lm], o);
                 }
                 const int trow = p.reverse ? lc - 1 - r : r;   // negative past the chunk: out of range
                 const int boff = (trow * H * DV + lm) * (int)sizeof(Tout);
@@ -478,13 +482,13 @@ __global__ __launch_bounds__(GTH) __attribute__((amdgpu_waves_per_eu(2))) void g
             const int t = wave + GNW * x;
             if (t < NT) {
                 gf32x4_t a = S[x];
-                const float evc = hv ? L.EVC[lm] : 1.f;
+                const float evc = hv ? L.EVC[cg][lm] : 1.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[e] *= P[PL::EKC + 16 * t + 4 * lk + e] * evc;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int s2 = 4 * lk + u;
-                    a = gmfma4(P[PL::KC + s2 * RS + 16 * t + lm], hv ? L.VC[s2][lm] : L.X[b][s2][lm], a);
+                    a = gmfma4(P[PL::KC + s2 * RS + 16 * t + lm], hv ? L.VC[cg][s2][lm] : L.X[cg][b][s2][lm], a);
                 }
                 S[x] = a;
             }
@@ -527,7 +531,14 @@ hipError_t launch_typed(const GatedParams& p, size_t slots, hipStream_t st)
     }
     const unsigned groups8 = (unsigned)((p.H * p.N + 7) / 8 * 8);
     if (groups8 == 0) return hipSuccess;
-    hipLaunchKernelGGL((gated_scan<DK, Tin, Tout>), dim3(groups8 * (unsigned)(p.dv / GJ)), dim3(GTH), 0, st, p);
+    // two column tiles per workgroup (one LDS copy of each block for both)
+    // once that still gives every CU a workgroup; else one
+    if (p.dv >= 2 * GJ && (size_t)p.H * p.N * (p.dv / (2 * GJ)) >= kGCUs)
+        hipLaunchKernelGGL((gated_scan<DK, Tin, Tout, 2>), dim3(groups8 * (unsigned)(p.dv / (2 * GJ))),
+                           dim3(2 * GTH), 0, st, p);
+    else
+        hipLaunchKernelGGL((gated_scan<DK, Tin, Tout, 1>), dim3(groups8 * (unsigned)(p.dv / GJ)), dim3(GTH), 0, st,
+                           p);
     return hipGetLastError();
 }
 

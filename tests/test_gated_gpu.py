@@ -77,6 +77,26 @@ def test_gated_varlen_grouped_bf16(reverse):
     _check(x, reverse, bf16=True, tol=2e-2)
 
 
+@pytest.mark.parametrize("reverse", [False, True], ids=["fwd", "rev"])
+def test_gated_two_tiles_per_scan_workgroup(reverse):
+    """Enough (sequence, head) units that each scan workgroup carries two
+    16-column tiles over one shared copy of the chunk operands: 256 units at
+    dv = 32 with value gates strong enough in some columns only for the
+    element-by-element path (float32), 256 units at dv = 128 (bf16), and 64
+    packed sequences of 4 grouped heads."""
+    x = _inputs(110 + reverse, 4, 40, 64, 64, 32, 32, ("g", "gk", "gv", "g_gamma"))
+    x["gv"][..., :5] *= 40.0
+    say("gated two tiles fp32 B4 T40 H64 d32", "reverse" if reverse else "forward")
+    _check(x, reverse)
+    x = _inputs(112 + reverse, 8, 50, 32, 32, 128, 128, ("gk", "gv"), bf16=True)
+    say("gated two tiles bf16 B8 T50 H32 d128", "reverse" if reverse else "forward")
+    _check(x, reverse, bf16=True, tol=2e-2)
+    lengths = [int(v) for v in np.random.default_rng(114 + reverse).integers(0, 40, size=64)]
+    x = _inputs(116 + reverse, 0, 0, 4, 2, 64, 128, ("g", "gk", "g_gamma"), lengths=lengths)
+    say("gated two tiles, 64 packed sequences", "reverse" if reverse else "forward")
+    _check(x, reverse)
+
+
 def test_gated_unaligned_rows():
     """A query 4 bytes past an allocation boundary: bitwise equal to the
     aligned call on the same values (the kernel's loads need no alignment)."""
