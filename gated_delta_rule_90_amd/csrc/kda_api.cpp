@@ -248,6 +248,8 @@ kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, k
                     (double)lower_bound);
     if (H > 65535 || N > 65535)
         return fail(KDA_EUNSUPPORTED, "kda_prefill_backward: H and the number of sequences must be <= 65535");
+    if ((long long)H * N > (1LL << 26))
+        return fail(KDA_EUNSUPPORTED, "kda_prefill_backward: H times the number of sequences must be <= 2^26");
     if (!cu_seqlens && (long long)B * T > 0x7fffffffLL)
         return fail(KDA_EUNSUPPORTED, "kda_prefill_backward: B * T must fit in 31 bits");
     // with no tokens the passes still run: they carry dL/d(final state) to
@@ -324,6 +326,8 @@ kda_status_t kda_recurrent_attention(const void* q, const void* k, const void* v
         return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: bf16 output needs bf16 input");
     if (H > 65535 || N > 65535)
         return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: H and the number of sequences must be <= 65535");
+    if ((long long)H * N > (1LL << 26))
+        return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: H times the number of sequences must be <= 2^26");
     if (!cu_seqlens && (long long)B * T > 0x7fffffffLL)
         return fail(KDA_EUNSUPPORTED, "kda_recurrent_attention: B * T must fit in 31 bits");
     if (N == 0 || (!has_tokens && !final_state)) return ok();

@@ -175,7 +175,9 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
  * Inputs q ... lower_bound, cu_seqlens, num_seqs, B, T, H, Hkv, dk, dv and
  * the flags KDA_QK_L2NORM / KDA_EJK are kda_prefill's, with the same shapes
  * and meaning (KDA_CHUNKED is accepted and changes nothing: the backward is
- * always chunk-parallel, in float32 arithmetic, chunks of 16 tokens).
+ * always chunk-parallel, in float32 arithmetic, chunks of 16 tokens).  H and
+ * the number of sequences at most 65535, their product at most 2^26
+ * (KDA_EUNSUPPORTED beyond).
  *   d_o              [B, T, H, dv] in do_dtype (KDA_F32 or KDA_BF16)
  *   d_final_state    [N, H, dk, dv] float32, NULL = 0
  * Outputs (device, float32, caller-allocated, fully written):
@@ -228,7 +230,7 @@ kda_status_t kda_prefill_backward(const void* q, const void* k, const void* v, k
  * (initial NULL = zeros; final NULL = not returned); o [B, T, H, dv]
  * (out_dtype; bf16 needs bf16 input).  scale <= 0 or NaN selects 1/sqrt(dk).
  * Grouped heads, cu_seqlens and num_seqs as for kda_prefill.  dk, dv in
- * {16, 32, 64, 128}.  Computed in float32 in chunks of 16 tokens (an exact
+ * {16, 32, 64, 128}; H times the number of sequences at most 2^26.  Computed in float32 in chunks of 16 tokens (an exact
  * regrouping of the token loop): the chunks' key-axis operands are formed
  * in parallel into the workspace, then each (sequence, head, 16 state
  * columns) walks its chunks in order.  The workspace

@@ -237,6 +237,7 @@ BACKWARD_ERRORS = [
     (dict(dk=48), kda.KDA_EUNSUPPORTED, "dk and dv"),
     (dict(ws=None), kda.KDA_EINVAL, "workspace"),
     (dict(ws=P, ws_bytes=1024), kda.KDA_EINVAL, "workspace"),
+    (dict(B=1, T=0, H=65535, cu=P, num_seqs=65535), kda.KDA_EUNSUPPORTED, "times the number of sequences"),
 ]
 
 
@@ -277,6 +278,7 @@ GATED_ERRORS = [
     (dict(in_dtype=kda.F32), kda.KDA_EUNSUPPORTED, "bf16 output needs bf16 input"),
     (dict(ws=None), kda.KDA_EINVAL, "workspace"),
     (dict(ws=P, ws_bytes=1024), kda.KDA_EINVAL, "workspace"),
+    (dict(B=1, T=0, H=65535, cu=P, num_seqs=65535), kda.KDA_EUNSUPPORTED, "times the number of sequences"),
 ]
 
 
