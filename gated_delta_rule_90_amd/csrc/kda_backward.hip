@@ -321,9 +321,12 @@ __device__ __forceinline__ float widen(Tin x)
 template <int DK>
 struct PrepLayout {
     static constexpr int RS = DK + 4;
-    static constexpr int QG = 0, KG = BC * RS, KC = 2 * BC * RS, TI = 3 * BC * RS, GP = TI + BC * BC;
-    static constexpr int EC = GP + BC * BC, BE = EC + DK, RF = BE + BC;
-    static constexpr int SIZE = (RF + 4 * BC + 63) / 64 * 64;
+    // what the forward scan reads comes first (it copies [0, FWD) only)
+    static constexpr int KG = 0, KC = BC * RS, TI = 2 * BC * RS, EC = TI + BC * BC, BE = EC + DK, RF = BE + BC;
+    static constexpr int FWD = (RF + 4 * BC + 63) / 64 * 64;
+    // then Qg and P, which only the reverse scan reads
+    static constexpr int QG = FWD, GP = QG + BC * RS;
+    static constexpr int SIZE = (GP + BC * BC + 63) / 64 * 64;
 };
 
 // The sequence, first row and row count of chunk slot `slot`.
@@ -628,7 +631,7 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     using PL = PrepLayout<DK>;
     constexpr int RS = PL::RS;
     constexpr int NT = DK / 16, NW = BT / kWave, TPW = (NT + NW - 1) / NW;
-    constexpr int N4 = PL::SIZE / 4, NP = (N4 + NG * BT - 1) / (NG * BT);
+    constexpr int N4 = PL::FWD / 4, NP = (N4 + NG * BT - 1) / (NG * BT);   // Qg and P unused here
     __shared__ ScanLds<DK, NG> L;
     // NG groups of four waves, each on its own 16 state columns, share the
     // chunk's operand block in LDS
