@@ -153,6 +153,15 @@ __device__ __forceinline__ int seq_chunks(const int32_t* off, int n, int t0, int
     return min((t1 - t0 + BC - 1) / BC, off[n + 1] - off[n]);
 }
 
+// The logistic on the hardware exponential and reciprocal (each within about
+// an ulp): 1 / (1 + 2^(-x log2 e)).  Rounding x log2 e adds a relative error
+// of about |x| 2^-24, under 1e-6 for the |x| < 20 that gate arguments and
+// beta logits take; large |x| saturates to 0 or 1.
+__device__ __forceinline__ float sigmoid_fast(float x)
+{
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
 // ---------------------------------------------------------------------------
 // The state-independent part of one chunk, in LDS: normalised rows, decay
 // factors, the Gram products GA (strict lower, without beta) and GP (lower).
@@ -165,7 +174,7 @@ struct ChunkLds {
     float ecb[BC][SR];   // KDA: e^{b_C - b}
     float ec[MAXD];      // KDA: e^{b_C}
     float beta[BC];
-    float nq[BC], nk[BC];
+    float nq[BC], nk[BC];   // inverse row norms 1 / sqrt(sum x^2 + eps)
     float sb[BC], seb[BC], sebp[BC], secb[BC];   // EJK: b, e^b, e^{b'}, e^{b_C - b}
     float sec;                                   // EJK: e^{b_C}
     float GA[BC][BC + 1];
@@ -207,7 +216,7 @@ __device__ void setup_rest(ChunkLds<DK, EJK>& L, const BwdParams& p)
         ss = xor_add<1>(ss);
         ss = xor_add<2>(ss);
         ss = xor_add<4>(ss);
-        if (part == 0) (pr < 16 ? L.nq : L.nk)[r] = sqrtf(ss + kNormEps);
+        if (part == 0) (pr < 16 ? L.nq : L.nk)[r] = 1.f / sqrtf(ss + kNormEps);
     }
     if (!EJK) {
         if (tid < DK) {
@@ -240,8 +249,8 @@ __device__ void setup_rest(ChunkLds<DK, EJK>& L, const BwdParams& p)
     for (int m = 0; m < NE; ++m) {
         const int e = tid + m * BT;
         const int r = e / DK, i = e % DK;
-        L.qh[r][i] = p.l2norm ? p.scale * L.qh[r][i] / L.nq[r] : p.scale * L.qh[r][i];
-        L.kh[r][i] = p.l2norm ? L.kh[r][i] / L.nk[r] : L.kh[r][i];
+        L.qh[r][i] = p.l2norm ? p.scale * L.qh[r][i] * L.nq[r] : p.scale * L.qh[r][i];
+        L.kh[r][i] = p.l2norm ? L.kh[r][i] * L.nk[r] : L.kh[r][i];
     }
     if (EJK && tid < BC) {
         const int r = tid;
@@ -397,14 +406,14 @@ __global__ __launch_bounds__(BT) void bwd_prep(BwdParams p)
             L.KG[r * RS + i] = ok ? kv : 0.f;
             if (!EJK) {
                 const float x = ea * (p.g[(tok * H + h) * DK + i] + dtb);
-                L.KI[r * RS + i] = ok ? lb2 * sigmoid_f(x) : 0.f;
+                L.KI[r * RS + i] = ok ? lb2 * sigmoid_fast(x) : 0.f;
             }
         }
         if (tid < BC) {
             const bool ok = tid < nr;
             const size_t tok = (size_t)(c0 + (ok ? tid : 0));
             const float bl = p.beta[tok * H + h];
-            L.BE[tid] = ok ? (EJK ? bl : sigmoid_f(bl)) : 0.f;
+            L.BE[tid] = ok ? (EJK ? bl : sigmoid_fast(bl)) : 0.f;
             if (EJK) L.SB[tid] = (ok && p.g) ? p.g[tok * H + h] * kLog2e : 0.f;
         }
     }
@@ -601,6 +610,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t store_range(const float* base,
 __device__ __forceinline__ void store_at(__amdgpu_buffer_rsrc_t r, int byte_off, float v)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
+}
+
+// Buffer accesses for the local pass: a resource over [base, base + bytes)
+// and a 32-bit byte offset per lane, so addresses are 32-bit adds; a load at
+// an offset past the end reads zero and a store there is dropped (the whole
+// offset goes in the lane's offset register: the scalar offset field is not
+// range-checked).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
+constexpr uint32_t kNoOffset = 0x80000000u;   // past every resource here (all < 2^31 bytes)
+
+// A resource over rows r .. nr - 1 of a block whose rows are `stride` bytes
+// apart and `width` bytes wide (none when r >= nr): a lane then addresses its
+// row relative to row r in its own offset, which the range check covers,
+// and its place within the row in the scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int r, int nr, int stride, int width)
+{
+    const int n = nr - r;
+    return brsrc(base + (size_t)r * stride, n > 0 ? (n - 1) * stride + width : 0);
 }
 
 // The scans' register layout: the dk x 16 state (or state gradient) tile is
@@ -995,20 +1040,24 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const bool has_b = ca + 1 < nck;
     const int nj = dv / 16;
     const float ea = EJK ? 0.f : expf(p.a_log[h]);
+    const float iss = 1.f / (p.scale * p.scale);
     // ---- loads.  S0 and dS1 rows of this wave's channel tiles, 16 bytes per
     // lane per 16 columns (lane (lm, lk): row 16 t + lm, columns 16 jb + 4 lk ..;
     // a 16-column tile's rows are 64 bytes apart)
     float4 s0r[TPW][NJ], d1r[TPW][NJ];
     const float* S0p = p.ckS + ((size_t)ps * H + h) * DK * dv;
+    // (16-column tiles past dv fall outside the resource and read as zero)
     auto load_tile = [&](float4 (&dst)[TPW][NJ], const float* src) __attribute__((always_inline)) {
+        const auto rs = brsrc(src, nj * DK * TV * 4);
+        const int vo = ((16 * wave + lm) * TV + 4 * lk) * 4;
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
-            const int t = wave + NW * x;
 #pragma unroll
             for (int jb = 0; jb < NJ; ++jb) {
-                const bool ok = t < NT && jb < nj;
-                const size_t o = ((size_t)jb * DK + 16 * t + lm) * TV + 4 * lk;
-                dst[x][jb] = ok ? *reinterpret_cast<const float4*>(src + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const uint32_t __attribute__((ext_vector_type(4))) u =
+                    __builtin_amdgcn_raw_buffer_load_b128(rs, vo + ((jb * DK + 16 * NW * x) * TV) * 4, 0, 0);
+                dst[x][jb] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                         __uint_as_float(u.w));
             }
         }
     };
@@ -1018,38 +1067,60 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     auto run_chunk = [&](const int c) __attribute__((always_inline)) {
         const int slot = p.off[n] + c;
         const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
-        // the rows of q, k and the gate (element e = tid + m BT: row e / DK, channel e % DK)
-        const Tin* qq = static_cast<const Tin*>(p.q);
-        const Tin* kk = static_cast<const Tin*>(p.k);
+        // the chunk's inputs through buffer resources over its rows: rows past
+        // the chunk's end read as zero.  q, k and the gate: element
+        // e = tid + m BT, row e / DK, channel e % DK
+        const int qs = H * DK, ks = Hkv * DK;   // row strides (elements)
+        constexpr int SQ = (int)sizeof(Tin);
+        const char* qsrc = reinterpret_cast<const char*>(static_cast<const Tin*>(p.q) + ((size_t)c0 * H + h) * DK);
+        const char* ksrc = reinterpret_cast<const char*>(static_cast<const Tin*>(p.k) + ((size_t)c0 * Hkv + hk) * DK);
+        const char* gsrc = EJK ? nullptr : reinterpret_cast<const char*>(p.g + ((size_t)c0 * H + h) * DK);
         Tin xq[NE], xk[NE];
         float xg[EJK ? 1 : NE];
+        {
+            // step m covers rows from m BT / DK on; the lane's row within the
+            // step is tid / DK
+            const int r0 = tid / DK, i = tid % DK;
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + m * BT;
-            const int r = e / DK, i = e % DK;
-            const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
-            xq[m] = qq[(tok * H + h) * DK + i];
-            xk[m] = kk[(tok * Hkv + hk) * DK + i];
-            if (!EJK) xg[m] = p.g[(tok * H + h) * DK + i];
+            for (int m = 0; m < NE; ++m) {
+                const int rm = m * (BT / DK);
+                xq[m] = bload<Tin>(rows_rsrc(qsrc, rm, nr, qs * SQ, DK * SQ), (r0 * qs + i) * SQ);
+                xk[m] = bload<Tin>(rows_rsrc(ksrc, rm, nr, ks * SQ, DK * SQ), (r0 * ks + i) * SQ);
+                if (!EJK) xg[m] = bload<float>(rows_rsrc(gsrc, rm, nr, qs * 4, DK * 4), (r0 * qs + i) * 4);
+            }
         }
         const float dtb_row = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
-        // dO (raw bits), U, Z, Y: element e = tid + m BT, row e / MAXD, column e % MAXD
+        // dO (raw bits), U, Z, Y: element e = tid + m BT, row e / MAXD, column
+        // e % MAXD (columns past dv are read, then replaced by zero)
         uint32_t xo[NV];
         float xu[NV], xz[NV], xy[NV];
         {
-            const float* yu = p.ckYU + ((size_t)slot * H + h) * 2 * BC * dv;
-            const float* zz = p.ckZ + ((size_t)slot * H + h) * BC * dv;
+            const int os = H * dv, so = p.do_bf16 ? 2 : 4;
+            const auto bo = brsrc(static_cast<const char*>(p.d_o) + ((size_t)c0 * H + h) * dv * so,
+                                  ((nr - 1) * os + dv) * so);
+            const auto by = brsrc(p.ckYU + ((size_t)slot * H + h) * 2 * BC * dv, 2 * BC * dv * 4);
+            const auto bz = brsrc(p.ckZ + ((size_t)slot * H + h) * BC * dv, BC * dv * 4);
+            const int r0 = tid / MAXD, j = tid % MAXD;
+            const bool ok = j < dv;
+            // dO kept as loaded (bf16 bits or float32 bits), widened where used
+            if (p.do_bf16) {
+#pragma unroll
+                for (int m = 0; m < NV; ++m)
+                    xo[m] = bload<uint16_t>(bo, ((r0 + m * (BT / MAXD)) * os + j) * 2);
+            } else {
+#pragma unroll
+                for (int m = 0; m < NV; ++m)
+                    xo[m] = bload<uint32_t>(bo, ((r0 + m * (BT / MAXD)) * os + j) * 4);
+            }
 #pragma unroll
             for (int m = 0; m < NV; ++m) {
-                const int e = tid + m * BT;
-                const int r = e / MAXD, j = e % MAXD;
-                const bool ok = j < dv;   // rows past nr: Y, U and Z are stored as zero
-                const size_t od = ((size_t)(c0 + (r < nr ? r : 0)) * H + h) * dv + j;
-                if (p.do_bf16) xo[m] = ok && r < nr ? (uint32_t)static_cast<const uint16_t*>(p.d_o)[od] << 16 : 0u;
-                else xo[m] = ok && r < nr ? __float_as_uint(static_cast<const float*>(p.d_o)[od]) : 0u;
-                xy[m] = ok ? yu[(size_t)r * dv + j] : 0.f;
-                xu[m] = ok ? yu[(size_t)(BC + r) * dv + j] : 0.f;
-                xz[m] = ok ? zz[(size_t)r * dv + j] : 0.f;
+                const int r = r0 + m * (BT / MAXD);
+                const float y = bload<float>(by, (r * dv + j) * 4);
+                const float u = bload<float>(by, ((BC + r) * dv + j) * 4);
+                const float z = bload<float>(bz, (r * dv + j) * 4);
+                xy[m] = ok ? y : 0.f;
+                xu[m] = ok ? u : 0.f;
+                xz[m] = ok ? z : 0.f;
             }
         }
         float xb = 0.f, xgs = 0.f;
@@ -1058,7 +1129,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             xb = p.beta[tok * H + h];
             xgs = (EJK && p.g) ? p.g[tok * H + h] : 0.f;
         }
-        // KDA: the gate and dt_bias of the elements this lane owns in the MFMA layout
+        // KDA: the gate and dt_bias of the elements this lane owns in the MFMA
+        // layout (row 4 lk + e, channel 16 t + lm)
         float gl[TPW][4], dtl[TPW];
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
@@ -1067,9 +1139,9 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             dtl[x] = ok && p.dt_bias ? p.dt_bias[(size_t)(16 * t + lm) * H + h] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lk + e;
-                const size_t tok = (size_t)(c0 + (r < nr ? r : 0));
-                gl[x][e] = ok ? p.g[(tok * H + h) * DK + 16 * t + lm] : 0.f;
+                // rows from e on; the lane's row 4 lk + e is 4 lk past the first
+                const float v = EJK ? 0.f : bload<float>(rows_rsrc(gsrc, e, nr, qs * 4, DK * 4), (4 * lk * qs + 16 * t + lm) * 4);
+                gl[x][e] = ok ? v : 0.f;
             }
         }
         // ---- to LDS: the raw rows, gate activations (log2 units), beta; dO, U, Z
@@ -1082,18 +1154,18 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                 const bool ok = r < nr;
                 L.qh[r][i] = ok ? widen(xq[m]) : 0.f;
                 L.kh[r][i] = ok ? widen(xk[m]) : 0.f;
-                if (!EJK) L.eb[r][i] = ok ? lb2 * sigmoid_f(ea * (xg[m] + dtb_row)) : 0.f;
+                if (!EJK) L.eb[r][i] = ok ? lb2 * sigmoid_fast(ea * (xg[m] + dtb_row)) : 0.f;
             }
             if (tid < BC) {
                 const bool ok = tid < nr;
-                L.beta[tid] = ok ? (EJK ? xb : sigmoid_f(xb)) : 0.f;
+                L.beta[tid] = ok ? (EJK ? xb : sigmoid_fast(xb)) : 0.f;
                 if (EJK) L.sb[tid] = ok ? xgs * kLog2e : 0.f;
             }
 #pragma unroll
             for (int m = 0; m < NV; ++m) {
                 const int e = tid + m * BT;
                 const int r = e / MAXD, j = e % MAXD;
-                dO[r][j] = __uint_as_float(xo[m]);
+                dO[r][j] = j < dv ? __uint_as_float(p.do_bf16 ? xo[m] << 16 : xo[m]) : 0.f;
                 U[r][j] = xu[m];
                 Z[r][j] = xz[m];
                 // Z.Y of row r: a partial per wave (each wave covers half a row)
@@ -1373,7 +1445,12 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
             }
             lds_barrier();
         }
-        // ---- the prologue's backward and the stores
+        // ---- the prologue's backward and the stores, through buffer resources
+        // over the chunk's rows (rows past its end are dropped)
+        const int hs = grouped ? H : Hkv, hh = grouped ? h : hk;
+        const char* dqdst = reinterpret_cast<const char*>(p.dq + ((size_t)c0 * H + h) * DK);
+        const char* dkdst = reinterpret_cast<const char*>(p.dk + ((size_t)c0 * hs + hh) * DK);
+        const char* dgdst = EJK ? nullptr : reinterpret_cast<const char*>(p.dg + ((size_t)c0 * H + h) * DK);
         float apart = 0.f;
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
@@ -1384,30 +1461,31 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * lk + e;
-                    if (r < nr) {
-                        const size_t tok = (size_t)(c0 + r);
-                        const float pq = (rq[0][r] + rq[1][r]) + (rq[2][r] + rq[3][r]);
-                        const float pk = (rk[0][r] + rk[1][r]) + (rk[2][r] + rk[3][r]);
-                        float dq, dk;
-                        if (p.l2norm) {
-                            const float inq = 1.f / L.nq[r], ink = 1.f / L.nk[r];
-                            dq = p.scale * inq * (dqh[x][e] - L.qh[r][i] * pq / (p.scale * p.scale));
-                            dk = ink * (dkh[x][e] - L.kh[r][i] * pk);
-                        } else {
-                            dq = p.scale * dqh[x][e];
-                            dk = dkh[x][e];
-                        }
-                        p.dq[(tok * H + h) * DK + i] = dq;
-                        p.dk[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * DK + i] = dk;
-                        if (!EJK) {
-                            const float xx = ea * (gl[x][e] + dtl[x]);
-                            // sigma'(x) = sigma(x) sigma(-x): no cancellation in
-                            // 1 - sigma(x) when the gate saturates
-                            const float dx = dgm[x][e] * p.lb * sigmoid_f(xx) * sigmoid_f(-xx);
-                            p.dg[(tok * H + h) * DK + i] = dx * ea;
-                            apart = fmaf(dx, xx, apart);
-                            pdt += dx * ea;
-                        }
+                    // rows from e on; the lane's row r = 4 lk + e is 4 lk past the first
+                    const uint32_t vo = (4 * lk * qs + i) * 4, vk = (4 * lk * hs * DK + i) * 4;
+                    const float pq = (rq[0][r] + rq[1][r]) + (rq[2][r] + rq[3][r]);
+                    const float pk = (rk[0][r] + rk[1][r]) + (rk[2][r] + rk[3][r]);
+                    float dq, dk;
+                    if (p.l2norm) {
+                        const float inq = L.nq[r], ink = L.nk[r];
+                        dq = p.scale * inq * (dqh[x][e] - L.qh[r][i] * pq * iss);
+                        dk = ink * (dkh[x][e] - L.kh[r][i] * pk);
+                    } else {
+                        dq = p.scale * dqh[x][e];
+                        dk = dkh[x][e];
+                    }
+                    bstore(rows_rsrc(dqdst, e, nr, qs * 4, DK * 4), vo, dq);
+                    bstore(rows_rsrc(dkdst, e, nr, hs * DK * 4, DK * 4), vk, dk);
+                    if (!EJK) {
+                        const float xx = ea * (gl[x][e] + dtl[x]);
+                        // sigma'(x) = sigma(x) sigma(-x): no cancellation in
+                        // 1 - sigma(x) when the gate saturates; rows past the
+                        // chunk add nothing to the parameter partials
+                        float dx = dgm[x][e] * p.lb * sigmoid_fast(xx) * sigmoid_fast(-xx);
+                        dx = r < nr ? dx : 0.f;
+                        bstore(rows_rsrc(dgdst, e, nr, qs * 4, DK * 4), vo, dx * ea);
+                        apart = fmaf(dx, xx, apart);
+                        pdt += dx * ea;
                     }
                 }
             }
@@ -1418,13 +1496,16 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                 if (t < NT && lk == 0) p.part_dt[((size_t)slot * H + h) * DK + 16 * t + lm] = pdt;
             }
         }
+        {
+            // dv = beta Z, per step m over rows from 2 m on; columns past dv get an
+            // offset past the resource
+            const char* dvb = reinterpret_cast<const char*>(p.dv_out + ((size_t)c0 * hs + hh) * dv);
+            const int r0 = tid / MAXD, j = tid % MAXD;
+            const uint32_t vo = j < dv ? (uint32_t)(r0 * hs * dv + j) * 4 : kNoOffset;
 #pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + m * BT;
-            const int r = e / MAXD, j = e % MAXD;
-            if (r < nr && j < dv) {
-                const size_t tok = (size_t)(c0 + r);
-                p.dv_out[(tok * (grouped ? H : Hkv) + (grouped ? h : hk)) * dv + j] = L.beta[r] * xz[m];
+            for (int m = 0; m < NV; ++m) {
+                const int rm = m * (BT / MAXD);
+                bstore(rows_rsrc(dvb, rm, nr, hs * dv * 4, dv * 4), vo, L.beta[r0 + rm] * xz[m]);
             }
         }
         if (tid < BC && tid < nr) {
@@ -1434,7 +1515,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                 p.dbeta[tok * H + h] = dbt[r];
                 if (p.dg) p.dg[tok * H + h] = dgs[r];
             } else {
-                p.dbeta[tok * H + h] = dbt[r] * sigmoid_f(xb) * sigmoid_f(-xb);
+                p.dbeta[tok * H + h] = dbt[r] * sigmoid_fast(xb) * sigmoid_fast(-xb);
             }
         }
         if (!EJK) {

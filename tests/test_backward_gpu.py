@@ -62,11 +62,11 @@ def _check(inp, tol, use_qk_l2norm=True, seed=0, do_bf16=False, margin=None, lab
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128)])
 @pytest.mark.parametrize("ejk", [False, True], ids=["kda", "ejk"])
-def test_backward_fp32_shapes(dk, dv, ejk):
+def test_backward_fp32_shapes(dk, dv, ejk, margin):
     inp = workloads.prefill_inputs(2, 45, 3, dk, dv, seed=1700 + dk + dv, dtype="f32", ejk=ejk,
                                    init_state=True)
     say("backward fp32", dk, dv, "EJK" if ejk else "KDA")
-    _check(inp, 1e-5, seed=dk + dv)
+    _check(inp, 1e-5, seed=dk + dv, margin=margin, label=f"fp32 dk{dk} dv{dv}")
 
 
 @pytest.mark.parametrize("ejk", [False, True], ids=["kda", "ejk"])
@@ -77,27 +77,27 @@ def test_backward_bf16_varlen_grouped(ejk, margin):
     _check(inp, 2e-2, seed=5, do_bf16=True, margin=margin, label="bf16 varlen grouped")
 
 
-def test_backward_fp32_varlen_grouped_tight():
+def test_backward_fp32_varlen_grouped_tight(margin):
     inp = workloads.prefill_inputs(1, 0, 6, 64, 32, seed=1712, dtype="f32", init_state=True,
                                    lengths=[33, 0, 16, 70], hkv=3)
     say("backward fp32 varlen grouped")
-    _check(inp, 1e-5, seed=6)
+    _check(inp, 1e-5, seed=6, margin=margin, label="fp32 varlen grouped")
 
 
-def test_backward_no_l2norm_and_strong_decay():
+def test_backward_no_l2norm_and_strong_decay(margin):
     inp = workloads.prefill_inputs(1, 90, 2, 64, 64, seed=1720, dtype="f32", init_state=True, scale=0.1)
     inp.q *= 0.2
     inp.k *= 0.2
     say("backward no l2 norm")
-    _check(inp, 1e-5, use_qk_l2norm=False, seed=7)
+    _check(inp, 1e-5, use_qk_l2norm=False, seed=7, margin=margin, label="fp32 no l2 norm")
     inp = workloads.prefill_inputs(1, 90, 2, 128, 64, seed=1721, dtype="f32", init_state=True)
     inp.g = (inp.g + 8.0).astype(np.float32)      # gates near lower_bound = -5
     say("backward saturated gates")
-    _check(inp, 1e-5, seed=8)
+    _check(inp, 1e-5, seed=8, margin=margin, label="fp32 saturated gates")
     inp = workloads.prefill_inputs(1, 90, 2, 128, 64, seed=1722, dtype="f32", ejk=True, init_state=True)
     inp.g = (-6.0 * np.abs(inp.g)).astype(np.float32)
     say("backward EJK strong decay")
-    _check(inp, 1e-5, seed=9)
+    _check(inp, 1e-5, seed=9, margin=margin, label="fp32 EJK strong decay")
 
 
 def test_backward_no_tokens_carries_the_state_gradient():
@@ -129,7 +129,7 @@ def test_backward_two_tiles_per_scan_workgroup(ejk, margin):
     heads with grouped keys (ragged, with empty ones)."""
     inp = workloads.prefill_inputs(4, 50, 64, 32, 32, seed=1760 + ejk, dtype="f32", ejk=ejk, init_state=True)
     say("backward fp32 B4 T50 H64 d32", "EJK" if ejk else "KDA")
-    _check(inp, 1e-5, seed=12)
+    _check(inp, 1e-5, seed=12, margin=margin, label="fp32 B4 T50 H64 d32 (two tiles per scan workgroup)")
     inp = workloads.prefill_inputs(8, 80, 32, 128, 128, seed=1762 + ejk, ejk=ejk, init_state=True)
     say("backward bf16 B8 T80 H32 d128", "EJK" if ejk else "KDA")
     _check(inp, 2e-2, seed=13, do_bf16=True, margin=margin, label="B8 T80 H32 (two tiles per scan workgroup)")
@@ -137,7 +137,7 @@ def test_backward_two_tiles_per_scan_workgroup(ejk, margin):
     inp = workloads.prefill_inputs(1, 0, 8, 64, 64, seed=1766 + ejk, dtype="f32", ejk=ejk, init_state=True,
                                    lengths=lengths, hkv=2)
     say("backward fp32 64 packed sequences H8 Hkv2 d64", "EJK" if ejk else "KDA")
-    _check(inp, 1e-5, seed=14)
+    _check(inp, 1e-5, seed=14, margin=margin, label="fp32 64 packed sequences (two tiles)")
 
 
 def test_backward_unaligned_inputs_take_the_own_forward_scan():
