@@ -612,41 +612,9 @@ __device__ __forceinline__ void store_at(__amdgpu_buffer_rsrc_t r, int byte_off,
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
 }
 
-// Buffer accesses for the local pass: a resource over [base, base + bytes)
-// and a 32-bit byte offset per lane, so addresses are 32-bit adds; a load at
-// an offset past the end reads zero and a store there is dropped (the whole
-// offset goes in the lane's offset register: the scalar offset field is not
-// range-checked).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-template <typename T>
-__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    if constexpr (sizeof(T) == 2)
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-    else
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-
-__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, float v)
-{
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
-}
-
-constexpr uint32_t kNoOffset = 0x80000000u;   // past every resource here (all < 2^31 bytes)
-
-// A resource over rows r .. nr - 1 of a block whose rows are `stride` bytes
-// apart and `width` bytes wide (none when r >= nr): a lane then addresses its
-// row relative to row r in its own offset, which the range check covers,
-// and its place within the row in the scalar offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int r, int nr, int stride, int width)
-{
-    const int n = nr - r;
-    return brsrc(base + (size_t)r * stride, n > 0 ? (n - 1) * stride + width : 0);
-}
+// The local pass's padded columns get an offset past every resource it uses
+// (all under 2^31 bytes), so their stores are dropped.
+constexpr uint32_t kNoOffset = 0x80000000u;
 
 // The scans' register layout: the dk x 16 state (or state gradient) tile is
 // held in the accumulators of 16x16x4 float32 MFMA, 16 rows per tile (tiles
@@ -1048,7 +1016,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const float* S0p = p.ckS + ((size_t)ps * H + h) * DK * dv;
     // (16-column tiles past dv fall outside the resource and read as zero)
     auto load_tile = [&](float4 (&dst)[TPW][NJ], const float* src) __attribute__((always_inline)) {
-        const auto rs = brsrc(src, nj * DK * TV * 4);
+        const auto rs = buf_rsrc(src, nj * DK * TV * 4);
         const int vo = ((16 * wave + lm) * TV + 4 * lk) * 4;
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
@@ -1084,9 +1052,9 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
             for (int m = 0; m < NE; ++m) {
                 const int rm = m * (BT / DK);
-                xq[m] = bload<Tin>(rows_rsrc(qsrc, rm, nr, qs * SQ, DK * SQ), (r0 * qs + i) * SQ);
-                xk[m] = bload<Tin>(rows_rsrc(ksrc, rm, nr, ks * SQ, DK * SQ), (r0 * ks + i) * SQ);
-                if (!EJK) xg[m] = bload<float>(rows_rsrc(gsrc, rm, nr, qs * 4, DK * 4), (r0 * qs + i) * 4);
+                xq[m] = buf_load<Tin>(rows_rsrc(qsrc, rm, nr, qs * SQ, DK * SQ), (r0 * qs + i) * SQ);
+                xk[m] = buf_load<Tin>(rows_rsrc(ksrc, rm, nr, ks * SQ, DK * SQ), (r0 * ks + i) * SQ);
+                if (!EJK) xg[m] = buf_load<float>(rows_rsrc(gsrc, rm, nr, qs * 4, DK * 4), (r0 * qs + i) * 4);
             }
         }
         const float dtb_row = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
@@ -1096,28 +1064,28 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
         float xu[NV], xz[NV], xy[NV];
         {
             const int os = H * dv, so = p.do_bf16 ? 2 : 4;
-            const auto bo = brsrc(static_cast<const char*>(p.d_o) + ((size_t)c0 * H + h) * dv * so,
+            const auto bo = buf_rsrc(static_cast<const char*>(p.d_o) + ((size_t)c0 * H + h) * dv * so,
                                   ((nr - 1) * os + dv) * so);
-            const auto by = brsrc(p.ckYU + ((size_t)slot * H + h) * 2 * BC * dv, 2 * BC * dv * 4);
-            const auto bz = brsrc(p.ckZ + ((size_t)slot * H + h) * BC * dv, BC * dv * 4);
+            const auto by = buf_rsrc(p.ckYU + ((size_t)slot * H + h) * 2 * BC * dv, 2 * BC * dv * 4);
+            const auto bz = buf_rsrc(p.ckZ + ((size_t)slot * H + h) * BC * dv, BC * dv * 4);
             const int r0 = tid / MAXD, j = tid % MAXD;
             const bool ok = j < dv;
             // dO kept as loaded (bf16 bits or float32 bits), widened where used
             if (p.do_bf16) {
 #pragma unroll
                 for (int m = 0; m < NV; ++m)
-                    xo[m] = bload<uint16_t>(bo, ((r0 + m * (BT / MAXD)) * os + j) * 2);
+                    xo[m] = buf_load<uint16_t>(bo, ((r0 + m * (BT / MAXD)) * os + j) * 2);
             } else {
 #pragma unroll
                 for (int m = 0; m < NV; ++m)
-                    xo[m] = bload<uint32_t>(bo, ((r0 + m * (BT / MAXD)) * os + j) * 4);
+                    xo[m] = buf_load<uint32_t>(bo, ((r0 + m * (BT / MAXD)) * os + j) * 4);
             }
 #pragma unroll
             for (int m = 0; m < NV; ++m) {
                 const int r = r0 + m * (BT / MAXD);
-                const float y = bload<float>(by, (r * dv + j) * 4);
-                const float u = bload<float>(by, ((BC + r) * dv + j) * 4);
-                const float z = bload<float>(bz, (r * dv + j) * 4);
+                const float y = buf_load<float>(by, (r * dv + j) * 4);
+                const float u = buf_load<float>(by, ((BC + r) * dv + j) * 4);
+                const float z = buf_load<float>(bz, (r * dv + j) * 4);
                 xy[m] = ok ? y : 0.f;
                 xu[m] = ok ? u : 0.f;
                 xz[m] = ok ? z : 0.f;
@@ -1140,7 +1108,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // rows from e on; the lane's row 4 lk + e is 4 lk past the first
-                const float v = EJK ? 0.f : bload<float>(rows_rsrc(gsrc, e, nr, qs * 4, DK * 4), (4 * lk * qs + 16 * t + lm) * 4);
+                const float v = EJK ? 0.f : buf_load<float>(rows_rsrc(gsrc, e, nr, qs * 4, DK * 4), (4 * lk * qs + 16 * t + lm) * 4);
                 gl[x][e] = ok ? v : 0.f;
             }
         }
@@ -1474,8 +1442,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                         dq = p.scale * dqh[x][e];
                         dk = dkh[x][e];
                     }
-                    bstore(rows_rsrc(dqdst, e, nr, qs * 4, DK * 4), vo, dq);
-                    bstore(rows_rsrc(dkdst, e, nr, hs * DK * 4, DK * 4), vk, dk);
+                    buf_store(rows_rsrc(dqdst, e, nr, qs * 4, DK * 4), vo, dq);
+                    buf_store(rows_rsrc(dkdst, e, nr, hs * DK * 4, DK * 4), vk, dk);
                     if (!EJK) {
                         const float xx = ea * (gl[x][e] + dtl[x]);
                         // sigma'(x) = sigma(x) sigma(-x): no cancellation in
@@ -1483,7 +1451,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                         // chunk add nothing to the parameter partials
                         float dx = dgm[x][e] * p.lb * sigmoid_fast(xx) * sigmoid_fast(-xx);
                         dx = r < nr ? dx : 0.f;
-                        bstore(rows_rsrc(dgdst, e, nr, qs * 4, DK * 4), vo, dx * ea);
+                        buf_store(rows_rsrc(dgdst, e, nr, qs * 4, DK * 4), vo, dx * ea);
                         apart = fmaf(dx, xx, apart);
                         pdt += dx * ea;
                     }
@@ -1505,7 +1473,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
             for (int m = 0; m < NV; ++m) {
                 const int rm = m * (BT / MAXD);
-                bstore(rows_rsrc(dvb, rm, nr, hs * dv * 4, dv * 4), vo, L.beta[r0 + rm] * xz[m]);
+                buf_store(rows_rsrc(dvb, rm, nr, hs * dv * 4, dv * 4), vo, L.beta[r0 + rm] * xz[m]);
             }
         }
         if (tid < BC && tid < nr) {

@@ -306,25 +306,29 @@ struct PrepRaw {
     float beta;           // lanes < 16: beta logit of row 16*blk + lane
 };
 
-// Rows past the sequence read the chunk's first row; they are zeroed on use.
-// EJK: g is [tokens][H] (one decay per token and head; NULL = no decay).
-// PART 0 loads q, k and beta, PART 1 the gates (half of the bytes), PART 2 both.
+// q, k and the KDA gates go through a buffer resource per group of rows (the
+// group's first row uniform, the lane's row within it in its offset): rows
+// past the sequence fall outside and read as zero (they are zeroed on use
+// as well).  The beta logits and EJK decays of rows past the sequence read the
+// chunk's first row.  EJK: g is [tokens][H] (one decay per token and head;
+// NULL = no decay).  PART 0 loads q, k and beta, PART 1 the gates (half of the
+// bytes), PART 2 both.
 template <bool EJK, int PART = 2>
 __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const bf16_t* q, const bf16_t* k,
                                           const float* g, const float* beta, int H, int HKV, int lane, int blk)
 {
     const size_t base = ((size_t)it.c0 * H + it.h) * DK;   // channel 0 of the item's first row
-    const size_t rstride = (size_t)H * DK;
+    const uint32_t rstride = (uint32_t)H * DK;
     if constexpr (PART != 1) {
         // k: the key/value head of head h, rows HKV heads apart
         const size_t kbase = ((size_t)it.c0 * HKV + it.h / (H / HKV)) * DK;
-        const size_t kstride = (size_t)HKV * DK;
+        const uint32_t kstride = (uint32_t)HKV * DK;
+        const uint32_t col = 16 * (lane & 15);   // bytes: 8 bf16 channels per lane
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * blk + 4 * i + (lane >> 4);
-            const int rr = (row < it.len) ? row : 0;
-            r.q[i] = *reinterpret_cast<const u32x4_t*>(q + base + (size_t)rr * rstride + 8 * (lane & 15));
-            r.k[i] = *reinterpret_cast<const u32x4_t*>(k + kbase + (size_t)rr * kstride + 8 * (lane & 15));
+            const int r0 = 16 * blk + 4 * i;      // rows r0 .. r0 + 3, the lane's is r0 + lane / 16
+            r.q[i] = buf_load<u32x4_t>(rows_rsrc(q + base, r0, it.len, 2 * rstride, 2 * DK), (lane >> 4) * 2 * rstride + col);
+            r.k[i] = buf_load<u32x4_t>(rows_rsrc(k + kbase, r0, it.len, 2 * kstride, 2 * DK), (lane >> 4) * 2 * kstride + col);
         }
         const int rb = 16 * blk + (lane & 15);
         r.beta = beta[(size_t)(it.c0 + ((rb < it.len) ? rb : 0)) * H + it.h];
@@ -339,9 +343,9 @@ __device__ __forceinline__ void prep_load(PrepRaw& r, const PrepItem& it, const 
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int row = 16 * blk + 2 * i + (lane >> 5);
-                const size_t off = base + (size_t)((row < it.len) ? row : 0) * rstride + 4 * (lane & 31);
-                r.g[i] = *reinterpret_cast<const u32x4_t*>(g + off);
+                const int r0 = 16 * blk + 2 * i;      // rows r0, r0 + 1, the lane's is r0 + lane / 32
+                r.g[i] = buf_load<u32x4_t>(rows_rsrc(g + base, r0, it.len, 4 * rstride, 4 * DK),
+                                           (lane >> 5) * 4 * rstride + 16 * (lane & 31));
             }
         }
     }
@@ -372,7 +376,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     int item = blockIdx.x;
     PrepItem it = prep_item(item, nitems, H, cu, off, N, T);
     PrepRaw cur;
-    if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, HKV, threadIdx.x & 63, threadIdx.x >> 6);
+    if (it.valid)
+        prep_load<EJK>(cur, it, q, k, g, beta, H, HKV, threadIdx.x & 63, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
     for (; item < nitems; item += gridDim.x) {
         // Thread indices are re-read opaquely in every iteration, so that the
         // per-lane address arithmetic derived from them is recomputed where it
@@ -393,13 +398,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         }
         const int h = me.h;
         const int len = me.len;
-        unsigned char* rec = ws + ((size_t)me.slot * H + h) * REC_BYTES;
-        uint16_t* gW = reinterpret_cast<uint16_t*>(rec + REC_W);
-        uint16_t* gQG = reinterpret_cast<uint16_t*>(rec + REC_QG);
-        uint16_t* gKCT = reinterpret_cast<uint16_t*>(rec + REC_KCT);
-        uint16_t* gTP = reinterpret_cast<uint16_t*>(rec + REC_TP);
-        uint16_t* gP = reinterpret_cast<uint16_t*>(rec + REC_P);
-        float* gEC = reinterpret_cast<float*>(rec + REC_EC);
+        // the item's record, stored through a buffer resource with 32-bit offsets
+        const __amdgpu_buffer_rsrc_t rr = buf_rsrc(ws + ((size_t)me.slot * H + h) * REC_BYTES, REC_BYTES);
         const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) folded with log2(e)
         const float dtb0 = (!EJK && dt_bias) ? dt_bias[(size_t)ch * H + h] : 0.f;
         const float dtb1 = (!EJK && dt_bias) ? dt_bias[(size_t)(ch + 1) * H + h] : 0.f;
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
             }
             if (blk == 0) {
                 const float ec = __builtin_amdgcn_exp2f(tot);
-                *reinterpret_cast<float2*>(gEC + ch) = make_float2(ec, ec);
+                buf_store(rr, REC_EC + 4 * ch, make_float2(ec, ec));
             }
             float kg0[16], kg1[16], kc0[16], kc1[16];
     #pragma unroll
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 const int at = r * SR + ch;
                 *reinterpret_cast<uint32_t*>(QL + at) = pack2(qh0, qh1);
                 *reinterpret_cast<uint32_t*>(KL + at) = pack2(kh0, kh1);
-                *reinterpret_cast<uint32_t*>(gQG + ksl(C, r, ch)) = pack2(eb * qh0, eb * qh1);
+                buf_store(rr, REC_QG + 2 * ksl(C, r, ch), pack2(eb * qh0, eb * qh1));
                 kg0[m] = ebx * kh0;
                 kg1[m] = ebx * kh1;
                 kc0[m] = ecb * kh0;
@@ -527,14 +527,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
             }
             uint16_t* g0p = KGT + ch * SW + 16 * blk;
             uint16_t* g1p = KGT + (ch + 1) * SW + 16 * blk;
-            uint16_t* c0p = gKCT + ksl(DK, ch, 16 * blk);
-            uint16_t* c1p = gKCT + ksl(DK, ch + 1, 16 * blk);
+            const uint32_t c0o = REC_KCT + 2 * ksl(DK, ch, 16 * blk);
+            const uint32_t c1o = REC_KCT + 2 * ksl(DK, ch + 1, 16 * blk);
     #pragma unroll
             for (int h8 = 0; h8 < 2; ++h8) {
                 *reinterpret_cast<uint4*>(g0p + 8 * h8) = pack8(kg0 + 8 * h8);
                 *reinterpret_cast<uint4*>(g1p + 8 * h8) = pack8(kg1 + 8 * h8);
-                *reinterpret_cast<uint4*>(c0p + 8 * h8) = pack8(kc0 + 8 * h8);
-                *reinterpret_cast<uint4*>(c1p + 8 * h8) = pack8(kc1 + 8 * h8);
+                buf_store(rr, c0o + 16 * h8, pack8(kc0 + 8 * h8));
+                buf_store(rr, c1o + 16 * h8, pack8(kc1 + 8 * h8));
             }
         } else {
             float P0 = 0.f, P1 = 0.f, tot0 = 0.f, tot1 = 0.f;
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 }
             }
             if (blk == 0) {
-                *reinterpret_cast<float2*>(gEC + ch) = make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
+                buf_store(rr, REC_EC + 4 * ch, make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1)));
             }
             float kg0[16], kg1[16], kc0[16], kc1[16];
     #pragma unroll
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 *reinterpret_cast<uint32_t*>(QL + at) = pack2(ql0, ql1);
                 *reinterpret_cast<uint32_t*>(KL + at) = pack2(kl0, kl1);
                 *reinterpret_cast<uint32_t*>(KRD + at) = pack2(kd0, kd1);
-                *reinterpret_cast<uint32_t*>(gQG + ksl(C, r, ch)) = pack2(E0 * ql0, E1 * ql1);
+                buf_store(rr, REC_QG + 2 * ksl(C, r, ch), pack2(E0 * ql0, E1 * ql1));
                 kg0[m] = E0 * kl0;
                 kg1[m] = E1 * kl1;
                 kc0[m] = N0 * c_0 * kd0;   // e^{b_C - b_e} e^{b_e - b_f} e^{b_f - b_s} kh_s
@@ -592,14 +592,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
             // 16 consecutive tokens of one channel = 32 contiguous bytes
             uint16_t* g0p = KGT + ch * SW + 16 * blk;
             uint16_t* g1p = KGT + (ch + 1) * SW + 16 * blk;
-            uint16_t* c0p = gKCT + ksl(DK, ch, 16 * blk);
-            uint16_t* c1p = gKCT + ksl(DK, ch + 1, 16 * blk);
+            const uint32_t c0o = REC_KCT + 2 * ksl(DK, ch, 16 * blk);
+            const uint32_t c1o = REC_KCT + 2 * ksl(DK, ch + 1, 16 * blk);
     #pragma unroll
             for (int h8 = 0; h8 < 2; ++h8) {
                 *reinterpret_cast<uint4*>(g0p + 8 * h8) = pack8(kg0 + 8 * h8);
                 *reinterpret_cast<uint4*>(g1p + 8 * h8) = pack8(kg1 + 8 * h8);
-                *reinterpret_cast<uint4*>(c0p + 8 * h8) = pack8(kc0 + 8 * h8);
-                *reinterpret_cast<uint4*>(c1p + 8 * h8) = pack8(kc1 + 8 * h8);
+                buf_store(rr, c0o + 16 * h8, pack8(kc0 + 8 * h8));
+                buf_store(rr, c1o + 16 * h8, pack8(kc1 + 8 * h8));
             }
             // this block's e^{b_e - b_f}, which turns KRd into e^{b_e - b_s} kh_s for later blocks
             VEC[V_C + blk * DK + ch] = c_0;
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 }
             }
             *reinterpret_cast<float4*>(AB + r * SA + 16 * J + 4 * g4) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-            st4bf(gP + ksl(C, r, 16 * J + 4 * g4), p4[0], p4[1], p4[2], p4[3]);
+            buf_store(rr, REC_P + 2 * ksl(C, r, 16 * J + 4 * g4), make_uint2(pack2(p4[0], p4[1]), pack2(p4[2], p4[3])));
         }
         lds_barrier();
 
@@ -791,7 +791,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                                      ld8(TP, SW, 16 * I + l16, 32 * ks + 8 * g4), acc);
                     }
                     // acc[e] = W[r = 16I + l16][i = 16ib + 4*g4 + e]
-                    st4bf(gW + ksl(C, 16 * I + l16, 16 * ib + 4 * g4), acc[0], acc[1], acc[2], acc[3]);
+                    buf_store(rr, REC_W + 2 * ksl(C, 16 * I + l16, 16 * ib + 4 * g4),
+                              make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
                 }
             }
             // T' [64][64] -> k-sliced, thread = (row, 16-column block); blocks above the
@@ -805,8 +806,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
                 for (int h8 = 0; h8 < 2; ++h8) {
                     uint4 val = *reinterpret_cast<const uint4*>(TP + r * SW + s0 + 8 * h8);
                     if (upper) val = make_uint4(0u, 0u, 0u, 0u);
-                    *reinterpret_cast<uint4*>(gTP + ksl(C, r, s0 + 8 * h8)) = val;
-                    if (upper) *reinterpret_cast<uint4*>(gP + ksl(C, r, s0 + 8 * h8)) = val;
+                    buf_store(rr, REC_TP + 2 * ksl(C, r, s0 + 8 * h8), val);
+                    if (upper) buf_store(rr, REC_P + 2 * ksl(C, r, s0 + 8 * h8), val);
                 }
             }
         }

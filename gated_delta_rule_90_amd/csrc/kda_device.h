@@ -31,6 +31,50 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x)
     return bf16_t{__builtin_bit_cast(uint16_t, b)};
 }
 
+// ---- buffer resources: 32-bit byte offsets with a range check.  A load at an
+// offset past the resource reads zero and a store there is dropped.  Only the
+// lane's offset register and the instruction's immediate offset enter the
+// check (the scalar offset field does not), so every offset that must be
+// checked goes in the lane's offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Rows r .. nr - 1 of a block whose rows are `stride` bytes apart and `width`
+// bytes wide (an empty resource when r >= nr): a lane then addresses its row
+// relative to row r, and rows from nr on fall past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int r, int nr, uint32_t stride,
+                                                            uint32_t width)
+{
+    const int n = nr - r;
+    return buf_rsrc(static_cast<const char*>(base) + (size_t)r * stride, n > 0 ? (uint32_t)(n - 1) * stride + width : 0u);
+}
+
+template <typename T>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    else if constexpr (sizeof(T) == 4)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, T v)
+{
+    typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+    if constexpr (sizeof(T) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    else if constexpr (sizeof(T) == 8)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_v, v), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_v, v), r, off, 0, 0);
+}
+
 // Numerically safe logistic: 1 / (1 + e^-x); exp overflow gives 0, underflow 1.
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
