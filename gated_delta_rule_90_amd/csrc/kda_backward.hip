@@ -648,8 +648,10 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     __shared__ ScanLds<DK, NG> L;
     // NG groups of four waves, each on its own 16 state columns, share the
     // chunk's operand block in LDS
-    const int tid = threadIdx.x % BT, grp = threadIdx.x / BT;
-    const int lane = tid & 63, wave = tid >> 6;
+    // (the group and wave indices are wave-uniform: kept in scalar registers,
+    // so that resources built from them need no per-lane loop)
+    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lm = lane & 15, lk = lane >> 4;
     int j0, h, n;
     if (!scan_unit(p, NG, j0, h, n)) return;
@@ -674,6 +676,12 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     settle(S);
     const int nck = seq_chunks(p.off, n, t0, t1);
     const int slot0 = p.off[n];
+    // the sequence's pair-checkpoint range, read once and kept wave-uniform (the
+    // checkpoint stores through p could alias p.poff, so inside the loop the
+    // compiler would reload it after every store, and a divergent-looking range
+    // makes every store a per-lane loop)
+    const int pair0 = __builtin_amdgcn_readfirstlane(p.poff[n]);
+    const int pair1 = __builtin_amdgcn_readfirstlane(p.poff[n + 1]);
     const Tin* vv = static_cast<const Tin*>(p.v);
     // a ring of two register sets: the inputs of chunk c + 2 are loaded while
     // chunk c computes (the loop is unrolled by two, so each set is fixed)
@@ -701,9 +709,9 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
                 // the state entering a pair's first chunk (c even); tiles t >= NT
                 // (idle waves at small dk) fall past the range
                 // (pairs past the capped count of overlapping ranges store nothing)
-                const int pi = p.poff[n] + c / 2;
+                const int pi = pair0 + c / 2;
                 const auto rs = store_range(p.ckS + (((size_t)pi * H + h) * (dv / TV) + j0 / TV) * DK * TV,
-                                            pi < p.poff[n + 1] ? DK * TV * 4 : 0);
+                                            pi < pair1 ? DK * TV * 4 : 0);
 #pragma unroll
                 for (int x = 0; x < TPW; ++x) {
                     const int t = wave + NW * x;
@@ -794,8 +802,10 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     __shared__ ScanLds<DK, NG> L;
     // NG groups of four waves, each on its own 16 state columns, share the
     // chunk's operand block in LDS
-    const int tid = threadIdx.x % BT, grp = threadIdx.x / BT;
-    const int lane = tid & 63, wave = tid >> 6;
+    // (the group and wave indices are wave-uniform: kept in scalar registers,
+    // so that resources built from them need no per-lane loop)
+    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lm = lane & 15, lk = lane >> 4;
     int j0, h, n;
     if (!scan_unit(p, NG, j0, h, n)) return;
@@ -816,6 +826,12 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     settle(dS);   // as in the forward scan
     const int nck = seq_chunks(p.off, n, t0, t1);
     const int slot0 = p.off[n];
+    // the sequence's pair-checkpoint range, read once and kept wave-uniform (the
+    // checkpoint stores through p could alias p.poff, so inside the loop the
+    // compiler would reload it after every store, and a divergent-looking range
+    // makes every store a per-lane loop)
+    const int pair0 = __builtin_amdgcn_readfirstlane(p.poff[n]);
+    const int pair1 = __builtin_amdgcn_readfirstlane(p.poff[n + 1]);
     // a ring of two register sets: the inputs of chunk c - 2 are loaded while
     // chunk c computes (the loop is unrolled by two, so each set is fixed);
     // dO as loaded (bf16 or float32 bits), widened where used
@@ -842,8 +858,8 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
                 // the state gradient leaving a pair's last chunk (c odd, or the
                 // sequence's last); the other chunks' stores get an empty range, as
                 // do tiles t >= NT (idle waves at small dk)
-                const int pi = p.poff[n] + c / 2;
-                const bool keep = ((c & 1) || c == nck - 1) && pi < p.poff[n + 1];
+                const int pi = pair0 + c / 2;
+                const bool keep = ((c & 1) || c == nck - 1) && pi < pair1;
                 const auto rs = store_range(p.ckdS + (((size_t)pi * H + h) * (dv / TV) + j0 / TV) * DK * TV,
                                             keep ? DK * TV * 4 : 0);
 #pragma unroll

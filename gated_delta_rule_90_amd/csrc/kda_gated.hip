@@ -325,8 +325,10 @@ __global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int NT = DK / 16, TPW = (NT + GNW - 1) / GNW;
     constexpr int N4 = PL::SIZE / 4, NP = (N4 + NG * GTH - 1) / (NG * GTH);
     __shared__ GScanLds<DK, NG> L;
-    const int tid = threadIdx.x % GTH, cg = threadIdx.x / GTH;
-    const int lane = tid & 63, wave = tid >> 6;
+    // (the group and wave indices are wave-uniform: kept in scalar registers,
+    // so that resources built from them need no per-lane loop)
+    const int tid = threadIdx.x % GTH, cg = __builtin_amdgcn_readfirstlane(threadIdx.x / GTH);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lm = lane & 15, lk = lane >> 4;
     const int H = p.H, DV = p.dv;
     const int ntile = DV / (GJ * NG);
