@@ -209,6 +209,9 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         const int i = e / FJ, j = e % FJ;
         L.ST[j * LT::SRS + i] = init ? init[soff + (size_t)i * DV + j0 + j] : 0.f;
     }
+    // the sequence bounds again in scalar registers after the divergent loop
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
     const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) in log2 units
     const float lb2 = lower_bound * kLog2e;
     // dt_bias of the four channels of this lane's pieces (the piece column
@@ -220,14 +223,14 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
 
     // One chunk's inputs as loaded into registers: q, k and (KDA) g as pieces of
     // four channels (row e / RL, channels 4 (e % RL) ..), v at (rows r16 + 16 hv,
-    // column c16), beta and the EJK decay of row tid.  The loads go
-    // through buffer resources that end after the sequence's last row, so rows
-    // past the sequence read zeros; each address is a per-lane offset fixed for
-    // the whole sequence plus a per-chunk scalar offset.  The values are masked
-    // where they are used, so no load is waited for where it is issued and
-    // every path issues the same loads (the wait before a chunk's first use
-    // then covers only its own).  A sequence's spans fit 31-bit offsets (the
-    // host routes longer ones to the token-by-token kernel).
+    // column c16), beta and the EJK decay of row tid.  The loads go through
+    // buffer resources over the chunk's rows up to the sequence's last (built
+    // per chunk in scalar registers); the lane's offset, fixed for the whole
+    // sequence, is its place within the chunk, so rows past the sequence fall
+    // outside and read zeros.  The values are masked where they are used as
+    // well, so no load is waited for where it is issued and every path issues
+    // the same loads (the wait before a chunk's first use then covers only its
+    // own).
     using P4 = Piece4<Tin>;
     using piece_t = typename P4::type;
     struct Raw {
@@ -238,16 +241,14 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     };
     constexpr int SI = (int)sizeof(Tin);
     const int nseq = t1 - t0;
-    auto rsrc = [](const void* base, long long bytes) {
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-    };
-    const long long last = nseq > 0 ? nseq - 1 : 0;
-    const __amdgpu_buffer_rsrc_t rq_ = rsrc(q + ((size_t)t0 * H + h) * DK, (last * H * DK + DK) * SI);
-    const __amdgpu_buffer_rsrc_t rk_ = rsrc(k + ((size_t)t0 * HKV + hk) * DK, (last * HKV * DK + DK) * SI);
-    const __amdgpu_buffer_rsrc_t rg_ = rsrc((EJK ? (g ? g : beta) : g) + (EJK ? (size_t)t0 * H + h : ((size_t)t0 * H + h) * DK),
-                                           EJK ? (last * H + 1) * 4 : (last * H * DK + DK) * 4);
-    const __amdgpu_buffer_rsrc_t rv_ = rsrc(v + ((size_t)t0 * HKV + hk) * DV + j0, (last * HKV * DV + FJ) * SI);
-    const __amdgpu_buffer_rsrc_t rb_ = rsrc(beta + (size_t)t0 * H + h, (last * H + 1) * 4);
+    // (the bases are moved to scalar registers: values the compiler carries
+    // through the divergent state-initialisation loop above land in vector
+    // registers otherwise, and every load would then need a per-lane loop)
+    const Tin* qb = uniform_ptr(q + ((size_t)t0 * H + h) * DK);
+    const Tin* kb = uniform_ptr(k + ((size_t)t0 * HKV + hk) * DK);
+    const float* gb = uniform_ptr((EJK ? (g ? g : beta) : g) + (EJK ? (size_t)t0 * H + h : ((size_t)t0 * H + h) * DK));
+    const Tin* vb = uniform_ptr(v + ((size_t)t0 * HKV + hk) * DV + j0);
+    const float* bb = uniform_ptr(beta + (size_t)t0 * H + h);
     int vq[QN], vk[QN];
 #pragma unroll
     for (int m = 0; m < QN; ++m) {
@@ -258,17 +259,22 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     }
     auto load = [&](Raw& R, int c) {
         const int r0 = c * FC;   // the chunk's first row within the sequence
+        const auto rq_ = rows_rsrc(qb, r0, nseq, H * DK * SI, DK * SI);
+        const auto rk_ = rows_rsrc(kb, r0, nseq, HKV * DK * SI, DK * SI);
+        const auto rg_ = EJK ? rows_rsrc(gb, r0, nseq, H * 4, 4) : rows_rsrc(gb, r0, nseq, H * DK * 4, DK * 4);
+        const auto rv_ = rows_rsrc(vb, r0, nseq, HKV * DV * SI, FJ * SI);
+        const auto rb_ = rows_rsrc(bb, r0, nseq, H * 4, 4);
 #pragma unroll
         for (int m = 0; m < QN; ++m) {
-            R.q[m] = P4::load(rq_, vq[m] * SI, r0 * H * DK * SI);
-            R.k[m] = P4::load(rk_, vk[m] * SI, r0 * HKV * DK * SI);
-            if constexpr (!EJK) R.g[m] = Piece4<float>::load(rg_, vq[m] * 4, r0 * H * DK * 4);
+            R.q[m] = P4::load(rq_, vq[m] * SI, 0);
+            R.k[m] = P4::load(rk_, vk[m] * SI, 0);
+            if constexpr (!EJK) R.g[m] = Piece4<float>::load(rg_, vq[m] * 4, 0);
         }
 #pragma unroll
         for (int hv = 0; hv < NB; ++hv)
-            R.v[hv] = P4::load1(rv_, ((r16 + FB * hv) * HKV * DV + c16) * SI, r0 * HKV * DV * SI);
-        R.b = Piece4<float>::load1(rb_, tid * H * 4, r0 * H * 4);
-        if constexpr (EJK) R.d = Piece4<float>::load1(rg_, tid * H * 4, r0 * H * 4);   // NULL decay: zeroed at use
+            R.v[hv] = P4::load1(rv_, ((r16 + FB * hv) * HKV * DV + c16) * SI, 0);
+        R.b = Piece4<float>::load1(rb_, tid * H * 4, 0);
+        if constexpr (EJK) R.d = Piece4<float>::load1(rg_, tid * H * 4, 0);   // NULL decay: zeroed at use
     };
     // chunks loaded ahead: at small dk a chunk computes in less than a memory
     // latency (64 tokens ahead); at large dk 32 tokens cover it
@@ -652,7 +658,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
         // after the chunk's last row: the buffer unit drops the stores of padded
         // rows, so every lane issues the same stores
         {
-            Tout* obase = o + ((size_t)c0 * H + h) * DV + j0;
+            Tout* obase = uniform_ptr(o + ((size_t)c0 * H + h) * DV + j0);
             const int rec = len > 0 ? ((len - 1) * H * DV + FJ) * (int)sizeof(Tout) : 0;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(obase, 0, rec, 0x00020000);
 #pragma unroll

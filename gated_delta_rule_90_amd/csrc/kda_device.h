@@ -41,14 +41,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
+// A pointer that is the same in every lane, moved to scalar registers (a
+// pointer chosen by a select, or carried through divergent control flow, can
+// otherwise land in vector registers, and a resource built from it then needs
+// a per-lane loop).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Rows r .. nr - 1 of a block whose rows are `stride` bytes apart and `width`
 // bytes wide (an empty resource when r >= nr): a lane then addresses its row
-// relative to row r, and rows from nr on fall past the end.
+// relative to row r, and rows from nr on fall past the end.  Every argument
+// is the same in every lane of the wave (the resource is built in scalar
+// registers).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int r, int nr, uint32_t stride,
                                                             uint32_t width)
 {
     const int n = nr - r;
-    return buf_rsrc(static_cast<const char*>(base) + (size_t)r * stride, n > 0 ? (uint32_t)(n - 1) * stride + width : 0u);
+    const uint32_t bytes = n > 0 ? (uint32_t)(n - 1) * stride + width : 0u;
+    return buf_rsrc(uniform_ptr(static_cast<const char*>(base) + (size_t)r * stride),
+                    __builtin_amdgcn_readfirstlane(bytes));
 }
 
 template <typename T>
