@@ -110,6 +110,30 @@ __device__ __forceinline__ void f32_seq_bounds(const int32_t* cu, int n, int T, 
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// An empty use of a loaded value: the compiler waits for its load here.
+__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
+// (vectors as one register tuple: split into scalars, they would have to be
+// gathered into a tuple again for the LDS stores)
+__device__ __forceinline__ void settle(float4& x)
+{
+    f32x4_t t = {x.x, x.y, x.z, x.w};
+    asm volatile("" : "+v"(t));
+    x = make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void settle(uint2& x)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 t = {x.x, x.y};
+    asm volatile("" : "+v"(t));
+    x = make_uint2(t[0], t[1]);
+}
+__device__ __forceinline__ void settle(bf16_t& x)
+{
+    uint32_t t = x.bits;
+    asm volatile("" : "+v"(t));
+    x.bits = (uint16_t)t;
+}
+
 // Four consecutive input channels as loaded: a float4 (float32 inputs) or
 // four bf16 in a uint2 (bf16 inputs), widened when used, so that a prefetched
 // load is not waited for where it is issued.
@@ -216,10 +240,18 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const float lb2 = lower_bound * kLog2e;
     // dt_bias of the four channels of this lane's pieces (the piece column
     // tid % RL is the same for every piece of the lane)
+    // (loaded on every path, zeros without a bias, and waited for here: a load
+    // still in flight on only some paths into the chunk loop makes the compiler
+    // wait for all loads at each of its later uses)
     float dtb4[4];
+    {
+        const auto rd = buf_rsrc(EJK ? nullptr : dt_bias, (!EJK && dt_bias) ? (uint32_t)(DK * H * 4) : 0u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        dtb4[j] = (!EJK && dt_bias) ? dt_bias[(size_t)(4 * (tid % RL) + j) * H + h] : 0.f;
+        for (int j = 0; j < 4; ++j) {
+            dtb4[j] = buf_load<float>(rd, (uint32_t)(((4 * (tid % RL) + j) * H + h) * 4));
+            settle(dtb4[j]);
+        }
+    }
 
     // One chunk's inputs as loaded into registers: q, k and (KDA) g as pieces of
     // four channels (row e / RL, channels 4 (e % RL) ..), v at (rows r16 + 16 hv,
@@ -227,10 +259,11 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     // buffer resources over the chunk's rows up to the sequence's last (built
     // per chunk in scalar registers); the lane's offset, fixed for the whole
     // sequence, is its place within the chunk, so rows past the sequence fall
-    // outside and read zeros.  The values are masked where they are used as
-    // well, so no load is waited for where it is issued and every path issues
-    // the same loads (the wait before a chunk's first use then covers only its
-    // own).
+    // outside and read zeros, as do all rows of a chunk past the sequence.  The
+    // raw values go to LDS unmasked (the gate and beta, which are not zero at
+    // zero input, are masked after they are computed), so no load is waited for
+    // where it is issued, every path issues the same loads, and the wait before
+    // a chunk's first use covers only its own.
     using P4 = Piece4<Tin>;
     using piece_t = typename P4::type;
     struct Raw {
@@ -278,11 +311,29 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     };
     // chunks loaded ahead: at small dk a chunk computes in less than a memory
     // latency (64 tokens ahead); at large dk 32 tokens cover it
+    auto settle_raw = [&](Raw& R) {
+#pragma unroll
+        for (int m = 0; m < QN; ++m) {
+            settle(R.q[m]);
+            settle(R.k[m]);
+            if constexpr (!EJK) settle(R.g[m]);
+        }
+#pragma unroll
+        for (int hv = 0; hv < NB; ++hv) settle(R.v[hv]);
+        settle(R.b);
+        if constexpr (EJK) settle(R.d);
+    };
     constexpr int FD = (DK <= 32 ? 4 : 2) / NB;
     Raw ring[FD];
     if (nch > 0) {
 #pragma unroll
-        for (int u = 0; u < FD; ++u) load(ring[u], min(u, nch - 1));
+        for (int u = 0; u < FD; ++u) load(ring[u], u);
+        // (the first chunks are waited for in full: the compiler's count of the
+        // loads in flight at the chunk loop's head is the larger of the counts on
+        // entry and around the loop, so waits left pending here would also be
+        // paid on every later chunk)
+#pragma unroll
+        for (int u = 0; u < FD; ++u) settle_raw(ring[u]);
     }
 
     // Forward substitution of one 16-row block on wave 0: column j on the four
@@ -326,6 +377,10 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     auto chunk = [&](Raw& R, int c) {
         const int c0 = t0 + c * FC;
         const int len = min(FC, t1 - c0);   // <= 0 for a padding chunk
+        // The chunk's inputs are waited for here, outside any lane-dependent
+        // branch, so the wait covers only them: inside such a branch the
+        // compiler waits for every load in flight, the prefetched chunks' too.
+        settle_raw(R);
         // ---- prologue from the registers: raw q, k rows to LDS, gate activations,
         // row norms (RL lanes per row), beta; then fetch the next chunk
 #pragma unroll
@@ -333,8 +388,8 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
             const int e = tid + m * FT;
             const int row = e / RL, c4 = e % RL;
             const bool in = e < Q4 && row < len;
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-            const float4 wq = in ? P4::widen(R.q[m]) : z, wk = in ? P4::widen(R.k[m]) : z;
+            // rows past the sequence were loaded as zeros
+            const float4 wq = P4::widen(R.q[m]), wk = P4::widen(R.k[m]);
             if (e < Q4) {
                 *reinterpret_cast<float4*>(L.QL + row * RS + 4 * c4) = wq;
                 *reinterpret_cast<float4*>(L.KL + row * RS + 4 * c4) = wk;
@@ -383,7 +438,7 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
                 L.BR[tid] = b;
             }
         }
-        load(R, min(c + FD, nch - 1));   // past the end this reloads the last chunk
+        load(R, c + FD);   // a chunk past the sequence loads zeros
         lds_barrier();
 
         // ---- the gate cumsum of every channel down the chunk's rows.  Two-block
