@@ -387,34 +387,58 @@ __global__ __launch_bounds__(BT) void bwd_prep(BwdParams p)
     int n, c0, nr;
     slot_rows(p, slot, n, c0, nr);
     float* o = p.prep + ((size_t)slot * H + h) * PL::SIZE;
-    // 1. the rows to LDS (rows past nr neutral), gate activations in log2 units
+    // 1. the rows to LDS (rows past nr neutral), gate activations in log2 units.
+    // Every load is issued before the first is used: through buffer resources
+    // over the chunk's rows (rows past nr outside the range, read as zero), so
+    // no path differs and one wait covers them all
     {
         const float ea = EJK ? 0.f : expf(p.a_log[h]);
         const float lb2 = p.lb * kLog2e;
-        const float dtb = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
-        const Tin* qq = static_cast<const Tin*>(p.q);
-        const Tin* kk = static_cast<const Tin*>(p.k);
+        constexpr int SQ = (int)sizeof(Tin);
+        const int qs = H * DK, ks = Hkv * DK;   // row strides (elements)
+        const char* qsrc = reinterpret_cast<const char*>(static_cast<const Tin*>(p.q) + ((size_t)c0 * H + h) * DK);
+        const char* ksrc = reinterpret_cast<const char*>(static_cast<const Tin*>(p.k) + ((size_t)c0 * Hkv + hk) * DK);
+        const char* gsrc = EJK ? nullptr : reinterpret_cast<const char*>(p.g + ((size_t)c0 * H + h) * DK);
+        // element e = tid + m BT: row e / DK (step m covers rows from m BT / DK
+        // on, the lane's row within it is tid / DK), channel e % DK
+        const int r0 = tid / DK, i = tid % DK;
+        Tin xq[NE], xk[NE];
+        float xg[EJK ? 1 : NE];
 #pragma unroll
         for (int m = 0; m < NE; ++m) {
-            const int e = tid + m * BT;
-            const int r = e / DK, i = e % DK;
-            const bool ok = r < nr;
-            const size_t tok = (size_t)(c0 + (ok ? r : 0));
-            const float qv = widen(qq[(tok * H + h) * DK + i]);
-            const float kv = widen(kk[(tok * Hkv + hk) * DK + i]);
-            L.QG[r * RS + i] = ok ? qv : 0.f;
-            L.KG[r * RS + i] = ok ? kv : 0.f;
-            if (!EJK) {
-                const float x = ea * (p.g[(tok * H + h) * DK + i] + dtb);
-                L.KI[r * RS + i] = ok ? lb2 * sigmoid_fast(x) : 0.f;
-            }
+            const int rm = m * (BT / DK);
+            xq[m] = buf_load<Tin>(rows_rsrc(qsrc, rm, nr, qs * SQ, DK * SQ), (r0 * qs + i) * SQ);
+            xk[m] = buf_load<Tin>(rows_rsrc(ksrc, rm, nr, ks * SQ, DK * SQ), (r0 * ks + i) * SQ);
+            if constexpr (!EJK) xg[m] = buf_load<float>(rows_rsrc(gsrc, rm, nr, qs * 4, DK * 4), (r0 * qs + i) * 4);
+        }
+        // dt_bias of the lane's channel (zeros without one); beta and the EJK
+        // decay of row tid % BC
+        const auto rd = buf_rsrc(EJK ? nullptr : p.dt_bias, (!EJK && p.dt_bias) ? (uint32_t)(DK * H * 4) : 0u);
+        const float dtb = buf_load<float>(rd, (uint32_t)((i * H + h) * 4));
+        const int rr = tid % BC;
+        float bl = buf_load<float>(rows_rsrc(p.beta + (size_t)c0 * H + h, 0, nr, H * 4, 4), rr * H * 4);
+        float sg = 0.f;
+        if constexpr (EJK)
+            sg = buf_load<float>(rows_rsrc(p.g ? p.g + (size_t)c0 * H + h : nullptr, 0, p.g ? nr : 0, H * 4, 4),
+                                 rr * H * 4);
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            settle(xq[m]);
+            settle(xk[m]);
+            if constexpr (!EJK) settle(xg[m]);
+        }
+        settle(bl);
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            const int r = m * (BT / DK) + r0;
+            L.QG[r * RS + i] = widen(xq[m]);
+            L.KG[r * RS + i] = widen(xk[m]);
+            if constexpr (!EJK) L.KI[r * RS + i] = r < nr ? lb2 * sigmoid_fast(ea * (xg[m] + dtb)) : 0.f;
         }
         if (tid < BC) {
             const bool ok = tid < nr;
-            const size_t tok = (size_t)(c0 + (ok ? tid : 0));
-            const float bl = p.beta[tok * H + h];
             L.BE[tid] = ok ? (EJK ? bl : sigmoid_fast(bl)) : 0.f;
-            if (EJK) L.SB[tid] = (ok && p.g) ? p.g[tok * H + h] * kLog2e : 0.f;
+            if (EJK) L.SB[tid] = ok ? sg * kLog2e : 0.f;
         }
     }
     __syncthreads();

@@ -110,23 +110,7 @@ __device__ __forceinline__ void f32_seq_bounds(const int32_t* cu, int n, int T, 
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// An empty use of a loaded value: the compiler waits for its load here.
-__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
-// (vectors as one register tuple: split into scalars, they would have to be
-// gathered into a tuple again for the LDS stores)
-__device__ __forceinline__ void settle(float4& x)
-{
-    f32x4_t t = {x.x, x.y, x.z, x.w};
-    asm volatile("" : "+v"(t));
-    x = make_float4(t[0], t[1], t[2], t[3]);
-}
-__device__ __forceinline__ void settle(uint2& x)
-{
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 t = {x.x, x.y};
-    asm volatile("" : "+v"(t));
-    x = make_uint2(t[0], t[1]);
-}
+using kda::settle;
 __device__ __forceinline__ void settle(bf16_t& x)
 {
     uint32_t t = x.bits;

@@ -210,6 +210,34 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// An empty use of a loaded value: the compiler waits for its load here, and
+// cannot sink the load into a branch that alone uses it (where it would be
+// waited for at once, with every other load in flight).  Vectors are settled
+// as one register tuple: split into scalars, they would have to be gathered
+// into a tuple again for 16-byte LDS stores.
+__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle(uint16_t& x)
+{
+    uint32_t t = x;
+    asm volatile("" : "+v"(t));
+    x = (uint16_t)t;
+}
+__device__ __forceinline__ void settle(float4& x)
+{
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 t = {x.x, x.y, x.z, x.w};
+    asm volatile("" : "+v"(t));
+    x = make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void settle(uint2& x)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 t = {x.x, x.y};
+    asm volatile("" : "+v"(t));
+    x = make_uint2(t[0], t[1]);
+}
+
 __device__ __forceinline__ float4 fma4(float a, float4 b, float4 c)
 {
     return make_float4(fmaf(a, b.x, c.x), fmaf(a, b.y, c.y), fmaf(a, b.z, c.z), fmaf(a, b.w, c.w));

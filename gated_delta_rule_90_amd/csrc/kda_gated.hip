@@ -175,21 +175,52 @@ __global__ __launch_bounds__(GTH) void gated_prep(GatedParams p)
     const float lg = p.g_gamma ? p.g_gamma[(size_t)min(n, p.g_gamma_rows - 1) * H + h] : 0.f;
     const Tin* q = static_cast<const Tin*>(p.q);
     const Tin* k = static_cast<const Tin*>(p.k);
-    // 1. the rows to LDS, zero past the chunk's rows; the gates in log2 units
+    // 1. the rows to LDS, zero past the chunk's rows; the gates in log2 units.
+    // The loads go through buffer resources over the chunk's rows in memory
+    // (from its lowest row: the first in processing order, or in reverse the
+    // last), absent gates through empty ones that read zeros, and are all
+    // issued before the first is used, so one wait covers them
+    const int base = p.reverse ? t1 - c * GC - lc : t0 + c * GC;
+    const int qs = H * DK, ks = p.Hkv * DK;   // row strides (elements)
+    constexpr uint32_t SQ = sizeof(Tin);
+    const uint32_t qbytes = ((lc - 1) * qs + DK) * 4;   // the chunk's rows of a float32 [T, H, dk] input
+    const auto rq = buf_rsrc(uniform_ptr(q + ((size_t)base * H + h) * DK),
+                             __builtin_amdgcn_readfirstlane(((lc - 1) * qs + DK) * SQ));
+    const auto rk = buf_rsrc(uniform_ptr(k + ((size_t)base * p.Hkv + hk) * DK),
+                             __builtin_amdgcn_readfirstlane(((lc - 1) * ks + DK) * SQ));
+    const auto rg = buf_rsrc(p.g ? uniform_ptr(p.g + ((size_t)base * H + h) * DK) : nullptr,
+                             __builtin_amdgcn_readfirstlane(p.g ? qbytes : 0u));
+    const auto rgk = buf_rsrc(p.gk ? uniform_ptr(p.gk + ((size_t)base * H + h) * DK) : nullptr,
+                              __builtin_amdgcn_readfirstlane(p.gk ? qbytes : 0u));
+    Tin xq[NE], xk[NE];
+    float xg[NE], xgk[NE];
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+        const int e = tid + m * GTH;
+        const int r = e / DK, i = e % DK;
+        // the row's place in memory from the chunk's lowest row (row 0 for the
+        // padding rows, whose values are replaced below)
+        const int mr = r < lc ? (p.reverse ? lc - 1 - r : r) : 0;
+        xq[m] = buf_load<Tin>(rq, (mr * qs + i) * SQ);
+        xk[m] = buf_load<Tin>(rk, (mr * ks + i) * SQ);
+        xg[m] = buf_load<float>(rg, (mr * qs + i) * 4);
+        xgk[m] = buf_load<float>(rgk, (mr * qs + i) * 4);
+    }
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+        settle(xq[m]);
+        settle(xk[m]);
+        settle(xg[m]);
+        settle(xgk[m]);
+    }
 #pragma unroll
     for (int m = 0; m < NE; ++m) {
         const int e = tid + m * GTH;
         const int r = e / DK, i = e % DK;
         const bool in = r < lc;
-        const int mm = c * GC + (in ? r : 0);
-        const size_t t = (size_t)(p.reverse ? t1 - 1 - mm : t0 + mm);
-        const float qv = widen(q[(t * H + h) * DK + i]);
-        const float kv = widen(k[(t * p.Hkv + hk) * DK + i]);
-        const float gq = p.g ? p.g[(t * H + h) * DK + i] : 0.f;
-        const float gkv = p.gk ? p.gk[(t * H + h) * DK + i] : 0.f;
-        L.QT[r * RS + i] = in ? p.scale * __builtin_amdgcn_exp2f(gq * kLog2e) * qv : 0.f;
-        L.KT[r * RS + i] = in ? kv : 0.f;
-        L.BK[r * RS + i] = in ? (gkv + lg) * kLog2e : 0.f;
+        L.QT[r * RS + i] = in ? p.scale * __builtin_amdgcn_exp2f(xg[m] * kLog2e) * widen(xq[m]) : 0.f;
+        L.KT[r * RS + i] = in ? widen(xk[m]) : 0.f;
+        L.BK[r * RS + i] = in ? (xgk[m] + lg) * kLog2e : 0.f;
     }
     if (tid == 0) L.wide = 0;
     __syncthreads();
