@@ -110,13 +110,6 @@ __device__ __forceinline__ void f32_seq_bounds(const int32_t* cu, int n, int T, 
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-using kda::settle;
-__device__ __forceinline__ void settle(bf16_t& x)
-{
-    uint32_t t = x.bits;
-    asm volatile("" : "+v"(t));
-    x.bits = (uint16_t)t;
-}
 
 // Four consecutive input channels as loaded: a float4 (float32 inputs) or
 // four bf16 in a uint2 (bf16 inputs), widened when used, so that a prefetched
@@ -213,11 +206,26 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     const int nch = (t1 - t0 + FC - 1) / FC;
     const size_t soff = ((size_t)n * H + h) * DK * DV;
 
-    for (int e = tid; e < DK * FJ; e += FT) {
-        const int i = e / FJ, j = e % FJ;
-        L.ST[j * LT::SRS + i] = init ? init[soff + (size_t)i * DV + j0 + j] : 0.f;
+    {
+        // the initial state tile (zeros without one): every load issued, then stored
+        constexpr int SN = DK * FJ / FT;
+        static_assert(SN * FT == DK * FJ, "state tile per thread");
+        const auto ri = buf_rsrc(init ? uniform_ptr(init + soff) : nullptr, init ? (uint32_t)(DK * DV * 4) : 0u);
+        float sv[SN];
+#pragma unroll
+        for (int m = 0; m < SN; ++m) {
+            const int e = tid + m * FT, i = e / FJ, j = e % FJ;
+            sv[m] = buf_load<float>(ri, (uint32_t)((i * DV + j0 + j) * 4));
+        }
+#pragma unroll
+        for (int m = 0; m < SN; ++m) {
+            const int e = tid + m * FT, i = e / FJ, j = e % FJ;
+            L.ST[j * LT::SRS + i] = sv[m];
+        }
     }
-    // the sequence bounds again in scalar registers after the divergent loop
+    // the sequence bounds in scalar registers (the resources built from them
+    // would otherwise need a per-lane loop where the compiler keeps them in
+    // vector registers)
     t0 = __builtin_amdgcn_readfirstlane(t0);
     t1 = __builtin_amdgcn_readfirstlane(t1);
     const float ea = EJK ? 0.f : expf(a_log[h]) * kLog2e;   // exp(a_log) in log2 units
@@ -231,10 +239,9 @@ __global__ __launch_bounds__(FT) void chunk_f32_kernel(
     {
         const auto rd = buf_rsrc(EJK ? nullptr : dt_bias, (!EJK && dt_bias) ? (uint32_t)(DK * H * 4) : 0u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            dtb4[j] = buf_load<float>(rd, (uint32_t)(((4 * (tid % RL) + j) * H + h) * 4));
-            settle(dtb4[j]);
-        }
+        for (int j = 0; j < 4; ++j) dtb4[j] = buf_load<float>(rd, (uint32_t)(((4 * (tid % RL) + j) * H + h) * 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) settle(dtb4[j]);
     }
 
     // One chunk's inputs as loaded into registers: q, k and (KDA) g as pieces of

@@ -217,12 +217,8 @@ __device__ __forceinline__ void lds_barrier()
 // into a tuple again for 16-byte LDS stores.
 __device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void settle(uint32_t& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void settle(uint16_t& x)
-{
-    uint32_t t = x;
-    asm volatile("" : "+v"(t));
-    x = (uint16_t)t;
-}
+__device__ __forceinline__ void settle(uint16_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle(bf16_t& x) { asm volatile("" : "+v"(x.bits)); }
 __device__ __forceinline__ void settle(float4& x)
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -77,6 +77,11 @@ __device__ __forceinline__ float lanes_sum(float x)
 // and the column's dot products finish with lanes_sum<LPC>.  Fewer rows per
 // lane shorten the per-token chain and the registers; the tiles of columns
 // run in parallel workgroups, each repeating the (cheap) prologue.
+__device__ __forceinline__ float raw_of(float x) { return x; }
+__device__ __forceinline__ uint32_t raw_of(bf16_t x) { return x.bits; }
+__device__ __forceinline__ float raw_f32(float x) { return x; }
+__device__ __forceinline__ float raw_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
 template <int DK, int LPC, typename Tin, typename Tout, bool EJK>
 __global__ __launch_bounds__(kWave) void recurrent_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
@@ -151,11 +156,15 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     constexpr int PD = (DK >= 64) ? 8 : 16;
     constexpr int NSLOT = PD / TPP;
     static_assert(NSLOT % 2 == 0, "even ring");
+    // bf16 inputs are carried as their bits zero-extended to 32: a 16-bit
+    // value carried around the loop gets a zero-extension where the loop
+    // starts, which waits for its load there
+    using RawT = std::conditional_t<std::is_same<Tin, float>::value, float, uint32_t>;
     struct Raw {
-        Tin q[PER_LANE], k[PER_LANE];
+        RawT q[PER_LANE], k[PER_LANE];
         float z[PER_LANE];
         float bt;         // this lane's token's beta
-        float vc[TPP];    // v of this lane's column for each token of the pack
+        RawT vc[TPP];     // v of this lane's column for each token of the pack (as loaded)
     };
     const int cc = active ? c : 0;
     const int vz = vector_zero();   // beta and the EJK decay: vector loads, see vector_zero()
@@ -167,15 +176,15 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         for (int p = 0; p < PER_LANE; ++p) {
             const int i = lch + p * kWave;
             const int ic = (i < DK) ? i : 0;   // lanes past dk read channel 0 and are zeroed on use
-            r.q[p] = q[th * DK + ic];
-            r.k[p] = k[tkv * DK + ic];
+            r.q[p] = raw_of(q[th * DK + ic]);
+            r.k[p] = raw_of(k[tkv * DK + ic]);
             if (!EJK) r.z[p] = g[th * DK + ic];
         }
         r.bt = beta[th + vz];
         if (EJK) r.z[0] = g ? g[th + vz] : 0.f;   // EJK: the token's scalar log-decay
 #pragma unroll
         for (int tk = 0; tk < TPP; ++tk)
-            r.vc[tk] = to_f32(v[((size_t)min(tp + tk, t1 - 1) * HKV + hk) * DV + cc]);
+            r.vc[tk] = raw_of(v[((size_t)min(tp + tk, t1 - 1) * HKV + hk) * DV + cc]);
     };
     Raw ring[NSLOT];
     if (t0 < t1) {
@@ -204,14 +213,25 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
     // prologue of the pack in ring slot J, written to set P
     auto prologue = [&](auto J, auto P) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value, pb = decltype(P)::value;
-        const Raw& r = ring[j];
+        Raw& r = ring[j];
+        // the slot's loads are waited for here, where they are used: otherwise
+        // the compiler may widen them where the loop carries them, right after
+        // they are issued
+#pragma unroll
+        for (int p = 0; p < PER_LANE; ++p) {
+            settle(r.q[p]);
+            settle(r.k[p]);
+            if (!EJK) settle(r.z[p]);
+        }
+        settle(r.bt);
+        if (EJK) settle(r.z[0]);
         float qv[PER_LANE], kv[PER_LANE];
         float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
         for (int p = 0; p < PER_LANE; ++p) {
             const bool in = lch + p * kWave < DK;
-            qv[p] = in ? to_f32(r.q[p]) : 0.f;
-            kv[p] = in ? to_f32(r.k[p]) : 0.f;
+            qv[p] = in ? raw_f32(r.q[p]) : 0.f;
+            kv[p] = in ? raw_f32(r.k[p]) : 0.f;
             sq += qv[p] * qv[p];
             sk += kv[p] * kv[p];
             sqk += qv[p] * kv[p];
@@ -281,7 +301,8 @@ __global__ __launch_bounds__(kWave) void recurrent_kernel(
         }
         u = lanes_sum<LPC>(u);
         pq = lanes_sum<LPC>(pq);
-        const float d = pr.bt * (ring[j].vc[tk] - u);
+        settle(ring[j].vc[tk]);
+        const float d = pr.bt * (raw_f32(ring[j].vc[tk]) - u);
         // one lane per column stores; the others pass an index past the row
         row_store(o + ((size_t)t * H + h) * DV, DV, part == 0 ? c : DV, from_f32<Tout>(fmaf(d, pr.kq, pr.as * pq)));
         const float* kk = &sh_k[pb][base];
