@@ -52,18 +52,21 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32
                                    int32_t dv, kda_dtype_t in_dtype, uint32_t flags)
 {
     if (B < 0 || T < 0 || H <= 0 || !dim_ok(dk) || !dim_ok(dv)) return 0;
-    if (!(flags & KDA_CHUNKED) || in_dtype != KDA_BF16) return 0;
+    if (!(flags & KDA_CHUNKED) || (in_dtype != KDA_BF16 && in_dtype != KDA_F32)) return 0;
     const bool packed = num_seqs > 0 && B == 1;
     const int N = packed ? num_seqs : B;
-    kda::PrefillArgs probe{};
-    probe.in_bf16 = true;
-    probe.ejk = (flags & KDA_EJK) != 0;
-    probe.dk = dk;
-    probe.dv = dv;
-    probe.g = reinterpret_cast<const float*>(1);
-    probe.a_log = reinterpret_cast<const float*>(1);
-    if (!kda::chunked_supported(probe)) return 0;
-    return kda::chunked_workspace_bytes(N, T, H, dk, dv, packed);
+    if (in_dtype == KDA_BF16) {
+        kda::PrefillArgs probe{};
+        probe.in_bf16 = true;
+        probe.ejk = (flags & KDA_EJK) != 0;
+        probe.dk = dk;
+        probe.dv = dv;
+        probe.g = reinterpret_cast<const float*>(1);
+        probe.a_log = reinterpret_cast<const float*>(1);
+        if (kda::chunked_supported(probe)) return kda::chunked_workspace_bytes(N, T, H, dk, dv, packed);
+    }
+    if (kda::prefill16_preferred(N, H, dk)) return kda::prefill16_workspace_bytes(N, T, H, dk, packed);
+    return 0;
 }
 
 // kda_prefill and kda_prefill_noalloc: with noalloc set, the chunked MFMA
@@ -156,8 +159,29 @@ static kda_status_t prefill_impl(const void* q, const void* k, const void* v, kd
         }
         return hip_status(kda::launch_chunked(a, st), "kda_prefill (chunked)");
     }
-    if (chunk_ok && kda::chunked_f32_supported(a))
+    if (chunk_ok && kda::chunked_f32_supported(a)) {
+        // at dk >= 64 the float32 arithmetic runs as two kernels on 16-token
+        // chunks when the workspace (or the fixed scratch) holds their operand
+        // blocks; else as the one kernel, which needs none
+        if (kda::prefill16_preferred(N, H, dk)) {
+            const size_t need = kda::prefill16_workspace_bytes(N, T, H, dk, cu_seqlens != nullptr);
+            void* ws = nullptr;
+            if (noalloc) {
+                if (need <= (size_t)KDA_NOALLOC_SCRATCH_BYTES) {
+                    const hipError_t e = kda::noalloc_scratch(&ws);
+                    if (e != hipSuccess) return hip_status(e, "kda_prefill_noalloc: address of the scratch array");
+                }
+            } else if (workspace && workspace_bytes >= need) {
+                ws = workspace;
+            }
+            if (ws) {
+                a.workspace = ws;
+                a.workspace_bytes = need;
+                return hip_status(kda::launch_prefill16(a, st), "kda_prefill (chunked float32, 16-token chunks)");
+            }
+        }
         return hip_status(kda::launch_chunked_f32(a, st), "kda_prefill (chunked float32)");
+    }
     // token-by-token path; with T == 0 it only carries initial_state to final_state
     return hip_status(kda::launch_recurrent(a, st), "kda_prefill (recurrent)");
 }

@@ -102,6 +102,10 @@ struct BwdParams {
     float* prep;          // [slots, H, PrepLayout<dk>::SIZE]  column-independent chunk operands
     float* part_a;        // [slots, H]          a_log gradient per chunk
     float* part_dt;       // [slots, H, dk]      dt_bias gradient per chunk
+    // the forward output (prefill16_scan only)
+    void* out;            // [Ntok, H, dv] float32 or bf16
+    int out_bf16;
+    float* fstate;        // [N, H, dk, dv] or null
 };
 
 typedef float bf32x4_t __attribute__((ext_vector_type(4)));
@@ -615,6 +619,7 @@ __device__ __forceinline__ void store_block(float* dst, const f4v (&pf)[NP])
 
 // An empty use of each register: the compiler waits here for the loads that
 // write them.
+using kda::settle;
 template <int N>
 __device__ __forceinline__ void settle(bf32x4_t (&v)[N])
 {
@@ -684,14 +689,17 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int hk = h / (H / p.Hkv);
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
+    // the initial state tile (zeros without one; rows of idle waves' tiles,
+    // t >= NT, fall past the range), every load issued before one wait
     bf32x4_t S[TPW];
+    {
+        const auto ri = buf_rsrc(p.init ? uniform_ptr(p.init + ((size_t)n * H + h) * DK * dv) : nullptr,
+                                 p.init ? (uint32_t)(DK * dv * 4) : 0u);
 #pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-        const int t = wave + NW * x;
+        for (int x = 0; x < TPW; ++x) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * t + 4 * lk + e;
-            S[x][e] = (t < NT && p.init) ? p.init[(((size_t)n * H + h) * DK + i) * dv + j0 + lm] : 0.f;
+            for (int e = 0; e < 4; ++e)
+                S[x][e] = buf_load<float>(ri, (uint32_t)(((16 * (wave + NW * x) + 4 * lk + e) * dv + j0 + lm) * 4));
         }
     }
     // the initial tile is used here, before the loop: else its loads stay
@@ -720,6 +728,14 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (nck > 0) {
         fetch(pfa, pva, 0);
         fetch(pfb, pvb, min(1, nck - 1));
+        // both sets waited for here: the compiler interleaves their loads, and
+        // the count of loads in flight that it assumes at the loop head is the
+        // larger of the counts on entry and around the loop, so a wait left
+        // pending here would drain the next chunk's prefetch on every chunk
+        settle(pfa);
+        settle(pfb);
+        settle(pva);
+        settle(pvb);
     }
     auto chunk = [&](f4v (&pf)[NP], Tin& pv, int c, auto bsel) __attribute__((always_inline)) {
         constexpr int b = decltype(bsel)::value;
@@ -803,9 +819,198 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
                 }
             }
     };
-    for (int c = 0; c < nck; c += 2) {
+    // both halves of the loop body run on every pass, an odd last chunk after
+    // the loop: a half skipped on some path into the loop head would make the
+    // compiler assume the shorter count of loads in flight there, and wait for
+    // the prefetch on every chunk
+    int c = 0;
+    for (; c + 1 < nck; c += 2) {
         chunk(pfa, pva, c, std::integral_constant<int, 0>{});
-        if (c + 1 < nck) chunk(pfb, pvb, c + 1, std::integral_constant<int, 1>{});
+        chunk(pfb, pvb, c + 1, std::integral_constant<int, 1>{});
+    }
+    if (c < nck) chunk(pfa, pva, c, std::integral_constant<int, 0>{});
+}
+
+// The prefill's output on the same 16-token chunks and operand blocks (the
+// float32-arithmetic route at dk >= 64): per (16 state columns, head,
+// sequence) and chunk
+//     Y = V - Kg S,  U = T diag(beta) Y,  O = Qg S + P U,
+//     S <- Diag(e^{b_C}) S + Kc^T U
+// (EJK: qh and kh with the scalar row factors, P with its decay factors
+// already applied), then the final state.  The products over dk are summed
+// over the waves in LDS; every wave then forms U and O in its registers and
+// stores one row of O in four.
+template <int DK, int NG>
+struct OutLds {
+    alignas(16) float P[2][PrepLayout<DK>::SIZE];
+    float X[NG][2][BC][TV + 1];               // V of each group's tile
+    float PU[NG][BT / kWave][BC][TV + 1];     // per-wave partials of Kg S
+    float PQ[NG][BT / kWave][BC][TV + 1];     // and of Qg S
+};
+
+template <int DK, bool EJK, typename Tin, typename Tout, int NG>
+__global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) void prefill16_scan(BwdParams p)
+{
+    using PL = PrepLayout<DK>;
+    constexpr int RS = PL::RS;
+    constexpr int NT = DK / 16, NW = BT / kWave, TPW = (NT + NW - 1) / NW;
+    constexpr int N4 = PL::SIZE / 4, NP = (N4 + NG * BT - 1) / (NG * BT);
+    constexpr uint32_t SO = sizeof(Tout);
+    __shared__ OutLds<DK, NG> L;
+    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lm = lane & 15, lk = lane >> 4;
+    int j0, h, n;
+    if (!scan_unit(p, NG, j0, h, n)) return;
+    j0 += grp * TV;
+    const int H = p.H, dv = p.dv;
+    const int hk = h / (H / p.Hkv);
+    int t0, t1;
+    seq_bounds(p.cu, n, p.T, t0, t1);
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
+    // the initial state tile (zeros without one), all loads before one wait
+    bf32x4_t S[TPW];
+    {
+        const auto ri = buf_rsrc(p.init ? uniform_ptr(p.init + ((size_t)n * H + h) * DK * dv) : nullptr,
+                                 p.init ? (uint32_t)(DK * dv * 4) : 0u);
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * t + 4 * lk + e;
+                // rows of idle waves' tiles (t >= NT) fall past the range
+                S[x][e] = buf_load<float>(ri, (uint32_t)((i * dv + j0 + lm) * 4));
+            }
+        }
+        settle(S);
+    }
+    const int nck = seq_chunks(p.off, n, t0, t1);
+    const int slot0 = p.off[n];
+    const Tin* vv = static_cast<const Tin*>(p.v);
+    // a ring of two register sets: the inputs of chunk c + 2 are loaded while
+    // chunk c computes (the loop is unrolled by two, so each set is fixed)
+    f4v pfa[NP], pfb[NP];
+    Tin pva = 0, pvb = 0;
+    const int rr = tid / TV, jj = tid % TV;
+    auto fetch = [&](f4v (&pf)[NP], Tin& pv, int c) __attribute__((always_inline)) {
+        const int cs = t0 + c * BC;
+        fetch_block<NP, N4, NG * BT>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
+        pv = vv[((size_t)(cs + (cs + rr < t1 ? rr : 0)) * p.Hkv + hk) * dv + j0 + jj];
+    };
+    if (nck > 0) {
+        fetch(pfa, pva, 0);
+        fetch(pfb, pvb, min(1, nck - 1));
+        // both sets waited for here: the compiler interleaves their loads, and
+        // the count of loads in flight that it assumes at the loop head is the
+        // larger of the counts on entry and around the loop, so a wait left
+        // pending here would drain the next chunk's prefetch on every chunk
+        settle(pfa);
+        settle(pfb);
+        settle(pva);
+        settle(pvb);
+    }
+    Tout* const ob = static_cast<Tout*>(p.out);
+    auto chunk = [&](f4v (&pf)[NP], Tin& pv, int c, auto bsel) __attribute__((always_inline)) {
+        constexpr int b = decltype(bsel)::value;
+        const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
+        const float* P = L.P[b];
+        store_block<NP, N4, NG * BT>(L.P[b], pf);
+        L.X[grp][b][rr][jj] = c0 + rr < t1 ? widen(pv) : 0.f;
+        fetch(pf, pv, min(c + 2, nck - 1));   // past the end: the last chunk again
+        lds_barrier();
+        // Kg S and Qg S: each wave its tiles' part (A = the rows, 16 bytes per lane)
+        {
+            bf32x4_t ak = bf32x4_t{0.f, 0.f, 0.f, 0.f}, aq = ak;
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                const int t = wave + NW * x;
+                if (t < NT) {
+                    const float4 a = *reinterpret_cast<const float4*>(P + PL::KG + lm * RS + 16 * t + 4 * lk);
+                    const float4 qa = *reinterpret_cast<const float4*>(P + PL::QG + lm * RS + 16 * t + 4 * lk);
+                    ak = bmfma4(a.x, S[x][0], ak);
+                    aq = bmfma4(qa.x, S[x][0], aq);
+                    ak = bmfma4(a.y, S[x][1], ak);
+                    aq = bmfma4(qa.y, S[x][1], aq);
+                    ak = bmfma4(a.z, S[x][2], ak);
+                    aq = bmfma4(qa.z, S[x][2], aq);
+                    ak = bmfma4(a.w, S[x][3], ak);
+                    aq = bmfma4(qa.w, S[x][3], aq);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                L.PU[grp][wave][4 * lk + e][lm] = ak[e];
+                L.PQ[grp][wave][4 * lk + e][lm] = aq[e];
+            }
+        }
+        lds_barrier();
+        // Y (rows 4 lk + u of column lm) and U = T diag(beta) Y, in every wave
+        bf32x4_t U = bf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = 4 * lk + u;
+            float ks = (L.PU[grp][0][k][lm] + L.PU[grp][1][k][lm]) + (L.PU[grp][2][k][lm] + L.PU[grp][3][k][lm]);
+            if (EJK) ks *= P[PL::RF + BC + k];
+            const float y = L.X[grp][b][k][lm] - ks;
+            U = bmfma4(P[PL::TI + lm * BC + k], P[PL::BE + k] * y, U);
+        }
+        // O = Qg S + P U (rows 4 lk + e of column lm); U is the B operand as held
+        {
+            bf32x4_t o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lk + e;
+                const float qs = (L.PQ[grp][0][r][lm] + L.PQ[grp][1][r][lm]) + (L.PQ[grp][2][r][lm] + L.PQ[grp][3][r][lm]);
+                o[e] = EJK ? qs * P[PL::RF + r] : qs;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o = bmfma4(P[PL::GP + lm * BC + 4 * lk + u], U[u], o);
+            // wave w stores rows 4 lk + w; rows past the sequence fall outside
+            const float ow = wave == 0 ? o[0] : wave == 1 ? o[1] : wave == 2 ? o[2] : o[3];
+            const auto ro = rows_rsrc(ob + ((size_t)c0 * H + h) * dv + j0, 0, nr, (uint32_t)(H * dv) * SO, TV * SO);
+            buf_store<Tout>(ro, (uint32_t)(((4 * lk + wave) * H * dv + lm) * SO), from_f32<Tout>(ow));
+        }
+        // S <- Diag(e^{b_C}) S + Kc^T U (EJK: kh^T (e^{b_C - b} U))
+        if (EJK) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) U[u] *= P[PL::RF + 2 * BC + 4 * lk + u];
+        }
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            if (t < NT) {
+                bf32x4_t a = S[x];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] *= EJK ? P[PL::RF + 3 * BC] : P[PL::EC + 16 * t + 4 * lk + e];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    a = bmfma4(P[(EJK ? PL::KG : PL::KC) + (4 * lk + u) * RS + 16 * t + lm], U[u], a);
+                S[x] = a;
+            }
+        }
+    };
+    // both halves of the loop body run on every pass, an odd last chunk after
+    // the loop: a half skipped on some path into the loop head would make the
+    // compiler assume the shorter count of loads in flight there, and wait for
+    // the prefetch on every chunk
+    int c = 0;
+    for (; c + 1 < nck; c += 2) {
+        chunk(pfa, pva, c, std::integral_constant<int, 0>{});
+        chunk(pfb, pvb, c + 1, std::integral_constant<int, 1>{});
+    }
+    if (c < nck) chunk(pfa, pva, c, std::integral_constant<int, 0>{});
+    if (p.fstate) {
+        float* fs = p.fstate + ((size_t)n * H + h) * DK * dv;
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const int t = wave + NW * x;
+            if (t < NT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fs[(size_t)(16 * t + 4 * lk + e) * dv + j0 + lm] = S[x][e];
+            }
+        }
     }
 }
 
@@ -838,13 +1043,14 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
     bf32x4_t dS[TPW];
+    {
+        const auto ri = buf_rsrc(p.dSf ? uniform_ptr(p.dSf + ((size_t)n * H + h) * DK * dv) : nullptr,
+                                 p.dSf ? (uint32_t)(DK * dv * 4) : 0u);
 #pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-        const int t = wave + NW * x;
+        for (int x = 0; x < TPW; ++x) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * t + 4 * lk + e;
-            dS[x][e] = (t < NT && p.dSf) ? p.dSf[(((size_t)n * H + h) * DK + i) * dv + j0 + lm] : 0.f;
+            for (int e = 0; e < 4; ++e)
+                dS[x][e] = buf_load<float>(ri, (uint32_t)(((16 * (wave + NW * x) + 4 * lk + e) * dv + j0 + lm) * 4));
         }
     }
     settle(dS);   // as in the forward scan
@@ -871,6 +1077,11 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (nck > 0) {
         fetch(pfa, pda, nck - 1);
         fetch(pfb, pdb, max(nck - 2, 0));
+        // both sets waited for here (as in the forward scan)
+        settle(pfa);
+        settle(pfb);
+        settle(pda);
+        settle(pdb);
     }
     auto chunk = [&](f4v (&pf)[NP], uint32_t& pd, int c, auto bsel) __attribute__((always_inline)) {
         constexpr int b = decltype(bsel)::value;
@@ -971,10 +1182,12 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
                 }
             }
     };
-    for (int k = 0; k < nck; k += 2) {
+    int k = 0;   // (loop shape as in the forward scan)
+    for (; k + 1 < nck; k += 2) {
         chunk(pfa, pda, nck - 1 - k, std::integral_constant<int, 0>{});
-        if (k + 1 < nck) chunk(pfb, pdb, nck - 2 - k, std::integral_constant<int, 1>{});
+        chunk(pfb, pdb, nck - 2 - k, std::integral_constant<int, 1>{});
     }
+    if (k < nck) chunk(pfa, pda, nck - 1 - k, std::integral_constant<int, 0>{});
     if (p.dS0) {
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
@@ -1724,7 +1937,82 @@ hipError_t launch_dk(const BwdParams& p, size_t slots, hipStream_t st)
     return hipGetLastError();
 }
 
+template <int DK, bool EJK>
+hipError_t launch16_dk(const BwdParams& p, size_t slots, hipStream_t st)
+{
+    const dim3 lgrid((unsigned)slots, (unsigned)p.H);
+    if (slots > 0) {
+        if (p.in_bf16) hipLaunchKernelGGL((bwd_prep<DK, EJK, uint16_t>), lgrid, dim3(BT), 0, st, p);
+        else hipLaunchKernelGGL((bwd_prep<DK, EJK, float>), lgrid, dim3(BT), 0, st, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // every (head, sequence) group runs, those without rows too (they carry
+    // the initial state to the final one); tiles as for the backward's scans
+    const unsigned groups8 = (unsigned)((p.H * p.N + 7) / 8 * 8);
+    if (groups8 == 0) return hipSuccess;
+    const bool two = p.dv >= 2 * TV && (size_t)p.H * p.N * (p.dv / (2 * TV)) >= kCUs;
+    const dim3 sgrid(groups8 * (unsigned)(p.dv / (two ? 2 * TV : TV)));
+    const dim3 blk(two ? 2 * BT : BT);
+    if (two) {
+        if (!p.in_bf16) hipLaunchKernelGGL((prefill16_scan<DK, EJK, float, float, 2>), sgrid, blk, 0, st, p);
+        else if (p.out_bf16) hipLaunchKernelGGL((prefill16_scan<DK, EJK, uint16_t, bf16_t, 2>), sgrid, blk, 0, st, p);
+        else hipLaunchKernelGGL((prefill16_scan<DK, EJK, uint16_t, float, 2>), sgrid, blk, 0, st, p);
+    } else {
+        if (!p.in_bf16) hipLaunchKernelGGL((prefill16_scan<DK, EJK, float, float, 1>), sgrid, blk, 0, st, p);
+        else if (p.out_bf16) hipLaunchKernelGGL((prefill16_scan<DK, EJK, uint16_t, bf16_t, 1>), sgrid, blk, 0, st, p);
+        else hipLaunchKernelGGL((prefill16_scan<DK, EJK, uint16_t, float, 1>), sgrid, blk, 0, st, p);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool prefill16_preferred(int N, int H, int dk)
+{
+    // dk >= 64: below that the one-kernel float32 route is as fast and has no
+    // launches to add; (head, sequence) groups as the backward's scans allow
+    return (dk == 64 || dk == 128) && N > 0 && (long long)H * N <= (1LL << 26);
+}
+
+size_t prefill16_workspace_bytes(int N, int T, int H, int dk, bool packed)
+{
+    if (N <= 0 || T <= 0) return 0;
+    const size_t slots = bwd_slots(N, T, packed);
+    return 2 * align256((size_t)(N + 1) * 4) + align256(slots * H * prep_floats(dk) * 4);
+}
+
+hipError_t launch_prefill16(const PrefillArgs& a, hipStream_t st)
+{
+    const bool packed = a.cu != nullptr;
+    const size_t slots = bwd_slots(a.N, a.T, packed);
+    unsigned char* w = static_cast<unsigned char*>(a.workspace);
+    BwdParams p{};
+    p.q = a.q; p.k = a.k; p.v = a.v; p.in_bf16 = a.in_bf16;
+    p.g = a.g; p.beta = a.beta; p.a_log = a.a_log; p.dt_bias = a.dt_bias;
+    p.init = a.init; p.cu = a.cu;
+    p.N = a.N; p.T = a.T; p.H = a.H; p.Hkv = a.Hkv; p.dv = a.dv;
+    p.scale = a.scale; p.lb = a.lower_bound; p.l2norm = a.l2norm;
+    p.out = a.o; p.out_bf16 = a.out_bf16; p.fstate = a.final_state;
+    const size_t pslots = (slots + (size_t)a.N + 1) / 2;
+    int32_t* off = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)(a.N + 1) * 4);
+    int32_t* poff = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)(a.N + 1) * 4);
+    p.off = off;
+    p.poff = poff;
+    p.prep = reinterpret_cast<float*>(w);
+    hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(64), 0, st, a.cu, a.N, a.T, (int)slots, (int)pslots, off,
+                       poff);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (a.dk * 2 + (a.ejk ? 1 : 0)) {
+    case 128: return launch16_dk<64, false>(p, slots, st);
+    case 129: return launch16_dk<64, true>(p, slots, st);
+    case 256: return launch16_dk<128, false>(p, slots, st);
+    default: return launch16_dk<128, true>(p, slots, st);
+    }
+}
 
 size_t backward_workspace_bytes(int N, int T, int H, int Hkv, int dk, int dv, bool packed)
 {

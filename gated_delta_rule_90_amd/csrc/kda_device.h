@@ -84,7 +84,9 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off
 {
     typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
-    if constexpr (sizeof(T) == 4)
+    if constexpr (sizeof(T) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, 0);
+    else if constexpr (sizeof(T) == 4)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
     else if constexpr (sizeof(T) == 8)
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_v, v), r, off, 0, 0);

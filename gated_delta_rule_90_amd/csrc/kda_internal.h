@@ -125,6 +125,12 @@ size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
 // the float32 chunked kernel (16-token chunks on the vector ALUs)
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
+// the float32-arithmetic route in two kernels on 16-token chunks (the
+// backward's operand blocks, then a scan that forms the output), taken over
+// from launch_chunked_f32 at dk >= 64 when the workspace holds the blocks
+bool prefill16_preferred(int N, int H, int dk);
+size_t prefill16_workspace_bytes(int N, int T, int H, int dk, bool packed);
+hipError_t launch_prefill16(const PrefillArgs& a, hipStream_t stream);
 // the gated recurrent attention (kda_gated.hip)
 hipError_t launch_gated(const GatedArgs& a, hipStream_t stream);
 size_t gated_workspace_bytes(int N, int T, int H, int dk, bool packed);

@@ -108,12 +108,15 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *     the MFMA chunked kernel (64-token chunks; KDA and EJK modes) when q, k,
  *     v, o and (KDA) g are 16-byte aligned and, in KDA mode,
  *     lower_bound >= -5 (its decay factors then stay inside the bf16/float32
- *     exponent range); this is the only route that uses the workspace;
+ *     exponent range);
  *   - KDA_CHUNKED with float32 inputs (any dk) or bf16 inputs with dk < 128
- *     runs the chunked kernel that computes in float32 (float32 MFMA,
- *     chunks of 32 tokens at dk <= 32 and 16 above: the chunking changes
- *     rounding only) when q, k and (KDA) g are 16-byte aligned and, in KDA
- *     mode, lower_bound >= -5;
+ *     computes in float32 (float32 MFMA) when q, k and (KDA) g are 16-byte
+ *     aligned and, in KDA mode, lower_bound >= -5: at dk = 64 and 128, when
+ *     the workspace holds them, as two kernels on 16-token chunks (every
+ *     chunk's state-independent operands in parallel, then a scan per 16
+ *     state columns); otherwise, and at dk <= 32, as one kernel (chunks of 32
+ *     tokens at dk <= 32 and 16 above).  The chunking and the split change
+ *     rounding only;
  *   - every other call (KDA_CHUNKED clear, unaligned pointers, or
  *     lower_bound < -5 in KDA mode), whatever its input dtype, runs the
  *     float32 token-by-token kernel.
@@ -142,7 +145,9 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
  * process ends.  A call that takes that route and needs more than that
  * (kda_prefill_workspace_bytes() of its arguments; about 1 KiB per token and
  * head, e.g. 16384 tokens at H = 16) returns KDA_EUNSUPPORTED before any
- * launch.  The array is used on the calling thread's current HIP device,
+ * launch.  The two-kernel float32 route uses the same array when its blocks
+ * fit (about 1.7 KiB per token and head at dk 128), and otherwise runs as one
+ * kernel.  The array is used on the calling thread's current HIP device,
  * which must be the device of `stream` and of the tensors.  Every call on one
  * GPU shares the array and leaves its contents behind: calls that may overlap
  * in time on one GPU (other streams, other host threads) race and must be
@@ -158,11 +163,14 @@ kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, kd
                                  kda_dtype_t out_dtype, float* final_state, void* stream);
 
 /* Device workspace (bytes) kda_prefill needs for these arguments; 0 = none.
- * Only the chunked MFMA path uses it: per (chunk, head) it holds the
- * state-independent operands of that chunk (64.5 KiB), plus the chunk
- * offsets of packed sequences (num_seqs > 0 with B == 1 means packed).  The
- * caller allocates it (the library never allocates); it must not be shared
- * by calls that may run concurrently. */
+ * The chunked routes that split a call into kernels use it: per (chunk,
+ * head) it holds the state-independent operands of that chunk (the MFMA
+ * route: 64.5 KiB per 64-token chunk; the two-kernel float32 route at dk 64
+ * and 128: 15.5 KiB and 27.75 KiB per 16-token chunk), plus the chunk offsets
+ * of packed sequences (num_seqs > 0 with B == 1 means packed).  The caller
+ * allocates it (the library never allocates); it must not be shared by calls
+ * that may run concurrently.  A float32-route call given less runs as one
+ * kernel, which needs none. */
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype_t in_dtype,
                                    uint32_t flags);

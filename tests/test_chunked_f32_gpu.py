@@ -1,6 +1,9 @@
-"""The chunked kernel that computes in float32 (KDA_CHUNKED with float32 inputs,
-or bf16 inputs with dk < 128: 16-token chunks on float32 MFMA) against the
-oracle, and its routing.
+"""The chunked routes that compute in float32 (KDA_CHUNKED with float32 inputs,
+or bf16 inputs with dk < 128) against the oracle, and their routing: at dk 16
+and 32 one kernel (32-token chunks on float32 MFMA); at dk 64 and 128, given the
+workspace, two kernels on 16-token chunks (the operand blocks of every chunk in
+parallel, then a scan per 16 state columns that forms the output), else that
+one kernel (16-token chunks).
 
 Bar: relative L2 <= 1e-5 for o and the final state (float32 path, as for the
 token-by-token kernel); packed sequences and chunk-aligned splits bit for bit."""
@@ -225,3 +228,83 @@ def test_ejkernel_worked_example_shapes(dtype, use_chunked):
     ro, rs = prefill_oracle(inp)
     assert rel_l2(s, rs) <= TOL
     assert rel_l2(o, ro) <= (2e-2 if dtype == "bf16" else TOL)
+
+
+# ---- the two-kernel route (dk 64 and 128 with the workspace)
+
+def _separate_runs_bitwise(inp, o, s):
+    """Each packed sequence run alone gives the packed call's rows and state bit for bit."""
+    cu = inp.cu_seqlens
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if a == b:
+            np.testing.assert_array_equal(s[n], inp.initial_state[n])
+            continue
+        sub = workloads.PrefillInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b],
+                                      None if inp.g is None else inp.g[:, a:b], inp.beta[:, a:b],
+                                      inp.a_log, inp.dt_bias, inp.initial_state[n:n + 1], None,
+                                      inp.dtype, inp.scale, inp.lower_bound, ejk=inp.ejk)
+        on, sn = prefill_gpu(sub)
+        np.testing.assert_array_equal(o[:, a:b], on)
+        np.testing.assert_array_equal(s[n], sn[0])
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("ejk", [False, True])
+def test_two_kernel_route_varlen_bitwise_equal_to_separate_runs(dk, ejk):
+    lens = [17, 0, 100, 1, 48, 3, 250, 16]
+    inp = workloads.prefill_inputs(1, 0, 3, dk, 32, seed=331 + dk, dtype="f32", lengths=lens, ejk=ejk,
+                                   init_state=True)
+    say("two-kernel route varlen", dk, lens, "ejk" if ejk else "kda")
+    o, s = _check(inp)
+    _separate_runs_bitwise(inp, o, s)
+
+
+@pytest.mark.parametrize("dtype,out", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("ejk", [False, True])
+def test_two_kernel_route_many_chunks_grouped_heads(dtype, out, ejk):
+    """600 tokens (38 chunks, a ragged last one) over two sequences, grouped key and
+    value heads, an initial state, dk 128 (float32 inputs) or 64 (bf16 inputs)."""
+    import torch
+    dk = 128 if dtype == "f32" else 64
+    inp = workloads.prefill_inputs(2, 600, 4, dk, 64, seed=392 + ejk, dtype=dtype, ejk=ejk,
+                                   init_state=True, hkv=2)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    say("two-kernel route", dtype, "out", out, "dk", dk, "ejk" if ejk else "kda")
+    o, s = prefill_gpu(inp, out_dtype=od)
+    ro, rs = prefill_oracle(inp)
+    eo, es = rel_l2(o, ro), rel_l2(s, rs)
+    say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
+    assert es <= TOL, es
+    assert eo <= (2e-2 if out == "bf16" else TOL), eo
+
+
+def test_two_kernel_route_split_at_16_token_boundary_bitwise():
+    inp = workloads.prefill_inputs(2, 200, 2, 128, 32, seed=341, dtype="f32", init_state=True)
+    say("two-kernel route split at 112")
+    o, s = prefill_gpu(inp)
+    cut = 112   # a multiple of the 16-token chunk
+    part = lambda x, a, b: x[:, a:b]
+    first = workloads.PrefillInputs(part(inp.q, 0, cut), part(inp.k, 0, cut), part(inp.v, 0, cut),
+                                    part(inp.g, 0, cut), part(inp.beta, 0, cut), inp.a_log, inp.dt_bias,
+                                    inp.initial_state, None, inp.dtype, inp.scale, inp.lower_bound)
+    o1, s1 = prefill_gpu(first)
+    second = workloads.PrefillInputs(part(inp.q, cut, 200), part(inp.k, cut, 200), part(inp.v, cut, 200),
+                                     part(inp.g, cut, 200), part(inp.beta, cut, 200), inp.a_log,
+                                     inp.dt_bias, s1, None, inp.dtype, inp.scale, inp.lower_bound)
+    o2, s2 = prefill_gpu(second)
+    np.testing.assert_array_equal(np.concatenate([o1, o2], axis=1), o)
+    np.testing.assert_array_equal(s2, s)
+
+
+@pytest.mark.parametrize("ejk", [False, True])
+def test_without_workspace_the_one_kernel_route_serves_dk128(monkeypatch, ejk):
+    """A call whose workspace cannot hold the operand blocks (here none) takes the
+    one-kernel float32 route instead: no error, the same bar."""
+    inp = workloads.prefill_inputs(2, 90, 3, 128, 32, seed=393 + ejk, dtype="f32", ejk=ejk, init_state=True)
+    say("dk 128 without a workspace", "ejk" if ejk else "kda")
+    import gated_delta_rule_90_amd as kda
+    o_w, s_w = _check(inp)
+    monkeypatch.setattr(kda, "prefill_workspace_bytes", lambda *a, **k: 0)
+    o_1, s_1 = _check(inp)
+    assert rel_l2(o_1, o_w) <= 2 * TOL and rel_l2(s_1, s_w) <= 2 * TOL

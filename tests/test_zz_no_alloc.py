@@ -49,11 +49,21 @@ def test_noalloc_matches_kda_prefill_two_calls(ejk):
         assert eo <= TOL and es <= TOL
 
 
-def test_noalloc_routes_without_scratch():
-    """float32 inputs take the float32 chunked kernel, which uses no scratch."""
-    inp = workloads.prefill_inputs(2, 70, 3, 64, 32, seed=1610, dtype="f32", init_state=True)
-    say("noalloc float32 route")
-    o_n, s_n = _run(inp, noalloc=True)
-    o_r, s_r = _run(inp, noalloc=False)
-    np.testing.assert_array_equal(o_n, o_r)
-    np.testing.assert_array_equal(s_n, s_r)
+@pytest.mark.parametrize("dk", [64, 128])
+def test_noalloc_float32_two_kernel_route_two_calls(dk):
+    """float32 inputs at dk 64 and 128 take the two-kernel float32 route, its
+    operand blocks in the scratch array: two calls in a row, the second smaller,
+    bit for bit kda_prefill's results and within the float32 bar of the oracle."""
+    big = workloads.prefill_inputs(2, 700, 4, dk, 64, seed=1610 + dk, dtype="f32", init_state=True)
+    small = workloads.prefill_inputs(1, 0, 3, dk, 32, seed=1611 + dk, dtype="f32", init_state=True,
+                                     lengths=[70, 0, 33])
+    for name, inp in (("B2 T700 H4", big), ("packed 70/0/33 H3 dv32", small)):
+        say("noalloc float32", dk, name)
+        o_n, s_n = _run(inp, noalloc=True)
+        o_r, s_r = _run(inp, noalloc=False)
+        np.testing.assert_array_equal(o_n, o_r)
+        np.testing.assert_array_equal(s_n, s_r)
+        ro, rs = prefill_oracle(inp)
+        eo, es = rel_l2(o_n, ro), rel_l2(s_n, rs)
+        say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
+        assert eo <= 1e-5 and es <= 1e-5
