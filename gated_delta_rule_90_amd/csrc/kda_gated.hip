@@ -375,14 +375,17 @@ __global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) v
     const int slot0 = p.off[n];
     const size_t soff = ((size_t)n * H + h) * DK;
     const bool hv = p.gv != nullptr;
+    // the initial state tile (zeros without one; rows of idle waves' tiles,
+    // t >= NT, fall past the range), every load issued before one wait
     gf32x4_t S[TPW];
+    {
+        const auto ri = buf_rsrc(p.init ? uniform_ptr(p.init + soff * DV) : nullptr,
+                                 p.init ? (uint32_t)(DK * DV * 4) : 0u);
 #pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-        const int t = wave + GNW * x;
+        for (int x = 0; x < TPW; ++x) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * t + 4 * lk + e;
-            S[x][e] = (t < NT && p.init) ? p.init[(soff + i) * DV + j0 + lm] : 0.f;
+            for (int e = 0; e < 4; ++e)
+                S[x][e] = buf_load<float>(ri, (uint32_t)(((16 * (wave + GNW * x) + 4 * lk + e) * DV + j0 + lm) * 4));
         }
     }
     // the initial tile is used here, before the loop: else its loads stay
@@ -405,11 +408,31 @@ __global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) v
         gfetch_block<NP, N4, NG * GTH>(pf, p.prep + ((size_t)(slot0 + c) * H + h) * PL::SIZE);
         const size_t t = tok(c * GC + rr);
         pv = vv[(t * p.Hkv + hk) * DV + j0 + jj];
-        pg = hv ? p.gv[(t * H + h) * DV + j0 + jj] : 0.f;
+        // the value gate through a resource over the chunk's rows in memory
+        // (from its lowest row; empty without the gate): a load on one path
+        // only would make the compiler's waits count the other path's loads
+        const int lc = min(GC, len - c * GC), tb = p.reverse ? t1 - c * GC - lc : t0 + c * GC;
+        const float* gb = hv ? p.gv + ((size_t)tb * H + h) * DV + j0 : nullptr;
+        const auto rg = buf_rsrc(uniform_ptr(gb), __builtin_amdgcn_readfirstlane(hv ? ((lc - 1) * H * DV + GJ) * 4 : 0));
+        const int mr = rr < lc ? (p.reverse ? lc - 1 - rr : rr) : 0;
+        pg = buf_load<float>(rg, (uint32_t)((mr * H * DV + jj) * 4));
     };
     if (nch > 0) {
         fetch(pfa, pva, pga, 0);
         fetch(pfb, pvb, pgb, min(1, nch - 1));
+        // both sets waited for here: the compiler interleaves their loads, and
+        // the count of loads in flight that it assumes at the loop head is the
+        // larger of the counts on entry and around the loop, so a wait left
+        // pending here would drain the next chunk's prefetch on every chunk
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+            asm volatile("" : "+v"(pfa[m]));
+            asm volatile("" : "+v"(pfb[m]));
+        }
+        settle(pva);
+        settle(pvb);
+        settle(pga);
+        settle(pgb);
     }
     auto chunk = [&](gf4v (&pf)[NP], Tin& pv, float& pg, int c, auto bsel) __attribute__((always_inline)) {
         constexpr int b = decltype(bsel)::value;
@@ -457,10 +480,11 @@ __global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) v
             if (rr == GC - 1) L.EVC[cg][jj] = __builtin_amdgcn_exp2f(bc);
         }
         lds_barrier();
-        // the outputs (wave 0): O = e^{bv} (QE S) + e^{bv - bv_0} A (e^{bv_0 - bv} v),
-        // the second product on MFMA (lane (lm, lk) supplies A[lm][4 lk + u] and
-        // the scaled v[4 lk + u][lm] at step u); element by element when wide
-        if (wave == 0) {
+        // the outputs: O = e^{bv} (QE S) + e^{bv - bv_0} A (e^{bv_0 - bv} v), the
+        // second product on MFMA in every wave (lane (lm, lk) supplies A[lm][4 lk + u]
+        // and the scaled v[4 lk + u][lm] at step u; element by element when wide);
+        // wave w forms and stores rows 4 lk + w, so every wave issues one store
+        {
             gf32x4_t ai = gf32x4_t{0.f, 0.f, 0.f, 0.f};
             const bool ew = hv && L.vwide[cg];
             if (!ew) {
@@ -470,44 +494,36 @@ __global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) v
                     ai = gmfma4(P[PL::AM + lm * GC + s2], hv ? L.VF[cg][s2][lm] : L.X[cg][b][s2][lm], ai);
                 }
             }
-            float bvs[GC];
-            if (ew) {
+            const int r = 4 * lk + wave;
+            const float aiw = wave == 0 ? ai[0] : wave == 1 ? ai[1] : wave == 2 ? ai[2] : ai[3];
+            const float oi = (L.PU[cg][0][r][lm] + L.PU[cg][1][r][lm]) + (L.PU[cg][2][r][lm] + L.PU[cg][3][r][lm]);
+            float o;
+            if (!hv) {
+                o = oi + aiw;
+            } else if (!ew) {
+                o = L.ER[cg][r][lm] * oi + L.EL[cg][r][lm] * aiw;
+            } else {
+                float bvs[GC];
                 float acc = 0.f;
 #pragma unroll
                 for (int s2 = 0; s2 < GC; ++s2) {
                     acc += L.GV[cg][b][s2][lm];
                     bvs[s2] = acc;
                 }
-            }
-            // rows 4 lk + e of column lm; rows past the chunk fall outside the
-            // store's range: forward order from the chunk's first token, reverse
-            // order from its last one backwards
-            const int tb = p.reverse ? t1 - c * GC - lc : t0 + c * GC;
-            Tout* ob = static_cast<Tout*>(p.o) + ((size_t)tb * H + h) * DV + j0;
-            const int range = ((lc - 1) * H * DV + GJ) * (int)sizeof(Tout);
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ob, 0, range, 0x00020000);
+                float br = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lk + e;
-                const float oi = (L.PU[cg][0][r][lm] + L.PU[cg][1][r][lm]) + (L.PU[cg][2][r][lm] + L.PU[cg][3][r][lm]);
-                float o;
-                if (!hv) {
-                    o = oi + ai[e];
-                } else if (!ew) {
-                    o = L.ER[cg][r][lm] * oi + L.EL[cg][r][lm] * ai[e];
-                } else {
-                    o = L.ER[cg][r][lm] * oi;
-                    for (int s2 = 0; s2 <= r; ++s2)
-                        o = fmaf(P[PL::AM + r * GC + s2] * __builtin_amdgcn_exp2f(bvs[r] - bvs[s2]), L.X[cg][b][s2][lm], o);
-                }
-                const int trow = p.reverse ? lc - 1 - r : r;   // negative past the chunk: out of range
-                const int boff = (trow * H * DV + lm) * (int)sizeof(Tout);
-                const Tout ov = from_f32<Tout>(o);
-                if constexpr (sizeof(Tout) == 4)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), rs, boff, 0, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, ov), rs, boff, 0, 0);
+                for (int s2 = 0; s2 < GC; ++s2) br = s2 == r ? bvs[s2] : br;
+                o = L.ER[cg][r][lm] * oi;
+                for (int s2 = 0; s2 <= r; ++s2)
+                    o = fmaf(P[PL::AM + r * GC + s2] * __builtin_amdgcn_exp2f(br - bvs[s2]), L.X[cg][b][s2][lm], o);
             }
+            // rows past the chunk fall outside the store's range: forward order
+            // from the chunk's first token, reverse order from its last one backwards
+            const int tb = p.reverse ? t1 - c * GC - lc : t0 + c * GC;
+            const auto rs = buf_rsrc(uniform_ptr(static_cast<Tout*>(p.o) + ((size_t)tb * H + h) * DV + j0),
+                                     __builtin_amdgcn_readfirstlane(((lc - 1) * H * DV + GJ) * (int)sizeof(Tout)));
+            const int trow = p.reverse ? lc - 1 - r : r;   // negative past the chunk: out of range
+            buf_store<Tout>(rs, (uint32_t)((trow * H * DV + lm) * (int)sizeof(Tout)), from_f32<Tout>(o));
         }
         // the state update: S <- e^{bk_C + bv_C} S + Kc^T (e^{bv_C - bv} v)
 #pragma unroll
@@ -527,10 +543,15 @@ __global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
     };
-    for (int c = 0; c < nch; c += 2) {
+    // both halves of the loop body run on every pass, an odd last chunk after
+    // the loop (a half skipped on some path into the loop head would make the
+    // compiler assume the shorter count of loads in flight there)
+    int c = 0;
+    for (; c + 1 < nch; c += 2) {
         chunk(pfa, pva, pga, c, std::integral_constant<int, 0>{});
-        if (c + 1 < nch) chunk(pfb, pvb, pgb, c + 1, std::integral_constant<int, 1>{});
+        chunk(pfb, pvb, pgb, c + 1, std::integral_constant<int, 1>{});
     }
+    if (c < nch) chunk(pfa, pva, pga, c, std::integral_constant<int, 0>{});
     if (p.final_state) {
 #pragma unroll
         for (int x = 0; x < TPW; ++x) {
