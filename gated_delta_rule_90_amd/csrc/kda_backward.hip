@@ -1253,11 +1253,17 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
         if (p.poff[mid] <= ps) lo = mid;
         else hi = mid - 1;
     }
-    const int n = lo;
+    // the sequence and its ranges in scalar registers, read once: read where
+    // used, the chunk offset was a vector load issued after the chunk's inputs
+    // and waited for at once, with them
+    const int n = __builtin_amdgcn_readfirstlane(lo);
     int t0, t1;
     seq_bounds(p.cu, n, p.T, t0, t1);
-    const int nck = seq_chunks(p.off, n, t0, t1);
-    const int ca = 2 * (ps - p.poff[n]);   // the pair's chunks: ca and, if it exists, ca + 1
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
+    const int offn = __builtin_amdgcn_readfirstlane(p.off[n]);
+    const int nck = __builtin_amdgcn_readfirstlane(seq_chunks(p.off, n, t0, t1));
+    const int ca = 2 * (ps - __builtin_amdgcn_readfirstlane(p.poff[n]));   // the pair's chunks: ca and, if it exists, ca + 1
     const bool has_b = ca + 1 < nck;
     const int nj = dv / 16;
     const float ea = EJK ? 0.f : expf(p.a_log[h]);
@@ -1286,7 +1292,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     load_tile(d1r, p.ckdS + ((size_t)ps * H + h) * DK * dv);
     // ---- one chunk: its inputs (S0, dS1 in s0r, d1r), its gradients
     auto run_chunk = [&](const int c) __attribute__((always_inline)) {
-        const int slot = p.off[n] + c;
+        const int slot = offn + c;
         const int c0 = t0 + c * BC, nr = min(BC, t1 - c0);
         // the chunk's inputs through buffer resources over its rows: rows past
         // the chunk's end read as zero.  q, k and the gate: element
@@ -1310,7 +1316,10 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                 if (!EJK) xg[m] = buf_load<float>(rows_rsrc(gsrc, rm, nr, qs * 4, DK * 4), (r0 * qs + i) * 4);
             }
         }
-        const float dtb_row = (!EJK && p.dt_bias) ? p.dt_bias[(size_t)(tid % DK) * H + h] : 0.f;
+        // dt_bias through a resource that is empty without one: loads on one
+        // path only would make the compiler's later waits drain every load in flight
+        const auto rdt = buf_rsrc(EJK ? nullptr : p.dt_bias, (!EJK && p.dt_bias) ? (uint32_t)(DK * H * 4) : 0u);
+        const float dtb_row = buf_load<float>(rdt, (uint32_t)(((tid % DK) * H + h) * 4));
         // dO (raw bits), U, Z, Y: element e = tid + m BT, row e / MAXD, column
         // e % MAXD (columns past dv are read, then replaced by zero)
         uint32_t xo[NV];
@@ -1344,12 +1353,13 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
                 xz[m] = ok ? z : 0.f;
             }
         }
-        float xb = 0.f, xgs = 0.f;
-        if (tid < BC) {
-            const size_t tok = (size_t)(c0 + (tid < nr ? tid : 0));
-            xb = p.beta[tok * H + h];
-            xgs = (EJK && p.g) ? p.g[tok * H + h] : 0.f;
-        }
+        // beta and the EJK decay of row tid % BC (used by lanes tid < BC): rows
+        // past the chunk read zero
+        const float xb = buf_load<float>(rows_rsrc(p.beta + (size_t)c0 * H + h, 0, nr, H * 4, 4), (tid % BC) * H * 4);
+        float xgs = 0.f;
+        if constexpr (EJK)
+            xgs = buf_load<float>(rows_rsrc(p.g ? p.g + (size_t)c0 * H + h : nullptr, 0, p.g ? nr : 0, H * 4, 4),
+                                  (tid % BC) * H * 4);
         // KDA: the gate and dt_bias of the elements this lane owns in the MFMA
         // layout (row 4 lk + e, channel 16 t + lm)
         float gl[TPW][4], dtl[TPW];
@@ -1357,7 +1367,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
         for (int x = 0; x < TPW; ++x) {
             const int t = wave + NW * x;
             const bool ok = !EJK && t < NT;
-            dtl[x] = ok && p.dt_bias ? p.dt_bias[(size_t)(16 * t + lm) * H + h] : 0.f;
+            dtl[x] = buf_load<float>(rdt, (uint32_t)(((16 * t + lm) * H + h) * 4));   // channels past dk: zero
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // rows from e on; the lane's row 4 lk + e is 4 lk past the first
@@ -1753,7 +1763,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
         // supplying U[4 lk + u][16 jb + lm] and Kc[4 lk + u][16 t + lm]
         {
             using PL = PrepLayout<DK>;
-            const int sa = p.off[n] + ca;
+            const int sa = offn + ca;
             const float* yu = p.ckYU + ((size_t)sa * H + h) * 2 * BC * dv;
             const float* pb = p.prep + ((size_t)sa * H + h) * PL::SIZE;
             for (int e = tid; e < BC * MAXD; e += BT) {
