@@ -160,9 +160,9 @@ static kda_status_t prefill_impl(const void* q, const void* k, const void* v, kd
         return hip_status(kda::launch_chunked(a, st), "kda_prefill (chunked)");
     }
     if (chunk_ok && kda::chunked_f32_supported(a)) {
-        // at dk >= 64 the float32 arithmetic runs as two kernels on 16-token
-        // chunks when the workspace (or the fixed scratch) holds their operand
-        // blocks; else as the one kernel, which needs none
+        // with H dk >= 128 the float32 arithmetic runs as two kernels on
+        // 16-token chunks when the workspace (or the fixed scratch) holds their
+        // operand blocks; else as the one kernel, which needs none
         if (kda::prefill16_preferred(N, H, dk)) {
             const size_t need = kda::prefill16_workspace_bytes(N, T, H, dk, cu_seqlens != nullptr);
             void* ws = nullptr;

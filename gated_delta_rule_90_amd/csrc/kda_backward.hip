@@ -832,7 +832,7 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // The prefill's output on the same 16-token chunks and operand blocks (the
-// float32-arithmetic route at dk >= 64): per (16 state columns, head,
+// float32-arithmetic route of calls with a workspace): per (16 state columns, head,
 // sequence) and chunk
 //     Y = V - Kg S,  U = T diag(beta) Y,  O = Qg S + P U,
 //     S <- Diag(e^{b_C}) S + Kc^T U
@@ -1980,9 +1980,12 @@ hipError_t launch16_dk(const BwdParams& p, size_t slots, hipStream_t st)
 
 bool prefill16_preferred(int N, int H, int dk)
 {
-    // dk >= 64: below that the one-kernel float32 route is as fast and has no
-    // launches to add; (head, sequence) groups as the backward's scans allow
-    return (dk == 64 || dk == 128) && N > 0 && (long long)H * N <= (1LL << 26);
+    // Narrow calls (H dk < 128: fp32 B1 T64 H2 d16 runs in 8.4 us as the one
+    // kernel against 12 us as two) stay on the one kernel.  The rule depends on
+    // neither the token count nor the packing, so that packed sequences and
+    // splits take the route of the sequences run alone.  (Head, sequence)
+    // groups as the backward's scans allow.
+    return N > 0 && (long long)H * N <= (1LL << 26) && H * dk >= 128;
 }
 
 size_t prefill16_workspace_bytes(int N, int T, int H, int dk, bool packed)
@@ -2017,6 +2020,10 @@ hipError_t launch_prefill16(const PrefillArgs& a, hipStream_t st)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (a.dk * 2 + (a.ejk ? 1 : 0)) {
+    case 32: return launch16_dk<16, false>(p, slots, st);
+    case 33: return launch16_dk<16, true>(p, slots, st);
+    case 64: return launch16_dk<32, false>(p, slots, st);
+    case 65: return launch16_dk<32, true>(p, slots, st);
     case 128: return launch16_dk<64, false>(p, slots, st);
     case 129: return launch16_dk<64, true>(p, slots, st);
     case 256: return launch16_dk<128, false>(p, slots, st);

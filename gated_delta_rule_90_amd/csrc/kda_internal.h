@@ -127,7 +127,7 @@ hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);
 // the float32-arithmetic route in two kernels on 16-token chunks (the
 // backward's operand blocks, then a scan that forms the output), taken over
-// from launch_chunked_f32 at dk >= 64 when the workspace holds the blocks
+// from launch_chunked_f32 when H dk >= 128 and the workspace holds the blocks
 bool prefill16_preferred(int N, int H, int dk);
 size_t prefill16_workspace_bytes(int N, int T, int H, int dk, bool packed);
 hipError_t launch_prefill16(const PrefillArgs& a, hipStream_t stream);

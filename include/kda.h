@@ -111,12 +111,13 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *     exponent range);
  *   - KDA_CHUNKED with float32 inputs (any dk) or bf16 inputs with dk < 128
  *     computes in float32 (float32 MFMA) when q, k and (KDA) g are 16-byte
- *     aligned and, in KDA mode, lower_bound >= -5: at dk = 64 and 128, when
+ *     aligned and, in KDA mode, lower_bound >= -5: with H * dk >= 128, when
  *     the workspace holds them, as two kernels on 16-token chunks (every
  *     chunk's state-independent operands in parallel, then a scan per 16
- *     state columns); otherwise, and at dk <= 32, as one kernel (chunks of 32
- *     tokens at dk <= 32 and 16 above).  The chunking and the split change
- *     rounding only;
+ *     state columns); otherwise as one kernel (chunks of 32 tokens at
+ *     dk <= 32 and 16 above).  The rule depends on neither the token count
+ *     nor the packing, so packed sequences take the route of the sequences
+ *     run alone.  The chunking and the split change rounding only;
  *   - every other call (KDA_CHUNKED clear, unaligned pointers, or
  *     lower_bound < -5 in KDA mode), whatever its input dtype, runs the
  *     float32 token-by-token kernel.
@@ -165,8 +166,9 @@ kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, kd
 /* Device workspace (bytes) kda_prefill needs for these arguments; 0 = none.
  * The chunked routes that split a call into kernels use it: per (chunk,
  * head) it holds the state-independent operands of that chunk (the MFMA
- * route: 64.5 KiB per 64-token chunk; the two-kernel float32 route at dk 64
- * and 128: 15.5 KiB and 27.75 KiB per 16-token chunk), plus the chunk offsets
+ * route: 64.5 KiB per 64-token chunk; the two-kernel float32 route: 6.25,
+ * 9.25, 15.5 and 27.75 KiB per 16-token chunk at dk 16, 32, 64 and 128), plus
+ * the chunk offsets
  * of packed sequences (num_seqs > 0 with B == 1 means packed).  The caller
  * allocates it (the library never allocates); it must not be shared by calls
  * that may run concurrently.  A float32-route call given less runs as one

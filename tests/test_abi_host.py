@@ -192,15 +192,21 @@ def test_workspace_query_is_host_only():
     assert packed == 256 + (512 + 8) * 32 * 66048
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 100, 128, kda.CHUNKED) == 0
     assert kda.prefill_workspace_bytes(0, 1, 64, 2, 128, 16, kda.CHUNKED) == 2 * 66048   # 16-column tiles
-    # float32 arithmetic at dk >= 64 (bf16 dk 64, float32 dk 64 and 128): two 256-byte
-    # blocks of chunk and pair offsets, then one operand block per 16-token chunk and
-    # head: 3968 floats at dk 64, 7104 at dk 128 (rows padded to dk + 4 floats)
+    # float32 arithmetic (float32 inputs, bf16 with dk < 128) with H dk >= 128: two
+    # 256-byte blocks of chunk and pair offsets, then one operand block per 16-token
+    # chunk and head: 1600, 2368, 3968, 7104 floats at dk 16, 32, 64, 128 (rows padded
+    # to dk + 4 floats)
     assert kda.prefill_workspace_bytes(0, 1, 64, 2, 64, 128, kda.CHUNKED) == 512 + 4 * 2 * 3968 * 4
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED, kda.F32) == \
         512 + 4 * 256 * 16 * 7104 * 4
     assert kda.prefill_workspace_bytes(5, 1, 1000, 4, 64, 32, kda.CHUNKED, kda.F32) == \
         512 + (1000 // 16 + 5) * 4 * 3968 * 4                   # packed: a slot bound per sequence
-    assert kda.prefill_workspace_bytes(0, 1, 64, 2, 32, 32, kda.CHUNKED, kda.F32) == 0   # dk 32: one kernel
+    assert kda.prefill_workspace_bytes(0, 2, 2048, 16, 32, 32, kda.CHUNKED, kda.F32) == \
+        512 + 2 * 128 * 16 * 2368 * 4
+    assert kda.prefill_workspace_bytes(0, 1, 256, 8, 16, 16, kda.CHUNKED, kda.F32) == 512 + 16 * 8 * 1600 * 4
+    # H dk < 128: the one kernel, no workspace, whatever the token count
+    assert kda.prefill_workspace_bytes(0, 1, 64, 2, 16, 16, kda.CHUNKED, kda.F32) == 0
+    assert kda.prefill_workspace_bytes(0, 1, 65536, 3, 32, 32, kda.CHUNKED, kda.F32) == 0
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.QK_L2NORM) == 0
     assert kda.prefill_workspace_bytes(0, 4, 4096, 16, 128, 128, kda.CHUNKED | kda.EJK) == n
 

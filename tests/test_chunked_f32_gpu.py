@@ -1,9 +1,8 @@
 """The chunked routes that compute in float32 (KDA_CHUNKED with float32 inputs,
-or bf16 inputs with dk < 128) against the oracle, and their routing: at dk 16
-and 32 one kernel (32-token chunks on float32 MFMA); at dk 64 and 128, given the
-workspace, two kernels on 16-token chunks (the operand blocks of every chunk in
-parallel, then a scan per 16 state columns that forms the output), else that
-one kernel (16-token chunks).
+or bf16 inputs with dk < 128) against the oracle, and their routing: with
+H dk >= 128 and the workspace, two kernels on 16-token chunks (the operand
+blocks of every chunk in parallel, then a scan per 16 state columns that forms
+the output); otherwise one kernel (32-token chunks at dk <= 32, 16 above).
 
 Bar: relative L2 <= 1e-5 for o and the final state (float32 path, as for the
 token-by-token kernel); packed sequences and chunk-aligned splits bit for bit."""
@@ -249,25 +248,25 @@ def _separate_runs_bitwise(inp, o, s):
         np.testing.assert_array_equal(s[n], sn[0])
 
 
-@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
 @pytest.mark.parametrize("ejk", [False, True])
 def test_two_kernel_route_varlen_bitwise_equal_to_separate_runs(dk, ejk):
     lens = [17, 0, 100, 1, 48, 3, 250, 16]
-    inp = workloads.prefill_inputs(1, 0, 3, dk, 32, seed=331 + dk, dtype="f32", lengths=lens, ejk=ejk,
-                                   init_state=True)
+    inp = workloads.prefill_inputs(1, 0, 8, dk, 32, seed=331 + dk, dtype="f32", lengths=lens, ejk=ejk,
+                                   init_state=True)   # H dk >= 128: the two-kernel route
     say("two-kernel route varlen", dk, lens, "ejk" if ejk else "kda")
     o, s = _check(inp)
     _separate_runs_bitwise(inp, o, s)
 
 
-@pytest.mark.parametrize("dtype,out", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("dtype,out,dk", [("f32", "f32", 128), ("f32", "f32", 32), ("bf16", "bf16", 64),
+                                          ("bf16", "f32", 64), ("bf16", "f32", 16)])
 @pytest.mark.parametrize("ejk", [False, True])
-def test_two_kernel_route_many_chunks_grouped_heads(dtype, out, ejk):
+def test_two_kernel_route_many_chunks_grouped_heads(dtype, out, dk, ejk):
     """600 tokens (38 chunks, a ragged last one) over two sequences, grouped key and
-    value heads, an initial state, dk 128 (float32 inputs) or 64 (bf16 inputs)."""
+    value heads, an initial state; H dk >= 128 (the two-kernel route) at every dk."""
     import torch
-    dk = 128 if dtype == "f32" else 64
-    inp = workloads.prefill_inputs(2, 600, 4, dk, 64, seed=392 + ejk, dtype=dtype, ejk=ejk,
+    inp = workloads.prefill_inputs(2, 600, max(4, 128 // dk), dk, 64, seed=392 + ejk, dtype=dtype, ejk=ejk,
                                    init_state=True, hkv=2)
     od = torch.bfloat16 if out == "bf16" else torch.float32
     say("two-kernel route", dtype, "out", out, "dk", dk, "ejk" if ejk else "kda")
