@@ -411,7 +411,9 @@ def _prefill_run(inp, steps, warmup, nsets=1, split=None, graph=False, keep=Fals
     nbytes = prefill_bytes(ntok, H, dk, dv, nst, s0 is not None, inp.ejk, io_bytes, inp.k.shape[2])
     res = {"tokens_per_s": round(ntok / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
            "wall_ms_per_call": round(wall * 1e3 / (steps + 1), 4), "alg_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "path": "chunked MFMA" if mfma else ("chunked float32" if chunked else "token-by-token")}
+           "path": "chunked MFMA" if mfma else (
+               ("chunked float32, two kernels (16-token operand blocks, then the scan)" if H * dk >= 128
+                else "chunked float32, one kernel") if chunked else "token-by-token")}
     if mfma:
         fl = prefill_flops(ntok, H, dk, dv)
         tfs = fl / (ms * 1e-3) / 1e12
