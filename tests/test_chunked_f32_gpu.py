@@ -257,6 +257,17 @@ def test_two_kernel_route_varlen_bitwise_equal_to_separate_runs(dk, ejk):
     say("two-kernel route varlen", dk, lens, "ejk" if ejk else "kda")
     o, s = _check(inp)
     _separate_runs_bitwise(inp, o, s)
+    # without the final state (no state stores) the output is the same bit for bit
+    import torch
+    import gated_delta_rule_90_amd as kda
+    from tests._common import dev
+    f = torch.float32
+    o2 = kda.prefill(dev(inp.q, f), dev(inp.k, f), dev(inp.v, f), dev(inp.g, f), dev(inp.beta, f),
+                     None if ejk else dev(inp.a_log, f), None if ejk else dev(inp.dt_bias, f),
+                     dev(inp.initial_state, f), dev(inp.cu_seqlens, torch.int32), scale=inp.scale,
+                     lower_bound=inp.lower_bound, ejk=ejk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o2.cpu().numpy(), o)
 
 
 @pytest.mark.parametrize("dtype,out,dk", [("f32", "f32", 128), ("f32", "f32", 32), ("bf16", "bf16", 64),
