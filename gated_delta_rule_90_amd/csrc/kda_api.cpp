@@ -147,15 +147,19 @@ static kda_status_t prefill_impl(const void* q, const void* k, const void* v, kd
     if (chunk_ok && kda::chunked_supported(a) && a16(v) && a16(o)) {
         // the MFMA kernel also moves v and o 16 bytes per lane
         const size_t need = kda::chunked_workspace_bytes(N, T, H, dk, dv, cu_seqlens != nullptr);
+        // a dense batch also runs with less, in segments of whole chunks (the
+        // same result bit for bit); packed sequences need the whole records
+        const size_t least = cu_seqlens ? need : kda::chunked_min_workspace_bytes(N, H, dk, dv, final_state == nullptr);
         if (noalloc) {
-            if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+            if (least > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
                 return fail(KDA_EUNSUPPORTED, "kda_prefill_noalloc: the call needs %zu bytes of scratch, "
-                            "more than the library's fixed %zu", need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+                            "more than the library's fixed %zu", least, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
             const hipError_t e = kda::noalloc_scratch(&a.workspace);
             if (e != hipSuccess) return hip_status(e, "kda_prefill_noalloc: address of the scratch array");
             a.workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
-        } else if (need > 0 && (!workspace || workspace_bytes < need)) {
-            return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        } else if (need > 0 && (!workspace || workspace_bytes < least)) {
+            return fail(KDA_EINVAL, "kda_prefill: workspace of %zu bytes required (got %zu; a dense batch "
+                        "runs in segments from %zu)", need, workspace_bytes, least);
         }
         return hip_status(kda::launch_chunked(a, st), "kda_prefill (chunked)");
     }

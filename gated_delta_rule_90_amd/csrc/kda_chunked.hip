@@ -197,14 +197,15 @@ __device__ __forceinline__ float rowsum16(float (&a)[16], int lane)
 // index of the off-diagonal pair (I, J), I > J, in the pair-vector table
 __device__ __forceinline__ int pair_slot(int I, int J) { return I * (I - 1) / 2 + J; }
 
-// Sequence bounds (clamped) of sequence n.
-__device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int T, int& t0, int& t1)
+// Sequence bounds (clamped) of sequence n.  Dense rows: sequences of T rows
+// starting ts rows apart (ts = T, except for a segment of longer sequences).
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int n, int T, int ts, int& t0, int& t1)
 {
     if (cu) {
         t0 = min(max(cu[n], 0), T);
         t1 = min(max(cu[n + 1], t0), T);
     } else {
-        t0 = n * T;
+        t0 = n * ts;
         t1 = t0 + T;
     }
 }
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void chunk_plan_kernel(const int32_t*
         int acc = 0;
         for (int n = 0; n < N; ++n) {
             int t0, t1;
-            seq_bounds(cu, n, T, t0, t1);
+            seq_bounds(cu, n, T, T, t0, t1);
             off[n] = acc;
             acc += (t1 - t0 + C - 1) / C;
         }
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void chunk_plan_kernel(const int32_t*
     }
     for (int n = tid; n < N; n += PLAN_THREADS) {
         int t0, t1;
-        seq_bounds(cu, n, T, t0, t1);
+        seq_bounds(cu, n, T, T, t0, t1);
         nchunks[n] = (t1 - t0 + C - 1) / C;
     }
     __syncthreads();
@@ -268,7 +269,7 @@ struct PrepItem {
 // Item = slot * H + head.  Slots past the packed chunk count (and items past
 // the end) are not valid.
 __device__ __forceinline__ PrepItem prep_item(int item, int nitems, int H, const int32_t* cu, const int32_t* off,
-                                              int N, int T)
+                                              int N, int T, int ts)
 {
     PrepItem it{0, 0, 0, 0, false};
     if (item >= nitems) return it;
@@ -290,7 +291,7 @@ __device__ __forceinline__ PrepItem prep_item(int item, int nitems, int H, const
         c = it.slot - n * ncs;
     }
     int t_begin, t_end;
-    seq_bounds(cu, n, T, t_begin, t_end);
+    seq_bounds(cu, n, T, ts, t_begin, t_end);
     it.c0 = t_begin + c * C;
     it.len = min(C, t_end - it.c0);
     it.valid = true;
@@ -355,7 +356,7 @@ template <bool EJK>
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const float* __restrict__ a_log, const float* __restrict__ dt_bias,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ off, int N, int T, int H, int HKV, int nslots,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ off, int N, int T, int ts, int H, int HKV, int nslots,
     float scale, float lower_bound, int l2norm, unsigned char* __restrict__ ws)
 {
     __shared__ __attribute__((aligned(16))) unsigned char smem[PREP_LDS];
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
 
     const int nitems = nslots * H;
     int item = blockIdx.x;
-    PrepItem it = prep_item(item, nitems, H, cu, off, N, T);
+    PrepItem it = prep_item(item, nitems, H, cu, off, N, T, ts);
     PrepRaw cur;
     if (it.valid)
         prep_load<EJK>(cur, it, q, k, g, beta, H, HKV, threadIdx.x & 63, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         const int blk = wave;             // this wave's 16-row block in the prologue
         const PrepItem me = it;
         if (!me.valid) {   // a slot past the packed chunk count: only move on
-            it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
+            it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T, ts);
             if (it.valid) prep_load<EJK>(cur, it, q, k, g, beta, H, HKV, lane, blk);
             continue;
         }
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_prep_kernel(
         // outstanding requests drain under this item's compute instead of stalling
         // issue in one place (unconditionally: past the end this reloads the current
         // item, which keeps the loaded registers out of a branch)
-        it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T);
+        it = prep_item(item + gridDim.x, nitems, H, cu, off, N, T, ts);
         const PrepItem nx = it.valid ? it : me;
         prep_load<EJK, 0>(cur, nx, q, k, g, beta, H, HKV, lane, blk);
         lds_barrier();
@@ -908,7 +909,7 @@ __device__ __forceinline__ void load_frags(Frags<NJB>& f, const unsigned char* r
 template <int NJB, typename Tout>
 __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ init, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ order, int N, int T, int H, int HKV, int DV,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ order, int N, int T, int ts, int H, int HKV, int DV,
     int nslots, const unsigned char* __restrict__ ws, Tout* __restrict__ o, float* __restrict__ final_state)
 {
     using Sh = ScanShape<NJB>;
@@ -943,7 +944,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void chunk_scan_kernel(
     const int j0 = tile * DVT;
 
     int t_begin, t_end;
-    seq_bounds(cu, n, T, t_begin, t_end);
+    seq_bounds(cu, n, T, ts, t_begin, t_end);
     const int slot0 = off ? off[n] : n * ((T + C - 1) / C);
     // Valid cu_seqlens never need the clamp: a packed batch has at most T / C + N
     // chunks.  Overlapping ranges (a decreasing pair) can count more; their
@@ -1134,6 +1135,7 @@ template <typename Tout>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
 {
     const bool packed = a.cu != nullptr;
+    const int ts = a.tstride > 0 ? a.tstride : a.T;   // dense: rows between sequence starts
     unsigned char* wsb = static_cast<unsigned char*>(a.workspace);
     int32_t* off = nullptr;
     int32_t* order = nullptr;
@@ -1155,11 +1157,11 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
         const bf16_t* kk = static_cast<const bf16_t*>(a.k);
         if (a.ejk)
             hipLaunchKernelGGL(chunk_prep_kernel<true>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
-                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.Hkv, (int)slots, a.scale,
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, ts, a.H, a.Hkv, (int)slots, a.scale,
                                a.lower_bound, (int)a.l2norm, recs);
         else
             hipLaunchKernelGGL(chunk_prep_kernel<false>, pgrid, dim3(NTHREADS), 0, stream, qq, kk, a.g, a.beta,
-                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, a.H, a.Hkv, (int)slots, a.scale,
+                               a.a_log, a.dt_bias, a.cu, off, a.N, a.T, ts, a.H, a.Hkv, (int)slots, a.scale,
                                a.lower_bound, (int)a.l2norm, recs);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1173,13 +1175,13 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream)
     Tout* oo = static_cast<Tout*>(a.o);
     if (njb == 4)
         hipLaunchKernelGGL((chunk_scan_kernel<4, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
+                           order, a.N, a.T, ts, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
     else if (njb == 2)
         hipLaunchKernelGGL((chunk_scan_kernel<2, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
+                           order, a.N, a.T, ts, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
     else
         hipLaunchKernelGGL((chunk_scan_kernel<1, Tout>), grid, dim3(SCAN_THREADS), 0, stream, vv, a.init, a.cu, off,
-                           order, a.N, a.T, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
+                           order, a.N, a.T, ts, a.H, a.Hkv, a.dv, (int)slots, recs, oo, a.final_state);
     return hipGetLastError();
 }
 
@@ -1196,10 +1198,54 @@ size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed)
     return (packed ? offsets_bytes(N) : 0) + max_slots(N, T, packed) * (size_t)H * REC_BYTES;
 }
 
+size_t chunked_min_workspace_bytes(int N, int H, int dk, int dv, bool carry)
+{
+    if (dk != DK || dv % DV_MULT != 0 || N <= 0) return 0;
+    const size_t st = carry ? ((size_t)N * H * dk * dv * 4 + 255) / 256 * 256 : 0;
+    return st + (size_t)N * H * REC_BYTES;
+}
+
 hipError_t launch_chunked(const PrefillArgs& a, hipStream_t stream)
 {
-    if (a.out_bf16) return launch_typed<bf16_t>(a, stream);
-    return launch_typed<float>(a, stream);
+    auto one = [&](const PrefillArgs& s) {
+        return s.out_bf16 ? launch_typed<bf16_t>(s, stream) : launch_typed<float>(s, stream);
+    };
+    const bool packed = a.cu != nullptr;
+    if (packed || a.workspace_bytes >= chunked_workspace_bytes(a.N, a.T, a.H, a.dk, a.dv, packed)) return one(a);
+    // Dense rows and a workspace below the whole call's records: segments of
+    // whole chunks of every sequence, each segment's final state the next
+    // one's initial state (in final_state, or without one in the workspace's
+    // first bytes).  Chunks start at the same rows as in one call, and the
+    // state passes through in float32, so the result is the same bit for bit.
+    const bool carry = a.final_state == nullptr;
+    const size_t st = carry ? ((size_t)a.N * a.H * a.dk * a.dv * 4 + 255) / 256 * 256 : 0;
+    unsigned char* w = static_cast<unsigned char*>(a.workspace);
+    float* state = carry ? reinterpret_cast<float*>(w) : a.final_state;
+    const size_t avail = a.workspace_bytes > st ? a.workspace_bytes - st : 0;
+    const size_t per_chunk = (size_t)a.N * a.H * REC_BYTES;
+    const size_t nchunk = (size_t)(a.T + C - 1) / C;
+    const int seg = (int)std::min(avail / per_chunk, nchunk) * C;
+    if (seg <= 0) return hipErrorInvalidValue;   // below chunked_min_workspace_bytes (checked by the caller)
+    const size_t so = a.out_bf16 ? 2 : 4;
+    for (int ta = 0; ta < a.T; ta += seg) {
+        PrefillArgs s = a;
+        s.T = std::min(seg, a.T - ta);
+        s.tstride = a.T;
+        const size_t r = (size_t)ta;   // first row of the segment in every sequence
+        s.q = static_cast<const unsigned char*>(a.q) + r * a.H * a.dk * 2;
+        s.k = static_cast<const unsigned char*>(a.k) + r * a.Hkv * a.dk * 2;
+        s.v = static_cast<const unsigned char*>(a.v) + r * a.Hkv * a.dv * 2;
+        s.g = a.g ? a.g + r * a.H * (a.ejk ? 1 : a.dk) : nullptr;
+        s.beta = a.beta + r * a.H;
+        s.o = static_cast<unsigned char*>(a.o) + r * a.H * a.dv * so;
+        s.init = ta == 0 ? a.init : state;
+        s.final_state = state;
+        s.workspace = w + st;
+        s.workspace_bytes = avail;
+        const hipError_t e = one(s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

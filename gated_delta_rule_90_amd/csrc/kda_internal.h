@@ -32,6 +32,7 @@ struct PrefillArgs {
     float* final_state;    // [N, H, dk, dv] or null
     void* workspace;
     size_t workspace_bytes;
+    int tstride;           // dense: rows between sequence starts (0 = T; set for a segment of longer sequences)
 };
 
 struct DecodeArgs {
@@ -122,6 +123,10 @@ inline hipError_t launch_recurrent(const PrefillArgs& a, hipStream_t stream)
 hipError_t launch_chunked(const PrefillArgs& a, hipStream_t stream);
 bool chunked_supported(const PrefillArgs& a);
 size_t chunked_workspace_bytes(int N, int T, int H, int dk, int dv, bool packed);
+// the least workspace with which a dense call still runs (in segments of whole
+// chunks of every sequence): one chunk's records per (sequence, head), plus the
+// state carried between segments when final_state is not given
+size_t chunked_min_workspace_bytes(int N, int H, int dk, int dv, bool carry);
 // the float32 chunked kernel (16-token chunks on the vector ALUs)
 hipError_t launch_chunked_f32(const PrefillArgs& a, hipStream_t stream);
 bool chunked_f32_supported(const PrefillArgs& a);

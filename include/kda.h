@@ -143,10 +143,12 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, kda_dtype_
  * allocates nothing.  The chunked MFMA route takes its workspace from a fixed
  * device array of KDA_NOALLOC_SCRATCH_BYTES (256 MiB) inside the library: one
  * copy per GPU, held from the library's first use on that GPU until the
- * process ends.  A call that takes that route and needs more than that
- * (kda_prefill_workspace_bytes() of its arguments; about 1 KiB per token and
- * head, e.g. 16384 tokens at H = 16) returns KDA_EUNSUPPORTED before any
- * launch.  The two-kernel float32 route uses the same array when its blocks
+ * process ends.  A dense call on that route that needs more than that runs in
+ * segments of whole chunks inside the array (as kda_prefill does with a small
+ * workspace, below); a packed call that needs more (kda_prefill_workspace_bytes()
+ * of its arguments; about 1 KiB per token and head, e.g. 16384 tokens at
+ * H = 16), or a dense one with more than about 4000 (sequence, head) pairs,
+ * returns KDA_EUNSUPPORTED before any launch.  The two-kernel float32 route uses the same array when its blocks
  * fit (about 1.7 KiB per token and head at dk 128), and otherwise runs as one
  * kernel.  The array is used on the calling thread's current HIP device,
  * which must be the device of `stream` and of the tensors.  Every call on one
@@ -172,7 +174,12 @@ kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, kd
  * of packed sequences (num_seqs > 0 with B == 1 means packed).  The caller
  * allocates it (the library never allocates); it must not be shared by calls
  * that may run concurrently.  A float32-route call given less runs as one
- * kernel, which needs none. */
+ * kernel, which needs none.  A dense call (no cu_seqlens) on the MFMA route
+ * given less runs in segments of whole 64-token chunks of every sequence, each
+ * segment's final state the next one's initial state, with the same result bit
+ * for bit; it needs at least 64.5 KiB per (sequence, head), plus
+ * N * H * dk * dv * 4 bytes (rounded up to 256) for the carried state when
+ * final_state is NULL.  Packed calls need the whole size. */
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int32_t B, int32_t T, int32_t H,
                                    int32_t dk, int32_t dv, kda_dtype_t in_dtype,
                                    uint32_t flags);

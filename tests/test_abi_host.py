@@ -142,9 +142,16 @@ def test_prefill_noalloc_rejects_calls_beyond_its_scratch():
     text = open(HEADER).read()
     assert re.search(r"KDA_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)256 << 20\)", text)
     L = kda.lib()
-    need = L.kda_prefill_workspace_bytes(0, 1, 1 << 16, 16, 128, 128, kda.BF16, kda.QK_L2NORM | kda.CHUNKED)
+    # packed sequences need the whole call's records: 1025 slots x 16 heads x 64.5 KiB
+    need = L.kda_prefill_workspace_bytes(1, 1, 1 << 16, 16, 128, 128, kda.BF16, kda.QK_L2NORM | kda.CHUNKED)
     assert need > (256 << 20)
-    st = L.kda_prefill_noalloc(P, P, P, kda.BF16, P, P, P, P, None, None, 0, 1, 1 << 16, 16, 0, 128, 128,
+    st = L.kda_prefill_noalloc(P, P, P, kda.BF16, P, P, P, P, None, P, 1, 1, 1 << 16, 16, 0, 128, 128,
+                               -1.0, -5.0, 64, kda.QK_L2NORM | kda.CHUNKED, P, kda.BF16, None, None)
+    assert st == kda.KDA_EUNSUPPORTED
+    assert "scratch" in L.kda_last_error().decode()
+    # a dense batch runs in segments of whole chunks, but needs one chunk's records for
+    # every (sequence, head): 300 x 16 x 64.5 KiB is more than the scratch
+    st = L.kda_prefill_noalloc(P, P, P, kda.BF16, P, P, P, P, None, None, 0, 300, 64, 16, 0, 128, 128,
                                -1.0, -5.0, 64, kda.QK_L2NORM | kda.CHUNKED, P, kda.BF16, None, None)
     assert st == kda.KDA_EUNSUPPORTED
     assert "scratch" in L.kda_last_error().decode()

@@ -300,3 +300,36 @@ def test_chunked_bf16_routing_falls_back_to_token_by_token():
                                use_chunked=False, return_state=True)
         torch.cuda.synchronize()
         assert torch.equal(o_u, o_r) and torch.equal(s_u, s_r)
+
+
+@pytest.mark.parametrize("ejk", [False, True], ids=["kda", "ejk"])
+@pytest.mark.parametrize("return_state", [True, False], ids=["state", "no_state"])
+def test_chunked_dense_workspace_below_the_call_runs_in_segments(monkeypatch, ejk, return_state):
+    """A dense call given less workspace than its whole records runs in segments of
+    whole 64-token chunks of every sequence (the state carried in final_state, or in
+    the workspace without one): the result equals the one-segment call bit for bit.
+    Here three chunks per segment over 1000 tokens (16 chunks, a ragged last one)."""
+    import torch
+    inp = workloads.prefill_inputs(2, 1000, 4, 128, 64, seed=1700 + ejk, ejk=ejk, init_state=True)
+    say("dense segments", "EJK" if ejk else "KDA", "with state" if return_state else "output only")
+    io, f = torch.bfloat16, torch.float32
+
+    def call():
+        r = kda.prefill(dev(inp.q, io), dev(inp.k, io), dev(inp.v, io), dev(inp.g, f), dev(inp.beta, f),
+                        None if ejk else dev(inp.a_log, f), None if ejk else dev(inp.dt_bias, f),
+                        dev(inp.initial_state, f), scale=inp.scale, lower_bound=inp.lower_bound, ejk=ejk,
+                        return_state=return_state)
+        torch.cuda.synchronize()
+        return [x.float().cpu().numpy() for x in (r if return_state else (r,))]
+
+    ref = call()
+    carry = 0 if return_state else 2 * 4 * 128 * 64 * 4
+    small = carry + 3 * 2 * 4 * 66048          # three chunks of records for every (sequence, head)
+    real = kda.prefill_workspace_bytes
+    assert real(0, 2, 1000, 4, 128, 64, kda.QK_L2NORM | kda.CHUNKED) > small
+    monkeypatch.setattr(kda, "prefill_workspace_bytes", lambda *a, **k: small)
+    seg = call()
+    for x, y in zip(seg, ref):
+        np.testing.assert_array_equal(x, y)
+    ro, rs = prefill_oracle(inp)
+    assert rel_l2(seg[0], ro) <= TOL

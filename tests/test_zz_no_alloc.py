@@ -67,3 +67,19 @@ def test_noalloc_float32_two_kernel_route_two_calls(dk):
         eo, es = rel_l2(o_n, ro), rel_l2(s_n, rs)
         say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
         assert eo <= 1e-5 and es <= 1e-5
+
+
+def test_noalloc_dense_call_beyond_the_scratch_runs_in_segments():
+    """One 32768-token sequence with 16 heads needs 541 MB of records, more than the
+    scratch array: the dense call runs in segments of whole chunks inside it, the
+    result the same bit for bit as kda_prefill with the whole workspace; then a
+    smaller call in a row."""
+    big = workloads.prefill_inputs(1, 32768, 16, 128, 128, seed=1620, init_state=True)
+    small = workloads.prefill_inputs(2, 300, 4, 128, 64, seed=1621, init_state=True)
+    assert kda.prefill_workspace_bytes(0, 1, 32768, 16, 128, 128, kda.QK_L2NORM | kda.CHUNKED) > (256 << 20)
+    for name, inp in (("B1 T32768 H16", big), ("B2 T300 H4 dv64", small)):
+        say("noalloc segments", name)
+        o_n, s_n = _run(inp, noalloc=True)
+        o_r, s_r = _run(inp, noalloc=False)
+        np.testing.assert_array_equal(o_n, o_r)
+        np.testing.assert_array_equal(s_n, s_r)
