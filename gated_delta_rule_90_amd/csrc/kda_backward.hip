@@ -679,8 +679,11 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     // chunk's operand block in LDS
     // (the group and wave indices are wave-uniform: kept in scalar registers,
     // so that resources built from them need no per-lane loop)
-    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT);
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT) & (NG - 1);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
+    // (the masks change no value: they restate the ranges that readfirstlane
+    // hides from the compiler, which then folds the per-wave selections)
+    static_assert((NG & (NG - 1)) == 0 && (NW & (NW - 1)) == 0, "power-of-two group and wave counts");
     const int lm = lane & 15, lk = lane >> 4;
     int j0, h, n;
     if (!scan_unit(p, NG, j0, h, n)) return;
@@ -857,8 +860,11 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     constexpr int N4 = PL::SIZE / 4, NP = (N4 + NG * BT - 1) / (NG * BT);
     constexpr uint32_t SO = sizeof(Tout);
     __shared__ OutLds<DK, NG> L;
-    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT);
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT) & (NG - 1);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
+    // (the masks change no value: they restate the ranges that readfirstlane
+    // hides from the compiler, which then folds the per-wave selections)
+    static_assert((NG & (NG - 1)) == 0 && (NW & (NW - 1)) == 0, "power-of-two group and wave counts");
     const int lm = lane & 15, lk = lane >> 4;
     int j0, h, n;
     if (!scan_unit(p, NG, j0, h, n)) return;
@@ -1033,8 +1039,11 @@ __global__ __launch_bounds__(NG * BT) __attribute__((amdgpu_waves_per_eu(2))) vo
     // chunk's operand block in LDS
     // (the group and wave indices are wave-uniform: kept in scalar registers,
     // so that resources built from them need no per-lane loop)
-    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT);
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x % BT, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / BT) & (NG - 1);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
+    // (the masks change no value: they restate the ranges that readfirstlane
+    // hides from the compiler, which then folds the per-wave selections)
+    static_assert((NG & (NG - 1)) == 0 && (NW & (NW - 1)) == 0, "power-of-two group and wave counts");
     const int lm = lane & 15, lk = lane >> 4;
     int j0, h, n;
     if (!scan_unit(p, NG, j0, h, n)) return;

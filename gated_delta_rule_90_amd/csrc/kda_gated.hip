@@ -358,8 +358,11 @@ __global__ __launch_bounds__(NG * GTH) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ GScanLds<DK, NG> L;
     // (the group and wave indices are wave-uniform: kept in scalar registers,
     // so that resources built from them need no per-lane loop)
-    const int tid = threadIdx.x % GTH, cg = __builtin_amdgcn_readfirstlane(threadIdx.x / GTH);
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x % GTH, cg = __builtin_amdgcn_readfirstlane(threadIdx.x / GTH) & (NG - 1);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (GNW - 1);
+    // (the masks change no value: they restate the ranges that readfirstlane
+    // hides from the compiler, which then folds the per-wave selections)
+    static_assert((NG & (NG - 1)) == 0 && (GNW & (GNW - 1)) == 0, "power-of-two group and wave counts");
     const int lm = lane & 15, lk = lane >> 4;
     const int H = p.H, DV = p.dv;
     const int ntile = DV / (GJ * NG);
