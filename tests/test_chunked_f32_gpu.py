@@ -318,3 +318,33 @@ def test_without_workspace_the_one_kernel_route_serves_dk128(monkeypatch, ejk):
     monkeypatch.setattr(kda, "prefill_workspace_bytes", lambda *a, **k: 0)
     o_1, s_1 = _check(inp)
     assert rel_l2(o_1, o_w) <= 2 * TOL and rel_l2(s_1, s_w) <= 2 * TOL
+
+
+@pytest.mark.parametrize("dtype,dk,dv,H", [("f32", 128, 128, 8), ("bf16", 64, 64, 16), ("f32", 32, 32, 32)])
+@pytest.mark.parametrize("ejk", [False, True])
+def test_two_kernel_route_two_tiles_per_scan_workgroup(dtype, dk, dv, H, ejk):
+    """Eight packed sequences (ragged, one empty) with H * 8 * dv / 32 >= 256, so that the
+    scan carries two 16-column state tiles per workgroup: every (sequence, head) unit
+    against the oracle, and each sequence run alone (few units: one tile per workgroup)
+    equal to the packed call bit for bit."""
+    import torch
+    lens = [37, 16, 5, 64, 21, 0, 50, 33]
+    assert H * len(lens) * (dv // 32) >= 256
+    inp = workloads.prefill_inputs(1, 0, H, dk, dv, seed=400 + dk + ejk, dtype=dtype, lengths=lens,
+                                   ejk=ejk, init_state=True)
+    say("two-kernel route, two tiles per scan workgroup", dtype, "dk", dk, "dv", dv, "H", H,
+        "ejk" if ejk else "kda")
+    o, s = prefill_gpu(inp, out_dtype=torch.float32)
+    ro, rs = prefill_oracle(inp)
+    cu = inp.cu_seqlens
+    worst_o = worst_s = 0.0
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        for h in range(H):
+            if b > a:
+                worst_o = max(worst_o, rel_l2(o[0, a:b, h], ro[0, a:b, h]))
+            worst_s = max(worst_s, rel_l2(s[n, h], rs[n, h]))
+    say(f"  worst unit rel-L2 o={worst_o:.3e} S={worst_s:.3e}")
+    assert worst_o <= TOL and worst_s <= TOL, (worst_o, worst_s)
+    o2, s2 = prefill_gpu(inp)
+    _separate_runs_bitwise(inp, o2, s2)
