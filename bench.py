@@ -226,6 +226,17 @@ def _unit_worst(o, ro, s, rs, cu=None):
     return wo, ws
 
 
+# float32 prefill workloads: (input generator in workloads, chunked route, kernel sources)
+FP32_CONFIGS = {
+    "recurrent_fp32_b1_t64_h2_d16": ("recurrent_fp32_small", False, ("kda_recurrent.hip", "kda_device.h")),
+    "chunked_fp32_b1_t64_h2_d16": ("recurrent_fp32_small", True, ("kda_chunked_f32.hip", "kda_device.h")),
+    "prefill_fp32_b1_t4096_h16_d128_token_by_token": ("prefill_fp32_b1_t4096_h16_d128", False,
+                                                      ("kda_recurrent.hip", "kda_device.h")),
+    "prefill_fp32_b1_t4096_h16_d128_chunked": ("prefill_fp32_b1_t4096_h16_d128", True,
+                                               ("kda_backward.hip", "kda_device.h")),
+}
+
+
 def kernel_counters(name, sources, alg_bytes):
     """HBM traffic per call of a workload from its committed counter summary
     (profiles/<name>_pmc.txt, taken on the current source of `sources`) and
@@ -713,6 +724,8 @@ def bench_configs(steps, warmup, cpu=True):
             out[key]["cpu_baseline"] = _cpu_prefill_leg(inp, range(nh), 3, "1 sequence x 4096 tokens",
                                                         check=out[key].pop("check"))
     del inp
+    for key, (_, _, sources) in FP32_CONFIGS.items():
+        out[key]["rocprof"] = kernel_counters(key, sources, out[key].get("alg_bytes"))
     gc.collect()
     for name in _mfma_configs():
         out[name] = bench_one_mfma_config(name, steps, warmup, cpu)
@@ -777,13 +790,19 @@ def main():
         elif args.config in _mfma_configs():
             res = bench_one_mfma_config(args.config, max(10, args.steps), args.warmup, cpu=False,
                                         extras=False)
+        elif args.config in FP32_CONFIGS:
+            from gated_delta_rule_90_amd import workloads
+            gen, chunked, _ = FP32_CONFIGS[args.config]
+            res = _prefill_run(getattr(workloads, gen)(), max(10, args.steps), args.warmup, use_chunked=chunked)
+            res.pop("check", None)
         elif args.config == "backward_b4_t4096_h16_d128_bf16":
             res = bench_backward(args.steps, args.warmup, cpu=False)
         elif args.config in GATED_CONFIGS:
             res = bench_gated(args.steps, args.warmup, cpu=False, only=args.config)[args.config]
         else:
             print(f"bench.py: unknown --config {args.config}; one of prefill_b4_t4096_h16_d128, "
-                  + ", ".join(list(_mfma_configs()) + ["backward_b4_t4096_h16_d128_bf16"] + GATED_CONFIGS),
+                  + ", ".join(list(_mfma_configs()) + list(FP32_CONFIGS) + ["backward_b4_t4096_h16_d128_bf16"]
+                              + GATED_CONFIGS),
                   file=sys.stderr)
             sys.exit(2)
         print(json.dumps({"config": args.config, **res}), flush=True)
