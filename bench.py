@@ -739,7 +739,9 @@ def bench_configs(steps, warmup, cpu=True):
     _, dres = _decode_run(ginp, 20 * steps, 2 * warmup)
     out["decode_grouped_b64_h32_hkv8_d128"] = {
         "steps_per_s": round(dres["steps_per_s"], 2), "ms_per_step": round(dres["ms"], 5),
-        "alg_bytes": dres["bytes"], "hbm_frac": dres["roofline"]["frac"]}
+        "alg_bytes": dres["bytes"], "hbm_frac": dres["roofline"]["frac"],
+        "rocprof": kernel_counters("decode_grouped_b64_h32_hkv8_d128", ("kda_decode.hip", "kda_device.h"),
+                                   dres["bytes"])}
     if cpu:
         out["decode_grouped_b64_h32_hkv8_d128"]["cpu_baseline"] = cpu_decode_baseline(ginp, 5.0,
                                                                                       check=dres.get("check"))
@@ -795,14 +797,19 @@ def main():
             gen, chunked, _ = FP32_CONFIGS[args.config]
             res = _prefill_run(getattr(workloads, gen)(), max(10, args.steps), args.warmup, use_chunked=chunked)
             res.pop("check", None)
+        elif args.config == "decode_grouped_b64_h32_hkv8_d128":
+            from gated_delta_rule_90_amd import workloads
+            _, dres = _decode_run(workloads.decode_grouped_b64_h32_hkv8_d128(), 20 * max(1, args.steps), args.warmup)
+            res = {"steps_per_s": round(dres["steps_per_s"], 2), "ms_per_step": round(dres["ms"], 5),
+                   "alg_bytes": dres["bytes"]}
         elif args.config == "backward_b4_t4096_h16_d128_bf16":
             res = bench_backward(args.steps, args.warmup, cpu=False)
         elif args.config in GATED_CONFIGS:
             res = bench_gated(args.steps, args.warmup, cpu=False, only=args.config)[args.config]
         else:
             print(f"bench.py: unknown --config {args.config}; one of prefill_b4_t4096_h16_d128, "
-                  + ", ".join(list(_mfma_configs()) + list(FP32_CONFIGS) + ["backward_b4_t4096_h16_d128_bf16"]
-                              + GATED_CONFIGS),
+                  + ", ".join(list(_mfma_configs()) + list(FP32_CONFIGS) + ["decode_grouped_b64_h32_hkv8_d128",
+                              "backward_b4_t4096_h16_d128_bf16"] + GATED_CONFIGS),
                   file=sys.stderr)
             sys.exit(2)
         print(json.dumps({"config": args.config, **res}), flush=True)
